@@ -1,0 +1,166 @@
+"""Attention on dequantized low-bit operands, in fp64.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+What the pages fix: Q, K and V all enter attention quantized, so both the
+score product Q K^T and the weighted sum with V take low-bit operands
+("FA 量化" page, 概述); attention runs in the FP8 domain and its output is
+dequantized back to the original precision (MindIE SD "量化" page, FA量化 /
+技术特点, FP8 Attention).  The flash-attention structure (tiles, online
+softmax) is the one of the FlashAttention reference the "FA 量化" page cites.
+
+What the pages leave open, and the reading taken here (parity unpinned: the
+rule below is pinned only by self-consistency properties - tile-order
+invariance, the single-tile closed form, equal-score and dominant-key cases -
+not by any value on the pages):
+
+* Keys are cut into P-tiles of 128 keys aligned to absolute key index.  For
+  each query row i and tile t with at least one unmasked key:
+  m_it = max_j s_ij, p_ij = exp(s_ij - m_it), L_it = sum_j p_ij (unquantized).
+* p enters the PV product quantized to the mode's own type with a static
+  scale (0 <= p <= 1):
+    - 'int8':  Pq = rne(127 p) / 127;
+    - 'fp8':   with sigma_t = max over the tile's keys of the per-key V scale
+               and w_j = s_v,j / sigma_t (the V scale folded into P):
+               Pq = E4M3(448 p w_j) / (448 w_j);
+    - 'mxfp4': the MXFP4 quantizer applied along keys, 32-key groups aligned
+               to absolute key index, masked keys counting as p = 0;
+    - 'exact': Pq = p (no quantization; reduces to softmax attention).
+  C_it = sum_j Pq_ij vhat_j with vhat the exactly dequantized V.
+* Combine: M_i = max_t m_it; O_i = sum_t e^{m_it-M_i} C_it / sum_t e^{m_it-M_i} L_it.
+* Scores s_ij = (qhat_i . khat_j) * sm_scale with sm_scale = 1/sqrt(D) by
+  default; under causal masking key j > query i is excluded (Sq == Skv).
+"""
+
+import numpy as np
+
+from . import formats as F
+from .quantize import mx_shared_exponent
+
+P_TILE = 128
+MX_GROUP = 32
+TIE_REL = 2.0 ** -12
+
+
+def _quantize_p(p, rule, w=None):
+    """Dequantized quantized probabilities for one row-chunk, per tile.
+
+    p: [nr, nt, 128] fp64 (masked -> 0); w: [nt, 128] (fp8 only).
+    Returns (Pq, step, near) where `near` flags elements whose pre-rounding
+    value lies within 2^-12 (relative) of a rounding boundary and `step` is
+    the size of the code step such an element may flip by (in p units)."""
+    if rule == "exact":
+        z = np.zeros_like(p)
+        return p.copy(), z, z.astype(bool)
+    if rule == "int8":
+        u = 127.0 * p
+        pq = np.rint(u) / 127.0
+        frac = u - np.floor(u)
+        near = (np.abs(frac - 0.5) <= TIE_REL * u) & (u > 0)
+        step = np.full_like(p, 1.0 / 127.0)
+        return pq, step, near
+    if rule == "fp8":
+        scale = 448.0 * w[None, :, :]
+        u = p * scale
+        pq = F.e4m3_decode(F.e4m3_encode(u)) / scale
+        lo, hi = F.e4m3_neighbors(u)
+        mid = 0.5 * (lo + hi)
+        near = (np.abs(u - mid) <= TIE_REL * u) & (u > 0)
+        step = (hi - lo) / scale
+        return pq, step, near
+    if rule == "mxfp4":
+        nr, nt, n = p.shape
+        g = p.reshape(nr, nt, n // MX_GROUP, MX_GROUP)
+        amax = g.max(axis=3)
+        E = mx_shared_exponent(amax)
+        v = np.ldexp(g, -E[..., None])
+        pq = np.ldexp(F.e2m1_decode(F.e2m1_encode(v)), E[..., None])
+        lo, hi = F.e2m1_neighbors(v)
+        mid = 0.5 * (lo + hi)
+        near = (np.abs(v - mid) <= TIE_REL * v) & (v > 0) & (v < 6.0)
+        step = np.ldexp(hi - lo, E[..., None])
+        # A group whose amax sits just off a power of two may take the other
+        # shared exponent; then every element of it may move by up to
+        # 3 * 2^(E+1).  amax == 1 exactly (the tile's own maximum) is exact on
+        # both sides and is not a tie.
+        k = np.rint(np.log2(np.where(amax > 0, amax, 1.0)))
+        gnear = (np.abs(amax - np.exp2(k)) <= TIE_REL * amax) & (amax > 0) & (amax != 1.0)
+        gstep = 3.0 * np.ldexp(1.0, E + 1)
+        near = near | gnear[..., None]
+        step = np.where(gnear[..., None], np.maximum(step, gstep[..., None]), step)
+        return (pq.reshape(nr, nt, n), step.reshape(nr, nt, n),
+                near.reshape(nr, nt, n))
+    raise ValueError(f"unknown P rule {rule!r}")
+
+
+def attention(qhat, khat, vhat, p_rule, *, v_scale=None, causal=False,
+              sm_scale=None, rows=None, allowance=False, chunk=128):
+    """Quantized-domain flash attention reference.
+
+    qhat: [B,H,Sq,D]; khat, vhat: [B,H,Skv,D] dequantized values.
+    v_scale: [B,H,Skv] per-key V scale (needed for p_rule 'fp8').
+    rows: optional sorted array of query rows to evaluate (for every (b,h)).
+    Returns O [B,H,R,D] fp64, plus (T [B,H,R,D], n_tie) when allowance=True:
+    T is the tie allowance - the sum, over probability elements near a
+    rounding boundary, of one code step * |vhat| * e^{m-M} / denominator."""
+    qhat = np.asarray(qhat, dtype=np.float64)
+    khat = np.asarray(khat, dtype=np.float64)
+    vhat = np.asarray(vhat, dtype=np.float64)
+    B, H, Sq, D = qhat.shape
+    Skv = khat.shape[2]
+    if causal and Sq != Skv:
+        raise ValueError("causal attention needs Sq == Skv")
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        rows = np.arange(Sq)
+    rows = np.asarray(rows, dtype=np.int64)
+    nt = -(-Skv // P_TILE)
+    pad = nt * P_TILE - Skv
+    key_idx = np.arange(nt * P_TILE)
+    out = np.zeros((B, H, rows.size, D))
+    tall = np.zeros((B, H, rows.size, D)) if allowance else None
+    n_tie = 0
+    for b in range(B):
+        for h in range(H):
+            k = khat[b, h]
+            v = np.concatenate([vhat[b, h], np.zeros((pad, D))], axis=0)
+            vt = v.reshape(nt, P_TILE, D)
+            w = None
+            if p_rule == "fp8":
+                sv = np.asarray(v_scale[b, h], dtype=np.float64)
+                svp = np.concatenate([sv, np.zeros(pad)]).reshape(nt, P_TILE)
+                sigma = svp.max(axis=1, keepdims=True)
+                w = np.where(svp > 0, svp / sigma, 1.0)
+            for c0 in range(0, rows.size, chunk):
+                r = rows[c0:c0 + chunk]
+                s = (qhat[b, h, r] @ k.T) * sm_scale  # [nr, Skv]
+                valid = np.ones((r.size, nt * P_TILE), dtype=bool)
+                valid[:, Skv:] = False
+                if causal:
+                    valid &= key_idx[None, :] <= r[:, None]
+                sp = np.full((r.size, nt * P_TILE), -np.inf)
+                sp[:, :Skv] = s
+                sp = np.where(valid, sp, -np.inf).reshape(r.size, nt, P_TILE)
+                vmask = valid.reshape(r.size, nt, P_TILE)
+                m_t = sp.max(axis=2)  # -inf for fully masked tiles
+                live = np.isfinite(m_t)
+                m_safe = np.where(live, m_t, 0.0)
+                p = np.where(vmask, np.exp(sp - m_safe[..., None]), 0.0)
+                L_t = p.sum(axis=2)
+                pq, step, near = _quantize_p(p, p_rule, w=w)
+                C_t = np.matmul(pq.transpose(1, 0, 2), vt).transpose(1, 0, 2)  # [nr, nt, D]
+                M = np.where(live, m_t, -np.inf).max(axis=1)
+                f = np.where(live, np.exp(m_safe - M[:, None]), 0.0)  # e^{m_t - M}
+                den = (f * L_t).sum(axis=1)
+                num = (f[..., None] * C_t).sum(axis=1)
+                out[b, h, c0:c0 + r.size] = num / den[:, None]
+                if allowance:
+                    t_el = np.where(near & vmask, step, 0.0) * f[..., None]
+                    n_tie += int((near & vmask).sum())
+                    tr = np.matmul(t_el.transpose(1, 0, 2), np.abs(vt)).sum(axis=0)
+                    tall[b, h, c0:c0 + r.size] = tr / den[:, None]
+    if allowance:
+        return out, tall, n_tie
+    return out
+

@@ -1,0 +1,171 @@
+"""Pins of the oracle's attention: softmax attention (torch SDPA, an
+independent library) when P is not quantized; closed forms where the P rule
+is exact; hand-worked two-key values; tile-order invariance."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import formats as F
+
+
+def _sdpa(q, k, v, causal, scale=None):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal, scale=scale)
+    return o.numpy()
+
+
+@pytest.mark.parametrize("S,D,causal", [(100, 64, False), (128, 64, True), (300, 128, False),
+                                        (300, 64, True), (513, 32, True)])
+def test_exact_p_equals_softmax_attention(S, D, causal):
+    g = np.random.default_rng(S + D)
+    q, k, v = (g.standard_normal((2, 2, S, D)) * 1.5 for _ in range(3))
+    o = A.attention(q, k, v, "exact", causal=causal)
+    assert np.allclose(o, _sdpa(q, k, v, causal), rtol=0, atol=1e-12)
+
+
+def test_row_sampling_is_exact():
+    g = np.random.default_rng(1)
+    q, k, v = (g.standard_normal((1, 2, 400, 64)) for _ in range(3))
+    rows = np.array([0, 5, 127, 128, 399])
+    full = A.attention(q, k, v, "int8", causal=True)
+    part = A.attention(q, k, v, "int8", causal=True, rows=rows)
+    assert np.array_equal(full[:, :, rows], part)
+
+
+def _two_key(p_rule, v_scale=None):
+    """Two keys in one tile with scores 0 and -1: q = e0 * sqrt(D), k0 = 0,
+    k1 = -e0  -> s = (0, -1) with sm_scale 1/sqrt(D)."""
+    D = 64
+    q = np.zeros((1, 1, 1, D)); q[..., 0] = math.sqrt(D)
+    k = np.zeros((1, 1, 2, D)); k[0, 0, 1, 0] = -1.0
+    v = np.zeros((1, 1, 2, D)); v[0, 0, 0, 1] = 1.0; v[0, 0, 1, 2] = 1.0
+    if v_scale is not None:
+        v[0, 0, 1, 2] = v_scale[0, 0, 1]  # v1 = s_v1 * code 1
+    return A.attention(q, k, v, p_rule, v_scale=v_scale)[0, 0, 0], v
+
+
+def test_two_key_hand_worked_int8():
+    # p = (1, e^-1); 127 e^-1 = 46.72 -> 47
+    o, _ = _two_key("int8")
+    den = 1 + math.exp(-1)
+    assert o[1] == pytest.approx(1 / den, abs=1e-15)
+    assert o[2] == pytest.approx((47 / 127) / den, abs=1e-15)
+
+
+def test_two_key_hand_worked_fp8():
+    # equal V scales: 448 e^-1 = 164.81 -> E4M3 160 (step 16 in [128, 256))
+    vs = np.ones((1, 1, 2))
+    o, _ = _two_key("fp8", vs)
+    den = 1 + math.exp(-1)
+    assert o[2] == pytest.approx((160 / 448) / den, abs=1e-15)
+    # V scales (1, 0.5): sigma = 1, w1 = 0.5: 448*0.5*e^-1 = 82.4 -> 80 (step 8);
+    # Pq1 = 80 / (448*0.5); v1 = 0.5
+    vs = np.array([[[1.0, 0.5]]])
+    o, _ = _two_key("fp8", vs)
+    assert o[2] == pytest.approx((80 / 224) * 0.5 / den, abs=1e-15)
+
+
+def test_two_key_hand_worked_mxfp4():
+    # group amax 1 -> E = -2; p * 4 = (4, 1.4715) -> (4, 1.5) -> Pq = (1, 0.375)
+    o, _ = _two_key("mxfp4")
+    den = 1 + math.exp(-1)
+    assert o[1] == pytest.approx(1 / den, abs=1e-15)
+    assert o[2] == pytest.approx(0.375 / den, abs=1e-15)
+
+
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4"])
+def test_equal_scores_give_mean_of_v(rule):
+    g = np.random.default_rng(2)
+    S, D = 300, 64
+    q = np.zeros((1, 1, 5, D))
+    k = g.standard_normal((1, 1, S, D))
+    v = g.standard_normal((1, 1, S, D))
+    vs = np.full((1, 1, S), 0.37)
+    o = A.attention(q, k, v, rule, v_scale=vs)
+    assert np.allclose(o, v.mean(axis=2, keepdims=True), atol=1e-13)
+
+
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "exact"])
+def test_dominant_key(rule):
+    g = np.random.default_rng(3)
+    S, D = 260, 64
+    q = np.zeros((1, 1, 1, D)); q[..., 0] = 1.0
+    k = np.zeros((1, 1, S, D)); k[0, 0, 200, 0] = 4000.0
+    v = g.standard_normal((1, 1, S, D))
+    o = A.attention(q, k, v, rule, v_scale=np.ones((1, 1, S)))
+    assert np.allclose(o[0, 0, 0], v[0, 0, 200], atol=1e-13)
+
+
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4"])
+def test_tile_local_max(rule):
+    """Tile 0: one key with a large score; tile 1: 128 keys of one lower
+    score.  With each tile's probabilities taken relative to its own max the
+    quantized P is exact in both tiles (1 and 0/1), so O is exactly softmax
+    attention.  Taking tile 1 relative to the running max would quantize
+    e^{b-a} instead and miss this."""
+    g = np.random.default_rng(4)
+    D = 64
+    q = np.zeros((1, 1, 1, D)); q[..., 0] = math.sqrt(D)
+    k = np.zeros((1, 1, 256, D))
+    k[0, 0, 0, 0] = 2.0       # score a = 2
+    k[0, 0, 1:128, 0] = -60.0  # p underflows far below any code step
+    k[0, 0, 128:, 0] = 0.3    # score b = 0.3 for the whole second tile
+    v = g.standard_normal((1, 1, 256, D))
+    o = A.attention(q, k, v, rule, v_scale=np.ones((1, 1, 256)))
+    ref = _sdpa(q, k, v, False)
+    assert np.allclose(o, ref, atol=1e-12)
+
+
+def test_fp8_sigma_is_per_tile():
+    """Equal scores, V scale 1 in tile 0 and 0.3 in tile 1: sigma per tile
+    makes w = 1 everywhere and P exact (O = mean v); a global sigma would
+    quantize 448*0.3 = 134.4 -> 128 in tile 1."""
+    g = np.random.default_rng(5)
+    D = 64
+    q = np.zeros((1, 1, 1, D))
+    k = g.standard_normal((1, 1, 256, D))
+    v = g.standard_normal((1, 1, 256, D))
+    vs = np.concatenate([np.ones(128), np.full(128, 0.3)]).reshape(1, 1, 256)
+    o = A.attention(q, k, v, "fp8", v_scale=vs)
+    assert np.allclose(o[0, 0, 0], v[0, 0].mean(axis=0), atol=1e-13)
+
+
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4"])
+def test_tile_order_invariance(rule):
+    g = np.random.default_rng(6)
+    S, D = 512, 64
+    q, k, v = (g.standard_normal((1, 1, S, D)) * 2 for _ in range(3))
+    vs = np.exp(g.standard_normal((1, 1, S)))
+    o = A.attention(q, k, v, rule, v_scale=vs)
+    perm = np.concatenate([np.arange(t * 128, t * 128 + 128) for t in [2, 0, 3, 1]])
+    o2 = A.attention(q, k[:, :, perm], v[:, :, perm], rule, v_scale=vs[:, :, perm])
+    assert np.allclose(o, o2, atol=1e-13)
+
+
+def test_quantized_close_to_exact():
+    """Each rule stays close to softmax attention on typical data (rule
+    sanity: int8/e4m3 P errors are ~1e-2 relative Frobenius)."""
+    g = np.random.default_rng(7)
+    q, k, v = (g.standard_normal((1, 2, 256, 64)) for _ in range(3))
+    ref = A.attention(q, k, v, "exact")
+    for rule, tol in [("int8", 0.05), ("fp8", 0.06), ("mxfp4", 0.25)]:
+        o = A.attention(q, k, v, rule, v_scale=np.ones((1, 2, 256)))
+        err = np.linalg.norm(o - ref) / np.linalg.norm(ref)
+        assert 1e-4 < err < tol, (rule, err)
+
+
+def test_allowance_flags_ties():
+    # p = exp(-x) with 127 p exactly at a half-integer up to 2^-13 relative
+    D = 64
+    t = 46.5 / 127
+    s1 = math.log(t)
+    q = np.zeros((1, 1, 1, D)); q[..., 0] = math.sqrt(D)
+    k = np.zeros((1, 1, 2, D)); k[0, 0, 1, 0] = s1
+    v = np.ones((1, 1, 2, D))
+    o, T, n = A.attention(q, k, v, "int8", allowance=True)
+    assert n == 1
+    assert T[0, 0, 0, 0] == pytest.approx((1 / 127) / (1 + t), rel=1e-9)
