@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the FA-quantization hot path on one MI355X.
+
+One step = quantize Q, K and V with the workload's mode, then quantized
+attention on the codes (the whole hot path; calibration of static per-head
+scales is offline - done once before timing - as the scales are frozen).
+Inputs are seeded synthetic tensors already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
+
+prints one JSON line.  The default workload is the INT8 per-head static
+LLM-prefill case (bf16 [2,32,4096,128], causal).  `value` is attention
+operations (4*D per unmasked query-key pair) per second of the whole step,
+in TOPS.  `roofline` reports the attention call (V re-layout + fused kernel)
+against the mode's dense MFMA peak; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized-attention TFLOPS/TOPS (% MFMA peak) + quantize GB/s, 1 MI355X"
+PEAK_HBM_GBS = 8000.0
+PEAK_TOPS = {"int8_head": 5000.0, "fp8_token": 5000.0, "rot_fp8_block": 5000.0, "mxfp4": 10100.0}
+DTYPE = {"int8_head": "int8", "fp8_token": "fp8_e4m3", "rot_fp8_block": "fp8_e4m3", "mxfp4": "mxfp4"}
+MODE_TEXT = {"int8_head": "INT8 per-head static", "fp8_token": "FP8 E4M3 per-token dynamic",
+             "mxfp4": "MXFP4 per-32 block dynamic", "rot_fp8_block": "rotate + FP8 E4M3 token-block"}
+
+
+def attention_ops(shape, causal):
+    B, H, S, D = shape
+    pairs = S * (S + 1) // 2 if causal else S * S
+    return 4 * D * B * H * pairs
+
+
+def quantize_bytes(w):
+    """Algorithmic bytes of quantizing Q, K, V: input read + codes + scales."""
+    B, H, S, D = w.shape
+    n = B * H * S * D
+    inb = 4 if w.spec["dtype"] == "f32" else 2
+    mode = w.spec["mode"]
+    if mode == "int8_head":
+        return 3 * (n * inb + n + H * 4)
+    if mode == "fp8_token":
+        return 3 * (n * inb + n + B * H * S * 4)
+    if mode == "mxfp4":
+        return 3 * (n * inb + n // 2 + n // 32)
+    tot = 0
+    for bt in (w.spec["q_block"], w.spec["kv_block"], w.spec["kv_block"]):
+        tot += n * inb + n + B * H * (-(-S // bt)) * 4
+    return tot + 2 * D * D * 2
+
+
+def make_step(w, dev):
+    """Pre-allocates every output and returns (step_fn, attention_fn)."""
+    import torch
+    import quantized_attention_fa_amd as faq
+
+    mode = w.spec["mode"]
+    xs = [t.to(dev) for t in (w.q, w.k, w.v)]
+    rot = w.rot.to(dev) if w.rot is not None else None
+    cfgs, statics, outs = [], [None] * 3, []
+    for br in range(3):
+        if mode == "int8_head":
+            cfg = faq.QConfig("int8", "per_head")
+            amax = torch.zeros(w.shape[1], dtype=torch.float32, device=dev)
+            for c in w.calib[br]:
+                faq.fa_quant_calibrate(c.to(dev), amax)
+            statics[br] = faq.fa_quant_scales_from_amax(amax, "int8")
+        elif mode == "fp8_token":
+            cfg = faq.QConfig("fp8_e4m3", "per_token")
+        elif mode == "mxfp4":
+            cfg = faq.QConfig("mxfp4", "per_block")
+        else:
+            cfg = faq.QConfig("fp8_e4m3", "per_token_block",
+                              block_tokens=w.spec["q_block"] if br == 0 else w.spec["kv_block"])
+        cfgs.append(cfg)
+        qt = faq.fa_quantize(xs[br], cfg, static_scale=statics[br], rot=rot if br < 2 else None)
+        if mode == "int8_head":
+            qt.scales = statics[br]  # per-head scales are used in place
+        outs.append(qt)
+    ws = torch.empty(max(faq.fa_quant_attention_workspace_bytes(*outs), 1), dtype=torch.uint8, device=dev)
+    out = torch.empty(w.shape, dtype=torch.bfloat16, device=dev)
+
+    def quantize():
+        for br in range(3):
+            faq.fa_quantize(xs[br], cfgs[br], static_scale=statics[br], rot=rot if br < 2 else None, out=outs[br])
+
+    def attention():
+        faq.fa_quant_attention(*outs, causal=w.spec["causal"], out=out, workspace=ws)
+
+    return quantize, attention
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle (as it stands) on a bounded sample of the workload: whole
+    (b,h) heads, quantize + attention, until about `budget_s` seconds."""
+    import numpy as np
+    import torch
+    from oracle import attention as OA
+    from oracle import formats as F
+    from oracle import quantize as OQ
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    cores = len(os.sched_getaffinity(0))
+    B, H, S, D = w.shape
+    mode = w.spec["mode"]
+    causal = w.spec["causal"]
+    rule = {"int8_head": "int8", "fp8_token": "fp8", "mxfp4": "mxfp4", "rot_fp8_block": "fp8"}[mode]
+    t0 = time.perf_counter()
+    ops = 0
+    heads = 0
+    rows = None
+    # a single head can exceed the budget at long sequence lengths: sample rows
+    full_pairs = S * (S + 1) // 2 if causal else S * S
+    if full_pairs > 4096 * 4096:
+        rows = np.arange(0, S, max(1, S // 1024))
+    for h in range(H):
+        if time.perf_counter() - t0 > budget_s:
+            break
+        x = [t[0:1, h:h + 1].to(torch.float32).numpy() for t in (w.q, w.k, w.v)]
+        vs = None
+        if mode == "int8_head":
+            deq = []
+            for br in range(3):
+                amax = None
+                for c in w.calib[br]:
+                    amax = OQ.calibrate_amax(c[:, h:h + 1].to(torch.float32).numpy(), amax)
+                s = OQ.int8_scales(amax)
+                deq.append(OQ.dequantize_per_head(OQ.quantize_int8_per_head(x[br], s), s))
+        elif mode == "fp8_token":
+            deq = []
+            for br in range(3):
+                c, s = OQ.quantize_fp8_per_token(x[br])
+                deq.append(OQ.dequantize_per_token(c, s, F.e4m3_decode))
+                vs = s
+        elif mode == "mxfp4":
+            deq = [OQ.dequantize_mxfp4(*OQ.quantize_mxfp4(x[br])) for br in range(3)]
+        else:
+            R = w.rot.to(torch.float32).numpy()
+            deq = []
+            for br, bt in enumerate((w.spec["q_block"], w.spec["kv_block"], w.spec["kv_block"])):
+                y = OQ.rotate(x[br], R) if br < 2 else x[br]
+                c, s = OQ.quantize_fp8_block(y, bt)
+                st = OQ.block_scales_per_token(s, bt, S)
+                deq.append(OQ.dequantize_per_token(c, st, F.e4m3_decode))
+                vs = st
+        OA.attention(*deq, rule, v_scale=vs, causal=causal, rows=rows)
+        r = np.arange(S) if rows is None else rows
+        ops += 4 * D * int(np.sum(np.minimum(r + 1, S) if causal else np.full(r.size, S)))
+        heads += 1
+    dt = time.perf_counter() - t0
+    sample = f"{heads} of {B * H} (b,h) heads" + ("" if rows is None else f", {rows.size} of {S} query rows each")
+    sample += ", quantize + attention"
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "blas_threads": blas, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, the metric's workload)")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the hot path shards over (batch, head) with no communication - see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import make_inputs
+
+    dev = "cuda:0"
+    w = make_inputs(args.config)
+    mode = w.spec["mode"]
+    quantize, attention = make_step(w, dev)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    for _ in range(args.warmup):
+        quantize()
+        attention()
+    torch.cuda.synchronize()
+
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xff)  # evict the inputs from the caches (outside the step's events)
+        ev[i][0].record(st)
+        quantize()
+        ev[i][1].record(st)
+        attention()
+        ev[i][2].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    q_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    a_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    step_ms = [q + a for q, a in zip(q_ms, a_ms)]
+    mean = lambda v: sum(v) / len(v)
+    ms_step = mean(step_ms)
+    ops = attention_ops(w.shape, w.spec["causal"])
+    qbytes = quantize_bytes(w)
+    att_ms = mean(a_ms)
+    att_tops = ops / (att_ms * 1e-3) / 1e12
+    q_gbs = qbytes / (mean(q_ms) * 1e-3) / 1e9
+    peak = PEAK_TOPS[mode]
+    B, H, S, D = w.shape
+    line = {
+        "metric": METRIC,
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TOPS" if mode == "int8_head" else "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE[mode],
+        "data": "synthetic",
+        "config": {"workload": w.spec["name"], "mode": MODE_TEXT[mode], "B": B, "H": H, "S": S, "D": D,
+                   "causal": w.spec["causal"], "input_dtype": w.spec["dtype"]},
+        "roofline": {"bound": "mfma", "achieved": round(att_tops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(att_tops / peak, 4), "traffic": None,
+                     "kernel": "fa_quant_attention (V re-layout + fused attention)",
+                     "ops_per_launch": ops, "ms_per_launch": round(att_ms, 4)},
+        "quantize": {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(q_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": qbytes,
+                     "ms_per_step": round(mean(q_ms), 4)},
+        "timing": {"method": "hip events on the compute stream, per step", "min_step_ms": round(min(step_ms), 4),
+                   "wall_s_incl_flush": round(wall, 3), "cache_flush_between_steps": flush is not None},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

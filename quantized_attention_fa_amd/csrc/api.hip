@@ -1,0 +1,252 @@
+// C ABI entry points: argument validation (host only, before any HIP call),
+// size queries and kernel dispatch.
+
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "launch.h"
+
+using namespace faq;
+
+namespace {
+
+bool log_enabled() {
+  static const int on = [] {
+    const char* e = getenv("FAQ_LOG");
+    return (e && *e && *e != '0') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+faq_status fail(faq_status st, const char* fn, const char* why) {
+  if (log_enabled()) fprintf(stderr, "[faquant] %s: %s (%s)\n", fn, why, fa_quant_status_string(st));
+  return st;
+}
+
+faq_status hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return FAQ_OK;
+  if (log_enabled()) fprintf(stderr, "[faquant] %s: HIP error %s\n", fn, hipGetErrorString(e));
+  return FAQ_ERR_HIP;
+}
+
+bool shape_ok(const faq_shape* s) {
+  return s && s->B >= 0 && s->H >= 0 && s->S >= 0 && s->D >= 0;
+}
+
+bool d_supported(int64_t D) { return D == 64 || D == 128; }
+
+int64_t numel(const faq_shape& s) { return s.B * s.H * s.S * s.D; }
+
+bool same_shape(const faq_shape& a, const faq_shape& b) {
+  return a.B == b.B && a.H == b.H && a.S == b.S && a.D == b.D;
+}
+
+bool same_cfg(const faq_qconfig& a, const faq_qconfig& b) {
+  return a.dtype == b.dtype && a.scope == b.scope && a.symmetric == b.symmetric &&
+         a.method == b.method && (a.scope != FAQ_PER_TOKEN_BLOCK || a.block_tokens == b.block_tokens);
+}
+
+// The (dtype, scope) pairs of the FA combinations implemented here.
+faq_status check_cfg(const faq_qconfig* c) {
+  if (!c) return FAQ_ERR_INVALID_ARG;
+  if (c->dtype < FAQ_FLOAT || c->dtype > FAQ_MXFP4) return FAQ_ERR_INVALID_ARG;
+  if (c->scope < FAQ_PER_HEAD || c->scope > FAQ_PER_TOKEN_BLOCK) return FAQ_ERR_INVALID_ARG;
+  if (c->symmetric != 1 || c->method != 0) return FAQ_ERR_UNSUPPORTED;
+  if (c->dtype == FAQ_INT8 && c->scope == FAQ_PER_HEAD) return FAQ_OK;
+  if (c->dtype == FAQ_FP8_E4M3 && c->scope == FAQ_PER_TOKEN) return FAQ_OK;
+  if (c->dtype == FAQ_MXFP4 && c->scope == FAQ_PER_BLOCK) return FAQ_OK;
+  if (c->dtype == FAQ_FP8_E4M3 && c->scope == FAQ_PER_TOKEN_BLOCK) {
+    if (c->block_tokens == 128 || c->block_tokens == 256) return FAQ_OK;
+    return c->block_tokens > 0 ? FAQ_ERR_UNSUPPORTED : FAQ_ERR_INVALID_ARG;
+  }
+  return FAQ_ERR_UNSUPPORTED;
+}
+
+size_t codes_bytes(const faq_qconfig& c, const faq_shape& s) {
+  const size_t n = (size_t)numel(s);
+  return c.dtype == FAQ_MXFP4 ? n / 2 : n;
+}
+
+size_t scales_bytes(const faq_qconfig& c, const faq_shape& s) {
+  switch (c.scope) {
+    case FAQ_PER_HEAD: return (size_t)s.H * 4;
+    case FAQ_PER_TOKEN: return (size_t)(s.B * s.H * s.S) * 4;
+    case FAQ_PER_BLOCK: return (size_t)(s.B * s.H * s.S) * (size_t)(s.D / 32);
+    default: return (size_t)(s.B * s.H * ((s.S + c.block_tokens - 1) / c.block_tokens)) * 4;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_quant_status_string(int32_t st) {
+  switch (st) {
+    case FAQ_OK: return "ok";
+    case FAQ_ERR_INVALID_ARG: return "invalid argument";
+    case FAQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FAQ_ERR_CONFIG_CONFLICT: return "qconfig and details are mutually exclusive";
+    case FAQ_ERR_NOT_CALIBRATED: return "static per-head quantization needs calibrated scales";
+    case FAQ_ERR_SHAPE: return "inconsistent shapes";
+    case FAQ_ERR_HIP: return "HIP runtime error";
+    case FAQ_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t fa_quant_codes_bytes(const faq_qconfig* cfg, const faq_shape* shape) {
+  if (check_cfg(cfg) != FAQ_OK || !shape_ok(shape) || !d_supported(shape->D)) return 0;
+  return codes_bytes(*cfg, *shape);
+}
+
+size_t fa_quant_scales_bytes(const faq_qconfig* cfg, const faq_shape* shape) {
+  if (check_cfg(cfg) != FAQ_OK || !shape_ok(shape) || !d_supported(shape->D)) return 0;
+  return scales_bytes(*cfg, *shape);
+}
+
+faq_status fa_quant_calibrate(const void* x, int32_t x_dtype, const faq_shape* shape, float* amax,
+                              void* stream) {
+  static const char* fn = "fa_quant_calibrate";
+  if (!shape_ok(shape)) return fail(FAQ_ERR_INVALID_ARG, fn, "shape");
+  if (x_dtype != FAQ_T_F32 && x_dtype != FAQ_T_BF16) return fail(FAQ_ERR_INVALID_ARG, fn, "x_dtype");
+  if (!d_supported(shape->D)) return fail(FAQ_ERR_UNSUPPORTED, fn, "head_dim must be 64 or 128");
+  if (shape->H > 0 && !amax) return fail(FAQ_ERR_INVALID_ARG, fn, "amax is NULL");
+  if (numel(*shape) == 0) return FAQ_OK;
+  if (!x) return fail(FAQ_ERR_INVALID_ARG, fn, "x is NULL");
+  return hip_status(launch_calibrate(x, x_dtype, *shape, amax, (hipStream_t)stream), fn);
+}
+
+faq_status fa_quant_scales_from_amax(const float* amax, int64_t H, int32_t dtype, float* scale,
+                                     void* stream) {
+  static const char* fn = "fa_quant_scales_from_amax";
+  if (H < 0) return fail(FAQ_ERR_INVALID_ARG, fn, "H < 0");
+  float qmax;
+  if (dtype == FAQ_INT8) qmax = 127.0f;
+  else if (dtype == FAQ_FP8_E4M3) qmax = 448.0f;
+  else return fail(FAQ_ERR_UNSUPPORTED, fn, "dtype has no per-head static scale");
+  if (H == 0) return FAQ_OK;
+  if (!amax || !scale) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL pointer");
+  return hip_status(launch_scales_from_amax(amax, H, qmax, scale, (hipStream_t)stream), fn);
+}
+
+faq_status fa_quantize(const void* x, int32_t x_dtype, const faq_shape* shape, const faq_qconfig* cfg,
+                       const float* static_scale, const void* rot, faq_qtensor* out,
+                       void* debug_rotated, void* stream) {
+  static const char* fn = "fa_quantize";
+  if (!shape_ok(shape)) return fail(FAQ_ERR_INVALID_ARG, fn, "shape");
+  if (x_dtype != FAQ_T_F32 && x_dtype != FAQ_T_BF16) return fail(FAQ_ERR_INVALID_ARG, fn, "x_dtype");
+  const faq_status cs = check_cfg(cfg);
+  if (cs != FAQ_OK) return fail(cs, fn, "qconfig");
+  if (!d_supported(shape->D)) return fail(FAQ_ERR_UNSUPPORTED, fn, "head_dim must be 64 or 128");
+  if (!out) return fail(FAQ_ERR_INVALID_ARG, fn, "out is NULL");
+  if (!same_cfg(out->cfg, *cfg)) return fail(FAQ_ERR_INVALID_ARG, fn, "out->cfg differs from cfg");
+  if (!same_shape(out->shape, *shape)) return fail(FAQ_ERR_SHAPE, fn, "out->shape differs from shape");
+  const bool per_head = cfg->scope == FAQ_PER_HEAD;
+  const bool tok_block = cfg->scope == FAQ_PER_TOKEN_BLOCK;
+  if (per_head && !static_scale) return fail(FAQ_ERR_NOT_CALIBRATED, fn, "per-head scales missing");
+  if (!per_head && static_scale) return fail(FAQ_ERR_INVALID_ARG, fn, "static_scale given for a dynamic scope");
+  if (rot && !tok_block) return fail(FAQ_ERR_UNSUPPORTED, fn, "rotation needs the token-block scope");
+  if (debug_rotated && !rot) return fail(FAQ_ERR_INVALID_ARG, fn, "debug_rotated without rot");
+  if (tok_block && x_dtype != FAQ_T_BF16) return fail(FAQ_ERR_UNSUPPORTED, fn, "token-block path needs bf16 input");
+  if (numel(*shape) == 0) {
+    if (per_head && shape->H > 0 && out->scales != static_scale) {
+      if (!out->scales) return fail(FAQ_ERR_INVALID_ARG, fn, "out->scales is NULL");
+      return hip_status(hipMemcpyAsync(out->scales, static_scale, (size_t)shape->H * 4,
+                                       hipMemcpyDeviceToDevice, (hipStream_t)stream), fn);
+    }
+    return FAQ_OK;
+  }
+  if (!x || !out->codes || !out->scales) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL pointer");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  switch (cfg->dtype) {
+    case FAQ_INT8:
+      e = launch_quant_int8_head(x, x_dtype, *shape, static_scale, (int8_t*)out->codes, st);
+      if (e == hipSuccess && out->scales != static_scale)
+        e = hipMemcpyAsync(out->scales, static_scale, (size_t)shape->H * 4, hipMemcpyDeviceToDevice, st);
+      break;
+    case FAQ_FP8_E4M3:
+      if (tok_block) {
+        if (rot)
+          e = launch_rot_fp8_block((const uint16_t*)x, (const uint16_t*)rot, *shape, cfg->block_tokens,
+                                   (uint8_t*)out->codes, (float*)out->scales, (uint16_t*)debug_rotated, st);
+        else
+          e = launch_quant_fp8_block((const uint16_t*)x, *shape, cfg->block_tokens, (uint8_t*)out->codes,
+                                     (float*)out->scales, st);
+      } else {
+        e = launch_quant_fp8_token(x, x_dtype, *shape, (uint8_t*)out->codes, (float*)out->scales, st);
+      }
+      break;
+    default:
+      e = launch_quant_mxfp4(x, x_dtype, *shape, (uint8_t*)out->codes, (uint8_t*)out->scales, st);
+      break;
+  }
+  return hip_status(e, fn);
+}
+
+static faq_status attn_check(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
+                             int* mode, const char* fn) {
+  if (!q || !k || !v) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL tensor");
+  for (const faq_qtensor* t : {q, k, v}) {
+    const faq_status cs = check_cfg(&t->cfg);
+    if (cs != FAQ_OK) return fail(cs, fn, "qconfig");
+    if (!shape_ok(&t->shape)) return fail(FAQ_ERR_INVALID_ARG, fn, "shape");
+    if (!d_supported(t->shape.D)) return fail(FAQ_ERR_UNSUPPORTED, fn, "head_dim must be 64 or 128");
+  }
+  if (q->cfg.dtype != k->cfg.dtype || q->cfg.dtype != v->cfg.dtype || q->cfg.scope != k->cfg.scope ||
+      q->cfg.scope != v->cfg.scope)
+    return fail(FAQ_ERR_UNSUPPORTED, fn, "q, k and v must share one (dtype, scope)");
+  if (q->cfg.scope == FAQ_PER_TOKEN_BLOCK && k->cfg.block_tokens != v->cfg.block_tokens)
+    return fail(FAQ_ERR_UNSUPPORTED, fn, "k and v must share one block size");
+  if (q->shape.B != k->shape.B || q->shape.B != v->shape.B || q->shape.H != k->shape.H ||
+      q->shape.H != v->shape.H || q->shape.D != k->shape.D || q->shape.D != v->shape.D ||
+      k->shape.S != v->shape.S)
+    return fail(FAQ_ERR_SHAPE, fn, "q/k/v shapes");
+  *mode = q->cfg.dtype == FAQ_INT8 ? ATTN_INT8 : q->cfg.dtype == FAQ_MXFP4 ? ATTN_MX : ATTN_FP8;
+  return FAQ_OK;
+}
+
+size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtensor* k,
+                                          const faq_qtensor* v) {
+  int mode;
+  if (attn_check(q, k, v, &mode, "fa_quant_attention_workspace_bytes") != FAQ_OK) return 0;
+  return attn_workspace_bytes(mode, k->shape.B, k->shape.H, k->shape.S, k->shape.D);
+}
+
+faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
+                              float sm_scale, int32_t causal, void* out, int32_t out_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "fa_quant_attention";
+  int mode;
+  const faq_status cs = attn_check(q, k, v, &mode, fn);
+  if (cs != FAQ_OK) return cs;
+  if (out_dtype != FAQ_T_F32 && out_dtype != FAQ_T_BF16) return fail(FAQ_ERR_INVALID_ARG, fn, "out_dtype");
+  if (causal != 0 && causal != 1) return fail(FAQ_ERR_INVALID_ARG, fn, "causal must be 0 or 1");
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return fail(FAQ_ERR_INVALID_ARG, fn, "sm_scale");
+  if (causal && q->shape.S != k->shape.S) return fail(FAQ_ERR_SHAPE, fn, "causal needs Sq == Skv");
+  const int64_t B = q->shape.B, H = q->shape.H, Sq = q->shape.S, Skv = k->shape.S, D = q->shape.D;
+  if (B * H * Sq == 0) return FAQ_OK;
+  if (Skv == 0) return fail(FAQ_ERR_SHAPE, fn, "no keys");
+  if (!out || !q->codes || !q->scales || !k->codes || !k->scales || !v->codes || !v->scales)
+    return fail(FAQ_ERR_INVALID_ARG, fn, "NULL pointer");
+  const size_t need = attn_workspace_bytes(mode, B, H, Skv, D);
+  if (workspace_bytes < need || !workspace) return fail(FAQ_ERR_WORKSPACE, fn, "workspace");
+  AttnArgs a{};
+  a.mode = mode;
+  a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv; a.D = D;
+  a.q_codes = q->codes; a.q_scales = q->scales;
+  a.k_codes = k->codes; a.k_scales = k->scales;
+  a.v_codes = v->codes; a.v_scales = v->scales;
+  const bool blk = q->cfg.scope == FAQ_PER_TOKEN_BLOCK;
+  a.q_block = blk ? q->cfg.block_tokens : 1;
+  a.kv_block = blk ? k->cfg.block_tokens : 1;
+  a.sm_scale = sm_scale == 0.0f ? 1.0f / sqrtf((float)D) : sm_scale;
+  a.causal = causal;
+  a.out = out;
+  a.out_bf16 = out_dtype == FAQ_T_BF16;
+  a.ws = workspace;
+  return hip_status(launch_attention(a, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

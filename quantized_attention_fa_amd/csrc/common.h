@@ -1,0 +1,128 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16
+// access, bit-exact format encoders, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+#define FAQ_DEV static __device__ __forceinline__
+
+// ---------------------------------------------------------------- bf16 / fp32
+
+FAQ_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+FAQ_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round a finite float to bf16 (nearest, ties to even); returns the bits.
+FAQ_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Load 8 consecutive input elements (fp32, or bf16 held as uint16_t) as floats.
+FAQ_DEV void load8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+FAQ_DEV void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x);
+  v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+  v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z);
+  v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+}
+
+// ---------------------------------------------------------------- encoders
+//
+// Every encoder takes the already-divided float32 quotient u = fl32(x / s)
+// and rounds it to the nearest code, ties to the even code.
+
+// INT8: clamp(round_half_even(u), -128, 127).
+FAQ_DEV int32_t enc_int8(float u) {
+  float r = __builtin_rintf(u);
+  r = fminf(fmaxf(r, -128.0f), 127.0f);
+  return (int32_t)r;
+}
+
+// FP8 E4M3FN (bias 7, 3 mantissa bits, no inf, S.1111.111 = NaN): nearest
+// value, ties to even mantissa, |u| > 448 saturating to 0x7E, sign kept.
+FAQ_DEV uint32_t enc_e4m3(float u) {
+  const uint32_t b = __float_as_uint(u);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  // normal range (|u| >= 2^-6): drop 20 mantissa bits with round-half-even,
+  // then rebias the exponent from 127 to 7.
+  uint32_t rn = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  uint32_t cn = rn - (120u << 3);
+  cn = cn > 0x7eu ? 0x7eu : cn;
+  // subnormal range: k * 2^-9 with k = round_half_even(|u| * 2^9) in 0..8
+  // (k = 8 is the smallest normal, code 0x08).
+  uint32_t cs = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  return sign | (a >= 0x3c800000u ? cn : cs);
+}
+
+// FP8 E5M2 (bias 15, 2 mantissa bits) of a non-negative-or-signed value that
+// is at most 6 in magnitude (no saturation needed): nearest, ties to even.
+FAQ_DEV uint32_t enc_e5m2_small(float u) {
+  const uint32_t b = __float_as_uint(u);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  uint32_t rn = (a + 0xfffffu + ((a >> 21) & 1u)) >> 21;
+  uint32_t cn = rn - (112u << 2);
+  // subnormal: k * 2^-16, k = round_half_even(|u| * 2^16) in 0..4
+  uint32_t cs = (uint32_t)__builtin_rintf(__uint_as_float(a) * 65536.0f);
+  return sign | (a >= 0x38800000u ? cn : cs);
+}
+
+// E2M1 magnitude code of |v| (0..7 for 0, .5, 1, 1.5, 2, 3, 4, 6): nearest,
+// ties to even code, saturating at 6.
+FAQ_DEV uint32_t enc_e2m1_mag(float a) {
+  uint32_t c = 0;
+  c += a > 0.25f;
+  c += a >= 0.75f;
+  c += a > 1.25f;
+  c += a >= 1.75f;
+  c += a > 2.5f;
+  c += a >= 3.5f;
+  c += a > 5.0f;
+  return c;
+}
+
+FAQ_DEV uint32_t enc_e2m1(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
+  return sign | enc_e2m1_mag(fabsf(v));
+}
+
+// Shared MX exponent E = clamp(floor(log2 amax) - 2, -127, 127), exact from
+// the float's exponent bits; zero or subnormal amax gives -127.
+FAQ_DEV int mx_exponent(float amax) {
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  int E = e - 129;
+  E = E < -127 ? -127 : E;
+  E = E > 127 ? 127 : E;
+  return e == 0 ? -127 : E;
+}
+
+// ---------------------------------------------------------------- reductions
+
+template <int WIDTH>
+FAQ_DEV float group_max(float v) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+FAQ_DEV float wave_max(float v) { return group_max<64>(v); }
+
+// ---------------------------------------------------------------- misc
+
+FAQ_DEV float scale_from_amax(float amax, float qmax) {
+  return amax == 0.0f ? 1.0f : amax / qmax;  // IEEE division
+}

@@ -1,0 +1,166 @@
+// Test-only probes (built into a separate library, never into libfaquant):
+// single-instruction kernels that pin the lane layout of the MFMA operands
+// and scales, and the rounding of the hardware conversion instructions,
+// against CPU references in the test suite.  Every kernel runs one wave on
+// fixed-size buffers.
+
+#include "common.h"
+
+namespace {
+
+// C[16][16] = A[16][64] . Bt[16][64]^T with v_mfma_i32_16x16x64_i8.
+// Assumed layout: lane (i = l%16, g = l/16) holds A[i][16g .. 16g+15] and
+// Bt[i][16g .. 16g+15]; C[4g + r][i] lands in accumulator r.
+__global__ void k_probe_i8(const int8_t* A, const int8_t* Bt, int32_t* C) {
+  const int l = threadIdx.x, i = l & 15, g = l >> 4;
+  const uint4 a = *reinterpret_cast<const uint4*>(A + i * 64 + 16 * g);
+  const uint4 b = *reinterpret_cast<const uint4*>(Bt + i * 64 + 16 * g);
+  const i32x4 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+  const i32x4 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  const i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, i32x4{0, 0, 0, 0}, 0, 0, 0);
+  for (int r = 0; r < 4; ++r) C[(4 * g + r) * 16 + i] = c[r];
+}
+
+// C = A[16][128] . Bt[16][128]^T with the f8f6f4 MFMA; element formats fa, fb
+// (0 E4M3, 1 E5M2, 4 E2M1); row bytes 128 (8-bit) or 64 (4-bit).  Scales
+// (E8M0 bytes) sa[i][g], sb[i][g] for row i and 32-element block g when
+// `scaled`; lane (i, g) holds elements 32g..32g+31 of its row.
+template <int FA, int FB>
+__global__ void k_probe_f8f6f4(const uint8_t* A, const uint8_t* Bt, const uint8_t* sa,
+                               const uint8_t* sb, int scaled, float* C) {
+  const int l = threadIdx.x, i = l & 15, g = l >> 4;
+  constexpr int RA = FA == 4 ? 64 : 128, RB = FB == 4 ? 64 : 128;
+  i32x8 av = {0, 0, 0, 0, 0, 0, 0, 0}, bv = {0, 0, 0, 0, 0, 0, 0, 0};
+  {
+    const uint4* p = reinterpret_cast<const uint4*>(A + i * RA + g * (RA / 4));
+    const uint4 x = p[0];
+    av[0] = x.x; av[1] = x.y; av[2] = x.z; av[3] = x.w;
+    if (FA != 4) { const uint4 y = p[1]; av[4] = y.x; av[5] = y.y; av[6] = y.z; av[7] = y.w; }
+  }
+  {
+    const uint4* p = reinterpret_cast<const uint4*>(Bt + i * RB + g * (RB / 4));
+    const uint4 x = p[0];
+    bv[0] = x.x; bv[1] = x.y; bv[2] = x.z; bv[3] = x.w;
+    if (FB != 4) { const uint4 y = p[1]; bv[4] = y.x; bv[5] = y.y; bv[6] = y.z; bv[7] = y.w; }
+  }
+  f32x4 c;
+  if (scaled) {
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, FA, FB, 0,
+                                                         (int)sa[i * 4 + g], 0, (int)sb[i * 4 + g]);
+  } else {
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, FA, FB, 0, 0,
+                                                         0, 0);
+  }
+  for (int r = 0; r < 4; ++r) C[(4 * g + r) * 16 + i] = c[r];
+}
+
+// C = A[16][32] . Bt[16][32]^T with v_mfma_f32_16x16x32_bf16; lane (i, g)
+// holds elements 8g..8g+7.
+__global__ void k_probe_bf16(const uint16_t* A, const uint16_t* Bt, float* C) {
+  const int l = threadIdx.x, i = l & 15, g = l >> 4;
+  const uint4 a = *reinterpret_cast<const uint4*>(A + i * 32 + 8 * g);
+  const uint4 b = *reinterpret_cast<const uint4*>(Bt + i * 32 + 8 * g);
+  const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, b),
+                                                          f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  for (int r = 0; r < 4; ++r) C[(4 * g + r) * 16 + i] = c[r];
+}
+
+// Conversions of n floats (n even): hardware E4M3 / E5M2 packs, the
+// hardware scaled FP4 pack (with scale `fp4_scale`), and the software E4M3
+// encoder, one output byte (or nibble byte) per input.
+__global__ void k_probe_cvt(const float* x, int n, float fp4_scale, uint8_t* hw_e4m3, uint8_t* hw_e5m2,
+                            uint8_t* hw_fp4, uint8_t* sw_e4m3) {
+  const int i = 2 * ((int)(blockIdx.x * blockDim.x + threadIdx.x));
+  if (i + 1 >= n + 1) return;
+  const float a = x[i], b = (i + 1 < n) ? x[i + 1] : 0.0f;
+  const int e4 = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  const int e5 = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  const unsigned f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, fp4_scale, 0);
+  hw_e4m3[i] = (uint8_t)(e4 & 0xff);
+  hw_e5m2[i] = (uint8_t)(e5 & 0xff);
+  hw_fp4[i] = (uint8_t)(f4 & 0xf);
+  sw_e4m3[i] = (uint8_t)enc_e4m3(a);
+  if (i + 1 < n) {
+    hw_e4m3[i + 1] = (uint8_t)((e4 >> 8) & 0xff);
+    hw_e5m2[i + 1] = (uint8_t)((e5 >> 8) & 0xff);
+    hw_fp4[i + 1] = (uint8_t)((f4 >> 4) & 0xf);
+    sw_e4m3[i + 1] = (uint8_t)enc_e4m3(b);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int faq_probe_mfma_i8(const int8_t* A, const int8_t* Bt, int32_t* C) {
+  k_probe_i8<<<1, 64>>>(A, Bt, C);
+  return (int)hipDeviceSynchronize();
+}
+
+int faq_probe_mfma_f8f6f4(const uint8_t* A, const uint8_t* Bt, const uint8_t* sa, const uint8_t* sb,
+                          int fa, int fb, int scaled, float* C) {
+#define FAQ_PROBE_CASE(X, Y)                                        \
+  if (fa == X && fb == Y) {                                         \
+    k_probe_f8f6f4<X, Y><<<1, 64>>>(A, Bt, sa, sb, scaled, C);      \
+    return (int)hipDeviceSynchronize();                             \
+  }
+  FAQ_PROBE_CASE(0, 0)
+  FAQ_PROBE_CASE(1, 1)
+  FAQ_PROBE_CASE(4, 4)
+  FAQ_PROBE_CASE(1, 4)
+  FAQ_PROBE_CASE(0, 4)
+#undef FAQ_PROBE_CASE
+  return -1;
+}
+
+int faq_probe_mfma_bf16(const uint16_t* A, const uint16_t* Bt, float* C) {
+  k_probe_bf16<<<1, 64>>>(A, Bt, C);
+  return (int)hipDeviceSynchronize();
+}
+
+int faq_probe_cvt(const float* x, int n, float fp4_scale, uint8_t* hw_e4m3, uint8_t* hw_e5m2,
+                  uint8_t* hw_fp4, uint8_t* sw_e4m3) {
+  const int pairs = (n + 1) / 2;
+  k_probe_cvt<<<(pairs + 255) / 256, 256>>>(x, n, fp4_scale, hw_e4m3, hw_e5m2, hw_fp4, sw_e4m3);
+  return (int)hipDeviceSynchronize();
+}
+
+}  // extern "C"
+
+namespace {
+// C = A[16][32] . Bt[16][32]^T with the 16x16x32 fp8 MFMA (E4M3 x E4M3);
+// lane (i, g) holds bytes 8g..8g+7 of its row.
+__global__ void k_probe_fp8_k32(const uint8_t* A, const uint8_t* Bt, float* C) {
+  const int l = threadIdx.x, i = l & 15, g = l >> 4;
+  const long a = *reinterpret_cast<const long*>(A + i * 32 + 8 * g);
+  const long b = *reinterpret_cast<const long*>(Bt + i * 32 + 8 * g);
+  const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  for (int r = 0; r < 4; ++r) C[(4 * g + r) * 16 + i] = c[r];
+}
+}  // namespace
+
+extern "C" int faq_probe_mfma_fp8_k32(const uint8_t* A, const uint8_t* Bt, float* C) {
+  k_probe_fp8_k32<<<1, 64>>>(A, Bt, C);
+  return (int)hipDeviceSynchronize();
+}
+
+namespace {
+// Up-conversions used by the attention kernels, one input word per thread:
+// bf16 pairs of the two low / two high E4M3 bytes (scale 1), and the bf16
+// pair of the two low E2M1 nibbles times `fp4_scale`.
+__global__ void k_probe_cvt_up(const uint32_t* w, int n, float fp4_scale, uint32_t* e4_lo, uint32_t* e4_hi,
+                               uint32_t* f4) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  e4_lo[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, false));
+  e4_hi[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, true));
+  f4[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], fp4_scale, 0));
+}
+}  // namespace
+
+extern "C" int faq_probe_cvt_up(const uint32_t* w, int n, float fp4_scale, uint32_t* e4_lo, uint32_t* e4_hi,
+                                uint32_t* f4) {
+  k_probe_cvt_up<<<(n + 255) / 256, 256>>>(w, n, fp4_scale, e4_lo, e4_hi, f4);
+  return (int)hipDeviceSynchronize();
+}

@@ -1,0 +1,478 @@
+// Q/K/V quantization kernels for gfx950.
+//
+// All of them are HBM-bound streaming kernels: 16-byte loads and stores,
+// several loads in flight per thread before any arithmetic, reductions
+// across lanes with shuffles.  The arithmetic is bit-exact with respect to
+// the formats' definitions:
+//   scale = fl32(amax / qmax) (IEEE division; amax == 0 -> 1),
+//   u     = fl32(x / scale)   (IEEE division),
+//   code  = nearest code to u, ties to even, saturating.
+// Formats and granularities follow the msModelSlim "FA 量化" page
+// (分支组合, 组合 1-3) and the MindIE SD "量化" page (FA量化 / 技术特点).
+
+#include "common.h"
+#include "launch.h"
+
+namespace faq {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------------------
+// Min-max calibration: amax[h] = max(amax[h], max |x[b,h,:,:]|).
+// grid = (chunks per (b,h) slice, B*H); the float bits of a non-negative
+// value order like unsigned integers, so the running max is an atomicMax.
+// ------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_calibrate(const T* __restrict__ x, int64_t per_bh,
+                                                        int H, float* __restrict__ amax) {
+  constexpr int U = 4;
+  const int64_t bh = blockIdx.y;
+  const T* base = x + bh * per_bh;
+  float m = 0.0f;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * 8 * U; c0 < per_bh;
+       c0 += (int64_t)gridDim.x * kThreads * 8 * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = c0 + ((int64_t)u * kThreads + threadIdx.x) * 8;
+      if (i < per_bh) {
+        load8(base + i, v[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
+  }
+  m = wave_max(m);
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax + (bh % H)), __float_as_uint(m));
+  }
+}
+
+__global__ void k_scales_from_amax(const float* amax, int64_t H, float qmax, float* scale) {
+  const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (h < H) scale[h] = scale_from_amax(amax[h], qmax);
+}
+
+// ------------------------------------------------------------------------
+// INT8 per-head static: code = clamp(rne(x / scale[h]), -128, 127).
+// grid = (chunks per (b,h) slice, B*H); 16 elements per thread-vector.
+// ------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_quant_int8_head(const T* __restrict__ x,
+                                                              const float* __restrict__ scale,
+                                                              int64_t per_bh, int H,
+                                                              int8_t* __restrict__ codes) {
+  constexpr int U = 2;
+  const int64_t bh = blockIdx.y;
+  const float s = scale[bh % H];
+  const T* src = x + bh * per_bh;
+  int8_t* dst = codes + bh * per_bh;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * 16 * U; c0 < per_bh;
+       c0 += (int64_t)gridDim.x * kThreads * 16 * U) {
+    float v[U][16];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = c0 + ((int64_t)u * kThreads + threadIdx.x) * 16;
+      if (i < per_bh) {
+        float a[8], b[8];
+        load8(src + i, a);
+        load8(src + i + 8, b);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { v[u][k] = a[k]; v[u][8 + k] = b[k]; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = c0 + ((int64_t)u * kThreads + threadIdx.x) * 16;
+      if (i < per_bh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t acc = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            acc |= ((uint32_t)enc_int8(v[u][4 * j + k] / s) & 0xffu) << (8 * k);
+          w[j] = acc;
+        }
+        *reinterpret_cast<uint4*>(dst + i) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// FP8 E4M3 per-token: one scale per (b,h,s) row of D elements.
+// D/8 threads per row, 8 elements per thread.
+// ------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_quant_fp8_token(const T* __restrict__ x, int64_t rows,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scales) {
+  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 4;
+  const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = r0 + u * RPB + rin;
+      if (row < rows) {
+        load8(x + row * D + sub * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = r0 + u * RPB + rin;
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
+      m = group_max<TPR>(m);
+      const float s = scale_from_amax(m, 448.0f);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lo |= enc_e4m3(v[u][k] / s) << (8 * k);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) hi |= enc_e4m3(v[u][4 + k] / s) << (8 * k);
+      if (row < rows) {
+        *reinterpret_cast<uint2*>(codes + row * D + sub * 8) = make_uint2(lo, hi);
+        if (sub == 0) scales[row] = s;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// MXFP4 per-block: 32 consecutive elements along D share an E8M0 exponent.
+// D/8 threads per row; 4 threads per 32-element block.
+// ------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ x, int64_t rows,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ e8m0) {
+  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 4, NB = D / 32;
+  const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
+  const int lane = threadIdx.x & 63;
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = r0 + u * RPB + rin;
+      if (row < rows) {
+        load8(x + row * D + sub * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = r0 + u * RPB + rin;
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
+      m = group_max<4>(m);
+      const int E = mx_exponent(m);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        packed |= enc_e2m1(__builtin_amdgcn_ldexpf(v[u][k], -E)) << (4 * k);
+      // gather the row's NB exponent bytes into the row's first lane
+      uint32_t eb = (uint32_t)(E + 127);
+      uint32_t word = eb;
+#pragma unroll
+      for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
+      if (row < rows) {
+        *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + sub * 4) = packed;
+        if (sub == 0) {
+          if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + row * NB) = word;
+          else *reinterpret_cast<uint16_t*>(e8m0 + row * NB) = (uint16_t)word;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// FP8 E4M3 token-block quantization without rotation (the V branch of the
+// rotate path): one scale per (b,h, BT tokens x D).  bf16 input.
+// One workgroup per block; the block stays in registers between the amax
+// reduction and the encode.
+// ------------------------------------------------------------------------
+template <int D, int BT>
+__global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __restrict__ x,
+                                                              int64_t S, int nblk,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scales) {
+  constexpr int NV = BT * D / (kThreads * 8);
+  const int64_t bh = blockIdx.y;
+  const int blk = blockIdx.x;
+  const int64_t tok0 = (int64_t)blk * BT;
+  const int64_t ntok = (S - tok0) < BT ? (S - tok0) : BT;
+  const uint16_t* src = x + (bh * S + tok0) * D;
+  uint8_t* dst = codes + (bh * S + tok0) * D;
+  uint4 raw[NV];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = (i * kThreads + threadIdx.x) * 8;
+    raw[i] = (e / D < ntok) ? *reinterpret_cast<const uint4*>(src + e) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+  }
+  m = wave_max(m);
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = scale_from_amax(m, 448.0f);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = (i * kThreads + threadIdx.x) * 8;
+    if (e / D < ntok) {
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        lo |= enc_e4m3(bf16_lo(w[j]) / s) << (16 * j);
+        lo |= enc_e4m3(bf16_hi(w[j]) / s) << (16 * j + 8);
+        hi |= enc_e4m3(bf16_lo(w[2 + j]) / s) << (16 * j);
+        hi |= enc_e4m3(bf16_hi(w[2 + j]) / s) << (16 * j + 8);
+      }
+      *reinterpret_cast<uint2*>(dst + e) = make_uint2(lo, hi);
+    }
+  }
+  if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
+}
+
+// ------------------------------------------------------------------------
+// Rotation + FP8 token-block quantization (Q and K of the rotate path):
+//   Y = bf16_rne(X . R),  then per (b,h, BT tokens): s = fl32(amax|Y| / 448),
+//   code = E4M3(fl32(Y / s)).
+// Y^T = R^T X^T on the bf16 MFMA (16x16x32, fp32 accumulate): the A operand
+// is R^T from LDS (staged once per workgroup; the workgroup then walks
+// blocks in a grid-stride loop), the B operand is X read straight from
+// global memory (each lane's 8 bf16 are contiguous in a token row).  The
+// accumulator holds, per lane, 4 consecutive output channels of one token.
+// One wave per 32 tokens: BT/32 waves per workgroup.
+// ------------------------------------------------------------------------
+template <int D, int BT>
+__global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ rot,
+                                                          int64_t S, int nblk, int64_t nwork,
+                                                          uint8_t* __restrict__ codes,
+                                                          float* __restrict__ scales,
+                                                          uint16_t* __restrict__ dbg) {
+  constexpr int NW = BT / 32, NT = BT * 2, KK = D / 32, DB = D / 16, RS = D + 8;
+  __shared__ uint16_t rt[D * RS];  // R^T, one padded row per output channel
+  __shared__ float red[NW];
+  for (int i = threadIdx.x; i < D * D; i += NT) {
+    const int k = i / D, n = i % D;
+    rt[n * RS + k] = rot[i];
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  for (int64_t work = blockIdx.x; work < nwork; work += gridDim.x) {
+    const int64_t bh = work / nblk;
+    const int blk = (int)(work % nblk);
+    const int64_t tok0 = (int64_t)blk * BT + w * 32;
+    const uint16_t* src = x + bh * S * D;
+    bf16x8 xb[2][KK];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t tok = tok0 + tb * 16 + l16;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        uint4 r = make_uint4(0, 0, 0, 0);
+        if (tok < S) r = *reinterpret_cast<const uint4*>(src + tok * D + kk * 32 + g * 8);
+        xb[tb][kk] = __builtin_bit_cast(bf16x8, r);
+      }
+    }
+    f32x4 acc[2][DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(&rt[(db * 16 + l16) * RS + kk * 32 + g * 8]);
+        acc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[0][kk], acc[0][db], 0, 0, 0);
+        acc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[1][kk], acc[1][db], 0, 0, 0);
+      }
+    }
+    // round to bf16 (the rotated tensor is bf16), block max
+    float m = 0.0f;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float y = __uint_as_float(f32_to_bf16_bits(acc[tb][db][r]) << 16);
+          acc[tb][db][r] = y;
+          m = fmaxf(m, fabsf(y));
+        }
+    m = wave_max(m);
+    if (lane == 0) red[w] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
+    __syncthreads();  // red is rewritten by the next block
+    const float s = scale_from_amax(m, 448.0f);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t tok = tok0 + tb * 16 + l16;
+      if (tok >= S) continue;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c |= enc_e4m3(acc[tb][db][r] / s) << (8 * r);
+        const int64_t off = (bh * S + tok) * D + db * 16 + g * 4;
+        *reinterpret_cast<uint32_t*>(codes + off) = c;
+        if (dbg) {
+          const uint32_t b0 = f32_to_bf16_bits(acc[tb][db][0]) | (f32_to_bf16_bits(acc[tb][db][1]) << 16);
+          const uint32_t b1 = f32_to_bf16_bits(acc[tb][db][2]) | (f32_to_bf16_bits(acc[tb][db][3]) << 16);
+          *reinterpret_cast<uint2*>(dbg + off) = make_uint2(b0, b1);
+        }
+      }
+    }
+    if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
+  }
+}
+
+inline unsigned grid_chunks(int64_t n, int64_t per_block, unsigned cap) {
+  int64_t g = (n + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (unsigned)(g > cap ? cap : g);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_calibrate(const void* x, int x_dtype, const faq_shape& s, float* amax,
+                            hipStream_t st) {
+  const int64_t per_bh = s.S * s.D;
+  dim3 grid(grid_chunks(per_bh, kThreads * 8 * 4, 65535), (unsigned)(s.B * s.H));
+  if (x_dtype == FAQ_T_BF16)
+    k_calibrate<uint16_t><<<grid, kThreads, 0, st>>>((const uint16_t*)x, per_bh, (int)s.H, amax);
+  else
+    k_calibrate<float><<<grid, kThreads, 0, st>>>((const float*)x, per_bh, (int)s.H, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_scales_from_amax(const float* amax, int64_t H, float qmax, float* scale,
+                                   hipStream_t st) {
+  k_scales_from_amax<<<(unsigned)((H + 255) / 256), 256, 0, st>>>(amax, H, qmax, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_int8_head(const void* x, int x_dtype, const faq_shape& s,
+                                  const float* scale, int8_t* codes, hipStream_t st) {
+  const int64_t per_bh = s.S * s.D;
+  dim3 grid(grid_chunks(per_bh, kThreads * 16 * 2, 65535), (unsigned)(s.B * s.H));
+  if (x_dtype == FAQ_T_BF16)
+    k_quant_int8_head<uint16_t><<<grid, kThreads, 0, st>>>((const uint16_t*)x, scale, per_bh,
+                                                           (int)s.H, codes);
+  else
+    k_quant_int8_head<float><<<grid, kThreads, 0, st>>>((const float*)x, scale, per_bh, (int)s.H,
+                                                        codes);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t fp8_token_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
+                              float* scales, hipStream_t st) {
+  constexpr int RPB = kThreads / (D / 8);
+  const unsigned grid = grid_chunks(rows, RPB * 4, 1u << 20);
+  if (x_dtype == FAQ_T_BF16)
+    k_quant_fp8_token<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, scales);
+  else
+    k_quant_fp8_token<float, D><<<grid, kThreads, 0, st>>>((const float*)x, rows, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8_token(const void* x, int x_dtype, const faq_shape& s,
+                                  uint8_t* codes, float* scales, hipStream_t st) {
+  const int64_t rows = s.B * s.H * s.S;
+  return s.D == 128 ? fp8_token_d<128>(x, x_dtype, rows, codes, scales, st)
+                    : fp8_token_d<64>(x, x_dtype, rows, codes, scales, st);
+}
+
+template <int D>
+static hipError_t mxfp4_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
+                          uint8_t* e8m0, hipStream_t st) {
+  constexpr int RPB = kThreads / (D / 8);
+  const unsigned grid = grid_chunks(rows, RPB * 4, 1u << 20);
+  if (x_dtype == FAQ_T_BF16)
+    k_quant_mxfp4<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, e8m0);
+  else
+    k_quant_mxfp4<float, D><<<grid, kThreads, 0, st>>>((const float*)x, rows, codes, e8m0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mxfp4(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
+                              uint8_t* e8m0, hipStream_t st) {
+  const int64_t rows = s.B * s.H * s.S;
+  return s.D == 128 ? mxfp4_d<128>(x, x_dtype, rows, codes, e8m0, st)
+                    : mxfp4_d<64>(x, x_dtype, rows, codes, e8m0, st);
+}
+
+template <int D, int BT>
+static hipError_t fp8_block_d(const uint16_t* x, const faq_shape& s, uint8_t* codes,
+                              float* scales, hipStream_t st) {
+  const int nblk = (int)((s.S + BT - 1) / BT);
+  dim3 grid((unsigned)nblk, (unsigned)(s.B * s.H));
+  k_quant_fp8_block<D, BT><<<grid, kThreads, 0, st>>>(x, s.S, nblk, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8_block(const uint16_t* x, const faq_shape& s, int block_tokens,
+                                  uint8_t* codes, float* scales, hipStream_t st) {
+  if (s.D == 128)
+    return block_tokens == 128 ? fp8_block_d<128, 128>(x, s, codes, scales, st)
+                               : fp8_block_d<128, 256>(x, s, codes, scales, st);
+  return block_tokens == 128 ? fp8_block_d<64, 128>(x, s, codes, scales, st)
+                             : fp8_block_d<64, 256>(x, s, codes, scales, st);
+}
+
+template <int D, int BT>
+static hipError_t rot_block_d(const uint16_t* x, const uint16_t* rot, const faq_shape& s,
+                              uint8_t* codes, float* scales, uint16_t* dbg, hipStream_t st) {
+  const int nblk = (int)((s.S + BT - 1) / BT);
+  const int64_t nwork = (int64_t)nblk * s.B * s.H;
+  const unsigned grid = (unsigned)(nwork < 2048 ? nwork : 2048);
+  k_rot_fp8_block<D, BT><<<grid, BT * 2, 0, st>>>(x, rot, s.S, nblk, nwork, codes, scales, dbg);
+  return hipGetLastError();
+}
+
+hipError_t launch_rot_fp8_block(const uint16_t* x, const uint16_t* rot, const faq_shape& s,
+                                int block_tokens, uint8_t* codes, float* scales,
+                                uint16_t* debug_rotated, hipStream_t st) {
+  if (s.D == 128)
+    return block_tokens == 128
+               ? rot_block_d<128, 128>(x, rot, s, codes, scales, debug_rotated, st)
+               : rot_block_d<128, 256>(x, rot, s, codes, scales, debug_rotated, st);
+  return block_tokens == 128 ? rot_block_d<64, 128>(x, rot, s, codes, scales, debug_rotated, st)
+                             : rot_block_d<64, 256>(x, rot, s, codes, scales, debug_rotated, st);
+}
+
+}  // namespace faq

@@ -1,0 +1,117 @@
+"""Helpers shared by the GPU parity tests: run a synthetic workload through
+the HIP library (via the C ABI binding) and bring its codes back to the CPU,
+and the oracle-side dequantization / attention on those same codes."""
+
+import numpy as np
+import torch
+
+import quantized_attention_fa_amd as faq
+from oracle import attention as OA
+from oracle import formats as F
+from oracle import quantize as OQ
+from synth import make_inputs
+
+DEV = "cuda:0"
+
+MODE_CFG = {
+    "int8_head": lambda spec, br: faq.QConfig("int8", "per_head"),
+    "fp8_token": lambda spec, br: faq.QConfig("fp8_e4m3", "per_token"),
+    "mxfp4": lambda spec, br: faq.QConfig("mxfp4", "per_block"),
+    "rot_fp8_block": lambda spec, br: faq.QConfig(
+        "fp8_e4m3", "per_token_block", block_tokens=spec["q_block"] if br == 0 else spec["kv_block"]),
+}
+P_RULE = {"int8_head": "int8", "fp8_token": "fp8", "mxfp4": "mxfp4", "rot_fp8_block": "fp8"}
+
+
+class GpuRun:
+    """Quantized Q/K/V of one workload produced by the HIP path."""
+
+    def __init__(self, w, keep_rotated=False):
+        self.w = w
+        mode = w.spec["mode"]
+        self.mode = mode
+        self.x = [t.to(DEV) for t in (w.q, w.k, w.v)]
+        self.static = [None, None, None]
+        self.amax = [None, None, None]
+        if mode == "int8_head":
+            for br in range(3):
+                amax = torch.zeros(w.shape[1], dtype=torch.float32, device=DEV)
+                for c in w.calib[br]:
+                    faq.fa_quant_calibrate(c.to(DEV), amax)
+                self.amax[br] = amax
+                self.static[br] = faq.fa_quant_scales_from_amax(amax, "int8")
+        self.rot = w.rot.to(DEV) if w.rot is not None else None
+        self.rotated = [None, None, None]
+        self.qt = []
+        for br in range(3):
+            cfg = MODE_CFG[mode](w.spec, br)
+            rot = self.rot if (self.rot is not None and br < 2) else None
+            dbg = None
+            if rot is not None and keep_rotated:
+                dbg = torch.empty_like(self.x[br])
+                self.rotated[br] = dbg
+            self.qt.append(faq.fa_quantize(self.x[br], cfg, static_scale=self.static[br], rot=rot,
+                                           debug_rotated=dbg))
+        torch.cuda.synchronize()
+
+    def codes_np(self, br):
+        return self.qt[br].codes.cpu().numpy()
+
+    def scales_np(self, br):
+        return self.qt[br].scales.cpu().numpy()
+
+    def attention(self, out_dtype=torch.float32, causal=None, sm_scale=0.0):
+        causal = self.w.spec["causal"] if causal is None else causal
+        o = faq.fa_quant_attention(self.qt[0], self.qt[1], self.qt[2], sm_scale=sm_scale, causal=causal,
+                                   out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        return o
+
+
+def dequant(run: GpuRun, br: int):
+    """(values fp64 [B,H,S,D], per-key scale [B,H,S] or None) of branch br,
+    decoded by the oracle from the GPU's codes and scales."""
+    mode = run.mode
+    c, s = run.codes_np(br), run.scales_np(br)
+    B, H, S, D = run.w.shape
+    if mode == "int8_head":
+        return OQ.dequantize_per_head(c, s), np.broadcast_to(s.reshape(1, H, 1), (B, H, S))
+    if mode == "fp8_token":
+        s = s.reshape(B, H, S)
+        return OQ.dequantize_per_token(c, s, F.e4m3_decode), s
+    if mode == "mxfp4":
+        return OQ.dequantize_mxfp4(c, s), None
+    bt = run.qt[br].cfg.block_tokens
+    st = OQ.block_scales_per_token(s.reshape(B, H, -1), bt, S)
+    return OQ.dequantize_per_token(c, st, F.e4m3_decode), st
+
+
+def oracle_attention(run: GpuRun, rows=None, causal=None, sm_scale=None):
+    causal = run.w.spec["causal"] if causal is None else causal
+    q, _ = dequant(run, 0)
+    k, _ = dequant(run, 1)
+    v, vs = dequant(run, 2)
+    return OA.attention(q, k, v, P_RULE[run.mode], v_scale=vs, causal=causal, rows=rows, allowance=True,
+                        sm_scale=sm_scale)
+
+
+def check_attention(gpu_out: np.ndarray, ref, label=""):
+    """Parity bar: relative Frobenius <= 1e-3 and |err| <= 2e-3 + T (tie
+    allowance) element by element."""
+    o, T, n_tie = ref
+    err = np.abs(gpu_out.astype(np.float64) - o)
+    rel = np.linalg.norm(gpu_out.astype(np.float64) - o) / max(np.linalg.norm(o), 1e-300)
+    viol = err > 2e-3 + T
+    assert not np.isnan(gpu_out).any(), f"{label}: NaN in output"
+    assert rel <= 1e-3, f"{label}: relative Frobenius {rel:.3e} > 1e-3"
+    assert not viol.any(), (f"{label}: {int(viol.sum())} elements over 2e-3 + T; max err {err.max():.3e}, "
+                            f"worst excess {(err - 2e-3 - T).max():.3e}; tie elements {n_tie}")
+    return rel, float(err.max()), n_tie
+
+
+def bf16_of(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+
+
+def small_workload(cfg, shape):
+    return make_inputs(cfg, shape=shape, calib_batch=2)

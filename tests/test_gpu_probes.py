@@ -1,0 +1,163 @@
+"""Single-instruction probes of the gfx950 facts the kernels rely on, each
+checked against a CPU reference built from the oracle's format tables:
+
+* MFMA operand layouts (i8 16x16x64, bf16 16x16x32, f8f6f4 16x16x128 with
+  E2M1 operands and per-lane E8M0 scales);
+* the K order of 8-bit f8f6f4 operands (lane group g: bytes 0-15 at K
+  16g.., bytes 16-31 at K 64+16g..), which differs from the 4-bit one;
+* the f8f6f4 MFMA sums 8-bit products with limited precision (the reason the
+  FP8 attention runs its products on the bf16 MFMA), the bf16 MFMA does not;
+* hardware conversions: f32 -> E4M3 (OCP, nearest even), f32 -> E2M1 with a
+  power-of-two scale (x / scale, saturating), E4M3 -> bf16 and
+  E2M1 * scale -> bf16 (both exact).
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from quantized_attention_fa_amd import _abi
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.probe_lib()
+
+
+def _d(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _pack4(codes):
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _f8f6f4(lib, A, Bt, fa, fb, sa=None, sb=None, scaled=0):
+    sa = np.full((16, 4), 127, np.uint8) if sa is None else sa
+    sb = np.full((16, 4), 127, np.uint8) if sb is None else sb
+    keep = [_d(A), _d(Bt), _d(sa), _d(sb)]
+    C = torch.zeros((16, 16), dtype=torch.float32, device=DEV)
+    assert lib.faq_probe_mfma_f8f6f4(*[_p(t) for t in keep], fa, fb, scaled, _p(C)) == 0
+    return C.cpu().numpy().astype(np.float64)
+
+
+def test_mfma_i8_layout(lib):
+    g = np.random.default_rng(0)
+    A = g.integers(-128, 128, (16, 64)).astype(np.int8)
+    B = g.integers(-128, 128, (16, 64)).astype(np.int8)
+    C = torch.zeros((16, 16), dtype=torch.int32, device=DEV)
+    a, b = _d(A), _d(B)
+    assert lib.faq_probe_mfma_i8(_p(a), _p(b), _p(C)) == 0
+    assert np.array_equal(C.cpu().numpy(), A.astype(np.int64) @ B.astype(np.int64).T)
+
+
+def test_mfma_bf16_layout_and_precision(lib):
+    g = np.random.default_rng(1)
+    # E4M3-valued operands (exact in bf16) with per-row magnitudes spread out
+    qa = np.clip(g.standard_normal((16, 32)) * np.exp(2 * g.standard_normal((16, 1))), -448, 448)
+    kb = np.clip(g.standard_normal((16, 32)) * np.exp(2 * g.standard_normal((16, 1))), -448, 448)
+    A = F.e4m3_decode(F.e4m3_encode(qa)).astype(np.float32)
+    B = F.e4m3_decode(F.e4m3_encode(kb)).astype(np.float32)
+    a = torch.from_numpy(A).to(torch.bfloat16).to(DEV)
+    b = torch.from_numpy(B).to(torch.bfloat16).to(DEV)
+    C = torch.zeros((16, 16), dtype=torch.float32, device=DEV)
+    assert lib.faq_probe_mfma_bf16(_p(a), _p(b), _p(C)) == 0
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    bound = 32 * 2.0 ** -22 * (np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T)
+    assert np.all(np.abs(C.cpu().numpy() - ref) <= bound)
+
+
+def test_mfma_fp4_scaled_layout(lib):
+    g = np.random.default_rng(2)
+    ca = g.integers(0, 16, (16, 128)).astype(np.uint8)
+    cb = g.integers(0, 16, (16, 128)).astype(np.uint8)
+    sa = g.integers(110, 140, (16, 4)).astype(np.uint8)
+    sb = g.integers(110, 140, (16, 4)).astype(np.uint8)
+    C = _f8f6f4(lib, _pack4(ca), _pack4(cb), 4, 4, sa, sb, 1)
+    va = F.e2m1_decode(ca) * np.repeat(F.e8m0_decode(sa), 32, axis=1)
+    vb = F.e2m1_decode(cb) * np.repeat(F.e8m0_decode(sb), 32, axis=1)
+    ref = va @ vb.T
+    # products inside a 32-block share one scale and span < 2^8, so each
+    # block sum is exact; the blocks are then added in fp32
+    bound = 4 * 2.0 ** -23 * (np.abs(va) @ np.abs(vb).T)
+    assert np.all(np.abs(C - ref) <= bound)
+
+
+def test_mfma_8bit_k_order(lib):
+    """Bit-encoded pairing of each E4M3 operand byte with an E2M1 nibble."""
+    kappa = np.full(128, -1)
+    for m in range(8):
+        A = np.zeros((16, 128), np.uint8)
+        for i in range(16):
+            A[i, 16 * m + i] = 0x38  # 1.0
+        Bc = np.zeros((16, 128), np.uint8)
+        for j in range(7):
+            Bc[j, [q for q in range(128) if (q >> j) & 1]] = 2  # 1.0
+        C = _f8f6f4(lib, A, _pack4(Bc), 0, 4)
+        for i in range(16):
+            kappa[16 * m + i] = int(sum(int(round(C[i, j])) << j for j in range(7)))
+    want = [16 * (p // 32) + p % 32 if p % 32 < 16 else 64 + 16 * (p // 32) + p % 32 - 16 for p in range(128)]
+    assert kappa.tolist() == want
+
+
+def test_mfma_fp8_accumulation_is_truncating(lib):
+    """One product of 448 and fifteen of 2^-7 in the same 16-group: the
+    f8f6f4 MFMA keeps about 12 fractional bits below the group's largest
+    product, so part of the small sum is lost (exact: 448 + 127/128)."""
+    A = np.zeros((16, 128), np.uint8)
+    A[:, 0] = 0x7E
+    A[:, 1:] = int(F.e4m3_encode(2.0 ** -7))
+    Bt = np.full((16, 128), 0x38, np.uint8)
+    C = _f8f6f4(lib, A, Bt, 0, 0)
+    exact = 448 + 127 * 2.0 ** -7
+    assert C[0, 0] < exact and exact - C[0, 0] < 2.0 ** -4
+
+
+def test_cvt_f32_to_e4m3_and_fp4(lib):
+    grid = F.E4M3_VALUES[:0x7F]
+    mids = (grid[1:] + grid[:-1]) / 2
+    g = np.random.default_rng(3)
+    x = np.concatenate([grid, mids, mids * (1 + 2.0 ** -20), mids * (1 - 2.0 ** -20), -grid, -mids,
+                        g.uniform(-448, 448, 4000), g.standard_normal(4000) * 0.01, [0.0, -0.0, -1e-6]]).astype(np.float32)
+    xt = _d(x)
+    outs = [torch.zeros(x.size, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    for scale in (1.0, 0.25, 2.0 ** -10, 8.0):
+        assert lib.faq_probe_cvt(_p(xt), x.size, ctypes.c_float(scale), *[_p(o) for o in outs]) == 0
+        e4, _, f4, sw = [o.cpu().numpy() for o in outs]
+        ref4 = F.e4m3_encode(x.astype(np.float64))
+        assert np.array_equal(e4, ref4)
+        assert np.array_equal(sw, ref4)
+        assert np.array_equal(f4, F.e2m1_encode(x.astype(np.float64) / scale))
+
+
+def test_cvt_up_to_bf16(lib):
+    words = np.arange(1 << 16, dtype=np.uint32)
+    words = words | (words[::-1] << 16)
+    codes = words.view(np.uint8).reshape(-1, 4)
+    finite = np.isfinite(F.E4M3_VALUES[codes]).all(axis=1)
+    words = words[finite]
+    codes = codes[finite]
+    w = _d(words)
+    n = words.size
+    outs = [torch.zeros(n, dtype=torch.int32, device=DEV) for _ in range(3)]
+    for scale in (1.0, 2.0 ** -3, 2.0 ** 5):
+        assert lib.faq_probe_cvt_up(_p(w), n, ctypes.c_float(scale), *[_p(o) for o in outs]) == 0
+        lo, hi, f4 = [o.cpu().numpy().view(np.uint32) for o in outs]
+        bf = lambda u: F.bf16_from_bits((u & 0xffff).astype(np.uint16)).astype(np.float64), \
+            lambda u: F.bf16_from_bits((u >> 16).astype(np.uint16)).astype(np.float64)
+        assert np.array_equal(bf[0](lo), F.E4M3_VALUES[codes[:, 0]])
+        assert np.array_equal(bf[1](lo), F.E4M3_VALUES[codes[:, 1]])
+        assert np.array_equal(bf[0](hi), F.E4M3_VALUES[codes[:, 2]])
+        assert np.array_equal(bf[1](hi), F.E4M3_VALUES[codes[:, 3]])
+        assert np.array_equal(bf[0](f4), F.e2m1_decode(codes[:, 0] & 0xF) * scale)
+        assert np.array_equal(bf[1](f4), F.e2m1_decode(codes[:, 0] >> 4) * scale)

@@ -1,0 +1,246 @@
+"""GPU parity of the quantization kernels: codes and scales bit-exact against
+the oracle, on small multi-tile shapes with ragged tails, on hand-built edge
+values, and at the full workload sizes (sampled rows / blocks there)."""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_attention_fa_amd as faq
+from oracle import formats as F
+from oracle import quantize as OQ
+from synth import CONFIGS, make_inputs, sample_rows
+from gpu_helpers import DEV, GpuRun, small_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.to(torch.float32).cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 2, 128, 64), torch.float32), ((2, 3, 300, 128), torch.bfloat16),
+                                         ((1, 4, 77, 64), torch.bfloat16), ((2, 2, 513, 128), torch.float32)])
+def test_int8_per_head_small(shape, dtype):
+    g = np.random.default_rng(sum(shape))
+    x = (g.standard_normal(shape) * np.exp(g.standard_normal((1, shape[1], 1, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).to(dtype)
+    xn = _np(xt)
+    amax = torch.zeros(shape[1], dtype=torch.float32, device=DEV)
+    faq.fa_quant_calibrate(xt[:, :, : shape[2] // 2].contiguous().to(DEV), amax)
+    faq.fa_quant_calibrate(xt.to(DEV), amax)
+    ref_amax = OQ.calibrate_amax(xn, OQ.calibrate_amax(xn[:, :, : shape[2] // 2]))
+    assert np.array_equal(amax.cpu().numpy(), ref_amax)
+    sc = faq.fa_quant_scales_from_amax(amax, "int8")
+    assert np.array_equal(sc.cpu().numpy(), OQ.int8_scales(ref_amax))
+    # scales tighter than the data so some values clamp to -128 / 127
+    tight = sc * 0.8
+    qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("int8", "per_head"), static_scale=tight)
+    want = OQ.quantize_int8_per_head(xn, tight.cpu().numpy())
+    assert np.array_equal(qt.codes.cpu().numpy(), want)
+    assert np.array_equal(qt.scales.cpu().numpy(), tight.cpu().numpy())
+
+
+def test_int8_divide_ties():
+    """Quotients that sit within an ulp of a rounding tie (see
+    tests/golden/divide_ties.txt): the GPU's division must be correctly
+    rounded."""
+    x = np.zeros((1, 1, 4, 64), np.float32)
+    x[0, 0, 0, :4] = [72, 74, -72, 144]
+    x[0, 0, 1, :3] = [148, 74, -74]
+    sc = torch.tensor([np.float32(144) / np.float32(127)], device=DEV)
+    qt = faq.fa_quantize(torch.from_numpy(x).to(DEV), faq.QConfig("int8", "per_head"), static_scale=sc)
+    assert np.array_equal(qt.codes.cpu().numpy(), OQ.quantize_int8_per_head(x, sc.cpu().numpy()))
+    assert qt.codes.cpu().numpy()[0, 0, 0, 0] == 63
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 2, 128, 64), torch.float32), ((2, 3, 300, 128), torch.bfloat16),
+                                         ((1, 1, 1000, 128), torch.bfloat16), ((1, 2, 37, 64), torch.bfloat16)])
+def test_fp8_per_token_small(shape, dtype):
+    g = np.random.default_rng(sum(shape) + 1)
+    x = (g.standard_normal(shape) * np.exp(2 * g.standard_normal(shape[:3] + (1,)))).astype(np.float32)
+    x[..., 0, :] = 0.0  # all-zero row: scale 1, codes 0
+    x[..., 1, :] = -1e-6
+    x[..., 1, 0] = 1.0  # tiny negatives -> 0x80
+    xt = torch.from_numpy(x).to(dtype)
+    xn = _np(xt)
+    qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("fp8_e4m3", "per_token"))
+    codes, s = OQ.quantize_fp8_per_token(xn)
+    assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
+    assert np.array_equal(qt.codes.cpu().numpy(), codes)
+
+
+def test_fp8_divide_ties_and_grid():
+    """Rows whose quotients hit E4M3 ties and the whole positive grid."""
+    rows = []
+    r = np.zeros(128, np.float32); r[:4] = [452, 169.5, -169.5, 1.0]; rows.append(r)
+    r = np.zeros(128, np.float32); r[:3] = [466, 349.5, 3.0]; rows.append(r)
+    grid = F.E4M3_VALUES[:0x7F].astype(np.float32)
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    vals = np.concatenate([grid, mids, -grid, -mids])
+    for i in range(0, vals.size, 127):
+        r = np.zeros(128, np.float32); r[0] = 448.0; chunk = vals[i:i + 127]; r[1:1 + chunk.size] = chunk
+        rows.append(r)
+    x = np.stack(rows).reshape(1, 1, len(rows), 128)
+    qt = faq.fa_quantize(torch.from_numpy(x).to(DEV), faq.QConfig("fp8_e4m3", "per_token"))
+    codes, s = OQ.quantize_fp8_per_token(x)
+    assert np.array_equal(qt.codes.cpu().numpy(), codes)
+    assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 2, 128, 64), torch.float32), ((2, 3, 300, 128), torch.bfloat16),
+                                         ((1, 1, 999, 128), torch.bfloat16)])
+def test_mxfp4_small(shape, dtype):
+    g = np.random.default_rng(sum(shape) + 2)
+    x = (g.standard_t(4, shape) * np.exp2(g.integers(-30, 30, shape[:3] + (1,)))).astype(np.float32)
+    x[..., 0, :] = 0.0
+    xt = torch.from_numpy(x).to(dtype)
+    xn = _np(xt)
+    qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("mxfp4", "per_block"))
+    packed, e8 = OQ.quantize_mxfp4(xn)
+    assert np.array_equal(qt.scales.cpu().numpy(), e8)
+    assert np.array_equal(qt.codes.cpu().numpy(), packed)
+
+
+def test_mxfp4_ties_and_saturation():
+    """Blocks with amax = 7 * 2^E (elements above 6 saturate) and elements on
+    every E2M1 tie, for a spread of exponents."""
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 7.0, 0.1, 0.0, -0.0], np.float32)
+    rows = []
+    for E in [-130, -100, -20, -3, 0, 5, 60, 125]:
+        blk = np.zeros(32, np.float32)
+        blk[: ties.size] = ties
+        blk[ties.size: 2 * ties.size] = -ties
+        blk[-1] = 7.0
+        rows.append(np.ldexp(blk, E).astype(np.float32))
+    x = np.stack([np.concatenate([r, r[::-1], r, r]) for r in rows]).reshape(1, 1, len(rows), 128)
+    qt = faq.fa_quantize(torch.from_numpy(x).to(DEV), faq.QConfig("mxfp4", "per_block"))
+    packed, e8 = OQ.quantize_mxfp4(x)
+    assert np.array_equal(qt.scales.cpu().numpy(), e8)
+    assert np.array_equal(qt.codes.cpu().numpy(), packed)
+
+
+@pytest.mark.parametrize("bt,S", [(128, 300), (256, 300), (256, 512), (128, 77)])
+def test_fp8_block_small(bt, S):
+    g = np.random.default_rng(bt + S)
+    x = g.standard_normal((2, 3, S, 128)).astype(np.float32)
+    x[1, 2] *= 1e-3
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("fp8_e4m3", "per_token_block", block_tokens=bt))
+    codes, s = OQ.quantize_fp8_block(_np(xt), bt)
+    assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
+    assert np.array_equal(qt.codes.cpu().numpy(), codes)
+
+
+def _check_rotated(y_gpu, x, R):
+    """The GPU rounds an fp32-accumulated product X.R to bf16, the oracle the
+    exact one: they agree except where the exact value lies within the fp32
+    accumulation error of a bf16 rounding boundary.  Bound: one bf16 ulp plus
+    D * 2^-22 * sum_i |x_i| |R_ij| (fp32 dot-product error of the MFMA);
+    at least 99.9% of the elements are identical."""
+    y_ref = OQ.rotate(x, R)
+    diff = np.abs(y_gpu.astype(np.float64) - y_ref)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(y_ref), 1e-30))) - 7)
+    D = R.shape[0]
+    acc = D * 2.0 ** -22 * (np.abs(x.astype(np.float64)) @ np.abs(R.astype(np.float64)))
+    assert np.all(diff <= ulp * 1.0001 + acc)
+    assert np.mean(diff == 0) >= 0.999
+
+
+@pytest.mark.parametrize("bt,S,D", [(128, 300, 128), (256, 300, 128), (128, 256, 64), (256, 70, 64)])
+def test_rotate_block_small(bt, S, D):
+    g = np.random.default_rng(bt + S + D)
+    x = g.standard_normal((2, 2, S, D)).astype(np.float32)
+    x[:, :, :, 3] *= 30
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    a = g.standard_normal((D, D))
+    qm, rm = np.linalg.qr(a)
+    R = torch.from_numpy((qm * np.sign(np.diag(rm))).astype(np.float32)).to(torch.bfloat16)
+    dbg = torch.empty_like(xt, device=DEV)
+    qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("fp8_e4m3", "per_token_block", block_tokens=bt),
+                         rot=R.to(DEV), debug_rotated=dbg)
+    y = _np(dbg)
+    _check_rotated(y, _np(xt), _np(R))
+    codes, s = OQ.quantize_fp8_block(y, bt)
+    assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
+    assert np.array_equal(qt.codes.cpu().numpy(), codes)
+
+
+def test_empty_tensor_is_a_no_op():
+    x = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    qt = faq.fa_quantize(x, faq.QConfig("fp8_e4m3", "per_token"))
+    assert qt.codes.numel() == 0
+    amax = torch.zeros(2, device=DEV)
+    faq.fa_quant_calibrate(x, amax)
+    assert amax.sum().item() == 0
+
+
+# ---------------------------------------------------------------- full sizes
+
+
+def _rows_check(run, br, rows_per_bh=24, seed=0):
+    """Oracle recomputation of sampled token rows (every (b,h)) from the
+    GPU's inputs; per-token and MX quantization are row-local."""
+    w = run.w
+    B, H, S, D = w.shape
+    x = (w.q, w.k, w.v)[br]
+    rows = sample_rows(w.cfg * 10 + br + seed, S, rows_per_bh, edge=4)
+    xs = x[:, :, rows].to(torch.float32).numpy()
+    if run.mode == "fp8_token":
+        codes, s = OQ.quantize_fp8_per_token(xs)
+        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
+        assert np.array_equal(run.qt[br].scales.view(B, H, S)[:, :, rows].cpu().numpy(), s)
+    elif run.mode == "mxfp4":
+        packed, e8 = OQ.quantize_mxfp4(xs)
+        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), packed)
+        assert np.array_equal(run.qt[br].scales[:, :, rows].cpu().numpy(), e8)
+    elif run.mode == "int8_head":
+        codes = OQ.quantize_int8_per_head(xs, run.static[br].cpu().numpy())
+        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
+
+
+def _calib_check(run):
+    w = run.w
+    for br in range(3):
+        ref = None
+        for c in w.calib[br]:
+            ref = OQ.calibrate_amax(c.to(torch.float32).numpy(), ref)
+        assert np.array_equal(run.amax[br].cpu().numpy(), ref)
+        assert np.array_equal(run.static[br].cpu().numpy(), OQ.int8_scales(ref))
+
+
+def _blocks_check(run, br, nblocks=6):
+    """Sampled token blocks of the rotate path: rotated values within a bf16
+    ulp of the oracle, codes/scales bit-exact against the oracle run on the
+    GPU's rotated values."""
+    w = run.w
+    B, H, S, D = w.shape
+    bt = run.qt[br].cfg.block_tokens
+    nb = -(-S // bt)
+    g = np.random.default_rng([w.cfg, br, 7])
+    scales = run.qt[br].scales.view(B, H, nb).cpu().numpy()
+    for _ in range(nblocks):
+        b, h, k = int(g.integers(B)), int(g.integers(H)), int(g.integers(nb))
+        sl = slice(k * bt, min(S, (k + 1) * bt))
+        x = (w.q, w.k, w.v)[br][b:b + 1, h:h + 1, sl].to(torch.float32).numpy()
+        if br < 2:
+            y = run.rotated[br][b:b + 1, h:h + 1, sl].to(torch.float32).cpu().numpy()
+            _check_rotated(y, x, w.rot.to(torch.float32).numpy())
+        else:
+            y = x
+        codes, s = OQ.quantize_fp8_block(y, bt)
+        assert np.array_equal(run.qt[br].codes[b:b + 1, h:h + 1, sl].cpu().numpy(), codes)
+        assert scales[b, h, k] == s.ravel()[0]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_size_quantize(cfg):
+    w = make_inputs(cfg)
+    run = GpuRun(w, keep_rotated=(cfg == 5))
+    if cfg in (1, 2):
+        _calib_check(run)
+    for br in range(3):
+        if cfg == 5:
+            _blocks_check(run, br)
+        else:
+            _rows_check(run, br)
