@@ -22,7 +22,8 @@ not by any value on the pages):
     - 'int8':  Pq = rne(127 p) / 127;
     - 'fp8':   with sigma_t = max over the tile's keys of the per-key V scale
                and w_j = s_v,j / sigma_t (the V scale folded into P):
-               Pq = E4M3(448 p w_j) / (448 w_j);
+               Pq = E4M3(448 p w_j) / (448 w_j), the code decided with the
+               multiplier 448 w_j rounded as fp32 (fl32(448 fl32(w_j)));
     - 'mxfp4': the MXFP4 quantizer applied along keys, 32-key groups aligned
                to absolute key index, masked keys counting as p = 0;
     - 'exact': Pq = p (no quantization; reduces to softmax attention).
@@ -42,10 +43,12 @@ MX_GROUP = 32
 TIE_REL = 2.0 ** -12
 
 
-def _quantize_p(p, rule, w=None):
+def _quantize_p(p, rule, w=None, w_dec=None):
     """Dequantized quantized probabilities for one row-chunk, per tile.
 
-    p: [nr, nt, 128] fp64 (masked -> 0); w: [nt, 128] (fp8 only).
+    p: [nr, nt, 128] fp64 (masked -> 0); w: [nt, 128] exact s_v,j / sigma_t
+    and w_dec: [nt, 128] the fp32 multiplier fl32(448 fl32(s_v,j / sigma_t))
+    (fp8 only).
     Returns (Pq, step, near) where `near` flags elements whose pre-rounding
     value lies within 2^-12 (relative) of a rounding boundary and `step` is
     the size of the code step such an element may flip by (in p units)."""
@@ -60,8 +63,15 @@ def _quantize_p(p, rule, w=None):
         step = np.full_like(p, 1.0 / 127.0)
         return pq, step, near
     if rule == "fp8":
+        # The E4M3 code is decided on u = 448 p w_j.  The pages fix no
+        # precision for this decision, so it is taken in fp32 as the kernel
+        # takes it: the multiplier is fl32(448 * fl32(s_v,j / sigma_t)) (for
+        # the tile's own maximum, p = 1, u is exactly that multiplier on both
+        # sides; bf16-derived scale ratios land on E4M3 ties there).  The
+        # dequantized value divides by the exact 448 w_j.
+        mult = w_dec[None, :, :]
         scale = 448.0 * w[None, :, :]
-        u = p * scale
+        u = p * mult
         pq = F.e4m3_decode(F.e4m3_encode(u)) / scale
         lo, hi = F.e4m3_neighbors(u)
         mid = 0.5 * (lo + hi)
@@ -126,12 +136,16 @@ def attention(qhat, khat, vhat, p_rule, *, v_scale=None, causal=False,
             k = khat[b, h]
             v = np.concatenate([vhat[b, h], np.zeros((pad, D))], axis=0)
             vt = v.reshape(nt, P_TILE, D)
-            w = None
+            w = w_dec = None
             if p_rule == "fp8":
                 sv = np.asarray(v_scale[b, h], dtype=np.float64)
                 svp = np.concatenate([sv, np.zeros(pad)]).reshape(nt, P_TILE)
                 sigma = svp.max(axis=1, keepdims=True)
                 w = np.where(svp > 0, svp / sigma, 1.0)
+                sv32 = svp.astype(np.float32)
+                ratio32 = (sv32 / sv32.max(axis=1, keepdims=True)).astype(np.float32)
+                w_dec = np.where(svp > 0, (np.float32(448.0) * ratio32).astype(np.float32), 448.0)
+                w_dec = w_dec.astype(np.float64)
             for c0 in range(0, rows.size, chunk):
                 r = rows[c0:c0 + chunk]
                 s = (qhat[b, h, r] @ k.T) * sm_scale  # [nr, Skv]
@@ -148,7 +162,7 @@ def attention(qhat, khat, vhat, p_rule, *, v_scale=None, causal=False,
                 m_safe = np.where(live, m_t, 0.0)
                 p = np.where(vmask, np.exp(sp - m_safe[..., None]), 0.0)
                 L_t = p.sum(axis=2)
-                pq, step, near = _quantize_p(p, p_rule, w=w)
+                pq, step, near = _quantize_p(p, p_rule, w=w, w_dec=w_dec)
                 C_t = np.matmul(pq.transpose(1, 0, 2), vt).transpose(1, 0, 2)  # [nr, nt, D]
                 M = np.where(live, m_t, -np.inf).max(axis=1)
                 f = np.where(live, np.exp(m_safe - M[:, None]), 0.0)  # e^{m_t - M}

@@ -240,49 +240,68 @@ struct KParams {
   int out_bf16;
 };
 
+// Raw bytes of one K/V tile (plus its per-key scale data) held in registers
+// between the prefetch issued before a tile's compute and the commit to LDS
+// at the start of the next one, so global-memory latency overlaps compute.
+template <int MODE, int D>
+struct TileRegs {
+  static constexpr int KSRC = (MODE == ATTN_MX) ? D / 2 : D;             // K bytes per key row
+  static constexpr int VSRC = (MODE == ATTN_MX) ? 2 * BN : BN;            // V^T bytes per channel row
+  static constexpr int NK = BN * KSRC / 16 / 256;                         // 16-byte chunks per thread
+  static constexpr int NV = D * VSRC / 16 / 256;
+  uint4 k[NK];
+  uint4 v[NV];
+  float sc;       // FP8: K scale of key tid (tid < 128) or 448 w of key tid-128
+  uint32_t kex;   // MXFP4: 2 K exponent bytes
+};
+
 template <int MODE, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
   // K tile in LDS: INT8 codes (D bytes/row), FP8 widened to bf16 (2D bytes),
   // MXFP4 packed E2M1 (D/2 bytes)
   constexpr int KB = (MODE == ATTN_MX) ? D / 2 : (MODE == ATTN_FP8 ? 2 * D : D);
-  constexpr int KCH = KB / 16;                      // 16-byte chunks per K row
+  constexpr int KCH = KB / 16;                           // 16-byte chunks per K row
   constexpr int VB = (MODE == ATTN_INT8) ? BN : 2 * BN;  // bytes per V^T row in LDS
   constexpr int VCH = VB / 16;
   constexpr int DB = D / 16;  // 16-channel output blocks
   constexpr int NB = D / 32;  // MX blocks per row
   constexpr int KK = D / 32;  // bf16 MFMA steps over D
+  using TR = TileRegs<MODE, D>;
+  constexpr int KSCH = TR::KSRC / 16;  // source chunks per K row
+  constexpr int VSCH = TR::VSRC / 16;  // source chunks per V^T row
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[BN * KB];
   __shared__ __attribute__((aligned(16))) uint8_t v_lds[D * VB];
   __shared__ __attribute__((aligned(16))) float sk_lds[BN];
   __shared__ __attribute__((aligned(16))) float vm_lds[BN];
-  __shared__ uint8_t kex_lds[BN * NB];
+  __shared__ __attribute__((aligned(4))) uint8_t kex_lds[BN * NB];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y;
   const int64_t h = bh % p.H;
   const int nqt = (int)((p.Sq + BM - 1) / BM);
   const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int64_t qbase = (int64_t)qt * BM + wave * 32;
+  const int qbase = qt * BM + wave * 32;
+  const int Skv = (int)p.Skv;
+  const uint8_t* kbase = p.k + bh * p.Skv * TR::KSRC;
+  const uint8_t* vtbase = p.vt + bh * p.nt * (int64_t)D * TR::VSRC;
 
   // ---- Q operands and per-query factors
-  i32x4 qbf[2][KK];  // FP8: bf16 images, 8 per lane per step kk
+  uint2 q8[2][KK];   // FP8: the E4M3 bytes of each bf16 MFMA step (widened per step)
   i32x4 qi8[2][2];   // INT8: 16 bytes per lane per 64-wide step
   i32x4 qmx[2];      // MXFP4: 32 E2M1 per lane
   int qsc[2];
   float cq[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int64_t qi = qbase + qb * 16 + l16;
+    const int qi = qbase + qb * 16 + l16;
     const bool ok = qi < p.Sq;
-    constexpr int QB = (MODE == ATTN_MX) ? D / 2 : D;  // bytes per Q row in HBM
-    const uint8_t* qrow = p.q + (bh * p.Sq + (ok ? qi : 0)) * QB;
+    const uint8_t* qrow = p.q + (bh * p.Sq + (ok ? qi : 0)) * TR::KSRC;
     if (MODE == ATTN_FP8) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         uint2 a = make_uint2(0, 0);
         if (ok) a = *reinterpret_cast<const uint2*>(qrow + 32 * kk + 8 * g);
-        qbf[qb][kk] = i32x4{(int)e4m3x2_to_bf16x2<false>(a.x), (int)e4m3x2_to_bf16x2<true>(a.x),
-                            (int)e4m3x2_to_bf16x2<false>(a.y), (int)e4m3x2_to_bf16x2<true>(a.y)};
+        q8[qb][kk] = a;
       }
       const float* qs = reinterpret_cast<const float*>(p.qs);
       const int64_t nqs = (p.Sq + p.q_block - 1) / p.q_block;
@@ -314,6 +333,87 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
     }
   }
 
+  // ---- tile prefetch (registers) and commit (LDS)
+  auto prefetch = [&](int t, TR& r) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < TR::NK; ++i) {
+      const int c = i * 256 + tid, row = c / KSCH, cc = c % KSCH;
+      r.k[i] = make_uint4(0, 0, 0, 0);
+      if (k0 + row < Skv) r.k[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(k0 + row) * TR::KSRC + cc * 16);
+    }
+    const uint8_t* vsrc = vtbase + (int64_t)t * D * TR::VSRC;
+#pragma unroll
+    for (int i = 0; i < TR::NV; ++i) {
+      const int c = i * 256 + tid;
+      r.v[i] = *reinterpret_cast<const uint4*>(vsrc + c * 16);
+    }
+    if (MODE == ATTN_FP8) {
+      if (tid < BN) {
+        const float* ks = reinterpret_cast<const float*>(p.ks);
+        const int64_t nks = (p.Skv + p.kv_block - 1) / p.kv_block;
+        r.sc = (k0 + tid < Skv) ? ks[bh * nks + (k0 + tid) / p.kv_block] : 0.0f;
+      } else {
+        r.sc = p.vmul[(bh * p.nt + t) * BN + (tid - BN)];
+      }
+    }
+    if (MODE == ATTN_MX) {
+      // 2 exponent bytes per thread (BN * NB <= 512)
+      const uint8_t* kes = reinterpret_cast<const uint8_t*>(p.ks);
+      uint32_t w = 0x7f7fu;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = 2 * tid + j;
+        if (c < BN * NB && k0 + c / NB < Skv) w = (w & ~(0xffu << (8 * j))) | ((uint32_t)kes[(bh * p.Skv + k0) * NB + c] << (8 * j));
+      }
+      r.kex = w;
+    }
+  };
+  auto commit = [&](const TR& r) {
+#pragma unroll
+    for (int i = 0; i < TR::NK; ++i) {
+      const int c = i * 256 + tid, row = c / KSCH, cc = c % KSCH;
+      const uint4 val = r.k[i];
+      if (MODE == ATTN_FP8) {
+        const int sw = swz_bf(row, KCH);
+        const uint4 lo = make_uint4(e4m3x2_to_bf16x2<false>(val.x), e4m3x2_to_bf16x2<true>(val.x),
+                                    e4m3x2_to_bf16x2<false>(val.y), e4m3x2_to_bf16x2<true>(val.y));
+        const uint4 hi = make_uint4(e4m3x2_to_bf16x2<false>(val.z), e4m3x2_to_bf16x2<true>(val.z),
+                                    e4m3x2_to_bf16x2<false>(val.w), e4m3x2_to_bf16x2<true>(val.w));
+        *reinterpret_cast<uint4*>(&k_lds[row * KB + (((2 * cc) ^ sw) * 16)]) = lo;
+        *reinterpret_cast<uint4*>(&k_lds[row * KB + (((2 * cc + 1) ^ sw) * 16)]) = hi;
+      } else {
+        const int sw = (MODE == ATTN_MX) ? (KCH == 4 ? swz_mx(row) : 0) : (KCH == 8 ? swz8(row) : swz4(row));
+        *reinterpret_cast<uint4*>(&k_lds[row * KB + ((cc ^ sw) * 16)]) = val;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TR::NV; ++i) {
+      const int c = i * 256 + tid, row = c / VSCH, cc = c % VSCH;
+      const uint4 val = r.v[i];
+      if (MODE == ATTN_INT8) {
+        *reinterpret_cast<uint4*>(&v_lds[row * VB + ((cc ^ swz8(row)) * 16)]) = val;
+      } else if (MODE == ATTN_FP8) {
+        const int sw = swz_bf(row, VCH);
+        const uint4 lo = make_uint4(e4m3x2_to_bf16x2<false>(val.x), e4m3x2_to_bf16x2<true>(val.x),
+                                    e4m3x2_to_bf16x2<false>(val.y), e4m3x2_to_bf16x2<true>(val.y));
+        const uint4 hi = make_uint4(e4m3x2_to_bf16x2<false>(val.z), e4m3x2_to_bf16x2<true>(val.z),
+                                    e4m3x2_to_bf16x2<false>(val.w), e4m3x2_to_bf16x2<true>(val.w));
+        *reinterpret_cast<uint4*>(&v_lds[row * VB + (((2 * cc) ^ sw) * 16)]) = lo;
+        *reinterpret_cast<uint4*>(&v_lds[row * VB + (((2 * cc + 1) ^ sw) * 16)]) = hi;
+      } else {
+        *reinterpret_cast<uint4*>(&v_lds[row * VB + ((cc ^ swz_bf(row, VCH)) * 16)]) = val;
+      }
+    }
+    if (MODE == ATTN_FP8) {
+      if (tid < BN) sk_lds[tid] = r.sc;
+      else vm_lds[tid - BN] = r.sc;
+    }
+    if (MODE == ATTN_MX) {
+      if (2 * tid < BN * NB) *reinterpret_cast<uint16_t*>(&kex_lds[2 * tid]) = (uint16_t)r.kex;
+    }
+  };
+
   float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
   f32x4 O[2][DB];
 #pragma unroll
@@ -324,140 +424,86 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
   const int t_end = CAUSAL ? (qt + 1 < (int)p.nt ? qt + 1 : (int)p.nt) : (int)p.nt;
   const float vscale_i8 = (MODE == ATTN_INT8) ? p.vs_head[h] * (1.0f / 127.0f) : 1.0f;
 
+  TR regs;
+  prefetch(0, regs);
   for (int t = 0; t < t_end; ++t) {
-    const int64_t k0 = (int64_t)t * BN;
+    const int k0 = t * BN;
+    __syncthreads();  // every wave is done reading the previous tile
+    commit(regs);
     __syncthreads();
-    // ---- stage the K tile (row-major, swizzled 16-byte chunks)
-    {
-      constexpr int SRC = (MODE == ATTN_MX) ? D / 2 : D;  // bytes per K row in HBM
-      constexpr int SCH = SRC / 16;
-      const uint8_t* ksrc = p.k + (bh * p.Skv + k0) * SRC;
-      for (int c = tid; c < BN * SCH; c += 256) {
-        const int row = c / SCH, cc = c % SCH;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (k0 + row < p.Skv) val = *reinterpret_cast<const uint4*>(ksrc + (int64_t)row * SRC + cc * 16);
-        if (MODE == ATTN_FP8) {
-          const int sw = swz_bf(row, KCH);
-          const uint4 lo = make_uint4(e4m3x2_to_bf16x2<false>(val.x), e4m3x2_to_bf16x2<true>(val.x),
-                                      e4m3x2_to_bf16x2<false>(val.y), e4m3x2_to_bf16x2<true>(val.y));
-          const uint4 hi = make_uint4(e4m3x2_to_bf16x2<false>(val.z), e4m3x2_to_bf16x2<true>(val.z),
-                                      e4m3x2_to_bf16x2<false>(val.w), e4m3x2_to_bf16x2<true>(val.w));
-          *reinterpret_cast<uint4*>(&k_lds[row * KB + (((2 * cc) ^ sw) * 16)]) = lo;
-          *reinterpret_cast<uint4*>(&k_lds[row * KB + (((2 * cc + 1) ^ sw) * 16)]) = hi;
-        } else {
-          const int sw = (MODE == ATTN_MX) ? (KCH == 4 ? swz_mx(row) : 0) : (KCH == 8 ? swz8(row) : swz4(row));
-          *reinterpret_cast<uint4*>(&k_lds[row * KB + ((cc ^ sw) * 16)]) = val;
-        }
-      }
-      // ---- stage the V^T tile
-      if (MODE == ATTN_INT8) {
-        const uint8_t* vsrc = p.vt + (bh * p.nt + t) * (int64_t)D * BN;
-        for (int c = tid; c < D * 8; c += 256) {
-          const int row = c >> 3, cc = c & 7;
-          const uint4 val = *reinterpret_cast<const uint4*>(vsrc + (int64_t)row * BN + cc * 16);
-          *reinterpret_cast<uint4*>(&v_lds[row * VB + ((cc ^ swz8(row)) * 16)]) = val;
-        }
-      } else if (MODE == ATTN_FP8) {
-        const uint8_t* vsrc = p.vt + (bh * p.nt + t) * (int64_t)D * BN;
-        for (int c = tid; c < D * 8; c += 256) {
-          const int row = c >> 3, cc = c & 7;
-          const uint4 val = *reinterpret_cast<const uint4*>(vsrc + (int64_t)row * BN + cc * 16);
-          const int sw = swz_bf(row, VCH);
-          const uint4 lo = make_uint4(e4m3x2_to_bf16x2<false>(val.x), e4m3x2_to_bf16x2<true>(val.x),
-                                      e4m3x2_to_bf16x2<false>(val.y), e4m3x2_to_bf16x2<true>(val.y));
-          const uint4 hi = make_uint4(e4m3x2_to_bf16x2<false>(val.z), e4m3x2_to_bf16x2<true>(val.z),
-                                      e4m3x2_to_bf16x2<false>(val.w), e4m3x2_to_bf16x2<true>(val.w));
-          *reinterpret_cast<uint4*>(&v_lds[row * VB + (((2 * cc) ^ sw) * 16)]) = lo;
-          *reinterpret_cast<uint4*>(&v_lds[row * VB + (((2 * cc + 1) ^ sw) * 16)]) = hi;
-        }
-      } else {
-        const uint8_t* vsrc = p.vt + (bh * p.nt + t) * (int64_t)D * BN * 2;
-        for (int c = tid; c < D * 16; c += 256) {
-          const int row = c >> 4, cc = c & 15;
-          const uint4 val = *reinterpret_cast<const uint4*>(vsrc + (int64_t)row * BN * 2 + cc * 16);
-          *reinterpret_cast<uint4*>(&v_lds[row * VB + ((cc ^ swz_bf(row, VCH)) * 16)]) = val;
-        }
-      }
-      if (MODE == ATTN_FP8) {
-        if (tid < BN) {
-          const float* ks = reinterpret_cast<const float*>(p.ks);
-          const int64_t nks = (p.Skv + p.kv_block - 1) / p.kv_block;
-          const int64_t kj = k0 + tid;
-          sk_lds[tid] = (kj < p.Skv) ? ks[bh * nks + kj / p.kv_block] : 0.0f;
-        } else {
-          vm_lds[tid - BN] = p.vmul[(bh * p.nt + t) * BN + (tid - BN)];
-        }
-      }
-      if (MODE == ATTN_MX) {
-        const uint8_t* kes = reinterpret_cast<const uint8_t*>(p.ks);
-        for (int c = tid; c < BN * NB; c += 256) {
-          const int row = c / NB;
-          kex_lds[c] = (k0 + row < p.Skv) ? kes[(bh * p.Skv + k0) * NB + c] : (uint8_t)127;
-        }
-      }
-    }
-    __syncthreads();
+    if (t + 1 < t_end) prefetch(t + 1, regs);  // in flight during this tile's compute
 
     // ---- S^T = K Q^T: s[qb][b][r] is the score of (query qb*16 + l16, key
     // of block b at output row 4g + r)
     f32x4 s[2][8];
+    if (MODE == ATTN_FP8) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      if (MODE == ATTN_FP8) {
-        const int row = 16 * b + l16;
-        const int sw = swz_bf(row, KCH);
-        s[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        s[1][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < 8; ++b) s[0][b] = s[1][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&k_lds[row * KB + (((4 * kk + g) ^ sw) * 16)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, __builtin_bit_cast(bf16x8, qbf[qb][kk]),
-                                                               s[qb][b], 0, 0, 0);
-        }
-      } else if (MODE == ATTN_INT8) {
-        const int row = 16 * b + l16;
-        i32x4 si[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
-#pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk) {
-          const int cc = 4 * kk + g;
-          const int sw = (KCH == 8 ? swz8(row) : swz4(row));
-          const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((cc ^ sw) * 16)]);
-          const i32x4 kop = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            si[qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qi8[qb][kk], si[qb], 0, 0, 0);
-        }
+      for (int kk = 0; kk < KK; ++kk) {
+        bf16x8 qop[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          s[qb][b] = f32x4{(float)si[qb][0], (float)si[qb][1], (float)si[qb][2], (float)si[qb][3]};
-      } else {
-        const int row = k_row_mx(b, l16);
-        i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
-        int ksc = 127;
-        if (32 * g < D) {
-          const int sw = (KCH == 4 ? swz_mx(row) : 0);
-          const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((g ^ sw) * 16)]);
-          kop = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-          ksc = kex_lds[row * NB + g];
-        }
+          qop[qb] = __builtin_bit_cast(bf16x8, i32x4{(int)e4m3x2_to_bf16x2<false>(q8[qb][kk].x),
+                                                     (int)e4m3x2_to_bf16x2<true>(q8[qb][kk].x),
+                                                     (int)e4m3x2_to_bf16x2<false>(q8[qb][kk].y),
+                                                     (int)e4m3x2_to_bf16x2<true>(q8[qb][kk].y)});
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const i32x4 qv = qmx[qb];
-          const i32x8 qop = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
-          s[qb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                      4, 4, 0, ksc, 0, qsc[qb]);
+        for (int b = 0; b < 8; ++b) {
+          const int row = 16 * b + l16;
+          const bf16x8 kop =
+              *reinterpret_cast<const bf16x8*>(&k_lds[row * KB + (((4 * kk + g) ^ swz_bf(row, KCH)) * 16)]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            s[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qb], s[qb][b], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        if (MODE == ATTN_INT8) {
+          const int row = 16 * b + l16;
+          i32x4 si[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+#pragma unroll
+          for (int kk = 0; kk < D / 64; ++kk) {
+            const int cc = 4 * kk + g;
+            const int sw = (KCH == 8 ? swz8(row) : swz4(row));
+            const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((cc ^ sw) * 16)]);
+            const i32x4 kop = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              si[qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qi8[qb][kk], si[qb], 0, 0, 0);
+          }
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            s[qb][b] = f32x4{(float)si[qb][0], (float)si[qb][1], (float)si[qb][2], (float)si[qb][3]};
+        } else {
+          const int row = k_row_mx(b, l16);
+          i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
+          int ksc = 127;
+          if (32 * g < D) {
+            const int sw = (KCH == 4 ? swz_mx(row) : 0);
+            const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((g ^ sw) * 16)]);
+            kop = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+            ksc = kex_lds[row * NB + g];
+          }
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const i32x4 qv = qmx[qb];
+            const i32x8 qop = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
+            s[qb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                        4, 4, 0, ksc, 0, qsc[qb]);
+          }
         }
       }
     }
 
     // ---- scores in "t units" (t * cq = log2-domain score), masking, tile max
-    const bool need_mask = (k0 + BN > p.Skv) || (CAUSAL && t == qt);
+    const bool need_mask = (k0 + BN > Skv) || (CAUSAL && t == qt);
     float mt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int64_t qi = qbase + qb * 16 + l16;
+      const int qi = qbase + qb * 16 + l16;
       float m = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
@@ -469,8 +515,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
           if (MODE == ATTN_FP8) x *= (r == 0 ? skv.x : r == 1 ? skv.y : r == 2 ? skv.z : skv.w);
           if (need_mask) {
             const int kl = (MODE == ATTN_MX) ? (32 * g + 4 * b + r) : (16 * b + 4 * g + r);
-            const int64_t kj = k0 + kl;
-            const bool valid = (kj < p.Skv) && (!CAUSAL || kj <= qi);
+            const int kj = k0 + kl;
+            const bool valid = (kj < Skv) && (!CAUSAL || kj <= qi);
             x = valid ? x : -INFINITY;
           }
           s[qb][b][r] = x;
@@ -596,7 +642,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
   // ---- normalize, store
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int64_t qi = qbase + qb * 16 + l16;
+    const int qi = qbase + qb * 16 + l16;
     if (qi >= p.Sq) continue;
     const float inv = 1.0f / L[qb];
 #pragma unroll

@@ -169,3 +169,20 @@ def test_allowance_flags_ties():
     o, T, n = A.attention(q, k, v, "int8", allowance=True)
     assert n == 1
     assert T[0, 0, 0, 0] == pytest.approx((1 / 127) / (1 + t), rel=1e-9)
+
+
+def test_fp8_code_decided_in_fp32():
+    """The probability code of the tile's maximum (p = 1) is decided on the
+    fp32 multiplier fl32(448 fl32(s_v,j / sigma_t)).  With V amaxes 2.125 and
+    14 (bf16 values) the exact 448 w_j is 68.000001 (above the 64/72 tie,
+    code 72) while the fp32 multiplier is exactly 68.0 (tie -> even, 64)."""
+    D = 64
+    sv0 = np.float32(2.125) / np.float32(448)
+    sv1 = np.float32(14.0) / np.float32(448)
+    q = np.zeros((1, 1, 1, D)); q[..., 0] = math.sqrt(D)
+    k = np.zeros((1, 1, 2, D)); k[0, 0, 1, 0] = -200.0  # p1 underflows
+    v = np.zeros((1, 1, 2, D)); v[0, 0, 0, 1] = float(sv0) * 448; v[0, 0, 1, 2] = float(sv1)
+    vs = np.array([[[sv0, sv1]]], dtype=np.float64)
+    o = A.attention(q, k, v, "fp8", v_scale=vs)[0, 0, 0]
+    w = float(sv0) / float(sv1)
+    assert o[1] == pytest.approx(64.0 / (448 * w) * float(sv0) * 448, rel=1e-12)
