@@ -35,6 +35,8 @@
 // with its keys permuted to match the order in which a lane holds its
 // probabilities.
 
+#include <climits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -68,6 +70,11 @@ FAQ_DEV int vt_key_mx(int col) {
   const int kk = col >> 5, g = (col >> 3) & 3, t = col & 7;
   return 32 * g + 8 * kk + t;
 }
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
 
 // Row of the K tile read by lane-row i of MFMA block b in the MXFP4 kernel.
 FAQ_DEV int k_row_mx(int b, int i) { return 32 * (i >> 2) + 4 * b + (i & 3); }
@@ -414,7 +421,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
     }
   };
 
-  float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f};
+  // Row state.  O holds the output of each row relative to a reference
+  // factor fref: the true accumulator is O * fref (INT8 keeps fref = 1 and
+  // folds its per-tile factor in with an fma; the bf16-MFMA modes rescale O
+  // once per tile and let the PV MFMA accumulate straight into it).
+  float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f}, fref[2] = {1.f, 1.f};
   f32x4 O[2][DB];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -432,9 +443,12 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
     commit(regs);
     __syncthreads();
     if (t + 1 < t_end) prefetch(t + 1, regs);  // in flight during this tile's compute
+    // the ragged last tile and the causal diagonal need a per-key validity
+    // test; the other tiles skip it (uniform branch)
+    const bool masked = (k0 + BN > Skv) || (CAUSAL && t == qt);
 
-    // ---- S^T = K Q^T: s[qb][b][r] is the score of (query qb*16 + l16, key
-    // of block b at output row 4g + r)
+    // ---- S^T = K Q^T: score of (query qb*16 + l16, key of block b at
+    // output row 4g + r)
     f32x4 s[2][8];
     if (MODE == ATTN_FP8) {
 #pragma unroll
@@ -458,152 +472,203 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
             s[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qb], s[qb][b], 0, 0, 0);
         }
       }
+    } else if (MODE == ATTN_INT8) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int row = 16 * b + l16;
+        i32x4 si[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk) {
+          const int cc = 4 * kk + g;
+          const int sw = (KCH == 8 ? swz8(row) : swz4(row));
+          const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((cc ^ sw) * 16)]);
+          const i32x4 kop = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            si[qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qi8[qb][kk], si[qb], 0, 0, 0);
+        }
+        // exact int32 scores (|s| < 2^21): the float conversion is exact
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[qb][b] = f32x4{(float)si[qb][0], (float)si[qb][1], (float)si[qb][2], (float)si[qb][3]};
+      }
     } else {
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
-        if (MODE == ATTN_INT8) {
-          const int row = 16 * b + l16;
-          i32x4 si[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+        const int row = k_row_mx(b, l16);
+        i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
+        int ksc = 127;
+        if (32 * g < D) {
+          const int sw = (KCH == 4 ? swz_mx(row) : 0);
+          const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((g ^ sw) * 16)]);
+          kop = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+          ksc = kex_lds[row * NB + g];
+        }
 #pragma unroll
-          for (int kk = 0; kk < D / 64; ++kk) {
-            const int cc = 4 * kk + g;
-            const int sw = (KCH == 8 ? swz8(row) : swz4(row));
-            const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((cc ^ sw) * 16)]);
-            const i32x4 kop = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-              si[qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qi8[qb][kk], si[qb], 0, 0, 0);
-          }
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[qb][b] = f32x4{(float)si[qb][0], (float)si[qb][1], (float)si[qb][2], (float)si[qb][3]};
-        } else {
-          const int row = k_row_mx(b, l16);
-          i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
-          int ksc = 127;
-          if (32 * g < D) {
-            const int sw = (KCH == 4 ? swz_mx(row) : 0);
-            const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((g ^ sw) * 16)]);
-            kop = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-            ksc = kex_lds[row * NB + g];
-          }
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const i32x4 qv = qmx[qb];
-            const i32x8 qop = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
-            s[qb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                        4, 4, 0, ksc, 0, qsc[qb]);
-          }
+        for (int qb = 0; qb < 2; ++qb) {
+          const i32x4 qv = qmx[qb];
+          const i32x8 qop = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
+          s[qb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                      4, 4, 0, ksc, 0, qsc[qb]);
         }
       }
     }
 
-    // ---- scores in "t units" (t * cq = log2-domain score), masking, tile max
-    const bool need_mask = (k0 + BN > Skv) || (CAUSAL && t == qt);
+    // ---- scores in "t units" (t * cq is the log2-domain score)
+    if (MODE == ATTN_FP8) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const float4 skv = *reinterpret_cast<const float4*>(&sk_lds[16 * b + 4 * g]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb][b][0] *= skv.x; s[qb][b][1] *= skv.y; s[qb][b][2] *= skv.z; s[qb][b][3] *= skv.w;
+        }
+      }
+    }
+    if (masked) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qbase + qb * 16 + l16;
+        const int lim = (CAUSAL ? min(Skv, qi + 1) : Skv) - k0;  // keys kl < lim are valid
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kl = (MODE == ATTN_MX) ? (32 * g + 4 * b + r) : (16 * b + 4 * g + r);
+            s[qb][b][r] = (kl < lim) ? s[qb][b][r] : -INFINITY;
+          }
+      }
+    }
     float mt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qi = qbase + qb * 16 + l16;
       float m = -INFINITY;
+      if (MODE == ATTN_INT8 && !masked) {
+        // exact integer scores: integer max (no float canonicalization)
+        int mi = INT_MIN;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        float4 skv = make_float4(1.f, 1.f, 1.f, 1.f);
-        if (MODE == ATTN_FP8) skv = *reinterpret_cast<const float4*>(&sk_lds[16 * b + 4 * g]);
+        for (int b = 0; b < 8; ++b)
+          mi = max(max(mi, max((int)s[qb][b][0], (int)s[qb][b][1])), max((int)s[qb][b][2], (int)s[qb][b][3]));
+        m = (float)mi;
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = s[qb][b][r];
-          if (MODE == ATTN_FP8) x *= (r == 0 ? skv.x : r == 1 ? skv.y : r == 2 ? skv.z : skv.w);
-          if (need_mask) {
-            const int kl = (MODE == ATTN_MX) ? (32 * g + 4 * b + r) : (16 * b + 4 * g + r);
-            const int kj = k0 + kl;
-            const bool valid = (kj < Skv) && (!CAUSAL || kj <= qi);
-            x = valid ? x : -INFINITY;
-          }
-          s[qb][b][r] = x;
-          m = fmaxf(m, x);
-        }
+        for (int b = 0; b < 8; ++b)
+          m = fmaxf(fmaxf(m, fmaxf(s[qb][b][0], s[qb][b][1])), fmaxf(s[qb][b][2], s[qb][b][3]));
       }
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      mt[qb] = m;
+      mt[qb] = rows4_max(m);
     }
 
-    // ---- probabilities, tile sums, quantized P operands
+    // ---- probabilities, tile sums, quantized P operands, row combination
     i32x8 pi8[2];      // INT8: rne(127 p) bytes, keys in vt_key_int8 order
     i32x4 pbf[2][4];   // FP8 / MXFP4: bf16 images of the quantized p, per step kk
-    float alpha[2], beta[2];
+    float rscale[2], bvi8[2];
+    bool rescale_any = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float m = mt[qb];
       const float msafe = (m == -INFINITY) ? 0.0f : m;
       float lsum = 0.0f, pmax = 0.0f;
-#pragma unroll
-      for (int b = 0; b < 8; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = __builtin_amdgcn_exp2f((s[qb][b][r] - msafe) * cq[qb]);
-          s[qb][b][r] = pv;
-          lsum += pv;
-          pmax = fmaxf(pmax, pv);
-        }
-      lsum += __shfl_xor(lsum, 16, 64);
-      lsum += __shfl_xor(lsum, 32, 64);
       if (MODE == ATTN_INT8) {
-        int w[8];
+        // p = 2^(s cq - m cq); p at the maximum may differ from 1 by an ulp,
+        // which cannot move rne(127 p)
+        const float mc = msafe * cq[qb];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          uint32_t acc = 0;
+        for (int b = 0; b < 8; ++b)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float f = __builtin_fmaf(s[qb][b][r], 127.0f, 12582912.0f);  // rne(127 p) in the low bits
-            acc |= (__float_as_uint(f) & 0xffu) << (8 * r);
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r], cq[qb], -mc));
+            s[qb][b][r] = pv;
+            lsum += pv;
           }
-          w[b] = (int)acc;
-        }
-        pi8[qb] = i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
-      } else if (MODE == ATTN_FP8) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const float4 vm = *reinterpret_cast<const float4*>(&vm_lds[16 * b + 4 * g]);
-          // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
-          int e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][b][0] * vm.x, s[qb][b][1] * vm.y, 0, false);
-          e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][b][2] * vm.z, s[qb][b][3] * vm.w, e8, true);
-          pbf[qb][b >> 1][2 * (b & 1)] = (int)e4m3x2_to_bf16x2<false>((uint32_t)e8);
-          pbf[qb][b >> 1][2 * (b & 1) + 1] = (int)e4m3x2_to_bf16x2<true>((uint32_t)e8);
-        }
       } else {
-        // this lane's 32 keys are one MX group: local max -> shared exponent;
-        // p -> E2M1(p / 2^E) * 2^E, exact in bf16
-        const int E = mx_exponent(pmax);
-        const float sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < 8; ++b)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s[qb][b][2 * hh], s[qb][b][2 * hh + 1], sc, 0);
-            pbf[qb][b >> 1][2 * (b & 1) + hh] =
-                (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
+          for (int r = 0; r < 4; ++r) {
+            // (x - m) is exactly 0 at the tile maximum, so p = 1 there exactly
+            const float pv = __builtin_amdgcn_exp2f((s[qb][b][r] - msafe) * cq[qb]);
+            s[qb][b][r] = pv;
+            lsum += pv;
+            if (MODE == ATTN_MX) pmax = fmaxf(pmax, pv);
           }
-        }
       }
+      lsum = rows4_sum(lsum);
+
       // online combination of tiles
       const float mnew = fmaxf(M[qb], m);
       const float a = __builtin_amdgcn_exp2f((M[qb] - mnew) * cq[qb]);
       const float bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - mnew) * cq[qb]);
       L[qb] = L[qb] * a + lsum * bt;
       M[qb] = mnew;
-      alpha[qb] = a;
-      beta[qb] = bt;
+
+      if (MODE == ATTN_INT8) {
+        int w[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          // rne(127 p) lands in the low byte of fma(p, 127, 1.5 * 2^23)
+          const uint32_t f0 = __float_as_uint(__builtin_fmaf(s[qb][b][0], 127.0f, 12582912.0f));
+          const uint32_t f1 = __float_as_uint(__builtin_fmaf(s[qb][b][1], 127.0f, 12582912.0f));
+          const uint32_t f2 = __float_as_uint(__builtin_fmaf(s[qb][b][2], 127.0f, 12582912.0f));
+          const uint32_t f3 = __float_as_uint(__builtin_fmaf(s[qb][b][3], 127.0f, 12582912.0f));
+          const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x0c0c0400u);
+          w[b] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+        pi8[qb] = i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+        rscale[qb] = a;
+        bvi8[qb] = bt * vscale_i8;
+        rescale_any |= (a != 1.0f);
+      } else {
+        // bf16-MFMA modes: new reference factor f = bt (times sigma_t / 448
+        // for FP8); a row whose tile is negligible (bt < 2^-64) keeps its
+        // reference and contributes nothing, which keeps O bounded.
+        float ft = bt;
+        if (MODE == ATTN_FP8) ft *= p.sig[bh * p.nt + t] * (1.0f / 448.0f);
+        const bool live = bt >= 0x1p-64f;
+        const float r = live ? (fref[qb] * a / ft) : a;
+        fref[qb] = live ? ft : fref[qb];
+        rscale[qb] = r;
+        rescale_any |= (r != 1.0f);
+        if (MODE == ATTN_FP8) {
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const float4 vm = *reinterpret_cast<const float4*>(&vm_lds[16 * b + 4 * g]);
+            // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
+            int e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][b][0] * vm.x, s[qb][b][1] * vm.y, 0, false);
+            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][b][2] * vm.z, s[qb][b][3] * vm.w, e8, true);
+            pbf[qb][b >> 1][2 * (b & 1)] = live ? (int)e4m3x2_to_bf16x2<false>((uint32_t)e8) : 0;
+            pbf[qb][b >> 1][2 * (b & 1) + 1] = live ? (int)e4m3x2_to_bf16x2<true>((uint32_t)e8) : 0;
+          }
+        } else {
+          // this lane's 32 keys are one MX group: local max -> shared
+          // exponent; p -> E2M1(p / 2^E) * 2^E, exact in bf16
+          const int E = mx_exponent(pmax);
+          const float sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const uint32_t f4 =
+                  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s[qb][b][2 * hh], s[qb][b][2 * hh + 1], sc, 0);
+              const int v2 = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
+              pbf[qb][b >> 1][2 * (b & 1) + hh] = live ? v2 : 0;
+            }
+          }
+        }
+      }
     }
 
-    float tile_vscale = vscale_i8;
-    if (MODE == ATTN_FP8) tile_vscale = p.sig[bh * p.nt + t] * (1.0f / 448.0f);
-
     // ---- O^T += V^T P^T (per 16-channel block)
+    const bool do_rescale = __any(rescale_any);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int row = 16 * db + l16;
-      f32x4 cv[2];
+      if (do_rescale) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[qb][db][r] *= rscale[qb];
+      }
       if (MODE == ATTN_INT8) {
         const uint4 a = *reinterpret_cast<const uint4*>(&v_lds[row * VB + (((2 * g) ^ swz8(row)) * 16)]);
         const uint4 c = *reinterpret_cast<const uint4*>(&v_lds[row * VB + (((2 * g + 1) ^ swz8(row)) * 16)]);
@@ -615,26 +680,19 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
           const i32x4 p1 = {pi8[qb][4], pi8[qb][5], pi8[qb][6], pi8[qb][7]};
           i32x4 ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(v0, p0, i32x4{0, 0, 0, 0}, 0, 0, 0);
           ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(v1, p1, ci, 0, 0, 0);
-          cv[qb] = f32x4{(float)ci[0], (float)ci[1], (float)ci[2], (float)ci[3]};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[qb][db][r] = __builtin_fmaf((float)ci[r], bvi8[qb], O[qb][db][r]);
         }
       } else {
         const int sw = swz_bf(row, VCH);
-        cv[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        cv[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const bf16x8 vop = *reinterpret_cast<const bf16x8*>(&v_lds[row * VB + (((4 * kk + g) ^ sw) * 16)]);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
-            cv[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, __builtin_bit_cast(bf16x8, pbf[qb][kk]),
-                                                             cv[qb], 0, 0, 0);
+            O[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, __builtin_bit_cast(bf16x8, pbf[qb][kk]),
+                                                                O[qb][db], 0, 0, 0);
         }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float bv = beta[qb] * tile_vscale;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) O[qb][db][r] = O[qb][db][r] * alpha[qb] + cv[qb][r] * bv;
       }
     }
   }
@@ -644,7 +702,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
   for (int qb = 0; qb < 2; ++qb) {
     const int qi = qbase + qb * 16 + l16;
     if (qi >= p.Sq) continue;
-    const float inv = 1.0f / L[qb];
+    const float inv = fref[qb] / L[qb];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int64_t off = (bh * p.Sq + qi) * D + 16 * db + 4 * g;

@@ -121,6 +121,22 @@ FAQ_DEV float group_max(float v) {
 
 FAQ_DEV float wave_max(float v) { return group_max<64>(v); }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) with the in-register row swaps of gfx950 (no LDS round trip).
+FAQ_DEV float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+FAQ_DEV float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------- misc
 
 FAQ_DEV float scale_from_amax(float amax, float qmax) {
