@@ -25,15 +25,22 @@
 // the tile sum L uses unquantized p, and tiles combine with the usual
 // running-max rescale, O = sum_t e^{m_t-M} C_t / sum_t e^{m_t-M} L_t.
 //
-// Kernel shape: one workgroup = 4 waves = 128 queries of one (b,h); each
-// wave owns 32 queries as two 16-query MFMA column blocks.  Scores are
-// computed transposed (S^T = K Q^T), so a lane holds one query and a run of
-// keys: the row max needs only two cross-lane steps, and the lane's
-// probabilities are already the B operand of O^T = V^T P^T.  K is staged in
-// LDS row-major (XOR-swizzled 16-byte chunks; FP8 codes widened to bf16 on
-// the way); V comes from the workspace already transposed per 128-key tile,
-// with its keys permuted to match the order in which a lane holds its
-// probabilities.
+// Kernel shape: one workgroup = 8 waves = 256 queries of one (b,h); each
+// wave owns 32 queries as two 16-query MFMA column blocks, and all eight
+// share each K / V^T tile.  Tiles stream from global memory straight into
+// LDS (global_load_lds, 16 bytes per lane), double buffered: the copy of
+// tile t+1 runs while tile t is computed, with one barrier per tile.
+// Scores are computed transposed (S^T = K Q^T), so a lane holds one query
+// and a run of keys: the row max needs only two cross-lane steps, and the
+// lane's probabilities are already the B operand of O^T = V^T P^T.  V comes
+// from a per-call workspace already transposed per 128-key tile, with its
+// keys permuted to match the order in which a lane holds its probabilities
+// (FP8: K and V^T widened there to their exact bf16 images).
+//
+// Workgroups are numbered so that all query tiles of one (b,h) land on the
+// same XCD (workgroups are dealt to the 8 XCDs round robin), which keeps a
+// head's K/V tiles in that XCD's L2; causal grids run the longest query
+// tiles first.
 
 #include <climits>
 
@@ -43,8 +50,10 @@
 namespace faq {
 namespace {
 
-constexpr int BM = 128;  // queries per workgroup
-constexpr int BN = 128;  // keys per tile = probability tile
+constexpr int NW = 8;          // waves per workgroup
+constexpr int NTHR = NW * 64;  // threads per workgroup
+constexpr int BM = NW * 32;    // queries per workgroup
+constexpr int BN = 128;        // keys per tile = probability tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Key order inside a V^T tile.  A lane of lane-group g (g = lane / 16) holds,
@@ -71,22 +80,19 @@ FAQ_DEV int vt_key_mx(int col) {
   return 32 * g + 8 * kk + t;
 }
 
-template <bool B>
-struct BoolC {
-  static constexpr bool value = B;
-};
-
 // Row of the K tile read by lane-row i of MFMA block b in the MXFP4 kernel.
 FAQ_DEV int k_row_mx(int b, int i) { return 32 * (i >> 2) + 4 * b + (i & 3); }
 
-// XOR swizzles of 16-byte chunks (bank spreading for the operand reads).
-FAQ_DEV int swz8(int row) { return (row ^ (row >> 3)) & 7; }
-FAQ_DEV int swz4(int row) { return (row ^ (row >> 3)) & 3; }
+// XOR swizzles of the 16-byte chunks of a tile row (bank spreading for
+// the MFMA operand reads, in which 8 consecutive lanes read the same chunk
+// column of 8 consecutive rows).  Each depends only on the row's low bits,
+// so the swizzle of row 16b + i is that of i: an operand address is a
+// per-lane base plus a constant offset per block.
+FAQ_DEV int swz8(int row) { return row & 7; }          // 128-byte rows
+FAQ_DEV int swz4(int row) { return (row >> 1) & 3; }   // 64-byte rows
 FAQ_DEV int swz_mx(int row) {
   return ((((row >> 1) & 1) | (((row >> 5) & 1) << 1)) ^ ((row >> 5) & 3)) & 3;
 }
-// bf16 rows: 16 rows read together hit 16 distinct chunks of a 256-byte row
-FAQ_DEV int swz_bf(int row, int nch) { return row & (nch - 1); }
 
 // Two E4M3 bytes (the low half-word of `w`, or the high one when HI) -> two
 // bf16, exactly.
@@ -95,47 +101,75 @@ FAQ_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
 }
 
+// Geometry of one LDS tile buffer: K rows, V^T rows, then per-key extras
+// (FP8: K scale and 448 w_j as floats; MXFP4: the K block exponents).
+template <int MODE, int D>
+struct Geo {
+  static constexpr int KROW = MODE == ATTN_INT8 ? D : (MODE == ATTN_FP8 ? 2 * D : D / 2);
+  static constexpr int KCH = KROW / 16;  // 16-byte chunks per K row
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VROW = MODE == ATTN_INT8 ? BN : 2 * BN;
+  static constexpr int VCH = VROW / 16;
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int XBYTES = MODE == ATTN_FP8 ? 2 * BN * 4 : (MODE == ATTN_MX ? BN * (D / 32) : 0);
+  static constexpr int VOFF = KBYTES;
+  static constexpr int XOFF = KBYTES + VBYTES;
+  static constexpr int BUF = XOFF + XBYTES;
+  // swizzled chunk of K row `row`
+  static FAQ_DEV int kswz(int row) {
+    if (MODE == ATTN_INT8) return KCH == 8 ? swz8(row) : swz4(row);
+    if (MODE == ATTN_FP8) return row & (KCH - 1);
+    return KCH == 4 ? swz_mx(row) : 0;
+  }
+  static FAQ_DEV int vswz(int row) { return MODE == ATTN_INT8 ? swz8(row) : (row & (VCH - 1)); }
+};
+
 // ------------------------------------------------------------------------
 // Workspace layout (per (b,h), per 128-key tile t):
-//   vt  : V^T of the tile, D rows x 128 keys: INT8 / E4M3 codes (1 byte) or,
-//         for MXFP4, the exactly dequantized values in bf16 (2 bytes)
-//   aux : FP8 only: 128 floats 448 * w_j = 448 * s_v,j / sigma_t
-//   sig : FP8 only: sigma_t = max over the tile's keys of s_v,j
+//   vt  : V^T of the tile, D rows x 128 keys: INT8 codes (1 byte) or, for
+//         FP8 and MXFP4, the exact values in bf16 (2 bytes)
+//   kb  : FP8: K widened to bf16, 128 rows x D (rows past the end are 0)
+//   aux : FP8: 128 K scales then 128 multipliers 448 * w_j (floats);
+//         MXFP4: the K block exponents, 128 rows x D/32 bytes (127 past
+//         the end)
+//   sig : FP8: sigma_t = max over the tile's keys of s_v,j
 // ------------------------------------------------------------------------
 struct WsLayout {
-  size_t vt_off, aux_off, sig_off, total;
+  size_t vt_off, kb_off, aux_off, sig_off, total;
 };
 
 inline WsLayout ws_layout(int mode, int64_t B, int64_t H, int64_t Skv, int64_t D) {
   const int64_t nt = (Skv + BN - 1) / BN;
-  const int64_t tiles = B * H * nt;
+  const size_t tiles = (size_t)(B * H * nt);
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const size_t vbytes = (mode == ATTN_MX) ? 2 : 1;
   WsLayout l{};
   l.vt_off = 0;
-  l.aux_off = up((size_t)tiles * D * BN * vbytes);
-  const size_t aux = (mode == ATTN_FP8) ? (size_t)tiles * BN * 4 : 0;
-  const size_t sig = (mode == ATTN_FP8) ? (size_t)tiles * 4 : 0;
+  l.kb_off = up(tiles * D * BN * (mode == ATTN_INT8 ? 1 : 2));
+  l.aux_off = l.kb_off + up(mode == ATTN_FP8 ? tiles * BN * D * 2 : 0);
+  const size_t aux = mode == ATTN_FP8 ? tiles * 2 * BN * 4 : (mode == ATTN_MX ? tiles * BN * (D / 32) : 0);
   l.sig_off = l.aux_off + up(aux);
-  l.total = l.sig_off + up(sig);
+  l.total = l.sig_off + up(mode == ATTN_FP8 ? tiles * 4 : 0);
   return l;
 }
 
 // ------------------------------------------------------------------------
-// V re-layout, INT8 / FP8 (1-byte codes): V^T per tile in the lane key
-// order; FP8 also gets sigma_t and the per-key multipliers 448 * w_j.
-// grid = (tiles, B*H), 256 threads.
+// Per-call re-layout.  grid = (tiles, B*H), 256 threads; one 128-key tile.
+//   INT8 : V^T codes in the lane key order.
+//   FP8  : K and V^T widened to bf16 (V^T in the lane key order), the
+//          per-key K scales and 448 w_j, and sigma_t.
 // ------------------------------------------------------------------------
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) void k_prep_v(const uint8_t* __restrict__ v, const float* __restrict__ vs,
-                                                int64_t Skv, int kv_block, int64_t nt,
-                                                uint8_t* __restrict__ vt, float* __restrict__ vmul,
-                                                float* __restrict__ sig) {
+__global__ __launch_bounds__(256) void k_prep(const uint8_t* __restrict__ k, const float* __restrict__ ks,
+                                              const uint8_t* __restrict__ v, const float* __restrict__ vs,
+                                              int64_t Skv, int kv_block, int64_t nt, uint8_t* __restrict__ vt,
+                                              uint16_t* __restrict__ kb, float* __restrict__ aux,
+                                              float* __restrict__ sig) {
   __shared__ uint8_t tile[BN][D + 4];
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t k0 = (int64_t)t * BN;
+  const int64_t tile_id = bh * nt + t;
   const uint8_t* src = v + (bh * Skv + k0) * D;
   constexpr int CPR = D / 16;  // 16-byte chunks per key row
   for (int c = threadIdx.x; c < BN * CPR; c += 256) {
@@ -144,52 +178,79 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint8_t* __restrict__ v, c
     if (k0 + kl < Skv) val = *reinterpret_cast<const uint4*>(src + (int64_t)kl * D + cc * 16);
     uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[kl][cc * 16]);
     dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
+    if (FP8) {
+      // K row chunk widened to bf16 (32 bytes)
+      uint4 kv = make_uint4(0, 0, 0, 0);
+      if (k0 + kl < Skv) kv = *reinterpret_cast<const uint4*>(k + (bh * Skv + k0 + kl) * D + cc * 16);
+      uint16_t* kd = kb + (tile_id * BN + kl) * D + cc * 16;
+      *reinterpret_cast<uint4*>(kd) = make_uint4(e4m3x2_to_bf16x2<false>(kv.x), e4m3x2_to_bf16x2<true>(kv.x),
+                                                 e4m3x2_to_bf16x2<false>(kv.y), e4m3x2_to_bf16x2<true>(kv.y));
+      *reinterpret_cast<uint4*>(kd + 8) = make_uint4(e4m3x2_to_bf16x2<false>(kv.z), e4m3x2_to_bf16x2<true>(kv.z),
+                                                     e4m3x2_to_bf16x2<false>(kv.w), e4m3x2_to_bf16x2<true>(kv.w));
+    }
   }
   __syncthreads();
-  uint8_t* out = vt + ((bh * nt) + t) * (int64_t)D * BN;
-  for (int c = threadIdx.x; c < D * (BN / 16); c += 256) {
-    const int d = c / (BN / 16), j = c % (BN / 16);
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t acc = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = 16 * j + 4 * q + r;
-        const int key = FP8 ? vt_key_fp8(col) : vt_key_int8(col);
-        acc |= (uint32_t)tile[key][d] << (8 * r);
-      }
-      w[q] = acc;
-    }
-    *reinterpret_cast<uint4*>(out + (int64_t)d * BN + 16 * j) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
   if (FP8) {
+    uint16_t* out = reinterpret_cast<uint16_t*>(vt) + tile_id * (int64_t)D * BN;
+    for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
+      const int d = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t pair = (uint32_t)tile[vt_key_fp8(c8 + 2 * q)][d] | ((uint32_t)tile[vt_key_fp8(c8 + 2 * q + 1)][d] << 8);
+        w[q] = e4m3x2_to_bf16x2<false>(pair);
+      }
+      *reinterpret_cast<uint4*>(out + (int64_t)d * BN + c8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
     const int kl = threadIdx.x;
-    float s = 0.0f;
-    if (kl < BN && k0 + kl < Skv) s = vs[bh * ((Skv + kv_block - 1) / kv_block) + (k0 + kl) / kv_block];
+    float s = 0.0f, sk = 0.0f;
+    if (kl < BN && k0 + kl < Skv) {
+      const int64_t nblk = (Skv + kv_block - 1) / kv_block;
+      s = vs[bh * nblk + (k0 + kl) / kv_block];
+      sk = ks[bh * nblk + (k0 + kl) / kv_block];
+    }
     float m = wave_max(s);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (kl < BN) vmul[(bh * nt + t) * BN + kl] = (s > 0.0f) ? 448.0f * (s / m) : 0.0f;
-    if (threadIdx.x == 0) sig[bh * nt + t] = m;
+    if (kl < BN) {
+      aux[tile_id * 2 * BN + kl] = sk;
+      aux[tile_id * 2 * BN + BN + kl] = (s > 0.0f) ? 448.0f * (s / m) : 0.0f;
+    }
+    if (threadIdx.x == 0) sig[tile_id] = m;
+  } else {
+    uint8_t* out = vt + tile_id * (int64_t)D * BN;
+    for (int c = threadIdx.x; c < D * (BN / 16); c += 256) {
+      const int d = c / (BN / 16), j = c % (BN / 16);
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc |= (uint32_t)tile[vt_key_int8(16 * j + 4 * q + r)][d] << (8 * r);
+        w[q] = acc;
+      }
+      *reinterpret_cast<uint4*>(out + (int64_t)d * BN + 16 * j) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
 // ------------------------------------------------------------------------
-// V re-layout, MXFP4: V^T per tile as the exact bf16 values E2M1 * 2^E
-// (E from the token's 32-channel block), in the lane key order.
+// MXFP4 re-layout: V^T per tile as the exact bf16 values E2M1 * 2^E (E from
+// the token's 32-channel block), in the lane key order; K block exponents
+// per tile (127 = 2^0 past the end).
 // ------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void k_prep_v_mx(const uint8_t* __restrict__ v,
-                                                   const uint8_t* __restrict__ ve, int64_t Skv,
-                                                   int64_t nt, uint16_t* __restrict__ vt) {
+__global__ __launch_bounds__(256) void k_prep_mx(const uint8_t* __restrict__ v, const uint8_t* __restrict__ ve,
+                                                 const uint8_t* __restrict__ ke, int64_t Skv, int64_t nt,
+                                                 uint16_t* __restrict__ vt, uint8_t* __restrict__ kex) {
   constexpr int NB = D / 32;
   __shared__ uint8_t codes[BN][D / 2 + 4];
   __shared__ uint8_t ex[BN][NB];
   const int t = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t k0 = (int64_t)t * BN;
+  const int64_t tile_id = bh * nt + t;
   for (int c = threadIdx.x; c < BN * (D / 32); c += 256) {
     const int kl = c / (D / 32), cc = c % (D / 32);  // 16-byte chunks of the packed row
     uint4 val = make_uint4(0, 0, 0, 0);
@@ -199,10 +260,12 @@ __global__ __launch_bounds__(256) void k_prep_v_mx(const uint8_t* __restrict__ v
   }
   for (int c = threadIdx.x; c < BN * NB; c += 256) {
     const int kl = c / NB, b = c % NB;
-    ex[kl][b] = (k0 + kl < Skv) ? ve[(bh * Skv + k0 + kl) * NB + b] : (uint8_t)127;
+    const bool ok = k0 + kl < Skv;
+    ex[kl][b] = ok ? ve[(bh * Skv + k0 + kl) * NB + b] : (uint8_t)127;
+    kex[tile_id * BN * NB + c] = ok ? ke[(bh * Skv + k0 + kl) * NB + b] : (uint8_t)127;
   }
   __syncthreads();
-  uint16_t* out = vt + ((bh * nt) + t) * (int64_t)D * BN;
+  uint16_t* out = vt + tile_id * (int64_t)D * BN;
   // 8 output columns (16 bytes) per item
   for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
     const int d = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
@@ -232,83 +295,111 @@ __global__ __launch_bounds__(256) void k_prep_v_mx(const uint8_t* __restrict__ v
 // The attention kernel.
 // ------------------------------------------------------------------------
 struct KParams {
-  int64_t H, Sq, Skv, nt;
+  int64_t H, BH, Sq, Skv, nt;
+  int nqt;
   const uint8_t* q;
   const void* qs;
-  const uint8_t* k;
-  const void* ks;
-  const uint8_t* vt;
-  const float* vmul;
-  const float* sig;
+  const uint8_t* k;      // INT8 / MXFP4: K codes; FP8: bf16 K tiles in the workspace
+  const void* ks;        // INT8: per-head K scale
+  const uint8_t* vt;     // V^T tiles in the workspace
+  const uint8_t* aux;    // FP8: K scales + 448 w_j; MXFP4: K exponents (per tile)
+  const float* sig;      // FP8: sigma_t
   const float* vs_head;  // INT8: per-head V scale
-  int q_block, kv_block;
+  int q_block;
   float c_log2;  // sm_scale * log2(e)
   void* out;
   int out_bf16;
 };
 
-// Raw bytes of one K/V tile (plus its per-key scale data) held in registers
-// between the prefetch issued before a tile's compute and the commit to LDS
-// at the start of the next one, so global-memory latency overlaps compute.
-template <int MODE, int D>
-struct TileRegs {
-  static constexpr int KSRC = (MODE == ATTN_MX) ? D / 2 : D;             // K bytes per key row
-  static constexpr int VSRC = (MODE == ATTN_MX) ? 2 * BN : BN;            // V^T bytes per channel row
-  static constexpr int NK = BN * KSRC / 16 / 256;                         // 16-byte chunks per thread
-  static constexpr int NV = D * VSRC / 16 / 256;
-  uint4 k[NK];
-  uint4 v[NV];
-  float sc;       // FP8: K scale of key tid (tid < 128) or 448 w of key tid-128
-  uint32_t kex;   // MXFP4: 2 K exponent bytes
-};
+using gptr = const __attribute__((address_space(1))) void*;
+using lptr = __attribute__((address_space(3))) void*;
+
+// Copy NCH 16-byte chunks global -> LDS.  The workgroup moves one round of
+// NW * 64 chunks per step (one global_load_lds_dwordx4 per wave, 1 KiB);
+// chunk p = 512 i + 64 wave + lane lands at lds + 16 p and comes from
+// base + off(i), off being the lane's 32-bit byte offset in round i.
+template <int NCH, class Off>
+FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, Off off) {
+  // the tile base is a wave-uniform value held in SGPRs; hiding it from the
+  // optimizer keeps it from turning every copy into a 64-bit per-lane
+  // pointer carried across loop iterations
+  asm volatile("" : "+s"(base));
+  constexpr int ROUNDS = NCH / (NW * 64);
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    const int grp = i * NW * 64 + wave * 64;
+    __builtin_amdgcn_global_load_lds((gptr)(base + (uint32_t)off(i)), (lptr)(lds + grp * 16), 16, 0, 0);
+  }
+  constexpr int REM = NCH - ROUNDS * NW * 64;  // < one round: the first waves take it
+  if (REM > 0) {
+    const int grp = ROUNDS * NW * 64 + wave * 64;
+    if (grp < NCH) {
+      if (REM % 64 == 0 || grp + lane < NCH)
+        __builtin_amdgcn_global_load_lds((gptr)(base + (uint32_t)off(ROUNDS)), (lptr)(lds + grp * 16), 16, 0, 0);
+    }
+  }
+}
 
 template <int MODE, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
-  // K tile in LDS: INT8 codes (D bytes/row), FP8 widened to bf16 (2D bytes),
-  // MXFP4 packed E2M1 (D/2 bytes)
-  constexpr int KB = (MODE == ATTN_MX) ? D / 2 : (MODE == ATTN_FP8 ? 2 * D : D);
-  constexpr int KCH = KB / 16;                           // 16-byte chunks per K row
-  constexpr int VB = (MODE == ATTN_INT8) ? BN : 2 * BN;  // bytes per V^T row in LDS
-  constexpr int VCH = VB / 16;
+__global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
+  using G = Geo<MODE, D>;
   constexpr int DB = D / 16;  // 16-channel output blocks
   constexpr int NB = D / 32;  // MX blocks per row
   constexpr int KK = D / 32;  // bf16 MFMA steps over D
-  using TR = TileRegs<MODE, D>;
-  constexpr int KSCH = TR::KSRC / 16;  // source chunks per K row
-  constexpr int VSCH = TR::VSRC / 16;  // source chunks per V^T row
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[BN * KB];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[D * VB];
-  __shared__ __attribute__((aligned(16))) float sk_lds[BN];
-  __shared__ __attribute__((aligned(16))) float vm_lds[BN];
-  __shared__ __attribute__((aligned(4))) uint8_t kex_lds[BN * NB];
+  // two tile buffers as separate objects: with the loop unrolled by two
+  // every LDS read names one of them statically, so the compiler knows it
+  // does not alias the copy in flight into the other and need not wait
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[G::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[G::BUF];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < NW);
+
+  // ---- work item: (b,h) and query tile
+  int64_t bh;
+  int qt;
+  {
+    const int L = blockIdx.x, nqt = p.nqt;
+    const int BH = (int)p.BH;
+    if ((BH & 7) == 0) {
+      const int xcd = L & 7, j = L >> 3, per = BH >> 3;
+      if (CAUSAL) { qt = nqt - 1 - j / per; bh = xcd + 8 * (j % per); }
+      else { bh = xcd + 8 * (j / nqt); qt = j % nqt; }
+    } else {
+      if (CAUSAL) { qt = nqt - 1 - L / BH; bh = L % BH; }
+      else { bh = L / nqt; qt = L % nqt; }
+    }
+  }
   const int64_t h = bh % p.H;
-  const int nqt = (int)((p.Sq + BM - 1) / BM);
-  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int qbase = qt * BM + wave * 32;
-  const int Skv = (int)p.Skv;
-  const uint8_t* kbase = p.k + bh * p.Skv * TR::KSRC;
-  const uint8_t* vtbase = p.vt + bh * p.nt * (int64_t)D * TR::VSRC;
+  const int Sq = (int)p.Sq, Skv = (int)p.Skv, nt = (int)p.nt;
+  const int qw = qt * BM + wave * 32;  // this wave's first query
+  // last tile this wave computes: its diagonal tile under causal masking
+  // (none when its queries are all past the end); every tile otherwise
+  // (rows past the end are computed on row 0's data and never stored)
+  const int wdiag = CAUSAL ? (qw < Sq ? qw / BN : -1) : INT_MAX;
+  const uint8_t* kbase = p.k + (MODE == ATTN_FP8 ? bh * nt * (int64_t)BN : bh * (int64_t)Skv) * G::KROW;
+  const uint8_t* vtbase = p.vt + bh * nt * (int64_t)G::VBYTES;
+  const uint8_t* auxbase = p.aux + bh * nt * (int64_t)G::XBYTES;
 
   // ---- Q operands and per-query factors
-  uint2 q8[2][KK];   // FP8: the E4M3 bytes of each bf16 MFMA step (widened per step)
-  i32x4 qi8[2][2];   // INT8: 16 bytes per lane per 64-wide step
-  i32x4 qmx[2];      // MXFP4: 32 E2M1 per lane
+  bf16x8 qw8[2][KK];  // FP8: the bf16 images of the E4M3 codes per bf16 MFMA step
+  i32x4 qi8[2][2];    // INT8: 16 bytes per lane per 64-wide step
+  i32x4 qmx[2];       // MXFP4: 32 E2M1 per lane
   int qsc[2];
   float cq[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qi = qbase + qb * 16 + l16;
-    const bool ok = qi < p.Sq;
-    const uint8_t* qrow = p.q + (bh * p.Sq + (ok ? qi : 0)) * TR::KSRC;
+    const int qi = qw + qb * 16 + l16;
+    const bool ok = qi < Sq;
+    const uint8_t* qrow = p.q + (bh * p.Sq + (ok ? qi : 0)) * (MODE == ATTN_MX ? D / 2 : D);
     if (MODE == ATTN_FP8) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         uint2 a = make_uint2(0, 0);
         if (ok) a = *reinterpret_cast<const uint2*>(qrow + 32 * kk + 8 * g);
-        q8[qb][kk] = a;
+        qw8[qb][kk] = __builtin_bit_cast(bf16x8, i32x4{(int)e4m3x2_to_bf16x2<false>(a.x), (int)e4m3x2_to_bf16x2<true>(a.x),
+                                                       (int)e4m3x2_to_bf16x2<false>(a.y), (int)e4m3x2_to_bf16x2<true>(a.y)});
       }
       const float* qs = reinterpret_cast<const float*>(p.qs);
       const int64_t nqs = (p.Sq + p.q_block - 1) / p.q_block;
@@ -340,85 +431,31 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
     }
   }
 
-  // ---- tile prefetch (registers) and commit (LDS)
-  auto prefetch = [&](int t, TR& r) {
+  // ---- tile copy into LDS buffer `buf`.  A lane's chunk in round i is
+  // row i * (512 / CH) + r0, column c0 of the tile: the same swizzled
+  // column every round, 8 KiB further on.
+  const int pw = wave * 64 + lane;
+  const int kr0 = pw / G::KCH;
+  const uint32_t koff0 = (uint32_t)(((pw % G::KCH) ^ G::kswz(kr0)) << 4);
+  const uint32_t voff0 = (uint32_t)((pw / G::VCH) * G::VROW + (((pw % G::VCH) ^ G::vswz(pw / G::VCH)) << 4));
+  auto issue = [&](int t, uint8_t* buf) {
     const int k0 = t * BN;
-#pragma unroll
-    for (int i = 0; i < TR::NK; ++i) {
-      const int c = i * 256 + tid, row = c / KSCH, cc = c % KSCH;
-      r.k[i] = make_uint4(0, 0, 0, 0);
-      if (k0 + row < Skv) r.k[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)(k0 + row) * TR::KSRC + cc * 16);
-    }
-    const uint8_t* vsrc = vtbase + (int64_t)t * D * TR::VSRC;
-#pragma unroll
-    for (int i = 0; i < TR::NV; ++i) {
-      const int c = i * 256 + tid;
-      r.v[i] = *reinterpret_cast<const uint4*>(vsrc + c * 16);
-    }
     if (MODE == ATTN_FP8) {
-      if (tid < BN) {
-        const float* ks = reinterpret_cast<const float*>(p.ks);
-        const int64_t nks = (p.Skv + p.kv_block - 1) / p.kv_block;
-        r.sc = (k0 + tid < Skv) ? ks[bh * nks + (k0 + tid) / p.kv_block] : 0.0f;
-      } else {
-        r.sc = p.vmul[(bh * p.nt + t) * BN + (tid - BN)];
-      }
+      // bf16 K tiles in the workspace, padded with zero rows
+      stage<G::KBYTES / 16>(buf, kbase + (int64_t)k0 * G::KROW, wave, lane,
+                            [&](int i) { return (uint32_t)(i * 8192 + kr0 * G::KROW) + koff0; });
+    } else {
+      // K codes: rows past the end are re-read from the last row (masked)
+      stage<G::KBYTES / 16>(buf, kbase, wave, lane, [&](int i) {
+        const int kr = min(k0 + i * (512 / G::KCH) + kr0, Skv - 1);
+        return (uint32_t)(kr * G::KROW) + koff0;
+      });
     }
-    if (MODE == ATTN_MX) {
-      // 2 exponent bytes per thread (BN * NB <= 512)
-      const uint8_t* kes = reinterpret_cast<const uint8_t*>(p.ks);
-      uint32_t w = 0x7f7fu;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = 2 * tid + j;
-        if (c < BN * NB && k0 + c / NB < Skv) w = (w & ~(0xffu << (8 * j))) | ((uint32_t)kes[(bh * p.Skv + k0) * NB + c] << (8 * j));
-      }
-      r.kex = w;
-    }
-  };
-  auto commit = [&](const TR& r) {
-#pragma unroll
-    for (int i = 0; i < TR::NK; ++i) {
-      const int c = i * 256 + tid, row = c / KSCH, cc = c % KSCH;
-      const uint4 val = r.k[i];
-      if (MODE == ATTN_FP8) {
-        const int sw = swz_bf(row, KCH);
-        const uint4 lo = make_uint4(e4m3x2_to_bf16x2<false>(val.x), e4m3x2_to_bf16x2<true>(val.x),
-                                    e4m3x2_to_bf16x2<false>(val.y), e4m3x2_to_bf16x2<true>(val.y));
-        const uint4 hi = make_uint4(e4m3x2_to_bf16x2<false>(val.z), e4m3x2_to_bf16x2<true>(val.z),
-                                    e4m3x2_to_bf16x2<false>(val.w), e4m3x2_to_bf16x2<true>(val.w));
-        *reinterpret_cast<uint4*>(&k_lds[row * KB + (((2 * cc) ^ sw) * 16)]) = lo;
-        *reinterpret_cast<uint4*>(&k_lds[row * KB + (((2 * cc + 1) ^ sw) * 16)]) = hi;
-      } else {
-        const int sw = (MODE == ATTN_MX) ? (KCH == 4 ? swz_mx(row) : 0) : (KCH == 8 ? swz8(row) : swz4(row));
-        *reinterpret_cast<uint4*>(&k_lds[row * KB + ((cc ^ sw) * 16)]) = val;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TR::NV; ++i) {
-      const int c = i * 256 + tid, row = c / VSCH, cc = c % VSCH;
-      const uint4 val = r.v[i];
-      if (MODE == ATTN_INT8) {
-        *reinterpret_cast<uint4*>(&v_lds[row * VB + ((cc ^ swz8(row)) * 16)]) = val;
-      } else if (MODE == ATTN_FP8) {
-        const int sw = swz_bf(row, VCH);
-        const uint4 lo = make_uint4(e4m3x2_to_bf16x2<false>(val.x), e4m3x2_to_bf16x2<true>(val.x),
-                                    e4m3x2_to_bf16x2<false>(val.y), e4m3x2_to_bf16x2<true>(val.y));
-        const uint4 hi = make_uint4(e4m3x2_to_bf16x2<false>(val.z), e4m3x2_to_bf16x2<true>(val.z),
-                                    e4m3x2_to_bf16x2<false>(val.w), e4m3x2_to_bf16x2<true>(val.w));
-        *reinterpret_cast<uint4*>(&v_lds[row * VB + (((2 * cc) ^ sw) * 16)]) = lo;
-        *reinterpret_cast<uint4*>(&v_lds[row * VB + (((2 * cc + 1) ^ sw) * 16)]) = hi;
-      } else {
-        *reinterpret_cast<uint4*>(&v_lds[row * VB + ((cc ^ swz_bf(row, VCH)) * 16)]) = val;
-      }
-    }
-    if (MODE == ATTN_FP8) {
-      if (tid < BN) sk_lds[tid] = r.sc;
-      else vm_lds[tid - BN] = r.sc;
-    }
-    if (MODE == ATTN_MX) {
-      if (2 * tid < BN * NB) *reinterpret_cast<uint16_t*>(&kex_lds[2 * tid]) = (uint16_t)r.kex;
-    }
+    stage<G::VBYTES / 16>(buf + G::VOFF, vtbase + (int64_t)t * G::VBYTES, wave, lane,
+                          [&](int i) { return (uint32_t)(i * 8192) + voff0; });
+    if (MODE != ATTN_INT8)
+      stage<G::XBYTES / 16>(buf + G::XOFF, auxbase + (int64_t)t * G::XBYTES, wave, lane,
+                            [&](int i) { return (uint32_t)(i * 8192 + pw * 16); });
   };
 
   // Row state.  O holds the output of each row relative to a reference
@@ -432,276 +469,312 @@ __global__ __launch_bounds__(256, 2) void k_attn(const KParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int t_end = CAUSAL ? (qt + 1 < (int)p.nt ? qt + 1 : (int)p.nt) : (int)p.nt;
+  const int qlast = min(Sq, (qt + 1) * BM) - 1;
+  const int t_end = CAUSAL ? min(nt, qlast / BN + 1) : nt;
   const float vscale_i8 = (MODE == ATTN_INT8) ? p.vs_head[h] * (1.0f / 127.0f) : 1.0f;
 
-  TR regs;
-  prefetch(0, regs);
-  for (int t = 0; t < t_end; ++t) {
+  auto step = [&](int t, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
     const int k0 = t * BN;
-    __syncthreads();  // every wave is done reading the previous tile
-    commit(regs);
+    // this wave's copies of tile t have landed; the barrier makes every
+    // wave's copies visible and retires all reads of the other buffer
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (t + 1 < t_end) prefetch(t + 1, regs);  // in flight during this tile's compute
+    if (t + 1 < t_end) issue(t + 1, nxt);
+    if (t > wdiag) return;
     // the ragged last tile and the causal diagonal need a per-key validity
     // test; the other tiles skip it (uniform branch)
-    const bool masked = (k0 + BN > Skv) || (CAUSAL && t == qt);
+    const bool masked = (k0 + BN > Skv) || (CAUSAL && t == wdiag);
+    const uint8_t* Kt = cur;
+    const uint8_t* Vl = cur + G::VOFF;
+    const float* Xt = reinterpret_cast<const float*>(cur + G::XOFF);
 
-    // ---- S^T = K Q^T: score of (query qb*16 + l16, key of block b at
-    // output row 4g + r)
-    f32x4 s[2][8];
-    if (MODE == ATTN_FP8) {
-#pragma unroll
-      for (int b = 0; b < 8; ++b) s[0][b] = s[1][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        bf16x8 qop[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          qop[qb] = __builtin_bit_cast(bf16x8, i32x4{(int)e4m3x2_to_bf16x2<false>(q8[qb][kk].x),
-                                                     (int)e4m3x2_to_bf16x2<true>(q8[qb][kk].x),
-                                                     (int)e4m3x2_to_bf16x2<false>(q8[qb][kk].y),
-                                                     (int)e4m3x2_to_bf16x2<true>(q8[qb][kk].y)});
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const int row = 16 * b + l16;
-          const bf16x8 kop =
-              *reinterpret_cast<const bf16x8*>(&k_lds[row * KB + (((4 * kk + g) ^ swz_bf(row, KCH)) * 16)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qb], s[qb][b], 0, 0, 0);
-        }
-      }
-    } else if (MODE == ATTN_INT8) {
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int row = 16 * b + l16;
-        i32x4 si[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
-#pragma unroll
-        for (int kk = 0; kk < D / 64; ++kk) {
-          const int cc = 4 * kk + g;
-          const int sw = (KCH == 8 ? swz8(row) : swz4(row));
-          const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((cc ^ sw) * 16)]);
-          const i32x4 kop = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            si[qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qi8[qb][kk], si[qb], 0, 0, 0);
-        }
-        // exact int32 scores (|s| < 2^21): the float conversion is exact
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[qb][b] = f32x4{(float)si[qb][0], (float)si[qb][1], (float)si[qb][2], (float)si[qb][3]};
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int row = k_row_mx(b, l16);
-        i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
-        int ksc = 127;
-        if (32 * g < D) {
-          const int sw = (KCH == 4 ? swz_mx(row) : 0);
-          const uint4 a = *reinterpret_cast<const uint4*>(&k_lds[row * KB + ((g ^ sw) * 16)]);
-          kop = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-          ksc = kex_lds[row * NB + g];
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const i32x4 qv = qmx[qb];
-          const i32x8 qop = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
-          s[qb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                      4, 4, 0, ksc, 0, qsc[qb]);
-        }
-      }
-    }
-
-    // ---- scores in "t units" (t * cq is the log2-domain score)
-    if (MODE == ATTN_FP8) {
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const float4 skv = *reinterpret_cast<const float4*>(&sk_lds[16 * b + 4 * g]);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[qb][b][0] *= skv.x; s[qb][b][1] *= skv.y; s[qb][b][2] *= skv.z; s[qb][b][3] *= skv.w;
-        }
-      }
-    }
-    if (masked) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qi = qbase + qb * 16 + l16;
-        const int lim = (CAUSAL ? min(Skv, qi + 1) : Skv) - k0;  // keys kl < lim are valid
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kl = (MODE == ATTN_MX) ? (32 * g + 4 * b + r) : (16 * b + 4 * g + r);
-            s[qb][b][r] = (kl < lim) ? s[qb][b][r] : -INFINITY;
-          }
-      }
-    }
-    float mt[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float m = -INFINITY;
-      if (MODE == ATTN_INT8 && !masked) {
-        // exact integer scores: integer max (no float canonicalization)
-        int mi = INT_MIN;
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-          mi = max(max(mi, max((int)s[qb][b][0], (int)s[qb][b][1])), max((int)s[qb][b][2], (int)s[qb][b][3]));
-        m = (float)mi;
-      } else {
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-          m = fmaxf(fmaxf(m, fmaxf(s[qb][b][0], s[qb][b][1])), fmaxf(s[qb][b][2], s[qb][b][3]));
-      }
-      mt[qb] = rows4_max(m);
-    }
-
-    // ---- probabilities, tile sums, quantized P operands, row combination
-    i32x8 pi8[2];      // INT8: rne(127 p) bytes, keys in vt_key_int8 order
+    // One query block at a time: scores, tile max, probabilities and the
+    // quantized P operand of block qb, so only one block's scores are held
+    // in registers (the K operands are read once per query block).
+    i32x4 pi8[2][2];   // INT8: rne(127 p) bytes, keys in vt_key_int8 order
     i32x4 pbf[2][4];   // FP8 / MXFP4: bf16 images of the quantized p, per step kk
     float rscale[2], bvi8[2];
     bool rescale_any = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float m = mt[qb];
-      const float msafe = (m == -INFINITY) ? 0.0f : m;
-      float lsum = 0.0f, pmax = 0.0f;
-      if (MODE == ATTN_INT8) {
-        // p = 2^(s cq - m cq); p at the maximum may differ from 1 by an ulp,
-        // which cannot move rne(127 p)
-        const float mc = msafe * cq[qb];
+      // The two query blocks read the same K operands and per-key factors;
+      // an opaque zero offset keeps the compiler from reusing the first
+      // block's reads (which would hold them all in registers) - LDS reads
+      // are cheap, registers are not.
+      int zq = 0;
+      asm volatile("" : "+v"(zq));
+      const uint8_t* Kl = Kt + zq;
+      const float* Xf = Xt + zq;
+      const uint8_t* Xb = reinterpret_cast<const uint8_t*>(Xt) + zq;
+      // ---- S^T = K Q^T: score of (query qb*16 + l16, key of block b at
+      // output row 4g + r).  Operands of block b+1 are read from LDS while
+      // block b multiplies, and the VALU work on block b-1 fills the MFMA
+      // shadow; a scheduling fence closes each step, which bounds the
+      // registers held by operands in flight.
+      f32x4 s[8];
+      int mi = INT_MIN;
+      if (MODE == ATTN_FP8) {
+        bf16x8 kop[1][KK];
+        auto kload = [&](int bb, bf16x8 (&dst)[KK]) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
+          for (int kk = 0; kk < KK; ++kk)
+            dst[kk] = *reinterpret_cast<const bf16x8*>(&Kl[(16 * bb + l16) * G::KROW + (((4 * kk + g) ^ G::kswz(l16)) << 4)]);
+        };
+        auto kscale = [&](int bb) {
+          const float4 skv = *reinterpret_cast<const float4*>(&Xf[16 * bb + 4 * g]);
+          s[bb][0] *= skv.x; s[bb][1] *= skv.y; s[bb][2] *= skv.z; s[bb][3] *= skv.w;
+        };
+        // (one block of K operands in flight: 16 registers each)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][r], cq[qb], -mc));
-            s[qb][b][r] = pv;
-            lsum += pv;
+        for (int bb = 0; bb < 8; ++bb) {
+          kload(bb, kop[0]);
+          s[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][0], qw8[qb][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int kk = 1; kk < KK; ++kk)
+            s[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][kk], qw8[qb][kk], s[bb], 0, 0, 0);
+          if (bb > 0) kscale(bb - 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        kscale(7);
+      } else if (MODE == ATTN_INT8) {
+        constexpr int K8 = D / 64;
+        i32x4 kop[2][K8];
+        i32x4 si[2];
+        auto kload = [&](int bb, i32x4 (&dst)[K8]) {
+#pragma unroll
+          for (int kk = 0; kk < K8; ++kk) {
+            const uint4 v = *reinterpret_cast<const uint4*>(&Kl[(16 * bb + l16) * G::KROW + (((4 * kk + g) ^ G::kswz(l16)) << 4)]);
+            dst[kk] = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
           }
-      } else {
+        };
+        // exact int32 scores (|s| < 2^21): the float conversion is exact
+        auto post = [&](int bb) {
+          const i32x4 v = si[bb & 1];
+          if (!masked) mi = max(mi, max(max(v[0], v[1]), max(v[2], v[3])));
+          s[bb] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        };
+        kload(0, kop[0]);
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
+        for (int bb = 0; bb < 8; ++bb) {
+          if (bb + 1 < 8) kload(bb + 1, kop[(bb + 1) & 1]);
+          si[bb & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[bb & 1][0], qi8[qb][0], i32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+          for (int kk = 1; kk < K8; ++kk)
+            si[bb & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[bb & 1][kk], qi8[qb][kk], si[bb & 1], 0, 0, 0);
+          if (bb > 0) post(bb - 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        post(7);
+      } else {
+        i32x8 kop[2];
+        int ksc[2];
+        auto kload = [&](int bb, i32x8& dst, int& sc) {
+          const int row = k_row_mx(bb, l16);
+          dst = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+          sc = 127;
+          if (32 * g < D) {
+            const uint4 v = *reinterpret_cast<const uint4*>(&Kl[row * G::KROW + ((g ^ G::kswz(row)) << 4)]);
+            dst = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            sc = Xb[row * NB + g];
+          }
+        };
+        const i32x4 qv = qmx[qb];
+        const i32x8 qop = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
+        kload(0, kop[0], ksc[0]);
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {
+          if (bb + 1 < 8) kload(bb + 1, kop[(bb + 1) & 1], ksc[(bb + 1) & 1]);
+          s[bb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop[bb & 1], qop, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                   4, 4, 0, ksc[bb & 1], 0, qsc[qb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      if (masked) {
+        // key kl of the tile is valid when kl < lim; the lane's own part of
+        // kl is folded into the limit so the rest is an immediate
+        const int qi = qw + qb * 16 + l16;
+        const int lim = (CAUSAL ? min(Skv, qi + 1) : Skv) - k0;
+        const int rel = lim - (MODE == ATTN_MX ? 32 * g : 4 * g);
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            // (x - m) is exactly 0 at the tile maximum, so p = 1 there exactly
-            const float pv = __builtin_amdgcn_exp2f((s[qb][b][r] - msafe) * cq[qb]);
-            s[qb][b][r] = pv;
-            lsum += pv;
-            if (MODE == ATTN_MX) pmax = fmaxf(pmax, pv);
+            const int kc = (MODE == ATTN_MX) ? (4 * bb + r) : (16 * bb + r);
+            s[bb][r] = (kc < rel) ? s[bb][r] : -INFINITY;
           }
       }
-      lsum = rows4_sum(lsum);
 
-      // online combination of tiles
+      // ---- tile max, then the row combination factors: a rescales what
+      // was accumulated so far, bt weights this tile
+      float m;
+      if (MODE == ATTN_INT8 && !masked) {
+        m = (float)mi;
+      } else {
+        m = -INFINITY;
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) m = fmaxf(fmaxf(m, fmaxf(s[bb][0], s[bb][1])), fmaxf(s[bb][2], s[bb][3]));
+      }
+      m = rows4_max(m);
       const float mnew = fmaxf(M[qb], m);
       const float a = __builtin_amdgcn_exp2f((M[qb] - mnew) * cq[qb]);
       const float bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - mnew) * cq[qb]);
-      L[qb] = L[qb] * a + lsum * bt;
       M[qb] = mnew;
-
+      // bf16-MFMA modes: new reference factor f = bt (times sigma_t / 448
+      // for FP8); a row whose tile is negligible (bt < 2^-64) keeps its
+      // reference and contributes nothing, which keeps O bounded.
+      bool live = true;
       if (MODE == ATTN_INT8) {
-        int w[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          // rne(127 p) lands in the low byte of fma(p, 127, 1.5 * 2^23)
-          const uint32_t f0 = __float_as_uint(__builtin_fmaf(s[qb][b][0], 127.0f, 12582912.0f));
-          const uint32_t f1 = __float_as_uint(__builtin_fmaf(s[qb][b][1], 127.0f, 12582912.0f));
-          const uint32_t f2 = __float_as_uint(__builtin_fmaf(s[qb][b][2], 127.0f, 12582912.0f));
-          const uint32_t f3 = __float_as_uint(__builtin_fmaf(s[qb][b][3], 127.0f, 12582912.0f));
-          const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x0c0c0400u);
-          const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x0c0c0400u);
-          w[b] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
-        }
-        pi8[qb] = i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
         rscale[qb] = a;
         bvi8[qb] = bt * vscale_i8;
-        rescale_any |= (a != 1.0f);
       } else {
-        // bf16-MFMA modes: new reference factor f = bt (times sigma_t / 448
-        // for FP8); a row whose tile is negligible (bt < 2^-64) keeps its
-        // reference and contributes nothing, which keeps O bounded.
         float ft = bt;
-        if (MODE == ATTN_FP8) ft *= p.sig[bh * p.nt + t] * (1.0f / 448.0f);
-        const bool live = bt >= 0x1p-64f;
-        const float r = live ? (fref[qb] * a / ft) : a;
+        if (MODE == ATTN_FP8) ft *= p.sig[bh * nt + t] * (1.0f / 448.0f);
+        live = bt >= 0x1p-64f;
+        rscale[qb] = live ? (fref[qb] * a / ft) : a;
         fref[qb] = live ? ft : fref[qb];
-        rscale[qb] = r;
-        rescale_any |= (r != 1.0f);
-        if (MODE == ATTN_FP8) {
+      }
+      rescale_any |= (rscale[qb] != 1.0f);
+
+      // ---- probabilities, tile sum and the quantized P operand
+      const float ms = (m == -INFINITY) ? 0.0f : m;
+      const float mc = ms * cq[qb];
+      float ls[2] = {0.f, 0.f};
+      float pmax = 0.0f;
 #pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            const float4 vm = *reinterpret_cast<const float4*>(&vm_lds[16 * b + 4 * g]);
-            // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
-            int e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][b][0] * vm.x, s[qb][b][1] * vm.y, 0, false);
-            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[qb][b][2] * vm.z, s[qb][b][3] * vm.w, e8, true);
-            pbf[qb][b >> 1][2 * (b & 1)] = live ? (int)e4m3x2_to_bf16x2<false>((uint32_t)e8) : 0;
-            pbf[qb][b >> 1][2 * (b & 1) + 1] = live ? (int)e4m3x2_to_bf16x2<true>((uint32_t)e8) : 0;
+      for (int bb = 0; bb < 8; ++bb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pv;
+          if (MODE == ATTN_INT8) {
+            // p = 2^(s cq - m cq); p at the maximum may differ from 1 by an
+            // ulp, which cannot move rne(127 p)
+            pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], cq[qb], -mc));
+          } else {
+            // (x - m) is exactly 0 at the tile maximum, so p = 1 there exactly
+            pv = __builtin_amdgcn_exp2f((s[bb][r] - ms) * cq[qb]);
           }
-        } else {
-          // this lane's 32 keys are one MX group: local max -> shared
-          // exponent; p -> E2M1(p / 2^E) * 2^E, exact in bf16
-          const int E = mx_exponent(pmax);
-          const float sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
+          s[bb][r] = pv;
+          ls[r & 1] += pv;
+          if (MODE == ATTN_MX) pmax = fmaxf(pmax, pv);
+        }
+        if (MODE == ATTN_INT8) {
+          // rne(127 p) lands in the low byte of fma(p, 127, 1.5 * 2^23)
+          const uint32_t f0 = __float_as_uint(__builtin_fmaf(s[bb][0], 127.0f, 12582912.0f));
+          const uint32_t f1 = __float_as_uint(__builtin_fmaf(s[bb][1], 127.0f, 12582912.0f));
+          const uint32_t f2 = __float_as_uint(__builtin_fmaf(s[bb][2], 127.0f, 12582912.0f));
+          const uint32_t f3 = __float_as_uint(__builtin_fmaf(s[bb][3], 127.0f, 12582912.0f));
+          const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x0c0c0400u);
+          pi8[qb][bb >> 2][bb & 3] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        } else if (MODE == ATTN_FP8) {
+          // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
+          const float4 vm = *reinterpret_cast<const float4*>(&Xf[BN + 16 * bb + 4 * g]);
+          int e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][0] * vm.x, s[bb][1] * vm.y, 0, false);
+          e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][2] * vm.z, s[bb][3] * vm.w, e8, true);
+          pbf[qb][bb >> 1][2 * (bb & 1)] = live ? (int)e4m3x2_to_bf16x2<false>((uint32_t)e8) : 0;
+          pbf[qb][bb >> 1][2 * (bb & 1) + 1] = live ? (int)e4m3x2_to_bf16x2<true>((uint32_t)e8) : 0;
+        }
+      }
+      if (MODE == ATTN_MX) {
+        // this lane's 32 keys are one MX group: local max -> shared
+        // exponent; p -> E2M1(p / 2^E) * 2^E, exact in bf16
+        const int E = mx_exponent(pmax);
+        const float sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
 #pragma unroll
-          for (int b = 0; b < 8; ++b) {
+        for (int bb = 0; bb < 8; ++bb) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const uint32_t f4 =
-                  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s[qb][b][2 * hh], s[qb][b][2 * hh + 1], sc, 0);
-              const int v2 = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
-              pbf[qb][b >> 1][2 * (b & 1) + hh] = live ? v2 : 0;
-            }
+          for (int hh = 0; hh < 2; ++hh) {
+            const uint32_t f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s[bb][2 * hh], s[bb][2 * hh + 1], sc, 0);
+            const int v2 = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
+            pbf[qb][bb >> 1][2 * (bb & 1) + hh] = live ? v2 : 0;
           }
         }
       }
+      L[qb] = L[qb] * a + rows4_sum(ls[0] + ls[1]) * bt;
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- O^T += V^T P^T (per 16-channel block)
-    const bool do_rescale = __any(rescale_any);
+    // ---- O^T += V^T P^T (per 16-channel block), V operands of block db+1
+    // read while block db multiplies
+    if (MODE == ATTN_INT8) {
+      const bool do_rescale = __any(rescale_any);
+      i32x4 vop[2][2], ci[2][2];
+      auto vload = [&](int db, i32x4 (&dst)[2]) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int row = 16 * db + l16;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&Vl[(16 * db + l16) * G::VROW + (((2 * g + h2) ^ G::vswz(l16)) << 4)]);
+          dst[h2] = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        }
+      };
+      auto accum = [&](int db) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[qb][db][r] = __builtin_fmaf((float)ci[qb][db & 1][r], bvi8[qb], O[qb][db][r]);
+      };
+      // the running max moves rarely once a row has seen its largest
+      // scores: rescale only when some row of the wave needs it
       if (do_rescale) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) O[qb][db][r] *= rscale[qb];
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[qb][db][r] *= rscale[qb];
       }
-      if (MODE == ATTN_INT8) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&v_lds[row * VB + (((2 * g) ^ swz8(row)) * 16)]);
-        const uint4 c = *reinterpret_cast<const uint4*>(&v_lds[row * VB + (((2 * g + 1) ^ swz8(row)) * 16)]);
-        const i32x4 v0 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-        const i32x4 v1 = {(int)c.x, (int)c.y, (int)c.z, (int)c.w};
+      vload(0, vop[0]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        if (db + 1 < DB) vload(db + 1, vop[(db + 1) & 1]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const i32x4 p0 = {pi8[qb][0], pi8[qb][1], pi8[qb][2], pi8[qb][3]};
-          const i32x4 p1 = {pi8[qb][4], pi8[qb][5], pi8[qb][6], pi8[qb][7]};
-          i32x4 ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(v0, p0, i32x4{0, 0, 0, 0}, 0, 0, 0);
-          ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(v1, p1, ci, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[qb][db][r] = __builtin_fmaf((float)ci[r], bvi8[qb], O[qb][db][r]);
+          ci[qb][db & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vop[db & 1][0], pi8[qb][0], i32x4{0, 0, 0, 0}, 0, 0, 0);
+          ci[qb][db & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vop[db & 1][1], pi8[qb][1], ci[qb][db & 1], 0, 0, 0);
         }
-      } else {
-        const int sw = swz_bf(row, VCH);
+        if (db > 0) accum(db - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      accum(DB - 1);
+    } else {
+      bf16x8 vop[2][4];
+      auto vload = [&](int db, bf16x8 (&dst)[4]) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 vop = *reinterpret_cast<const bf16x8*>(&v_lds[row * VB + (((4 * kk + g) ^ sw) * 16)]);
+        for (int kk = 0; kk < 4; ++kk)
+          dst[kk] = *reinterpret_cast<const bf16x8*>(&Vl[(16 * db + l16) * G::VROW + (((4 * kk + g) ^ G::vswz(l16)) << 4)]);
+      };
+      vload(0, vop[0]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        if (db + 1 < DB) vload(db + 1, vop[(db + 1) & 1]);
+        // the reference factor moves almost every tile: rescale unconditionally
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[qb][db][r] *= rscale[qb];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
-            O[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, __builtin_bit_cast(bf16x8, pbf[qb][kk]),
+            O[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db & 1][kk], __builtin_bit_cast(bf16x8, pbf[qb][kk]),
                                                                 O[qb][db], 0, 0, 0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+
+  issue(0, buf0);
+#pragma clang loop unroll(disable)
+  for (int t = 0; t < t_end; t += 2) {
+    step(t, buf0, buf1);
+    if (t + 1 < t_end) step(t + 1, buf1, buf0);
   }
 
   // ---- normalize, store
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qi = qbase + qb * 16 + l16;
-    if (qi >= p.Sq) continue;
+    const int qi = qw + qb * 16 + l16;
+    if (qi >= Sq) continue;
     const float inv = fref[qb] / L[qb];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -723,32 +796,35 @@ template <int MODE, int D>
 hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   const int64_t nt = (a.Skv + BN - 1) / BN;
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
-  uint8_t* vt = ws + l.vt_off;
   dim3 pgrid((unsigned)nt, (unsigned)(a.B * a.H));
   if (MODE == ATTN_MX) {
-    k_prep_v_mx<D><<<pgrid, 256, 0, st>>>((const uint8_t*)a.v_codes, (const uint8_t*)a.v_scales, a.Skv, nt,
-                                          reinterpret_cast<uint16_t*>(vt));
+    k_prep_mx<D><<<pgrid, 256, 0, st>>>((const uint8_t*)a.v_codes, (const uint8_t*)a.v_scales,
+                                        (const uint8_t*)a.k_scales, a.Skv, nt,
+                                        reinterpret_cast<uint16_t*>(ws + l.vt_off), ws + l.aux_off);
   } else {
-    k_prep_v<D, MODE == ATTN_FP8><<<pgrid, 256, 0, st>>>(
-        (const uint8_t*)a.v_codes, (const float*)a.v_scales, a.Skv, a.kv_block, nt, vt,
+    k_prep<D, MODE == ATTN_FP8><<<pgrid, 256, 0, st>>>(
+        (const uint8_t*)a.k_codes, (const float*)a.k_scales, (const uint8_t*)a.v_codes, (const float*)a.v_scales,
+        a.Skv, a.kv_block, nt, ws + l.vt_off, reinterpret_cast<uint16_t*>(ws + l.kb_off),
         reinterpret_cast<float*>(ws + l.aux_off), reinterpret_cast<float*>(ws + l.sig_off));
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   KParams p{};
-  p.H = a.H; p.Sq = a.Sq; p.Skv = a.Skv; p.nt = nt;
+  p.H = a.H; p.BH = a.B * a.H; p.Sq = a.Sq; p.Skv = a.Skv; p.nt = nt;
+  p.nqt = (int)((a.Sq + BM - 1) / BM);
   p.q = (const uint8_t*)a.q_codes; p.qs = a.q_scales;
-  p.k = (const uint8_t*)a.k_codes; p.ks = a.k_scales;
-  p.vt = vt;
-  p.vmul = reinterpret_cast<const float*>(ws + l.aux_off);
+  p.k = MODE == ATTN_FP8 ? ws + l.kb_off : (const uint8_t*)a.k_codes;
+  p.ks = a.k_scales;
+  p.vt = ws + l.vt_off;
+  p.aux = ws + l.aux_off;
   p.sig = reinterpret_cast<const float*>(ws + l.sig_off);
   p.vs_head = (const float*)a.v_scales;
-  p.q_block = a.q_block; p.kv_block = a.kv_block;
+  p.q_block = a.q_block;
   p.c_log2 = a.sm_scale * kLog2e;
   p.out = a.out; p.out_bf16 = a.out_bf16;
-  dim3 grid((unsigned)((a.Sq + BM - 1) / BM), (unsigned)(a.B * a.H));
-  if (a.causal) k_attn<MODE, D, true><<<grid, 256, 0, st>>>(p);
-  else k_attn<MODE, D, false><<<grid, 256, 0, st>>>(p);
+  dim3 grid((unsigned)(p.nqt * p.BH));
+  if (a.causal) k_attn<MODE, D, true><<<grid, NTHR, 0, st>>>(p);
+  else k_attn<MODE, D, false><<<grid, NTHR, 0, st>>>(p);
   return hipGetLastError();
 }
 

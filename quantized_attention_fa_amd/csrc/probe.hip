@@ -164,3 +164,27 @@ extern "C" int faq_probe_cvt_up(const uint32_t* w, int n, float fp4_scale, uint3
   k_probe_cvt_up<<<(n + 255) / 256, 256>>>(w, n, fp4_scale, e4_lo, e4_hi, f4);
   return (int)hipDeviceSynchronize();
 }
+
+namespace {
+// global_load_lds_dwordx4: each lane's 16 source bytes land at the LDS
+// address given to the instruction plus 16 * lane.  One wave copies 64
+// chunks src[perm[lane]] into bytes 1024..2047 of a zeroed 2 KiB buffer,
+// which is then written out whole.
+__global__ void k_probe_gll(const uint8_t* src, const int* perm, uint8_t* out) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[2048];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < 512; i += 64) reinterpret_cast<uint32_t*>(buf)[i] = 0u;
+  __syncthreads();
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + perm[lane] * 16),
+                                   (__attribute__((address_space(3))) void*)(buf + 1024), 16, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  for (int i = lane; i < 512; i += 64) reinterpret_cast<uint32_t*>(out)[i] = reinterpret_cast<uint32_t*>(buf)[i];
+}
+}  // namespace
+
+// src: 1024 bytes; perm: 64 ints in [0, 64); out: 2048 bytes.
+extern "C" int faq_probe_global_load_lds(const uint8_t* src, const int* perm, uint8_t* out) {
+  k_probe_gll<<<1, 64>>>(src, perm, out);
+  return (int)hipDeviceSynchronize();
+}

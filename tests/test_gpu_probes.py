@@ -161,3 +161,18 @@ def test_cvt_up_to_bf16(lib):
         assert np.array_equal(bf[1](hi), F.E4M3_VALUES[codes[:, 3]])
         assert np.array_equal(bf[0](f4), F.e2m1_decode(codes[:, 0] & 0xF) * scale)
         assert np.array_equal(bf[1](f4), F.e2m1_decode(codes[:, 0] >> 4) * scale)
+
+
+def test_global_load_lds_layout(lib):
+    """Each lane's 16 bytes land at the instruction's LDS address + 16 * lane
+    (the attention kernel stages its K / V^T tiles this way)."""
+    g = np.random.default_rng(4)
+    src = g.integers(0, 256, 1024).astype(np.uint8)
+    perm = g.permutation(64).astype(np.int32)
+    s_d, p_d = _d(src), _d(perm)
+    out = torch.zeros(2048, dtype=torch.uint8, device=DEV)
+    assert lib.faq_probe_global_load_lds(_p(s_d), _p(p_d), _p(out)) == 0
+    o = out.cpu().numpy()
+    assert not o[:1024].any()
+    want = src.reshape(64, 16)[perm].reshape(-1)
+    assert np.array_equal(o[1024:], want)
