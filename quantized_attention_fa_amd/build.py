@@ -44,9 +44,14 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
+# The attention kernels handle no NaN (codes are finite; masked scores are
+# -inf): without NaN semantics max/min need no quieting of their inputs.
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -83,16 +83,15 @@ FAQ_DEV int vt_key_mx(int col) {
 // Row of the K tile read by lane-row i of MFMA block b in the MXFP4 kernel.
 FAQ_DEV int k_row_mx(int b, int i) { return 32 * (i >> 2) + 4 * b + (i & 3); }
 
-// XOR swizzles of the 16-byte chunks of a tile row (bank spreading for
-// the MFMA operand reads, in which 8 consecutive lanes read the same chunk
-// column of 8 consecutive rows).  Each depends only on the row's low bits,
-// so the swizzle of row 16b + i is that of i: an operand address is a
-// per-lane base plus a constant offset per block.
-FAQ_DEV int swz8(int row) { return row & 7; }          // 128-byte rows
-FAQ_DEV int swz4(int row) { return (row >> 1) & 3; }   // 64-byte rows
-FAQ_DEV int swz_mx(int row) {
-  return ((((row >> 1) & 1) | (((row >> 5) & 1) << 1)) ^ ((row >> 5) & 3)) & 3;
-}
+// XOR swizzles of the 16-byte chunks of a tile row.  An MFMA operand read
+// has 16 consecutive lanes fetch the same chunk column of 16 consecutive
+// rows; the LDS serves 64 banks (256 bytes) per cycle, so those 16 reads
+// must land in 16 distinct 16-byte bank groups.  Each swizzle depends only
+// on row bits that are the same for rows i and 16b + i, so an operand
+// address is a per-lane base plus a constant offset per block.
+FAQ_DEV int swz8(int row) { return (row >> 1) & 7; }   // 128-byte rows
+FAQ_DEV int swz4(int row) { return (row >> 2) & 3; }   // 64-byte rows
+FAQ_DEV int swz_mx(int row) { return (row >> 5) & 3; } // MXFP4 K rows (64 bytes, rows 32(i/4) + 4b + i%4)
 
 // Two E4M3 bytes (the low half-word of `w`, or the high one when HI) -> two
 // bf16, exactly.
@@ -615,6 +614,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) m = fmaxf(fmaxf(m, fmaxf(s[bb][0], s[bb][1])), fmaxf(s[bb][2], s[bb][3]));
       }
+      const float mlane = m;  // max over this lane's keys (MXFP4: its 32-key group)
       m = rows4_max(m);
       const float mnew = fmaxf(M[qb], m);
       const float a = __builtin_amdgcn_exp2f((M[qb] - mnew) * cq[qb]);
@@ -636,11 +636,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
       }
       rescale_any |= (rscale[qb] != 1.0f);
 
-      // ---- probabilities, tile sum and the quantized P operand
-      const float ms = (m == -INFINITY) ? 0.0f : m;
+      // ---- probabilities, tile sum and the quantized P operand.  A row
+      // that is not live takes +inf as its reference, so all its p are 0.
+      const float ms = (m == -INFINITY) ? 0.0f : (live ? m : INFINITY);
       const float mc = ms * cq[qb];
       float ls[2] = {0.f, 0.f};
-      float pmax = 0.0f;
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
 #pragma unroll
@@ -656,7 +656,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
           }
           s[bb][r] = pv;
           ls[r & 1] += pv;
-          if (MODE == ATTN_MX) pmax = fmaxf(pmax, pv);
         }
         if (MODE == ATTN_INT8) {
           // rne(127 p) lands in the low byte of fma(p, 127, 1.5 * 2^23)
@@ -672,13 +671,15 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
           const float4 vm = *reinterpret_cast<const float4*>(&Xf[BN + 16 * bb + 4 * g]);
           int e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][0] * vm.x, s[bb][1] * vm.y, 0, false);
           e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][2] * vm.z, s[bb][3] * vm.w, e8, true);
-          pbf[qb][bb >> 1][2 * (bb & 1)] = live ? (int)e4m3x2_to_bf16x2<false>((uint32_t)e8) : 0;
-          pbf[qb][bb >> 1][2 * (bb & 1) + 1] = live ? (int)e4m3x2_to_bf16x2<true>((uint32_t)e8) : 0;
+          pbf[qb][bb >> 1][2 * (bb & 1)] = (int)e4m3x2_to_bf16x2<false>((uint32_t)e8);
+          pbf[qb][bb >> 1][2 * (bb & 1) + 1] = (int)e4m3x2_to_bf16x2<true>((uint32_t)e8);
         }
       }
       if (MODE == ATTN_MX) {
         // this lane's 32 keys are one MX group: local max -> shared
-        // exponent; p -> E2M1(p / 2^E) * 2^E, exact in bf16
+        // exponent; p -> E2M1(p / 2^E) * 2^E, exact in bf16.  The group's
+        // largest p is the same function of the lane's largest score.
+        const float pmax = __builtin_amdgcn_exp2f((mlane - ms) * cq[qb]);
         const int E = mx_exponent(pmax);
         const float sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
 #pragma unroll
@@ -687,7 +688,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
           for (int hh = 0; hh < 2; ++hh) {
             const uint32_t f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s[bb][2 * hh], s[bb][2 * hh + 1], sc, 0);
             const int v2 = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
-            pbf[qb][bb >> 1][2 * (bb & 1) + hh] = live ? v2 : 0;
+            pbf[qb][bb >> 1][2 * (bb & 1) + hh] = v2;
           }
         }
       }

@@ -188,3 +188,16 @@ extern "C" int faq_probe_global_load_lds(const uint8_t* src, const int* perm, ui
   k_probe_gll<<<1, 64>>>(src, perm, out);
   return (int)hipDeviceSynchronize();
 }
+
+namespace {
+// v_cvt_pk_u8_f32 on n floats, one byte each (byte 0 of a zero word).
+__global__ void k_probe_cvt_u8(const float* x, int n, uint8_t* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_u8_f32(x[i], 0, 0u) & 0xffu);
+}
+}  // namespace
+
+extern "C" int faq_probe_cvt_u8(const float* x, int n, uint8_t* out) {
+  k_probe_cvt_u8<<<(n + 255) / 256, 256>>>(x, n, out);
+  return (int)hipDeviceSynchronize();
+}
