@@ -50,9 +50,17 @@
 namespace faq {
 namespace {
 
-constexpr int NW = 8;          // waves per workgroup
-constexpr int NTHR = NW * 64;  // threads per workgroup
-constexpr int BM = NW * 32;    // queries per workgroup
+// Waves per workgroup: INT8 runs two 4-wave workgroups per CU (their
+// tiles fit twice in LDS, and the two waves sharing a SIMD then come from
+// independent workgroups, so one's softmax overlaps the other's MFMAs);
+// FP8 and MXFP4 tiles are larger and run one 8-wave workgroup per CU.
+template <int MODE>
+struct Waves {
+  static constexpr int NW = MODE == ATTN_INT8 ? 4 : 8;
+  static constexpr int NTHR = NW * 64;  // threads per workgroup
+  static constexpr int BM = NW * 32;    // queries per workgroup
+  static constexpr int WG_PER_CU = 8 / NW;
+};
 constexpr int BN = 128;        // keys per tile = probability tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -115,12 +123,12 @@ struct Geo {
   static constexpr int XOFF = KBYTES + VBYTES;
   static constexpr int BUF = XOFF + XBYTES;
   // swizzled chunk of K row `row`
-  static FAQ_DEV int kswz(int row) {
+  FAQ_DEV int kswz(int row) {
     if (MODE == ATTN_INT8) return KCH == 8 ? swz8(row) : swz4(row);
     if (MODE == ATTN_FP8) return row & (KCH - 1);
     return KCH == 4 ? swz_mx(row) : 0;
   }
-  static FAQ_DEV int vswz(int row) { return MODE == ATTN_INT8 ? swz8(row) : (row & (VCH - 1)); }
+  FAQ_DEV int vswz(int row) { return MODE == ATTN_INT8 ? swz8(row) : (row & (VCH - 1)); }
 };
 
 // ------------------------------------------------------------------------
@@ -317,7 +325,7 @@ using lptr = __attribute__((address_space(3))) void*;
 // NW * 64 chunks per step (one global_load_lds_dwordx4 per wave, 1 KiB);
 // chunk p = 512 i + 64 wave + lane lands at lds + 16 p and comes from
 // base + off(i), off being the lane's 32-bit byte offset in round i.
-template <int NCH, class Off>
+template <int NCH, int NW, class Off>
 FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, Off off) {
   // the tile base is a wave-uniform value held in SGPRs; hiding it from the
   // optimizer keeps it from turning every copy into a 64-bit per-lane
@@ -339,8 +347,14 @@ FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, Off of
   }
 }
 
-template <int MODE, int D, bool CAUSAL>
-__global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
+// KVC (FP8 only): the K and V scales are constant over each 128-key tile
+// (token blocks of a multiple of 128 keys), so the K scale folds into the
+// query's exponent factor and every w_j is 1.
+template <int MODE, int D, bool CAUSAL, bool KVC>
+__global__ __launch_bounds__(Waves<MODE>::NTHR, Waves<MODE>::WG_PER_CU) void k_attn(const KParams p) {
+  constexpr int NW = Waves<MODE>::NW;
+  constexpr int BM = Waves<MODE>::BM;
+  constexpr int RB = NW * 64 * 16;  // bytes one staging round moves
   using G = Geo<MODE, D>;
   constexpr int DB = D / 16;  // 16-channel output blocks
   constexpr int NB = D / 32;  // MX blocks per row
@@ -431,8 +445,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
   }
 
   // ---- tile copy into LDS buffer `buf`.  A lane's chunk in round i is
-  // row i * (512 / CH) + r0, column c0 of the tile: the same swizzled
-  // column every round, 8 KiB further on.
+  // row i * (NW * 64 / CH) + r0, column c0 of the tile: the same swizzled
+  // column every round, RB bytes further on.
   const int pw = wave * 64 + lane;
   const int kr0 = pw / G::KCH;
   const uint32_t koff0 = (uint32_t)(((pw % G::KCH) ^ G::kswz(kr0)) << 4);
@@ -441,20 +455,20 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
     const int k0 = t * BN;
     if (MODE == ATTN_FP8) {
       // bf16 K tiles in the workspace, padded with zero rows
-      stage<G::KBYTES / 16>(buf, kbase + (int64_t)k0 * G::KROW, wave, lane,
-                            [&](int i) { return (uint32_t)(i * 8192 + kr0 * G::KROW) + koff0; });
+      stage<G::KBYTES / 16, NW>(buf, kbase + (int64_t)k0 * G::KROW, wave, lane,
+                            [&](int i) { return (uint32_t)(i * RB + kr0 * G::KROW) + koff0; });
     } else {
       // K codes: rows past the end are re-read from the last row (masked)
-      stage<G::KBYTES / 16>(buf, kbase, wave, lane, [&](int i) {
-        const int kr = min(k0 + i * (512 / G::KCH) + kr0, Skv - 1);
+      stage<G::KBYTES / 16, NW>(buf, kbase, wave, lane, [&](int i) {
+        const int kr = min(k0 + i * (NW * 64 / G::KCH) + kr0, Skv - 1);
         return (uint32_t)(kr * G::KROW) + koff0;
       });
     }
-    stage<G::VBYTES / 16>(buf + G::VOFF, vtbase + (int64_t)t * G::VBYTES, wave, lane,
-                          [&](int i) { return (uint32_t)(i * 8192) + voff0; });
+    stage<G::VBYTES / 16, NW>(buf + G::VOFF, vtbase + (int64_t)t * G::VBYTES, wave, lane,
+                          [&](int i) { return (uint32_t)(i * RB) + voff0; });
     if (MODE != ATTN_INT8)
-      stage<G::XBYTES / 16>(buf + G::XOFF, auxbase + (int64_t)t * G::XBYTES, wave, lane,
-                            [&](int i) { return (uint32_t)(i * 8192 + pw * 16); });
+      stage<G::XBYTES / 16, NW>(buf + G::XOFF, auxbase + (int64_t)t * G::XBYTES, wave, lane,
+                            [&](int i) { return (uint32_t)(i * RB + pw * 16); });
   };
 
   // Row state.  O holds the output of each row relative to a reference
@@ -531,13 +545,14 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
 #pragma unroll
           for (int kk = 1; kk < KK; ++kk)
             s[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][kk], qw8[qb][kk], s[bb], 0, 0, 0);
-          if (bb > 0) kscale(bb - 1);
+          if (!KVC && bb > 0) kscale(bb - 1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        kscale(7);
+        if (!KVC) kscale(7);
       } else if (MODE == ATTN_INT8) {
         constexpr int K8 = D / 64;
-        i32x4 kop[2][K8];
+        constexpr int PD = 3;  // K operand blocks in flight
+        i32x4 kop[PD + 1][K8];
         i32x4 si[2];
         auto kload = [&](int bb, i32x4 (&dst)[K8]) {
 #pragma unroll
@@ -552,14 +567,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
           if (!masked) mi = max(mi, max(max(v[0], v[1]), max(v[2], v[3])));
           s[bb] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
         };
-        kload(0, kop[0]);
+#pragma unroll
+        for (int bb = 0; bb < PD; ++bb) kload(bb, kop[bb]);
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {
-          if (bb + 1 < 8) kload(bb + 1, kop[(bb + 1) & 1]);
-          si[bb & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[bb & 1][0], qi8[qb][0], i32x4{0, 0, 0, 0}, 0, 0, 0);
+          if (bb + PD < 8) kload(bb + PD, kop[(bb + PD) % (PD + 1)]);
+          const int ko = bb % (PD + 1);
+          si[bb & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[ko][0], qi8[qb][0], i32x4{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
           for (int kk = 1; kk < K8; ++kk)
-            si[bb & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[bb & 1][kk], qi8[qb][kk], si[bb & 1], 0, 0, 0);
+            si[bb & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[ko][kk], qi8[qb][kk], si[bb & 1], 0, 0, 0);
           if (bb > 0) post(bb - 1);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -616,10 +633,23 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
       }
       const float mlane = m;  // max over this lane's keys (MXFP4: its 32-key group)
       m = rows4_max(m);
-      const float mnew = fmaxf(M[qb], m);
-      const float a = __builtin_amdgcn_exp2f((M[qb] - mnew) * cq[qb]);
-      const float bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - mnew) * cq[qb]);
-      M[qb] = mnew;
+      // exponent factor of this row and tile: scores times ce are log2 units
+      const float ce = (MODE == ATTN_FP8 && KVC) ? cq[qb] * Xf[0] : cq[qb];
+      const float ml = m * ce;  // tile max, log2 units (M is kept in these units)
+      float Mn, a;
+      if (MODE == ATTN_INT8) {
+        // lazy reference: keep the running reference unless this tile's max
+        // exceeds it by more than 2^8 (tile weights stay <= 2^8, far from
+        // overflow), so O is rescaled only when the max jumps
+        const bool jump = ml > M[qb] + 8.0f;
+        Mn = jump ? ml : M[qb];
+        a = jump ? __builtin_amdgcn_exp2f(M[qb] - ml) : 1.0f;
+      } else {
+        Mn = fmaxf(M[qb], ml);
+        a = __builtin_amdgcn_exp2f(M[qb] - Mn);
+      }
+      const float bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml - Mn);
+      M[qb] = Mn;
       // bf16-MFMA modes: new reference factor f = bt (times sigma_t / 448
       // for FP8); a row whose tile is negligible (bt < 2^-64) keeps its
       // reference and contributes nothing, which keeps O bounded.
@@ -638,8 +668,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
 
       // ---- probabilities, tile sum and the quantized P operand.  A row
       // that is not live takes +inf as its reference, so all its p are 0.
+      // INT8 and KVC fold the static P scale into the exponent (127 p and
+      // 448 p come out of the exp); their sums are scaled back once.
       const float ms = (m == -INFINITY) ? 0.0f : (live ? m : INFINITY);
-      const float mc = ms * cq[qb];
+      constexpr float kLog2_127 = 6.9886846867721655f, kLog2_448 = 8.807354922057604f;
+      const float mc = ms * ce - kLog2_127;
       float ls[2] = {0.f, 0.f};
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
@@ -647,30 +680,38 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
         for (int r = 0; r < 4; ++r) {
           float pv;
           if (MODE == ATTN_INT8) {
-            // p = 2^(s cq - m cq); p at the maximum may differ from 1 by an
-            // ulp, which cannot move rne(127 p)
-            pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], cq[qb], -mc));
+            // 127 p = 2^(s ce - (m ce - log2 127)); at the maximum this may
+            // differ from 127 by an ulp, which cannot move rne(127 p)
+            pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], ce, -mc));
+          } else if (MODE == ATTN_FP8 && KVC) {
+            // 448 p (w = 1): at the maximum within an ulp of 448, whose code
+            // both roundings give
+            pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r] - ms, ce, kLog2_448));
           } else {
             // (x - m) is exactly 0 at the tile maximum, so p = 1 there exactly
-            pv = __builtin_amdgcn_exp2f((s[bb][r] - ms) * cq[qb]);
+            pv = __builtin_amdgcn_exp2f((s[bb][r] - ms) * ce);
           }
           s[bb][r] = pv;
           ls[r & 1] += pv;
         }
         if (MODE == ATTN_INT8) {
-          // rne(127 p) lands in the low byte of fma(p, 127, 1.5 * 2^23)
-          const uint32_t f0 = __float_as_uint(__builtin_fmaf(s[bb][0], 127.0f, 12582912.0f));
-          const uint32_t f1 = __float_as_uint(__builtin_fmaf(s[bb][1], 127.0f, 12582912.0f));
-          const uint32_t f2 = __float_as_uint(__builtin_fmaf(s[bb][2], 127.0f, 12582912.0f));
-          const uint32_t f3 = __float_as_uint(__builtin_fmaf(s[bb][3], 127.0f, 12582912.0f));
-          const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x0c0c0400u);
-          const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x0c0c0400u);
-          pi8[qb][bb >> 2][bb & 3] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          // rne(127 p), saturated to [0, 255], packed byte by byte
+          uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(s[bb][0], 0u, 0u);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(s[bb][1], 1u, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(s[bb][2], 2u, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(s[bb][3], 3u, w);
+          pi8[qb][bb >> 2][bb & 3] = (int)w;
         } else if (MODE == ATTN_FP8) {
           // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
-          const float4 vm = *reinterpret_cast<const float4*>(&Xf[BN + 16 * bb + 4 * g]);
-          int e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][0] * vm.x, s[bb][1] * vm.y, 0, false);
-          e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][2] * vm.z, s[bb][3] * vm.w, e8, true);
+          int e8;
+          if (KVC) {
+            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][0], s[bb][1], 0, false);
+            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][2], s[bb][3], e8, true);
+          } else {
+            const float4 vm = *reinterpret_cast<const float4*>(&Xf[BN + 16 * bb + 4 * g]);
+            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][0] * vm.x, s[bb][1] * vm.y, 0, false);
+            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][2] * vm.z, s[bb][3] * vm.w, e8, true);
+          }
           pbf[qb][bb >> 1][2 * (bb & 1)] = (int)e4m3x2_to_bf16x2<false>((uint32_t)e8);
           pbf[qb][bb >> 1][2 * (bb & 1) + 1] = (int)e4m3x2_to_bf16x2<true>((uint32_t)e8);
         }
@@ -679,7 +720,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
         // this lane's 32 keys are one MX group: local max -> shared
         // exponent; p -> E2M1(p / 2^E) * 2^E, exact in bf16.  The group's
         // largest p is the same function of the lane's largest score.
-        const float pmax = __builtin_amdgcn_exp2f((mlane - ms) * cq[qb]);
+        const float pmax = __builtin_amdgcn_exp2f((mlane - ms) * ce);
         const int E = mx_exponent(pmax);
         const float sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
 #pragma unroll
@@ -692,7 +733,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
           }
         }
       }
-      L[qb] = L[qb] * a + rows4_sum(ls[0] + ls[1]) * bt;
+      const float lscale = MODE == ATTN_INT8 ? 1.0f / 127.0f : ((MODE == ATTN_FP8 && KVC) ? 1.0f / 448.0f : 1.0f);
+      L[qb] = L[qb] * a + rows4_sum(ls[0] + ls[1]) * (bt * lscale);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -700,7 +742,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
     // read while block db multiplies
     if (MODE == ATTN_INT8) {
       const bool do_rescale = __any(rescale_any);
-      i32x4 vop[2][2], ci[2][2];
+      constexpr int PD = 3;  // V operand blocks in flight
+      i32x4 vop[PD + 1][2], ci[2][2];
       auto vload = [&](int db, i32x4 (&dst)[2]) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -724,14 +767,16 @@ __global__ __launch_bounds__(NTHR, 1) void k_attn(const KParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) O[qb][db][r] *= rscale[qb];
       }
-      vload(0, vop[0]);
+#pragma unroll
+      for (int db = 0; db < PD && db < DB; ++db) vload(db, vop[db]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        if (db + 1 < DB) vload(db + 1, vop[(db + 1) & 1]);
+        if (db + PD < DB) vload(db + PD, vop[(db + PD) % (PD + 1)]);
+        const int vo = db % (PD + 1);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          ci[qb][db & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vop[db & 1][0], pi8[qb][0], i32x4{0, 0, 0, 0}, 0, 0, 0);
-          ci[qb][db & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vop[db & 1][1], pi8[qb][1], ci[qb][db & 1], 0, 0, 0);
+          ci[qb][db & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vop[vo][0], pi8[qb][0], i32x4{0, 0, 0, 0}, 0, 0, 0);
+          ci[qb][db & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vop[vo][1], pi8[qb][1], ci[qb][db & 1], 0, 0, 0);
         }
         if (db > 0) accum(db - 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -812,7 +857,7 @@ hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   if (e != hipSuccess) return e;
   KParams p{};
   p.H = a.H; p.BH = a.B * a.H; p.Sq = a.Sq; p.Skv = a.Skv; p.nt = nt;
-  p.nqt = (int)((a.Sq + BM - 1) / BM);
+  p.nqt = (int)((a.Sq + Waves<MODE>::BM - 1) / Waves<MODE>::BM);
   p.q = (const uint8_t*)a.q_codes; p.qs = a.q_scales;
   p.k = MODE == ATTN_FP8 ? ws + l.kb_off : (const uint8_t*)a.k_codes;
   p.ks = a.k_scales;
@@ -824,8 +869,17 @@ hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   p.c_log2 = a.sm_scale * kLog2e;
   p.out = a.out; p.out_bf16 = a.out_bf16;
   dim3 grid((unsigned)(p.nqt * p.BH));
-  if (a.causal) k_attn<MODE, D, true><<<grid, NTHR, 0, st>>>(p);
-  else k_attn<MODE, D, false><<<grid, NTHR, 0, st>>>(p);
+  if constexpr (MODE == ATTN_FP8) {
+    if (a.kv_block % BN == 0) {
+      if (a.causal) k_attn<MODE, D, true, true><<<grid, Waves<MODE>::NTHR, 0, st>>>(p);
+      else k_attn<MODE, D, false, true><<<grid, Waves<MODE>::NTHR, 0, st>>>(p);
+      return hipGetLastError();
+    }
+  }
+  {
+    if (a.causal) k_attn<MODE, D, true, false><<<grid, Waves<MODE>::NTHR, 0, st>>>(p);
+    else k_attn<MODE, D, false, false><<<grid, Waves<MODE>::NTHR, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 
