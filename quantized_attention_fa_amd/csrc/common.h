@@ -9,6 +9,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define FAQ_DEV static __device__ __forceinline__
 
@@ -135,6 +136,85 @@ FAQ_DEV float rows4_sum(float x) {
   const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// ---------------------------------------------------------------- division
+//
+// The quantizers divide every element by its scale, correctly rounded.  A
+// full IEEE division costs about ten instructions; with r = RN(1/s) taken
+// once per scale, the quotient is q0 = x r (within an ulp), the residual
+// x - q0 s is exact under fma, and one correction q0 + (x - q0 s) r rounds
+// to the IEEE quotient (Markstein's theorem for round-to-nearest).  The
+// theorem needs x, s, the quotient and the residual to be normal numbers:
+// callers take this path only for s in [2^-80, 2^80] and rely on it only
+// for quotients that can decide a code (|q| >= 2^-12, where all four are
+// normal); smaller quotients stay smaller than any code boundary.
+
+FAQ_DEV bool div_fast_ok(float s) { return s >= 0x1p-80f && s <= 0x1p80f; }
+
+FAQ_DEV float div_rn(float x, float s, float r) {
+  const float q0 = x * r;
+  return __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+}
+
+// The sign of x on q (x / s has the sign of x for s > 0; the correction
+// step alone turns x = -0 into +0).
+FAQ_DEV float with_sign_of(float q, float x) {
+  return __uint_as_float((__float_as_uint(q) & 0x7fffffffu) | (__float_as_uint(x) & 0x80000000u));
+}
+
+// INT8 code of x / s, clamp(rne(fl32(x / s)), -128, 127), in the low byte
+// of the returned word: adding 1.5 * 2^23 to the clamped quotient rounds it
+// to an integer (ties to even) held in the low mantissa bits.  On the fast
+// path x r is first clamped to +-256, which keeps the correction finite for
+// inputs far beyond the scale (their codes saturate either way).
+template <bool FAST>
+FAQ_DEV uint32_t int8_code_word(float x, float s, float r) {
+  float q;
+  if (FAST) {
+    const float q0 = __builtin_amdgcn_fmed3f(x * r, -256.0f, 256.0f);
+    q = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+  } else {
+    q = x / s;
+  }
+  return __float_as_uint(__builtin_amdgcn_fmed3f(q, -128.0f, 127.0f) + 0x1.8p23f);
+}
+
+// Low bytes of a, b, c, d as one word (a in byte 0).
+FAQ_DEV uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// E4M3 codes of x0 / s .. x3 / s (nearest, ties to even) packed in a word,
+// x0 in byte 0.  The hardware conversion rounds to nearest even and keeps
+// the sign; every quotient here is at most 448 in magnitude.
+template <bool FAST>
+FAQ_DEV uint32_t e4m3_code_word(const float* x, float s, float r) {
+  float q[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) q[k] = FAST ? with_sign_of(div_rn(x[k], s, r), x[k]) : x[k] / s;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+  return (uint32_t)w;
+}
+
+// N / 4 code words of x[0..N) / s: the fast division, redone with IEEE
+// divisions by the rare lanes whose scale is outside the fast path's range
+// (a wave-uniform test first, so the common case skips that code).
+template <int N>
+FAQ_DEV void e4m3_code_words(const float* x, float s, uint32_t* w) {
+  const float r = 1.0f / s;
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j) w[j] = e4m3_code_word<true>(x + 4 * j, s, r);
+  const bool slow = !div_fast_ok(s);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(slow) != 0, 0)) {
+    if (slow) {
+#pragma unroll
+      for (int j = 0; j < N / 4; ++j) w[j] = e4m3_code_word<false>(x + 4 * j, s, r);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- misc

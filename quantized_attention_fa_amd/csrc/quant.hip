@@ -5,8 +5,10 @@
 // across lanes with shuffles.  The arithmetic is bit-exact with respect to
 // the formats' definitions:
 //   scale = fl32(amax / qmax) (IEEE division; amax == 0 -> 1),
-//   u     = fl32(x / scale)   (IEEE division),
-//   code  = nearest code to u, ties to even, saturating.
+//   u     = fl32(x / scale)   (correctly rounded: one fma correction of
+//                              x * RN(1 / scale), see div_rn),
+//   code  = nearest code to u, ties to even, saturating (hardware E4M3 and
+//           E2M1 conversions, an exact integer rounding for INT8).
 // Formats and granularities follow the msModelSlim "FA 量化" page
 // (分支组合, 组合 1-3) and the MindIE SD "量化" page (FA量化 / 技术特点).
 
@@ -67,16 +69,10 @@ __global__ void k_scales_from_amax(const float* amax, int64_t H, float qmax, flo
 // INT8 per-head static: code = clamp(rne(x / scale[h]), -128, 127).
 // grid = (chunks per (b,h) slice, B*H); 16 elements per thread-vector.
 // ------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_quant_int8_head(const T* __restrict__ x,
-                                                              const float* __restrict__ scale,
-                                                              int64_t per_bh, int H,
-                                                              int8_t* __restrict__ codes) {
+template <bool FAST, typename T>
+FAQ_DEV void int8_head_slice(const T* __restrict__ src, int8_t* __restrict__ dst, int64_t per_bh, float s) {
   constexpr int U = 2;
-  const int64_t bh = blockIdx.y;
-  const float s = scale[bh % H];
-  const T* src = x + bh * per_bh;
-  int8_t* dst = codes + bh * per_bh;
+  const float r = 1.0f / s;
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads * 16 * U; c0 < per_bh;
        c0 += (int64_t)gridDim.x * kThreads * 16 * U) {
     float v[U][16];
@@ -98,11 +94,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8_head(const T* __restric
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          uint32_t acc = 0;
+          uint32_t c[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            acc |= ((uint32_t)enc_int8(v[u][4 * j + k] / s) & 0xffu) << (8 * k);
-          w[j] = acc;
+          for (int k = 0; k < 4; ++k) c[k] = int8_code_word<FAST>(v[u][4 * j + k], s, r);
+          w[j] = pack_low_bytes(c[0], c[1], c[2], c[3]);
         }
         *reinterpret_cast<uint4*>(dst + i) = make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -110,26 +105,42 @@ __global__ __launch_bounds__(kThreads) void k_quant_int8_head(const T* __restric
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_quant_int8_head(const T* __restrict__ x,
+                                                              const float* __restrict__ scale,
+                                                              int64_t per_bh, int H,
+                                                              int8_t* __restrict__ codes) {
+  const int64_t bh = blockIdx.y;
+  const float s = scale[bh % H];
+  // the head's scale picks the division path once for the whole slice
+  if (div_fast_ok(s)) int8_head_slice<true>(x + bh * per_bh, codes + bh * per_bh, per_bh, s);
+  else int8_head_slice<false>(x + bh * per_bh, codes + bh * per_bh, per_bh, s);
+}
+
 // ------------------------------------------------------------------------
 // FP8 E4M3 per-token: one scale per (b,h,s) row of D elements.
-// D/8 threads per row, 8 elements per thread.
+// D/16 threads per row, 16 elements per thread.
 // ------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_quant_fp8_token(const T* __restrict__ x, int64_t rows,
                                                               uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales) {
-  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 4;
+  constexpr int EPT = 16, TPR = D / EPT, RPB = kThreads / TPR, U = 2;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
   for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
-    float v[U][8];
+    float v[U][EPT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       if (row < rows) {
-        load8(x + row * D + sub * 8, v[u]);
+        float a[8], b[8];
+        load8(x + row * D + sub * EPT, a);
+        load8(x + row * D + sub * EPT + 8, b);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { v[u][k] = a[k]; v[u][8 + k] = b[k]; }
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
+        for (int k = 0; k < EPT; ++k) v[u][k] = 0.0f;
       }
     }
 #pragma unroll
@@ -137,16 +148,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_token(const T* __restric
       const int64_t row = r0 + u * RPB + rin;
       float m = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
+      for (int k = 0; k < EPT; ++k) m = fmaxf(m, fabsf(v[u][k]));
       m = group_max<TPR>(m);
       const float s = scale_from_amax(m, 448.0f);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) lo |= enc_e4m3(v[u][k] / s) << (8 * k);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) hi |= enc_e4m3(v[u][4 + k] / s) << (8 * k);
+      uint32_t w[4];
+      e4m3_code_words<EPT>(v[u], s, w);
       if (row < rows) {
-        *reinterpret_cast<uint2*>(codes + row * D + sub * 8) = make_uint2(lo, hi);
+        *reinterpret_cast<uint4*>(codes + row * D + sub * EPT) = make_uint4(w[0], w[1], w[2], w[3]);
         if (sub == 0) scales[row] = s;
       }
     }
@@ -184,10 +192,24 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
       for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
       m = group_max<4>(m);
       const int E = mx_exponent(m);
+      // hardware E2M1 of x / 2^E (exact division by a power of two;
+      // nearest, ties to even, saturating at 6, sign kept)
+      const float sc = __uint_as_float((uint32_t)(E > -127 ? E + 127 : 127) << 23);
       uint32_t packed = 0;
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[u][0], v[u][1], sc, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[u][2], v[u][3], sc, 1);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[u][4], v[u][5], sc, 2);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[u][6], v[u][7], sc, 3);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(E == -127) != 0, 0)) {
+        // 2^-127 is not a normal float: blocks with zero or subnormal amax
+        // scale with ldexp and encode in software
+        if (E == -127) {
+          packed = 0;
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        packed |= enc_e2m1(__builtin_amdgcn_ldexpf(v[u][k], -E)) << (4 * k);
+          for (int k = 0; k < 8; ++k)
+            packed |= enc_e2m1(__builtin_amdgcn_ldexpf(v[u][k], 127)) << (4 * k);
+        }
+      }
       // gather the row's NB exponent bytes into the row's first lane
       uint32_t eb = (uint32_t)(E + 127);
       uint32_t word = eb;
@@ -246,15 +268,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __
     const int e = (i * kThreads + threadIdx.x) * 8;
     if (e / D < ntok) {
       const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-      uint32_t lo = 0, hi = 0;
+      float f[8];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        lo |= enc_e4m3(bf16_lo(w[j]) / s) << (16 * j);
-        lo |= enc_e4m3(bf16_hi(w[j]) / s) << (16 * j + 8);
-        hi |= enc_e4m3(bf16_lo(w[2 + j]) / s) << (16 * j);
-        hi |= enc_e4m3(bf16_hi(w[2 + j]) / s) << (16 * j + 8);
-      }
-      *reinterpret_cast<uint2*>(dst + e) = make_uint2(lo, hi);
+      for (int j = 0; j < 4; ++j) { f[2 * j] = bf16_lo(w[j]); f[2 * j + 1] = bf16_hi(w[j]); }
+      uint32_t c[2];
+      e4m3_code_words<8>(f, s, c);
+      *reinterpret_cast<uint2*>(dst + e) = make_uint2(c[0], c[1]);
     }
   }
   if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
@@ -316,17 +335,20 @@ __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __rest
         acc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[1][kk], acc[1][db], 0, 0, 0);
       }
     }
-    // round to bf16 (the rotated tensor is bf16), block max
+    // round to bf16 (the rotated tensor is bf16; the hardware conversion
+    // rounds to nearest even), block max
     float m = 0.0f;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float y = __uint_as_float(f32_to_bf16_bits(acc[tb][db][r]) << 16);
-          acc[tb][db][r] = y;
-          m = fmaxf(m, fabsf(y));
+        for (int r = 0; r < 4; r += 2) {
+          const bf16x2 y = {(__bf16)acc[tb][db][r], (__bf16)acc[tb][db][r + 1]};
+          const uint32_t yw = __builtin_bit_cast(uint32_t, y);
+          acc[tb][db][r] = bf16_lo(yw);
+          acc[tb][db][r + 1] = bf16_hi(yw);
+          m = fmaxf(m, fmaxf(fabsf(acc[tb][db][r]), fabsf(acc[tb][db][r + 1])));
         }
     m = wave_max(m);
     if (lane == 0) red[w] = m;
@@ -340,16 +362,22 @@ __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __rest
     for (int tb = 0; tb < 2; ++tb) {
       const int64_t tok = tok0 + tb * 16 + l16;
       if (tok >= S) continue;
+      float y[4 * DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[4 * db + r] = acc[tb][db][r];
+      uint32_t c[DB];
+      e4m3_code_words<4 * DB>(y, s, c);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) c |= enc_e4m3(acc[tb][db][r] / s) << (8 * r);
         const int64_t off = (bh * S + tok) * D + db * 16 + g * 4;
-        *reinterpret_cast<uint32_t*>(codes + off) = c;
+        *reinterpret_cast<uint32_t*>(codes + off) = c[db];
         if (dbg) {
-          const uint32_t b0 = f32_to_bf16_bits(acc[tb][db][0]) | (f32_to_bf16_bits(acc[tb][db][1]) << 16);
-          const uint32_t b1 = f32_to_bf16_bits(acc[tb][db][2]) | (f32_to_bf16_bits(acc[tb][db][3]) << 16);
+          // y holds bf16 values: their top halves are the bf16 bits
+          const float* yd = y + 4 * db;
+          const uint32_t b0 = (__float_as_uint(yd[0]) >> 16) | (__float_as_uint(yd[1]) & 0xffff0000u);
+          const uint32_t b1 = (__float_as_uint(yd[2]) >> 16) | (__float_as_uint(yd[3]) & 0xffff0000u);
           *reinterpret_cast<uint2*>(dbg + off) = make_uint2(b0, b1);
         }
       }
@@ -401,8 +429,8 @@ hipError_t launch_quant_int8_head(const void* x, int x_dtype, const faq_shape& s
 template <int D>
 static hipError_t fp8_token_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
                               float* scales, hipStream_t st) {
-  constexpr int RPB = kThreads / (D / 8);
-  const unsigned grid = grid_chunks(rows, RPB * 4, 1u << 20);
+  constexpr int RPB = kThreads / (D / 16);
+  const unsigned grid = grid_chunks(rows, RPB * 2, 1u << 20);
   if (x_dtype == FAQ_T_BF16)
     k_quant_fp8_token<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, scales);
   else

@@ -54,6 +54,54 @@ def test_int8_divide_ties():
     assert qt.codes.cpu().numpy()[0, 0, 0, 0] == 63
 
 
+def test_int8_scales_and_inputs_at_the_extremes():
+    """Heads whose scale lies outside the fast division's range (2^-90,
+    2^90), inputs far beyond the scale (codes saturate), subnormal inputs and
+    signed zeros: every code still equals clamp(rne(fl32(x / s)))."""
+    g = np.random.default_rng(11)
+    x = (g.standard_normal((1, 6, 40, 64)) * 3).astype(np.float32)
+    x[0, :, 0, :8] = [1e30, -1e30, 3e38, -3e38, 1e-40, -1e-40, 0.0, -0.0]
+    x[0, 1] *= 2.0 ** -95  # tiny head, tiny scale
+    x[0, 2] *= 2.0 ** 95  # huge head, huge scale
+    x[0, 3] *= 2.0 ** -120  # mostly subnormal values
+    for dtype in (torch.float32, torch.bfloat16):
+        xt = torch.from_numpy(x).to(dtype)
+        xn = _np(xt)
+        sc = np.array([0.02, 2.0 ** -96, 2.0 ** 93, 2.0 ** -126, 1e-3, 7.0], np.float32)
+        sct = torch.from_numpy(sc).to(DEV)
+        qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("int8", "per_head"), static_scale=sct)
+        assert np.array_equal(qt.codes.cpu().numpy(), OQ.quantize_int8_per_head(xn, sc))
+
+
+def test_fp8_rows_at_the_extremes():
+    """Per-token and token-block FP8 on rows whose amax puts the scale
+    outside the fast division's range, rows of subnormals, huge rows and
+    signed zeros."""
+    g = np.random.default_rng(12)
+    x = g.standard_normal((1, 2, 256, 128)).astype(np.float32)
+    x[0, 0, 0] *= 1e-30
+    x[0, 0, 1] *= 1e30
+    x[0, 0, 2] *= 1e-39
+    x[0, 0, 3, :4] = [0.0, -0.0, -1e-20, 1.0]
+    x[0, 0, 4] = -0.0
+    x[0, 1, :128] *= 2.0 ** -100  # a whole token block of tiny values
+    x[0, 1, 128:] *= 2.0 ** 100
+    for dtype in (torch.float32, torch.bfloat16):
+        xt = torch.from_numpy(x).to(dtype)
+        xn = _np(xt)
+        qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("fp8_e4m3", "per_token"))
+        codes, s = OQ.quantize_fp8_per_token(xn)
+        assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
+        assert np.array_equal(qt.codes.cpu().numpy(), codes)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    xn = _np(xt)
+    for bt in (128, 256):
+        qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("fp8_e4m3", "per_token_block", block_tokens=bt))
+        codes, s = OQ.quantize_fp8_block(xn, bt)
+        assert np.array_equal(qt.codes.cpu().numpy(), codes)
+        assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
+
+
 @pytest.mark.parametrize("shape,dtype", [((1, 2, 128, 64), torch.float32), ((2, 3, 300, 128), torch.bfloat16),
                                          ((1, 1, 1000, 128), torch.bfloat16), ((1, 2, 37, 64), torch.bfloat16)])
 def test_fp8_per_token_small(shape, dtype):
