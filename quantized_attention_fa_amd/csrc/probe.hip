@@ -201,3 +201,63 @@ extern "C" int faq_probe_cvt_u8(const float* x, int n, uint8_t* out) {
   k_probe_cvt_u8<<<(n + 255) / 256, 256>>>(x, n, out);
   return (int)hipDeviceSynchronize();
 }
+
+namespace {
+// 32x32 MFMA shapes.  Assumed layout: lane (i = l%32, h = l/32) holds row i
+// of A and of Bt at K elements [K/2 h, K/2 h + K/2) of the instruction's K;
+// C[8(r/4) + 4h + r%4][i] lands in accumulator r (r = 0..15).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_32x32x16_bf16: A, Bt [32][16] bf16.
+__global__ void k_probe_mfma32_bf16(const uint16_t* A, const uint16_t* Bt, float* C) {
+  const int l = threadIdx.x, i = l & 31, h = l >> 5;
+  const uint4 a = *reinterpret_cast<const uint4*>(A + i * 16 + 8 * h);
+  const uint4 b = *reinterpret_cast<const uint4*>(Bt + i * 16 + 8 * h);
+  f32x16 c = {};
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  for (int r = 0; r < 16; ++r) C[(8 * (r / 4) + 4 * h + r % 4) * 32 + i] = c[r];
+}
+
+// v_mfma_i32_32x32x32_i8: A, Bt [32][32] int8.
+__global__ void k_probe_mfma32_i8(const int8_t* A, const int8_t* Bt, int32_t* C) {
+  const int l = threadIdx.x, i = l & 31, h = l >> 5;
+  const uint4 a = *reinterpret_cast<const uint4*>(A + i * 32 + 16 * h);
+  const uint4 b = *reinterpret_cast<const uint4*>(Bt + i * 32 + 16 * h);
+  i32x16 c = {};
+  c = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)a.x, (int)a.y, (int)a.z, (int)a.w},
+                                            i32x4{(int)b.x, (int)b.y, (int)b.z, (int)b.w}, c, 0, 0, 0);
+  for (int r = 0; r < 16; ++r) C[(8 * (r / 4) + 4 * h + r % 4) * 32 + i] = c[r];
+}
+
+// v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands: A, Bt [32][32] bytes
+// (64 elements per row, element 2k in the low nibble of byte k); E8M0 scales
+// sa, sb [32][2] for row i and 32-element block h.
+__global__ void k_probe_mfma32_fp4(const uint8_t* A, const uint8_t* Bt, const uint8_t* sa, const uint8_t* sb,
+                                   float* C) {
+  const int l = threadIdx.x, i = l & 31, h = l >> 5;
+  const uint4 a = *reinterpret_cast<const uint4*>(A + i * 32 + 16 * h);
+  const uint4 b = *reinterpret_cast<const uint4*>(Bt + i * 32 + 16 * h);
+  const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  f32x16 c = {};
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa[i * 2 + h], 0, (int)sb[i * 2 + h]);
+  for (int r = 0; r < 16; ++r) C[(8 * (r / 4) + 4 * h + r % 4) * 32 + i] = c[r];
+}
+}  // namespace
+
+extern "C" int faq_probe_mfma32_bf16(const uint16_t* A, const uint16_t* Bt, float* C) {
+  k_probe_mfma32_bf16<<<1, 64>>>(A, Bt, C);
+  return (int)hipDeviceSynchronize();
+}
+
+extern "C" int faq_probe_mfma32_i8(const int8_t* A, const int8_t* Bt, int32_t* C) {
+  k_probe_mfma32_i8<<<1, 64>>>(A, Bt, C);
+  return (int)hipDeviceSynchronize();
+}
+
+extern "C" int faq_probe_mfma32_fp4(const uint8_t* A, const uint8_t* Bt, const uint8_t* sa, const uint8_t* sb,
+                                    float* C) {
+  k_probe_mfma32_fp4<<<1, 64>>>(A, Bt, sa, sb, C);
+  return (int)hipDeviceSynchronize();
+}

@@ -77,6 +77,45 @@ def test_mfma_bf16_layout_and_precision(lib):
     assert np.all(np.abs(C.cpu().numpy() - ref) <= bound)
 
 
+def test_mfma32_bf16_layout(lib):
+    """v_mfma_f32_32x32x16_bf16: lane (i, h) holds K elements 8h..8h+7 of
+    row i; accumulator r is row 8(r/4) + 4h + r%4 of column i."""
+    g = np.random.default_rng(21)
+    A = g.integers(-8, 9, (32, 16)).astype(np.float32)
+    B = g.integers(-8, 9, (32, 16)).astype(np.float32)
+    a = torch.from_numpy(A).to(torch.bfloat16).to(DEV)
+    b = torch.from_numpy(B).to(torch.bfloat16).to(DEV)
+    C = torch.zeros((32, 32), dtype=torch.float32, device=DEV)
+    assert lib.faq_probe_mfma32_bf16(_p(a), _p(b), _p(C)) == 0
+    assert np.array_equal(C.cpu().numpy(), A @ B.T)
+
+
+def test_mfma32_i8_layout(lib):
+    g = np.random.default_rng(22)
+    A = g.integers(-128, 128, (32, 32)).astype(np.int8)
+    B = g.integers(-128, 128, (32, 32)).astype(np.int8)
+    C = torch.zeros((32, 32), dtype=torch.int32, device=DEV)
+    a, b = _d(A), _d(B)
+    assert lib.faq_probe_mfma32_i8(_p(a), _p(b), _p(C)) == 0
+    assert np.array_equal(C.cpu().numpy(), A.astype(np.int64) @ B.astype(np.int64).T)
+
+
+def test_mfma32_fp4_scaled_layout(lib):
+    """v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands: lane (i, h) holds
+    elements 32h..32h+31 of row i (16 bytes) and that block's E8M0 scale."""
+    g = np.random.default_rng(23)
+    ca = g.integers(0, 16, (32, 64)).astype(np.uint8)
+    cb = g.integers(0, 16, (32, 64)).astype(np.uint8)
+    sa = g.integers(125, 130, (32, 2)).astype(np.uint8)
+    sb = g.integers(125, 130, (32, 2)).astype(np.uint8)
+    va = F.e2m1_decode(ca) * np.repeat(2.0 ** (sa.astype(np.float64) - 127), 32, axis=1)
+    vb = F.e2m1_decode(cb) * np.repeat(2.0 ** (sb.astype(np.float64) - 127), 32, axis=1)
+    keep = [_d(_pack4(ca)), _d(_pack4(cb)), _d(sa), _d(sb)]
+    C = torch.zeros((32, 32), dtype=torch.float32, device=DEV)
+    assert lib.faq_probe_mfma32_fp4(*[_p(t) for t in keep], _p(C)) == 0
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), va @ vb.T)
+
+
 def test_mfma_fp4_scaled_layout(lib):
     g = np.random.default_rng(2)
     ca = g.integers(0, 16, (16, 128)).astype(np.uint8)
