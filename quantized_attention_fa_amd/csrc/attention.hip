@@ -1,16 +1,16 @@
 // Flash-style attention on quantized Q/K/V for gfx950.
 //
 // Both products take the low-bit operands ("FA 量化" page, 概述) on MFMA:
-//   INT8 per-head  v_mfma_i32_16x16x64_i8 for Q K^T and P V (int8 P):
+//   INT8 per-head  v_mfma_i32_32x32x32_i8 for Q K^T and P V (int8 P):
 //                  exact int32 accumulation.
-//   FP8 E4M3       v_mfma_f32_16x16x32_bf16 on the exact bf16 images of the
+//   FP8 E4M3       v_mfma_f32_32x32x16_bf16 on the exact bf16 images of the
 //                  E4M3 codes (Q, K, V and the E4M3 probabilities).  The
-//                  f8f6f4 MFMA sums each group of 16 products aligned to the
+//                  f8f6f4 MFMA sums each group of products aligned to the
 //                  group's largest with about 12 fractional bits, so score
 //                  errors reach ~1e-4 of amax_q * amax_k and move probability
 //                  codes; the bf16 MFMA accumulates these exact products at
 //                  fp32 precision.
-//   MXFP4          Q K^T on v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1
+//   MXFP4          Q K^T on v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1
 //                  operands and their E8M0 block exponents as MFMA scales
 //                  (exact: products within a block span < 2^8); P V on the
 //                  bf16 MFMA with P = E2M1 * 2^E and V dequantized exactly.
@@ -25,17 +25,24 @@
 // the tile sum L uses unquantized p, and tiles combine with the usual
 // running-max rescale, O = sum_t e^{m_t-M} C_t / sum_t e^{m_t-M} L_t.
 //
-// Kernel shape: one workgroup = 8 waves = 256 queries of one (b,h); each
-// wave owns 32 queries as two 16-query MFMA column blocks, and all eight
-// share each K / V^T tile.  Tiles stream from global memory straight into
-// LDS (global_load_lds, 16 bytes per lane), double buffered: the copy of
-// tile t+1 runs while tile t is computed, with one barrier per tile.
-// Scores are computed transposed (S^T = K Q^T), so a lane holds one query
-// and a run of keys: the row max needs only two cross-lane steps, and the
-// lane's probabilities are already the B operand of O^T = V^T P^T.  V comes
-// from a per-call workspace already transposed per 128-key tile, with its
-// keys permuted to match the order in which a lane holds its probabilities
-// (FP8: K and V^T widened there to their exact bf16 images).
+// Kernel shape: a workgroup is 4 waves and 128 queries of one (b,h); two
+// workgroups share a CU, so the two waves on a SIMD come from independent
+// workgroups and one's softmax (VALU) overlaps the other's products (MFMA).
+// Each wave owns 32 queries: one 32x32 MFMA column block for both products.
+// Scores are computed transposed (S^T = K Q^T): a lane holds one query and,
+// with the K rows fed to the MFMA permuted (qk_row), 64 consecutive keys of
+// the tile, i.e. two whole 32-key MX groups.  The row max and sum need one
+// cross-lane step, and the lane's probabilities are already the B operand of
+// O^T = V^T P^T.  V^T comes from a per-call workspace with its key columns in
+// the order the lanes hold their probabilities (FP8: K and V^T widened there
+// to their exact bf16 images).
+//
+// LDS tiles are chunk-major: 16-byte column c of every row, then column c+1.
+// The 16 lanes that share an LDS cycle read 16 distinct rows of one column,
+// which the row permutation kslot spreads over all 64 banks, and every
+// operand address is a per-lane base plus a constant.  The K tile of t+1 is
+// copied (global_load_lds) while P V of tile t runs, and V^T of tile t while
+// the scores and probabilities of t are computed: two barriers per tile.
 //
 // Workgroups are numbered so that all query tiles of one (b,h) land on the
 // same XCD (workgroups are dealt to the 8 XCDs round robin), which keeps a
@@ -50,56 +57,35 @@
 namespace faq {
 namespace {
 
-// Waves per workgroup: INT8 runs two 4-wave workgroups per CU (their
-// tiles fit twice in LDS, and the two waves sharing a SIMD then come from
-// independent workgroups, so one's softmax overlaps the other's MFMAs);
-// FP8 and MXFP4 tiles are larger and run one 8-wave workgroup per CU.
-template <int MODE>
-struct Waves {
-  static constexpr int NW = MODE == ATTN_INT8 ? 4 : 8;
-  static constexpr int NTHR = NW * 64;  // threads per workgroup
-  static constexpr int BM = NW * 32;    // queries per workgroup
-  static constexpr int WG_PER_CU = 8 / NW;
-};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int NW = 4;          // waves per workgroup
+constexpr int NTHR = NW * 64;  // threads per workgroup
+constexpr int BM = NW * 32;    // queries per workgroup
 constexpr int BN = 128;        // keys per tile = probability tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2_127 = 6.9886846867721655f, kLog2_448 = 8.807354922057604f;
 
-// Key order inside a V^T tile.  A lane of lane-group g (g = lane / 16) holds,
-// for query column l16, the scores of MFMA block b (16 keys) at output rows
-// 4g + r.  The K rows fed to block b are chosen per mode:
-//   INT8, FP8: row 16b + i            -> lane g holds keys 16b + 4g + r
-//   MXFP4:     row 32(i/4) + 4b + i%4 -> lane g holds keys 32g + 4b + r (one
-//                                        32-key MX group per lane)
-// The probabilities then feed O^T = V^T P^T as the B operand without moving
-// between lanes, so V^T's columns are stored in the order the lanes hold
-// their keys:
-//   INT8 (i8 MFMA, 16 K-bytes per lane): column 32g + 4b + r <-> key 16b + 4g + r
-//   FP8 / MXFP4 (bf16 MFMA 16x16x32, 8 K-elements per lane and block kk, the
-//   lane's blocks b = 2kk and 2kk+1): column 32kk + 8g + t <-> key
-//     FP8:   16(2kk + t/4) + 4g + t%4
-//     MXFP4: 32g + 8kk + t
-FAQ_DEV int vt_key_int8(int col) { return 16 * ((col >> 2) & 7) + 4 * (col >> 5) + (col & 3); }
-FAQ_DEV int vt_key_fp8(int col) {
-  const int kk = col >> 5, g = (col >> 3) & 3, t = col & 7;
-  return 16 * (2 * kk + (t >> 2)) + 4 * g + (t & 3);
-}
-FAQ_DEV int vt_key_mx(int col) {
-  const int kk = col >> 5, g = (col >> 3) & 3, t = col & 7;
-  return 32 * g + 8 * kk + t;
-}
+// Key order.  Output row R of the 32x32 block kb of S^T reads K row
+// 16 kb + qk_row(R); the accumulator puts row 8 (r/4) + 4 h + r%4 in
+// register r of lane half h, so register r of block kb in lane half h is
+// key 64 h + 16 kb + r.
+FAQ_DEV int qk_row(int R) { return 64 * ((R >> 2) & 1) + 4 * (R >> 3) + (R & 3); }
 
-// Row of the K tile read by lane-row i of MFMA block b in the MXFP4 kernel.
-FAQ_DEV int k_row_mx(int b, int i) { return 32 * (i >> 2) + 4 * b + (i & 3); }
+// LDS slot of K row `row` within a 16-byte column: rows 64.. swap their
+// 8-row halves, so the 16 rows one LDS cycle reads ({16kb + 0..7} and
+// {64 + 16kb + 0..7}, or the next eight of each) fill 16 distinct bank
+// groups.  An involution that commutes with adding 16 kb.
+FAQ_DEV int kslot(int row) { return row ^ ((row >> 3) & 8); }
 
-// XOR swizzles of the 16-byte chunks of a tile row.  An MFMA operand read
-// has 16 consecutive lanes fetch the same chunk column of 16 consecutive
-// rows; the LDS serves 64 banks (256 bytes) per cycle, so those 16 reads
-// must land in 16 distinct 16-byte bank groups.  Each swizzle depends only
-// on row bits that are the same for rows i and 16b + i, so an operand
-// address is a per-lane base plus a constant offset per block.
-FAQ_DEV int swz8(int row) { return (row >> 1) & 7; }   // 128-byte rows
-FAQ_DEV int swz4(int row) { return (row >> 2) & 3; }   // 64-byte rows
-FAQ_DEV int swz_mx(int row) { return (row >> 5) & 3; } // MXFP4 K rows (64 bytes, rows 32(i/4) + 4b + i%4)
+// Key at column p of a V^T tile.  bf16 P V (32x32x16): k-step 2 kb + s of
+// the tile takes, in lane half h, registers 8 s .. 8 s + 7 of block kb:
+// column p = 32 kb + 16 s + 8 h + t <-> key 64 h + 16 kb + 8 s + t.
+// int8 P V (32x32x32): k-step kb takes registers 0..15 of block kb:
+// column p = 32 kb + 16 h + r <-> key 64 h + 16 kb + r.
+FAQ_DEV int vt_key_bf16(int p) { return 64 * ((p >> 3) & 1) + 16 * (p >> 5) + 8 * ((p >> 4) & 1) + (p & 7); }
+FAQ_DEV int vt_key_i8(int p) { return 64 * ((p >> 4) & 1) + 16 * (p >> 5) + (p & 15); }
 
 // Two E4M3 bytes (the low half-word of `w`, or the high one when HI) -> two
 // bf16, exactly.
@@ -108,34 +94,40 @@ FAQ_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
 }
 
-// Geometry of one LDS tile buffer: K rows, V^T rows, then per-key extras
-// (FP8: K scale and 448 w_j as floats; MXFP4: the K block exponents).
+// Max / sum over the two lanes holding one query (l and l ^ 32).
+FAQ_DEV float halves_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+FAQ_DEV float halves_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// Geometry of the LDS tiles.
 template <int MODE, int D>
-struct Geo {
-  static constexpr int KROW = MODE == ATTN_INT8 ? D : (MODE == ATTN_FP8 ? 2 * D : D / 2);
-  static constexpr int KCH = KROW / 16;  // 16-byte chunks per K row
+struct Cfg {
+  static constexpr int KROW = MODE == ATTN_INT8 ? D : (MODE == ATTN_FP8 ? 2 * D : D / 2);  // bytes of a K row
   static constexpr int KBYTES = BN * KROW;
-  static constexpr int VROW = MODE == ATTN_INT8 ? BN : 2 * BN;
-  static constexpr int VCH = VROW / 16;
+  static constexpr int NB = D / 32;  // MX blocks per row
+  // per-key extras: after the K tile the FP8 K scales (floats) or the MXFP4
+  // K block exponents; after the V^T tile the FP8 multipliers 448 w_j
+  // (floats), which the probabilities read after the K buffer is refilled
+  static constexpr int XKBYTES = MODE == ATTN_FP8 ? BN * 4 : (MODE == ATTN_MX ? BN * NB : 0);
+  static constexpr int XVBYTES = MODE == ATTN_FP8 ? BN * 4 : 0;
+  static constexpr int XBYTES = XKBYTES + XVBYTES;  // per tile in the workspace
+  static constexpr int VROW = MODE == ATTN_INT8 ? BN : 2 * BN;  // bytes of a V^T row
   static constexpr int VBYTES = D * VROW;
-  static constexpr int XBYTES = MODE == ATTN_FP8 ? 2 * BN * 4 : (MODE == ATTN_MX ? BN * (D / 32) : 0);
-  static constexpr int VOFF = KBYTES;
-  static constexpr int XOFF = KBYTES + VBYTES;
-  static constexpr int BUF = XOFF + XBYTES;
-  // swizzled chunk of K row `row`
-  FAQ_DEV int kswz(int row) {
-    if (MODE == ATTN_INT8) return KCH == 8 ? swz8(row) : swz4(row);
-    if (MODE == ATTN_FP8) return row & (KCH - 1);
-    return KCH == 4 ? swz_mx(row) : 0;
-  }
-  FAQ_DEV int vswz(int row) { return MODE == ATTN_INT8 ? swz8(row) : (row & (VCH - 1)); }
+  static constexpr int KS = MODE == ATTN_INT8 ? D / 32 : (MODE == ATTN_FP8 ? D / 16 : D / 64);  // QK k-steps
+  static constexpr int DB = D / 32;  // 32-channel output blocks
 };
 
 // ------------------------------------------------------------------------
 // Workspace layout (per (b,h), per 128-key tile t):
-//   vt  : V^T of the tile, D rows x 128 keys: INT8 codes (1 byte) or, for
-//         FP8 and MXFP4, the exact values in bf16 (2 bytes)
-//   kb  : FP8: K widened to bf16, 128 rows x D (rows past the end are 0)
+//   vt  : V^T of the tile as its LDS image (chunk-major, columns in the lane
+//         key order): INT8 codes (1 byte) or, for FP8 and MXFP4, the exact
+//         values in bf16 (2 bytes)
+//   kb  : FP8: K widened to bf16 as its LDS image (rows past the end are 0)
 //   aux : FP8: 128 K scales then 128 multipliers 448 * w_j (floats);
 //         MXFP4: the K block exponents, 128 rows x D/32 bytes (127 past
 //         the end)
@@ -161,54 +153,70 @@ inline WsLayout ws_layout(int mode, int64_t B, int64_t H, int64_t Skv, int64_t D
 
 // ------------------------------------------------------------------------
 // Per-call re-layout.  grid = (tiles, B*H), 256 threads; one 128-key tile.
-//   INT8 : V^T codes in the lane key order.
-//   FP8  : K and V^T widened to bf16 (V^T in the lane key order), the
-//          per-key K scales and 448 w_j, and sigma_t.
+//   INT8 : the V^T image (codes).
+//   FP8  : the K and V^T images widened to bf16, the per-key K scales and
+//          448 w_j, and sigma_t.
 // ------------------------------------------------------------------------
 template <int D, bool FP8>
 __global__ __launch_bounds__(256) void k_prep(const uint8_t* __restrict__ k, const float* __restrict__ ks,
                                               const uint8_t* __restrict__ v, const float* __restrict__ vs,
                                               int64_t Skv, int kv_block, int64_t nt, uint8_t* __restrict__ vt,
-                                              uint16_t* __restrict__ kb, float* __restrict__ aux,
+                                              uint8_t* __restrict__ kb, float* __restrict__ aux,
                                               float* __restrict__ sig) {
+  using C = Cfg<FP8 ? ATTN_FP8 : ATTN_INT8, D>;
   __shared__ uint8_t tile[BN][D + 4];
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t k0 = (int64_t)t * BN;
   const int64_t tile_id = bh * nt + t;
-  const uint8_t* src = v + (bh * Skv + k0) * D;
-  constexpr int CPR = D / 16;  // 16-byte chunks per key row
+  constexpr int CPR = D / 16;  // 16-byte chunks per key row of codes
   for (int c = threadIdx.x; c < BN * CPR; c += 256) {
     const int kl = c / CPR, cc = c % CPR;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (k0 + kl < Skv) val = *reinterpret_cast<const uint4*>(src + (int64_t)kl * D + cc * 16);
+    if (k0 + kl < Skv) val = *reinterpret_cast<const uint4*>(v + (bh * Skv + k0 + kl) * D + cc * 16);
     uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[kl][cc * 16]);
     dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
     if (FP8) {
-      // K row chunk widened to bf16 (32 bytes)
+      // K row chunk widened to bf16: columns 2 cc and 2 cc + 1 of the image
       uint4 kv = make_uint4(0, 0, 0, 0);
       if (k0 + kl < Skv) kv = *reinterpret_cast<const uint4*>(k + (bh * Skv + k0 + kl) * D + cc * 16);
-      uint16_t* kd = kb + (tile_id * BN + kl) * D + cc * 16;
-      *reinterpret_cast<uint4*>(kd) = make_uint4(e4m3x2_to_bf16x2<false>(kv.x), e4m3x2_to_bf16x2<true>(kv.x),
-                                                 e4m3x2_to_bf16x2<false>(kv.y), e4m3x2_to_bf16x2<true>(kv.y));
-      *reinterpret_cast<uint4*>(kd + 8) = make_uint4(e4m3x2_to_bf16x2<false>(kv.z), e4m3x2_to_bf16x2<true>(kv.z),
-                                                     e4m3x2_to_bf16x2<false>(kv.w), e4m3x2_to_bf16x2<true>(kv.w));
+      uint8_t* img = kb + tile_id * C::KBYTES + kslot(kl) * 16;
+      *reinterpret_cast<uint4*>(img + (2 * cc) * BN * 16) =
+          make_uint4(e4m3x2_to_bf16x2<false>(kv.x), e4m3x2_to_bf16x2<true>(kv.x), e4m3x2_to_bf16x2<false>(kv.y),
+                     e4m3x2_to_bf16x2<true>(kv.y));
+      *reinterpret_cast<uint4*>(img + (2 * cc + 1) * BN * 16) =
+          make_uint4(e4m3x2_to_bf16x2<false>(kv.z), e4m3x2_to_bf16x2<true>(kv.z), e4m3x2_to_bf16x2<false>(kv.w),
+                     e4m3x2_to_bf16x2<true>(kv.w));
     }
   }
   __syncthreads();
-  if (FP8) {
-    uint16_t* out = reinterpret_cast<uint16_t*>(vt) + tile_id * (int64_t)D * BN;
-    for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
-      const int d = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
-      uint32_t w[4];
+  uint8_t* img = vt + tile_id * C::VBYTES;
+  constexpr int VCOLS = C::VROW / 16;
+  // item i: column c = i / D, row d = i % D (consecutive threads write
+  // consecutive 16-byte slots of one column)
+  for (int i = threadIdx.x; i < VCOLS * D; i += 256) {
+    const int c = i / D, d = i % D;
+    uint32_t w[4];
+    if (FP8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t pair = (uint32_t)tile[vt_key_fp8(c8 + 2 * q)][d] | ((uint32_t)tile[vt_key_fp8(c8 + 2 * q + 1)][d] << 8);
+        const uint32_t pair =
+            (uint32_t)tile[vt_key_bf16(8 * c + 2 * q)][d] | ((uint32_t)tile[vt_key_bf16(8 * c + 2 * q + 1)][d] << 8);
         w[q] = e4m3x2_to_bf16x2<false>(pair);
       }
-      *reinterpret_cast<uint4*>(out + (int64_t)d * BN + c8) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc |= (uint32_t)tile[vt_key_i8(16 * c + 4 * q + r)][d] << (8 * r);
+        w[q] = acc;
+      }
     }
+    *reinterpret_cast<uint4*>(img + (c * D + d) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (FP8) {
     const int kl = threadIdx.x;
     float s = 0.0f, sk = 0.0f;
     if (kl < BN && k0 + kl < Skv) {
@@ -225,32 +233,19 @@ __global__ __launch_bounds__(256) void k_prep(const uint8_t* __restrict__ k, con
       aux[tile_id * 2 * BN + BN + kl] = (s > 0.0f) ? 448.0f * (s / m) : 0.0f;
     }
     if (threadIdx.x == 0) sig[tile_id] = m;
-  } else {
-    uint8_t* out = vt + tile_id * (int64_t)D * BN;
-    for (int c = threadIdx.x; c < D * (BN / 16); c += 256) {
-      const int d = c / (BN / 16), j = c % (BN / 16);
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc |= (uint32_t)tile[vt_key_int8(16 * j + 4 * q + r)][d] << (8 * r);
-        w[q] = acc;
-      }
-      *reinterpret_cast<uint4*>(out + (int64_t)d * BN + 16 * j) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
   }
 }
 
 // ------------------------------------------------------------------------
-// MXFP4 re-layout: V^T per tile as the exact bf16 values E2M1 * 2^E (E from
-// the token's 32-channel block), in the lane key order; K block exponents
-// per tile (127 = 2^0 past the end).
+// MXFP4 re-layout: the V^T image as the exact bf16 values E2M1 * 2^E (E
+// from the token's 32-channel block) in the lane key order; the K block
+// exponents per tile (127 = 2^0 past the end).
 // ------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_prep_mx(const uint8_t* __restrict__ v, const uint8_t* __restrict__ ve,
                                                  const uint8_t* __restrict__ ke, int64_t Skv, int64_t nt,
-                                                 uint16_t* __restrict__ vt, uint8_t* __restrict__ kex) {
+                                                 uint8_t* __restrict__ vt, uint8_t* __restrict__ kex) {
+  using C = Cfg<ATTN_MX, D>;
   constexpr int NB = D / 32;
   __shared__ uint8_t codes[BN][D / 2 + 4];
   __shared__ uint8_t ex[BN][NB];
@@ -272,17 +267,16 @@ __global__ __launch_bounds__(256) void k_prep_mx(const uint8_t* __restrict__ v, 
     kex[tile_id * BN * NB + c] = ok ? ke[(bh * Skv + k0 + kl) * NB + b] : (uint8_t)127;
   }
   __syncthreads();
-  uint16_t* out = vt + tile_id * (int64_t)D * BN;
-  // 8 output columns (16 bytes) per item
-  for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
-    const int d = c / (BN / 8), c8 = (c % (BN / 8)) * 8;
+  uint8_t* img = vt + tile_id * C::VBYTES;
+  for (int i = threadIdx.x; i < (C::VROW / 16) * D; i += 256) {
+    const int c = i / D, d = i % D;
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t pair = 0;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = vt_key_mx(c8 + 2 * q + h);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = vt_key_bf16(8 * c + 2 * q + hh);
         const uint32_t nib = (codes[key][d >> 1] >> (4 * (d & 1))) & 0xfu;
         const uint32_t mag = nib & 7u;
         // E2M1 magnitude: 0, .5, 1, 1.5, 2, 3, 4, 6; times 2^(e8m0 - 127)
@@ -290,11 +284,11 @@ __global__ __launch_bounds__(256) void k_prep_mx(const uint8_t* __restrict__ v, 
                                  : (float)(1u << ((mag >> 1) - 1)) * (1.0f + 0.5f * (float)(mag & 1u));
         float f = __builtin_amdgcn_ldexpf(fm, (int)ex[key][d >> 5] - 127);
         f = (nib & 8u) ? -f : f;
-        pair |= (__float_as_uint(f) >> 16) << (16 * h);  // exact: at most 2 significant bits
+        pair |= (__float_as_uint(f) >> 16) << (16 * hh);  // exact: at most 2 significant bits
       }
       w[q] = pair;
     }
-    *reinterpret_cast<uint4*>(out + (int64_t)d * BN + c8) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(img + (c * D + d) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -306,9 +300,9 @@ struct KParams {
   int nqt;
   const uint8_t* q;
   const void* qs;
-  const uint8_t* k;      // INT8 / MXFP4: K codes; FP8: bf16 K tiles in the workspace
+  const uint8_t* k;      // INT8 / MXFP4: K codes; FP8: bf16 K images in the workspace
   const void* ks;        // INT8: per-head K scale
-  const uint8_t* vt;     // V^T tiles in the workspace
+  const uint8_t* vt;     // V^T images in the workspace
   const uint8_t* aux;    // FP8: K scales + 448 w_j; MXFP4: K exponents (per tile)
   const float* sig;      // FP8: sigma_t
   const float* vs_head;  // INT8: per-head V scale
@@ -322,24 +316,24 @@ using gptr = const __attribute__((address_space(1))) void*;
 using lptr = __attribute__((address_space(3))) void*;
 
 // Copy NCH 16-byte chunks global -> LDS.  The workgroup moves one round of
-// NW * 64 chunks per step (one global_load_lds_dwordx4 per wave, 1 KiB);
-// chunk p = 512 i + 64 wave + lane lands at lds + 16 p and comes from
+// NTHR chunks per step (one global_load_lds_dwordx4 per wave, 1 KiB);
+// chunk p = NTHR i + 64 wave + lane lands at lds + 16 p and comes from
 // base + off(i), off being the lane's 32-bit byte offset in round i.
-template <int NCH, int NW, class Off>
+template <int NCH, class Off>
 FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, Off off) {
   // the tile base is a wave-uniform value held in SGPRs; hiding it from the
   // optimizer keeps it from turning every copy into a 64-bit per-lane
   // pointer carried across loop iterations
   asm volatile("" : "+s"(base));
-  constexpr int ROUNDS = NCH / (NW * 64);
+  constexpr int ROUNDS = NCH / NTHR;
 #pragma unroll
   for (int i = 0; i < ROUNDS; ++i) {
-    const int grp = i * NW * 64 + wave * 64;
+    const int grp = i * NTHR + wave * 64;
     __builtin_amdgcn_global_load_lds((gptr)(base + (uint32_t)off(i)), (lptr)(lds + grp * 16), 16, 0, 0);
   }
-  constexpr int REM = NCH - ROUNDS * NW * 64;  // < one round: the first waves take it
+  constexpr int REM = NCH - ROUNDS * NTHR;  // < one round: the first waves take it
   if (REM > 0) {
-    const int grp = ROUNDS * NW * 64 + wave * 64;
+    const int grp = ROUNDS * NTHR + wave * 64;
     if (grp < NCH) {
       if (REM % 64 == 0 || grp + lane < NCH)
         __builtin_amdgcn_global_load_lds((gptr)(base + (uint32_t)off(ROUNDS)), (lptr)(lds + grp * 16), 16, 0, 0);
@@ -347,25 +341,27 @@ FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, Off of
   }
 }
 
+template <class T>
+FAQ_DEV T lds_ld(const uint8_t* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
 // KVC (FP8 only): the K and V scales are constant over each 128-key tile
 // (token blocks of a multiple of 128 keys), so the K scale folds into the
 // query's exponent factor and every w_j is 1.
 template <int MODE, int D, bool CAUSAL, bool KVC>
-__global__ __launch_bounds__(Waves<MODE>::NTHR, Waves<MODE>::WG_PER_CU) void k_attn(const KParams p) {
-  constexpr int NW = Waves<MODE>::NW;
-  constexpr int BM = Waves<MODE>::BM;
-  constexpr int RB = NW * 64 * 16;  // bytes one staging round moves
-  using G = Geo<MODE, D>;
-  constexpr int DB = D / 16;  // 16-channel output blocks
-  constexpr int NB = D / 32;  // MX blocks per row
-  constexpr int KK = D / 32;  // bf16 MFMA steps over D
-  // two tile buffers as separate objects: with the loop unrolled by two
-  // every LDS read names one of them statically, so the compiler knows it
-  // does not alias the copy in flight into the other and need not wait
-  __shared__ __attribute__((aligned(1024))) uint8_t buf0[G::BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf1[G::BUF];
+__global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
+  using G = Cfg<MODE, D>;
+  constexpr int KS = G::KS, DB = G::DB, NB = G::NB;
+  // K (+ its per-key extras) and V^T tiles in separate LDS objects: V(t)
+  // is copied while the scores and probabilities of tile t are computed
+  // from K(t), and K(t+1) while the products with V(t) run.  As distinct
+  // objects the compiler knows an LDS read of one does not alias a copy in
+  // flight into the other, so it never waits for the copy.
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[G::KBYTES + G::XKBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[G::VBYTES + G::XVBYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, j = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < NW);
 
@@ -376,465 +372,406 @@ __global__ __launch_bounds__(Waves<MODE>::NTHR, Waves<MODE>::WG_PER_CU) void k_a
     const int L = blockIdx.x, nqt = p.nqt;
     const int BH = (int)p.BH;
     if ((BH & 7) == 0) {
-      const int xcd = L & 7, j = L >> 3, per = BH >> 3;
-      if (CAUSAL) { qt = nqt - 1 - j / per; bh = xcd + 8 * (j % per); }
-      else { bh = xcd + 8 * (j / nqt); qt = j % nqt; }
+      const int xcd = L & 7, jj = L >> 3, per = BH >> 3;
+      if (CAUSAL) { qt = nqt - 1 - jj / per; bh = xcd + 8 * (jj % per); }
+      else { bh = xcd + 8 * (jj / nqt); qt = jj % nqt; }
     } else {
       if (CAUSAL) { qt = nqt - 1 - L / BH; bh = L % BH; }
       else { bh = L / nqt; qt = L % nqt; }
     }
   }
-  const int64_t h = bh % p.H;
+  const int64_t hd = bh % p.H;
   const int Sq = (int)p.Sq, Skv = (int)p.Skv, nt = (int)p.nt;
-  const int qw = qt * BM + wave * 32;  // this wave's first query
-  // last tile this wave computes: its diagonal tile under causal masking
-  // (none when its queries are all past the end); every tile otherwise
-  // (rows past the end are computed on row 0's data and never stored)
-  const int wdiag = CAUSAL ? (qw < Sq ? qw / BN : -1) : INT_MAX;
-  const uint8_t* kbase = p.k + (MODE == ATTN_FP8 ? bh * nt * (int64_t)BN : bh * (int64_t)Skv) * G::KROW;
+  const int q0 = qt * BM + wave * 32;  // this wave's first query
+  const int qi = q0 + j;               // this lane's query
+  const bool act = q0 < Sq;            // uniform per wave: any query to compute
+  const uint8_t* kbase = p.k + (MODE == ATTN_FP8 ? bh * nt * (int64_t)G::KBYTES : bh * (int64_t)Skv * G::KROW);
   const uint8_t* vtbase = p.vt + bh * nt * (int64_t)G::VBYTES;
   const uint8_t* auxbase = p.aux + bh * nt * (int64_t)G::XBYTES;
 
-  // ---- Q operands and per-query factors
-  bf16x8 qw8[2][KK];  // FP8: the bf16 images of the E4M3 codes per bf16 MFMA step
-  i32x4 qi8[2][2];    // INT8: 16 bytes per lane per 64-wide step
-  i32x4 qmx[2];       // MXFP4: 32 E2M1 per lane
-  int qsc[2];
-  float cq[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = qw + qb * 16 + l16;
+  // ---- Q operands (B of S^T = K Q^T): lane (j, h) holds, for k-step ks,
+  // the K-slice [K/2 h, K/2 h + K/2) of the instruction's K range
+  bf16x8 qbf[MODE == ATTN_FP8 ? KS : 1];  // FP8: bf16 images of the E4M3 codes
+  i32x4 qi8[MODE == ATTN_INT8 ? KS : 1];  // INT8: 16 codes
+  i32x8 qmx[MODE == ATTN_MX ? KS : 1];    // MXFP4: 32 E2M1 codes (16 bytes used)
+  int qsc[MODE == ATTN_MX ? KS : 1];      // MXFP4: their E8M0 exponents
+  float cq;
+  {
     const bool ok = qi < Sq;
-    const uint8_t* qrow = p.q + (bh * p.Sq + (ok ? qi : 0)) * (MODE == ATTN_MX ? D / 2 : D);
+    const int64_t qrow_i = bh * p.Sq + (ok ? qi : 0);
     if (MODE == ATTN_FP8) {
+      const uint8_t* qrow = p.q + qrow_i * D;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
+      for (int ks = 0; ks < KS; ++ks) {
         uint2 a = make_uint2(0, 0);
-        if (ok) a = *reinterpret_cast<const uint2*>(qrow + 32 * kk + 8 * g);
-        qw8[qb][kk] = __builtin_bit_cast(bf16x8, i32x4{(int)e4m3x2_to_bf16x2<false>(a.x), (int)e4m3x2_to_bf16x2<true>(a.x),
-                                                       (int)e4m3x2_to_bf16x2<false>(a.y), (int)e4m3x2_to_bf16x2<true>(a.y)});
+        if (ok) a = *reinterpret_cast<const uint2*>(qrow + 16 * ks + 8 * h);
+        qbf[ks] = __builtin_bit_cast(bf16x8, i32x4{(int)e4m3x2_to_bf16x2<false>(a.x), (int)e4m3x2_to_bf16x2<true>(a.x),
+                                                  (int)e4m3x2_to_bf16x2<false>(a.y), (int)e4m3x2_to_bf16x2<true>(a.y)});
       }
       const float* qs = reinterpret_cast<const float*>(p.qs);
       const int64_t nqs = (p.Sq + p.q_block - 1) / p.q_block;
-      cq[qb] = (ok ? qs[bh * nqs + qi / p.q_block] : 1.0f) * p.c_log2;
+      cq = (ok ? qs[bh * nqs + qi / p.q_block] : 1.0f) * p.c_log2;
     } else if (MODE == ATTN_INT8) {
+      const uint8_t* qrow = p.q + qrow_i * D;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        i32x4 v = {0, 0, 0, 0};
-        if (ok && 64 * kk < D) {
-          const uint4 a = *reinterpret_cast<const uint4*>(qrow + 64 * kk + 16 * g);
-          v = i32x4{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-        }
-        qi8[qb][kk] = v;
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 a = make_uint4(0, 0, 0, 0);
+        if (ok) a = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 16 * h);
+        qi8[ks] = i32x4{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
       }
       const float* qs = reinterpret_cast<const float*>(p.qs);
-      const float* ks = reinterpret_cast<const float*>(p.ks);
-      cq[qb] = qs[h] * ks[h] * p.c_log2;
+      const float* ksc = reinterpret_cast<const float*>(p.ks);
+      cq = qs[hd] * ksc[hd] * p.c_log2;
     } else {
-      i32x4 v = {0, 0, 0, 0};
-      int sc = 127;
-      if (ok && 32 * g < D) {
-        const uint4 a = *reinterpret_cast<const uint4*>(qrow + 16 * g);
-        v = i32x4{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-        sc = reinterpret_cast<const uint8_t*>(p.qs)[(bh * p.Sq + qi) * NB + g];
+      const uint8_t* qrow = p.q + qrow_i * (D / 2);
+      const uint8_t* qe = reinterpret_cast<const uint8_t*>(p.qs) + qrow_i * NB;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 a = make_uint4(0, 0, 0, 0);
+        int sc = 127;
+        if (ok) {
+          a = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 16 * h);
+          sc = qe[2 * ks + h];
+        }
+        qmx[ks] = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+        qsc[ks] = sc;
       }
-      qmx[qb] = v;
-      qsc[qb] = sc;
-      cq[qb] = p.c_log2;
+      cq = p.c_log2;
     }
   }
 
-  // ---- tile copy into LDS buffer `buf`.  A lane's chunk in round i is
-  // row i * (NW * 64 / CH) + r0, column c0 of the tile: the same swizzled
-  // column every round, RB bytes further on.
+  // ---- operand addresses: per-lane bases, constant offsets per step
+  const uint8_t* kop_base = kbuf + h * (BN * 16) + kslot(qk_row(j)) * 16;  // + ks 2 BN 16 + kb 256
+  const uint8_t* vop_base = vbuf + h * (D * 16) + j * 16;                   // + kstep 2 D 16 + db 512
+  const float* xk = reinterpret_cast<const float*>(kbuf + G::KBYTES) + 64 * h;  // FP8: the lane's keys' K scales
+  const float* xv = reinterpret_cast<const float*>(vbuf + G::VBYTES) + 64 * h;  // FP8: their 448 w_j
+  const uint8_t* xmx = kbuf + G::KBYTES + qk_row(j) * NB + h;               // MXFP4: + 16 kb NB + 2 ks
+
+  // ---- tile copies.  K: FP8 copies the bf16 image from the workspace;
+  // INT8 / MXFP4 gather K rows into the chunk-major layout (round i of a
+  // lane moves column 2 i + pw / 128 of slot pw % 128, i.e. of K row
+  // kslot(pw % 128); rows past the end re-read the last row, masked).
   const int pw = wave * 64 + lane;
-  const int kr0 = pw / G::KCH;
-  const uint32_t koff0 = (uint32_t)(((pw % G::KCH) ^ G::kswz(kr0)) << 4);
-  const uint32_t voff0 = (uint32_t)((pw / G::VCH) * G::VROW + (((pw % G::VCH) ^ G::vswz(pw / G::VCH)) << 4));
-  auto issue = [&](int t, uint8_t* buf) {
-    const int k0 = t * BN;
+  const int krow = kslot(pw & (BN - 1));
+  auto issue_k = [&](int t) {
     if (MODE == ATTN_FP8) {
-      // bf16 K tiles in the workspace, padded with zero rows
-      stage<G::KBYTES / 16, NW>(buf, kbase + (int64_t)k0 * G::KROW, wave, lane,
-                            [&](int i) { return (uint32_t)(i * RB + kr0 * G::KROW) + koff0; });
+      stage<G::KBYTES / 16>(kbuf, kbase + (int64_t)t * G::KBYTES, wave, lane,
+                            [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
     } else {
-      // K codes: rows past the end are re-read from the last row (masked)
-      stage<G::KBYTES / 16, NW>(buf, kbase, wave, lane, [&](int i) {
-        const int kr = min(k0 + i * (NW * 64 / G::KCH) + kr0, Skv - 1);
-        return (uint32_t)(kr * G::KROW) + koff0;
-      });
+      const uint32_t roff = (uint32_t)(min(t * BN + krow, Skv - 1) * G::KROW) + (uint32_t)((pw >> 7) * 16);
+      stage<G::KBYTES / 16>(kbuf, kbase, wave, lane, [&](int i) { return roff + (uint32_t)(2 * i * 16); });
     }
-    stage<G::VBYTES / 16, NW>(buf + G::VOFF, vtbase + (int64_t)t * G::VBYTES, wave, lane,
-                          [&](int i) { return (uint32_t)(i * RB) + voff0; });
     if (MODE != ATTN_INT8)
-      stage<G::XBYTES / 16, NW>(buf + G::XOFF, auxbase + (int64_t)t * G::XBYTES, wave, lane,
-                            [&](int i) { return (uint32_t)(i * RB + pw * 16); });
+      stage<G::XKBYTES / 16>(kbuf + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
+                             [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
+  };
+  auto issue_v = [&](int t) {
+    stage<G::VBYTES / 16>(vbuf, vtbase + (int64_t)t * G::VBYTES, wave, lane,
+                          [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
+    if (MODE == ATTN_FP8)
+      stage<G::XVBYTES / 16>(vbuf + G::VBYTES, auxbase + (int64_t)t * G::XBYTES + G::XKBYTES, wave, lane,
+                             [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
   };
 
-  // Row state.  O holds the output of each row relative to a reference
-  // factor fref: the true accumulator is O * fref (INT8 keeps fref = 1 and
-  // folds its per-tile factor in with an fma; the bf16-MFMA modes rescale O
-  // once per tile and let the PV MFMA accumulate straight into it).
-  float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f}, fref[2] = {1.f, 1.f};
-  f32x4 O[2][DB];
+  // Row state (each lane holds its query's; both halves agree).  O holds
+  // the output relative to a reference factor fref: the true accumulator is
+  // O * fref (INT8 keeps fref = 1 and folds its per-tile factor in with an
+  // fma; the bf16-MFMA modes rescale O once per tile and let the P V MFMA
+  // accumulate straight into it).
+  float M = -INFINITY, L = 0.f, fref = 1.f;
+  f32x16 O[DB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) O[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < DB; ++db) O[db] = f32x16{};
 
   const int qlast = min(Sq, (qt + 1) * BM) - 1;
   const int t_end = CAUSAL ? min(nt, qlast / BN + 1) : nt;
-  const float vscale_i8 = (MODE == ATTN_INT8) ? p.vs_head[h] * (1.0f / 127.0f) : 1.0f;
+  const float vscale_i8 = (MODE == ATTN_INT8) ? p.vs_head[hd] * (1.0f / 127.0f) : 1.0f;
+  // valid keys of this lane's query: [0, lim)
+  const int lim = CAUSAL ? min(Skv, qi + 1) : Skv;
 
-  auto step = [&](int t, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+  issue_k(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+#pragma clang loop unroll(disable)
+  for (int t = 0; t < t_end; ++t) {
+    issue_v(t);
     const int k0 = t * BN;
-    // this wave's copies of tile t have landed; the barrier makes every
-    // wave's copies visible and retires all reads of the other buffer
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (t + 1 < t_end) issue(t + 1, nxt);
-    if (t > wdiag) return;
     // the ragged last tile and the causal diagonal need a per-key validity
     // test; the other tiles skip it (uniform branch)
-    const bool masked = (k0 + BN > Skv) || (CAUSAL && t == wdiag);
-    const uint8_t* Kt = cur;
-    const uint8_t* Vl = cur + G::VOFF;
-    const float* Xt = reinterpret_cast<const float*>(cur + G::XOFF);
+    const bool masked = (k0 + BN > Skv) || (CAUSAL && t == qt);
+    const int rel = lim - k0 - 64 * h;  // key 64 h + 16 kb + r is valid when 16 kb + r < rel
 
-    // One query block at a time: scores, tile max, probabilities and the
-    // quantized P operand of block qb, so only one block's scores are held
-    // in registers (the K operands are read once per query block).
-    i32x4 pi8[2][2];   // INT8: rne(127 p) bytes, keys in vt_key_int8 order
-    i32x4 pbf[2][4];   // FP8 / MXFP4: bf16 images of the quantized p, per step kk
-    float rscale[2], bvi8[2];
-    bool rescale_any = false;
+    f32x16 S[4];
+    i32x16 SI[4];
+    float rscale = 1.f, ce = cq, ms = 0.f, bt = 0.f;
+    float gmax[2] = {-INFINITY, -INFINITY};
+    if (act) {
+      // ---- S^T = K Q^T: four 32-key blocks, two at a time (two
+      // independent accumulation chains keep the MFMA pipe full)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // The two query blocks read the same K operands and per-key factors;
-      // an opaque zero offset keeps the compiler from reusing the first
-      // block's reads (which would hold them all in registers) - LDS reads
-      // are cheap, registers are not.
-      int zq = 0;
-      asm volatile("" : "+v"(zq));
-      const uint8_t* Kl = Kt + zq;
-      const float* Xf = Xt + zq;
-      const uint8_t* Xb = reinterpret_cast<const uint8_t*>(Xt) + zq;
-      // ---- S^T = K Q^T: score of (query qb*16 + l16, key of block b at
-      // output row 4g + r).  Operands of block b+1 are read from LDS while
-      // block b multiplies, and the VALU work on block b-1 fills the MFMA
-      // shadow; a scheduling fence closes each step, which bounds the
-      // registers held by operands in flight.
-      f32x4 s[8];
-      int mi = INT_MIN;
-      if (MODE == ATTN_FP8) {
-        bf16x8 kop[1][KK];
-        auto kload = [&](int bb, bf16x8 (&dst)[KK]) {
+      for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            dst[kk] = *reinterpret_cast<const bf16x8*>(&Kl[(16 * bb + l16) * G::KROW + (((4 * kk + g) ^ G::kswz(l16)) << 4)]);
-        };
-        auto kscale = [&](int bb) {
-          const float4 skv = *reinterpret_cast<const float4*>(&Xf[16 * bb + 4 * g]);
-          s[bb][0] *= skv.x; s[bb][1] *= skv.y; s[bb][2] *= skv.z; s[bb][3] *= skv.w;
-        };
-        // (one block of K operands in flight: 16 registers each)
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-          kload(bb, kop[0]);
-          s[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][0], qw8[qb][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-          for (int kk = 1; kk < KK; ++kk)
-            s[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][kk], qw8[qb][kk], s[bb], 0, 0, 0);
-          if (!KVC && bb > 0) kscale(bb - 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!KVC) kscale(7);
-      } else if (MODE == ATTN_INT8) {
-        constexpr int K8 = D / 64;
-        constexpr int PD = 3;  // K operand blocks in flight
-        i32x4 kop[PD + 1][K8];
-        i32x4 si[2];
-        auto kload = [&](int bb, i32x4 (&dst)[K8]) {
-#pragma unroll
-          for (int kk = 0; kk < K8; ++kk) {
-            const uint4 v = *reinterpret_cast<const uint4*>(&Kl[(16 * bb + l16) * G::KROW + (((4 * kk + g) ^ G::kswz(l16)) << 4)]);
-            dst[kk] = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+          for (int kk = 0; kk < 2; ++kk) {
+            const int kb = 2 * pr + kk;
+            const uint8_t* a = kop_base + ks * (2 * BN * 16) + kb * 256;
+            if (MODE == ATTN_FP8) {
+              if (ks == 0) S[kb] = f32x16{};
+              S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld<bf16x8>(a), qbf[ks], S[kb], 0, 0, 0);
+            } else if (MODE == ATTN_INT8) {
+              if (ks == 0) SI[kb] = i32x16{};
+              const uint4 v = lds_ld<uint4>(a);
+              SI[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, qi8[ks],
+                                                             SI[kb], 0, 0, 0);
+            } else {
+              if (ks == 0) S[kb] = f32x16{};
+              const uint4 v = lds_ld<uint4>(a);
+              const int sc = xmx[16 * kb * NB + 2 * ks];
+              S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}, qmx[ks], S[kb], 4, 4, 0, sc, 0, qsc[ks]);
+            }
           }
-        };
-        // exact int32 scores (|s| < 2^21): the float conversion is exact
-        auto post = [&](int bb) {
-          const i32x4 v = si[bb & 1];
-          if (!masked) mi = max(mi, max(max(v[0], v[1]), max(v[2], v[3])));
-          s[bb] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-        };
-#pragma unroll
-        for (int bb = 0; bb < PD; ++bb) kload(bb, kop[bb]);
-#pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-          if (bb + PD < 8) kload(bb + PD, kop[(bb + PD) % (PD + 1)]);
-          const int ko = bb % (PD + 1);
-          si[bb & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[ko][0], qi8[qb][0], i32x4{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-          for (int kk = 1; kk < K8; ++kk)
-            si[bb & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[ko][kk], qi8[qb][kk], si[bb & 1], 0, 0, 0);
-          if (bb > 0) post(bb - 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        post(7);
-      } else {
-        i32x8 kop[2];
-        int ksc[2];
-        auto kload = [&](int bb, i32x8& dst, int& sc) {
-          const int row = k_row_mx(bb, l16);
-          dst = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-          sc = 127;
-          if (32 * g < D) {
-            const uint4 v = *reinterpret_cast<const uint4*>(&Kl[row * G::KROW + ((g ^ G::kswz(row)) << 4)]);
-            dst = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            sc = Xb[row * NB + g];
-          }
-        };
-        const i32x4 qv = qmx[qb];
-        const i32x8 qop = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
-        kload(0, kop[0], ksc[0]);
-#pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-          if (bb + 1 < 8) kload(bb + 1, kop[(bb + 1) & 1], ksc[(bb + 1) & 1]);
-          s[bb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop[bb & 1], qop, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                   4, 4, 0, ksc[bb & 1], 0, qsc[qb]);
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
 
-      if (masked) {
-        // key kl of the tile is valid when kl < lim; the lane's own part of
-        // kl is folded into the limit so the rest is an immediate
-        const int qi = qw + qb * 16 + l16;
-        const int lim = (CAUSAL ? min(Skv, qi + 1) : Skv) - k0;
-        const int rel = lim - (MODE == ATTN_MX ? 32 * g : 4 * g);
-#pragma unroll
-        for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kc = (MODE == ATTN_MX) ? (4 * bb + r) : (16 * bb + r);
-            s[bb][r] = (kc < rel) ? s[bb][r] : -INFINITY;
-          }
-      }
-
-      // ---- tile max, then the row combination factors: a rescales what
-      // was accumulated so far, bt weights this tile
+      // ---- per-key K scale (FP8 per-token), masking, tile maximum
       float m;
-      if (MODE == ATTN_INT8 && !masked) {
-        m = (float)mi;
-      } else {
-        m = -INFINITY;
+      if (MODE == ATTN_INT8) {
+        if (!masked) {
+          // exact int32 scores (|s| < 2^21): max in integers, converted once
+          int mi = INT_MIN;
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) m = fmaxf(fmaxf(m, fmaxf(s[bb][0], s[bb][1])), fmaxf(s[bb][2], s[bb][3]));
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mi = max(mi, max(SI[kb][r], SI[kb][r + 1]));
+          m = (float)mi;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[kb][r] = (float)SI[kb][r];
+        } else {
+          m = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              S[kb][r] = (16 * kb + r < rel) ? (float)SI[kb][r] : -INFINITY;
+              m = fmaxf(m, S[kb][r]);
+            }
+        }
+      } else {
+        if (MODE == ATTN_FP8 && !KVC) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const float4 sk = *reinterpret_cast<const float4*>(xk + 16 * kb + 4 * q4);
+              S[kb][4 * q4 + 0] *= sk.x; S[kb][4 * q4 + 1] *= sk.y;
+              S[kb][4 * q4 + 2] *= sk.z; S[kb][4 * q4 + 3] *= sk.w;
+            }
+        }
+        if (masked) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[kb][r] = (16 * kb + r < rel) ? S[kb][r] : -INFINITY;
+        }
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          float x = -INFINITY;
+#pragma unroll
+          for (int kb = 2 * g2; kb < 2 * g2 + 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(S[kb][r], S[kb][r + 1]));
+          gmax[g2] = x;  // MXFP4: the lane's 32-key group maxima
+        }
+        m = fmaxf(gmax[0], gmax[1]);
       }
-      const float mlane = m;  // max over this lane's keys (MXFP4: its 32-key group)
-      m = rows4_max(m);
-      // exponent factor of this row and tile: scores times ce are log2 units
-      const float ce = (MODE == ATTN_FP8 && KVC) ? cq[qb] * Xf[0] : cq[qb];
+      m = halves_max(m);
+
+      // ---- the row's combination factors: a rescales what was
+      // accumulated so far, bt weights this tile
+      if (MODE == ATTN_FP8 && KVC) ce = cq * xk[-64 * h];  // the tile's K scale
       const float ml = m * ce;  // tile max, log2 units (M is kept in these units)
       float Mn, a;
       if (MODE == ATTN_INT8) {
         // lazy reference: keep the running reference unless this tile's max
         // exceeds it by more than 2^8 (tile weights stay <= 2^8, far from
         // overflow), so O is rescaled only when the max jumps
-        const bool jump = ml > M[qb] + 8.0f;
-        Mn = jump ? ml : M[qb];
-        a = jump ? __builtin_amdgcn_exp2f(M[qb] - ml) : 1.0f;
+        const bool jump = ml > M + 8.0f;
+        Mn = jump ? ml : M;
+        a = jump ? __builtin_amdgcn_exp2f(M - ml) : 1.0f;
       } else {
-        Mn = fmaxf(M[qb], ml);
-        a = __builtin_amdgcn_exp2f(M[qb] - Mn);
+        Mn = fmaxf(M, ml);
+        a = __builtin_amdgcn_exp2f(M - Mn);
       }
-      const float bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml - Mn);
-      M[qb] = Mn;
-      // bf16-MFMA modes: new reference factor f = bt (times sigma_t / 448
-      // for FP8); a row whose tile is negligible (bt < 2^-64) keeps its
-      // reference and contributes nothing, which keeps O bounded.
+      bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml - Mn);
+      M = Mn;
       bool live = true;
       if (MODE == ATTN_INT8) {
-        rscale[qb] = a;
-        bvi8[qb] = bt * vscale_i8;
+        rscale = a;
       } else {
+        // new reference factor f = bt (times sigma_t / 448 for FP8); a row
+        // whose tile is negligible (bt < 2^-64) keeps its reference and
+        // contributes nothing, which keeps O bounded
         float ft = bt;
         if (MODE == ATTN_FP8) ft *= p.sig[bh * nt + t] * (1.0f / 448.0f);
         live = bt >= 0x1p-64f;
-        rscale[qb] = live ? (fref[qb] * a / ft) : a;
-        fref[qb] = live ? ft : fref[qb];
+        rscale = live ? fref * a * __builtin_amdgcn_rcpf(ft) : a;
+        fref = live ? ft : fref;
       }
-      rescale_any |= (rscale[qb] != 1.0f);
-
-      // ---- probabilities, tile sum and the quantized P operand.  A row
-      // that is not live takes +inf as its reference, so all its p are 0.
-      // INT8 and KVC fold the static P scale into the exponent (127 p and
-      // 448 p come out of the exp); their sums are scaled back once.
-      const float ms = (m == -INFINITY) ? 0.0f : (live ? m : INFINITY);
-      constexpr float kLog2_127 = 6.9886846867721655f, kLog2_448 = 8.807354922057604f;
-      const float mc = ms * ce - kLog2_127;
-      float ls[2] = {0.f, 0.f};
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float pv;
-          if (MODE == ATTN_INT8) {
-            // 127 p = 2^(s ce - (m ce - log2 127)); at the maximum this may
-            // differ from 127 by an ulp, which cannot move rne(127 p)
-            pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], ce, -mc));
-          } else if (MODE == ATTN_FP8 && KVC) {
-            // 448 p (w = 1): at the maximum within an ulp of 448, whose code
-            // both roundings give
-            pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r] - ms, ce, kLog2_448));
-          } else {
-            // (x - m) is exactly 0 at the tile maximum, so p = 1 there exactly
-            pv = __builtin_amdgcn_exp2f((s[bb][r] - ms) * ce);
-          }
-          s[bb][r] = pv;
-          ls[r & 1] += pv;
-        }
-        if (MODE == ATTN_INT8) {
-          // rne(127 p), saturated to [0, 255], packed byte by byte
-          uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(s[bb][0], 0u, 0u);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(s[bb][1], 1u, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(s[bb][2], 2u, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(s[bb][3], 3u, w);
-          pi8[qb][bb >> 2][bb & 3] = (int)w;
-        } else if (MODE == ATTN_FP8) {
-          // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
-          int e8;
-          if (KVC) {
-            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][0], s[bb][1], 0, false);
-            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][2], s[bb][3], e8, true);
-          } else {
-            const float4 vm = *reinterpret_cast<const float4*>(&Xf[BN + 16 * bb + 4 * g]);
-            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][0] * vm.x, s[bb][1] * vm.y, 0, false);
-            e8 = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][2] * vm.z, s[bb][3] * vm.w, e8, true);
-          }
-          pbf[qb][bb >> 1][2 * (bb & 1)] = (int)e4m3x2_to_bf16x2<false>((uint32_t)e8);
-          pbf[qb][bb >> 1][2 * (bb & 1) + 1] = (int)e4m3x2_to_bf16x2<true>((uint32_t)e8);
-        }
-      }
-      if (MODE == ATTN_MX) {
-        // this lane's 32 keys are one MX group: local max -> shared
-        // exponent; p -> E2M1(p / 2^E) * 2^E, exact in bf16.  The group's
-        // largest p is the same function of the lane's largest score.
-        const float pmax = __builtin_amdgcn_exp2f((mlane - ms) * ce);
-        const int E = mx_exponent(pmax);
-        const float sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
-#pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, s[bb][2 * hh], s[bb][2 * hh + 1], sc, 0);
-            const int v2 = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
-            pbf[qb][bb >> 1][2 * (bb & 1) + hh] = v2;
-          }
-        }
-      }
-      const float lscale = MODE == ATTN_INT8 ? 1.0f / 127.0f : ((MODE == ATTN_FP8 && KVC) ? 1.0f / 448.0f : 1.0f);
-      L[qb] = L[qb] * a + rows4_sum(ls[0] + ls[1]) * (bt * lscale);
-      __builtin_amdgcn_sched_barrier(0);
+      L *= a;
+      // a row that is not live takes +inf as its reference, so all its p are 0
+      ms = (m == -INFINITY) ? 0.0f : (live ? m : INFINITY);
     }
 
-    // ---- O^T += V^T P^T (per 16-channel block), V operands of block db+1
-    // read while block db multiplies
-    if (MODE == ATTN_INT8) {
-      const bool do_rescale = __any(rescale_any);
-      constexpr int PD = 3;  // V operand blocks in flight
-      i32x4 vop[PD + 1][2], ci[2][2];
-      auto vload = [&](int db, i32x4 (&dst)[2]) {
+    // V(t) has landed everywhere and every wave is done with K(t)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (t + 1 < t_end) issue_k(t + 1);
+
+    if (act) {
+      // ---- probabilities, tile sum, the quantized P operand and
+      // O^T += V^T P^T
+      float ls0 = 0.f, ls1 = 0.f;
+      if (MODE == ATTN_INT8) {
+        // 127 p = 2^(s ce - (m ce - log2 127)); at the maximum this may
+        // differ from 127 by an ulp, which cannot move rne(127 p)
+        const float mc = ms * ce - kLog2_127;
+        i32x4 P[4];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const uint4 v = *reinterpret_cast<const uint4*>(&Vl[(16 * db + l16) * G::VROW + (((2 * g + h2) ^ G::vswz(l16)) << 4)]);
-          dst[h2] = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * w + b], ce, -mc));
+              if (b & 1) ls1 += pv; else ls0 += pv;
+              word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p)
+            }
+            P[kb][w] = (int)word;
+          }
         }
-      };
-      auto accum = [&](int db) {
+        L += halves_sum(ls0 + ls1) * (bt * (1.0f / 127.0f));
+        // the running max moves rarely once a row has seen its largest
+        // scores: rescale only when some row of the wave needs it
+        if (__builtin_amdgcn_ballot_w64(rscale != 1.0f) != 0) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[qb][db][r] = __builtin_fmaf((float)ci[qb][db & 1][r], bvi8[qb], O[qb][db][r]);
-      };
-      // the running max moves rarely once a row has seen its largest
-      // scores: rescale only when some row of the wave needs it
-      if (do_rescale) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[qb][db][r] *= rscale[qb];
-      }
-#pragma unroll
-      for (int db = 0; db < PD && db < DB; ++db) vload(db, vop[db]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        if (db + PD < DB) vload(db + PD, vop[(db + PD) % (PD + 1)]);
-        const int vo = db % (PD + 1);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          ci[qb][db & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vop[vo][0], pi8[qb][0], i32x4{0, 0, 0, 0}, 0, 0, 0);
-          ci[qb][db & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(vop[vo][1], pi8[qb][1], ci[qb][db & 1], 0, 0, 0);
+          for (int db = 0; db < DB; ++db) O[db] *= rscale;
         }
-        if (db > 0) accum(db - 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      accum(DB - 1);
-    } else {
-      bf16x8 vop[2][4];
-      auto vload = [&](int db, bf16x8 (&dst)[4]) {
+        const float bv = bt * vscale_i8;
+        // two output blocks at a time: two independent accumulation chains
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          dst[kk] = *reinterpret_cast<const bf16x8*>(&Vl[(16 * db + l16) * G::VROW + (((4 * kk + g) ^ G::vswz(l16)) << 4)]);
-      };
-      vload(0, vop[0]);
+        for (int d2 = 0; d2 < DB; d2 += 2) {
+          i32x16 C[2] = {i32x16{}, i32x16{}};
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        if (db + 1 < DB) vload(db + 1, vop[(db + 1) & 1]);
-        // the reference factor moves almost every tile: rescale unconditionally
+          for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+            for (int dd = 0; dd < 2; ++dd) {
+              const uint4 v = lds_ld<uint4>(vop_base + kb * (2 * D * 16) + (d2 + dd) * 512);
+              C[dd] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, P[kb],
+                                                            C[dd], 0, 0, 0);
+            }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) O[qb][db][r] *= rscale[qb];
+          for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+            for (int r = 0; r < 16; ++r) O[d2 + dd][r] = __builtin_fmaf((float)C[dd][r], bv, O[d2 + dd][r]);
+        }
+      } else {
+        // FP8 / MXFP4: rescale, then per 32-key block: probabilities, the
+        // bf16 P operand of its two k-steps, and their products
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            O[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db & 1][kk], __builtin_bit_cast(bf16x8, pbf[qb][kk]),
-                                                                O[qb][db], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int db = 0; db < DB; ++db) O[db] *= rscale;
+        const float mce = ms * ce;
+        float sc = 1.0f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          if (MODE == ATTN_MX && (kb & 1) == 0) {
+            // this lane's keys of blocks kb, kb + 1 are one MX group:
+            // group max -> shared exponent; p -> E2M1(p / 2^E) * 2^E, exact
+            // in bf16.  The group's largest p is the same function of the
+            // group's largest score.
+            const float pmax = __builtin_amdgcn_exp2f((gmax[kb >> 1] - ms) * ce);
+            const int E = mx_exponent(pmax);
+            sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            float pv[8];
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) {
+              const float x = S[kb][8 * s2 + t8];
+              // KVC: 448 p comes out of the exponent (448 p at the maximum
+              // is within an ulp of 448, whose code both roundings give).
+              // Otherwise p = 1 exactly at the tile maximum ((x - m) is 0):
+              // there 448 w_j can sit on an E4M3 tie (bf16-derived scale
+              // ratios do), and the MX group of the maximum has its amax at
+              // a power of two
+              pv[t8] = (MODE == ATTN_FP8 && KVC) ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, kLog2_448 - mce))
+                                                 : __builtin_amdgcn_exp2f((x - ms) * ce);
+              if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
+            }
+            i32x4 pop;
+            if (MODE == ATTN_FP8) {
+              // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
+              if (!KVC) {
+                const float4 v0 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2);
+                const float4 v1 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2 + 4);
+                pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
+                pv[4] *= v1.x; pv[5] *= v1.y; pv[6] *= v1.z; pv[7] *= v1.w;
+              }
+              int e0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+              e0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], e0, true);
+              int e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4], pv[5], 0, false);
+              e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], e1, true);
+              pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0), (int)e4m3x2_to_bf16x2<true>((uint32_t)e0),
+                          (int)e4m3x2_to_bf16x2<false>((uint32_t)e1), (int)e4m3x2_to_bf16x2<true>((uint32_t)e1)};
+            } else {
+              // each pair through byte 0: E2M1(p / 2^E), then back times 2^E
+#pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                const uint32_t f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv[2 * b], pv[2 * b + 1], sc, 0);
+                pop[b] = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
+              }
+            }
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pop);
+            const int kst = 2 * kb + s2;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+              O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  lds_ld<bf16x8>(vop_base + kst * (2 * D * 16) + db * 512), pb, O[db], 0, 0, 0);
+          }
+        }
+        const float lsc = (MODE == ATTN_FP8 && KVC) ? (1.0f / 448.0f) : 1.0f;
+        L += halves_sum(ls0 + ls1) * (bt * lsc);
       }
     }
-  };
-
-  issue(0, buf0);
-#pragma clang loop unroll(disable)
-  for (int t = 0; t < t_end; t += 2) {
-    step(t, buf0, buf1);
-    if (t + 1 < t_end) step(t + 1, buf1, buf0);
+    // K(t+1) has landed everywhere and every wave is done with V(t)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
   }
 
-  // ---- normalize, store
+  // ---- normalize, store: register r of block db is channel
+  // 32 db + 8 (r / 4) + 4 h + r % 4 of query qi
+  if (qi < Sq) {
+    const float inv = fref / L;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = qw + qb * 16 + l16;
-    if (qi >= Sq) continue;
-    const float inv = fref[qb] / L[qb];
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int64_t off = (bh * p.Sq + qi) * D + 16 * db + 4 * g;
-      const float o0 = O[qb][db][0] * inv, o1 = O[qb][db][1] * inv;
-      const float o2 = O[qb][db][2] * inv, o3 = O[qb][db][3] * inv;
-      if (p.out_bf16) {
-        const uint32_t w0 = f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(o2) | (f32_to_bf16_bits(o3) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + off) = make_uint2(w0, w1);
-      } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) = make_float4(o0, o1, o2, o3);
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int64_t off = (bh * p.Sq + qi) * D + 32 * db + 8 * a4 + 4 * h;
+        const float o0 = O[db][4 * a4] * inv, o1 = O[db][4 * a4 + 1] * inv;
+        const float o2 = O[db][4 * a4 + 2] * inv, o3 = O[db][4 * a4 + 3] * inv;
+        if (p.out_bf16) {
+          const uint32_t w0 = f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16);
+          const uint32_t w1 = f32_to_bf16_bits(o2) | (f32_to_bf16_bits(o3) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + off) = make_uint2(w0, w1);
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) = make_float4(o0, o1, o2, o3);
+        }
       }
-    }
   }
 }
 
@@ -845,19 +782,18 @@ hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   dim3 pgrid((unsigned)nt, (unsigned)(a.B * a.H));
   if (MODE == ATTN_MX) {
     k_prep_mx<D><<<pgrid, 256, 0, st>>>((const uint8_t*)a.v_codes, (const uint8_t*)a.v_scales,
-                                        (const uint8_t*)a.k_scales, a.Skv, nt,
-                                        reinterpret_cast<uint16_t*>(ws + l.vt_off), ws + l.aux_off);
+                                        (const uint8_t*)a.k_scales, a.Skv, nt, ws + l.vt_off, ws + l.aux_off);
   } else {
     k_prep<D, MODE == ATTN_FP8><<<pgrid, 256, 0, st>>>(
         (const uint8_t*)a.k_codes, (const float*)a.k_scales, (const uint8_t*)a.v_codes, (const float*)a.v_scales,
-        a.Skv, a.kv_block, nt, ws + l.vt_off, reinterpret_cast<uint16_t*>(ws + l.kb_off),
-        reinterpret_cast<float*>(ws + l.aux_off), reinterpret_cast<float*>(ws + l.sig_off));
+        a.Skv, a.kv_block, nt, ws + l.vt_off, ws + l.kb_off, reinterpret_cast<float*>(ws + l.aux_off),
+        reinterpret_cast<float*>(ws + l.sig_off));
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   KParams p{};
   p.H = a.H; p.BH = a.B * a.H; p.Sq = a.Sq; p.Skv = a.Skv; p.nt = nt;
-  p.nqt = (int)((a.Sq + Waves<MODE>::BM - 1) / Waves<MODE>::BM);
+  p.nqt = (int)((a.Sq + BM - 1) / BM);
   p.q = (const uint8_t*)a.q_codes; p.qs = a.q_scales;
   p.k = MODE == ATTN_FP8 ? ws + l.kb_off : (const uint8_t*)a.k_codes;
   p.ks = a.k_scales;
@@ -871,15 +807,13 @@ hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   dim3 grid((unsigned)(p.nqt * p.BH));
   if constexpr (MODE == ATTN_FP8) {
     if (a.kv_block % BN == 0) {
-      if (a.causal) k_attn<MODE, D, true, true><<<grid, Waves<MODE>::NTHR, 0, st>>>(p);
-      else k_attn<MODE, D, false, true><<<grid, Waves<MODE>::NTHR, 0, st>>>(p);
+      if (a.causal) k_attn<MODE, D, true, true><<<grid, NTHR, 0, st>>>(p);
+      else k_attn<MODE, D, false, true><<<grid, NTHR, 0, st>>>(p);
       return hipGetLastError();
     }
   }
-  {
-    if (a.causal) k_attn<MODE, D, true, false><<<grid, Waves<MODE>::NTHR, 0, st>>>(p);
-    else k_attn<MODE, D, false, false><<<grid, Waves<MODE>::NTHR, 0, st>>>(p);
-  }
+  if (a.causal) k_attn<MODE, D, true, false><<<grid, NTHR, 0, st>>>(p);
+  else k_attn<MODE, D, false, false><<<grid, NTHR, 0, st>>>(p);
   return hipGetLastError();
 }
 
