@@ -18,14 +18,17 @@ not by any value on the pages):
   each query row i and tile t with at least one unmasked key:
   m_it = max_j s_ij, p_ij = exp(s_ij - m_it), L_it = sum_j p_ij (unquantized).
 * p enters the PV product quantized to the mode's own type with a static
-  scale (0 <= p <= 1):
-    - 'int8':  Pq = rne(127 p) / 127;
-    - 'fp8':   with sigma_t = max over the tile's keys of the per-key V scale
-               and w_j = s_v,j / sigma_t (the V scale folded into P):
-               Pq = E4M3(448 p w_j) / (448 w_j), the code decided with the
-               multiplier 448 w_j rounded as fp32 (fl32(448 fl32(w_j)));
+  scale (0 <= p <= 1).  With sigma_t = max over the tile's keys of the
+  per-key V scale and w_j = s_v,j / sigma_t (the V scale folded into P; w = 1
+  when V has one scale per tile - per-head and token-block scopes - or when
+  no V scale is given):
+    - 'int8':  Pq = rne(127 p w_j) / (127 w_j), the code decided with the
+               multiplier fl32(127 fl32(w_j));
+    - 'fp8':   Pq = E4M3(448 p w_j) / (448 w_j), the code decided with the
+               multiplier fl32(448 fl32(w_j));
     - 'mxfp4': the MXFP4 quantizer applied along keys, 32-key groups aligned
                to absolute key index, masked keys counting as p = 0;
+    - 'mxfp8': the same with the MXFP8 quantizer (E4M3 elements, emax 8);
     - 'exact': Pq = p (no quantization; reduces to softmax attention).
   C_it = sum_j Pq_ij vhat_j with vhat the exactly dequantized V.
 * Combine: M_i = max_t m_it; O_i = sum_t e^{m_it-M_i} C_it / sum_t e^{m_it-M_i} L_it.
@@ -38,6 +41,9 @@ import numpy as np
 from . import formats as F
 from .quantize import mx_shared_exponent
 
+# P rule -> qmax of its static probability scale
+_PQMAX = {"int8": 127.0, "fp8": F.E4M3_MAX}
+
 P_TILE = 128
 MX_GROUP = 32
 TIE_REL = 2.0 ** -12
@@ -47,55 +53,64 @@ def _quantize_p(p, rule, w=None, w_dec=None):
     """Dequantized quantized probabilities for one row-chunk, per tile.
 
     p: [nr, nt, 128] fp64 (masked -> 0); w: [nt, 128] exact s_v,j / sigma_t
-    and w_dec: [nt, 128] the fp32 multiplier fl32(448 fl32(s_v,j / sigma_t))
-    (fp8 only).
+    and w_dec: [nt, 128] the fp32 multiplier fl32(qmax fl32(s_v,j / sigma_t))
+    ('int8' / 'fp8'; None means w = 1).
     Returns (Pq, step, near) where `near` flags elements whose pre-rounding
     value lies within 2^-12 (relative) of a rounding boundary and `step` is
     the size of the code step such an element may flip by (in p units)."""
     if rule == "exact":
         z = np.zeros_like(p)
         return p.copy(), z, z.astype(bool)
-    if rule == "int8":
-        u = 127.0 * p
-        pq = np.rint(u) / 127.0
-        frac = u - np.floor(u)
-        near = (np.abs(frac - 0.5) <= TIE_REL * u) & (u > 0)
-        step = np.full_like(p, 1.0 / 127.0)
-        return pq, step, near
-    if rule == "fp8":
-        # The E4M3 code is decided on u = 448 p w_j.  The pages fix no
-        # precision for this decision, so it is taken in fp32 as the kernel
-        # takes it: the multiplier is fl32(448 * fl32(s_v,j / sigma_t)) (for
-        # the tile's own maximum, p = 1, u is exactly that multiplier on both
+    if rule in _PQMAX:
+        # The code is decided on u = qmax p w_j.  The pages fix no precision
+        # for this decision, so it is taken in fp32 as the kernel takes it:
+        # the multiplier is fl32(qmax * fl32(s_v,j / sigma_t)) (for the
+        # tile's own maximum, p = 1, u is exactly that multiplier on both
         # sides; bf16-derived scale ratios land on E4M3 ties there).  The
-        # dequantized value divides by the exact 448 w_j.
-        mult = w_dec[None, :, :]
-        scale = 448.0 * w[None, :, :]
+        # dequantized value divides by the exact qmax w_j.
+        qmax = _PQMAX[rule]
+        if w is None:
+            mult = np.full(p.shape[1:], qmax)[None]
+            scale = mult
+        else:
+            mult = w_dec[None, :, :]
+            scale = qmax * w[None, :, :]
         u = p * mult
-        pq = F.e4m3_decode(F.e4m3_encode(u)) / scale
-        lo, hi = F.e4m3_neighbors(u)
-        mid = 0.5 * (lo + hi)
-        near = (np.abs(u - mid) <= TIE_REL * u) & (u > 0)
-        step = (hi - lo) / scale
+        if rule == "int8":
+            pq = np.rint(u) / scale
+            frac = u - np.floor(u)
+            near = (np.abs(frac - 0.5) <= TIE_REL * u) & (u > 0)
+            step = 1.0 / scale * np.ones_like(p)
+        else:
+            pq = F.e4m3_decode(F.e4m3_encode(u)) / scale
+            lo, hi = F.e4m3_neighbors(u)
+            mid = 0.5 * (lo + hi)
+            near = (np.abs(u - mid) <= TIE_REL * u) & (u > 0)
+            step = (hi - lo) / scale
         return pq, step, near
-    if rule == "mxfp4":
+    if rule in ("mxfp4", "mxfp8"):
+        if rule == "mxfp4":
+            enc, dec, nbr, emax, vmax = F.e2m1_encode, F.e2m1_decode, F.e2m1_neighbors, F.E2M1_EMAX, F.E2M1_MAX
+        else:
+            enc, dec, nbr, emax, vmax = F.e4m3_encode, F.e4m3_decode, F.e4m3_neighbors, F.E4M3_EMAX, F.E4M3_MAX
         nr, nt, n = p.shape
         g = p.reshape(nr, nt, n // MX_GROUP, MX_GROUP)
         amax = g.max(axis=3)
-        E = mx_shared_exponent(amax)
+        E = mx_shared_exponent(amax, emax=emax)
         v = np.ldexp(g, -E[..., None])
-        pq = np.ldexp(F.e2m1_decode(F.e2m1_encode(v)), E[..., None])
-        lo, hi = F.e2m1_neighbors(v)
+        pq = np.ldexp(dec(enc(v)), E[..., None])
+        lo, hi = nbr(v)
         mid = 0.5 * (lo + hi)
-        near = (np.abs(v - mid) <= TIE_REL * v) & (v > 0) & (v < 6.0)
+        near = (np.abs(v - mid) <= TIE_REL * v) & (v > 0) & (v < vmax)
         step = np.ldexp(hi - lo, E[..., None])
         # A group whose amax sits just off a power of two may take the other
-        # shared exponent; then every element of it may move by up to
-        # 3 * 2^(E+1).  amax == 1 exactly (the tile's own maximum) is exact on
-        # both sides and is not a tie.
+        # shared exponent; every element of it may then move by up to the
+        # larger grid's top step plus the saturation of the top binade:
+        # 3 * 2^(E+1) for E2M1, 3 * 2^(E+5) for E4M3.  amax == 1 exactly
+        # (the tile's own maximum) is exact on both sides and is not a tie.
         k = np.rint(np.log2(np.where(amax > 0, amax, 1.0)))
         gnear = (np.abs(amax - np.exp2(k)) <= TIE_REL * amax) & (amax > 0) & (amax != 1.0)
-        gstep = 3.0 * np.ldexp(1.0, E + 1)
+        gstep = 3.0 * np.ldexp(1.0, E + (1 if rule == "mxfp4" else 5))
         near = near | gnear[..., None]
         step = np.where(gnear[..., None], np.maximum(step, gstep[..., None]), step)
         return (pq.reshape(nr, nt, n), step.reshape(nr, nt, n),
@@ -108,7 +123,8 @@ def attention(qhat, khat, vhat, p_rule, *, v_scale=None, causal=False,
     """Quantized-domain flash attention reference.
 
     qhat: [B,H,Sq,D]; khat, vhat: [B,H,Skv,D] dequantized values.
-    v_scale: [B,H,Skv] per-key V scale (needed for p_rule 'fp8').
+    v_scale: [B,H,Skv] per-key V scale, folded into P by the 'int8' and 'fp8'
+    rules (None: w = 1).
     rows: optional sorted array of query rows to evaluate (for every (b,h)).
     Returns O [B,H,R,D] fp64, plus (T [B,H,R,D], n_tie) when allowance=True:
     T is the tie allowance - the sum, over probability elements near a
@@ -137,14 +153,16 @@ def attention(qhat, khat, vhat, p_rule, *, v_scale=None, causal=False,
             v = np.concatenate([vhat[b, h], np.zeros((pad, D))], axis=0)
             vt = v.reshape(nt, P_TILE, D)
             w = w_dec = None
-            if p_rule == "fp8":
+            if p_rule in _PQMAX and v_scale is not None:
+                qmax = _PQMAX[p_rule]
                 sv = np.asarray(v_scale[b, h], dtype=np.float64)
                 svp = np.concatenate([sv, np.zeros(pad)]).reshape(nt, P_TILE)
                 sigma = svp.max(axis=1, keepdims=True)
-                w = np.where(svp > 0, svp / sigma, 1.0)
+                w = np.where(svp > 0, svp / np.where(sigma > 0, sigma, 1.0), 1.0)
                 sv32 = svp.astype(np.float32)
-                ratio32 = (sv32 / sv32.max(axis=1, keepdims=True)).astype(np.float32)
-                w_dec = np.where(svp > 0, (np.float32(448.0) * ratio32).astype(np.float32), 448.0)
+                s32 = sv32.max(axis=1, keepdims=True)
+                ratio32 = (sv32 / np.where(s32 > 0, s32, np.float32(1.0))).astype(np.float32)
+                w_dec = np.where(svp > 0, (np.float32(qmax) * ratio32).astype(np.float32), qmax)
                 w_dec = w_dec.astype(np.float64)
             for c0 in range(0, rows.size, chunk):
                 r = rows[c0:c0 + chunk]

@@ -41,6 +41,7 @@ E4M3_VALUES = np.array([_e4m3_decode_code(c) for c in range(256)], dtype=np.floa
 # Non-negative finite codes 0x00..0x7E are increasing in value.
 _E4M3_POS = E4M3_VALUES[:0x7F].copy()
 E4M3_MAX = float(_E4M3_POS[-1])  # 448.0
+E4M3_EMAX = 8  # exponent of the largest normal (448 = 1.75 * 2^8)
 
 
 def _nearest_code(a: np.ndarray, grid: np.ndarray) -> np.ndarray:

@@ -77,6 +77,16 @@ def quantize_int8_per_head(x, scale) -> np.ndarray:
     return F.int8_encode(_div32(x, s))
 
 
+def quantize_fp8_per_head(x, scale) -> np.ndarray:
+    """FA PerHead, FP8 variant ("FA 量化" page, 该类下的模式清单: per-head
+    static INT8/FP8; "量化模式" page, 模式索引 / FA 量化, FP8 per-head static):
+    code = E4M3(fl32(x / scale[h])), saturating at +-448 for inputs beyond
+    the calibrated range.  uint8 E4M3 bit patterns [B,H,S,D]."""
+    x = _as_f32(x)
+    s = _as_f32(scale).reshape(1, -1, 1, 1)
+    return F.e4m3_encode(_div32(x, s))
+
+
 def dequantize_per_head(codes, scale, decode=None) -> np.ndarray:
     vals = codes.astype(np.float64) if decode is None else decode(codes)
     return vals * _as_f32(scale).astype(np.float64).reshape(1, -1, 1, 1)
@@ -99,7 +109,10 @@ def quantize_fp8_per_token(x):
 
 
 def quantize_int8_per_token(x):
-    """INT8 per-token dynamic (FA PerToken, INT8 variant): s = fl32(amax/127)."""
+    """FA PerToken, INT8 variant ("FA 量化" page, 该类下的模式清单: per-token
+    dynamic INT8/FP8): per (b,h,s) row s = fl32(amax / 127) and
+    code = clip(rne(fl32(x / s)), -128, 127).  Returns (codes int8 [B,H,S,D],
+    scales float32 [B,H,S])."""
     x = _as_f32(x)
     amax = np.abs(x).max(axis=3)
     s = _scale_from_amax(amax, QMAX_INT8)
@@ -117,12 +130,14 @@ def dequantize_per_token(codes, scales, decode) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-def mx_shared_exponent(amax) -> np.ndarray:
-    """E = clamp(floor(log2 amax) - 2, -127, 127), read exactly from the
-    binary exponent of amax; amax == 0 gives -127."""
+def mx_shared_exponent(amax, emax=F.E2M1_EMAX) -> np.ndarray:
+    """E = clamp(floor(log2 amax) - emax, -127, 127), read exactly from the
+    binary exponent of amax; amax == 0 gives -127.  emax is the exponent of
+    the element format's largest normal: 2 for E2M1 (max 6 = 1.5 * 2^2),
+    8 for E4M3 (max 448 = 1.75 * 2^8)."""
     amax = np.asarray(amax, dtype=np.float64)
     _, e = np.frexp(amax)  # amax = m * 2^e, 0.5 <= m < 1  =>  floor(log2) = e - 1
-    E = (e - 1) - F.E2M1_EMAX
+    E = (e - 1) - emax
     E = np.where(amax == 0, -127, E)
     return np.clip(E, -127, 127).astype(np.int64)
 
@@ -140,6 +155,34 @@ def quantize_mxfp4(x):
     codes = F.e2m1_encode(v).reshape(B, H, S, D)
     packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
     return packed, (E + 127).astype(np.uint8)
+
+
+def quantize_mxfp8(x):
+    """FA PerBlock, MXFP8 variant ("FA 量化" page, 该类下的模式清单: block
+    shared-exponent MXFP8/MXFP4; "量化模式" page, 模式索引 / FA 量化): the
+    组合 3 structure - 32 consecutive elements along head_dim share one E8M0
+    exponent - with E4M3 elements, whose largest normal exponent is 8 (max
+    448): E = clamp(floor(log2 amax) - 8, -127, 127), element =
+    E4M3(x * 2^-E) with ties to even, saturating at 448 (block values in
+    (448, 512) * 2^E).  Returns (codes uint8 [B,H,S,D] E4M3 bit patterns,
+    E8M0 bytes uint8 [B,H,S,D/32])."""
+    x = _as_f32(x)
+    B, H, S, D = x.shape
+    if D % MX_BLOCK:
+        raise ValueError("head_dim must be a multiple of 32 for MXFP8")
+    blk = x.reshape(B, H, S, D // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    E = mx_shared_exponent(np.abs(blk).max(axis=4), emax=F.E4M3_EMAX)
+    v = np.ldexp(blk, -E[..., None])  # exact power-of-two scaling
+    codes = F.e4m3_encode(v).reshape(B, H, S, D)
+    return codes, (E + 127).astype(np.uint8)
+
+
+def dequantize_mxfp8(codes, e8m0) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    B, H, S, D = codes.shape
+    vals = F.e4m3_decode(codes).reshape(B, H, S, D // MX_BLOCK, MX_BLOCK)
+    scale = F.e8m0_decode(e8m0)[..., None]
+    return (vals * scale).reshape(B, H, S, D)
 
 
 def unpack_fp4(packed) -> np.ndarray:

@@ -23,6 +23,11 @@ Workloads (BNSD shapes):
      (head, channel) pairs x30; one seeded orthogonal R (QR of a Gaussian,
      signs fixed by diag(R_qr)) in bf16 used as both q_rot and k_rot;
      Q block 128, K/V block 256; non-causal.
+The sibling modes of the FA mode list run on the recipe and shape of the
+workload of their own family:
+  6  FP8 per-head static: as 2 (calibration batch, outliers, causal).
+  7  INT8 per-token dynamic: as 3 (log-normal row magnitudes).
+  8  MXFP8 per-block dynamic: as 4 (Student-t(4)).
 """
 
 from dataclasses import dataclass, field
@@ -32,18 +37,25 @@ import numpy as np
 import torch
 
 CONFIGS: Dict[int, dict] = {
-    1: dict(name="int8_per_head_tiny", mode="int8_head", dtype="f32",
+    1: dict(name="int8_per_head_tiny", mode="int8_head", dtype="f32", dist="normal",
             shape=(1, 2, 128, 64), causal=False, calib="self"),
-    2: dict(name="int8_per_head_prefill", mode="int8_head", dtype="bf16",
+    2: dict(name="int8_per_head_prefill", mode="int8_head", dtype="bf16", dist="normal",
             shape=(2, 32, 4096, 128), causal=True, calib="batch",
             calib_batch=4, outlier_frac=0.005, outlier_gain=20.0),
-    3: dict(name="fp8_per_token_video_dit", mode="fp8_token", dtype="bf16",
+    3: dict(name="fp8_per_token_video_dit", mode="fp8_token", dtype="bf16", dist="lognormal_rows",
             shape=(1, 40, 32760, 128), causal=False),
-    4: dict(name="mxfp4_per_block_image_edit", mode="mxfp4", dtype="bf16",
+    4: dict(name="mxfp4_per_block_image_edit", mode="mxfp4", dtype="bf16", dist="t4",
             shape=(1, 24, 8192, 128), causal=False),
-    5: dict(name="rotate_fp8_block", mode="rot_fp8_block", dtype="bf16",
+    5: dict(name="rotate_fp8_block", mode="rot_fp8_block", dtype="bf16", dist="normal",
             shape=(2, 24, 16384, 128), causal=False, outlier_frac=0.01,
             outlier_gain=30.0, q_block=128, kv_block=256),
+    6: dict(name="fp8_per_head_prefill", mode="fp8_head", dtype="bf16", dist="normal",
+            shape=(2, 32, 4096, 128), causal=True, calib="batch",
+            calib_batch=4, outlier_frac=0.005, outlier_gain=20.0),
+    7: dict(name="int8_per_token_video_dit", mode="int8_token", dtype="bf16", dist="lognormal_rows",
+            shape=(1, 40, 32760, 128), causal=False),
+    8: dict(name="mxfp8_per_block_image_edit", mode="mxfp8", dtype="bf16", dist="t4",
+            shape=(1, 24, 8192, 128), causal=False),
 }
 
 TID_Q, TID_K, TID_V = 0, 1, 2
@@ -68,10 +80,10 @@ def outlier_pairs(cfg: int, branch: int, H: int, D: int, frac: float) -> np.ndar
 
 def _draw(cfg: int, tid: int, shape, spec: dict, branch: int) -> np.ndarray:
     g = rng(cfg, tid)
-    mode = spec["mode"]
-    if mode == "mxfp4":
+    dist = spec["dist"]
+    if dist == "t4":
         x = g.standard_t(4.0, size=shape).astype(np.float32)
-    elif mode == "fp8_token":
+    elif dist == "lognormal_rows":
         z = g.standard_normal(shape, dtype=np.float32)
         lg = g.standard_normal(shape[:3], dtype=np.float32)
         x = z * np.exp(np.float32(0.5) * lg)[..., None]
@@ -110,7 +122,7 @@ class Workload:
 
 
 def make_inputs(cfg: int, shape=None, calib_batch=None) -> Workload:
-    """CPU tensors for workload `cfg` (1..5).  `shape` overrides the BNSD
+    """CPU tensors for workload `cfg` (1..8).  `shape` overrides the BNSD
     shape with the same recipe (smaller test cases); `calib_batch` overrides
     the calibration batch size of workload 2."""
     spec = dict(CONFIGS[cfg])

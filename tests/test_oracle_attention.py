@@ -77,7 +77,30 @@ def test_two_key_hand_worked_mxfp4():
     assert o[2] == pytest.approx(0.375 / den, abs=1e-15)
 
 
-@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4"])
+def test_two_key_hand_worked_int8_per_key_v_scale():
+    # V scales (1, 0.5): sigma = 1, w1 = 0.5: 127 * 0.5 * e^-1 = 23.36 -> 23;
+    # Pq1 = 23 / 63.5, v1 = 0.5 (code 1 times its scale)
+    vs = np.array([[[1.0, 0.5]]])
+    o, _ = _two_key("int8", vs)
+    den = 1 + math.exp(-1)
+    assert o[1] == pytest.approx(1 / den, abs=1e-15)
+    assert o[2] == pytest.approx((23 / 63.5) * 0.5 / den, abs=1e-15)
+    # one V scale for the tile: the per-head rule (no scale given)
+    o1, _ = _two_key("int8", np.full((1, 1, 2), 0.37))
+    o0, _ = _two_key("int8")
+    assert np.array_equal(o1[:2], o0[:2])
+
+
+def test_two_key_hand_worked_mxfp8():
+    # group amax 1 -> E = floor(log2 1) - 8 = -8; p * 256 = (256, 94.18):
+    # 94.18 lies in [64, 128) where E4M3 steps by 8 -> 96; Pq = (1, 0.375)
+    o, _ = _two_key("mxfp8")
+    den = 1 + math.exp(-1)
+    assert o[1] == pytest.approx(1 / den, abs=1e-15)
+    assert o[2] == pytest.approx(0.375 / den, abs=1e-15)
+
+
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8"])
 def test_equal_scores_give_mean_of_v(rule):
     g = np.random.default_rng(2)
     S, D = 300, 64
@@ -89,7 +112,7 @@ def test_equal_scores_give_mean_of_v(rule):
     assert np.allclose(o, v.mean(axis=2, keepdims=True), atol=1e-13)
 
 
-@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "exact"])
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8", "exact"])
 def test_dominant_key(rule):
     g = np.random.default_rng(3)
     S, D = 260, 64
@@ -100,7 +123,7 @@ def test_dominant_key(rule):
     assert np.allclose(o[0, 0, 0], v[0, 0, 200], atol=1e-13)
 
 
-@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8"])
 def test_tile_local_max(rule):
     """Tile 0: one key with a large score; tile 1: 128 keys of one lower
     score.  With each tile's probabilities taken relative to its own max the
@@ -120,21 +143,22 @@ def test_tile_local_max(rule):
     assert np.allclose(o, ref, atol=1e-12)
 
 
-def test_fp8_sigma_is_per_tile():
+@pytest.mark.parametrize("rule", ["fp8", "int8"])
+def test_sigma_is_per_tile(rule):
     """Equal scores, V scale 1 in tile 0 and 0.3 in tile 1: sigma per tile
     makes w = 1 everywhere and P exact (O = mean v); a global sigma would
-    quantize 448*0.3 = 134.4 -> 128 in tile 1."""
+    quantize 448*0.3 = 134.4 -> 128 (127*0.3 = 38.1 -> 38) in tile 1."""
     g = np.random.default_rng(5)
     D = 64
     q = np.zeros((1, 1, 1, D))
     k = g.standard_normal((1, 1, 256, D))
     v = g.standard_normal((1, 1, 256, D))
     vs = np.concatenate([np.ones(128), np.full(128, 0.3)]).reshape(1, 1, 256)
-    o = A.attention(q, k, v, "fp8", v_scale=vs)
+    o = A.attention(q, k, v, rule, v_scale=vs)
     assert np.allclose(o[0, 0, 0], v[0, 0].mean(axis=0), atol=1e-13)
 
 
-@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4"])
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8"])
 def test_tile_order_invariance(rule):
     g = np.random.default_rng(6)
     S, D = 512, 64
@@ -152,7 +176,7 @@ def test_quantized_close_to_exact():
     g = np.random.default_rng(7)
     q, k, v = (g.standard_normal((1, 2, 256, 64)) for _ in range(3))
     ref = A.attention(q, k, v, "exact")
-    for rule, tol in [("int8", 0.05), ("fp8", 0.06), ("mxfp4", 0.25)]:
+    for rule, tol in [("int8", 0.05), ("fp8", 0.06), ("mxfp4", 0.25), ("mxfp8", 0.06)]:
         o = A.attention(q, k, v, rule, v_scale=np.ones((1, 2, 256)))
         err = np.linalg.norm(o - ref) / np.linalg.norm(ref)
         assert 1e-4 < err < tol, (rule, err)

@@ -217,3 +217,109 @@ def test_correctly_rounded_divide_at_ties():
             row[0, 0, 0, 1] = float(x)
             codes, s = Q.quantize_fp8_per_token(row)
             assert int(codes.ravel()[1]) == int(want, 16), (x, hex(codes.ravel()[1]))
+
+
+# ---- sibling FA modes: FP8 per-head static, INT8 per-token dynamic, MXFP8
+
+
+def test_fp8_per_head_calibrated_max_and_saturation():
+    g = np.random.default_rng(14)
+    x = g.standard_normal((2, 3, 16, 64)).astype(np.float32)
+    s = Q.fp8_scales(Q.calibrate_amax(x))
+    c = Q.quantize_fp8_per_head(x, s)
+    # the calibrated maximum of every head encodes to +-448 exactly
+    for h in range(3):
+        top = c[:, h].ravel()[np.abs(x[:, h]).argmax()]
+        assert top in (0x7E, 0xFE)
+    # symmetric: negation flips only the sign bit
+    assert np.array_equal(Q.quantize_fp8_per_head(-x, s), c ^ 0x80)
+    # beyond the calibrated range codes saturate at 448 (no NaN code)
+    big = np.full((1, 3, 1, 64), 1e6, np.float32)
+    assert np.all(Q.quantize_fp8_per_head(big, s) == 0x7E)
+    assert np.all(Q.quantize_fp8_per_head(-big, s) == 0xFE)
+
+
+def test_fp8_per_head_brute_force_tiny():
+    g = np.random.default_rng(15)
+    x = (g.standard_normal((1, 2, 3, 32)) * 4).astype(np.float32)
+    s = np.float32([0.01, 0.003])
+    c = Q.quantize_fp8_per_head(x, s)
+    finite = np.where(np.isfinite(F.E4M3_VALUES))[0]
+    for h in range(2):
+        for v, code in zip(x[0, h].ravel(), c[0, h].ravel()):
+            u = float(np.float32(v) / s[h])
+            u = min(max(u, -448.0), 448.0)
+            d = np.abs(F.E4M3_VALUES[finite] - u)
+            best = finite[d == d.min()]
+            if best.size > 1:
+                best = best[best % 2 == 0]
+            assert code == best[0]
+
+
+def test_int8_per_token_rows():
+    g = np.random.default_rng(16)
+    x = (g.standard_normal((1, 2, 40, 64)) * np.exp(g.standard_normal((1, 2, 40, 1)))).astype(np.float32)
+    x[0, 1, 7] = 0.0
+    codes, s = Q.quantize_int8_per_token(x)
+    assert s.shape == (1, 2, 40) and codes.dtype == np.int8
+    am = np.abs(x).argmax(axis=3)
+    top = np.take_along_axis(codes, am[..., None], axis=3)[..., 0].astype(int)
+    nz = np.abs(x).max(axis=3) > 0
+    assert np.all(np.abs(top[nz]) == 127)  # each row's max maps to +-127
+    assert s[0, 1, 7] == 1.0 and np.all(codes[0, 1, 7] == 0)
+    assert np.array_equal(s[nz], (np.abs(x).max(axis=3)[nz] / np.float32(127)).astype(np.float32))
+    # brute force on a few rows: nearest integer of the fp32 quotient, ties to even
+    for r in range(3):
+        for v, code in zip(x[0, 0, r], codes[0, 0, r]):
+            u = float(np.float32(v) / s[0, 0, r])
+            cands = np.arange(-128, 128)
+            d = np.abs(cands - u)
+            best = cands[d == d.min()]
+            if best.size > 1:
+                best = best[best % 2 == 0]
+            assert int(code) == best[0]
+
+
+def test_mxfp8_hand_worked_block():
+    # amax 3: floor(log2 3) = 1, E = 1 - 8 = -7, x * 2^7:
+    #   1 -> 128 = 2^7 (0x70); 0.5 -> 64 (0x68); -3 -> -384 = -1.5 * 2^8 (0xFC);
+    #   0.001 -> 0.128, nearest E4M3 0.125 = 2^-3 (0x20); 1e-6 -> 1.28e-4 < 2^-10: 0
+    x = np.zeros((1, 1, 1, 32), np.float32)
+    x[0, 0, 0, :5] = [1.0, 0.5, -3.0, 0.001, 1e-6]
+    codes, e8 = Q.quantize_mxfp8(x)
+    assert int(e8.ravel()[0]) == 127 - 7
+    assert list(codes.ravel()[:5]) == [0x70, 0x68, 0xFC, 0x20, 0x00]
+    assert np.all(codes.ravel()[5:] == 0)
+    # amax 1.9375: E = -8, 1.9375 * 256 = 496 lies in (448, 512): saturates to 448
+    x[0, 0, 0, :5] = [1.9375, 0, 0, 0, 0]
+    codes, e8 = Q.quantize_mxfp8(x)
+    assert int(e8.ravel()[0]) == 127 - 8 and int(codes.ravel()[0]) == 0x7E
+
+
+def test_mxfp8_exponent_rule_pins_emax8_max448():
+    g = np.random.default_rng(17)
+    x = (g.standard_t(4, (2, 3, 17, 128)) * np.exp2(g.integers(-20, 20, (2, 3, 17, 1)))).astype(np.float32)
+    codes, e8 = Q.quantize_mxfp8(x)
+    E = e8.astype(np.int64) - 127
+    amax = np.abs(x.reshape(2, 3, 17, 4, 32)).max(axis=4)
+    # amax in [256, 512) * 2^E  (E = floor(log2 amax) - 8, 448 = 1.75 * 2^8)
+    assert np.all(amax >= 256.0 * np.exp2(E)) and np.all(amax < 512.0 * np.exp2(E))
+    deq = Q.dequantize_mxfp8(codes, e8)
+    assert np.all(np.abs(deq).reshape(2, 3, 17, 4, 32).max(axis=4) <= 448.0 * np.exp2(E))
+
+
+def test_mxfp8_elements_match_torch_float8_cast():
+    """torch's float8_e4m3fn cast (an independent implementation) of the
+    exactly scaled block values x * 2^-E, clamped to +-448 first (torch gives
+    NaN from 464 up)."""
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(18)
+    x = (g.standard_t(3, (1, 4, 33, 64)) * np.exp2(g.integers(-30, 30, (1, 4, 33, 1)))).astype(np.float32)
+    x[0, 0, 0, :32] = 0.0
+    codes, e8 = Q.quantize_mxfp8(x)
+    E = e8.astype(np.int64) - 127
+    v = np.ldexp(x.reshape(1, 4, 33, 2, 32).astype(np.float64), -E[..., None])
+    v = np.clip(v, -448.0, 448.0).reshape(x.shape).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    assert list(e8[0, 0, 0]) == [0, e8[0, 0, 0, 1]]  # all-zero block: E = -127
