@@ -52,9 +52,9 @@ typedef enum {
 } faq_status;
 
 /* Quantized data type ("fa3_quant 配置说明" §2.2 QConfig.dtype, the subset the
-   FA combinations use).  FAQ_FLOAT means "not quantized" and is rejected by
-   this version of the library. */
-typedef enum { FAQ_FLOAT = 0, FAQ_INT8 = 1, FAQ_FP8_E4M3 = 2, FAQ_MXFP4 = 3 } faq_dtype;
+   FA modes use: "FA 量化" page, 该类下的模式清单).  FAQ_FLOAT means "not
+   quantized" and is rejected by this version of the library. */
+typedef enum { FAQ_FLOAT = 0, FAQ_INT8 = 1, FAQ_FP8_E4M3 = 2, FAQ_MXFP4 = 3, FAQ_MXFP8 = 4 } faq_dtype;
 
 /* Quantization granularity (QConfig.scope):
    PER_HEAD        one float scale per head, shared over B and S  -> float[H]

@@ -18,7 +18,7 @@ from typing import Dict, Optional
 import torch
 
 from . import _abi
-from ._abi import (FAQ_FP8_E4M3, FAQ_INT8, FAQ_MXFP4, FAQ_FLOAT, FAQ_PER_BLOCK, FAQ_PER_HEAD,
+from ._abi import (FAQ_FP8_E4M3, FAQ_INT8, FAQ_MXFP4, FAQ_MXFP8, FAQ_FLOAT, FAQ_PER_BLOCK, FAQ_PER_HEAD,
                    FAQ_PER_TOKEN, FAQ_PER_TOKEN_BLOCK, FAQ_T_BF16, FAQ_T_F32)
 
 __all__ = [
@@ -28,7 +28,8 @@ __all__ = [
     "fa_quant_codes_bytes", "fa_quant_scales_bytes", "fa_quant_status_string",
 ]
 
-_DTYPES = {"float": FAQ_FLOAT, "int8": FAQ_INT8, "fp8_e4m3": FAQ_FP8_E4M3, "mxfp4": FAQ_MXFP4}
+_DTYPES = {"float": FAQ_FLOAT, "int8": FAQ_INT8, "fp8_e4m3": FAQ_FP8_E4M3, "mxfp4": FAQ_MXFP4,
+           "mxfp8": FAQ_MXFP8}
 _SCOPES = {"per_head": FAQ_PER_HEAD, "per_token": FAQ_PER_TOKEN, "per_block": FAQ_PER_BLOCK,
            "per_token_block": FAQ_PER_TOKEN_BLOCK}
 _METHODS = {"minmax": 0}
@@ -158,8 +159,9 @@ def fa_quantize(x: torch.Tensor, cfg: QConfig, static_scale: torch.Tensor = None
             raise FaQuantError(_abi.FAQ_ERR_UNSUPPORTED, f"fa_quantize: {cfg}")
         cdt = torch.int8 if cfg.dtype == "int8" else torch.uint8
         codes = torch.empty(nc, dtype=cdt, device=x.device)
-        if cfg.dtype == "mxfp4":
-            codes = codes.view(shape[0], shape[1], shape[2], shape[3] // 2)
+        if cfg.dtype in ("mxfp4", "mxfp8"):
+            cd = shape[3] // 2 if cfg.dtype == "mxfp4" else shape[3]
+            codes = codes.view(shape[0], shape[1], shape[2], cd)
             scales = torch.empty(ns, dtype=torch.uint8, device=x.device).view(shape[0], shape[1], shape[2],
                                                                                shape[3] // 32)
         else:

@@ -18,7 +18,7 @@ FAQ_ERR_HIP = -6
 FAQ_ERR_WORKSPACE = -7
 
 # faq_dtype
-FAQ_FLOAT, FAQ_INT8, FAQ_FP8_E4M3, FAQ_MXFP4 = 0, 1, 2, 3
+FAQ_FLOAT, FAQ_INT8, FAQ_FP8_E4M3, FAQ_MXFP4, FAQ_MXFP8 = 0, 1, 2, 3, 4
 # faq_scope
 FAQ_PER_HEAD, FAQ_PER_TOKEN, FAQ_PER_BLOCK, FAQ_PER_TOKEN_BLOCK = 0, 1, 2, 3
 # faq_tdtype

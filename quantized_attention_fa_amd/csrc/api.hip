@@ -47,15 +47,18 @@ bool same_cfg(const faq_qconfig& a, const faq_qconfig& b) {
          a.method == b.method && (a.scope != FAQ_PER_TOKEN_BLOCK || a.block_tokens == b.block_tokens);
 }
 
-// The (dtype, scope) pairs of the FA combinations implemented here.
+// The (dtype, scope) pairs of the FA modes implemented here: per-head
+// static INT8/FP8, per-token dynamic INT8/FP8, per-block MXFP4/MXFP8, and
+// FP8 token blocks of the rotate path.
 faq_status check_cfg(const faq_qconfig* c) {
   if (!c) return FAQ_ERR_INVALID_ARG;
-  if (c->dtype < FAQ_FLOAT || c->dtype > FAQ_MXFP4) return FAQ_ERR_INVALID_ARG;
+  if (c->dtype < FAQ_FLOAT || c->dtype > FAQ_MXFP8) return FAQ_ERR_INVALID_ARG;
   if (c->scope < FAQ_PER_HEAD || c->scope > FAQ_PER_TOKEN_BLOCK) return FAQ_ERR_INVALID_ARG;
   if (c->symmetric != 1 || c->method != 0) return FAQ_ERR_UNSUPPORTED;
-  if (c->dtype == FAQ_INT8 && c->scope == FAQ_PER_HEAD) return FAQ_OK;
-  if (c->dtype == FAQ_FP8_E4M3 && c->scope == FAQ_PER_TOKEN) return FAQ_OK;
-  if (c->dtype == FAQ_MXFP4 && c->scope == FAQ_PER_BLOCK) return FAQ_OK;
+  if ((c->dtype == FAQ_INT8 || c->dtype == FAQ_FP8_E4M3) &&
+      (c->scope == FAQ_PER_HEAD || c->scope == FAQ_PER_TOKEN))
+    return FAQ_OK;
+  if ((c->dtype == FAQ_MXFP4 || c->dtype == FAQ_MXFP8) && c->scope == FAQ_PER_BLOCK) return FAQ_OK;
   if (c->dtype == FAQ_FP8_E4M3 && c->scope == FAQ_PER_TOKEN_BLOCK) {
     if (c->block_tokens == 128 || c->block_tokens == 256) return FAQ_OK;
     return c->block_tokens > 0 ? FAQ_ERR_UNSUPPORTED : FAQ_ERR_INVALID_ARG;
@@ -162,12 +165,15 @@ faq_status fa_quantize(const void* x, int32_t x_dtype, const faq_shape* shape, c
   hipError_t e = hipSuccess;
   switch (cfg->dtype) {
     case FAQ_INT8:
-      e = launch_quant_int8_head(x, x_dtype, *shape, static_scale, (int8_t*)out->codes, st);
-      if (e == hipSuccess && out->scales != static_scale)
-        e = hipMemcpyAsync(out->scales, static_scale, (size_t)shape->H * 4, hipMemcpyDeviceToDevice, st);
+      if (per_head)
+        e = launch_quant_int8_head(x, x_dtype, *shape, static_scale, (int8_t*)out->codes, st);
+      else
+        e = launch_quant_int8_token(x, x_dtype, *shape, (int8_t*)out->codes, (float*)out->scales, st);
       break;
     case FAQ_FP8_E4M3:
-      if (tok_block) {
+      if (per_head) {
+        e = launch_quant_fp8_head(x, x_dtype, *shape, static_scale, (uint8_t*)out->codes, st);
+      } else if (tok_block) {
         if (rot)
           e = launch_rot_fp8_block((const uint16_t*)x, (const uint16_t*)rot, *shape, cfg->block_tokens,
                                    (uint8_t*)out->codes, (float*)out->scales, (uint16_t*)debug_rotated, st);
@@ -178,10 +184,15 @@ faq_status fa_quantize(const void* x, int32_t x_dtype, const faq_shape* shape, c
         e = launch_quant_fp8_token(x, x_dtype, *shape, (uint8_t*)out->codes, (float*)out->scales, st);
       }
       break;
+    case FAQ_MXFP8:
+      e = launch_quant_mxfp8(x, x_dtype, *shape, (uint8_t*)out->codes, (uint8_t*)out->scales, st);
+      break;
     default:
       e = launch_quant_mxfp4(x, x_dtype, *shape, (uint8_t*)out->codes, (uint8_t*)out->scales, st);
       break;
   }
+  if (e == hipSuccess && per_head && out->scales != static_scale)
+    e = hipMemcpyAsync(out->scales, static_scale, (size_t)shape->H * 4, hipMemcpyDeviceToDevice, st);
   return hip_status(e, fn);
 }
 

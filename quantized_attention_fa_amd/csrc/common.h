@@ -101,11 +101,14 @@ FAQ_DEV uint32_t enc_e2m1(float v) {
   return sign | enc_e2m1_mag(fabsf(v));
 }
 
-// Shared MX exponent E = clamp(floor(log2 amax) - 2, -127, 127), exact from
-// the float's exponent bits; zero or subnormal amax gives -127.
+// Shared MX exponent E = clamp(floor(log2 amax) - EMAX, -127, 127), exact
+// from the float's exponent bits; zero or subnormal amax gives -127.  EMAX
+// is the exponent of the element format's largest normal: 2 for E2M1
+// (max 6), 8 for E4M3 (max 448).
+template <int EMAX = 2>
 FAQ_DEV int mx_exponent(float amax) {
   const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-  int E = e - 129;
+  int E = e - 127 - EMAX;
   E = E < -127 ? -127 : E;
   E = E > 127 ? 127 : E;
   return e == 0 ? -127 : E;
@@ -213,6 +216,50 @@ FAQ_DEV void e4m3_code_words(const float* x, float s, uint32_t* w) {
     if (slow) {
 #pragma unroll
       for (int j = 0; j < N / 4; ++j) w[j] = e4m3_code_word<false>(x + 4 * j, s, r);
+    }
+  }
+}
+
+// E4M3 codes of x0 / s .. x3 / s for a static scale, where inputs beyond the
+// calibrated range occur: quotients saturate at +-448 (the hardware
+// conversion is only used within that range).  On the fast path x r is
+// first clamped to +-512 (the correction then stays finite; quotients that
+// large saturate either way).
+template <bool FAST>
+FAQ_DEV uint32_t e4m3_sat_code_word(const float* x, float s, float r) {
+  float q[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float d;
+    if (FAST) {
+      const float q0 = __builtin_amdgcn_fmed3f(x[k] * r, -512.0f, 512.0f);
+      d = __builtin_fmaf(__builtin_fmaf(-q0, s, x[k]), r, q0);
+    } else {
+      d = x[k] / s;
+    }
+    q[k] = with_sign_of(__builtin_amdgcn_fmed3f(d, -448.0f, 448.0f), x[k]);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+  return (uint32_t)w;
+}
+
+// N / 4 words of INT8 codes of x[0..N) / s (x0 in byte 0 of word 0), with
+// the same wave-uniform fallback to IEEE division as e4m3_code_words.
+template <int N>
+FAQ_DEV void int8_code_words(const float* x, float s, uint32_t* w) {
+  const float r = 1.0f / s;
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j)
+    w[j] = pack_low_bytes(int8_code_word<true>(x[4 * j], s, r), int8_code_word<true>(x[4 * j + 1], s, r),
+                          int8_code_word<true>(x[4 * j + 2], s, r), int8_code_word<true>(x[4 * j + 3], s, r));
+  const bool slow = !div_fast_ok(s);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(slow) != 0, 0)) {
+    if (slow) {
+#pragma unroll
+      for (int j = 0; j < N / 4; ++j)
+        w[j] = pack_low_bytes(int8_code_word<false>(x[4 * j], s, r), int8_code_word<false>(x[4 * j + 1], s, r),
+                              int8_code_word<false>(x[4 * j + 2], s, r), int8_code_word<false>(x[4 * j + 3], s, r));
     }
   }
 }

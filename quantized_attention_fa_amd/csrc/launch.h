@@ -17,6 +17,12 @@ hipError_t launch_quant_int8_head(const void* x, int x_dtype, const faq_shape& s
                                   const float* scale, int8_t* codes, hipStream_t st);
 hipError_t launch_quant_fp8_token(const void* x, int x_dtype, const faq_shape& s,
                                   uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_fp8_head(const void* x, int x_dtype, const faq_shape& s,
+                                 const float* scale, uint8_t* codes, hipStream_t st);
+hipError_t launch_quant_int8_token(const void* x, int x_dtype, const faq_shape& s,
+                                   int8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_mxfp8(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
+                              uint8_t* e8m0, hipStream_t st);
 hipError_t launch_quant_mxfp4(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
                               uint8_t* e8m0, hipStream_t st);
 hipError_t launch_quant_fp8_block(const uint16_t* x, const faq_shape& s, int block_tokens,

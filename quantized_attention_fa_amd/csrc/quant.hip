@@ -66,11 +66,12 @@ __global__ void k_scales_from_amax(const float* amax, int64_t H, float qmax, flo
 }
 
 // ------------------------------------------------------------------------
-// INT8 per-head static: code = clamp(rne(x / scale[h]), -128, 127).
+// Per-head static: INT8 code = clamp(rne(x / scale[h]), -128, 127); FP8
+// code = E4M3(x / scale[h]) saturating at +-448 (FA PerHead, INT8 / FP8).
 // grid = (chunks per (b,h) slice, B*H); 16 elements per thread-vector.
 // ------------------------------------------------------------------------
-template <bool FAST, typename T>
-FAQ_DEV void int8_head_slice(const T* __restrict__ src, int8_t* __restrict__ dst, int64_t per_bh, float s) {
+template <bool FAST, bool FP8, typename T>
+FAQ_DEV void head_slice(const T* __restrict__ src, uint8_t* __restrict__ dst, int64_t per_bh, float s) {
   constexpr int U = 2;
   const float r = 1.0f / s;
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads * 16 * U; c0 < per_bh;
@@ -94,10 +95,14 @@ FAQ_DEV void int8_head_slice(const T* __restrict__ src, int8_t* __restrict__ dst
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          uint32_t c[4];
+          if (FP8) {
+            w[j] = e4m3_sat_code_word<FAST>(v[u] + 4 * j, s, r);
+          } else {
+            uint32_t c[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) c[k] = int8_code_word<FAST>(v[u][4 * j + k], s, r);
-          w[j] = pack_low_bytes(c[0], c[1], c[2], c[3]);
+            for (int k = 0; k < 4; ++k) c[k] = int8_code_word<FAST>(v[u][4 * j + k], s, r);
+            w[j] = pack_low_bytes(c[0], c[1], c[2], c[3]);
+          }
         }
         *reinterpret_cast<uint4*>(dst + i) = make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -105,26 +110,27 @@ FAQ_DEV void int8_head_slice(const T* __restrict__ src, int8_t* __restrict__ dst
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_quant_int8_head(const T* __restrict__ x,
-                                                              const float* __restrict__ scale,
-                                                              int64_t per_bh, int H,
-                                                              int8_t* __restrict__ codes) {
+template <typename T, bool FP8>
+__global__ __launch_bounds__(kThreads) void k_quant_head(const T* __restrict__ x,
+                                                         const float* __restrict__ scale,
+                                                         int64_t per_bh, int H,
+                                                         uint8_t* __restrict__ codes) {
   const int64_t bh = blockIdx.y;
   const float s = scale[bh % H];
   // the head's scale picks the division path once for the whole slice
-  if (div_fast_ok(s)) int8_head_slice<true>(x + bh * per_bh, codes + bh * per_bh, per_bh, s);
-  else int8_head_slice<false>(x + bh * per_bh, codes + bh * per_bh, per_bh, s);
+  if (div_fast_ok(s)) head_slice<true, FP8>(x + bh * per_bh, codes + bh * per_bh, per_bh, s);
+  else head_slice<false, FP8>(x + bh * per_bh, codes + bh * per_bh, per_bh, s);
 }
 
 // ------------------------------------------------------------------------
-// FP8 E4M3 per-token: one scale per (b,h,s) row of D elements.
+// Per-token dynamic: one scale per (b,h,s) row of D elements, FP8 E4M3
+// (s = amax / 448) or INT8 (s = amax / 127) (FA PerToken, FP8 / INT8).
 // D/16 threads per row, 16 elements per thread.
 // ------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void k_quant_fp8_token(const T* __restrict__ x, int64_t rows,
-                                                              uint8_t* __restrict__ codes,
-                                                              float* __restrict__ scales) {
+template <typename T, int D, bool I8>
+__global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ x, int64_t rows,
+                                                          uint8_t* __restrict__ codes,
+                                                          float* __restrict__ scales) {
   constexpr int EPT = 16, TPR = D / EPT, RPB = kThreads / TPR, U = 2;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
   for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
@@ -150,9 +156,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_token(const T* __restric
 #pragma unroll
       for (int k = 0; k < EPT; ++k) m = fmaxf(m, fabsf(v[u][k]));
       m = group_max<TPR>(m);
-      const float s = scale_from_amax(m, 448.0f);
+      const float s = scale_from_amax(m, I8 ? 127.0f : 448.0f);
       uint32_t w[4];
-      e4m3_code_words<EPT>(v[u], s, w);
+      if (I8) int8_code_words<EPT>(v[u], s, w);
+      else e4m3_code_words<EPT>(v[u], s, w);
       if (row < rows) {
         *reinterpret_cast<uint4*>(codes + row * D + sub * EPT) = make_uint4(w[0], w[1], w[2], w[3]);
         if (sub == 0) scales[row] = s;
@@ -217,6 +224,64 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
       for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
       if (row < rows) {
         *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + sub * 4) = packed;
+        if (sub == 0) {
+          if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + row * NB) = word;
+          else *reinterpret_cast<uint16_t*>(e8m0 + row * NB) = (uint16_t)word;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// MXFP8 per-block: 32 consecutive elements along D share an E8M0 exponent
+// E = floor(log2 amax) - 8; elements are E4M3 of x / 2^E (exact scaling),
+// saturating at 448 (FA PerBlock, MXFP8).  D/8 threads per row, 4 per block.
+// ------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ x, int64_t rows,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ e8m0) {
+  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 4, NB = D / 32;
+  const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
+  const int lane = threadIdx.x & 63;
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = r0 + u * RPB + rin;
+      if (row < rows) {
+        load8(x + row * D + sub * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = r0 + u * RPB + rin;
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
+      m = group_max<4>(m);
+      const int E = mx_exponent<8>(m);
+      // x / 2^E is exact wherever it can reach a nonzero code; the block
+      // maximum lies in [256, 512) and saturates above 448
+      float q[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        q[k] = with_sign_of(__builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(v[u][k], -E), -448.0f, 448.0f), v[u][k]);
+      int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
+      int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
+      // gather the row's NB exponent bytes into the row's first lane
+      uint32_t eb = (uint32_t)(E + 127);
+      uint32_t word = eb;
+#pragma unroll
+      for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
+      if (row < rows) {
+        *reinterpret_cast<uint2*>(codes + row * D + sub * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
         if (sub == 0) {
           if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + row * NB) = word;
           else *reinterpret_cast<uint16_t*>(e8m0 + row * NB) = (uint16_t)word;
@@ -413,36 +478,53 @@ hipError_t launch_scales_from_amax(const float* amax, int64_t H, float qmax, flo
   return hipGetLastError();
 }
 
-hipError_t launch_quant_int8_head(const void* x, int x_dtype, const faq_shape& s,
-                                  const float* scale, int8_t* codes, hipStream_t st) {
+template <bool FP8>
+static hipError_t head_q(const void* x, int x_dtype, const faq_shape& s, const float* scale,
+                         uint8_t* codes, hipStream_t st) {
   const int64_t per_bh = s.S * s.D;
   dim3 grid(grid_chunks(per_bh, kThreads * 16 * 2, 65535), (unsigned)(s.B * s.H));
   if (x_dtype == FAQ_T_BF16)
-    k_quant_int8_head<uint16_t><<<grid, kThreads, 0, st>>>((const uint16_t*)x, scale, per_bh,
-                                                           (int)s.H, codes);
+    k_quant_head<uint16_t, FP8><<<grid, kThreads, 0, st>>>((const uint16_t*)x, scale, per_bh, (int)s.H, codes);
   else
-    k_quant_int8_head<float><<<grid, kThreads, 0, st>>>((const float*)x, scale, per_bh, (int)s.H,
-                                                        codes);
+    k_quant_head<float, FP8><<<grid, kThreads, 0, st>>>((const float*)x, scale, per_bh, (int)s.H, codes);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t fp8_token_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
-                              float* scales, hipStream_t st) {
+hipError_t launch_quant_int8_head(const void* x, int x_dtype, const faq_shape& s,
+                                  const float* scale, int8_t* codes, hipStream_t st) {
+  return head_q<false>(x, x_dtype, s, scale, reinterpret_cast<uint8_t*>(codes), st);
+}
+
+hipError_t launch_quant_fp8_head(const void* x, int x_dtype, const faq_shape& s,
+                                 const float* scale, uint8_t* codes, hipStream_t st) {
+  return head_q<true>(x, x_dtype, s, scale, codes, st);
+}
+
+template <int D, bool I8>
+static hipError_t token_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
+                          float* scales, hipStream_t st) {
   constexpr int RPB = kThreads / (D / 16);
   const unsigned grid = grid_chunks(rows, RPB * 2, 1u << 20);
   if (x_dtype == FAQ_T_BF16)
-    k_quant_fp8_token<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, scales);
+    k_quant_token<uint16_t, D, I8><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, scales);
   else
-    k_quant_fp8_token<float, D><<<grid, kThreads, 0, st>>>((const float*)x, rows, codes, scales);
+    k_quant_token<float, D, I8><<<grid, kThreads, 0, st>>>((const float*)x, rows, codes, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_fp8_token(const void* x, int x_dtype, const faq_shape& s,
                                   uint8_t* codes, float* scales, hipStream_t st) {
   const int64_t rows = s.B * s.H * s.S;
-  return s.D == 128 ? fp8_token_d<128>(x, x_dtype, rows, codes, scales, st)
-                    : fp8_token_d<64>(x, x_dtype, rows, codes, scales, st);
+  return s.D == 128 ? token_d<128, false>(x, x_dtype, rows, codes, scales, st)
+                    : token_d<64, false>(x, x_dtype, rows, codes, scales, st);
+}
+
+hipError_t launch_quant_int8_token(const void* x, int x_dtype, const faq_shape& s,
+                                   int8_t* codes, float* scales, hipStream_t st) {
+  const int64_t rows = s.B * s.H * s.S;
+  uint8_t* c = reinterpret_cast<uint8_t*>(codes);
+  return s.D == 128 ? token_d<128, true>(x, x_dtype, rows, c, scales, st)
+                    : token_d<64, true>(x, x_dtype, rows, c, scales, st);
 }
 
 template <int D>
@@ -462,6 +544,25 @@ hipError_t launch_quant_mxfp4(const void* x, int x_dtype, const faq_shape& s, ui
   const int64_t rows = s.B * s.H * s.S;
   return s.D == 128 ? mxfp4_d<128>(x, x_dtype, rows, codes, e8m0, st)
                     : mxfp4_d<64>(x, x_dtype, rows, codes, e8m0, st);
+}
+
+template <int D>
+static hipError_t mxfp8_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
+                          uint8_t* e8m0, hipStream_t st) {
+  constexpr int RPB = kThreads / (D / 8);
+  const unsigned grid = grid_chunks(rows, RPB * 4, 1u << 20);
+  if (x_dtype == FAQ_T_BF16)
+    k_quant_mxfp8<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, e8m0);
+  else
+    k_quant_mxfp8<float, D><<<grid, kThreads, 0, st>>>((const float*)x, rows, codes, e8m0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mxfp8(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
+                              uint8_t* e8m0, hipStream_t st) {
+  const int64_t rows = s.B * s.H * s.S;
+  return s.D == 128 ? mxfp8_d<128>(x, x_dtype, rows, codes, e8m0, st)
+                    : mxfp8_d<64>(x, x_dtype, rows, codes, e8m0, st);
 }
 
 template <int D, int BT>

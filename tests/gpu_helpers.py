@@ -19,8 +19,13 @@ MODE_CFG = {
     "mxfp4": lambda spec, br: faq.QConfig("mxfp4", "per_block"),
     "rot_fp8_block": lambda spec, br: faq.QConfig(
         "fp8_e4m3", "per_token_block", block_tokens=spec["q_block"] if br == 0 else spec["kv_block"]),
+    "fp8_head": lambda spec, br: faq.QConfig("fp8_e4m3", "per_head"),
+    "int8_token": lambda spec, br: faq.QConfig("int8", "per_token"),
+    "mxfp8": lambda spec, br: faq.QConfig("mxfp8", "per_block"),
 }
-P_RULE = {"int8_head": "int8", "fp8_token": "fp8", "mxfp4": "mxfp4", "rot_fp8_block": "fp8"}
+P_RULE = {"int8_head": "int8", "fp8_token": "fp8", "mxfp4": "mxfp4", "rot_fp8_block": "fp8",
+          "fp8_head": "fp8", "int8_token": "int8", "mxfp8": "mxfp8"}
+STATIC_DTYPE = {"int8_head": "int8", "fp8_head": "fp8_e4m3"}
 
 
 class GpuRun:
@@ -33,13 +38,13 @@ class GpuRun:
         self.x = [t.to(DEV) for t in (w.q, w.k, w.v)]
         self.static = [None, None, None]
         self.amax = [None, None, None]
-        if mode == "int8_head":
+        if mode in STATIC_DTYPE:
             for br in range(3):
                 amax = torch.zeros(w.shape[1], dtype=torch.float32, device=DEV)
                 for c in w.calib[br]:
                     faq.fa_quant_calibrate(c.to(DEV), amax)
                 self.amax[br] = amax
-                self.static[br] = faq.fa_quant_scales_from_amax(amax, "int8")
+                self.static[br] = faq.fa_quant_scales_from_amax(amax, STATIC_DTYPE[mode])
         self.rot = w.rot.to(DEV) if w.rot is not None else None
         self.rotated = [None, None, None]
         self.qt = []
@@ -76,11 +81,18 @@ def dequant(run: GpuRun, br: int):
     B, H, S, D = run.w.shape
     if mode == "int8_head":
         return OQ.dequantize_per_head(c, s), np.broadcast_to(s.reshape(1, H, 1), (B, H, S))
+    if mode == "fp8_head":
+        return OQ.dequantize_per_head(c, s, F.e4m3_decode), np.broadcast_to(s.reshape(1, H, 1), (B, H, S))
     if mode == "fp8_token":
         s = s.reshape(B, H, S)
         return OQ.dequantize_per_token(c, s, F.e4m3_decode), s
+    if mode == "int8_token":
+        s = s.reshape(B, H, S)
+        return OQ.dequantize_per_token(c, s, lambda a: a.astype(np.float64)), s
     if mode == "mxfp4":
         return OQ.dequantize_mxfp4(c, s), None
+    if mode == "mxfp8":
+        return OQ.dequantize_mxfp8(c, s), None
     bt = run.qt[br].cfg.block_tokens
     st = OQ.block_scales_per_token(s.reshape(B, H, -1), bt, S)
     return OQ.dequantize_per_token(c, st, F.e4m3_decode), st

@@ -214,6 +214,111 @@ def test_rotate_block_small(bt, S, D):
     assert np.array_equal(qt.codes.cpu().numpy(), codes)
 
 
+# ---------------------------------------------------------------- sibling modes
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 2, 128, 64), torch.float32), ((2, 3, 300, 128), torch.bfloat16),
+                                         ((1, 4, 77, 64), torch.bfloat16)])
+def test_fp8_per_head_small(shape, dtype):
+    g = np.random.default_rng(sum(shape) + 3)
+    x = (g.standard_normal(shape) * np.exp(g.standard_normal((1, shape[1], 1, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).to(dtype)
+    xn = _np(xt)
+    amax = torch.zeros(shape[1], dtype=torch.float32, device=DEV)
+    faq.fa_quant_calibrate(xt.to(DEV), amax)
+    ref_amax = OQ.calibrate_amax(xn)
+    sc = faq.fa_quant_scales_from_amax(amax, "fp8_e4m3")
+    assert np.array_equal(sc.cpu().numpy(), OQ.fp8_scales(ref_amax))
+    # scales tighter than the data: values beyond the calibrated range saturate
+    for f in (1.0, 0.7):
+        s2 = sc * f
+        qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("fp8_e4m3", "per_head"), static_scale=s2)
+        assert np.array_equal(qt.codes.cpu().numpy(), OQ.quantize_fp8_per_head(xn, s2.cpu().numpy()))
+        assert np.array_equal(qt.scales.cpu().numpy(), s2.cpu().numpy())
+
+
+def test_fp8_per_head_at_the_extremes():
+    """Scales outside the fast division's range, inputs far beyond the scale
+    (saturate at 448, never NaN), subnormals and signed zeros."""
+    g = np.random.default_rng(13)
+    x = (g.standard_normal((1, 6, 40, 64)) * 3).astype(np.float32)
+    x[0, :, 0, :8] = [1e30, -1e30, 3e38, -3e38, 1e-40, -1e-40, 0.0, -0.0]
+    x[0, 1] *= 2.0 ** -95
+    x[0, 2] *= 2.0 ** 95
+    x[0, 3] *= 2.0 ** -120
+    sc = np.array([0.02, 2.0 ** -96, 2.0 ** 93, 2.0 ** -126, 1e-3, 7.0], np.float32)
+    for dtype in (torch.float32, torch.bfloat16):
+        xt = torch.from_numpy(x).to(dtype)
+        xn = _np(xt)
+        qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("fp8_e4m3", "per_head"), static_scale=torch.from_numpy(sc).to(DEV))
+        assert np.array_equal(qt.codes.cpu().numpy(), OQ.quantize_fp8_per_head(xn, sc))
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 2, 128, 64), torch.float32), ((2, 3, 300, 128), torch.bfloat16),
+                                         ((1, 1, 1000, 128), torch.bfloat16)])
+def test_int8_per_token_small(shape, dtype):
+    g = np.random.default_rng(sum(shape) + 4)
+    x = (g.standard_normal(shape) * np.exp(2 * g.standard_normal(shape[:3] + (1,)))).astype(np.float32)
+    x[..., 0, :] = 0.0
+    x[..., 1, :] = -1e-6
+    x[..., 1, 0] = 1.0
+    xt = torch.from_numpy(x).to(dtype)
+    xn = _np(xt)
+    qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("int8", "per_token"))
+    codes, s = OQ.quantize_int8_per_token(xn)
+    assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
+    assert np.array_equal(qt.codes.cpu().numpy(), codes)
+
+
+def test_int8_per_token_rows_at_the_extremes():
+    g = np.random.default_rng(14)
+    x = g.standard_normal((1, 2, 64, 128)).astype(np.float32)
+    x[0, 0, 0] *= 1e-30
+    x[0, 0, 1] *= 1e30
+    x[0, 0, 2] *= 1e-39
+    x[0, 0, 3, :4] = [0.0, -0.0, -1e-20, 1.0]
+    x[0, 0, 4] = -0.0
+    x[0, 1, 5, :3] = [254.0, 1.0, 3.0]  # 127 * x / 254: exact half-integers
+    for dtype in (torch.float32, torch.bfloat16):
+        xt = torch.from_numpy(x).to(dtype)
+        xn = _np(xt)
+        qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("int8", "per_token"))
+        codes, s = OQ.quantize_int8_per_token(xn)
+        assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
+        assert np.array_equal(qt.codes.cpu().numpy(), codes)
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 2, 128, 64), torch.float32), ((2, 3, 300, 128), torch.bfloat16),
+                                         ((1, 1, 999, 128), torch.bfloat16)])
+def test_mxfp8_small(shape, dtype):
+    g = np.random.default_rng(sum(shape) + 5)
+    x = (g.standard_t(4, shape) * np.exp2(g.integers(-30, 30, shape[:3] + (1,)))).astype(np.float32)
+    x[..., 0, :] = 0.0
+    xt = torch.from_numpy(x).to(dtype)
+    xn = _np(xt)
+    qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("mxfp8", "per_block"))
+    codes, e8 = OQ.quantize_mxfp8(xn)
+    assert np.array_equal(qt.scales.cpu().numpy(), e8)
+    assert np.array_equal(qt.codes.cpu().numpy(), codes)
+
+
+def test_mxfp8_ties_saturation_and_exponent_range():
+    """Blocks whose maximum sits in (448, 512) * 2^E (saturates), elements on
+    E4M3 ties and in the subnormal range, at exponents from the clamp at
+    -127 to the top of fp32."""
+    grid = F.E4M3_VALUES[:0x7F]
+    mids = (grid[1:] + grid[:-1]) / 2
+    rows = []
+    for E in [-140, -127, -100, -20, -9, 0, 7, 60, 119]:
+        blk = np.concatenate([[500.0], mids[::4][:15], -grid[::8][:16]])[:32]
+        rows.append(np.ldexp(blk, E).astype(np.float32))
+    x = np.stack([np.concatenate([r, r[::-1], -r, r]) for r in rows]).reshape(1, 1, len(rows), 128)
+    qt = faq.fa_quantize(torch.from_numpy(x).to(DEV), faq.QConfig("mxfp8", "per_block"))
+    codes, e8 = OQ.quantize_mxfp8(x)
+    assert np.array_equal(qt.scales.cpu().numpy(), e8)
+    assert np.array_equal(qt.codes.cpu().numpy(), codes)
+
+
 def test_empty_tensor_is_a_no_op():
     x = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
     qt = faq.fa_quantize(x, faq.QConfig("fp8_e4m3", "per_token"))
@@ -245,16 +350,30 @@ def _rows_check(run, br, rows_per_bh=24, seed=0):
     elif run.mode == "int8_head":
         codes = OQ.quantize_int8_per_head(xs, run.static[br].cpu().numpy())
         assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
+    elif run.mode == "fp8_head":
+        codes = OQ.quantize_fp8_per_head(xs, run.static[br].cpu().numpy())
+        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
+    elif run.mode == "int8_token":
+        codes, s = OQ.quantize_int8_per_token(xs)
+        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
+        assert np.array_equal(run.qt[br].scales.view(B, H, S)[:, :, rows].cpu().numpy(), s)
+    elif run.mode == "mxfp8":
+        codes, e8 = OQ.quantize_mxfp8(xs)
+        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
+        assert np.array_equal(run.qt[br].scales[:, :, rows].cpu().numpy(), e8)
+    else:
+        raise AssertionError(run.mode)
 
 
 def _calib_check(run):
     w = run.w
+    scales = OQ.int8_scales if run.mode == "int8_head" else OQ.fp8_scales
     for br in range(3):
         ref = None
         for c in w.calib[br]:
             ref = OQ.calibrate_amax(c.to(torch.float32).numpy(), ref)
         assert np.array_equal(run.amax[br].cpu().numpy(), ref)
-        assert np.array_equal(run.static[br].cpu().numpy(), OQ.int8_scales(ref))
+        assert np.array_equal(run.static[br].cpu().numpy(), scales(ref))
 
 
 def _blocks_check(run, br, nblocks=6):
@@ -281,11 +400,11 @@ def _blocks_check(run, br, nblocks=6):
         assert scales[b, h, k] == s.ravel()[0]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_full_size_quantize(cfg):
     w = make_inputs(cfg)
     run = GpuRun(w, keep_rotated=(cfg == 5))
-    if cfg in (1, 2):
+    if run.static[0] is not None:
         _calib_check(run)
     for br in range(3):
         if cfg == 5:
