@@ -11,7 +11,10 @@
  *     exponent ("FA 量化" page, 组合 3);
  *   - learned rotation of Q and K, then FP8 E4M3 block quantization with
  *     128-token Q blocks and 256-token K/V blocks (MindIE SD "量化" page,
- *     FA量化 / 技术特点: 旋转, 块量化, FP8 Attention).
+ *     FA量化 / 技术特点: 旋转, 块量化, FP8 Attention);
+ *   - the sibling modes of the FA mode list ("FA 量化" page, 该类下的模式清单;
+ *     "量化模式" page, 模式索引 / FA 量化): FP8 per-head static, INT8
+ *     per-token dynamic and MXFP8 per-block dynamic.
  *
  * Conventions shared by every entry point:
  *   - Tensors are BNSD [B, H, S, D], contiguous, row-major ("量化" page,
@@ -59,7 +62,8 @@ typedef enum { FAQ_FLOAT = 0, FAQ_INT8 = 1, FAQ_FP8_E4M3 = 2, FAQ_MXFP4 = 3, FAQ
 /* Quantization granularity (QConfig.scope):
    PER_HEAD        one float scale per head, shared over B and S  -> float[H]
    PER_TOKEN       one float scale per (b,h,s) row of D          -> float[B,H,S]
-   PER_BLOCK       MX: one E8M0 byte per 32 consecutive d        -> uint8[B,H,S,D/32]
+   PER_BLOCK       MX (MXFP4, MXFP8): one E8M0 byte per 32
+                   consecutive d                                  -> uint8[B,H,S,D/32]
    PER_TOKEN_BLOCK one float scale per (b,h, block_tokens rows)  -> float[B,H,ceil(S/bt)] */
 typedef enum {
   FAQ_PER_HEAD = 0,
@@ -88,6 +92,7 @@ typedef struct {
    codes:  INT8       int8 [B,H,S,D]
            FP8_E4M3   uint8 E4M3FN bit patterns [B,H,S,D]
            MXFP4      uint8 [B,H,S,D/2], element 2i in the low nibble
+           MXFP8      uint8 E4M3FN bit patterns [B,H,S,D]
    scales: see faq_scope.  fa_quant_codes_bytes / fa_quant_scales_bytes give
    the sizes. */
 typedef struct {
@@ -121,7 +126,8 @@ faq_status fa_quant_scales_from_amax(const float* amax, int64_t H, int32_t dtype
    x           device [B,H,S,D] of x_dtype (F32 or BF16; the rotation path
                needs BF16).
    cfg         the branch's QConfig; must equal out->cfg.
-   static_scale PER_HEAD only: device float[H] from fa_quant_scales_from_amax;
+   static_scale PER_HEAD only (INT8 or FP8): device float[H] from
+               fa_quant_scales_from_amax (same dtype);
                NULL -> FAQ_ERR_NOT_CALIBRATED.  Must be NULL for other scopes.
                Copied into out->scales unless it is the same pointer.
    rot         PER_TOKEN_BLOCK only, optional: device bf16 [D,D] rotation R;
@@ -135,8 +141,11 @@ faq_status fa_quant_scales_from_amax(const float* amax, int64_t H, int32_t dtype
      scale = fl32(amax / qmax) (amax == 0 -> 1), code = round-half-even of
      fl32(x / scale) onto the target grid, saturating (INT8 clamps to
      [-128,127]; E4M3 saturates at +-448 and keeps the sign of zero);
+     FP8 per-head saturates inputs beyond the calibrated range at +-448;
      MXFP4: E = clamp(floor(log2 amax) - 2, -127, 127), E8M0 byte = E + 127,
-     element = E2M1(x * 2^-E) with ties to even, saturating at 6. */
+     element = E2M1(x * 2^-E) with ties to even, saturating at 6;
+     MXFP8: E = clamp(floor(log2 amax) - 8, -127, 127), element =
+     E4M3(x * 2^-E), ties to even, saturating at 448. */
 faq_status fa_quantize(const void* x, int32_t x_dtype, const faq_shape* shape,
                        const faq_qconfig* cfg, const float* static_scale, const void* rot,
                        faq_qtensor* out, void* debug_rotated, void* stream);
@@ -150,19 +159,21 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
 /* Attention on quantized operands: both Q K^T and P V run on low-bit MFMA
    operands ("FA 量化" page, 概述), output dequantized to the original
    precision ("量化" page, FA量化 / FP8 Attention).
-   q, k, v     quantized with one common (dtype, scope) - INT8/PER_HEAD,
-               FP8/PER_TOKEN, MXFP4/PER_BLOCK or FP8/PER_TOKEN_BLOCK (Q block
-               128, K/V block 256, or any multiples of 128).  B, H, D equal;
-               k and v share S.
+   q, k, v     quantized with one common (dtype, scope) - INT8 or FP8
+               PER_HEAD / PER_TOKEN, MXFP4 or MXFP8 PER_BLOCK, or
+               FP8/PER_TOKEN_BLOCK (Q block 128, K/V block 256).  B, H, D
+               equal; k and v share S.
    sm_scale    softmax scale; 0 means 1/sqrt(D).
    causal      1: key j is masked for query i when j > i (needs Sq == Skv).
    out         device [B,H,Sq,D], out_dtype F32 or BF16 (bf16 = the float
                result rounded to nearest even).
    workspace   device buffer of at least fa_quant_attention_workspace_bytes.
    Probabilities enter the PV product quantized per 128-key tile relative
-   to the tile's own row maximum: int8 round(127 p), E4M3 of 448 p w_j with
-   w_j the key's V scale over the tile's largest (FP8 modes), or MXFP4 over
-   32-key groups (MXFP4 mode); the softmax denominator uses unquantized p. */
+   to the tile's own row maximum: int8 round(127 p w_j) or E4M3 of
+   448 p w_j, with w_j the key's V scale over the tile's largest (1 when V
+   has one scale per tile), decided on the fp32 multiplier
+   fl32(qmax fl32(w_j)); MXFP4 / MXFP8 over 32-key groups in the MX modes.
+   The softmax denominator uses unquantized p. */
 faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
                               float sm_scale, int32_t causal, void* out, int32_t out_dtype,
                               void* workspace, size_t workspace_bytes, void* stream);

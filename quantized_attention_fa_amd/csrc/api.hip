@@ -196,6 +196,20 @@ faq_status fa_quantize(const void* x, int32_t x_dtype, const faq_shape* shape, c
   return hip_status(e, fn);
 }
 
+// Where the float scale of token i of head (b, h) sits: b * sb + h * sh +
+// i / block.  Per-head scales are one block spanning the sequence (rounded
+// up to whole 128-key tiles).
+static void scale_index(const faq_qconfig& c, const faq_shape& s, int* block, int64_t* sb, int64_t* sh) {
+  if (c.scope == FAQ_PER_TOKEN_BLOCK) {
+    const int64_t nb = (s.S + c.block_tokens - 1) / c.block_tokens;
+    *block = c.block_tokens; *sh = nb; *sb = s.H * nb;
+  } else if (c.scope == FAQ_PER_HEAD) {
+    *block = (int)(((s.S > 0 ? s.S : 1) + 127) / 128 * 128); *sh = 1; *sb = 0;
+  } else {
+    *block = 1; *sh = s.S; *sb = s.H * s.S;
+  }
+}
+
 static faq_status attn_check(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
                              int* mode, const char* fn) {
   if (!q || !k || !v) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL tensor");
@@ -214,7 +228,12 @@ static faq_status attn_check(const faq_qtensor* q, const faq_qtensor* k, const f
       q->shape.H != v->shape.H || q->shape.D != k->shape.D || q->shape.D != v->shape.D ||
       k->shape.S != v->shape.S)
     return fail(FAQ_ERR_SHAPE, fn, "q/k/v shapes");
-  *mode = q->cfg.dtype == FAQ_INT8 ? ATTN_INT8 : q->cfg.dtype == FAQ_MXFP4 ? ATTN_MX : ATTN_FP8;
+  switch (q->cfg.dtype) {
+    case FAQ_INT8: *mode = q->cfg.scope == FAQ_PER_HEAD ? ATTN_INT8 : ATTN_I8TOK; break;
+    case FAQ_MXFP4: *mode = ATTN_MX; break;
+    case FAQ_MXFP8: *mode = ATTN_MX8; break;
+    default: *mode = ATTN_FP8; break;
+  }
   return FAQ_OK;
 }
 
@@ -249,9 +268,8 @@ faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const 
   a.q_codes = q->codes; a.q_scales = q->scales;
   a.k_codes = k->codes; a.k_scales = k->scales;
   a.v_codes = v->codes; a.v_scales = v->scales;
-  const bool blk = q->cfg.scope == FAQ_PER_TOKEN_BLOCK;
-  a.q_block = blk ? q->cfg.block_tokens : 1;
-  a.kv_block = blk ? k->cfg.block_tokens : 1;
+  scale_index(q->cfg, q->shape, &a.q_block, &a.q_sb, &a.q_sh);
+  scale_index(k->cfg, k->shape, &a.kv_block, &a.kv_sb, &a.kv_sh);
   a.sm_scale = sm_scale == 0.0f ? 1.0f / sqrtf((float)D) : sm_scale;
   a.causal = causal;
   a.out = out;

@@ -14,14 +14,23 @@
 //                  operands and their E8M0 block exponents as MFMA scales
 //                  (exact: products within a block span < 2^8); P V on the
 //                  bf16 MFMA with P = E2M1 * 2^E and V dequantized exactly.
+//   INT8 per-token int8 MFMA for both products as INT8 per-head; the per-key
+//                  K scale multiplies the exact integer scores, the per-key
+//                  V scale is folded into the int8 probabilities (as FP8).
+//   MXFP8          the bf16 MFMA path of FP8: each Q/K row is widened to
+//                  bf16 relative to its largest block exponent (exact), the
+//                  row exponents scale the scores; V is dequantized exactly
+//                  to bf16; P is MX-quantized with E4M3 elements.
+// FP8 per-head static runs the FP8 path with one scale per tile.
 // The output is dequantized to bf16 (or fp32) ("量化" page, FA量化 / FP8
 // Attention).
 //
 // Probability rule (the pages leave it open; this is the library's contract):
 // keys are cut into 128-key tiles aligned to absolute key index; per query
 // row and tile, m = max score, p = exp(s - m) is quantized with a static
-// scale relative to that tile maximum (int8: rne(127 p); E4M3: 448 p w_j with
-// w_j = s_v,j / max_tile s_v; MXFP4: the MX quantizer over 32-key groups),
+// scale relative to that tile maximum (int8: rne(127 p w_j); E4M3: 448 p w_j
+// with w_j = s_v,j / max_tile s_v (1 when V has one scale per tile); MXFP4 /
+// MXFP8: the MX quantizer over 32-key groups),
 // the tile sum L uses unquantized p, and tiles combine with the usual
 // running-max rescale, O = sum_t e^{m_t-M} C_t / sum_t e^{m_t-M} L_t.
 //
@@ -94,6 +103,16 @@ FAQ_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
 }
 
+// The same times the power of two `sc` (exact while the products stay in
+// bf16's normal range).
+template <bool HI>
+FAQ_DEV uint32_t e4m3x2_to_bf16x2_scaled(uint32_t w, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, sc, HI));
+}
+
+// 2^e as a float for e in [-126, 127] (a normal number, built from its bits).
+FAQ_DEV float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
 // Max / sum over the two lanes holding one query (l and l ^ 32).
 FAQ_DEV float halves_max(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -107,31 +126,37 @@ FAQ_DEV float halves_sum(float x) {
 // Geometry of the LDS tiles.
 template <int MODE, int D>
 struct Cfg {
-  static constexpr int KROW = MODE == ATTN_INT8 ? D : (MODE == ATTN_FP8 ? 2 * D : D / 2);  // bytes of a K row
+  static constexpr bool I8 = MODE == ATTN_INT8 || MODE == ATTN_I8TOK;  // int8 MFMA for both products
+  static constexpr bool BFK = MODE == ATTN_FP8 || MODE == ATTN_MX8;    // bf16 K image, bf16 MFMA
+  static constexpr bool MXP = MODE == ATTN_MX || MODE == ATTN_MX8;     // MX probability groups
+  static constexpr bool VW = MODE == ATTN_FP8 || MODE == ATTN_I8TOK;   // per-key V scale folded into P
+  static constexpr int KROW = I8 ? D : (BFK ? 2 * D : D / 2);  // bytes of a K row
   static constexpr int KBYTES = BN * KROW;
   static constexpr int NB = D / 32;  // MX blocks per row
-  // per-key extras: after the K tile the FP8 K scales (floats) or the MXFP4
-  // K block exponents; after the V^T tile the FP8 multipliers 448 w_j
-  // (floats), which the probabilities read after the K buffer is refilled
-  static constexpr int XKBYTES = MODE == ATTN_FP8 ? BN * 4 : (MODE == ATTN_MX ? BN * NB : 0);
-  static constexpr int XVBYTES = MODE == ATTN_FP8 ? BN * 4 : 0;
+  // per-key extras: after the K tile the K scales (floats; MXFP8: 2^ of
+  // the row exponent) or the MXFP4 K block exponents; after the V^T tile
+  // the multipliers qmax w_j (floats), which the probabilities read after
+  // the K buffer is refilled
+  static constexpr int XKBYTES = MODE == ATTN_MX ? BN * NB : (MODE == ATTN_INT8 ? 0 : BN * 4);
+  static constexpr int XVBYTES = VW ? BN * 4 : 0;
   static constexpr int XBYTES = XKBYTES + XVBYTES;  // per tile in the workspace
-  static constexpr int VROW = MODE == ATTN_INT8 ? BN : 2 * BN;  // bytes of a V^T row
+  static constexpr int VROW = I8 ? BN : 2 * BN;     // bytes of a V^T row
   static constexpr int VBYTES = D * VROW;
-  static constexpr int KS = MODE == ATTN_INT8 ? D / 32 : (MODE == ATTN_FP8 ? D / 16 : D / 64);  // QK k-steps
-  static constexpr int DB = D / 32;  // 32-channel output blocks
+  static constexpr int KS = I8 ? D / 32 : (BFK ? D / 16 : D / 64);  // QK k-steps
+  static constexpr int DB = D / 32;                                 // 32-channel output blocks
 };
 
 // ------------------------------------------------------------------------
 // Workspace layout (per (b,h), per 128-key tile t):
 //   vt  : V^T of the tile as its LDS image (chunk-major, columns in the lane
-//         key order): INT8 codes (1 byte) or, for FP8 and MXFP4, the exact
-//         values in bf16 (2 bytes)
-//   kb  : FP8: K widened to bf16 as its LDS image (rows past the end are 0)
-//   aux : FP8: 128 K scales then 128 multipliers 448 * w_j (floats);
-//         MXFP4: the K block exponents, 128 rows x D/32 bytes (127 past
-//         the end)
-//   sig : FP8: sigma_t = max over the tile's keys of s_v,j
+//         key order): INT8 codes (1 byte) or, for FP8, MXFP4 and MXFP8, the
+//         values in bf16 (2 bytes; E4M3 codes, exact values for MX)
+//   kb  : FP8 / MXFP8: K widened to bf16 as its LDS image (rows past the
+//         end are 0; MXFP8 relative to the row's largest block exponent)
+//   aux : FP8 / INT8 per-token: 128 K scales then 128 multipliers qmax w_j
+//         (floats); MXFP8: 128 K row scales 2^(E_row); MXFP4: the K block
+//         exponents, 128 rows x D/32 bytes (127 past the end)
+//   sig : FP8 / INT8 per-token: sigma_t = max over the tile's keys of s_v,j
 // ------------------------------------------------------------------------
 struct WsLayout {
   size_t vt_off, kb_off, aux_off, sig_off, total;
@@ -140,70 +165,119 @@ struct WsLayout {
 inline WsLayout ws_layout(int mode, int64_t B, int64_t H, int64_t Skv, int64_t D) {
   const int64_t nt = (Skv + BN - 1) / BN;
   const size_t tiles = (size_t)(B * H * nt);
+  const bool i8 = mode == ATTN_INT8 || mode == ATTN_I8TOK;
+  const bool bfk = mode == ATTN_FP8 || mode == ATTN_MX8;
+  const bool vw = mode == ATTN_FP8 || mode == ATTN_I8TOK;
+  const size_t xk = mode == ATTN_MX ? BN * (D / 32) : (mode == ATTN_INT8 ? 0 : BN * 4);
+  const size_t xv = vw ? BN * 4 : 0;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WsLayout l{};
   l.vt_off = 0;
-  l.kb_off = up(tiles * D * BN * (mode == ATTN_INT8 ? 1 : 2));
-  l.aux_off = l.kb_off + up(mode == ATTN_FP8 ? tiles * BN * D * 2 : 0);
-  const size_t aux = mode == ATTN_FP8 ? tiles * 2 * BN * 4 : (mode == ATTN_MX ? tiles * BN * (D / 32) : 0);
-  l.sig_off = l.aux_off + up(aux);
-  l.total = l.sig_off + up(mode == ATTN_FP8 ? tiles * 4 : 0);
+  l.kb_off = up(tiles * D * BN * (i8 ? 1 : 2));
+  l.aux_off = l.kb_off + up(bfk ? tiles * BN * D * 2 : 0);
+  l.sig_off = l.aux_off + up(tiles * (xk + xv));
+  l.total = l.sig_off + up(vw ? tiles * 4 : 0);
   return l;
 }
 
 // ------------------------------------------------------------------------
 // Per-call re-layout.  grid = (tiles, B*H), 256 threads; one 128-key tile.
-//   INT8 : the V^T image (codes).
-//   FP8  : the K and V^T images widened to bf16, the per-key K scales and
-//          448 w_j, and sigma_t.
+//   INT8 per-head : the V^T image (codes).
+//   INT8 per-token: the V^T image (codes), the per-key K scales and
+//                   127 w_j, and sigma_t.
+//   FP8           : the K and V^T images widened to bf16, the per-key K
+//                   scales and 448 w_j, and sigma_t.
+//   MXFP8         : the K image (each row relative to its largest block
+//                   exponent) with the row scales 2^(E_row), and the V^T
+//                   image as the exact bf16 values.
+// Scales of K and V are read at b * sb + h * sh + key / blk (per-token:
+// blk 1; token blocks: blk tokens; per-head: sb 0, sh 1, one block).
 // ------------------------------------------------------------------------
-template <int D, bool FP8>
-__global__ __launch_bounds__(256) void k_prep(const uint8_t* __restrict__ k, const float* __restrict__ ks,
-                                              const uint8_t* __restrict__ v, const float* __restrict__ vs,
-                                              int64_t Skv, int kv_block, int64_t nt, uint8_t* __restrict__ vt,
-                                              uint8_t* __restrict__ kb, float* __restrict__ aux,
-                                              float* __restrict__ sig) {
-  using C = Cfg<FP8 ? ATTN_FP8 : ATTN_INT8, D>;
+struct PrepArgs {
+  const uint8_t* k;
+  const void* ks;
+  const uint8_t* v;
+  const void* vs;
+  int64_t H, Skv, nt, sb, sh;
+  int blk;
+  uint8_t* vt;
+  uint8_t* kb;
+  float* aux;
+  float* sig;
+};
+
+template <int MODE, int D>
+__global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
+  using C = Cfg<MODE, D>;
+  constexpr int NB = D / 32;
+  constexpr bool MX8 = MODE == ATTN_MX8;
   __shared__ uint8_t tile[BN][D + 4];
+  __shared__ uint8_t vex[MX8 ? BN : 1][NB];
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t k0 = (int64_t)t * BN;
-  const int64_t tile_id = bh * nt + t;
+  const int64_t tile_id = bh * a.nt + t;
+  const int64_t sbase = (bh / a.H) * a.sb + (bh % a.H) * a.sh;  // scale index of key 0 of the head
   constexpr int CPR = D / 16;  // 16-byte chunks per key row of codes
   for (int c = threadIdx.x; c < BN * CPR; c += 256) {
     const int kl = c / CPR, cc = c % CPR;
+    const bool ok = k0 + kl < a.Skv;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (k0 + kl < Skv) val = *reinterpret_cast<const uint4*>(v + (bh * Skv + k0 + kl) * D + cc * 16);
+    if (ok) val = *reinterpret_cast<const uint4*>(a.v + (bh * a.Skv + k0 + kl) * D + cc * 16);
     uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[kl][cc * 16]);
     dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
-    if (FP8) {
+    if (C::BFK) {
       // K row chunk widened to bf16: columns 2 cc and 2 cc + 1 of the image
       uint4 kv = make_uint4(0, 0, 0, 0);
-      if (k0 + kl < Skv) kv = *reinterpret_cast<const uint4*>(k + (bh * Skv + k0 + kl) * D + cc * 16);
-      uint8_t* img = kb + tile_id * C::KBYTES + kslot(kl) * 16;
+      float sc = 1.0f;
+      if (ok) {
+        kv = *reinterpret_cast<const uint4*>(a.k + (bh * a.Skv + k0 + kl) * D + cc * 16);
+        if (MX8) {
+          const uint8_t* ke = reinterpret_cast<const uint8_t*>(a.ks) + (bh * a.Skv + k0 + kl) * NB;
+          int emax = 0;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) emax = max(emax, (int)ke[b]);
+          sc = __builtin_amdgcn_ldexpf(1.0f, (int)ke[cc >> 1] - emax);
+        }
+      }
+      uint8_t* img = a.kb + tile_id * C::KBYTES + kslot(kl) * 16;
       *reinterpret_cast<uint4*>(img + (2 * cc) * BN * 16) =
-          make_uint4(e4m3x2_to_bf16x2<false>(kv.x), e4m3x2_to_bf16x2<true>(kv.x), e4m3x2_to_bf16x2<false>(kv.y),
-                     e4m3x2_to_bf16x2<true>(kv.y));
+          make_uint4(e4m3x2_to_bf16x2_scaled<false>(kv.x, sc), e4m3x2_to_bf16x2_scaled<true>(kv.x, sc),
+                     e4m3x2_to_bf16x2_scaled<false>(kv.y, sc), e4m3x2_to_bf16x2_scaled<true>(kv.y, sc));
       *reinterpret_cast<uint4*>(img + (2 * cc + 1) * BN * 16) =
-          make_uint4(e4m3x2_to_bf16x2<false>(kv.z), e4m3x2_to_bf16x2<true>(kv.z), e4m3x2_to_bf16x2<false>(kv.w),
-                     e4m3x2_to_bf16x2<true>(kv.w));
+          make_uint4(e4m3x2_to_bf16x2_scaled<false>(kv.z, sc), e4m3x2_to_bf16x2_scaled<true>(kv.z, sc),
+                     e4m3x2_to_bf16x2_scaled<false>(kv.w, sc), e4m3x2_to_bf16x2_scaled<true>(kv.w, sc));
+    }
+  }
+  if (MX8) {
+    for (int c = threadIdx.x; c < BN * NB; c += 256) {
+      const int kl = c / NB, b = c % NB;
+      vex[kl][b] = k0 + kl < a.Skv ? reinterpret_cast<const uint8_t*>(a.vs)[(bh * a.Skv + k0 + kl) * NB + b]
+                                   : (uint8_t)127;
     }
   }
   __syncthreads();
-  uint8_t* img = vt + tile_id * C::VBYTES;
+  uint8_t* img = a.vt + tile_id * C::VBYTES;
   constexpr int VCOLS = C::VROW / 16;
   // item i: column c = i / D, row d = i % D (consecutive threads write
   // consecutive 16-byte slots of one column)
   for (int i = threadIdx.x; i < VCOLS * D; i += 256) {
     const int c = i / D, d = i % D;
     uint32_t w[4];
-    if (FP8) {
+    if (!C::I8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t pair =
-            (uint32_t)tile[vt_key_bf16(8 * c + 2 * q)][d] | ((uint32_t)tile[vt_key_bf16(8 * c + 2 * q + 1)][d] << 8);
+        const int key0 = vt_key_bf16(8 * c + 2 * q), key1 = vt_key_bf16(8 * c + 2 * q + 1);
+        const uint32_t pair = (uint32_t)tile[key0][d] | ((uint32_t)tile[key1][d] << 8);
         w[q] = e4m3x2_to_bf16x2<false>(pair);
+        if (MX8) {
+          // the exact value code * 2^(E - 127), rounded to bf16 (exact
+          // within bf16's normal range)
+          const float f0 = __builtin_amdgcn_ldexpf(bf16_lo(w[q]), (int)vex[key0][d >> 5] - 127);
+          const float f1 = __builtin_amdgcn_ldexpf(bf16_hi(w[q]), (int)vex[key1][d >> 5] - 127);
+          w[q] = f32_to_bf16_bits(f0) | (f32_to_bf16_bits(f1) << 16);
+        }
       }
     } else {
 #pragma unroll
@@ -216,23 +290,35 @@ __global__ __launch_bounds__(256) void k_prep(const uint8_t* __restrict__ k, con
     }
     *reinterpret_cast<uint4*>(img + (c * D + d) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  if (FP8) {
-    const int kl = threadIdx.x;
-    float s = 0.0f, sk = 0.0f;
-    if (kl < BN && k0 + kl < Skv) {
-      const int64_t nblk = (Skv + kv_block - 1) / kv_block;
-      s = vs[bh * nblk + (k0 + kl) / kv_block];
-      sk = ks[bh * nblk + (k0 + kl) / kv_block];
+  const int kl = threadIdx.x;
+  if (C::VW) {
+    float sv = 0.0f, sk = 0.0f;
+    if (kl < BN && k0 + kl < a.Skv) {
+      const int64_t si = sbase + (k0 + kl) / a.blk;
+      sv = reinterpret_cast<const float*>(a.vs)[si];
+      sk = reinterpret_cast<const float*>(a.ks)[si];
     }
-    float m = wave_max(s);
+    float m = wave_max(sv);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    constexpr float qmax = MODE == ATTN_FP8 ? 448.0f : 127.0f;
     if (kl < BN) {
-      aux[tile_id * 2 * BN + kl] = sk;
-      aux[tile_id * 2 * BN + BN + kl] = (s > 0.0f) ? 448.0f * (s / m) : 0.0f;
+      a.aux[tile_id * 2 * BN + kl] = sk;
+      a.aux[tile_id * 2 * BN + BN + kl] = (sv > 0.0f) ? qmax * (sv / m) : 0.0f;
     }
-    if (threadIdx.x == 0) sig[tile_id] = m;
+    if (threadIdx.x == 0) a.sig[tile_id] = m;
+  }
+  if (MX8 && kl < BN) {
+    float sk = 0.0f;
+    if (k0 + kl < a.Skv) {
+      const uint8_t* ke = reinterpret_cast<const uint8_t*>(a.ks) + (bh * a.Skv + k0 + kl) * NB;
+      int emax = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) emax = max(emax, (int)ke[b]);
+      sk = __builtin_amdgcn_ldexpf(1.0f, emax - 127);
+    }
+    a.aux[tile_id * BN + kl] = sk;
   }
 }
 
@@ -300,12 +386,13 @@ struct KParams {
   int nqt;
   const uint8_t* q;
   const void* qs;
-  const uint8_t* k;      // INT8 / MXFP4: K codes; FP8: bf16 K images in the workspace
-  const void* ks;        // INT8: per-head K scale
+  const uint8_t* k;      // INT8 / MXFP4: K codes; FP8 / MXFP8: bf16 K images in the workspace
+  const void* ks;        // INT8 per-head: K scale
   const uint8_t* vt;     // V^T images in the workspace
-  const uint8_t* aux;    // FP8: K scales + 448 w_j; MXFP4: K exponents (per tile)
-  const float* sig;      // FP8: sigma_t
-  const float* vs_head;  // INT8: per-head V scale
+  const uint8_t* aux;    // per-tile K extras, then V extras (see Cfg)
+  const float* sig;      // FP8 / INT8 per-token: sigma_t
+  const float* vs_head;  // INT8 per-head: V scale
+  int64_t q_sb, q_sh;    // FP8 / INT8 per-token: Q scale index b * q_sb + h * q_sh + i / q_block
   int q_block;
   float c_log2;  // sm_scale * log2(e)
   void* out;
@@ -353,6 +440,8 @@ template <int MODE, int D, bool CAUSAL, bool KVC>
 __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   using G = Cfg<MODE, D>;
   constexpr int KS = G::KS, DB = G::DB, NB = G::NB;
+  // per-key K scales multiply the scores (per-token scopes, MXFP8 rows)
+  constexpr bool PERKEY = (MODE == ATTN_FP8 && !KVC) || MODE == ATTN_I8TOK || MODE == ATTN_MX8;
   // K (+ its per-key extras) and V^T tiles in separate LDS objects: V(t)
   // is copied while the scores and probabilities of tile t are computed
   // from K(t), and K(t+1) while the products with V(t) run.  As distinct
@@ -385,33 +474,47 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   const int q0 = qt * BM + wave * 32;  // this wave's first query
   const int qi = q0 + j;               // this lane's query
   const bool act = q0 < Sq;            // uniform per wave: any query to compute
-  const uint8_t* kbase = p.k + (MODE == ATTN_FP8 ? bh * nt * (int64_t)G::KBYTES : bh * (int64_t)Skv * G::KROW);
+  const uint8_t* kbase = p.k + (G::BFK ? bh * nt * (int64_t)G::KBYTES : bh * (int64_t)Skv * G::KROW);
   const uint8_t* vtbase = p.vt + bh * nt * (int64_t)G::VBYTES;
   const uint8_t* auxbase = p.aux + bh * nt * (int64_t)G::XBYTES;
 
   // ---- Q operands (B of S^T = K Q^T): lane (j, h) holds, for k-step ks,
   // the K-slice [K/2 h, K/2 h + K/2) of the instruction's K range
-  bf16x8 qbf[MODE == ATTN_FP8 ? KS : 1];  // FP8: bf16 images of the E4M3 codes
-  i32x4 qi8[MODE == ATTN_INT8 ? KS : 1];  // INT8: 16 codes
+  bf16x8 qbf[G::BFK ? KS : 1];  // FP8 / MXFP8: bf16 images of the E4M3 codes
+  i32x4 qi8[G::I8 ? KS : 1];    // INT8: 16 codes
   i32x8 qmx[MODE == ATTN_MX ? KS : 1];    // MXFP4: 32 E2M1 codes (16 bytes used)
   int qsc[MODE == ATTN_MX ? KS : 1];      // MXFP4: their E8M0 exponents
   float cq;
   {
     const bool ok = qi < Sq;
     const int64_t qrow_i = bh * p.Sq + (ok ? qi : 0);
-    if (MODE == ATTN_FP8) {
+    // per-token / token-block / per-head float Q scale of this query
+    const int64_t qsi = (bh / p.H) * p.q_sb + hd * p.q_sh + (ok ? qi : 0) / p.q_block;
+    if (G::BFK) {
       const uint8_t* qrow = p.q + qrow_i * D;
+      // MXFP8: the row relative to its largest block exponent
+      int eb[MODE == ATTN_MX8 ? NB : 1], emax = 127;
+      if (MODE == ATTN_MX8) {
+        const uint8_t* qe = reinterpret_cast<const uint8_t*>(p.qs) + qrow_i * NB;
+        emax = 0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          eb[b] = ok ? (int)qe[b] : 127;
+          emax = max(emax, eb[b]);
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         uint2 a = make_uint2(0, 0);
         if (ok) a = *reinterpret_cast<const uint2*>(qrow + 16 * ks + 8 * h);
-        qbf[ks] = __builtin_bit_cast(bf16x8, i32x4{(int)e4m3x2_to_bf16x2<false>(a.x), (int)e4m3x2_to_bf16x2<true>(a.x),
-                                                  (int)e4m3x2_to_bf16x2<false>(a.y), (int)e4m3x2_to_bf16x2<true>(a.y)});
+        const float sc = MODE == ATTN_MX8 ? __builtin_amdgcn_ldexpf(1.0f, eb[ks >> 1] - emax) : 1.0f;
+        qbf[ks] = __builtin_bit_cast(
+            bf16x8, i32x4{(int)e4m3x2_to_bf16x2_scaled<false>(a.x, sc), (int)e4m3x2_to_bf16x2_scaled<true>(a.x, sc),
+                          (int)e4m3x2_to_bf16x2_scaled<false>(a.y, sc), (int)e4m3x2_to_bf16x2_scaled<true>(a.y, sc)});
       }
-      const float* qs = reinterpret_cast<const float*>(p.qs);
-      const int64_t nqs = (p.Sq + p.q_block - 1) / p.q_block;
-      cq = (ok ? qs[bh * nqs + qi / p.q_block] : 1.0f) * p.c_log2;
-    } else if (MODE == ATTN_INT8) {
+      if (MODE == ATTN_MX8) cq = __builtin_amdgcn_ldexpf(1.0f, emax - 127) * p.c_log2;
+      else cq = (ok ? reinterpret_cast<const float*>(p.qs)[qsi] : 1.0f) * p.c_log2;
+    } else if (G::I8) {
       const uint8_t* qrow = p.q + qrow_i * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -420,8 +523,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
         qi8[ks] = i32x4{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
       }
       const float* qs = reinterpret_cast<const float*>(p.qs);
-      const float* ksc = reinterpret_cast<const float*>(p.ks);
-      cq = qs[hd] * ksc[hd] * p.c_log2;
+      if (MODE == ATTN_INT8) cq = qs[hd] * reinterpret_cast<const float*>(p.ks)[hd] * p.c_log2;
+      else cq = (ok ? qs[qsi] : 1.0f) * p.c_log2;
     } else {
       const uint8_t* qrow = p.q + qrow_i * (D / 2);
       const uint8_t* qe = reinterpret_cast<const uint8_t*>(p.qs) + qrow_i * NB;
@@ -454,21 +557,21 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   const int pw = wave * 64 + lane;
   const int krow = kslot(pw & (BN - 1));
   auto issue_k = [&](int t) {
-    if (MODE == ATTN_FP8) {
+    if (G::BFK) {
       stage<G::KBYTES / 16>(kbuf, kbase + (int64_t)t * G::KBYTES, wave, lane,
                             [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
     } else {
       const uint32_t roff = (uint32_t)(min(t * BN + krow, Skv - 1) * G::KROW) + (uint32_t)((pw >> 7) * 16);
       stage<G::KBYTES / 16>(kbuf, kbase, wave, lane, [&](int i) { return roff + (uint32_t)(2 * i * 16); });
     }
-    if (MODE != ATTN_INT8)
+    if (G::XKBYTES > 0)
       stage<G::XKBYTES / 16>(kbuf + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
                              [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
   };
   auto issue_v = [&](int t) {
     stage<G::VBYTES / 16>(vbuf, vtbase + (int64_t)t * G::VBYTES, wave, lane,
                           [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
-    if (MODE == ATTN_FP8)
+    if (G::XVBYTES > 0)
       stage<G::XVBYTES / 16>(vbuf + G::VBYTES, auxbase + (int64_t)t * G::XBYTES + G::XKBYTES, wave, lane,
                              [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
   };
@@ -516,10 +619,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
           for (int kk = 0; kk < 2; ++kk) {
             const int kb = 2 * pr + kk;
             const uint8_t* a = kop_base + ks * (2 * BN * 16) + kb * 256;
-            if (MODE == ATTN_FP8) {
+            if (G::BFK) {
               if (ks == 0) S[kb] = f32x16{};
               S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld<bf16x8>(a), qbf[ks], S[kb], 0, 0, 0);
-            } else if (MODE == ATTN_INT8) {
+            } else if (G::I8) {
               if (ks == 0) SI[kb] = i32x16{};
               const uint4 v = lds_ld<uint4>(a);
               SI[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, qi8[ks],
@@ -561,7 +664,13 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
             }
         }
       } else {
-        if (MODE == ATTN_FP8 && !KVC) {
+        if (MODE == ATTN_I8TOK) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[kb][r] = (float)SI[kb][r];
+        }
+        if (PERKEY) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -595,7 +704,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       if (MODE == ATTN_FP8 && KVC) ce = cq * xk[-64 * h];  // the tile's K scale
       const float ml = m * ce;  // tile max, log2 units (M is kept in these units)
       float Mn, a;
-      if (MODE == ATTN_INT8) {
+      if (G::I8) {
         // lazy reference: keep the running reference unless this tile's max
         // exceeds it by more than 2^8 (tile weights stay <= 2^8, far from
         // overflow), so O is rescaled only when the max jumps
@@ -609,7 +718,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml - Mn);
       M = Mn;
       bool live = true;
-      if (MODE == ATTN_INT8) {
+      if (G::I8) {
         rscale = a;
       } else {
         // new reference factor f = bt (times sigma_t / 448 for FP8); a row
@@ -635,33 +744,41 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       // ---- probabilities, tile sum, the quantized P operand and
       // O^T += V^T P^T
       float ls0 = 0.f, ls1 = 0.f;
-      if (MODE == ATTN_INT8) {
-        // 127 p = 2^(s ce - (m ce - log2 127)); at the maximum this may
-        // differ from 127 by an ulp, which cannot move rne(127 p)
-        const float mc = ms * ce - kLog2_127;
+      if (G::I8) {
+        // per-head: 127 p = 2^(s ce - (m ce - log2 127)); at the maximum
+        // this may differ from 127 by an ulp, which cannot move rne(127 p).
+        // per-token: p = 1 exactly at the maximum, times 127 w_j.
+        // the running max moves rarely once a row has seen its largest
+        // scores: rescale only when some row of the wave needs it (before
+        // the probabilities, so that they and their products share a block)
+        if (__builtin_amdgcn_ballot_w64(rscale != 1.0f) != 0) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) O[db] *= rscale;
+        }
+        const float mc = MODE == ATTN_INT8 ? ms * ce - kLog2_127 : ms;
         i32x4 P[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
+            float4 vm4;
+            if (MODE == ATTN_I8TOK) vm4 = *reinterpret_cast<const float4*>(xv + 16 * kb + 4 * w);
+            const float vm[4] = {vm4.x, vm4.y, vm4.z, vm4.w};
             uint32_t word = 0;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * w + b], ce, -mc));
+              const float x = S[kb][4 * w + b];
+              float pv = MODE == ATTN_INT8 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, -mc))
+                                           : __builtin_amdgcn_exp2f((x - mc) * ce);
               if (b & 1) ls1 += pv; else ls0 += pv;
-              word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p)
+              if (MODE == ATTN_I8TOK) pv *= vm[b];
+              word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
             }
             P[kb][w] = (int)word;
           }
         }
-        L += halves_sum(ls0 + ls1) * (bt * (1.0f / 127.0f));
-        // the running max moves rarely once a row has seen its largest
-        // scores: rescale only when some row of the wave needs it
-        if (__builtin_amdgcn_ballot_w64(rscale != 1.0f) != 0) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) O[db] *= rscale;
-        }
-        const float bv = bt * vscale_i8;
+        L += halves_sum(ls0 + ls1) * (MODE == ATTN_INT8 ? bt * (1.0f / 127.0f) : bt);
+        const float bv = MODE == ATTN_INT8 ? bt * vscale_i8 : bt * p.sig[bh * nt + t] * (1.0f / 127.0f);
         // two output blocks at a time: two independent accumulation chains
 #pragma unroll
         for (int d2 = 0; d2 < DB; d2 += 2) {
@@ -685,17 +802,18 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) O[db] *= rscale;
         const float mce = ms * ce;
-        float sc = 1.0f;
+        float sc = 1.0f, isc = 1.0f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          if (MODE == ATTN_MX && (kb & 1) == 0) {
+          if (G::MXP && (kb & 1) == 0) {
             // this lane's keys of blocks kb, kb + 1 are one MX group:
-            // group max -> shared exponent; p -> E2M1(p / 2^E) * 2^E, exact
-            // in bf16.  The group's largest p is the same function of the
-            // group's largest score.
+            // group max -> shared exponent; p -> E2M1 / E4M3 of p / 2^E,
+            // times 2^E, exact in bf16.  The group's largest p is the same
+            // function of the group's largest score.
             const float pmax = __builtin_amdgcn_exp2f((gmax[kb >> 1] - ms) * ce);
-            const int E = mx_exponent(pmax);
-            sc = E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
+            const int E = MODE == ATTN_MX ? mx_exponent(pmax) : mx_exponent<8>(pmax);
+            sc = E > -127 ? pow2f(E) : 1.0f;
+            isc = E > -127 ? pow2f(-E) : 1.0f;
           }
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
@@ -728,6 +846,20 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
               e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], e1, true);
               pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0), (int)e4m3x2_to_bf16x2<true>((uint32_t)e0),
                           (int)e4m3x2_to_bf16x2<false>((uint32_t)e1), (int)e4m3x2_to_bf16x2<true>((uint32_t)e1)};
+            } else if (MODE == ATTN_MX8) {
+              // E4M3 of p / 2^E (exact scaling; the group maximum lies in
+              // [256, 512) and saturates above 448), then back times 2^E
+              float u[8];
+#pragma unroll
+              for (int t8 = 0; t8 < 8; ++t8) u[t8] = fminf(pv[t8] * isc, 448.0f);
+              int e0 = __builtin_amdgcn_cvt_pk_fp8_f32(u[0], u[1], 0, false);
+              e0 = __builtin_amdgcn_cvt_pk_fp8_f32(u[2], u[3], e0, true);
+              int e1 = __builtin_amdgcn_cvt_pk_fp8_f32(u[4], u[5], 0, false);
+              e1 = __builtin_amdgcn_cvt_pk_fp8_f32(u[6], u[7], e1, true);
+              pop = i32x4{(int)e4m3x2_to_bf16x2_scaled<false>((uint32_t)e0, sc),
+                          (int)e4m3x2_to_bf16x2_scaled<true>((uint32_t)e0, sc),
+                          (int)e4m3x2_to_bf16x2_scaled<false>((uint32_t)e1, sc),
+                          (int)e4m3x2_to_bf16x2_scaled<true>((uint32_t)e1, sc)};
             } else {
               // each pair through byte 0: E2M1(p / 2^E), then back times 2^E
 #pragma unroll
@@ -784,24 +916,29 @@ hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
     k_prep_mx<D><<<pgrid, 256, 0, st>>>((const uint8_t*)a.v_codes, (const uint8_t*)a.v_scales,
                                         (const uint8_t*)a.k_scales, a.Skv, nt, ws + l.vt_off, ws + l.aux_off);
   } else {
-    k_prep<D, MODE == ATTN_FP8><<<pgrid, 256, 0, st>>>(
-        (const uint8_t*)a.k_codes, (const float*)a.k_scales, (const uint8_t*)a.v_codes, (const float*)a.v_scales,
-        a.Skv, a.kv_block, nt, ws + l.vt_off, ws + l.kb_off, reinterpret_cast<float*>(ws + l.aux_off),
-        reinterpret_cast<float*>(ws + l.sig_off));
+    PrepArgs pa{};
+    pa.k = (const uint8_t*)a.k_codes; pa.ks = a.k_scales;
+    pa.v = (const uint8_t*)a.v_codes; pa.vs = a.v_scales;
+    pa.H = a.H; pa.Skv = a.Skv; pa.nt = nt; pa.sb = a.kv_sb; pa.sh = a.kv_sh; pa.blk = a.kv_block;
+    pa.vt = ws + l.vt_off; pa.kb = ws + l.kb_off;
+    pa.aux = reinterpret_cast<float*>(ws + l.aux_off);
+    pa.sig = reinterpret_cast<float*>(ws + l.sig_off);
+    k_prep<MODE, D><<<pgrid, 256, 0, st>>>(pa);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  using G = Cfg<MODE, D>;
   KParams p{};
   p.H = a.H; p.BH = a.B * a.H; p.Sq = a.Sq; p.Skv = a.Skv; p.nt = nt;
   p.nqt = (int)((a.Sq + BM - 1) / BM);
   p.q = (const uint8_t*)a.q_codes; p.qs = a.q_scales;
-  p.k = MODE == ATTN_FP8 ? ws + l.kb_off : (const uint8_t*)a.k_codes;
+  p.k = G::BFK ? ws + l.kb_off : (const uint8_t*)a.k_codes;
   p.ks = a.k_scales;
   p.vt = ws + l.vt_off;
   p.aux = ws + l.aux_off;
   p.sig = reinterpret_cast<const float*>(ws + l.sig_off);
   p.vs_head = (const float*)a.v_scales;
-  p.q_block = a.q_block;
+  p.q_sb = a.q_sb; p.q_sh = a.q_sh; p.q_block = a.q_block;
   p.c_log2 = a.sm_scale * kLog2e;
   p.out = a.out; p.out_bf16 = a.out_bf16;
   dim3 grid((unsigned)(p.nqt * p.BH));
@@ -817,6 +954,11 @@ hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int MODE>
+hipError_t launch_mode(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
+  return a.D == 128 ? launch_mode_d<MODE, 128>(a, l, st) : launch_mode_d<MODE, 64>(a, l, st);
+}
+
 }  // namespace
 
 size_t attn_workspace_bytes(int mode, int64_t B, int64_t H, int64_t Skv, int64_t D) {
@@ -826,9 +968,11 @@ size_t attn_workspace_bytes(int mode, int64_t B, int64_t H, int64_t Skv, int64_t
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   const WsLayout l = ws_layout(a.mode, a.B, a.H, a.Skv, a.D);
   switch (a.mode) {
-    case ATTN_INT8: return a.D == 128 ? launch_mode_d<ATTN_INT8, 128>(a, l, st) : launch_mode_d<ATTN_INT8, 64>(a, l, st);
-    case ATTN_FP8: return a.D == 128 ? launch_mode_d<ATTN_FP8, 128>(a, l, st) : launch_mode_d<ATTN_FP8, 64>(a, l, st);
-    default: return a.D == 128 ? launch_mode_d<ATTN_MX, 128>(a, l, st) : launch_mode_d<ATTN_MX, 64>(a, l, st);
+    case ATTN_INT8: return launch_mode<ATTN_INT8>(a, l, st);
+    case ATTN_FP8: return launch_mode<ATTN_FP8>(a, l, st);
+    case ATTN_I8TOK: return launch_mode<ATTN_I8TOK>(a, l, st);
+    case ATTN_MX8: return launch_mode<ATTN_MX8>(a, l, st);
+    default: return launch_mode<ATTN_MX>(a, l, st);
   }
 }
 

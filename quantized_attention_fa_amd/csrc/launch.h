@@ -32,7 +32,9 @@ hipError_t launch_rot_fp8_block(const uint16_t* x, const uint16_t* rot, const fa
                                 uint16_t* debug_rotated, hipStream_t st);
 
 // ---- attention (attention.hip)
-enum AttnMode { ATTN_INT8 = 0, ATTN_FP8 = 1, ATTN_MX = 2 };
+// INT8 per-head; FP8 (per-token, token-block or per-head); MXFP4;
+// INT8 per-token; MXFP8.
+enum AttnMode { ATTN_INT8 = 0, ATTN_FP8 = 1, ATTN_MX = 2, ATTN_I8TOK = 3, ATTN_MX8 = 4 };
 
 struct AttnArgs {
   int mode;
@@ -43,8 +45,11 @@ struct AttnArgs {
   const void* k_scales;
   const void* v_codes;
   const void* v_scales;
-  int q_block;   // FP8: tokens per Q scale (1 = per token)
-  int kv_block;  // FP8: tokens per K/V scale (1 = per token)
+  // float scales of per-token, token-block and per-head scopes sit at
+  // b * sb + h * sh + token / block
+  int q_block;   // tokens per Q scale (1 = per token)
+  int kv_block;  // tokens per K/V scale (1 = per token)
+  int64_t q_sb, q_sh, kv_sb, kv_sh;
   float sm_scale;
   int causal;
   void* out;

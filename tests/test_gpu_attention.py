@@ -1,5 +1,7 @@
-"""GPU parity of the quantized attention: the HIP output (fp32) against the
-oracle run on the same quantized codes - relative Frobenius <= 1e-3 and
+"""GPU parity of the quantized attention in every FA mode (INT8 / FP8
+per-head, INT8 / FP8 per-token, MXFP4 / MXFP8 per-block, rotate + FP8 token
+blocks): the HIP output (fp32) against the oracle run on the same quantized
+codes - relative Frobenius <= 1e-3 and
 max |error| <= 2e-3 + tie allowance - on multi-tile shapes with ragged tails,
 causal and not, and at the full workload sizes on sampled query rows.  The
 bf16 output must be the round-to-nearest-even of the fp32 output, bit for
@@ -28,6 +30,14 @@ SMALL = [
     (4, (1, 2, 300, 128), True),
     (5, (1, 2, 300, 128), False),
     (5, (1, 2, 640, 128), True),
+    (6, (1, 2, 300, 128), True),
+    (6, (1, 2, 257, 64), False),
+    (7, (1, 2, 300, 128), False),
+    (7, (1, 2, 257, 64), False),
+    (7, (1, 2, 384, 128), True),
+    (8, (1, 2, 300, 128), False),
+    (8, (1, 2, 256, 64), False),
+    (8, (1, 2, 300, 128), True),
 ]
 
 
@@ -51,7 +61,8 @@ def test_attention_custom_scale_and_determinism():
     check_attention(a, oracle_attention(run, sm_scale=0.05), "sm_scale 0.05")
 
 
-@pytest.mark.parametrize("cfg,rows_per_bh", [(1, None), (2, 24), (3, 8), (4, 24), (5, 8)])
+@pytest.mark.parametrize("cfg,rows_per_bh", [(1, None), (2, 24), (3, 8), (4, 24), (5, 8), (6, 24), (7, 8),
+                                             (8, 24)])
 def test_full_size_attention(cfg, rows_per_bh):
     w = make_inputs(cfg)
     run = GpuRun(w)
