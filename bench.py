@@ -27,10 +27,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized-attention TFLOPS/TOPS (% MFMA peak) + quantize GB/s, 1 MI355X"
 PEAK_HBM_GBS = 8000.0
-PEAK_TOPS = {"int8_head": 5000.0, "fp8_token": 5000.0, "rot_fp8_block": 5000.0, "mxfp4": 10100.0}
-DTYPE = {"int8_head": "int8", "fp8_token": "fp8_e4m3", "rot_fp8_block": "fp8_e4m3", "mxfp4": "mxfp4"}
+PEAK_TOPS = {"int8_head": 5000.0, "fp8_token": 5000.0, "rot_fp8_block": 5000.0, "mxfp4": 10100.0,
+             "fp8_head": 5000.0, "int8_token": 5000.0, "mxfp8": 5000.0}
+DTYPE = {"int8_head": "int8", "fp8_token": "fp8_e4m3", "rot_fp8_block": "fp8_e4m3", "mxfp4": "mxfp4",
+         "fp8_head": "fp8_e4m3", "int8_token": "int8", "mxfp8": "mxfp8"}
 MODE_TEXT = {"int8_head": "INT8 per-head static", "fp8_token": "FP8 E4M3 per-token dynamic",
-             "mxfp4": "MXFP4 per-32 block dynamic", "rot_fp8_block": "rotate + FP8 E4M3 token-block"}
+             "mxfp4": "MXFP4 per-32 block dynamic", "rot_fp8_block": "rotate + FP8 E4M3 token-block",
+             "fp8_head": "FP8 E4M3 per-head static", "int8_token": "INT8 per-token dynamic",
+             "mxfp8": "MXFP8 per-32 block dynamic"}
+P_RULE = {"int8_head": "int8", "fp8_token": "fp8", "mxfp4": "mxfp4", "rot_fp8_block": "fp8",
+          "fp8_head": "fp8", "int8_token": "int8", "mxfp8": "mxfp8"}
+STATIC = {"int8_head": "int8", "fp8_head": "fp8_e4m3"}  # per-head static modes -> scale dtype
 
 
 def attention_ops(shape, causal):
@@ -45,12 +52,14 @@ def quantize_bytes(w):
     n = B * H * S * D
     inb = 4 if w.spec["dtype"] == "f32" else 2
     mode = w.spec["mode"]
-    if mode == "int8_head":
+    if mode in STATIC:
         return 3 * (n * inb + n + H * 4)
-    if mode == "fp8_token":
+    if mode in ("fp8_token", "int8_token"):
         return 3 * (n * inb + n + B * H * S * 4)
     if mode == "mxfp4":
         return 3 * (n * inb + n // 2 + n // 32)
+    if mode == "mxfp8":
+        return 3 * (n * inb + n + n // 32)
     tot = 0
     for bt in (w.spec["q_block"], w.spec["kv_block"], w.spec["kv_block"]):
         tot += n * inb + n + B * H * (-(-S // bt)) * 4
@@ -67,22 +76,24 @@ def make_step(w, dev):
     rot = w.rot.to(dev) if w.rot is not None else None
     cfgs, statics, outs = [], [None] * 3, []
     for br in range(3):
-        if mode == "int8_head":
-            cfg = faq.QConfig("int8", "per_head")
+        if mode in STATIC:
+            cfg = faq.QConfig(STATIC[mode], "per_head")
             amax = torch.zeros(w.shape[1], dtype=torch.float32, device=dev)
             for c in w.calib[br]:
                 faq.fa_quant_calibrate(c.to(dev), amax)
-            statics[br] = faq.fa_quant_scales_from_amax(amax, "int8")
+            statics[br] = faq.fa_quant_scales_from_amax(amax, STATIC[mode])
         elif mode == "fp8_token":
             cfg = faq.QConfig("fp8_e4m3", "per_token")
-        elif mode == "mxfp4":
-            cfg = faq.QConfig("mxfp4", "per_block")
+        elif mode == "int8_token":
+            cfg = faq.QConfig("int8", "per_token")
+        elif mode in ("mxfp4", "mxfp8"):
+            cfg = faq.QConfig(mode, "per_block")
         else:
             cfg = faq.QConfig("fp8_e4m3", "per_token_block",
                               block_tokens=w.spec["q_block"] if br == 0 else w.spec["kv_block"])
         cfgs.append(cfg)
         qt = faq.fa_quantize(xs[br], cfg, static_scale=statics[br], rot=rot if br < 2 else None)
-        if mode == "int8_head":
+        if mode in STATIC:
             qt.scales = statics[br]  # per-head scales are used in place
         outs.append(qt)
     ws = torch.empty(max(faq.fa_quant_attention_workspace_bytes(*outs), 1), dtype=torch.uint8, device=dev)
@@ -116,7 +127,7 @@ def cpu_baseline(w, budget_s=20.0):
     B, H, S, D = w.shape
     mode = w.spec["mode"]
     causal = w.spec["causal"]
-    rule = {"int8_head": "int8", "fp8_token": "fp8", "mxfp4": "mxfp4", "rot_fp8_block": "fp8"}[mode]
+    rule = P_RULE[mode]
     t0 = time.perf_counter()
     ops = 0
     heads = 0
@@ -130,22 +141,33 @@ def cpu_baseline(w, budget_s=20.0):
             break
         x = [t[0:1, h:h + 1].to(torch.float32).numpy() for t in (w.q, w.k, w.v)]
         vs = None
-        if mode == "int8_head":
+        if mode in STATIC:
             deq = []
             for br in range(3):
                 amax = None
                 for c in w.calib[br]:
                     amax = OQ.calibrate_amax(c[:, h:h + 1].to(torch.float32).numpy(), amax)
-                s = OQ.int8_scales(amax)
-                deq.append(OQ.dequantize_per_head(OQ.quantize_int8_per_head(x[br], s), s))
-        elif mode == "fp8_token":
+                if mode == "int8_head":
+                    s = OQ.int8_scales(amax)
+                    deq.append(OQ.dequantize_per_head(OQ.quantize_int8_per_head(x[br], s), s))
+                else:
+                    s = OQ.fp8_scales(amax)
+                    deq.append(OQ.dequantize_per_head(OQ.quantize_fp8_per_head(x[br], s), s, F.e4m3_decode))
+                vs = np.full((1, 1, S), s[0])
+        elif mode in ("fp8_token", "int8_token"):
             deq = []
             for br in range(3):
-                c, s = OQ.quantize_fp8_per_token(x[br])
-                deq.append(OQ.dequantize_per_token(c, s, F.e4m3_decode))
+                if mode == "fp8_token":
+                    c, s = OQ.quantize_fp8_per_token(x[br])
+                    deq.append(OQ.dequantize_per_token(c, s, F.e4m3_decode))
+                else:
+                    c, s = OQ.quantize_int8_per_token(x[br])
+                    deq.append(OQ.dequantize_per_token(c, s, lambda a: a.astype(np.float64)))
                 vs = s
         elif mode == "mxfp4":
             deq = [OQ.dequantize_mxfp4(*OQ.quantize_mxfp4(x[br])) for br in range(3)]
+        elif mode == "mxfp8":
+            deq = [OQ.dequantize_mxfp8(*OQ.quantize_mxfp8(x[br])) for br in range(3)]
         else:
             R = w.rot.to(torch.float32).numpy()
             deq = []
@@ -207,7 +229,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, the metric's workload)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload 1..8 (default 2, the metric's workload; 6-8 are the sibling FA modes)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -266,7 +289,7 @@ def main():
     line = {
         "metric": METRIC,
         "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
-        "unit": "TOPS" if mode == "int8_head" else "TFLOPS",
+        "unit": "TOPS" if DTYPE[mode] == "int8" else "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -280,7 +303,7 @@ def main():
                    "causal": w.spec["causal"], "input_dtype": w.spec["dtype"]},
         "roofline": {"bound": "mfma", "achieved": round(att_tops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(att_tops / peak, 4), "traffic": recorded_traffic(w.spec["name"]),
-                     "kernel": "fa_quant_attention: k_prep_v (V re-layout) + k_attn (fused attention)",
+                     "kernel": "fa_quant_attention: k_prep (V / K re-layout) + k_attn (fused attention)",
                      "attention_source": source_digest(),
                      "ops_per_launch": ops, "ms_per_launch": round(att_ms, 4)},
         "quantize": {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -58,6 +58,21 @@ def test_size_queries():
     assert lib.fa_quant_scales_bytes(B(c), B(shp)) == 2 * 3 * 300 * 4
     c = _cfg(_abi.FAQ_FP8_E4M3, _abi.FAQ_PER_TOKEN_BLOCK, 256)
     assert lib.fa_quant_scales_bytes(B(c), B(shp)) == 2 * 3 * 2 * 4
+    # sibling modes: FP8 per-head, INT8 per-token, MXFP8 per-block
+    c = _cfg(_abi.FAQ_FP8_E4M3, _abi.FAQ_PER_HEAD)
+    assert lib.fa_quant_codes_bytes(B(c), B(shp)) == 2 * 3 * 300 * 128
+    assert lib.fa_quant_scales_bytes(B(c), B(shp)) == 3 * 4
+    c = _cfg(_abi.FAQ_INT8, _abi.FAQ_PER_TOKEN)
+    assert lib.fa_quant_codes_bytes(B(c), B(shp)) == 2 * 3 * 300 * 128
+    assert lib.fa_quant_scales_bytes(B(c), B(shp)) == 2 * 3 * 300 * 4
+    c = _cfg(_abi.FAQ_MXFP8, _abi.FAQ_PER_BLOCK)
+    assert lib.fa_quant_codes_bytes(B(c), B(shp)) == 2 * 3 * 300 * 128
+    assert lib.fa_quant_scales_bytes(B(c), B(shp)) == 2 * 3 * 300 * 4
+    # combinations outside the mode list stay unsupported (size 0)
+    for dt, sc in [(_abi.FAQ_MXFP8, _abi.FAQ_PER_TOKEN), (_abi.FAQ_INT8, _abi.FAQ_PER_BLOCK),
+                   (_abi.FAQ_MXFP4, _abi.FAQ_PER_HEAD), (_abi.FAQ_INT8, _abi.FAQ_PER_TOKEN_BLOCK)]:
+        c = _cfg(dt, sc, 128)
+        assert lib.fa_quant_codes_bytes(B(c), B(shp)) == 0
     # unsupported combinations report 0
     assert lib.fa_quant_codes_bytes(B(_cfg(_abi.FAQ_INT8, _abi.FAQ_PER_BLOCK)), B(shp)) == 0
     assert lib.fa_quant_codes_bytes(B(c), B(_abi.faq_shape(1, 1, 4, 96))) == 0
