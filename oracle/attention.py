@@ -29,6 +29,8 @@ not by any value on the pages):
     - 'mxfp4': the MXFP4 quantizer applied along keys, 32-key groups aligned
                to absolute key index, masked keys counting as p = 0;
     - 'mxfp8': the same with the MXFP8 quantizer (E4M3 elements, emax 8);
+    - 'bf16':  V not quantized (an unconfigured branch, "fa3_quant 配置说明"
+               §2.3): the product takes P in bf16, Pq = bf16_rne(p);
     - 'exact': Pq = p (no quantization; reduces to softmax attention).
   C_it = sum_j Pq_ij vhat_j with vhat the exactly dequantized V.
 * Combine: M_i = max_t m_it; O_i = sum_t e^{m_it-M_i} C_it / sum_t e^{m_it-M_i} L_it.
@@ -88,6 +90,13 @@ def _quantize_p(p, rule, w=None, w_dec=None):
             near = (np.abs(u - mid) <= TIE_REL * u) & (u > 0)
             step = (hi - lo) / scale
         return pq, step, near
+    if rule == "bf16":
+        pq = F.bf16_round(p)
+        _, e = np.frexp(np.where(p > 0, p, 1.0))
+        ulp = np.ldexp(1.0, np.maximum(e, -125) - 8)  # bf16 spacing at p
+        frac = p / ulp - np.floor(p / ulp)
+        near = (np.abs(frac - 0.5) <= TIE_REL * p / ulp) & (p > 0)
+        return pq, ulp, near
     if rule in ("mxfp4", "mxfp8"):
         if rule == "mxfp4":
             enc, dec, nbr, emax, vmax = F.e2m1_encode, F.e2m1_decode, F.e2m1_neighbors, F.E2M1_EMAX, F.E2M1_MAX

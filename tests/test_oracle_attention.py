@@ -100,7 +100,16 @@ def test_two_key_hand_worked_mxfp8():
     assert o[2] == pytest.approx(0.375 / den, abs=1e-15)
 
 
-@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8"])
+def test_two_key_hand_worked_bf16():
+    # p = (1, e^-1); e^-1 = 1.4715177 * 2^-2, 7 fraction bits: 188.35 / 128
+    # -> 188 / 128 -> Pq1 = 0.3671875
+    o, _ = _two_key("bf16")
+    den = 1 + math.exp(-1)
+    assert o[1] == pytest.approx(1 / den, abs=1e-15)
+    assert o[2] == pytest.approx(0.3671875 / den, abs=1e-15)
+
+
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8", "bf16"])
 def test_equal_scores_give_mean_of_v(rule):
     g = np.random.default_rng(2)
     S, D = 300, 64
@@ -112,7 +121,7 @@ def test_equal_scores_give_mean_of_v(rule):
     assert np.allclose(o, v.mean(axis=2, keepdims=True), atol=1e-13)
 
 
-@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8", "exact"])
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8", "bf16", "exact"])
 def test_dominant_key(rule):
     g = np.random.default_rng(3)
     S, D = 260, 64
@@ -123,7 +132,7 @@ def test_dominant_key(rule):
     assert np.allclose(o[0, 0, 0], v[0, 0, 200], atol=1e-13)
 
 
-@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8"])
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8", "bf16"])
 def test_tile_local_max(rule):
     """Tile 0: one key with a large score; tile 1: 128 keys of one lower
     score.  With each tile's probabilities taken relative to its own max the
@@ -158,7 +167,7 @@ def test_sigma_is_per_tile(rule):
     assert np.allclose(o[0, 0, 0], v[0, 0].mean(axis=0), atol=1e-13)
 
 
-@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8"])
+@pytest.mark.parametrize("rule", ["int8", "fp8", "mxfp4", "mxfp8", "bf16"])
 def test_tile_order_invariance(rule):
     g = np.random.default_rng(6)
     S, D = 512, 64
@@ -176,7 +185,7 @@ def test_quantized_close_to_exact():
     g = np.random.default_rng(7)
     q, k, v = (g.standard_normal((1, 2, 256, 64)) for _ in range(3))
     ref = A.attention(q, k, v, "exact")
-    for rule, tol in [("int8", 0.05), ("fp8", 0.06), ("mxfp4", 0.25), ("mxfp8", 0.06)]:
+    for rule, tol in [("int8", 0.05), ("fp8", 0.06), ("mxfp4", 0.25), ("mxfp8", 0.06), ("bf16", 0.01)]:
         o = A.attention(q, k, v, rule, v_scale=np.ones((1, 2, 256)))
         err = np.linalg.norm(o - ref) / np.linalg.norm(ref)
         assert 1e-4 < err < tol, (rule, err)
@@ -210,3 +219,15 @@ def test_fp8_code_decided_in_fp32():
     o = A.attention(q, k, v, "fp8", v_scale=vs)[0, 0, 0]
     w = float(sv0) / float(sv1)
     assert o[1] == pytest.approx(64.0 / (448 * w) * float(sv0) * 448, rel=1e-12)
+
+
+def test_bf16_rule_is_one_rounding_of_p():
+    """Against torch's bf16 cast (an independent rounding): every quantized
+    probability is the bf16 value nearest to the exact p."""
+    g = np.random.default_rng(8)
+    p = np.exp(-np.abs(g.standard_normal((3, 2, 128))) * 4)
+    pq, step, near = A._quantize_p(p, "bf16")
+    ref = torch.from_numpy(p.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    # the float32 detour of the reference can only differ at exact ties
+    assert np.mean(pq == ref) > 0.999
+    assert np.all(np.abs(pq - p) <= step / 2 * (1 + 1e-12))
