@@ -22,7 +22,7 @@ from ._abi import (FAQ_FP8_E4M3, FAQ_INT8, FAQ_MXFP4, FAQ_MXFP8, FAQ_FLOAT, FAQ_
                    FAQ_PER_TOKEN, FAQ_PER_TOKEN_BLOCK, FAQ_T_BF16, FAQ_T_F32)
 
 __all__ = [
-    "QConfig", "QTensor", "FaQuantError", "resolve_fa3_config", "default_qconfig",
+    "QConfig", "QTensor", "FaQuantError", "resolve_fa3_config", "default_qconfig", "float_branch",
     "fa_quant_calibrate", "fa_quant_scales_from_amax", "fa_quantize",
     "fa_quant_attention", "fa_quant_attention_workspace_bytes",
     "fa_quant_codes_bytes", "fa_quant_scales_bytes", "fa_quant_status_string",
@@ -90,6 +90,16 @@ class QTensor:
     def to_c(self) -> _abi.faq_qtensor:
         return _abi.faq_qtensor(self.cfg.to_c(), _abi.faq_shape(*self.shape),
                                 self.codes.data_ptr(), self.scales.data_ptr())
+
+
+def float_branch(x: torch.Tensor) -> QTensor:
+    """An unquantized branch ("fa3_quant 配置说明" §2.3: a branch without a
+    configuration is not quantized): the bf16 tensor itself, passed to
+    fa_quant_attention as a QTensor of dtype "float" (no scales)."""
+    shape = _bnsd(x, "float_branch")
+    if x.dtype != torch.bfloat16:
+        raise FaQuantError(_abi.FAQ_ERR_UNSUPPORTED, "float_branch: unquantized branches are bf16")
+    return QTensor(QConfig("float", "per_head"), shape, x, torch.empty(0, dtype=torch.uint8, device=x.device))
 
 
 def fa_quant_status_string(status: int) -> str:

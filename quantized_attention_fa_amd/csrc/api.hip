@@ -210,46 +210,68 @@ static void scale_index(const faq_qconfig& c, const faq_shape& s, int* block, in
   }
 }
 
+static int qk_mode(const faq_qconfig& c) {
+  switch (c.dtype) {
+    case FAQ_FLOAT: return QK_BF;
+    case FAQ_INT8: return c.scope == FAQ_PER_HEAD ? QK_I8H : QK_I8T;
+    case FAQ_MXFP4: return QK_MX4;
+    case FAQ_MXFP8: return QK_MX8;
+    default: return c.scope == FAQ_PER_TOKEN ? QK_F8T : QK_F8C;  // per-head, 128/256-token blocks
+  }
+}
+
+static int pv_mode(const faq_qconfig& c) {
+  switch (c.dtype) {
+    case FAQ_FLOAT: return PV_BF;
+    case FAQ_INT8: return c.scope == FAQ_PER_HEAD ? PV_I8H : PV_I8T;
+    case FAQ_MXFP4: return PV_MX4;
+    case FAQ_MXFP8: return PV_MX8;
+    default: return c.scope == FAQ_PER_TOKEN ? PV_F8W : PV_F8C;
+  }
+}
+
+// Branch configurations for attention ("fa3_quant 配置说明" §2.3: each of
+// fa_q / fa_k / fa_v configured on its own, an unconfigured branch not
+// quantized - FAQ_FLOAT, bf16 values in `codes`).  Q and K share one
+// configuration (token blocks may differ in size) or are both unquantized;
+// V is either of their configuration or unquantized.
 static faq_status attn_check(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
-                             int* mode, const char* fn) {
+                             int* qk, int* pv, const char* fn) {
   if (!q || !k || !v) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL tensor");
   for (const faq_qtensor* t : {q, k, v}) {
-    const faq_status cs = check_cfg(&t->cfg);
-    if (cs != FAQ_OK) return fail(cs, fn, "qconfig");
+    if (t->cfg.dtype != FAQ_FLOAT) {
+      const faq_status cs = check_cfg(&t->cfg);
+      if (cs != FAQ_OK) return fail(cs, fn, "qconfig");
+    }
     if (!shape_ok(&t->shape)) return fail(FAQ_ERR_INVALID_ARG, fn, "shape");
     if (!d_supported(t->shape.D)) return fail(FAQ_ERR_UNSUPPORTED, fn, "head_dim must be 64 or 128");
   }
-  if (q->cfg.dtype != k->cfg.dtype || q->cfg.dtype != v->cfg.dtype || q->cfg.scope != k->cfg.scope ||
-      q->cfg.scope != v->cfg.scope)
-    return fail(FAQ_ERR_UNSUPPORTED, fn, "q, k and v must share one (dtype, scope)");
-  if (q->cfg.scope == FAQ_PER_TOKEN_BLOCK && k->cfg.block_tokens != v->cfg.block_tokens)
-    return fail(FAQ_ERR_UNSUPPORTED, fn, "k and v must share one block size");
+  if (q->cfg.dtype != k->cfg.dtype || (q->cfg.dtype != FAQ_FLOAT && q->cfg.scope != k->cfg.scope))
+    return fail(FAQ_ERR_UNSUPPORTED, fn, "q and k must share one (dtype, scope)");
+  *qk = qk_mode(k->cfg);
+  *pv = pv_mode(v->cfg);
+  if (!attn_pair_supported(*qk, *pv))
+    return fail(FAQ_ERR_UNSUPPORTED, fn, "v must share the (dtype, scope) of q and k, or be unquantized");
   if (q->shape.B != k->shape.B || q->shape.B != v->shape.B || q->shape.H != k->shape.H ||
       q->shape.H != v->shape.H || q->shape.D != k->shape.D || q->shape.D != v->shape.D ||
       k->shape.S != v->shape.S)
     return fail(FAQ_ERR_SHAPE, fn, "q/k/v shapes");
-  switch (q->cfg.dtype) {
-    case FAQ_INT8: *mode = q->cfg.scope == FAQ_PER_HEAD ? ATTN_INT8 : ATTN_I8TOK; break;
-    case FAQ_MXFP4: *mode = ATTN_MX; break;
-    case FAQ_MXFP8: *mode = ATTN_MX8; break;
-    default: *mode = ATTN_FP8; break;
-  }
   return FAQ_OK;
 }
 
 size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtensor* k,
                                           const faq_qtensor* v) {
-  int mode;
-  if (attn_check(q, k, v, &mode, "fa_quant_attention_workspace_bytes") != FAQ_OK) return 0;
-  return attn_workspace_bytes(mode, k->shape.B, k->shape.H, k->shape.S, k->shape.D);
+  int qk, pv;
+  if (attn_check(q, k, v, &qk, &pv, "fa_quant_attention_workspace_bytes") != FAQ_OK) return 0;
+  return attn_workspace_bytes(qk, pv, k->shape.B, k->shape.H, k->shape.S, k->shape.D);
 }
 
 faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
                               float sm_scale, int32_t causal, void* out, int32_t out_dtype,
                               void* workspace, size_t workspace_bytes, void* stream) {
   static const char* fn = "fa_quant_attention";
-  int mode;
-  const faq_status cs = attn_check(q, k, v, &mode, fn);
+  int qk, pv;
+  const faq_status cs = attn_check(q, k, v, &qk, &pv, fn);
   if (cs != FAQ_OK) return cs;
   if (out_dtype != FAQ_T_F32 && out_dtype != FAQ_T_BF16) return fail(FAQ_ERR_INVALID_ARG, fn, "out_dtype");
   if (causal != 0 && causal != 1) return fail(FAQ_ERR_INVALID_ARG, fn, "causal must be 0 or 1");
@@ -258,18 +280,21 @@ faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const 
   const int64_t B = q->shape.B, H = q->shape.H, Sq = q->shape.S, Skv = k->shape.S, D = q->shape.D;
   if (B * H * Sq == 0) return FAQ_OK;
   if (Skv == 0) return fail(FAQ_ERR_SHAPE, fn, "no keys");
-  if (!out || !q->codes || !q->scales || !k->codes || !k->scales || !v->codes || !v->scales)
-    return fail(FAQ_ERR_INVALID_ARG, fn, "NULL pointer");
-  const size_t need = attn_workspace_bytes(mode, B, H, Skv, D);
+  if (!out || !q->codes || !k->codes || !v->codes) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL pointer");
+  for (const faq_qtensor* t : {q, k, v})
+    if (t->cfg.dtype != FAQ_FLOAT && !t->scales) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL scales");
+  const size_t need = attn_workspace_bytes(qk, pv, B, H, Skv, D);
   if (workspace_bytes < need || !workspace) return fail(FAQ_ERR_WORKSPACE, fn, "workspace");
   AttnArgs a{};
-  a.mode = mode;
+  a.qk = qk;
+  a.pv = pv;
   a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv; a.D = D;
   a.q_codes = q->codes; a.q_scales = q->scales;
   a.k_codes = k->codes; a.k_scales = k->scales;
   a.v_codes = v->codes; a.v_scales = v->scales;
   scale_index(q->cfg, q->shape, &a.q_block, &a.q_sb, &a.q_sh);
-  scale_index(k->cfg, k->shape, &a.kv_block, &a.kv_sb, &a.kv_sh);
+  scale_index(k->cfg, k->shape, &a.k_block, &a.k_sb, &a.k_sh);
+  scale_index(v->cfg, v->shape, &a.v_block, &a.v_sb, &a.v_sh);
   a.sm_scale = sm_scale == 0.0f ? 1.0f / sqrtf((float)D) : sm_scale;
   a.causal = causal;
   a.out = out;

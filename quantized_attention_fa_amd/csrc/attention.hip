@@ -1,27 +1,35 @@
 // Flash-style attention on quantized Q/K/V for gfx950.
 //
-// Both products take the low-bit operands ("FA 量化" page, 概述) on MFMA:
-//   INT8 per-head  v_mfma_i32_32x32x32_i8 for Q K^T and P V (int8 P):
-//                  exact int32 accumulation.
-//   FP8 E4M3       v_mfma_f32_32x32x16_bf16 on the exact bf16 images of the
-//                  E4M3 codes (Q, K, V and the E4M3 probabilities).  The
-//                  f8f6f4 MFMA sums each group of products aligned to the
-//                  group's largest with about 12 fractional bits, so score
-//                  errors reach ~1e-4 of amax_q * amax_k and move probability
-//                  codes; the bf16 MFMA accumulates these exact products at
-//                  fp32 precision.
-//   MXFP4          Q K^T on v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1
-//                  operands and their E8M0 block exponents as MFMA scales
-//                  (exact: products within a block span < 2^8); P V on the
-//                  bf16 MFMA with P = E2M1 * 2^E and V dequantized exactly.
-//   INT8 per-token int8 MFMA for both products as INT8 per-head; the per-key
-//                  K scale multiplies the exact integer scores, the per-key
-//                  V scale is folded into the int8 probabilities (as FP8).
-//   MXFP8          the bf16 MFMA path of FP8: each Q/K row is widened to
-//                  bf16 relative to its largest block exponent (exact), the
-//                  row exponents scale the scores; V is dequantized exactly
-//                  to bf16; P is MX-quantized with E4M3 elements.
-// FP8 per-head static runs the FP8 path with one scale per tile.
+// Both products take the low-bit operands ("FA 量化" page, 概述) on MFMA.
+// Each branch is configured on its own ("fa3_quant 配置说明" page, §2.3
+// FA3AttentionDetails; an unconfigured branch is not quantized), so the
+// score product Q K^T follows the (shared) configuration of Q and K and the
+// value product P V follows V's:
+//
+//   scores, by the Q/K configuration
+//     INT8 per-head   v_mfma_i32_32x32x32_i8, exact int32 scores
+//     INT8 per-token  the same; the per-key K scale multiplies the scores
+//     FP8 E4M3        v_mfma_f32_32x32x16_bf16 on the exact bf16 images of
+//                     the E4M3 codes.  The f8f6f4 MFMA sums each group of
+//                     products aligned to the group's largest with about 12
+//                     fractional bits, so score errors reach ~1e-4 of
+//                     amax_q * amax_k and move probability codes; the bf16
+//                     MFMA accumulates these exact products at fp32 precision.
+//     MXFP4           v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands and
+//                     their E8M0 block exponents as MFMA scales (exact:
+//                     products within a block span < 2^8)
+//     MXFP8           the bf16 MFMA; each row widened relative to its
+//                     largest block exponent (exact), the row exponents
+//                     scale the scores
+//     unquantized     the bf16 MFMA on the bf16 inputs
+//   values, by V's configuration, with the probabilities P quantized to
+//   V's type
+//     INT8            int8 P, v_mfma_i32_32x32x32_i8, exact int32 sums
+//     FP8 E4M3        E4M3 P on the bf16 MFMA (exact images)
+//     MXFP4 / MXFP8   MX-quantized P on the bf16 MFMA, V exact in bf16 (V's
+//                     exponents run along D, not along the keys the MFMA
+//                     sums over)
+//     unquantized     bf16 P on the bf16 MFMA
 // The output is dequantized to bf16 (or fp32) ("量化" page, FA量化 / FP8
 // Attention).
 //
@@ -29,8 +37,8 @@
 // keys are cut into 128-key tiles aligned to absolute key index; per query
 // row and tile, m = max score, p = exp(s - m) is quantized with a static
 // scale relative to that tile maximum (int8: rne(127 p w_j); E4M3: 448 p w_j
-// with w_j = s_v,j / max_tile s_v (1 when V has one scale per tile); MXFP4 /
-// MXFP8: the MX quantizer over 32-key groups),
+// with w_j = s_v,j / max_tile s_v, 1 when V has one scale per tile; MXFP4 /
+// MXFP8: the MX quantizer over 32-key groups; unquantized V: bf16 of p),
 // the tile sum L uses unquantized p, and tiles combine with the usual
 // running-max rescale, O = sum_t e^{m_t-M} C_t / sum_t e^{m_t-M} L_t.
 //
@@ -43,8 +51,8 @@
 // the tile, i.e. two whole 32-key MX groups.  The row max and sum need one
 // cross-lane step, and the lane's probabilities are already the B operand of
 // O^T = V^T P^T.  V^T comes from a per-call workspace with its key columns in
-// the order the lanes hold their probabilities (FP8: K and V^T widened there
-// to their exact bf16 images).
+// the order the lanes hold their probabilities (FP8 / MXFP8 K widened there
+// to bf16 too).
 //
 // LDS tiles are chunk-major: 16-byte column c of every row, then column c+1.
 // The 16 lanes that share an LDS cycle read 16 distinct rows of one column,
@@ -97,16 +105,10 @@ FAQ_DEV int vt_key_bf16(int p) { return 64 * ((p >> 3) & 1) + 16 * (p >> 5) + 8 
 FAQ_DEV int vt_key_i8(int p) { return 64 * ((p >> 4) & 1) + 16 * (p >> 5) + (p & 15); }
 
 // Two E4M3 bytes (the low half-word of `w`, or the high one when HI) -> two
-// bf16, exactly.
+// bf16, times the power of two `sc` (exact while the values stay in bf16's
+// normal range).
 template <bool HI>
-FAQ_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
-}
-
-// The same times the power of two `sc` (exact while the products stay in
-// bf16's normal range).
-template <bool HI>
-FAQ_DEV uint32_t e4m3x2_to_bf16x2_scaled(uint32_t w, float sc) {
+FAQ_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w, float sc = 1.0f) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, sc, HI));
 }
 
@@ -123,117 +125,135 @@ FAQ_DEV float halves_sum(float x) {
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
-// Geometry of the LDS tiles.
-template <int MODE, int D>
+// Geometry of the LDS tiles, from the score mode QK and the value mode PV.
+template <int QK, int PV, int D>
 struct Cfg {
-  static constexpr bool I8 = MODE == ATTN_INT8 || MODE == ATTN_I8TOK;  // int8 MFMA for both products
-  static constexpr bool BFK = MODE == ATTN_FP8 || MODE == ATTN_MX8;    // bf16 K image, bf16 MFMA
-  static constexpr bool MXP = MODE == ATTN_MX || MODE == ATTN_MX8;     // MX probability groups
-  static constexpr bool VW = MODE == ATTN_FP8 || MODE == ATTN_I8TOK;   // per-key V scale folded into P
-  static constexpr int KROW = I8 ? D : (BFK ? 2 * D : D / 2);  // bytes of a K row
+  static constexpr bool QI8 = QK == QK_I8H || QK == QK_I8T;                                 // int8 score MFMA
+  static constexpr bool QBF = QK == QK_F8T || QK == QK_F8C || QK == QK_MX8 || QK == QK_BF;  // bf16 score MFMA
+  static constexpr bool QIMG = QK == QK_F8T || QK == QK_F8C || QK == QK_MX8;  // K widened in the workspace
+  static constexpr bool KSC = QK == QK_I8T || QK == QK_F8T || QK == QK_F8C || QK == QK_MX8;  // per-key K floats
+  static constexpr bool PI8 = PV == PV_I8H || PV == PV_I8T;  // int8 value MFMA
+  static constexpr bool PMX = PV == PV_MX4 || PV == PV_MX8;  // MX probability groups
+  static constexpr bool PVW = PV == PV_I8T || PV == PV_F8W;  // per-key V scale folded into P
+  static constexpr bool SIG = PVW || PV == PV_F8C;            // sigma_t per tile
+  static constexpr int KROW = QI8 ? D : (QBF ? 2 * D : D / 2);  // bytes of a K row in LDS
   static constexpr int KBYTES = BN * KROW;
   static constexpr int NB = D / 32;  // MX blocks per row
   // per-key extras: after the K tile the K scales (floats; MXFP8: 2^ of
   // the row exponent) or the MXFP4 K block exponents; after the V^T tile
   // the multipliers qmax w_j (floats), which the probabilities read after
   // the K buffer is refilled
-  static constexpr int XKBYTES = MODE == ATTN_MX ? BN * NB : (MODE == ATTN_INT8 ? 0 : BN * 4);
-  static constexpr int XVBYTES = VW ? BN * 4 : 0;
+  static constexpr int XKBYTES = QK == QK_MX4 ? BN * NB : (KSC ? BN * 4 : 0);
+  static constexpr int XVBYTES = PVW ? BN * 4 : 0;
   static constexpr int XBYTES = XKBYTES + XVBYTES;  // per tile in the workspace
-  static constexpr int VROW = I8 ? BN : 2 * BN;     // bytes of a V^T row
+  static constexpr int VROW = PI8 ? BN : 2 * BN;    // bytes of a V^T row
   static constexpr int VBYTES = D * VROW;
-  static constexpr int KS = I8 ? D / 32 : (BFK ? D / 16 : D / 64);  // QK k-steps
-  static constexpr int DB = D / 32;                                 // 32-channel output blocks
+  static constexpr int KS = QI8 ? D / 32 : (QBF ? D / 16 : D / 64);  // score k-steps
+  static constexpr int DB = D / 32;                                  // 32-channel output blocks
 };
 
 // ------------------------------------------------------------------------
 // Workspace layout (per (b,h), per 128-key tile t):
 //   vt  : V^T of the tile as its LDS image (chunk-major, columns in the lane
-//         key order): INT8 codes (1 byte) or, for FP8, MXFP4 and MXFP8, the
-//         values in bf16 (2 bytes; E4M3 codes, exact values for MX)
-//   kb  : FP8 / MXFP8: K widened to bf16 as its LDS image (rows past the
-//         end are 0; MXFP8 relative to the row's largest block exponent)
-//   aux : FP8 / INT8 per-token: 128 K scales then 128 multipliers qmax w_j
-//         (floats); MXFP8: 128 K row scales 2^(E_row); MXFP4: the K block
-//         exponents, 128 rows x D/32 bytes (127 past the end)
-//   sig : FP8 / INT8 per-token: sigma_t = max over the tile's keys of s_v,j
+//         key order): INT8 codes (1 byte) or bf16 values (2 bytes: E4M3
+//         codes, exact MX values, or the unquantized V)
+//   kb  : FP8 / MXFP8 scores: K widened to bf16 as its LDS image (rows past
+//         the end are 0; MXFP8 relative to the row's largest block exponent)
+//   aux : K extras (K scales; MXFP8 row scales 2^(E_row); MXFP4 K block
+//         exponents, 128 rows x D/32 bytes, 127 past the end), then V
+//         extras (the multipliers qmax w_j)
+//   sig : sigma_t = max over the tile's keys of s_v,j (FP8 / INT8 per-token
+//         and FP8 with one V scale per tile)
 // ------------------------------------------------------------------------
 struct WsLayout {
   size_t vt_off, kb_off, aux_off, sig_off, total;
 };
 
-inline WsLayout ws_layout(int mode, int64_t B, int64_t H, int64_t Skv, int64_t D) {
+inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Skv, int64_t D) {
   const int64_t nt = (Skv + BN - 1) / BN;
   const size_t tiles = (size_t)(B * H * nt);
-  const bool i8 = mode == ATTN_INT8 || mode == ATTN_I8TOK;
-  const bool bfk = mode == ATTN_FP8 || mode == ATTN_MX8;
-  const bool vw = mode == ATTN_FP8 || mode == ATTN_I8TOK;
-  const size_t xk = mode == ATTN_MX ? BN * (D / 32) : (mode == ATTN_INT8 ? 0 : BN * 4);
-  const size_t xv = vw ? BN * 4 : 0;
+  const bool pi8 = pv == PV_I8H || pv == PV_I8T;
+  const bool qimg = qk == QK_F8T || qk == QK_F8C || qk == QK_MX8;
+  const bool ksc = qk == QK_I8T || qimg;
+  const bool pvw = pv == PV_I8T || pv == PV_F8W;
+  const bool sig = pvw || pv == PV_F8C;
+  const size_t xk = qk == QK_MX4 ? BN * (D / 32) : (ksc ? BN * 4 : 0);
+  const size_t xv = pvw ? BN * 4 : 0;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WsLayout l{};
   l.vt_off = 0;
-  l.kb_off = up(tiles * D * BN * (i8 ? 1 : 2));
-  l.aux_off = l.kb_off + up(bfk ? tiles * BN * D * 2 : 0);
+  l.kb_off = up(tiles * D * BN * (pi8 ? 1 : 2));
+  l.aux_off = l.kb_off + up(qimg ? tiles * BN * D * 2 : 0);
   l.sig_off = l.aux_off + up(tiles * (xk + xv));
-  l.total = l.sig_off + up(vw ? tiles * 4 : 0);
+  l.total = l.sig_off + up(sig ? tiles * 4 : 0);
   return l;
 }
 
 // ------------------------------------------------------------------------
 // Per-call re-layout.  grid = (tiles, B*H), 256 threads; one 128-key tile.
-//   INT8 per-head : the V^T image (codes).
-//   INT8 per-token: the V^T image (codes), the per-key K scales and
-//                   127 w_j, and sigma_t.
-//   FP8           : the K and V^T images widened to bf16, the per-key K
-//                   scales and 448 w_j, and sigma_t.
-//   MXFP8         : the K image (each row relative to its largest block
-//                   exponent) with the row scales 2^(E_row), and the V^T
-//                   image as the exact bf16 values.
-// Scales of K and V are read at b * sb + h * sh + key / blk (per-token:
-// blk 1; token blocks: blk tokens; per-head: sb 0, sh 1, one block).
+//   K (by QK): FP8 / MXFP8 the bf16 image (MXFP8 rows relative to their
+//              largest block exponent); the per-key K scales (INT8 / FP8
+//              per-token, FP8 one-per-tile, MXFP8 2^(E_row)); MXFP4 the K
+//              block exponents.
+//   V (by PV): the V^T image: INT8 codes, E4M3 codes widened to bf16, MX
+//              values exact in bf16, or the unquantized bf16 values; the
+//              per-key multipliers qmax w_j and sigma_t.
+// Float scales of K and V are read at b * sb + h * sh + key / blk
+// (per-token: blk 1; token blocks: blk tokens; per-head: sb 0, sh 1, one
+// block).
 // ------------------------------------------------------------------------
 struct PrepArgs {
   const uint8_t* k;
   const void* ks;
   const uint8_t* v;
   const void* vs;
-  int64_t H, Skv, nt, sb, sh;
-  int blk;
+  int64_t H, Skv, nt, ksb, ksh, vsb, vsh;
+  int kblk, vblk;
   uint8_t* vt;
   uint8_t* kb;
-  float* aux;
+  uint8_t* aux;
   float* sig;
 };
 
-template <int MODE, int D>
+template <int QK, int PV, int D>
 __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
-  using C = Cfg<MODE, D>;
+  using C = Cfg<QK, PV, D>;
   constexpr int NB = D / 32;
-  constexpr bool MX8 = MODE == ATTN_MX8;
-  __shared__ uint8_t tile[BN][D + 4];
-  __shared__ uint8_t vex[MX8 ? BN : 1][NB];
+  // bytes of a V row: packed E2M1, bf16, or one-byte codes
+  constexpr int VR = PV == PV_MX4 ? D / 2 : (PV == PV_BF ? 2 * D : D);
+  constexpr bool VEX = PV == PV_MX4 || PV == PV_MX8;
+  __shared__ uint8_t tile[BN][VR + 4];
+  __shared__ uint8_t vex[VEX ? BN : 1][NB];
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t k0 = (int64_t)t * BN;
   const int64_t tile_id = bh * a.nt + t;
-  const int64_t sbase = (bh / a.H) * a.sb + (bh % a.H) * a.sh;  // scale index of key 0 of the head
-  constexpr int CPR = D / 16;  // 16-byte chunks per key row of codes
-  for (int c = threadIdx.x; c < BN * CPR; c += 256) {
-    const int kl = c / CPR, cc = c % CPR;
-    const bool ok = k0 + kl < a.Skv;
+  uint8_t* auxt = a.aux + tile_id * C::XBYTES;
+  // V rows -> LDS
+  for (int c = threadIdx.x; c < BN * (VR / 16); c += 256) {
+    const int kl = c / (VR / 16), cc = c % (VR / 16);
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (ok) val = *reinterpret_cast<const uint4*>(a.v + (bh * a.Skv + k0 + kl) * D + cc * 16);
+    if (k0 + kl < a.Skv) val = *reinterpret_cast<const uint4*>(a.v + (bh * a.Skv + k0 + kl) * VR + cc * 16);
     uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[kl][cc * 16]);
     dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
-    if (C::BFK) {
-      // K row chunk widened to bf16: columns 2 cc and 2 cc + 1 of the image
+  }
+  if (VEX) {
+    for (int c = threadIdx.x; c < BN * NB; c += 256) {
+      const int kl = c / NB, b = c % NB;
+      vex[kl][b] = k0 + kl < a.Skv ? reinterpret_cast<const uint8_t*>(a.vs)[(bh * a.Skv + k0 + kl) * NB + b]
+                                   : (uint8_t)127;
+    }
+  }
+  // K image, 16 codes (two 16-byte image columns) per item
+  if (C::QIMG) {
+    for (int c = threadIdx.x; c < BN * (D / 16); c += 256) {
+      const int kl = c / (D / 16), cc = c % (D / 16);
       uint4 kv = make_uint4(0, 0, 0, 0);
       float sc = 1.0f;
-      if (ok) {
+      if (k0 + kl < a.Skv) {
         kv = *reinterpret_cast<const uint4*>(a.k + (bh * a.Skv + k0 + kl) * D + cc * 16);
-        if (MX8) {
+        if (QK == QK_MX8) {
           const uint8_t* ke = reinterpret_cast<const uint8_t*>(a.ks) + (bh * a.Skv + k0 + kl) * NB;
           int emax = 0;
 #pragma unroll
@@ -243,43 +263,46 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
       }
       uint8_t* img = a.kb + tile_id * C::KBYTES + kslot(kl) * 16;
       *reinterpret_cast<uint4*>(img + (2 * cc) * BN * 16) =
-          make_uint4(e4m3x2_to_bf16x2_scaled<false>(kv.x, sc), e4m3x2_to_bf16x2_scaled<true>(kv.x, sc),
-                     e4m3x2_to_bf16x2_scaled<false>(kv.y, sc), e4m3x2_to_bf16x2_scaled<true>(kv.y, sc));
+          make_uint4(e4m3x2_to_bf16x2<false>(kv.x, sc), e4m3x2_to_bf16x2<true>(kv.x, sc),
+                     e4m3x2_to_bf16x2<false>(kv.y, sc), e4m3x2_to_bf16x2<true>(kv.y, sc));
       *reinterpret_cast<uint4*>(img + (2 * cc + 1) * BN * 16) =
-          make_uint4(e4m3x2_to_bf16x2_scaled<false>(kv.z, sc), e4m3x2_to_bf16x2_scaled<true>(kv.z, sc),
-                     e4m3x2_to_bf16x2_scaled<false>(kv.w, sc), e4m3x2_to_bf16x2_scaled<true>(kv.w, sc));
+          make_uint4(e4m3x2_to_bf16x2<false>(kv.z, sc), e4m3x2_to_bf16x2<true>(kv.z, sc),
+                     e4m3x2_to_bf16x2<false>(kv.w, sc), e4m3x2_to_bf16x2<true>(kv.w, sc));
     }
   }
-  if (MX8) {
+  // K extras
+  if (QK == QK_MX4) {
     for (int c = threadIdx.x; c < BN * NB; c += 256) {
       const int kl = c / NB, b = c % NB;
-      vex[kl][b] = k0 + kl < a.Skv ? reinterpret_cast<const uint8_t*>(a.vs)[(bh * a.Skv + k0 + kl) * NB + b]
-                                   : (uint8_t)127;
+      auxt[c] = k0 + kl < a.Skv ? reinterpret_cast<const uint8_t*>(a.ks)[(bh * a.Skv + k0 + kl) * NB + b]
+                                : (uint8_t)127;
     }
   }
+  const int kl = threadIdx.x;
+  if (C::KSC && kl < BN) {
+    float sk = 0.0f;
+    if (k0 + kl < a.Skv) {
+      if (QK == QK_MX8) {
+        const uint8_t* ke = reinterpret_cast<const uint8_t*>(a.ks) + (bh * a.Skv + k0 + kl) * NB;
+        int emax = 0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) emax = max(emax, (int)ke[b]);
+        sk = __builtin_amdgcn_ldexpf(1.0f, emax - 127);
+      } else {
+        sk = reinterpret_cast<const float*>(a.ks)[(bh / a.H) * a.ksb + (bh % a.H) * a.ksh + (k0 + kl) / a.kblk];
+      }
+    }
+    reinterpret_cast<float*>(auxt)[kl] = sk;
+  }
   __syncthreads();
+  // V^T image.  item i: column c = i / D, row d = i % D (consecutive
+  // threads write consecutive 16-byte slots of one column)
   uint8_t* img = a.vt + tile_id * C::VBYTES;
   constexpr int VCOLS = C::VROW / 16;
-  // item i: column c = i / D, row d = i % D (consecutive threads write
-  // consecutive 16-byte slots of one column)
   for (int i = threadIdx.x; i < VCOLS * D; i += 256) {
     const int c = i / D, d = i % D;
     uint32_t w[4];
-    if (!C::I8) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int key0 = vt_key_bf16(8 * c + 2 * q), key1 = vt_key_bf16(8 * c + 2 * q + 1);
-        const uint32_t pair = (uint32_t)tile[key0][d] | ((uint32_t)tile[key1][d] << 8);
-        w[q] = e4m3x2_to_bf16x2<false>(pair);
-        if (MX8) {
-          // the exact value code * 2^(E - 127), rounded to bf16 (exact
-          // within bf16's normal range)
-          const float f0 = __builtin_amdgcn_ldexpf(bf16_lo(w[q]), (int)vex[key0][d >> 5] - 127);
-          const float f1 = __builtin_amdgcn_ldexpf(bf16_hi(w[q]), (int)vex[key1][d >> 5] - 127);
-          w[q] = f32_to_bf16_bits(f0) | (f32_to_bf16_bits(f1) << 16);
-        }
-      }
-    } else {
+    if (C::PI8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t acc = 0;
@@ -287,94 +310,57 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
         for (int r = 0; r < 4; ++r) acc |= (uint32_t)tile[vt_key_i8(16 * c + 4 * q + r)][d] << (8 * r);
         w[q] = acc;
       }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int key0 = vt_key_bf16(8 * c + 2 * q), key1 = vt_key_bf16(8 * c + 2 * q + 1);
+        if (PV == PV_BF) {
+          w[q] = (uint32_t)*reinterpret_cast<const uint16_t*>(&tile[key0][2 * d]) |
+                 ((uint32_t)*reinterpret_cast<const uint16_t*>(&tile[key1][2 * d]) << 16);
+        } else if (PV == PV_MX4) {
+          uint32_t pair = 0;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int key = hh ? key1 : key0;
+            const uint32_t nib = (tile[key][d >> 1] >> (4 * (d & 1))) & 0xfu;
+            const uint32_t mag = nib & 7u;
+            // E2M1 magnitude: 0, .5, 1, 1.5, 2, 3, 4, 6; times 2^(e8m0 - 127)
+            const float fm = mag < 2 ? 0.5f * (float)mag
+                                     : (float)(1u << ((mag >> 1) - 1)) * (1.0f + 0.5f * (float)(mag & 1u));
+            float f = __builtin_amdgcn_ldexpf(fm, (int)vex[key][d >> 5] - 127);
+            f = (nib & 8u) ? -f : f;
+            pair |= (__float_as_uint(f) >> 16) << (16 * hh);  // exact: at most 2 significant bits
+          }
+          w[q] = pair;
+        } else {
+          const uint32_t pair = (uint32_t)tile[key0][d] | ((uint32_t)tile[key1][d] << 8);
+          w[q] = e4m3x2_to_bf16x2<false>(pair);
+          if (PV == PV_MX8) {
+            // the exact value code * 2^(E - 127), rounded to bf16 (exact
+            // within bf16's normal range)
+            const float f0 = __builtin_amdgcn_ldexpf(bf16_lo(w[q]), (int)vex[key0][d >> 5] - 127);
+            const float f1 = __builtin_amdgcn_ldexpf(bf16_hi(w[q]), (int)vex[key1][d >> 5] - 127);
+            w[q] = f32_to_bf16_bits(f0) | (f32_to_bf16_bits(f1) << 16);
+          }
+        }
+      }
     }
     *reinterpret_cast<uint4*>(img + (c * D + d) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  const int kl = threadIdx.x;
-  if (C::VW) {
-    float sv = 0.0f, sk = 0.0f;
-    if (kl < BN && k0 + kl < a.Skv) {
-      const int64_t si = sbase + (k0 + kl) / a.blk;
-      sv = reinterpret_cast<const float*>(a.vs)[si];
-      sk = reinterpret_cast<const float*>(a.ks)[si];
-    }
+  // V extras: sigma_t and the multipliers qmax w_j
+  if (C::SIG) {
+    float sv = 0.0f;
+    if (kl < BN && k0 + kl < a.Skv)
+      sv = reinterpret_cast<const float*>(a.vs)[(bh / a.H) * a.vsb + (bh % a.H) * a.vsh + (k0 + kl) / a.vblk];
     float m = wave_max(sv);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    constexpr float qmax = MODE == ATTN_FP8 ? 448.0f : 127.0f;
-    if (kl < BN) {
-      a.aux[tile_id * 2 * BN + kl] = sk;
-      a.aux[tile_id * 2 * BN + BN + kl] = (sv > 0.0f) ? qmax * (sv / m) : 0.0f;
+    if (C::PVW && kl < BN) {
+      constexpr float qmax = PV == PV_F8W ? 448.0f : 127.0f;
+      reinterpret_cast<float*>(auxt + C::XKBYTES)[kl] = (sv > 0.0f) ? qmax * (sv / m) : 0.0f;
     }
     if (threadIdx.x == 0) a.sig[tile_id] = m;
-  }
-  if (MX8 && kl < BN) {
-    float sk = 0.0f;
-    if (k0 + kl < a.Skv) {
-      const uint8_t* ke = reinterpret_cast<const uint8_t*>(a.ks) + (bh * a.Skv + k0 + kl) * NB;
-      int emax = 0;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) emax = max(emax, (int)ke[b]);
-      sk = __builtin_amdgcn_ldexpf(1.0f, emax - 127);
-    }
-    a.aux[tile_id * BN + kl] = sk;
-  }
-}
-
-// ------------------------------------------------------------------------
-// MXFP4 re-layout: the V^T image as the exact bf16 values E2M1 * 2^E (E
-// from the token's 32-channel block) in the lane key order; the K block
-// exponents per tile (127 = 2^0 past the end).
-// ------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void k_prep_mx(const uint8_t* __restrict__ v, const uint8_t* __restrict__ ve,
-                                                 const uint8_t* __restrict__ ke, int64_t Skv, int64_t nt,
-                                                 uint8_t* __restrict__ vt, uint8_t* __restrict__ kex) {
-  using C = Cfg<ATTN_MX, D>;
-  constexpr int NB = D / 32;
-  __shared__ uint8_t codes[BN][D / 2 + 4];
-  __shared__ uint8_t ex[BN][NB];
-  const int t = blockIdx.x;
-  const int64_t bh = blockIdx.y;
-  const int64_t k0 = (int64_t)t * BN;
-  const int64_t tile_id = bh * nt + t;
-  for (int c = threadIdx.x; c < BN * (D / 32); c += 256) {
-    const int kl = c / (D / 32), cc = c % (D / 32);  // 16-byte chunks of the packed row
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (k0 + kl < Skv) val = *reinterpret_cast<const uint4*>(v + (bh * Skv + k0 + kl) * (D / 2) + cc * 16);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&codes[kl][cc * 16]);
-    dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
-  }
-  for (int c = threadIdx.x; c < BN * NB; c += 256) {
-    const int kl = c / NB, b = c % NB;
-    const bool ok = k0 + kl < Skv;
-    ex[kl][b] = ok ? ve[(bh * Skv + k0 + kl) * NB + b] : (uint8_t)127;
-    kex[tile_id * BN * NB + c] = ok ? ke[(bh * Skv + k0 + kl) * NB + b] : (uint8_t)127;
-  }
-  __syncthreads();
-  uint8_t* img = vt + tile_id * C::VBYTES;
-  for (int i = threadIdx.x; i < (C::VROW / 16) * D; i += 256) {
-    const int c = i / D, d = i % D;
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t pair = 0;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int key = vt_key_bf16(8 * c + 2 * q + hh);
-        const uint32_t nib = (codes[key][d >> 1] >> (4 * (d & 1))) & 0xfu;
-        const uint32_t mag = nib & 7u;
-        // E2M1 magnitude: 0, .5, 1, 1.5, 2, 3, 4, 6; times 2^(e8m0 - 127)
-        const float fm = mag < 2 ? 0.5f * (float)mag
-                                 : (float)(1u << ((mag >> 1) - 1)) * (1.0f + 0.5f * (float)(mag & 1u));
-        float f = __builtin_amdgcn_ldexpf(fm, (int)ex[key][d >> 5] - 127);
-        f = (nib & 8u) ? -f : f;
-        pair |= (__float_as_uint(f) >> 16) << (16 * hh);  // exact: at most 2 significant bits
-      }
-      w[q] = pair;
-    }
-    *reinterpret_cast<uint4*>(img + (c * D + d) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -384,15 +370,15 @@ __global__ __launch_bounds__(256) void k_prep_mx(const uint8_t* __restrict__ v, 
 struct KParams {
   int64_t H, BH, Sq, Skv, nt;
   int nqt;
-  const uint8_t* q;
-  const void* qs;
-  const uint8_t* k;      // INT8 / MXFP4: K codes; FP8 / MXFP8: bf16 K images in the workspace
+  const uint8_t* q;      // Q codes or bf16 values
+  const void* qs;        // Q scales
+  const uint8_t* k;      // K codes / bf16 values, or the bf16 K images in the workspace
   const void* ks;        // INT8 per-head: K scale
   const uint8_t* vt;     // V^T images in the workspace
   const uint8_t* aux;    // per-tile K extras, then V extras (see Cfg)
-  const float* sig;      // FP8 / INT8 per-token: sigma_t
-  const float* vs_head;  // INT8 per-head: V scale
-  int64_t q_sb, q_sh;    // FP8 / INT8 per-token: Q scale index b * q_sb + h * q_sh + i / q_block
+  const float* sig;      // sigma_t per tile
+  const float* vs_head;  // INT8 per-head V: V scale
+  int64_t q_sb, q_sh;    // float Q scale index b * q_sb + h * q_sh + i / q_block
   int q_block;
   float c_log2;  // sm_scale * log2(e)
   void* out;
@@ -433,15 +419,15 @@ FAQ_DEV T lds_ld(const uint8_t* p) {
   return *reinterpret_cast<const T*>(p);
 }
 
-// KVC (FP8 only): the K and V scales are constant over each 128-key tile
-// (token blocks of a multiple of 128 keys), so the K scale folds into the
-// query's exponent factor and every w_j is 1.
-template <int MODE, int D, bool CAUSAL, bool KVC>
+template <int QK, int PV, int D, bool CAUSAL>
 __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
-  using G = Cfg<MODE, D>;
+  using G = Cfg<QK, PV, D>;
   constexpr int KS = G::KS, DB = G::DB, NB = G::NB;
-  // per-key K scales multiply the scores (per-token scopes, MXFP8 rows)
-  constexpr bool PERKEY = (MODE == ATTN_FP8 && !KVC) || MODE == ATTN_I8TOK || MODE == ATTN_MX8;
+  // per-key K scales multiply the scores (per-token scopes, MXFP8 rows); a
+  // K scale constant over the tile folds into the exponent factor
+  constexpr bool PERKEY = QK == QK_I8T || QK == QK_F8T || QK == QK_MX8;
+  constexpr bool KCONST = QK == QK_F8C;
+  static_assert(!(G::PMX && QK == QK_I8H), "MX probabilities need the float score path");
   // K (+ its per-key extras) and V^T tiles in separate LDS objects: V(t)
   // is copied while the scores and probabilities of tile t are computed
   // from K(t), and K(t+1) while the products with V(t) run.  As distinct
@@ -474,27 +460,36 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   const int q0 = qt * BM + wave * 32;  // this wave's first query
   const int qi = q0 + j;               // this lane's query
   const bool act = q0 < Sq;            // uniform per wave: any query to compute
-  const uint8_t* kbase = p.k + (G::BFK ? bh * nt * (int64_t)G::KBYTES : bh * (int64_t)Skv * G::KROW);
+  const uint8_t* kbase = p.k + (G::QIMG ? bh * nt * (int64_t)G::KBYTES : bh * (int64_t)Skv * G::KROW);
   const uint8_t* vtbase = p.vt + bh * nt * (int64_t)G::VBYTES;
   const uint8_t* auxbase = p.aux + bh * nt * (int64_t)G::XBYTES;
 
   // ---- Q operands (B of S^T = K Q^T): lane (j, h) holds, for k-step ks,
   // the K-slice [K/2 h, K/2 h + K/2) of the instruction's K range
-  bf16x8 qbf[G::BFK ? KS : 1];  // FP8 / MXFP8: bf16 images of the E4M3 codes
-  i32x4 qi8[G::I8 ? KS : 1];    // INT8: 16 codes
-  i32x8 qmx[MODE == ATTN_MX ? KS : 1];    // MXFP4: 32 E2M1 codes (16 bytes used)
-  int qsc[MODE == ATTN_MX ? KS : 1];      // MXFP4: their E8M0 exponents
+  bf16x8 qbf[G::QBF ? KS : 1];       // bf16 (images of E4M3 codes, or the inputs)
+  i32x4 qi8[G::QI8 ? KS : 1];        // INT8: 16 codes
+  i32x8 qmx[QK == QK_MX4 ? KS : 1];  // MXFP4: 32 E2M1 codes (16 bytes used)
+  int qsc[QK == QK_MX4 ? KS : 1];    // MXFP4: their E8M0 exponents
   float cq;
   {
     const bool ok = qi < Sq;
     const int64_t qrow_i = bh * p.Sq + (ok ? qi : 0);
     // per-token / token-block / per-head float Q scale of this query
     const int64_t qsi = (bh / p.H) * p.q_sb + hd * p.q_sh + (ok ? qi : 0) / p.q_block;
-    if (G::BFK) {
+    if (QK == QK_BF) {
+      const uint8_t* qrow = p.q + qrow_i * (2 * D);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 a = make_uint4(0, 0, 0, 0);
+        if (ok) a = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 16 * h);
+        qbf[ks] = __builtin_bit_cast(bf16x8, a);
+      }
+      cq = p.c_log2;
+    } else if (G::QBF) {
       const uint8_t* qrow = p.q + qrow_i * D;
       // MXFP8: the row relative to its largest block exponent
-      int eb[MODE == ATTN_MX8 ? NB : 1], emax = 127;
-      if (MODE == ATTN_MX8) {
+      int eb[QK == QK_MX8 ? NB : 1], emax = 127;
+      if (QK == QK_MX8) {
         const uint8_t* qe = reinterpret_cast<const uint8_t*>(p.qs) + qrow_i * NB;
         emax = 0;
 #pragma unroll
@@ -507,14 +502,15 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       for (int ks = 0; ks < KS; ++ks) {
         uint2 a = make_uint2(0, 0);
         if (ok) a = *reinterpret_cast<const uint2*>(qrow + 16 * ks + 8 * h);
-        const float sc = MODE == ATTN_MX8 ? __builtin_amdgcn_ldexpf(1.0f, eb[ks >> 1] - emax) : 1.0f;
-        qbf[ks] = __builtin_bit_cast(
-            bf16x8, i32x4{(int)e4m3x2_to_bf16x2_scaled<false>(a.x, sc), (int)e4m3x2_to_bf16x2_scaled<true>(a.x, sc),
-                          (int)e4m3x2_to_bf16x2_scaled<false>(a.y, sc), (int)e4m3x2_to_bf16x2_scaled<true>(a.y, sc)});
+        const float sc = QK == QK_MX8 ? __builtin_amdgcn_ldexpf(1.0f, eb[ks >> 1] - emax) : 1.0f;
+        qbf[ks] = __builtin_bit_cast(bf16x8, i32x4{(int)e4m3x2_to_bf16x2<false>(a.x, sc),
+                                                  (int)e4m3x2_to_bf16x2<true>(a.x, sc),
+                                                  (int)e4m3x2_to_bf16x2<false>(a.y, sc),
+                                                  (int)e4m3x2_to_bf16x2<true>(a.y, sc)});
       }
-      if (MODE == ATTN_MX8) cq = __builtin_amdgcn_ldexpf(1.0f, emax - 127) * p.c_log2;
+      if (QK == QK_MX8) cq = __builtin_amdgcn_ldexpf(1.0f, emax - 127) * p.c_log2;
       else cq = (ok ? reinterpret_cast<const float*>(p.qs)[qsi] : 1.0f) * p.c_log2;
-    } else if (G::I8) {
+    } else if (G::QI8) {
       const uint8_t* qrow = p.q + qrow_i * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -523,7 +519,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
         qi8[ks] = i32x4{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
       }
       const float* qs = reinterpret_cast<const float*>(p.qs);
-      if (MODE == ATTN_INT8) cq = qs[hd] * reinterpret_cast<const float*>(p.ks)[hd] * p.c_log2;
+      if (QK == QK_I8H) cq = qs[hd] * reinterpret_cast<const float*>(p.ks)[hd] * p.c_log2;
       else cq = (ok ? qs[qsi] : 1.0f) * p.c_log2;
     } else {
       const uint8_t* qrow = p.q + qrow_i * (D / 2);
@@ -546,18 +542,19 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   // ---- operand addresses: per-lane bases, constant offsets per step
   const uint8_t* kop_base = kbuf + h * (BN * 16) + kslot(qk_row(j)) * 16;  // + ks 2 BN 16 + kb 256
   const uint8_t* vop_base = vbuf + h * (D * 16) + j * 16;                   // + kstep 2 D 16 + db 512
-  const float* xk = reinterpret_cast<const float*>(kbuf + G::KBYTES) + 64 * h;  // FP8: the lane's keys' K scales
-  const float* xv = reinterpret_cast<const float*>(vbuf + G::VBYTES) + 64 * h;  // FP8: their 448 w_j
+  const float* xk = reinterpret_cast<const float*>(kbuf + G::KBYTES) + 64 * h;  // the lane's keys' K scales
+  const float* xv = reinterpret_cast<const float*>(vbuf + G::VBYTES) + 64 * h;  // their qmax w_j
   const uint8_t* xmx = kbuf + G::KBYTES + qk_row(j) * NB + h;               // MXFP4: + 16 kb NB + 2 ks
 
-  // ---- tile copies.  K: FP8 copies the bf16 image from the workspace;
-  // INT8 / MXFP4 gather K rows into the chunk-major layout (round i of a
-  // lane moves column 2 i + pw / 128 of slot pw % 128, i.e. of K row
-  // kslot(pw % 128); rows past the end re-read the last row, masked).
+  // ---- tile copies.  K: FP8 / MXFP8 copy the bf16 image from the
+  // workspace; the other modes gather K rows into the chunk-major layout
+  // (round i of a lane moves column 2 i + pw / 128 of slot pw % 128, i.e.
+  // of K row kslot(pw % 128); rows past the end re-read the last row,
+  // masked).
   const int pw = wave * 64 + lane;
   const int krow = kslot(pw & (BN - 1));
   auto issue_k = [&](int t) {
-    if (G::BFK) {
+    if (G::QIMG) {
       stage<G::KBYTES / 16>(kbuf, kbase + (int64_t)t * G::KBYTES, wave, lane,
                             [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
     } else {
@@ -578,9 +575,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 
   // Row state (each lane holds its query's; both halves agree).  O holds
   // the output relative to a reference factor fref: the true accumulator is
-  // O * fref (INT8 keeps fref = 1 and folds its per-tile factor in with an
-  // fma; the bf16-MFMA modes rescale O once per tile and let the P V MFMA
-  // accumulate straight into it).
+  // O * fref (int8 values keep fref = 1 and fold their per-tile factor in
+  // with an fma; the bf16 value product rescales O once per tile and lets
+  // the P V MFMA accumulate straight into it).
   float M = -INFINITY, L = 0.f, fref = 1.f;
   f32x16 O[DB];
 #pragma unroll
@@ -588,7 +585,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 
   const int qlast = min(Sq, (qt + 1) * BM) - 1;
   const int t_end = CAUSAL ? min(nt, qlast / BN + 1) : nt;
-  const float vscale_i8 = (MODE == ATTN_INT8) ? p.vs_head[hd] * (1.0f / 127.0f) : 1.0f;
+  const float vscale_i8 = (PV == PV_I8H) ? p.vs_head[hd] * (1.0f / 127.0f) : 1.0f;
   // valid keys of this lane's query: [0, lim)
   const int lim = CAUSAL ? min(Skv, qi + 1) : Skv;
 
@@ -619,10 +616,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
           for (int kk = 0; kk < 2; ++kk) {
             const int kb = 2 * pr + kk;
             const uint8_t* a = kop_base + ks * (2 * BN * 16) + kb * 256;
-            if (G::BFK) {
+            if (G::QBF) {
               if (ks == 0) S[kb] = f32x16{};
               S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld<bf16x8>(a), qbf[ks], S[kb], 0, 0, 0);
-            } else if (G::I8) {
+            } else if (G::QI8) {
               if (ks == 0) SI[kb] = i32x16{};
               const uint4 v = lds_ld<uint4>(a);
               SI[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, qi8[ks],
@@ -638,9 +635,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
         }
       }
 
-      // ---- per-key K scale (FP8 per-token), masking, tile maximum
+      // ---- per-key K scale, masking, tile maximum
       float m;
-      if (MODE == ATTN_INT8) {
+      if (QK == QK_I8H) {
         if (!masked) {
           // exact int32 scores (|s| < 2^21): max in integers, converted once
           int mi = INT_MIN;
@@ -664,7 +661,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
             }
         }
       } else {
-        if (MODE == ATTN_I8TOK) {
+        if (QK == QK_I8T) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -693,7 +690,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
           for (int kb = 2 * g2; kb < 2 * g2 + 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(S[kb][r], S[kb][r + 1]));
-          gmax[g2] = x;  // MXFP4: the lane's 32-key group maxima
+          gmax[g2] = x;  // MX probabilities: the lane's 32-key group maxima
         }
         m = fmaxf(gmax[0], gmax[1]);
       }
@@ -701,10 +698,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 
       // ---- the row's combination factors: a rescales what was
       // accumulated so far, bt weights this tile
-      if (MODE == ATTN_FP8 && KVC) ce = cq * xk[-64 * h];  // the tile's K scale
+      if (KCONST) ce = cq * xk[-64 * h];  // the tile's K scale
       const float ml = m * ce;  // tile max, log2 units (M is kept in these units)
       float Mn, a;
-      if (G::I8) {
+      if (G::PI8) {
         // lazy reference: keep the running reference unless this tile's max
         // exceeds it by more than 2^8 (tile weights stay <= 2^8, far from
         // overflow), so O is rescaled only when the max jumps
@@ -718,14 +715,14 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml - Mn);
       M = Mn;
       bool live = true;
-      if (G::I8) {
+      if (G::PI8) {
         rscale = a;
       } else {
-        // new reference factor f = bt (times sigma_t / 448 for FP8); a row
-        // whose tile is negligible (bt < 2^-64) keeps its reference and
-        // contributes nothing, which keeps O bounded
+        // new reference factor f = bt (times sigma_t / 448 for FP8 values);
+        // a row whose tile is negligible (bt < 2^-64) keeps its reference
+        // and contributes nothing, which keeps O bounded
         float ft = bt;
-        if (MODE == ATTN_FP8) ft *= p.sig[bh * nt + t] * (1.0f / 448.0f);
+        if (PV == PV_F8W || PV == PV_F8C) ft *= p.sig[bh * nt + t] * (1.0f / 448.0f);
         live = bt >= 0x1p-64f;
         rscale = live ? fref * a * __builtin_amdgcn_rcpf(ft) : a;
         fref = live ? ft : fref;
@@ -744,10 +741,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       // ---- probabilities, tile sum, the quantized P operand and
       // O^T += V^T P^T
       float ls0 = 0.f, ls1 = 0.f;
-      if (G::I8) {
-        // per-head: 127 p = 2^(s ce - (m ce - log2 127)); at the maximum
-        // this may differ from 127 by an ulp, which cannot move rne(127 p).
-        // per-token: p = 1 exactly at the maximum, times 127 w_j.
+      if (G::PI8) {
         // the running max moves rarely once a row has seen its largest
         // scores: rescale only when some row of the wave needs it (before
         // the probabilities, so that they and their products share a block)
@@ -755,30 +749,33 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) O[db] *= rscale;
         }
-        const float mc = MODE == ATTN_INT8 ? ms * ce - kLog2_127 : ms;
+        // per-head: 127 p = 2^(s ce - (m ce - log2 127)); at the maximum
+        // this may differ from 127 by an ulp, which cannot move rne(127 p).
+        // per-token: p = 1 exactly at the maximum, times 127 w_j.
+        const float mc = PV == PV_I8H ? ms * ce - kLog2_127 : ms;
         i32x4 P[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             float4 vm4;
-            if (MODE == ATTN_I8TOK) vm4 = *reinterpret_cast<const float4*>(xv + 16 * kb + 4 * w);
+            if (PV == PV_I8T) vm4 = *reinterpret_cast<const float4*>(xv + 16 * kb + 4 * w);
             const float vm[4] = {vm4.x, vm4.y, vm4.z, vm4.w};
             uint32_t word = 0;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
               const float x = S[kb][4 * w + b];
-              float pv = MODE == ATTN_INT8 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, -mc))
-                                           : __builtin_amdgcn_exp2f((x - mc) * ce);
+              float pv = PV == PV_I8H ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, -mc))
+                                      : __builtin_amdgcn_exp2f((x - mc) * ce);
               if (b & 1) ls1 += pv; else ls0 += pv;
-              if (MODE == ATTN_I8TOK) pv *= vm[b];
+              if (PV == PV_I8T) pv *= vm[b];
               word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
             }
             P[kb][w] = (int)word;
           }
         }
-        L += halves_sum(ls0 + ls1) * (MODE == ATTN_INT8 ? bt * (1.0f / 127.0f) : bt);
-        const float bv = MODE == ATTN_INT8 ? bt * vscale_i8 : bt * p.sig[bh * nt + t] * (1.0f / 127.0f);
+        L += halves_sum(ls0 + ls1) * (PV == PV_I8H ? bt * (1.0f / 127.0f) : bt);
+        const float bv = PV == PV_I8H ? bt * vscale_i8 : bt * p.sig[bh * nt + t] * (1.0f / 127.0f);
         // two output blocks at a time: two independent accumulation chains
 #pragma unroll
         for (int d2 = 0; d2 < DB; d2 += 2) {
@@ -797,21 +794,21 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
             for (int r = 0; r < 16; ++r) O[d2 + dd][r] = __builtin_fmaf((float)C[dd][r], bv, O[d2 + dd][r]);
         }
       } else {
-        // FP8 / MXFP4: rescale, then per 32-key block: probabilities, the
-        // bf16 P operand of its two k-steps, and their products
+        // bf16 value product: rescale, then per 32-key block: probabilities,
+        // the bf16 P operand of its two k-steps, and their products
 #pragma unroll
         for (int db = 0; db < DB; ++db) O[db] *= rscale;
         const float mce = ms * ce;
         float sc = 1.0f, isc = 1.0f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          if (G::MXP && (kb & 1) == 0) {
+          if (G::PMX && (kb & 1) == 0) {
             // this lane's keys of blocks kb, kb + 1 are one MX group:
             // group max -> shared exponent; p -> E2M1 / E4M3 of p / 2^E,
             // times 2^E, exact in bf16.  The group's largest p is the same
             // function of the group's largest score.
             const float pmax = __builtin_amdgcn_exp2f((gmax[kb >> 1] - ms) * ce);
-            const int E = MODE == ATTN_MX ? mx_exponent(pmax) : mx_exponent<8>(pmax);
+            const int E = PV == PV_MX4 ? mx_exponent(pmax) : mx_exponent<8>(pmax);
             sc = E > -127 ? pow2f(E) : 1.0f;
             isc = E > -127 ? pow2f(-E) : 1.0f;
           }
@@ -821,20 +818,20 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 #pragma unroll
             for (int t8 = 0; t8 < 8; ++t8) {
               const float x = S[kb][8 * s2 + t8];
-              // KVC: 448 p comes out of the exponent (448 p at the maximum
-              // is within an ulp of 448, whose code both roundings give).
-              // Otherwise p = 1 exactly at the tile maximum ((x - m) is 0):
-              // there 448 w_j can sit on an E4M3 tie (bf16-derived scale
-              // ratios do), and the MX group of the maximum has its amax at
-              // a power of two
-              pv[t8] = (MODE == ATTN_FP8 && KVC) ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, kLog2_448 - mce))
-                                                 : __builtin_amdgcn_exp2f((x - ms) * ce);
+              // one V scale per tile: 448 p comes out of the exponent (448 p
+              // at the maximum is within an ulp of 448, whose code both
+              // roundings give).  Otherwise p = 1 exactly at the tile
+              // maximum ((x - m) is 0): there 448 w_j can sit on an E4M3 tie
+              // (bf16-derived scale ratios do), and the MX group of the
+              // maximum has its amax at a power of two
+              pv[t8] = PV == PV_F8C ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, kLog2_448 - mce))
+                                    : __builtin_amdgcn_exp2f((x - ms) * ce);
               if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
             }
             i32x4 pop;
-            if (MODE == ATTN_FP8) {
+            if (PV == PV_F8W || PV == PV_F8C) {
               // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
-              if (!KVC) {
+              if (PV == PV_F8W) {
                 const float4 v0 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2);
                 const float4 v1 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2 + 4);
                 pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
@@ -846,7 +843,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
               e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], e1, true);
               pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0), (int)e4m3x2_to_bf16x2<true>((uint32_t)e0),
                           (int)e4m3x2_to_bf16x2<false>((uint32_t)e1), (int)e4m3x2_to_bf16x2<true>((uint32_t)e1)};
-            } else if (MODE == ATTN_MX8) {
+            } else if (PV == PV_MX8) {
               // E4M3 of p / 2^E (exact scaling; the group maximum lies in
               // [256, 512) and saturates above 448), then back times 2^E
               float u[8];
@@ -856,16 +853,23 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
               e0 = __builtin_amdgcn_cvt_pk_fp8_f32(u[2], u[3], e0, true);
               int e1 = __builtin_amdgcn_cvt_pk_fp8_f32(u[4], u[5], 0, false);
               e1 = __builtin_amdgcn_cvt_pk_fp8_f32(u[6], u[7], e1, true);
-              pop = i32x4{(int)e4m3x2_to_bf16x2_scaled<false>((uint32_t)e0, sc),
-                          (int)e4m3x2_to_bf16x2_scaled<true>((uint32_t)e0, sc),
-                          (int)e4m3x2_to_bf16x2_scaled<false>((uint32_t)e1, sc),
-                          (int)e4m3x2_to_bf16x2_scaled<true>((uint32_t)e1, sc)};
-            } else {
+              pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0, sc),
+                          (int)e4m3x2_to_bf16x2<true>((uint32_t)e0, sc),
+                          (int)e4m3x2_to_bf16x2<false>((uint32_t)e1, sc),
+                          (int)e4m3x2_to_bf16x2<true>((uint32_t)e1, sc)};
+            } else if (PV == PV_MX4) {
               // each pair through byte 0: E2M1(p / 2^E), then back times 2^E
 #pragma unroll
               for (int b = 0; b < 4; ++b) {
                 const uint32_t f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv[2 * b], pv[2 * b + 1], sc, 0);
                 pop[b] = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
+              }
+            } else {
+              // unquantized V: p rounded to bf16 (nearest even)
+#pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                const bf16x2 pr2 = {(__bf16)pv[2 * b], (__bf16)pv[2 * b + 1]};
+                pop[b] = (int)__builtin_bit_cast(uint32_t, pr2);
               }
             }
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pop);
@@ -876,7 +880,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
                   lds_ld<bf16x8>(vop_base + kst * (2 * D * 16) + db * 512), pb, O[db], 0, 0, 0);
           }
         }
-        const float lsc = (MODE == ATTN_FP8 && KVC) ? (1.0f / 448.0f) : 1.0f;
+        const float lsc = PV == PV_F8C ? (1.0f / 448.0f) : 1.0f;
         L += halves_sum(ls0 + ls1) * (bt * lsc);
       }
     }
@@ -907,32 +911,27 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   }
 }
 
-template <int MODE, int D>
-hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
+template <int QK, int PV, int D>
+hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
+  using G = Cfg<QK, PV, D>;
   const int64_t nt = (a.Skv + BN - 1) / BN;
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
-  dim3 pgrid((unsigned)nt, (unsigned)(a.B * a.H));
-  if (MODE == ATTN_MX) {
-    k_prep_mx<D><<<pgrid, 256, 0, st>>>((const uint8_t*)a.v_codes, (const uint8_t*)a.v_scales,
-                                        (const uint8_t*)a.k_scales, a.Skv, nt, ws + l.vt_off, ws + l.aux_off);
-  } else {
-    PrepArgs pa{};
-    pa.k = (const uint8_t*)a.k_codes; pa.ks = a.k_scales;
-    pa.v = (const uint8_t*)a.v_codes; pa.vs = a.v_scales;
-    pa.H = a.H; pa.Skv = a.Skv; pa.nt = nt; pa.sb = a.kv_sb; pa.sh = a.kv_sh; pa.blk = a.kv_block;
-    pa.vt = ws + l.vt_off; pa.kb = ws + l.kb_off;
-    pa.aux = reinterpret_cast<float*>(ws + l.aux_off);
-    pa.sig = reinterpret_cast<float*>(ws + l.sig_off);
-    k_prep<MODE, D><<<pgrid, 256, 0, st>>>(pa);
-  }
+  PrepArgs pa{};
+  pa.k = (const uint8_t*)a.k_codes; pa.ks = a.k_scales;
+  pa.v = (const uint8_t*)a.v_codes; pa.vs = a.v_scales;
+  pa.H = a.H; pa.Skv = a.Skv; pa.nt = nt;
+  pa.ksb = a.k_sb; pa.ksh = a.k_sh; pa.kblk = a.k_block;
+  pa.vsb = a.v_sb; pa.vsh = a.v_sh; pa.vblk = a.v_block;
+  pa.vt = ws + l.vt_off; pa.kb = ws + l.kb_off; pa.aux = ws + l.aux_off;
+  pa.sig = reinterpret_cast<float*>(ws + l.sig_off);
+  k_prep<QK, PV, D><<<dim3((unsigned)nt, (unsigned)(a.B * a.H)), 256, 0, st>>>(pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  using G = Cfg<MODE, D>;
   KParams p{};
   p.H = a.H; p.BH = a.B * a.H; p.Sq = a.Sq; p.Skv = a.Skv; p.nt = nt;
   p.nqt = (int)((a.Sq + BM - 1) / BM);
   p.q = (const uint8_t*)a.q_codes; p.qs = a.q_scales;
-  p.k = G::BFK ? ws + l.kb_off : (const uint8_t*)a.k_codes;
+  p.k = G::QIMG ? ws + l.kb_off : (const uint8_t*)a.k_codes;
   p.ks = a.k_scales;
   p.vt = ws + l.vt_off;
   p.aux = ws + l.aux_off;
@@ -942,37 +941,62 @@ hipError_t launch_mode_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   p.c_log2 = a.sm_scale * kLog2e;
   p.out = a.out; p.out_bf16 = a.out_bf16;
   dim3 grid((unsigned)(p.nqt * p.BH));
-  if constexpr (MODE == ATTN_FP8) {
-    if (a.kv_block % BN == 0) {
-      if (a.causal) k_attn<MODE, D, true, true><<<grid, NTHR, 0, st>>>(p);
-      else k_attn<MODE, D, false, true><<<grid, NTHR, 0, st>>>(p);
-      return hipGetLastError();
-    }
-  }
-  if (a.causal) k_attn<MODE, D, true, false><<<grid, NTHR, 0, st>>>(p);
-  else k_attn<MODE, D, false, false><<<grid, NTHR, 0, st>>>(p);
+  if (a.causal) k_attn<QK, PV, D, true><<<grid, NTHR, 0, st>>>(p);
+  else k_attn<QK, PV, D, false><<<grid, NTHR, 0, st>>>(p);
   return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t launch_mode(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
-  return a.D == 128 ? launch_mode_d<MODE, 128>(a, l, st) : launch_mode_d<MODE, 64>(a, l, st);
+template <int QK, int PV>
+hipError_t launch_pair(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
+  return a.D == 128 ? launch_d<QK, PV, 128>(a, l, st) : launch_d<QK, PV, 64>(a, l, st);
+}
+
+// Quantized Q and K: V of their own configuration, or unquantized V.
+template <int QK, int PV_OWN>
+hipError_t launch_qk(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
+  if (a.pv == PV_BF) return launch_pair<QK, PV_BF>(a, l, st);
+  return launch_pair<QK, PV_OWN>(a, l, st);
 }
 
 }  // namespace
 
-size_t attn_workspace_bytes(int mode, int64_t B, int64_t H, int64_t Skv, int64_t D) {
-  return ws_layout(mode, B, H, Skv, D).total;
+bool attn_pair_supported(int qk, int pv) {
+  if (pv == PV_BF || qk == QK_BF) return true;
+  switch (qk) {
+    case QK_I8H: return pv == PV_I8H;
+    case QK_I8T: return pv == PV_I8T;
+    case QK_F8T: return pv == PV_F8W;
+    case QK_F8C: return pv == PV_F8C;
+    case QK_MX4: return pv == PV_MX4;
+    case QK_MX8: return pv == PV_MX8;
+    default: return false;
+  }
+}
+
+size_t attn_workspace_bytes(int qk, int pv, int64_t B, int64_t H, int64_t Skv, int64_t D) {
+  return ws_layout(qk, pv, B, H, Skv, D).total;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
-  const WsLayout l = ws_layout(a.mode, a.B, a.H, a.Skv, a.D);
-  switch (a.mode) {
-    case ATTN_INT8: return launch_mode<ATTN_INT8>(a, l, st);
-    case ATTN_FP8: return launch_mode<ATTN_FP8>(a, l, st);
-    case ATTN_I8TOK: return launch_mode<ATTN_I8TOK>(a, l, st);
-    case ATTN_MX8: return launch_mode<ATTN_MX8>(a, l, st);
-    default: return launch_mode<ATTN_MX>(a, l, st);
+  const WsLayout l = ws_layout(a.qk, a.pv, a.B, a.H, a.Skv, a.D);
+  switch (a.qk) {
+    case QK_I8H: return launch_qk<QK_I8H, PV_I8H>(a, l, st);
+    case QK_I8T: return launch_qk<QK_I8T, PV_I8T>(a, l, st);
+    case QK_F8T: return launch_qk<QK_F8T, PV_F8W>(a, l, st);
+    case QK_F8C: return launch_qk<QK_F8C, PV_F8C>(a, l, st);
+    case QK_MX4: return launch_qk<QK_MX4, PV_MX4>(a, l, st);
+    case QK_MX8: return launch_qk<QK_MX8, PV_MX8>(a, l, st);
+    default:
+      // unquantized Q and K with any value mode
+      switch (a.pv) {
+        case PV_I8H: return launch_pair<QK_BF, PV_I8H>(a, l, st);
+        case PV_I8T: return launch_pair<QK_BF, PV_I8T>(a, l, st);
+        case PV_F8W: return launch_pair<QK_BF, PV_F8W>(a, l, st);
+        case PV_F8C: return launch_pair<QK_BF, PV_F8C>(a, l, st);
+        case PV_MX4: return launch_pair<QK_BF, PV_MX4>(a, l, st);
+        case PV_MX8: return launch_pair<QK_BF, PV_MX8>(a, l, st);
+        default: return launch_pair<QK_BF, PV_BF>(a, l, st);
+      }
   }
 }
 

@@ -32,12 +32,17 @@ hipError_t launch_rot_fp8_block(const uint16_t* x, const uint16_t* rot, const fa
                                 uint16_t* debug_rotated, hipStream_t st);
 
 // ---- attention (attention.hip)
-// INT8 per-head; FP8 (per-token, token-block or per-head); MXFP4;
-// INT8 per-token; MXFP8.
-enum AttnMode { ATTN_INT8 = 0, ATTN_FP8 = 1, ATTN_MX = 2, ATTN_I8TOK = 3, ATTN_MX8 = 4 };
+// Score modes, from the configuration Q and K share: INT8 per-head, INT8
+// per-token, FP8 with per-token K scales, FP8 with one K scale per 128-key
+// tile (per-head, token blocks), MXFP4, MXFP8, unquantized bf16.
+enum QkMode { QK_I8H = 0, QK_I8T, QK_F8T, QK_F8C, QK_MX4, QK_MX8, QK_BF };
+// Value modes, from V's configuration: INT8 per-head, INT8 per-token, FP8
+// with per-token V scales (folded into P), FP8 with one V scale per tile,
+// MXFP4, MXFP8, unquantized bf16.
+enum PvMode { PV_I8H = 0, PV_I8T, PV_F8W, PV_F8C, PV_MX4, PV_MX8, PV_BF };
 
 struct AttnArgs {
-  int mode;
+  int qk, pv;
   int64_t B, H, Sq, Skv, D;
   const void* q_codes;
   const void* q_scales;
@@ -47,9 +52,8 @@ struct AttnArgs {
   const void* v_scales;
   // float scales of per-token, token-block and per-head scopes sit at
   // b * sb + h * sh + token / block
-  int q_block;   // tokens per Q scale (1 = per token)
-  int kv_block;  // tokens per K/V scale (1 = per token)
-  int64_t q_sb, q_sh, kv_sb, kv_sh;
+  int q_block, k_block, v_block;
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh;
   float sm_scale;
   int causal;
   void* out;
@@ -57,7 +61,10 @@ struct AttnArgs {
   void* ws;
 };
 
-size_t attn_workspace_bytes(int mode, int64_t B, int64_t H, int64_t Skv, int64_t D);
+// Pairs with kernels: Q, K and V of one configuration, or either side
+// unquantized.
+bool attn_pair_supported(int qk, int pv);
+size_t attn_workspace_bytes(int qk, int pv, int64_t B, int64_t H, int64_t Skv, int64_t D);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
 }  // namespace faq

@@ -29,28 +29,35 @@ STATIC_DTYPE = {"int8_head": "int8", "fp8_head": "fp8_e4m3"}
 
 
 class GpuRun:
-    """Quantized Q/K/V of one workload produced by the HIP path."""
+    """Quantized Q/K/V of one workload produced by the HIP path.  `modes`
+    gives each branch's mode (default: the workload's mode for all three);
+    "float" leaves a branch unquantized (bf16)."""
 
-    def __init__(self, w, keep_rotated=False):
+    def __init__(self, w, keep_rotated=False, modes=None):
         self.w = w
         mode = w.spec["mode"]
         self.mode = mode
+        self.modes = list(modes) if modes is not None else [mode] * 3
         self.x = [t.to(DEV) for t in (w.q, w.k, w.v)]
         self.static = [None, None, None]
         self.amax = [None, None, None]
-        if mode in STATIC_DTYPE:
-            for br in range(3):
+        for br in range(3):
+            if self.modes[br] in STATIC_DTYPE:
                 amax = torch.zeros(w.shape[1], dtype=torch.float32, device=DEV)
                 for c in w.calib[br]:
                     faq.fa_quant_calibrate(c.to(DEV), amax)
                 self.amax[br] = amax
-                self.static[br] = faq.fa_quant_scales_from_amax(amax, STATIC_DTYPE[mode])
+                self.static[br] = faq.fa_quant_scales_from_amax(amax, STATIC_DTYPE[self.modes[br]])
         self.rot = w.rot.to(DEV) if w.rot is not None else None
         self.rotated = [None, None, None]
         self.qt = []
         for br in range(3):
-            cfg = MODE_CFG[mode](w.spec, br)
-            rot = self.rot if (self.rot is not None and br < 2) else None
+            m = self.modes[br]
+            if m == "float":
+                self.qt.append(faq.float_branch(self.x[br]))
+                continue
+            cfg = MODE_CFG[m](w.spec, br)
+            rot = self.rot if (self.rot is not None and br < 2 and m == "rot_fp8_block") else None
             dbg = None
             if rot is not None and keep_rotated:
                 dbg = torch.empty_like(self.x[br])
@@ -76,9 +83,11 @@ class GpuRun:
 def dequant(run: GpuRun, br: int):
     """(values fp64 [B,H,S,D], per-key scale [B,H,S] or None) of branch br,
     decoded by the oracle from the GPU's codes and scales."""
-    mode = run.mode
-    c, s = run.codes_np(br), run.scales_np(br)
+    mode = run.modes[br]
     B, H, S, D = run.w.shape
+    if mode == "float":
+        return run.x[br].to(torch.float64).cpu().numpy(), None
+    c, s = run.codes_np(br), run.scales_np(br)
     if mode == "int8_head":
         return OQ.dequantize_per_head(c, s), np.broadcast_to(s.reshape(1, H, 1), (B, H, S))
     if mode == "fp8_head":
@@ -103,7 +112,8 @@ def oracle_attention(run: GpuRun, rows=None, causal=None, sm_scale=None):
     q, _ = dequant(run, 0)
     k, _ = dequant(run, 1)
     v, vs = dequant(run, 2)
-    return OA.attention(q, k, v, P_RULE[run.mode], v_scale=vs, causal=causal, rows=rows, allowance=True,
+    rule = "bf16" if run.modes[2] == "float" else P_RULE[run.modes[2]]
+    return OA.attention(q, k, v, rule, v_scale=vs, causal=causal, rows=rows, allowance=True,
                         sm_scale=sm_scale)
 
 

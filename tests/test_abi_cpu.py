@@ -141,9 +141,23 @@ def test_attention_validation():
     assert _attn(q, k, v, causal=2) == _abi.FAQ_ERR_INVALID_ARG
     assert _attn(q, k, v, sm=-1.0) == _abi.FAQ_ERR_INVALID_ARG
     assert _attn(q, k, v, sm=float("nan")) == _abi.FAQ_ERR_INVALID_ARG
+    # per-branch configurations: Q and K share one configuration (token
+    # blocks may differ in size) or are both unquantized; V has theirs or is
+    # unquantized
+    ws = lambda a, b, c: lib.fa_quant_attention_workspace_bytes(ctypes.byref(_qt(a, s)), ctypes.byref(_qt(b, s)),
+                                                                ctypes.byref(_qt(c, s)))
     b1 = _cfg(_abi.FAQ_FP8_E4M3, _abi.FAQ_PER_TOKEN_BLOCK, 128)
     b2 = _cfg(_abi.FAQ_FP8_E4M3, _abi.FAQ_PER_TOKEN_BLOCK, 256)
-    assert _attn(_qt(b1, s), _qt(b2, s), _qt(b1, s)) == _abi.FAQ_ERR_UNSUPPORTED
+    fl = _cfg(_abi.FAQ_FLOAT, _abi.FAQ_PER_HEAD)
+    i8t = _cfg(_abi.FAQ_INT8, _abi.FAQ_PER_TOKEN)
+    for ok in [(b1, b2, b2), (b1, b2, fl), (fl, fl, tok), (fl, fl, mx), (fl, fl, fl), (tok, tok, fl), (i8t, i8t, i8t)]:
+        assert ws(*ok) > 0, ok
+    for bad in [(tok, tok, i8t), (fl, tok, tok), (tok, fl, fl), (i8t, tok, tok), (mx, mx, tok)]:
+        assert ws(*bad) == 0, bad
+        assert _attn(_qt(bad[0], s), _qt(bad[1], s), _qt(bad[2], s)) == _abi.FAQ_ERR_UNSUPPORTED
+    # unquantized branches need no scales; quantized ones do
+    nos = _abi.faq_qtensor(tok, s, 0x2000, None)
+    assert _attn(nos, k, v) == _abi.FAQ_ERR_INVALID_ARG
     assert lib.fa_quant_attention(None, ctypes.byref(k), ctypes.byref(v), 0.0, 0, FAKE, 1, FAKE, 1, None) \
         == _abi.FAQ_ERR_INVALID_ARG
 

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import quantized_attention_fa_amd as faq
 from synth import make_inputs, sample_rows
 from gpu_helpers import GpuRun, bf16_of, check_attention, oracle_attention, small_workload
 
@@ -71,3 +72,59 @@ def test_full_size_attention(cfg, rows_per_bh):
     rows = None if rows_per_bh is None else sample_rows(cfg, S, rows_per_bh, edge=4)
     got = o.cpu().numpy() if rows is None else o[:, :, torch.from_numpy(rows).to(o.device)].cpu().numpy()
     check_attention(got, oracle_attention(run, rows=rows), f"cfg{cfg} full size")
+
+
+# ---- per-branch configurations ("fa3_quant 配置说明" §2.3): Q and K of one
+# configuration with V unquantized, unquantized Q and K with a quantized V,
+# and no quantization at all
+
+MIXED = [
+    (2, (1, 2, 300, 128), True, ("int8_head", "int8_head", "float")),
+    (3, (1, 2, 300, 128), False, ("fp8_token", "fp8_token", "float")),
+    (4, (1, 2, 300, 64), False, ("mxfp4", "mxfp4", "float")),
+    (5, (1, 2, 300, 128), True, ("rot_fp8_block", "rot_fp8_block", "float")),
+    (6, (1, 2, 257, 128), False, ("fp8_head", "fp8_head", "float")),
+    (7, (1, 2, 300, 64), True, ("int8_token", "int8_token", "float")),
+    (8, (1, 2, 300, 128), False, ("mxfp8", "mxfp8", "float")),
+    (2, (1, 2, 300, 128), True, ("float", "float", "int8_head")),
+    (3, (1, 2, 300, 64), False, ("float", "float", "fp8_token")),
+    (4, (1, 2, 300, 128), False, ("float", "float", "mxfp4")),
+    (5, (1, 2, 384, 128), False, ("float", "float", "rot_fp8_block")),
+    (6, (1, 2, 300, 128), True, ("float", "float", "fp8_head")),
+    (7, (1, 2, 300, 128), False, ("float", "float", "int8_token")),
+    (8, (1, 2, 257, 64), False, ("float", "float", "mxfp8")),
+    (2, (1, 2, 300, 128), True, ("float", "float", "float")),
+    (3, (1, 2, 257, 64), False, ("float", "float", "float")),
+]
+
+
+@pytest.mark.parametrize("cfg,shape,causal,modes", MIXED)
+def test_attention_per_branch_configs(cfg, shape, causal, modes):
+    w = small_workload(cfg, shape)
+    run = GpuRun(w, modes=modes)
+    o32 = run.attention(torch.float32, causal=causal).cpu().numpy()
+    ref = oracle_attention(run, causal=causal)
+    check_attention(o32, ref, f"cfg{cfg} {shape} causal={causal} {modes}")
+    o16 = run.attention(torch.bfloat16, causal=causal)
+    assert np.array_equal(o16.view(torch.int16).cpu().numpy(), bf16_of(o32))
+
+
+@pytest.mark.parametrize("cfg,modes,rows_per_bh", [(3, ("fp8_token", "fp8_token", "float"), 8),
+                                                   (2, ("float", "float", "float"), 24)])
+def test_full_size_per_branch_configs(cfg, modes, rows_per_bh):
+    w = make_inputs(cfg)
+    run = GpuRun(w, modes=modes)
+    o = run.attention(torch.float32)
+    rows = sample_rows(cfg, w.shape[2], rows_per_bh, edge=4)
+    got = o[:, :, torch.from_numpy(rows).to(o.device)].cpu().numpy()
+    check_attention(got, oracle_attention(run, rows=rows), f"cfg{cfg} {modes} full size")
+
+
+def test_mixed_q_k_configurations_are_rejected():
+    w = small_workload(3, (1, 2, 128, 128))
+    run = GpuRun(w, modes=("fp8_token", "float", "float"))
+    with pytest.raises(faq.FaQuantError):
+        run.attention(torch.float32)
+    run = GpuRun(w, modes=("fp8_token", "fp8_token", "int8_token"))
+    with pytest.raises(faq.FaQuantError):
+        run.attention(torch.float32)
