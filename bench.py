@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the FA-quantization hot path on one MI355X.
 
-One step = quantize Q, K and V with the workload's mode, then quantized
-attention on the codes (the whole hot path; calibration of static per-head
-scales is offline - done once before timing - as the scales are frozen).
+One step = quantize Q, K and V with the workload's mode (each configured
+branch), then quantized attention on the codes (the whole hot path;
+calibration of static per-head scales is offline - done once before timing -
+as the scales are frozen).
 Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
@@ -36,7 +37,8 @@ MODE_TEXT = {"int8_head": "INT8 per-head static", "fp8_token": "FP8 E4M3 per-tok
              "fp8_head": "FP8 E4M3 per-head static", "int8_token": "INT8 per-token dynamic",
              "mxfp8": "MXFP8 per-32 block dynamic"}
 P_RULE = {"int8_head": "int8", "fp8_token": "fp8", "mxfp4": "mxfp4", "rot_fp8_block": "fp8",
-          "fp8_head": "fp8", "int8_token": "int8", "mxfp8": "mxfp8"}
+          "fp8_head": "fp8", "int8_token": "int8", "mxfp8": "mxfp8", "float": "bf16"}
+BF16_PEAK = 2500.0
 STATIC = {"int8_head": "int8", "fp8_head": "fp8_e4m3"}  # per-head static modes -> scale dtype
 
 
@@ -46,24 +48,43 @@ def attention_ops(shape, causal):
     return 4 * D * B * H * pairs
 
 
+def branch_modes(w):
+    """The mode of each branch (Q, K, V); "float" = not quantized."""
+    return tuple(w.spec.get("modes", (w.spec["mode"],) * 3))
+
+
+def peak_of(w):
+    """Dense MFMA peak the attention is quoted against: the mode's; with an
+    unquantized side, the harmonic combination of the two products' peaks
+    (each product is half the operations)."""
+    mq, _, mv = branch_modes(w)
+    pk = lambda m: BF16_PEAK if m == "float" else PEAK_TOPS[m]
+    a, b = pk(mq), pk(mv)
+    return a if a == b else round(2.0 / (1.0 / a + 1.0 / b), 1)
+
+
 def quantize_bytes(w):
-    """Algorithmic bytes of quantizing Q, K, V: input read + codes + scales."""
+    """Algorithmic bytes of quantizing the configured branches: input read +
+    codes + scales (an unquantized branch moves nothing)."""
     B, H, S, D = w.shape
     n = B * H * S * D
     inb = 4 if w.spec["dtype"] == "f32" else 2
-    mode = w.spec["mode"]
-    if mode in STATIC:
-        return 3 * (n * inb + n + H * 4)
-    if mode in ("fp8_token", "int8_token"):
-        return 3 * (n * inb + n + B * H * S * 4)
-    if mode == "mxfp4":
-        return 3 * (n * inb + n // 2 + n // 32)
-    if mode == "mxfp8":
-        return 3 * (n * inb + n + n // 32)
     tot = 0
-    for bt in (w.spec["q_block"], w.spec["kv_block"], w.spec["kv_block"]):
-        tot += n * inb + n + B * H * (-(-S // bt)) * 4
-    return tot + 2 * D * D * 2
+    for br, mode in enumerate(branch_modes(w)):
+        if mode == "float":
+            continue
+        if mode in STATIC:
+            tot += n * inb + n + H * 4
+        elif mode in ("fp8_token", "int8_token"):
+            tot += n * inb + n + B * H * S * 4
+        elif mode == "mxfp4":
+            tot += n * inb + n // 2 + n // 32
+        elif mode == "mxfp8":
+            tot += n * inb + n + n // 32
+        else:
+            bt = w.spec["q_block"] if br == 0 else w.spec["kv_block"]
+            tot += n * inb + n + B * H * (-(-S // bt)) * 4 + (D * D * 2 if br < 2 else 0)
+    return tot
 
 
 def make_step(w, dev):
@@ -71,11 +92,16 @@ def make_step(w, dev):
     import torch
     import quantized_attention_fa_amd as faq
 
-    mode = w.spec["mode"]
+    modes = branch_modes(w)
     xs = [t.to(dev) for t in (w.q, w.k, w.v)]
     rot = w.rot.to(dev) if w.rot is not None else None
     cfgs, statics, outs = [], [None] * 3, []
     for br in range(3):
+        mode = modes[br]
+        if mode == "float":
+            cfgs.append(None)
+            outs.append(faq.float_branch(xs[br]))
+            continue
         if mode in STATIC:
             cfg = faq.QConfig(STATIC[mode], "per_head")
             amax = torch.zeros(w.shape[1], dtype=torch.float32, device=dev)
@@ -101,7 +127,9 @@ def make_step(w, dev):
 
     def quantize():
         for br in range(3):
-            faq.fa_quantize(xs[br], cfgs[br], static_scale=statics[br], rot=rot if br < 2 else None, out=outs[br])
+            if cfgs[br] is not None:
+                faq.fa_quantize(xs[br], cfgs[br], static_scale=statics[br], rot=rot if br < 2 else None,
+                                out=outs[br])
 
     def attention():
         faq.fa_quant_attention(*outs, causal=w.spec["causal"], out=out, workspace=ws)
@@ -125,9 +153,9 @@ def cpu_baseline(w, budget_s=20.0):
         blas = 1
     cores = len(os.sched_getaffinity(0))
     B, H, S, D = w.shape
-    mode = w.spec["mode"]
+    modes = branch_modes(w)
     causal = w.spec["causal"]
-    rule = P_RULE[mode]
+    rule = P_RULE[modes[2]]
     t0 = time.perf_counter()
     ops = 0
     heads = 0
@@ -136,47 +164,46 @@ def cpu_baseline(w, budget_s=20.0):
     full_pairs = S * (S + 1) // 2 if causal else S * S
     if full_pairs > 4096 * 4096:
         rows = np.arange(0, S, max(1, S // 1024))
+    blocks = (w.spec.get("q_block"), w.spec.get("kv_block"), w.spec.get("kv_block"))
     for h in range(H):
         if time.perf_counter() - t0 > budget_s:
             break
         x = [t[0:1, h:h + 1].to(torch.float32).numpy() for t in (w.q, w.k, w.v)]
-        vs = None
-        if mode in STATIC:
-            deq = []
-            for br in range(3):
+        deq, scl = [], []
+        for br in range(3):
+            mode = modes[br]
+            sv = None
+            if mode == "float":
+                d = x[br].astype(np.float64)
+            elif mode in STATIC:
                 amax = None
                 for c in w.calib[br]:
                     amax = OQ.calibrate_amax(c[:, h:h + 1].to(torch.float32).numpy(), amax)
                 if mode == "int8_head":
                     s = OQ.int8_scales(amax)
-                    deq.append(OQ.dequantize_per_head(OQ.quantize_int8_per_head(x[br], s), s))
+                    d = OQ.dequantize_per_head(OQ.quantize_int8_per_head(x[br], s), s)
                 else:
                     s = OQ.fp8_scales(amax)
-                    deq.append(OQ.dequantize_per_head(OQ.quantize_fp8_per_head(x[br], s), s, F.e4m3_decode))
-                vs = np.full((1, 1, S), s[0])
-        elif mode in ("fp8_token", "int8_token"):
-            deq = []
-            for br in range(3):
-                if mode == "fp8_token":
-                    c, s = OQ.quantize_fp8_per_token(x[br])
-                    deq.append(OQ.dequantize_per_token(c, s, F.e4m3_decode))
-                else:
-                    c, s = OQ.quantize_int8_per_token(x[br])
-                    deq.append(OQ.dequantize_per_token(c, s, lambda a: a.astype(np.float64)))
-                vs = s
-        elif mode == "mxfp4":
-            deq = [OQ.dequantize_mxfp4(*OQ.quantize_mxfp4(x[br])) for br in range(3)]
-        elif mode == "mxfp8":
-            deq = [OQ.dequantize_mxfp8(*OQ.quantize_mxfp8(x[br])) for br in range(3)]
-        else:
-            R = w.rot.to(torch.float32).numpy()
-            deq = []
-            for br, bt in enumerate((w.spec["q_block"], w.spec["kv_block"], w.spec["kv_block"])):
-                y = OQ.rotate(x[br], R) if br < 2 else x[br]
-                c, s = OQ.quantize_fp8_block(y, bt)
-                st = OQ.block_scales_per_token(s, bt, S)
-                deq.append(OQ.dequantize_per_token(c, st, F.e4m3_decode))
-                vs = st
+                    d = OQ.dequantize_per_head(OQ.quantize_fp8_per_head(x[br], s), s, F.e4m3_decode)
+                sv = np.full((1, 1, S), s[0])
+            elif mode == "fp8_token":
+                c, sv = OQ.quantize_fp8_per_token(x[br])
+                d = OQ.dequantize_per_token(c, sv, F.e4m3_decode)
+            elif mode == "int8_token":
+                c, sv = OQ.quantize_int8_per_token(x[br])
+                d = OQ.dequantize_per_token(c, sv, lambda a: a.astype(np.float64))
+            elif mode == "mxfp4":
+                d = OQ.dequantize_mxfp4(*OQ.quantize_mxfp4(x[br]))
+            elif mode == "mxfp8":
+                d = OQ.dequantize_mxfp8(*OQ.quantize_mxfp8(x[br]))
+            else:
+                y = OQ.rotate(x[br], w.rot.to(torch.float32).numpy()) if br < 2 else x[br]
+                c, s = OQ.quantize_fp8_block(y, blocks[br])
+                sv = OQ.block_scales_per_token(s, blocks[br], S)
+                d = OQ.dequantize_per_token(c, sv, F.e4m3_decode)
+            deq.append(d)
+            scl.append(sv)
+        vs = scl[2]
         OA.attention(*deq, rule, v_scale=vs, causal=causal, rows=rows)
         r = np.arange(S) if rows is None else rows
         ops += 4 * D * int(np.sum(np.minimum(r + 1, S) if causal else np.full(r.size, S)))
@@ -230,7 +257,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload 1..8 (default 2, the metric's workload; 6-8 are the sibling FA modes)")
+                    help="workload 1..10 (default 2, the metric's workload; 6-8 are the sibling FA modes, "
+                         "9-10 per-branch configurations)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -251,7 +279,7 @@ def main():
         copy_calibration(dev)
         return
     w = make_inputs(args.config)
-    mode = w.spec["mode"]
+    modes = branch_modes(w)
     quantize, attention = make_step(w, dev)
     flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -283,13 +311,18 @@ def main():
     qbytes = quantize_bytes(w)
     att_ms = mean(a_ms)
     att_tops = ops / (att_ms * 1e-3) / 1e12
-    q_gbs = qbytes / (mean(q_ms) * 1e-3) / 1e9
-    peak = PEAK_TOPS[mode]
+    q_gbs = qbytes / (mean(q_ms) * 1e-3) / 1e9 if qbytes else 0.0
+    peak = peak_of(w)
+    dtypes = [DTYPE.get(m, "bf16") for m in (modes[0], modes[2])]
+    dtype = dtypes[0] if dtypes[0] == dtypes[1] else "+".join(dtypes)
+    mode_text = (MODE_TEXT[modes[0]] if len(set(modes)) == 1 and modes[0] != "float" else
+                 "Q/K " + MODE_TEXT.get(modes[0], "bf16 (not quantized)") + ", V " +
+                 MODE_TEXT.get(modes[2], "bf16 (not quantized)"))
     B, H, S, D = w.shape
     line = {
         "metric": METRIC,
         "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
-        "unit": "TOPS" if DTYPE[mode] == "int8" else "TFLOPS",
+        "unit": "TOPS" if dtype == "int8" else "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -297,18 +330,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": DTYPE[mode],
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": w.spec["name"], "mode": MODE_TEXT[mode], "B": B, "H": H, "S": S, "D": D,
+        "config": {"workload": w.spec["name"], "mode": mode_text, "B": B, "H": H, "S": S, "D": D,
                    "causal": w.spec["causal"], "input_dtype": w.spec["dtype"]},
         "roofline": {"bound": "mfma", "achieved": round(att_tops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(att_tops / peak, 4), "traffic": recorded_traffic(w.spec["name"]),
                      "kernel": "fa_quant_attention: k_prep (V / K re-layout) + k_attn (fused attention)",
                      "attention_source": source_digest(),
                      "ops_per_launch": ops, "ms_per_launch": round(att_ms, 4)},
-        "quantize": {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(q_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": qbytes,
-                     "ms_per_step": round(mean(q_ms), 4)},
+        "quantize": ({"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(q_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": qbytes,
+                      "ms_per_step": round(mean(q_ms), 4)} if qbytes else None),
         "timing": {"method": "hip events on the compute stream, per step", "min_step_ms": round(min(step_ms), 4),
                    "wall_s_incl_flush": round(wall, 3), "cache_flush_between_steps": flush is not None},
     }

@@ -28,6 +28,10 @@ workload of their own family:
   6  FP8 per-head static: as 2 (calibration batch, outliers, causal).
   7  INT8 per-token dynamic: as 3 (log-normal row magnitudes).
   8  MXFP8 per-block dynamic: as 4 (Student-t(4)).
+Per-branch configurations (an unconfigured branch is not quantized):
+  9  FP8 per-token Q and K, V unquantized (bf16): as 3.
+  10 no branch quantized (bf16 attention): as 2, without outliers' effect on
+     any scale (the tensors are the same recipe).
 """
 
 from dataclasses import dataclass, field
@@ -56,6 +60,11 @@ CONFIGS: Dict[int, dict] = {
             shape=(1, 40, 32760, 128), causal=False),
     8: dict(name="mxfp8_per_block_image_edit", mode="mxfp8", dtype="bf16", dist="t4",
             shape=(1, 24, 8192, 128), causal=False),
+    9: dict(name="fp8_qk_bf16_v_video_dit", mode="fp8_token", dtype="bf16", dist="lognormal_rows",
+            shape=(1, 40, 32760, 128), causal=False, modes=("fp8_token", "fp8_token", "float")),
+    10: dict(name="bf16_attention_prefill", mode="float", dtype="bf16", dist="normal",
+             shape=(2, 32, 4096, 128), causal=True, outlier_frac=0.005, outlier_gain=20.0,
+             modes=("float", "float", "float")),
 }
 
 TID_Q, TID_K, TID_V = 0, 1, 2
@@ -122,7 +131,7 @@ class Workload:
 
 
 def make_inputs(cfg: int, shape=None, calib_batch=None) -> Workload:
-    """CPU tensors for workload `cfg` (1..8).  `shape` overrides the BNSD
+    """CPU tensors for workload `cfg` (1..10).  `shape` overrides the BNSD
     shape with the same recipe (smaller test cases); `calib_batch` overrides
     the calibration batch size of workload 2."""
     spec = dict(CONFIGS[cfg])
