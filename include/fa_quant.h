@@ -17,8 +17,11 @@
  *     per-token dynamic and MXFP8 per-block dynamic.
  *
  * Conventions shared by every entry point:
- *   - Tensors are BNSD [B, H, S, D], contiguous, row-major ("量化" page,
- *     注意事项: BNSD input layout).  D must be 64 or 128.
+ *   - Tensors are contiguous, row-major, in one of the two layouts the
+ *     "量化" page (注意事项) lists for Q/K/V: BNSD [B, H, S, D] or BSND
+ *     [B, S, H, D] (faq_shape.layout).  Shapes are always given as the
+ *     logical (B, H, S, D); scale arrays are always indexed (b, h, s) in
+ *     that order, whatever the layout of the tensor.  D must be 64 or 128.
  *   - Every tensor pointer is a DEVICE pointer, except the descriptor structs
  *     themselves (faq_shape, faq_qconfig, faq_qtensor), which live in host
  *     memory and are read during the call only.  The caller owns every
@@ -84,8 +87,12 @@ typedef struct {
                            positive multiple of 128 is accepted               */
 } faq_qconfig;
 
+/* Memory layout of a tensor with logical shape (B, H, S, D). */
+typedef enum { FAQ_LAYOUT_BNSD = 0, FAQ_LAYOUT_BSND = 1 } faq_layout;
+
 typedef struct {
   int64_t B, H, S, D;
+  int64_t layout; /* faq_layout; 0 (BNSD) when zero-initialised */
 } faq_shape;
 
 /* A quantized tensor: codes and scales in device memory.
@@ -93,6 +100,9 @@ typedef struct {
            FP8_E4M3   uint8 E4M3FN bit patterns [B,H,S,D]
            MXFP4      uint8 [B,H,S,D/2], element 2i in the low nibble
            MXFP8      uint8 E4M3FN bit patterns [B,H,S,D]
+           FLOAT      (attention only: an unquantized branch) the bf16
+                      values [B,H,S,D]; scales unused (may be NULL)
+           in shape.layout (BSND: [B,S,H,.] with the same last dimension)
    scales: see faq_scope.  fa_quant_codes_bytes / fa_quant_scales_bytes give
    the sizes. */
 typedef struct {
@@ -134,7 +144,8 @@ faq_status fa_quant_scales_from_amax(const float* amax, int64_t H, int32_t dtype
                the tensor is replaced by Y = bf16_rne(X . R) before block
                quantization ("量化" page, FA量化 / 技术特点: 旋转 of Q and K
                by q_rot / k_rot).  NULL = no rotation (the V branch).
-   out         shape must equal *shape; codes/scales must hold the sizes
+   out         shape (layout included) must equal *shape: codes are
+               written in the layout of x; codes/scales must hold the sizes
                the size queries report.
    debug_rotated optional device bf16 [B,H,S,D]: receives Y when rot != NULL.
    Codes and scales are bit-exact functions of the inputs:
@@ -165,8 +176,9 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
                equal; k and v share S.
    sm_scale    softmax scale; 0 means 1/sqrt(D).
    causal      1: key j is masked for query i when j > i (needs Sq == Skv).
-   out         device [B,H,Sq,D], out_dtype F32 or BF16 (bf16 = the float
-               result rounded to nearest even).
+   out         device [B,H,Sq,D] in q's layout, out_dtype F32 or BF16
+               (bf16 = the float result rounded to nearest even).  q, k and
+               v may have different layouts.
    workspace   device buffer of at least fa_quant_attention_workspace_bytes.
    Probabilities enter the PV product quantized per 128-key tile relative
    to the tile's own row maximum: int8 round(127 p w_j) or E4M3 of

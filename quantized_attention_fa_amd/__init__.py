@@ -33,6 +33,8 @@ _DTYPES = {"float": FAQ_FLOAT, "int8": FAQ_INT8, "fp8_e4m3": FAQ_FP8_E4M3, "mxfp
 _SCOPES = {"per_head": FAQ_PER_HEAD, "per_token": FAQ_PER_TOKEN, "per_block": FAQ_PER_BLOCK,
            "per_token_block": FAQ_PER_TOKEN_BLOCK}
 _METHODS = {"minmax": 0}
+# Q/K/V memory layouts ("量化" page, 注意事项: BNSD and BSND)
+_LAYOUTS = {"bnsd": _abi.FAQ_LAYOUT_BNSD, "bsnd": _abi.FAQ_LAYOUT_BSND}
 
 
 class FaQuantError(RuntimeError):
@@ -81,25 +83,29 @@ def resolve_fa3_config(qconfig: Optional[QConfig] = None,
 
 @dataclass
 class QTensor:
-    """Quantized BNSD tensor: device codes + scales and their config."""
+    """Quantized tensor: device codes + scales and their config.  `shape` is
+    the logical (B, H, S, D); the codes are laid out as `layout` ("bnsd" or
+    "bsnd"); scales are indexed (b, h, s)."""
     cfg: QConfig
     shape: tuple
     codes: torch.Tensor
     scales: torch.Tensor
+    layout: str = "bnsd"
 
     def to_c(self) -> _abi.faq_qtensor:
-        return _abi.faq_qtensor(self.cfg.to_c(), _abi.faq_shape(*self.shape),
+        return _abi.faq_qtensor(self.cfg.to_c(), _abi.faq_shape(*self.shape, _LAYOUTS[self.layout]),
                                 self.codes.data_ptr(), self.scales.data_ptr())
 
 
-def float_branch(x: torch.Tensor) -> QTensor:
+def float_branch(x: torch.Tensor, layout: str = "bnsd") -> QTensor:
     """An unquantized branch ("fa3_quant 配置说明" §2.3: a branch without a
     configuration is not quantized): the bf16 tensor itself, passed to
     fa_quant_attention as a QTensor of dtype "float" (no scales)."""
-    shape = _bnsd(x, "float_branch")
+    shape = _bnsd(x, "float_branch", layout)
     if x.dtype != torch.bfloat16:
         raise FaQuantError(_abi.FAQ_ERR_UNSUPPORTED, "float_branch: unquantized branches are bf16")
-    return QTensor(QConfig("float", "per_head"), shape, x, torch.empty(0, dtype=torch.uint8, device=x.device))
+    return QTensor(QConfig("float", "per_head"), shape, x, torch.empty(0, dtype=torch.uint8, device=x.device),
+                   layout)
 
 
 def fa_quant_status_string(status: int) -> str:
@@ -123,10 +129,19 @@ def _tdtype(t: torch.Tensor) -> int:
     raise FaQuantError(_abi.FAQ_ERR_UNSUPPORTED, f"input dtype {t.dtype}")
 
 
-def _bnsd(x: torch.Tensor, where: str) -> tuple:
+def _bnsd(x: torch.Tensor, where: str, layout: str = "bnsd") -> tuple:
+    """Logical (B, H, S, D) of a contiguous device tensor in `layout`."""
     if x.dim() != 4 or not x.is_contiguous() or not x.is_cuda:
-        raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG, f"{where}: need a contiguous CUDA BNSD tensor")
-    return tuple(int(s) for s in x.shape)
+        raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG, f"{where}: need a contiguous CUDA 4-d tensor")
+    if layout not in _LAYOUTS:
+        raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG, f"{where}: layout must be 'bnsd' or 'bsnd'")
+    d = tuple(int(s) for s in x.shape)
+    return d if layout == "bnsd" else (d[0], d[2], d[1], d[3])
+
+
+def _physical(shape: tuple, layout: str, last: int) -> tuple:
+    B, H, S, _ = shape
+    return (B, H, S, last) if layout == "bnsd" else (B, S, H, last)
 
 
 def fa_quant_codes_bytes(cfg: QConfig, shape) -> int:
@@ -139,12 +154,12 @@ def fa_quant_scales_bytes(cfg: QConfig, shape) -> int:
     return int(_abi.lib().fa_quant_scales_bytes(ctypes.byref(c), ctypes.byref(s)))
 
 
-def fa_quant_calibrate(x: torch.Tensor, amax: torch.Tensor) -> torch.Tensor:
+def fa_quant_calibrate(x: torch.Tensor, amax: torch.Tensor, layout: str = "bnsd") -> torch.Tensor:
     """Running per-head max|x| into `amax` (float32 [H] on the device)."""
-    shape = _bnsd(x, "fa_quant_calibrate")
+    shape = _bnsd(x, "fa_quant_calibrate", layout)
     if amax.dtype != torch.float32 or amax.numel() != shape[1] or not amax.is_cuda:
         raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG, "fa_quant_calibrate: amax must be float32 [H] on the GPU")
-    s = _abi.faq_shape(*shape)
+    s = _abi.faq_shape(*shape, _LAYOUTS[layout])
     _check(_abi.lib().fa_quant_calibrate(x.data_ptr(), _tdtype(x), ctypes.byref(s), amax.data_ptr(), _stream(x)),
            "fa_quant_calibrate")
     return amax
@@ -158,10 +173,11 @@ def fa_quant_scales_from_amax(amax: torch.Tensor, dtype: str = "int8", out: torc
 
 
 def fa_quantize(x: torch.Tensor, cfg: QConfig, static_scale: torch.Tensor = None, rot: torch.Tensor = None,
-                debug_rotated: torch.Tensor = None, out: QTensor = None) -> QTensor:
-    shape = _bnsd(x, "fa_quantize")
+                debug_rotated: torch.Tensor = None, out: QTensor = None, layout: str = "bnsd") -> QTensor:
+    """Quantize one branch; x and its codes are laid out as `layout`."""
+    shape = _bnsd(x, "fa_quantize", layout)
     lib = _abi.lib()
-    c, s = cfg.to_c(), _abi.faq_shape(*shape)
+    c, s = cfg.to_c(), _abi.faq_shape(*shape, _LAYOUTS[layout])
     if out is None:
         nc = lib.fa_quant_codes_bytes(ctypes.byref(c), ctypes.byref(s))
         ns = lib.fa_quant_scales_bytes(ctypes.byref(c), ctypes.byref(s))
@@ -171,13 +187,13 @@ def fa_quantize(x: torch.Tensor, cfg: QConfig, static_scale: torch.Tensor = None
         codes = torch.empty(nc, dtype=cdt, device=x.device)
         if cfg.dtype in ("mxfp4", "mxfp8"):
             cd = shape[3] // 2 if cfg.dtype == "mxfp4" else shape[3]
-            codes = codes.view(shape[0], shape[1], shape[2], cd)
+            codes = codes.view(*_physical(shape, layout, cd))
             scales = torch.empty(ns, dtype=torch.uint8, device=x.device).view(shape[0], shape[1], shape[2],
                                                                                shape[3] // 32)
         else:
-            codes = codes.view(*shape)
+            codes = codes.view(*_physical(shape, layout, shape[3]))
             scales = torch.empty(max(ns // 4, 0), dtype=torch.float32, device=x.device)
-        out = QTensor(cfg, shape, codes, scales)
+        out = QTensor(cfg, shape, codes, scales, layout)
     qt = out.to_c()
     st = lib.fa_quantize(x.data_ptr(), _tdtype(x), ctypes.byref(s), ctypes.byref(c),
                          static_scale.data_ptr() if static_scale is not None else None,
@@ -199,7 +215,7 @@ def fa_quant_attention(q: QTensor, k: QTensor, v: QTensor, sm_scale: float = 0.0
     qc, kc, vc = q.to_c(), k.to_c(), v.to_c()
     dev = q.codes.device
     if out is None:
-        out = torch.empty((q.shape[0], q.shape[1], q.shape[2], q.shape[3]), dtype=out_dtype, device=dev)
+        out = torch.empty(_physical(q.shape, q.layout, q.shape[3]), dtype=out_dtype, device=dev)
     odt = FAQ_T_BF16 if out.dtype == torch.bfloat16 else FAQ_T_F32 if out.dtype == torch.float32 else -1
     if workspace is None:
         need = lib.fa_quant_attention_workspace_bytes(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc))

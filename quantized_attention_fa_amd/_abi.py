@@ -19,6 +19,7 @@ FAQ_ERR_WORKSPACE = -7
 
 # faq_dtype
 FAQ_FLOAT, FAQ_INT8, FAQ_FP8_E4M3, FAQ_MXFP4, FAQ_MXFP8 = 0, 1, 2, 3, 4
+FAQ_LAYOUT_BNSD, FAQ_LAYOUT_BSND = 0, 1
 # faq_scope
 FAQ_PER_HEAD, FAQ_PER_TOKEN, FAQ_PER_BLOCK, FAQ_PER_TOKEN_BLOCK = 0, 1, 2, 3
 # faq_tdtype
@@ -47,7 +48,8 @@ class faq_qconfig(ctypes.Structure):
 
 
 class faq_shape(ctypes.Structure):
-    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("S", ctypes.c_int64), ("D", ctypes.c_int64)]
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("S", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("layout", ctypes.c_int64)]
 
 
 class faq_qtensor(ctypes.Structure):

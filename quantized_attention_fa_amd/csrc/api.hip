@@ -30,8 +30,11 @@ faq_status hip_status(hipError_t e, const char* fn) {
   return FAQ_ERR_HIP;
 }
 
+// Non-negative sizes, a known layout, and rows (B H S) that index in 32 bits.
 bool shape_ok(const faq_shape* s) {
-  return s && s->B >= 0 && s->H >= 0 && s->S >= 0 && s->D >= 0;
+  return s && s->B >= 0 && s->H >= 0 && s->S >= 0 && s->D >= 0 &&
+         (s->layout == FAQ_LAYOUT_BNSD || s->layout == FAQ_LAYOUT_BSND) &&
+         (s->H == 0 || s->S == 0 || s->B <= (int64_t)INT32_MAX / s->H / s->S);
 }
 
 bool d_supported(int64_t D) { return D == 64 || D == 128; }
@@ -39,7 +42,7 @@ bool d_supported(int64_t D) { return D == 64 || D == 128; }
 int64_t numel(const faq_shape& s) { return s.B * s.H * s.S * s.D; }
 
 bool same_shape(const faq_shape& a, const faq_shape& b) {
-  return a.B == b.B && a.H == b.H && a.S == b.S && a.D == b.D;
+  return a.B == b.B && a.H == b.H && a.S == b.S && a.D == b.D && a.layout == b.layout;
 }
 
 bool same_cfg(const faq_qconfig& a, const faq_qconfig& b) {
@@ -289,6 +292,7 @@ faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const 
   a.qk = qk;
   a.pv = pv;
   a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv; a.D = D;
+  a.qmap = row_map(q->shape); a.kmap = row_map(k->shape); a.vmap = row_map(v->shape);
   a.q_codes = q->codes; a.q_scales = q->scales;
   a.k_codes = k->codes; a.k_scales = k->scales;
   a.v_codes = v->codes; a.v_scales = v->scales;

@@ -207,6 +207,7 @@ struct PrepArgs {
   const void* ks;
   const uint8_t* v;
   const void* vs;
+  RowMap kmap, vmap;  // rows of K and V codes (BNSD or BSND)
   int64_t H, Skv, nt, ksb, ksh, vsb, vsh;
   int kblk, vblk;
   uint8_t* vt;
@@ -229,12 +230,13 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
   const int64_t bh = blockIdx.y;
   const int64_t k0 = (int64_t)t * BN;
   const int64_t tile_id = bh * a.nt + t;
+  const int64_t b_ = bh / a.H, h_ = bh % a.H;
   uint8_t* auxt = a.aux + tile_id * C::XBYTES;
   // V rows -> LDS
   for (int c = threadIdx.x; c < BN * (VR / 16); c += 256) {
     const int kl = c / (VR / 16), cc = c % (VR / 16);
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (k0 + kl < a.Skv) val = *reinterpret_cast<const uint4*>(a.v + (bh * a.Skv + k0 + kl) * VR + cc * 16);
+    if (k0 + kl < a.Skv) val = *reinterpret_cast<const uint4*>(a.v + a.vmap.row(b_, h_, k0 + kl) * VR + cc * 16);
     uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[kl][cc * 16]);
     dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
   }
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
       uint4 kv = make_uint4(0, 0, 0, 0);
       float sc = 1.0f;
       if (k0 + kl < a.Skv) {
-        kv = *reinterpret_cast<const uint4*>(a.k + (bh * a.Skv + k0 + kl) * D + cc * 16);
+        kv = *reinterpret_cast<const uint4*>(a.k + a.kmap.row(b_, h_, k0 + kl) * D + cc * 16);
         if (QK == QK_MX8) {
           const uint8_t* ke = reinterpret_cast<const uint8_t*>(a.ks) + (bh * a.Skv + k0 + kl) * NB;
           int emax = 0;
@@ -370,6 +372,7 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
 struct KParams {
   int64_t H, BH, Sq, Skv, nt;
   int nqt;
+  RowMap qmap, kmap, omap;  // rows of Q codes, K codes (when gathered) and the output
   const uint8_t* q;      // Q codes or bf16 values
   const void* qs;        // Q scales
   const uint8_t* k;      // K codes / bf16 values, or the bf16 K images in the workspace
@@ -460,7 +463,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   const int q0 = qt * BM + wave * 32;  // this wave's first query
   const int qi = q0 + j;               // this lane's query
   const bool act = q0 < Sq;            // uniform per wave: any query to compute
-  const uint8_t* kbase = p.k + (G::QIMG ? bh * nt * (int64_t)G::KBYTES : bh * (int64_t)Skv * G::KROW);
+  const int64_t bb = bh / p.H;
+  // K rows gathered from the codes: row r of head (b, h) at kbase + r kstride
+  const uint8_t* kbase = p.k + (G::QIMG ? bh * nt * (int64_t)G::KBYTES : p.kmap.row(bb, hd, 0) * G::KROW);
+  const uint32_t kstride = (uint32_t)(p.kmap.ss * G::KROW);
   const uint8_t* vtbase = p.vt + bh * nt * (int64_t)G::VBYTES;
   const uint8_t* auxbase = p.aux + bh * nt * (int64_t)G::XBYTES;
 
@@ -473,11 +479,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   float cq;
   {
     const bool ok = qi < Sq;
-    const int64_t qrow_i = bh * p.Sq + (ok ? qi : 0);
+    const int64_t qrow_i = bh * p.Sq + (ok ? qi : 0);      // logical row (scales)
+    const int64_t qmem = p.qmap.row(bb, hd, ok ? qi : 0);  // memory row (codes)
     // per-token / token-block / per-head float Q scale of this query
     const int64_t qsi = (bh / p.H) * p.q_sb + hd * p.q_sh + (ok ? qi : 0) / p.q_block;
     if (QK == QK_BF) {
-      const uint8_t* qrow = p.q + qrow_i * (2 * D);
+      const uint8_t* qrow = p.q + qmem * (2 * D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         uint4 a = make_uint4(0, 0, 0, 0);
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       }
       cq = p.c_log2;
     } else if (G::QBF) {
-      const uint8_t* qrow = p.q + qrow_i * D;
+      const uint8_t* qrow = p.q + qmem * D;
       // MXFP8: the row relative to its largest block exponent
       int eb[QK == QK_MX8 ? NB : 1], emax = 127;
       if (QK == QK_MX8) {
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       if (QK == QK_MX8) cq = __builtin_amdgcn_ldexpf(1.0f, emax - 127) * p.c_log2;
       else cq = (ok ? reinterpret_cast<const float*>(p.qs)[qsi] : 1.0f) * p.c_log2;
     } else if (G::QI8) {
-      const uint8_t* qrow = p.q + qrow_i * D;
+      const uint8_t* qrow = p.q + qmem * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         uint4 a = make_uint4(0, 0, 0, 0);
@@ -522,7 +529,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       if (QK == QK_I8H) cq = qs[hd] * reinterpret_cast<const float*>(p.ks)[hd] * p.c_log2;
       else cq = (ok ? qs[qsi] : 1.0f) * p.c_log2;
     } else {
-      const uint8_t* qrow = p.q + qrow_i * (D / 2);
+      const uint8_t* qrow = p.q + qmem * (D / 2);
       const uint8_t* qe = reinterpret_cast<const uint8_t*>(p.qs) + qrow_i * NB;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       stage<G::KBYTES / 16>(kbuf, kbase + (int64_t)t * G::KBYTES, wave, lane,
                             [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
     } else {
-      const uint32_t roff = (uint32_t)(min(t * BN + krow, Skv - 1) * G::KROW) + (uint32_t)((pw >> 7) * 16);
+      const uint32_t roff = (uint32_t)min(t * BN + krow, Skv - 1) * kstride + (uint32_t)((pw >> 7) * 16);
       stage<G::KBYTES / 16>(kbuf, kbase, wave, lane, [&](int i) { return roff + (uint32_t)(2 * i * 16); });
     }
     if (G::XKBYTES > 0)
@@ -897,7 +904,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const int64_t off = (bh * p.Sq + qi) * D + 32 * db + 8 * a4 + 4 * h;
+        const int64_t off = p.omap.row(bb, hd, qi) * D + 32 * db + 8 * a4 + 4 * h;
         const float o0 = O[db][4 * a4] * inv, o1 = O[db][4 * a4 + 1] * inv;
         const float o2 = O[db][4 * a4 + 2] * inv, o3 = O[db][4 * a4 + 3] * inv;
         if (p.out_bf16) {
@@ -919,6 +926,7 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   PrepArgs pa{};
   pa.k = (const uint8_t*)a.k_codes; pa.ks = a.k_scales;
   pa.v = (const uint8_t*)a.v_codes; pa.vs = a.v_scales;
+  pa.kmap = a.kmap; pa.vmap = a.vmap;
   pa.H = a.H; pa.Skv = a.Skv; pa.nt = nt;
   pa.ksb = a.k_sb; pa.ksh = a.k_sh; pa.kblk = a.k_block;
   pa.vsb = a.v_sb; pa.vsh = a.v_sh; pa.vblk = a.v_block;
@@ -930,6 +938,7 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   KParams p{};
   p.H = a.H; p.BH = a.B * a.H; p.Sq = a.Sq; p.Skv = a.Skv; p.nt = nt;
   p.nqt = (int)((a.Sq + BM - 1) / BM);
+  p.qmap = a.qmap; p.kmap = a.kmap; p.omap = a.qmap;
   p.q = (const uint8_t*)a.q_codes; p.qs = a.q_scales;
   p.k = G::QIMG ? ws + l.kb_off : (const uint8_t*)a.k_codes;
   p.ks = a.k_scales;

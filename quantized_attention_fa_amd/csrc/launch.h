@@ -8,9 +8,24 @@
 
 namespace faq {
 
+// Row (in units of D elements) of token (b, h, s) of a contiguous tensor
+// in either layout: BNSD rows are (b H + h) S + s, BSND rows (b S + s) H + h.
+struct RowMap {
+  int64_t sb, sh, ss;
+  int ident;  // BNSD: logical row index == memory row index
+  __host__ __device__ int64_t row(int64_t b, int64_t h, int64_t s) const { return b * sb + h * sh + s * ss; }
+};
+
+inline RowMap row_map(const faq_shape& s) {
+  if (s.layout == FAQ_LAYOUT_BSND) return RowMap{s.S * s.H, 1, s.H, s.H == 1 ? 1 : 0};
+  return RowMap{s.H * s.S, s.S, 1, 1};
+}
+
 // ---- quantization (quant.hip)
 hipError_t launch_calibrate(const void* x, int x_dtype, const faq_shape& s, float* amax,
                             hipStream_t st);
+// Every quantizer reads x and writes its codes in the layout of `s`; scales
+// are indexed (b, h, s).
 hipError_t launch_scales_from_amax(const float* amax, int64_t H, float qmax, float* scale,
                                    hipStream_t st);
 hipError_t launch_quant_int8_head(const void* x, int x_dtype, const faq_shape& s,
@@ -54,6 +69,7 @@ struct AttnArgs {
   // b * sb + h * sh + token / block
   int q_block, k_block, v_block;
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh;
+  RowMap qmap, kmap, vmap;  // memory rows of Q, K, V (the output takes Q's layout)
   float sm_scale;
   int causal;
   void* out;

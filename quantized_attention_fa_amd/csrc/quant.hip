@@ -20,17 +20,30 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Memory row of logical row r = (b H + h) S + s (rows below 2^32).
+FAQ_DEV int64_t mem_row(const RowMap& m, int64_t r, uint32_t H, uint32_t S) {
+  if (m.ident) return r;
+  const uint32_t r32 = (uint32_t)r, bh = r32 / S, s = r32 - bh * S, b = bh / H, h = bh - b * H;
+  return m.row(b, h, s);
+}
+
+// Element offset of element i (0 <= i < S D) of the (b, h) slice: rows of D
+// = 2^dsh elements, consecutive tokens m.ss rows apart.
+FAQ_DEV int64_t slice_off(int64_t row0, int64_t i, const RowMap& m, int dsh) {
+  return ((row0 + (i >> dsh) * m.ss) << dsh) + (i & ((1 << dsh) - 1));
+}
+
 // ------------------------------------------------------------------------
 // Min-max calibration: amax[h] = max(amax[h], max |x[b,h,:,:]|).
 // grid = (chunks per (b,h) slice, B*H); the float bits of a non-negative
 // value order like unsigned integers, so the running max is an atomicMax.
 // ------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_calibrate(const T* __restrict__ x, int64_t per_bh,
+__global__ __launch_bounds__(kThreads) void k_calibrate(const T* __restrict__ x, RowMap rm, int dsh, int64_t per_bh,
                                                         int H, float* __restrict__ amax) {
   constexpr int U = 4;
   const int64_t bh = blockIdx.y;
-  const T* base = x + bh * per_bh;
+  const int64_t row0 = rm.row(bh / H, bh % H, 0);
   float m = 0.0f;
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads * 8 * U; c0 < per_bh;
        c0 += (int64_t)gridDim.x * kThreads * 8 * U) {
@@ -39,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void k_calibrate(const T* __restrict__ x,
     for (int u = 0; u < U; ++u) {
       const int64_t i = c0 + ((int64_t)u * kThreads + threadIdx.x) * 8;
       if (i < per_bh) {
-        load8(base + i, v[u]);
+        load8(x + slice_off(row0, i, rm, dsh), v[u]);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
@@ -71,7 +84,8 @@ __global__ void k_scales_from_amax(const float* amax, int64_t H, float qmax, flo
 // grid = (chunks per (b,h) slice, B*H); 16 elements per thread-vector.
 // ------------------------------------------------------------------------
 template <bool FAST, bool FP8, typename T>
-FAQ_DEV void head_slice(const T* __restrict__ src, uint8_t* __restrict__ dst, int64_t per_bh, float s) {
+FAQ_DEV void head_slice(const T* __restrict__ src, uint8_t* __restrict__ dst, int64_t row0, const RowMap& rm,
+                        int dsh, int64_t per_bh, float s) {
   constexpr int U = 2;
   const float r = 1.0f / s;
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads * 16 * U; c0 < per_bh;
@@ -81,9 +95,10 @@ FAQ_DEV void head_slice(const T* __restrict__ src, uint8_t* __restrict__ dst, in
     for (int u = 0; u < U; ++u) {
       const int64_t i = c0 + ((int64_t)u * kThreads + threadIdx.x) * 16;
       if (i < per_bh) {
+        const int64_t o = slice_off(row0, i, rm, dsh);
         float a[8], b[8];
-        load8(src + i, a);
-        load8(src + i + 8, b);
+        load8(src + o, a);
+        load8(src + o + 8, b);
 #pragma unroll
         for (int k = 0; k < 8; ++k) { v[u][k] = a[k]; v[u][8 + k] = b[k]; }
       }
@@ -104,7 +119,7 @@ FAQ_DEV void head_slice(const T* __restrict__ src, uint8_t* __restrict__ dst, in
             w[j] = pack_low_bytes(c[0], c[1], c[2], c[3]);
           }
         }
-        *reinterpret_cast<uint4*>(dst + i) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(dst + slice_off(row0, i, rm, dsh)) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   }
@@ -112,14 +127,15 @@ FAQ_DEV void head_slice(const T* __restrict__ src, uint8_t* __restrict__ dst, in
 
 template <typename T, bool FP8>
 __global__ __launch_bounds__(kThreads) void k_quant_head(const T* __restrict__ x,
-                                                         const float* __restrict__ scale,
+                                                         const float* __restrict__ scale, RowMap rm, int dsh,
                                                          int64_t per_bh, int H,
                                                          uint8_t* __restrict__ codes) {
   const int64_t bh = blockIdx.y;
   const float s = scale[bh % H];
+  const int64_t row0 = rm.row(bh / H, bh % H, 0);
   // the head's scale picks the division path once for the whole slice
-  if (div_fast_ok(s)) head_slice<true, FP8>(x + bh * per_bh, codes + bh * per_bh, per_bh, s);
-  else head_slice<false, FP8>(x + bh * per_bh, codes + bh * per_bh, per_bh, s);
+  if (div_fast_ok(s)) head_slice<true, FP8>(x, codes, row0, rm, dsh, per_bh, s);
+  else head_slice<false, FP8>(x, codes, row0, rm, dsh, per_bh, s);
 }
 
 // ------------------------------------------------------------------------
@@ -128,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_head(const T* __restrict__ x
 // D/16 threads per row, 16 elements per thread.
 // ------------------------------------------------------------------------
 template <typename T, int D, bool I8>
-__global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ x, int64_t rows,
-                                                          uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ x, int64_t rows, RowMap rm,
+                                                          uint32_t H, uint32_t S, uint8_t* __restrict__ codes,
                                                           float* __restrict__ scales) {
   constexpr int EPT = 16, TPR = D / EPT, RPB = kThreads / TPR, U = 2;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
@@ -139,9 +155,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ 
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       if (row < rows) {
+        const int64_t mr = mem_row(rm, row, H, S);
         float a[8], b[8];
-        load8(x + row * D + sub * EPT, a);
-        load8(x + row * D + sub * EPT + 8, b);
+        load8(x + mr * D + sub * EPT, a);
+        load8(x + mr * D + sub * EPT + 8, b);
 #pragma unroll
         for (int k = 0; k < 8; ++k) { v[u][k] = a[k]; v[u][8 + k] = b[k]; }
       } else {
@@ -161,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ 
       if (I8) int8_code_words<EPT>(v[u], s, w);
       else e4m3_code_words<EPT>(v[u], s, w);
       if (row < rows) {
-        *reinterpret_cast<uint4*>(codes + row * D + sub * EPT) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(codes + mem_row(rm, row, H, S) * D + sub * EPT) = make_uint4(w[0], w[1], w[2], w[3]);
         if (sub == 0) scales[row] = s;
       }
     }
@@ -173,8 +190,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ 
 // D/8 threads per row; 4 threads per 32-element block.
 // ------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ x, int64_t rows,
-                                                          uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ x, int64_t rows, RowMap rm,
+                                                          uint32_t H, uint32_t S, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ e8m0) {
   constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 4, NB = D / 32;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
@@ -185,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       if (row < rows) {
-        load8(x + row * D + sub * 8, v[u]);
+        load8(x + mem_row(rm, row, H, S) * D + sub * 8, v[u]);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
@@ -223,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
 #pragma unroll
       for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
       if (row < rows) {
-        *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + sub * 4) = packed;
+        *reinterpret_cast<uint32_t*>(codes + mem_row(rm, row, H, S) * (D / 2) + sub * 4) = packed;
         if (sub == 0) {
           if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + row * NB) = word;
           else *reinterpret_cast<uint16_t*>(e8m0 + row * NB) = (uint16_t)word;
@@ -239,8 +256,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
 // saturating at 448 (FA PerBlock, MXFP8).  D/8 threads per row, 4 per block.
 // ------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ x, int64_t rows,
-                                                          uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ x, int64_t rows, RowMap rm,
+                                                          uint32_t H, uint32_t S, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ e8m0) {
   constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 4, NB = D / 32;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
@@ -251,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ 
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       if (row < rows) {
-        load8(x + row * D + sub * 8, v[u]);
+        load8(x + mem_row(rm, row, H, S) * D + sub * 8, v[u]);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
@@ -281,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ 
 #pragma unroll
       for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
       if (row < rows) {
-        *reinterpret_cast<uint2*>(codes + row * D + sub * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
+        *reinterpret_cast<uint2*>(codes + mem_row(rm, row, H, S) * D + sub * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
         if (sub == 0) {
           if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + row * NB) = word;
           else *reinterpret_cast<uint16_t*>(e8m0 + row * NB) = (uint16_t)word;
@@ -298,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ 
 // reduction and the encode.
 // ------------------------------------------------------------------------
 template <int D, int BT>
-__global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __restrict__ x, RowMap rm, int H,
                                                               int64_t S, int nblk,
                                                               uint8_t* __restrict__ codes,
                                                               float* __restrict__ scales) {
@@ -307,14 +324,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __
   const int blk = blockIdx.x;
   const int64_t tok0 = (int64_t)blk * BT;
   const int64_t ntok = (S - tok0) < BT ? (S - tok0) : BT;
-  const uint16_t* src = x + (bh * S + tok0) * D;
-  uint8_t* dst = codes + (bh * S + tok0) * D;
+  // element e of the block: token tok0 + e / D, channel e % D
+  const int64_t row0 = rm.row(bh / H, bh % H, tok0);
+  auto off = [&](int e) { return (row0 + (int64_t)(e / D) * rm.ss) * D + e % D; };
   uint4 raw[NV];
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = (i * kThreads + threadIdx.x) * 8;
-    raw[i] = (e / D < ntok) ? *reinterpret_cast<const uint4*>(src + e) : make_uint4(0, 0, 0, 0);
+    raw[i] = (e / D < ntok) ? *reinterpret_cast<const uint4*>(x + off(e)) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -338,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __
       for (int j = 0; j < 4; ++j) { f[2 * j] = bf16_lo(w[j]); f[2 * j + 1] = bf16_hi(w[j]); }
       uint32_t c[2];
       e4m3_code_words<8>(f, s, c);
-      *reinterpret_cast<uint2*>(dst + e) = make_uint2(c[0], c[1]);
+      *reinterpret_cast<uint2*>(codes + off(e)) = make_uint2(c[0], c[1]);
     }
   }
   if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
@@ -357,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __
 // ------------------------------------------------------------------------
 template <int D, int BT>
 __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ rot,
+                                                          const uint16_t* __restrict__ rot, RowMap rm, int H,
                                                           int64_t S, int nblk, int64_t nwork,
                                                           uint8_t* __restrict__ codes,
                                                           float* __restrict__ scales,
@@ -375,7 +393,7 @@ __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __rest
     const int64_t bh = work / nblk;
     const int blk = (int)(work % nblk);
     const int64_t tok0 = (int64_t)blk * BT + w * 32;
-    const uint16_t* src = x + bh * S * D;
+    const int64_t row0 = rm.row(bh / H, bh % H, 0);  // token tok is row row0 + tok rm.ss
     bf16x8 xb[2][KK];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -383,7 +401,7 @@ __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __rest
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         uint4 r = make_uint4(0, 0, 0, 0);
-        if (tok < S) r = *reinterpret_cast<const uint4*>(src + tok * D + kk * 32 + g * 8);
+        if (tok < S) r = *reinterpret_cast<const uint4*>(x + (row0 + tok * rm.ss) * D + kk * 32 + g * 8);
         xb[tb][kk] = __builtin_bit_cast(bf16x8, r);
       }
     }
@@ -436,7 +454,7 @@ __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __rest
       e4m3_code_words<4 * DB>(y, s, c);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int64_t off = (bh * S + tok) * D + db * 16 + g * 4;
+        const int64_t off = (row0 + tok * rm.ss) * D + db * 16 + g * 4;
         *reinterpret_cast<uint32_t*>(codes + off) = c[db];
         if (dbg) {
           // y holds bf16 values: their top halves are the bf16 bits
@@ -464,11 +482,13 @@ inline unsigned grid_chunks(int64_t n, int64_t per_block, unsigned cap) {
 hipError_t launch_calibrate(const void* x, int x_dtype, const faq_shape& s, float* amax,
                             hipStream_t st) {
   const int64_t per_bh = s.S * s.D;
+  const RowMap rm = row_map(s);
+  const int dsh = s.D == 128 ? 7 : 6;
   dim3 grid(grid_chunks(per_bh, kThreads * 8 * 4, 65535), (unsigned)(s.B * s.H));
   if (x_dtype == FAQ_T_BF16)
-    k_calibrate<uint16_t><<<grid, kThreads, 0, st>>>((const uint16_t*)x, per_bh, (int)s.H, amax);
+    k_calibrate<uint16_t><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rm, dsh, per_bh, (int)s.H, amax);
   else
-    k_calibrate<float><<<grid, kThreads, 0, st>>>((const float*)x, per_bh, (int)s.H, amax);
+    k_calibrate<float><<<grid, kThreads, 0, st>>>((const float*)x, rm, dsh, per_bh, (int)s.H, amax);
   return hipGetLastError();
 }
 
@@ -482,11 +502,14 @@ template <bool FP8>
 static hipError_t head_q(const void* x, int x_dtype, const faq_shape& s, const float* scale,
                          uint8_t* codes, hipStream_t st) {
   const int64_t per_bh = s.S * s.D;
+  const RowMap rm = row_map(s);
+  const int dsh = s.D == 128 ? 7 : 6;
   dim3 grid(grid_chunks(per_bh, kThreads * 16 * 2, 65535), (unsigned)(s.B * s.H));
   if (x_dtype == FAQ_T_BF16)
-    k_quant_head<uint16_t, FP8><<<grid, kThreads, 0, st>>>((const uint16_t*)x, scale, per_bh, (int)s.H, codes);
+    k_quant_head<uint16_t, FP8><<<grid, kThreads, 0, st>>>((const uint16_t*)x, scale, rm, dsh, per_bh, (int)s.H,
+                                                           codes);
   else
-    k_quant_head<float, FP8><<<grid, kThreads, 0, st>>>((const float*)x, scale, per_bh, (int)s.H, codes);
+    k_quant_head<float, FP8><<<grid, kThreads, 0, st>>>((const float*)x, scale, rm, dsh, per_bh, (int)s.H, codes);
   return hipGetLastError();
 }
 
@@ -501,68 +524,66 @@ hipError_t launch_quant_fp8_head(const void* x, int x_dtype, const faq_shape& s,
 }
 
 template <int D, bool I8>
-static hipError_t token_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
+static hipError_t token_d(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
                           float* scales, hipStream_t st) {
   constexpr int RPB = kThreads / (D / 16);
+  const int64_t rows = s.B * s.H * s.S;
+  const RowMap rm = row_map(s);
   const unsigned grid = grid_chunks(rows, RPB * 2, 1u << 20);
   if (x_dtype == FAQ_T_BF16)
-    k_quant_token<uint16_t, D, I8><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, scales);
+    k_quant_token<uint16_t, D, I8><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, rm, (uint32_t)s.H,
+                                                              (uint32_t)s.S, codes, scales);
   else
-    k_quant_token<float, D, I8><<<grid, kThreads, 0, st>>>((const float*)x, rows, codes, scales);
+    k_quant_token<float, D, I8><<<grid, kThreads, 0, st>>>((const float*)x, rows, rm, (uint32_t)s.H,
+                                                           (uint32_t)s.S, codes, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_fp8_token(const void* x, int x_dtype, const faq_shape& s,
                                   uint8_t* codes, float* scales, hipStream_t st) {
-  const int64_t rows = s.B * s.H * s.S;
-  return s.D == 128 ? token_d<128, false>(x, x_dtype, rows, codes, scales, st)
-                    : token_d<64, false>(x, x_dtype, rows, codes, scales, st);
+  return s.D == 128 ? token_d<128, false>(x, x_dtype, s, codes, scales, st)
+                    : token_d<64, false>(x, x_dtype, s, codes, scales, st);
 }
 
 hipError_t launch_quant_int8_token(const void* x, int x_dtype, const faq_shape& s,
                                    int8_t* codes, float* scales, hipStream_t st) {
-  const int64_t rows = s.B * s.H * s.S;
   uint8_t* c = reinterpret_cast<uint8_t*>(codes);
-  return s.D == 128 ? token_d<128, true>(x, x_dtype, rows, c, scales, st)
-                    : token_d<64, true>(x, x_dtype, rows, c, scales, st);
+  return s.D == 128 ? token_d<128, true>(x, x_dtype, s, c, scales, st)
+                    : token_d<64, true>(x, x_dtype, s, c, scales, st);
 }
 
-template <int D>
-static hipError_t mxfp4_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
-                          uint8_t* e8m0, hipStream_t st) {
+template <int D, bool FP4>
+static hipError_t mx_d(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
+                       uint8_t* e8m0, hipStream_t st) {
   constexpr int RPB = kThreads / (D / 8);
+  const int64_t rows = s.B * s.H * s.S;
+  const RowMap rm = row_map(s);
+  const uint32_t H = (uint32_t)s.H, S = (uint32_t)s.S;
   const unsigned grid = grid_chunks(rows, RPB * 4, 1u << 20);
-  if (x_dtype == FAQ_T_BF16)
-    k_quant_mxfp4<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, e8m0);
-  else
-    k_quant_mxfp4<float, D><<<grid, kThreads, 0, st>>>((const float*)x, rows, codes, e8m0);
+  if (FP4) {
+    if (x_dtype == FAQ_T_BF16)
+      k_quant_mxfp4<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, rm, H, S, codes, e8m0);
+    else
+      k_quant_mxfp4<float, D><<<grid, kThreads, 0, st>>>((const float*)x, rows, rm, H, S, codes, e8m0);
+  } else {
+    if (x_dtype == FAQ_T_BF16)
+      k_quant_mxfp8<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, rm, H, S, codes, e8m0);
+    else
+      k_quant_mxfp8<float, D><<<grid, kThreads, 0, st>>>((const float*)x, rows, rm, H, S, codes, e8m0);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_mxfp4(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
                               uint8_t* e8m0, hipStream_t st) {
-  const int64_t rows = s.B * s.H * s.S;
-  return s.D == 128 ? mxfp4_d<128>(x, x_dtype, rows, codes, e8m0, st)
-                    : mxfp4_d<64>(x, x_dtype, rows, codes, e8m0, st);
-}
-
-template <int D>
-static hipError_t mxfp8_d(const void* x, int x_dtype, int64_t rows, uint8_t* codes,
-                          uint8_t* e8m0, hipStream_t st) {
-  constexpr int RPB = kThreads / (D / 8);
-  const unsigned grid = grid_chunks(rows, RPB * 4, 1u << 20);
-  if (x_dtype == FAQ_T_BF16)
-    k_quant_mxfp8<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, codes, e8m0);
-  else
-    k_quant_mxfp8<float, D><<<grid, kThreads, 0, st>>>((const float*)x, rows, codes, e8m0);
-  return hipGetLastError();
+  return s.D == 128 ? mx_d<128, true>(x, x_dtype, s, codes, e8m0, st)
+                    : mx_d<64, true>(x, x_dtype, s, codes, e8m0, st);
 }
 
 hipError_t launch_quant_mxfp8(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
                               uint8_t* e8m0, hipStream_t st) {
-  const int64_t rows = s.B * s.H * s.S;
-  return s.D == 128 ? mxfp8_d<128>(x, x_dtype, rows, codes, e8m0, st)
-                    : mxfp8_d<64>(x, x_dtype, rows, codes, e8m0, st);
+  return s.D == 128 ? mx_d<128, false>(x, x_dtype, s, codes, e8m0, st)
+                    : mx_d<64, false>(x, x_dtype, s, codes, e8m0, st);
 }
 
 template <int D, int BT>
@@ -570,7 +591,7 @@ static hipError_t fp8_block_d(const uint16_t* x, const faq_shape& s, uint8_t* co
                               float* scales, hipStream_t st) {
   const int nblk = (int)((s.S + BT - 1) / BT);
   dim3 grid((unsigned)nblk, (unsigned)(s.B * s.H));
-  k_quant_fp8_block<D, BT><<<grid, kThreads, 0, st>>>(x, s.S, nblk, codes, scales);
+  k_quant_fp8_block<D, BT><<<grid, kThreads, 0, st>>>(x, row_map(s), (int)s.H, s.S, nblk, codes, scales);
   return hipGetLastError();
 }
 
@@ -589,7 +610,8 @@ static hipError_t rot_block_d(const uint16_t* x, const uint16_t* rot, const faq_
   const int nblk = (int)((s.S + BT - 1) / BT);
   const int64_t nwork = (int64_t)nblk * s.B * s.H;
   const unsigned grid = (unsigned)(nwork < 2048 ? nwork : 2048);
-  k_rot_fp8_block<D, BT><<<grid, BT * 2, 0, st>>>(x, rot, s.S, nblk, nwork, codes, scales, dbg);
+  k_rot_fp8_block<D, BT><<<grid, BT * 2, 0, st>>>(x, rot, row_map(s), (int)s.H, s.S, nblk, nwork, codes, scales,
+                                                   dbg);
   return hipGetLastError();
 }
 

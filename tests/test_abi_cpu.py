@@ -107,6 +107,8 @@ def test_quantize_validation():
     assert _quantize(_cfg(_abi.FAQ_FP8_E4M3, _abi.FAQ_PER_TOKEN_BLOCK, 0), shp) == _abi.FAQ_ERR_INVALID_ARG
     assert _quantize(_cfg(_abi.FAQ_FP8_E4M3, _abi.FAQ_PER_TOKEN_BLOCK, 64), shp) == _abi.FAQ_ERR_UNSUPPORTED
     assert _quantize(tok, _abi.faq_shape(1, -2, 64, 128)) == _abi.FAQ_ERR_INVALID_ARG
+    assert _quantize(tok, _abi.faq_shape(1, 2, 64, 128, 2)) == _abi.FAQ_ERR_INVALID_ARG  # unknown layout
+    assert _quantize(tok, _abi.faq_shape(1 << 20, 1 << 10, 1 << 10, 128)) == _abi.FAQ_ERR_INVALID_ARG  # rows >= 2^31
     lib = _abi.lib()
     assert lib.fa_quant_calibrate(FAKE, 5, ctypes.byref(shp), FAKE, None) == _abi.FAQ_ERR_INVALID_ARG
     assert lib.fa_quant_calibrate(FAKE, 1, ctypes.byref(shp), None, None) == _abi.FAQ_ERR_INVALID_ARG
