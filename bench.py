@@ -87,26 +87,29 @@ def quantize_bytes(w):
     return tot
 
 
-def make_step(w, dev):
-    """Pre-allocates every output and returns (step_fn, attention_fn)."""
+def make_step(w, dev, layout="bnsd"):
+    """Pre-allocates every output and returns (step_fn, attention_fn).  With
+    layout "bsnd" the inputs, codes and output are BSND."""
     import torch
     import quantized_attention_fa_amd as faq
 
     modes = branch_modes(w)
     xs = [t.to(dev) for t in (w.q, w.k, w.v)]
+    if layout == "bsnd":
+        xs = [x.permute(0, 2, 1, 3).contiguous() for x in xs]
     rot = w.rot.to(dev) if w.rot is not None else None
     cfgs, statics, outs = [], [None] * 3, []
     for br in range(3):
         mode = modes[br]
         if mode == "float":
             cfgs.append(None)
-            outs.append(faq.float_branch(xs[br]))
+            outs.append(faq.float_branch(xs[br], layout=layout))
             continue
         if mode in STATIC:
             cfg = faq.QConfig(STATIC[mode], "per_head")
             amax = torch.zeros(w.shape[1], dtype=torch.float32, device=dev)
             for c in w.calib[br]:
-                faq.fa_quant_calibrate(c.to(dev), amax)
+                faq.fa_quant_calibrate(c.to(dev), amax)  # calibration data stays BNSD
             statics[br] = faq.fa_quant_scales_from_amax(amax, STATIC[mode])
         elif mode == "fp8_token":
             cfg = faq.QConfig("fp8_e4m3", "per_token")
@@ -118,18 +121,19 @@ def make_step(w, dev):
             cfg = faq.QConfig("fp8_e4m3", "per_token_block",
                               block_tokens=w.spec["q_block"] if br == 0 else w.spec["kv_block"])
         cfgs.append(cfg)
-        qt = faq.fa_quantize(xs[br], cfg, static_scale=statics[br], rot=rot if br < 2 else None)
+        qt = faq.fa_quantize(xs[br], cfg, static_scale=statics[br], rot=rot if br < 2 else None, layout=layout)
         if mode in STATIC:
             qt.scales = statics[br]  # per-head scales are used in place
         outs.append(qt)
     ws = torch.empty(max(faq.fa_quant_attention_workspace_bytes(*outs), 1), dtype=torch.uint8, device=dev)
-    out = torch.empty(w.shape, dtype=torch.bfloat16, device=dev)
+    B_, H_, S_, D_ = w.shape
+    out = torch.empty((B_, H_, S_, D_) if layout == "bnsd" else (B_, S_, H_, D_), dtype=torch.bfloat16, device=dev)
 
     def quantize():
         for br in range(3):
             if cfgs[br] is not None:
                 faq.fa_quantize(xs[br], cfgs[br], static_scale=statics[br], rot=rot if br < 2 else None,
-                                out=outs[br])
+                                out=outs[br], layout=layout)
 
     def attention():
         faq.fa_quant_attention(*outs, causal=w.spec["causal"], out=out, workspace=ws)
@@ -260,6 +264,8 @@ def main():
                     help="workload 1..10 (default 2, the metric's workload; 6-8 are the sibling FA modes, "
                          "9-10 per-branch configurations)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--layout", choices=("bnsd", "bsnd"), default="bnsd",
+                    help="memory layout of Q/K/V, their codes and the output")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -280,7 +286,7 @@ def main():
         return
     w = make_inputs(args.config)
     modes = branch_modes(w)
-    quantize, attention = make_step(w, dev)
+    quantize, attention = make_step(w, dev, args.layout)
     flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     for _ in range(args.warmup):
@@ -319,6 +325,7 @@ def main():
                  "Q/K " + MODE_TEXT.get(modes[0], "bf16 (not quantized)") + ", V " +
                  MODE_TEXT.get(modes[2], "bf16 (not quantized)"))
     B, H, S, D = w.shape
+    line_workload = w.spec["name"] + ("" if args.layout == "bnsd" else "_bsnd")
     line = {
         "metric": METRIC,
         "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
@@ -332,10 +339,11 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": w.spec["name"], "mode": mode_text, "B": B, "H": H, "S": S, "D": D,
+        "config": {"workload": line_workload, "mode": mode_text,
+                   "layout": args.layout.upper(), "B": B, "H": H, "S": S, "D": D,
                    "causal": w.spec["causal"], "input_dtype": w.spec["dtype"]},
         "roofline": {"bound": "mfma", "achieved": round(att_tops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(att_tops / peak, 4), "traffic": recorded_traffic(w.spec["name"]),
+                     "frac": round(att_tops / peak, 4), "traffic": recorded_traffic(line_workload),
                      "kernel": "fa_quant_attention: k_prep (V / K re-layout) + k_attn (fused attention)",
                      "attention_source": source_digest(),
                      "ops_per_launch": ops, "ms_per_launch": round(att_ms, 4)},
