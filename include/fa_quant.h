@@ -162,8 +162,9 @@ faq_status fa_quantize(const void* x, int32_t x_dtype, const faq_shape* shape,
                        faq_qtensor* out, void* debug_rotated, void* stream);
 
 /* Device workspace (bytes) fa_quant_attention needs for these operands
-   (V re-laid out tile by tile with its per-tile scale data); 0 on invalid
-   operands. */
+   (V re-laid out tile by tile with its per-tile scale data; with few
+   queries per head - decode - also the partial results of the key splits);
+   enough for causal and non-causal calls; 0 on invalid operands. */
 size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtensor* k,
                                           const faq_qtensor* v);
 
@@ -180,6 +181,10 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
                (bf16 = the float result rounded to nearest even).  q, k and
                v may have different layouts.
    workspace   device buffer of at least fa_quant_attention_workspace_bytes.
+   Short query sets (decode: a few queries per head against a long key
+   cache) split the keys across workgroups on 128-key tile boundaries and
+   merge the partial results; the probability rule below makes the split
+   exact up to fp32 rounding.
    Probabilities enter the PV product quantized per 128-key tile relative
    to the tile's own row maximum: int8 round(127 p w_j) or E4M3 of
    448 p w_j, with w_j the key's V scale over the tile's largest (1 when V

@@ -266,7 +266,8 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
                                           const faq_qtensor* v) {
   int qk, pv;
   if (attn_check(q, k, v, &qk, &pv, "fa_quant_attention_workspace_bytes") != FAQ_OK) return 0;
-  return attn_workspace_bytes(qk, pv, k->shape.B, k->shape.H, k->shape.S, k->shape.D);
+  // the non-causal size: it covers causal calls too (they never split keys)
+  return attn_workspace_bytes(qk, pv, k->shape.B, k->shape.H, q->shape.S, k->shape.S, k->shape.D, 0);
 }
 
 faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
@@ -286,7 +287,7 @@ faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const 
   if (!out || !q->codes || !k->codes || !v->codes) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL pointer");
   for (const faq_qtensor* t : {q, k, v})
     if (t->cfg.dtype != FAQ_FLOAT && !t->scales) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL scales");
-  const size_t need = attn_workspace_bytes(qk, pv, B, H, Skv, D);
+  const size_t need = attn_workspace_bytes(qk, pv, B, H, Sq, Skv, D, causal);
   if (workspace_bytes < need || !workspace) return fail(FAQ_ERR_WORKSPACE, fn, "workspace");
   AttnArgs a{};
   a.qk = qk;

@@ -166,10 +166,29 @@ struct Cfg {
 //         and FP8 with one V scale per tile)
 // ------------------------------------------------------------------------
 struct WsLayout {
-  size_t vt_off, kb_off, aux_off, sig_off, total;
+  size_t vt_off, kb_off, aux_off, sig_off, part_off, total;
 };
 
-inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Skv, int64_t D) {
+// Key splits: with few query tiles per head (decode: a handful of queries
+// against a long cache) the (b,h, query tile) grid cannot fill 256 CUs, so
+// the key tiles are split across workgroups, tps tiles each, for about
+// 2048 workgroups.  Causal attention (Sq == Skv) never splits.
+struct KvSplit {
+  int nsplit, tps;
+};
+
+inline KvSplit kv_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int causal) {
+  const int64_t nt = (Skv + BN - 1) / BN;
+  const int64_t base = B * H * ((Sq + BM - 1) / BM);
+  if (causal || base >= 1024 || nt < 4) return KvSplit{1, (int)nt};
+  int64_t want = (2048 + base - 1) / base;
+  if (want > nt / 2) want = nt / 2;
+  const int64_t tps = (nt + want - 1) / want;
+  return KvSplit{(int)((nt + tps - 1) / tps), (int)tps};
+}
+
+inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                          int causal) {
   const int64_t nt = (Skv + BN - 1) / BN;
   const size_t tiles = (size_t)(B * H * nt);
   const bool pi8 = pv == PV_I8H || pv == PV_I8T;
@@ -185,7 +204,9 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Skv, int
   l.kb_off = up(tiles * D * BN * (pi8 ? 1 : 2));
   l.aux_off = l.kb_off + up(qimg ? tiles * BN * D * 2 : 0);
   l.sig_off = l.aux_off + up(tiles * (xk + xv));
-  l.total = l.sig_off + up(sig ? tiles * 4 : 0);
+  l.part_off = l.sig_off + up(sig ? tiles * 4 : 0);
+  const KvSplit sp = kv_split(B, H, Sq, Skv, causal);
+  l.total = l.part_off + up(sp.nsplit > 1 ? (size_t)sp.nsplit * B * H * Sq * (D + 2) * 4 : 0);
   return l;
 }
 
@@ -386,7 +407,21 @@ struct KParams {
   float c_log2;  // sm_scale * log2(e)
   void* out;
   int out_bf16;
+  // split keys (non-causal): split c of a (b,h, query tile) runs tiles
+  // [c tps, (c + 1) tps) and leaves its unnormalized O, running reference M
+  // and sum L in part (nsplit > 1) for k_combine
+  int nsplit, tps;
+  float* part;
 };
+
+// Partial results of split c: O at part + ((c BH + bh) Sq + i) D, then
+// (M, L) pairs after all nsplit BH Sq rows of O.
+FAQ_DEV float* part_o(float* part, int c, int64_t BH, int64_t Sq, int64_t bh, int64_t i, int D) {
+  return part + (((int64_t)c * BH + bh) * Sq + i) * D;
+}
+FAQ_DEV float* part_ml(float* part, int nsplit, int c, int64_t BH, int64_t Sq, int64_t bh, int64_t i, int D) {
+  return part + (int64_t)nsplit * BH * Sq * D + (((int64_t)c * BH + bh) * Sq + i) * 2;
+}
 
 using gptr = const __attribute__((address_space(1))) void*;
 using lptr = __attribute__((address_space(3))) void*;
@@ -443,11 +478,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < NW);
 
-  // ---- work item: (b,h) and query tile
+  // ---- work item: (b,h), query tile and key split
   int64_t bh;
   int qt;
+  const int split = p.nsplit > 1 ? (int)(blockIdx.x % p.nsplit) : 0;
   {
-    const int L = blockIdx.x, nqt = p.nqt;
+    const int L = p.nsplit > 1 ? (int)(blockIdx.x / p.nsplit) : (int)blockIdx.x, nqt = p.nqt;
     const int BH = (int)p.BH;
     if ((BH & 7) == 0) {
       const int xcd = L & 7, jj = L >> 3, per = BH >> 3;
@@ -591,16 +627,17 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   for (int db = 0; db < DB; ++db) O[db] = f32x16{};
 
   const int qlast = min(Sq, (qt + 1) * BM) - 1;
-  const int t_end = CAUSAL ? min(nt, qlast / BN + 1) : nt;
+  const int t_beg = split * p.tps;
+  const int t_end = CAUSAL ? min(nt, qlast / BN + 1) : min(nt, t_beg + p.tps);
   const float vscale_i8 = (PV == PV_I8H) ? p.vs_head[hd] * (1.0f / 127.0f) : 1.0f;
   // valid keys of this lane's query: [0, lim)
   const int lim = CAUSAL ? min(Skv, qi + 1) : Skv;
 
-  issue_k(0);
+  issue_k(t_beg);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 #pragma clang loop unroll(disable)
-  for (int t = 0; t < t_end; ++t) {
+  for (int t = t_beg; t < t_end; ++t) {
     issue_v(t);
     const int k0 = t * BN;
     // the ragged last tile and the causal diagonal need a per-key validity
@@ -896,6 +933,24 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
     __syncthreads();
   }
 
+  // ---- a key split leaves its partial result: O times its reference
+  // factor (unnormalized, relative to the running reference M), M and L
+  if (p.nsplit > 1) {
+    if (qi < Sq) {
+      float* po = part_o(p.part, split, p.BH, p.Sq, bh, qi, D);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+          *reinterpret_cast<float4*>(po + 32 * db + 8 * a4 + 4 * h) =
+              make_float4(O[db][4 * a4] * fref, O[db][4 * a4 + 1] * fref, O[db][4 * a4 + 2] * fref,
+                          O[db][4 * a4 + 3] * fref);
+      if (h == 0)
+        *reinterpret_cast<float2*>(part_ml(p.part, p.nsplit, split, p.BH, p.Sq, bh, qi, D)) = make_float2(M, L);
+    }
+    return;
+  }
+
   // ---- normalize, store: register r of block db is channel
   // 32 db + 8 (r / 4) + 4 h + r % 4 of query qi
   if (qi < Sq) {
@@ -915,6 +970,43 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + off) = make_float4(o0, o1, o2, o3);
         }
       }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Merge of the key splits: one wave per (b,h, query), D / 64 channels per
+// lane.  M* = max_c M_c; O = sum_c 2^(M_c - M*) O_c / sum_c 2^(M_c - M*) L_c
+// (M is kept in log2 units).
+// ------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int nsplit, int64_t BH, int64_t H,
+                                                 int64_t Sq, RowMap omap, void* __restrict__ out, int out_bf16) {
+  constexpr int CPL = D / 64;  // channels per lane
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= BH * Sq) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = row / Sq, i = row % Sq;
+  float Ms = -INFINITY;
+  for (int c = 0; c < nsplit; ++c) Ms = fmaxf(Ms, part_ml(const_cast<float*>(part), nsplit, c, BH, Sq, bh, i, D)[0]);
+  float num[CPL] = {}, den = 0.0f;
+  for (int c = 0; c < nsplit; ++c) {
+    const float* ml = part_ml(const_cast<float*>(part), nsplit, c, BH, Sq, bh, i, D);
+    const float wgt = __builtin_amdgcn_exp2f(ml[0] - Ms);
+    den = __builtin_fmaf(wgt, ml[1], den);
+    const float* po = part_o(const_cast<float*>(part), c, BH, Sq, bh, i, D) + lane * CPL;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) num[k] = __builtin_fmaf(wgt, po[k], num[k]);
+  }
+  const float inv = 1.0f / den;
+  const int64_t off = omap.row(bh / H, bh % H, i) * D + lane * CPL;
+  if (out_bf16) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(out) + off;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) o[k] = (uint16_t)f32_to_bf16_bits(num[k] * inv);
+  } else {
+    float* o = reinterpret_cast<float*>(out) + off;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) o[k] = num[k] * inv;
   }
 }
 
@@ -949,9 +1041,16 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   p.q_sb = a.q_sb; p.q_sh = a.q_sh; p.q_block = a.q_block;
   p.c_log2 = a.sm_scale * kLog2e;
   p.out = a.out; p.out_bf16 = a.out_bf16;
-  dim3 grid((unsigned)(p.nqt * p.BH));
+  const KvSplit sp = kv_split(a.B, a.H, a.Sq, a.Skv, a.causal);
+  p.nsplit = sp.nsplit; p.tps = sp.tps;
+  p.part = reinterpret_cast<float*>(ws + l.part_off);
+  dim3 grid((unsigned)(p.nqt * p.BH * sp.nsplit));
   if (a.causal) k_attn<QK, PV, D, true><<<grid, NTHR, 0, st>>>(p);
   else k_attn<QK, PV, D, false><<<grid, NTHR, 0, st>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess || sp.nsplit == 1) return e;
+  k_combine<D><<<(unsigned)((p.BH * p.Sq + 3) / 4), 256, 0, st>>>(p.part, sp.nsplit, p.BH, a.H, a.Sq, a.qmap, a.out,
+                                                                 a.out_bf16);
   return hipGetLastError();
 }
 
@@ -982,12 +1081,12 @@ bool attn_pair_supported(int qk, int pv) {
   }
 }
 
-size_t attn_workspace_bytes(int qk, int pv, int64_t B, int64_t H, int64_t Skv, int64_t D) {
-  return ws_layout(qk, pv, B, H, Skv, D).total;
+size_t attn_workspace_bytes(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int causal) {
+  return ws_layout(qk, pv, B, H, Sq, Skv, D, causal).total;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
-  const WsLayout l = ws_layout(a.qk, a.pv, a.B, a.H, a.Skv, a.D);
+  const WsLayout l = ws_layout(a.qk, a.pv, a.B, a.H, a.Sq, a.Skv, a.D, a.causal);
   switch (a.qk) {
     case QK_I8H: return launch_qk<QK_I8H, PV_I8H>(a, l, st);
     case QK_I8T: return launch_qk<QK_I8T, PV_I8T>(a, l, st);

@@ -80,7 +80,9 @@ struct AttnArgs {
 // Pairs with kernels: Q, K and V of one configuration, or either side
 // unquantized.
 bool attn_pair_supported(int qk, int pv);
-size_t attn_workspace_bytes(int qk, int pv, int64_t B, int64_t H, int64_t Skv, int64_t D);
+// Workspace of one call; it depends on Sq and causal through the key
+// splits of short query sets (their partial results live there too).
+size_t attn_workspace_bytes(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int causal);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
 }  // namespace faq

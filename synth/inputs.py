@@ -32,6 +32,10 @@ Per-branch configurations (an unconfigured branch is not quantized):
   9  FP8 per-token Q and K, V unquantized (bf16): as 3.
   10 no branch quantized (bf16 attention): as 2, without outliers' effect on
      any scale (the tensors are the same recipe).
+Decode over a quantized KV cache (a few queries per head against a long
+cache; Q has q_len rows, K and V the shape's S):
+  11 INT8 per-head static: the recipe of 2, [4,32,16384,128] cache, 16
+     queries per head, not causal.
 """
 
 from dataclasses import dataclass, field
@@ -65,6 +69,9 @@ CONFIGS: Dict[int, dict] = {
     10: dict(name="bf16_attention_prefill", mode="float", dtype="bf16", dist="normal",
              shape=(2, 32, 4096, 128), causal=True, outlier_frac=0.005, outlier_gain=20.0,
              modes=("float", "float", "float")),
+    11: dict(name="int8_per_head_decode", mode="int8_head", dtype="bf16", dist="normal",
+             shape=(4, 32, 16384, 128), q_len=16, causal=False, calib="batch", calib_batch=4,
+             outlier_frac=0.005, outlier_gain=20.0),
 }
 
 TID_Q, TID_K, TID_V = 0, 1, 2
@@ -130,26 +137,31 @@ class Workload:
         return t.to(torch.float32).numpy()
 
 
-def make_inputs(cfg: int, shape=None, calib_batch=None) -> Workload:
-    """CPU tensors for workload `cfg` (1..10).  `shape` overrides the BNSD
+def make_inputs(cfg: int, shape=None, calib_batch=None, q_len=None) -> Workload:
+    """CPU tensors for workload `cfg` (1..11).  `shape` overrides the BNSD
     shape with the same recipe (smaller test cases); `calib_batch` overrides
-    the calibration batch size of workload 2."""
+    the calibration batch size of workloads with a calibration batch;
+    `q_len` gives Q its own sequence length (decode), else the workload's
+    q_len or the shape's S."""
     spec = dict(CONFIGS[cfg])
     shape = tuple(shape or spec["shape"])
+    q_len = q_len or spec.get("q_len")
+    if q_len:
+        spec["q_len"] = q_len
     bf16 = spec["dtype"] == "bf16"
 
     def mk(tid, shp, branch):
         x = _draw(cfg, tid, shp, spec, branch)
         return _to_bf16(x) if bf16 else torch.from_numpy(x)
 
-    q, k, v = (mk(t, shape, t) for t in (TID_Q, TID_K, TID_V))
+    qshape = (shape[0], shape[1], q_len, shape[3]) if q_len else shape
+    q, k, v = mk(TID_Q, qshape, 0), mk(TID_K, shape, 1), mk(TID_V, shape, 2)
     w = Workload(cfg=cfg, spec=spec, shape=shape, q=q, k=k, v=v)
     if spec.get("calib") == "self":
         w.calib = [[q], [k], [v]]
     elif spec.get("calib") == "batch":
         nb = calib_batch or spec["calib_batch"]
-        cshape = (nb,) + shape[1:]
-        w.calib = [[mk(TID_CALIB + br, cshape, br)] for br in range(3)]
+        w.calib = [[mk(TID_CALIB + br, (nb,) + (qshape if br == 0 else shape)[1:], br)] for br in range(3)]
     if spec["mode"] == "rot_fp8_block":
         w.rot = rotation(cfg, shape[3])
     return w

@@ -84,7 +84,7 @@ def dequant(run: GpuRun, br: int):
     """(values fp64 [B,H,S,D], per-key scale [B,H,S] or None) of branch br,
     decoded by the oracle from the GPU's codes and scales."""
     mode = run.modes[br]
-    B, H, S, D = run.w.shape
+    B, H, S, D = run.x[br].shape  # Q may have its own length (decode)
     if mode == "float":
         return run.x[br].to(torch.float64).cpu().numpy(), None
     c, s = run.codes_np(br), run.scales_np(br)
@@ -135,5 +135,5 @@ def bf16_of(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
 
 
-def small_workload(cfg, shape):
-    return make_inputs(cfg, shape=shape, calib_batch=2)
+def small_workload(cfg, shape, q_len=None):
+    return make_inputs(cfg, shape=shape, calib_batch=2, q_len=q_len)
