@@ -42,10 +42,37 @@ BF16_PEAK = 2500.0
 STATIC = {"int8_head": "int8", "fp8_head": "fp8_e4m3"}  # per-head static modes -> scale dtype
 
 
-def attention_ops(shape, causal):
-    B, H, S, D = shape
-    pairs = S * (S + 1) // 2 if causal else S * S
+def attention_ops(w):
+    """4 D operations per unmasked (query, key) pair."""
+    B, H, S, D = w.shape
+    Sq = int(w.q.shape[2])
+    pairs = S * (S + 1) // 2 if w.spec["causal"] else Sq * S
     return 4 * D * B * H * pairs
+
+
+def is_decode(w):
+    return "q_len" in w.spec
+
+
+def attention_bytes(w):
+    """Algorithmic HBM bytes of one decode attention call: the Q, K and V
+    codes and scales once, and the bf16 output."""
+    B, H, S, D = w.shape
+    Sq = int(w.q.shape[2])
+    tot = 0
+    for br, mode in enumerate(branch_modes(w)):
+        n = B * H * (Sq if br == 0 else S)
+        if mode == "float":
+            tot += 2 * n * D
+        elif mode == "mxfp4":
+            tot += n * D // 2 + n * D // 32
+        elif mode == "mxfp8":
+            tot += n * D + n * D // 32
+        elif mode in STATIC:
+            tot += n * D + H * 4
+        else:
+            tot += n * D + n * 4
+    return tot + 2 * B * H * Sq * D
 
 
 def branch_modes(w):
@@ -67,12 +94,12 @@ def quantize_bytes(w):
     """Algorithmic bytes of quantizing the configured branches: input read +
     codes + scales (an unquantized branch moves nothing)."""
     B, H, S, D = w.shape
-    n = B * H * S * D
     inb = 4 if w.spec["dtype"] == "f32" else 2
     tot = 0
     for br, mode in enumerate(branch_modes(w)):
-        if mode == "float":
-            continue
+        if mode == "float" or (br > 0 and is_decode(w)):
+            continue  # decode: the K/V cache is quantized once, outside the step
+        n = B * H * (int(w.q.shape[2]) if br == 0 else S) * D
         if mode in STATIC:
             tot += n * inb + n + H * 4
         elif mode in ("fp8_token", "int8_token"):
@@ -126,11 +153,11 @@ def make_step(w, dev, layout="bnsd"):
             qt.scales = statics[br]  # per-head scales are used in place
         outs.append(qt)
     ws = torch.empty(max(faq.fa_quant_attention_workspace_bytes(*outs), 1), dtype=torch.uint8, device=dev)
-    B_, H_, S_, D_ = w.shape
+    B_, H_, S_, D_ = outs[0].shape
     out = torch.empty((B_, H_, S_, D_) if layout == "bnsd" else (B_, S_, H_, D_), dtype=torch.bfloat16, device=dev)
 
     def quantize():
-        for br in range(3):
+        for br in range(1 if is_decode(w) else 3):
             if cfgs[br] is not None:
                 faq.fa_quantize(xs[br], cfgs[br], static_scale=statics[br], rot=rot if br < 2 else None,
                                 out=outs[br], layout=layout)
@@ -165,9 +192,10 @@ def cpu_baseline(w, budget_s=20.0):
     heads = 0
     rows = None
     # a single head can exceed the budget at long sequence lengths: sample rows
-    full_pairs = S * (S + 1) // 2 if causal else S * S
+    Sq = int(w.q.shape[2])
+    full_pairs = S * (S + 1) // 2 if causal else Sq * S
     if full_pairs > 4096 * 4096:
-        rows = np.arange(0, S, max(1, S // 1024))
+        rows = np.arange(0, Sq, max(1, Sq // 1024))
     blocks = (w.spec.get("q_block"), w.spec.get("kv_block"), w.spec.get("kv_block"))
     for h in range(H):
         if time.perf_counter() - t0 > budget_s:
@@ -209,11 +237,11 @@ def cpu_baseline(w, budget_s=20.0):
             scl.append(sv)
         vs = scl[2]
         OA.attention(*deq, rule, v_scale=vs, causal=causal, rows=rows)
-        r = np.arange(S) if rows is None else rows
+        r = np.arange(Sq) if rows is None else rows
         ops += 4 * D * int(np.sum(np.minimum(r + 1, S) if causal else np.full(r.size, S)))
         heads += 1
     dt = time.perf_counter() - t0
-    sample = f"{heads} of {B * H} (b,h) heads" + ("" if rows is None else f", {rows.size} of {S} query rows each")
+    sample = f"{heads} of {B * H} (b,h) heads" + ("" if rows is None else f", {rows.size} of {Sq} query rows each")
     sample += ", quantize + attention"
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": cores, "blas_threads": blas, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2)}
@@ -261,8 +289,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
-                    help="workload 1..10 (default 2, the metric's workload; 6-8 are the sibling FA modes, "
-                         "9-10 per-branch configurations)")
+                    help="workload 1..11 (default 2, the metric's workload; 6-8 are the sibling FA modes, "
+                         "9-10 per-branch configurations, 11 decode over a quantized cache)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--layout", choices=("bnsd", "bsnd"), default="bnsd",
                     help="memory layout of Q/K/V, their codes and the output")
@@ -313,7 +341,7 @@ def main():
     step_ms = [q + a for q, a in zip(q_ms, a_ms)]
     mean = lambda v: sum(v) / len(v)
     ms_step = mean(step_ms)
-    ops = attention_ops(w.shape, w.spec["causal"])
+    ops = attention_ops(w)
     qbytes = quantize_bytes(w)
     att_ms = mean(a_ms)
     att_tops = ops / (att_ms * 1e-3) / 1e12
@@ -326,6 +354,21 @@ def main():
                  MODE_TEXT.get(modes[2], "bf16 (not quantized)"))
     B, H, S, D = w.shape
     line_workload = w.spec["name"] + ("" if args.layout == "bnsd" else "_bsnd")
+    kernel = "fa_quant_attention: k_prep (V / K re-layout) + k_attn (fused attention)"
+    if is_decode(w):
+        # a few queries against a long cache: bound by reading the cache
+        abytes = attention_bytes(w)
+        a_gbs = abytes / (att_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(a_gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(line_workload),
+                    "kernel": kernel + " + k_combine (key-split merge)", "attention_source": source_digest(),
+                    "bytes_per_launch": abytes, "ops_per_launch": ops, "ms_per_launch": round(att_ms, 4),
+                    "tops": round(att_tops, 2)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(att_tops, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(att_tops / peak, 4), "traffic": recorded_traffic(line_workload),
+                    "kernel": kernel, "attention_source": source_digest(),
+                    "ops_per_launch": ops, "ms_per_launch": round(att_ms, 4)}
     line = {
         "metric": METRIC,
         "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
@@ -341,12 +384,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": line_workload, "mode": mode_text,
                    "layout": args.layout.upper(), "B": B, "H": H, "S": S, "D": D,
+                   **({"q_len": int(w.q.shape[2]), "cache": "quantized once, outside the step"}
+                      if is_decode(w) else {}),
                    "causal": w.spec["causal"], "input_dtype": w.spec["dtype"]},
-        "roofline": {"bound": "mfma", "achieved": round(att_tops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(att_tops / peak, 4), "traffic": recorded_traffic(line_workload),
-                     "kernel": "fa_quant_attention: k_prep (V / K re-layout) + k_attn (fused attention)",
-                     "attention_source": source_digest(),
-                     "ops_per_launch": ops, "ms_per_launch": round(att_ms, 4)},
+        "roofline": roofline,
         "quantize": ({"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(q_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": qbytes,
                       "ms_per_step": round(mean(q_ms), 4)} if qbytes else None),
