@@ -793,10 +793,11 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) O[db] *= rscale;
         }
-        // per-head: 127 p = 2^(s ce - (m ce - log2 127)); at the maximum
-        // this may differ from 127 by an ulp, which cannot move rne(127 p).
-        // per-token: p = 1 exactly at the maximum, times 127 w_j.
-        const float mc = PV == PV_I8H ? ms * ce - kLog2_127 : ms;
+        // per-head: 127 p = 2^((s - m) ce + log2 127), s - m exact (integer
+        // scores), so every p of the tile is relative to the tile maximum
+        // with no error growing with |m ce| (the unquantized p also feed
+        // the row sum L).  per-token: p = 1 exactly at the maximum, times
+        // 127 w_j.
         i32x4 P[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -809,8 +810,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
               const float x = S[kb][4 * w + b];
-              float pv = PV == PV_I8H ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, -mc))
-                                      : __builtin_amdgcn_exp2f((x - mc) * ce);
+              float pv = PV == PV_I8H ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_127))
+                                      : __builtin_amdgcn_exp2f((x - ms) * ce);
               if (b & 1) ls1 += pv; else ls0 += pv;
               if (PV == PV_I8T) pv *= vm[b];
               word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
@@ -842,7 +843,6 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
         // the bf16 P operand of its two k-steps, and their products
 #pragma unroll
         for (int db = 0; db < DB; ++db) O[db] *= rscale;
-        const float mce = ms * ce;
         float sc = 1.0f, isc = 1.0f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -862,13 +862,14 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 #pragma unroll
             for (int t8 = 0; t8 < 8; ++t8) {
               const float x = S[kb][8 * s2 + t8];
-              // one V scale per tile: 448 p comes out of the exponent (448 p
-              // at the maximum is within an ulp of 448, whose code both
-              // roundings give).  Otherwise p = 1 exactly at the tile
-              // maximum ((x - m) is 0): there 448 w_j can sit on an E4M3 tie
-              // (bf16-derived scale ratios do), and the MX group of the
-              // maximum has its amax at a power of two
-              pv[t8] = PV == PV_F8C ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, kLog2_448 - mce))
+              // one V scale per tile: 448 p = 2^((x - m) ce + log2 448), at
+              // the maximum within an ulp of 448, whose code both roundings
+              // give.  Otherwise p = 1 exactly at the tile maximum: there
+              // 448 w_j can sit on an E4M3 tie (bf16-derived scale ratios
+              // do), and the MX group of the maximum has its amax at a power
+              // of two.  Both are relative to the tile maximum with no error
+              // growing with |m ce| (the unquantized p also feed L).
+              pv[t8] = PV == PV_F8C ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_448))
                                     : __builtin_amdgcn_exp2f((x - ms) * ce);
               if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
             }

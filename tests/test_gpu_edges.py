@@ -1,0 +1,78 @@
+"""Degenerate and extreme cases on the GPU, every mode, against the oracle:
+all-zero tensors (scale 1, codes 0, uniform attention over zero values), a
+single key, a single query, a one-key ragged last tile, score ranges so wide
+that each row's softmax is one-hot, and calls with nothing to compute."""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_attention_fa_amd as faq
+from gpu_helpers import DEV, GpuRun, check_attention, oracle_attention, small_workload
+
+pytestmark = pytest.mark.gpu
+
+MODES = [(2, "int8_head"), (6, "fp8_head"), (3, "fp8_token"), (7, "int8_token"), (4, "mxfp4"), (8, "mxfp8"),
+         (5, "rot_fp8_block"), (3, "float")]
+
+
+def _run(cfg, mode, shape, q_len=None, scale_q=1.0, zero=False):
+    w = small_workload(cfg, shape, q_len=q_len)
+    if zero:
+        w.q.zero_(); w.k.zero_(); w.v.zero_()
+        for c in w.calib:
+            for t in c:
+                t.zero_()
+    if scale_q != 1.0:
+        w.q.mul_(scale_q)
+        for t in (w.calib[0] if w.calib else []):
+            t.mul_(scale_q)
+    return GpuRun(w, modes=None if mode != "float" else ("float",) * 3)
+
+
+@pytest.mark.parametrize("cfg,mode", MODES)
+def test_all_zero_tensors(cfg, mode):
+    run = _run(cfg, mode, (1, 2, 200, 128), zero=True)
+    for br in range(3):
+        if mode != "float":
+            assert int(run.qt[br].codes.abs().max() if run.qt[br].codes.dtype == torch.int8
+                       else (run.qt[br].codes & 0x7F).max()) == 0
+    o = run.attention(torch.float32, causal=False).cpu().numpy()
+    assert not np.isnan(o).any() and np.all(o == 0)
+    check_attention(o, oracle_attention(run, causal=False), f"zeros {mode}")
+
+
+@pytest.mark.parametrize("cfg,mode", MODES)
+@pytest.mark.parametrize("shape,q_len,causal", [((1, 2, 1, 128), None, False), ((1, 2, 1, 64), None, True),
+                                                ((2, 1, 129, 128), 3, False), ((1, 3, 1, 128), 1, False)])
+def test_tiny_and_ragged(cfg, mode, shape, q_len, causal):
+    run = _run(cfg, mode, shape, q_len=q_len)
+    o = run.attention(torch.float32, causal=causal).cpu().numpy()
+    check_attention(o, oracle_attention(run, causal=causal), f"{mode} {shape} q_len={q_len} causal={causal}")
+    if shape[2] == 1:  # one key: the output is that key's (dequantized) value
+        from gpu_helpers import dequant
+        v, _ = dequant(run, 2)
+        assert np.allclose(o, np.broadcast_to(v, o.shape), rtol=0, atol=2e-3 * max(1.0, np.abs(v).max()))
+
+
+@pytest.mark.parametrize("cfg,mode", MODES)
+def test_one_hot_softmax(cfg, mode):
+    """Q scaled by 200: score gaps of hundreds, every row's weights are one
+    key; no overflow, no NaN."""
+    run = _run(cfg, mode, (1, 2, 300, 128), scale_q=200.0)
+    o = run.attention(torch.float32, causal=False).cpu().numpy()
+    check_attention(o, oracle_attention(run, causal=False), f"one-hot {mode}")
+
+
+def test_nothing_to_compute():
+    w = small_workload(3, (1, 2, 256, 128))
+    run = GpuRun(w)
+    q0 = faq.QTensor(run.qt[0].cfg, (1, 2, 0, 128), run.qt[0].codes[:, :, :0], run.qt[0].scales)
+    out = faq.fa_quant_attention(q0, run.qt[1], run.qt[2], out_dtype=torch.float32)
+    assert out.numel() == 0
+    x = torch.empty((0, 2, 64, 128), dtype=torch.bfloat16, device=DEV)
+    qt = faq.fa_quantize(x, faq.QConfig("mxfp8", "per_block"))
+    assert qt.codes.numel() == 0
+    k0 = faq.QTensor(run.qt[1].cfg, (1, 2, 0, 128), run.qt[1].codes[:, :, :0], run.qt[1].scales)
+    with pytest.raises(faq.FaQuantError):
+        faq.fa_quant_attention(run.qt[0], k0, k0)
