@@ -183,6 +183,7 @@ inline KvSplit kv_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int causa
   if (causal || base >= 1024 || nt < 4) return KvSplit{1, (int)nt};
   int64_t want = (2048 + base - 1) / base;
   if (want > nt / 2) want = nt / 2;
+  if (want > 64) want = 64;  // the merge keeps one split per lane
   const int64_t tps = (nt + want - 1) / want;
   return KvSplit{(int)((nt + tps - 1) / tps), (int)tps};
 }
@@ -412,6 +413,10 @@ struct KParams {
   // and sum L in part (nsplit > 1) for k_combine
   int nsplit, tps;
   float* part;
+  // direct V (INT8 codes, decode): V rows read from the codes and transposed
+  // into the LDS V^T tile by the kernel itself, no re-layout pass
+  const uint8_t* vcodes;
+  RowMap vmap;
 };
 
 // Partial results of split c: O at part + ((c BH + bh) Sq + i) D, then
@@ -457,9 +462,10 @@ FAQ_DEV T lds_ld(const uint8_t* p) {
   return *reinterpret_cast<const T*>(p);
 }
 
-template <int QK, int PV, int D, bool CAUSAL>
+template <int QK, int PV, int D, bool CAUSAL, bool VDIR = false>
 __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   using G = Cfg<QK, PV, D>;
+  static_assert(!VDIR || (G::PI8 && D == 128), "direct V: int8 codes, D = 128");
   constexpr int KS = G::KS, DB = G::DB, NB = G::NB;
   // per-key K scales multiply the scores (per-token scopes, MXFP8 rows); a
   // K scale constant over the tile folds into the exponent factor
@@ -608,6 +614,37 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       stage<G::XKBYTES / 16>(kbuf + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
                              [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
   };
+  // direct V: thread (cc, g) = (tid / 32, tid % 32) moves the 16 keys of
+  // V^T column cc (keys 64 (cc & 1) + 16 (cc >> 1) + r) times channels
+  // 4 g .. 4 g + 3: 16 four-byte row loads, four 4x4 byte transposes, and
+  // four 16-byte chunks of V^T rows 4 g .. 4 g + 3
+  uint32_t vreg[VDIR ? 16 : 1];
+  const int vcc = tid >> 5, vg = tid & 31;
+  const int vkey0 = 64 * (vcc & 1) + 16 * (vcc >> 1);
+  const uint8_t* vrow = VDIR ? p.vcodes + p.vmap.row(bb, hd, 0) * D + 4 * vg : nullptr;
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = t * BN + vkey0 + r;
+      vreg[r] = key < Skv ? *reinterpret_cast<const uint32_t*>(vrow + (int64_t)key * p.vmap.ss * D) : 0u;
+    }
+  };
+  auto store_vt = [&]() {
+    uint32_t o[4][4];  // [channel j][4-key group]
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const uint32_t w0 = vreg[4 * kg], w1 = vreg[4 * kg + 1], w2 = vreg[4 * kg + 2], w3 = vreg[4 * kg + 3];
+      const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u), t1 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+      const uint32_t t2 = __builtin_amdgcn_perm(w3, w2, 0x05010400u), t3 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+      o[0][kg] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+      o[1][kg] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+      o[2][kg] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+      o[3][kg] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      *reinterpret_cast<uint4*>(vbuf + (vcc * D + 4 * vg + jj) * 16) = make_uint4(o[jj][0], o[jj][1], o[jj][2], o[jj][3]);
+  };
   auto issue_v = [&](int t) {
     stage<G::VBYTES / 16>(vbuf, vtbase + (int64_t)t * G::VBYTES, wave, lane,
                           [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
@@ -638,7 +675,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   __syncthreads();
 #pragma clang loop unroll(disable)
   for (int t = t_beg; t < t_end; ++t) {
-    issue_v(t);
+    if (VDIR) load_v(t);
+    else issue_v(t);
     const int k0 = t * BN;
     // the ragged last tile and the causal diagonal need a per-key validity
     // test; the other tiles skip it (uniform branch)
@@ -776,8 +814,11 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
       ms = (m == -INFINITY) ? 0.0f : (live ? m : INFINITY);
     }
 
-    // V(t) has landed everywhere and every wave is done with K(t)
+    // V(t) has landed everywhere and every wave is done with K(t) (direct V:
+    // every wave finished P V of tile t - 1 at the last barrier, so V^T(t)
+    // goes into the LDS tile now)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (VDIR) store_vt();
     __syncthreads();
     if (t + 1 < t_end) issue_k(t + 1);
 
@@ -987,16 +1028,21 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   if (row >= BH * Sq) return;
   const int lane = threadIdx.x & 63;
   const int64_t bh = row / Sq, i = row % Sq;
-  float Ms = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) Ms = fmaxf(Ms, part_ml(const_cast<float*>(part), nsplit, c, BH, Sq, bh, i, D)[0]);
-  float num[CPL] = {}, den = 0.0f;
-  for (int c = 0; c < nsplit; ++c) {
-    const float* ml = part_ml(const_cast<float*>(part), nsplit, c, BH, Sq, bh, i, D);
-    const float wgt = __builtin_amdgcn_exp2f(ml[0] - Ms);
-    den = __builtin_fmaf(wgt, ml[1], den);
-    const float* po = part_o(const_cast<float*>(part), c, BH, Sq, bh, i, D) + lane * CPL;
+  float* pp = const_cast<float*>(part);
+  // lane c < nsplit holds split c's (M, L); its weight 2^(M_c - M*)
+  float2 ml = make_float2(-INFINITY, 0.0f);
+  if (lane < nsplit) ml = *reinterpret_cast<const float2*>(part_ml(pp, nsplit, lane, BH, Sq, bh, i, D));
+  const float Ms = wave_max(ml.x);
+  const float wgt = lane < nsplit ? __builtin_amdgcn_exp2f(ml.x - Ms) : 0.0f;
+  float den = wgt * ml.y;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) num[k] = __builtin_fmaf(wgt, po[k], num[k]);
+  for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m, 64);
+  float num[CPL] = {};
+  for (int c = 0; c < nsplit; ++c) {
+    const float wc = __shfl(wgt, c, 64);
+    const float* po = part_o(pp, c, BH, Sq, bh, i, D) + lane * CPL;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) num[k] = __builtin_fmaf(wc, po[k], num[k]);
   }
   const float inv = 1.0f / den;
   const int64_t off = omap.row(bh / H, bh % H, i) * D + lane * CPL;
@@ -1025,9 +1071,16 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   pa.vsb = a.v_sb; pa.vsh = a.v_sh; pa.vblk = a.v_block;
   pa.vt = ws + l.vt_off; pa.kb = ws + l.kb_off; pa.aux = ws + l.aux_off;
   pa.sig = reinterpret_cast<float*>(ws + l.sig_off);
-  k_prep<QK, PV, D><<<dim3((unsigned)nt, (unsigned)(a.B * a.H)), 256, 0, st>>>(pa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const KvSplit sp = kv_split(a.B, a.H, a.Sq, a.Skv, a.causal);
+  // decode with INT8 per-head V: the kernel transposes V itself
+  constexpr bool VDIR_OK = QK == QK_I8H && PV == PV_I8H && D == 128;
+  const bool vdir = VDIR_OK && sp.nsplit > 1;
+  hipError_t e = hipSuccess;
+  if (!vdir) {
+    k_prep<QK, PV, D><<<dim3((unsigned)nt, (unsigned)(a.B * a.H)), 256, 0, st>>>(pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   KParams p{};
   p.H = a.H; p.BH = a.B * a.H; p.Sq = a.Sq; p.Skv = a.Skv; p.nt = nt;
   p.nqt = (int)((a.Sq + BM - 1) / BM);
@@ -1042,10 +1095,20 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   p.q_sb = a.q_sb; p.q_sh = a.q_sh; p.q_block = a.q_block;
   p.c_log2 = a.sm_scale * kLog2e;
   p.out = a.out; p.out_bf16 = a.out_bf16;
-  const KvSplit sp = kv_split(a.B, a.H, a.Sq, a.Skv, a.causal);
   p.nsplit = sp.nsplit; p.tps = sp.tps;
   p.part = reinterpret_cast<float*>(ws + l.part_off);
+  p.vcodes = (const uint8_t*)a.v_codes; p.vmap = a.vmap;
   dim3 grid((unsigned)(p.nqt * p.BH * sp.nsplit));
+  if constexpr (VDIR_OK) {
+    if (vdir) {
+      k_attn<QK, PV, D, false, true><<<grid, NTHR, 0, st>>>(p);  // splits are never causal
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      k_combine<D><<<(unsigned)((p.BH * p.Sq + 3) / 4), 256, 0, st>>>(p.part, sp.nsplit, p.BH, a.H, a.Sq, a.qmap,
+                                                                     a.out, a.out_bf16);
+      return hipGetLastError();
+    }
+  }
   if (a.causal) k_attn<QK, PV, D, true><<<grid, NTHR, 0, st>>>(p);
   else k_attn<QK, PV, D, false><<<grid, NTHR, 0, st>>>(p);
   e = hipGetLastError();

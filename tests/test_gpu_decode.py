@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 
 DECODE = [
     (2, (1, 2, 1000, 128), 1, None),
+    (2, (2, 3, 777, 128), 16, None),
     (2, (2, 3, 777, 64), 16, None),
     (3, (1, 2, 1000, 128), 5, None),
     (4, (1, 2, 1000, 128), 16, None),
@@ -42,8 +43,9 @@ def test_decode_against_oracle(cfg, shape, q_len, modes):
     assert np.array_equal(o16.view(torch.int16).cpu().numpy(), bf16_of(o32))
 
 
-def test_decode_bsnd_equals_bnsd():
-    w = small_workload(7, (2, 3, 1000, 128), q_len=9)
+@pytest.mark.parametrize("cfg", [7, 2])
+def test_decode_bsnd_equals_bnsd(cfg):
+    w = small_workload(cfg, (2, 3, 1000, 128), q_len=9)
     run = GpuRun(w)
     ref = run.attention(torch.float32, causal=False)
     bs = lambda qt: faq.QTensor(qt.cfg, qt.shape, qt.codes.permute(0, 2, 1, 3).contiguous(), qt.scales, "bsnd")
