@@ -162,7 +162,8 @@ faq_status fa_quantize(const void* x, int32_t x_dtype, const faq_shape* shape,
                        faq_qtensor* out, void* debug_rotated, void* stream);
 
 /* Device workspace (bytes) fa_quant_attention needs for these operands
-   (V re-laid out tile by tile with its per-tile scale data; with few
+   (V re-laid out tile by tile with its per-tile scale data, K widened to
+   bf16 where its format has no MFMA path of its own; with few
    queries per head - decode - also the partial results of the key splits);
    enough for causal and non-causal calls; 0 on invalid operands. */
 size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtensor* k,
@@ -171,10 +172,16 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
 /* Attention on quantized operands: both Q K^T and P V run on low-bit MFMA
    operands ("FA 量化" page, 概述), output dequantized to the original
    precision ("量化" page, FA量化 / FP8 Attention).
-   q, k, v     quantized with one common (dtype, scope) - INT8 or FP8
-               PER_HEAD / PER_TOKEN, MXFP4 or MXFP8 PER_BLOCK, or
-               FP8/PER_TOKEN_BLOCK (Q block 128, K/V block 256).  B, H, D
-               equal; k and v share S.
+   q, k, v     each quantized in its own configuration ("fa3_quant 配置说明"
+               §2.3) - INT8 or FP8 PER_HEAD / PER_TOKEN, MXFP4 or MXFP8
+               PER_BLOCK, FP8/PER_TOKEN_BLOCK (128 or 256 tokens) - or
+               FLOAT (bf16, not quantized).  Every combination runs: Q and
+               K of one (dtype, scope) with V of theirs or FLOAT take
+               kernels specialised to that pair (INT8 scores on INT8 MFMA,
+               MXFP4 on the scaled f8f6f4 MFMA); any other mix widens Q and
+               K exactly to bf16 (MX rows relative to their largest block
+               exponent) and scores on bf16 MFMA.  B, H, D equal; k and v
+               share S.
    sm_scale    softmax scale; 0 means 1/sqrt(D).
    causal      1: key j is masked for query i when j > i (needs Sq == Skv).
    out         device [B,H,Sq,D] in q's layout, out_dtype F32 or BF16

@@ -223,6 +223,16 @@ static int qk_mode(const faq_qconfig& c) {
   }
 }
 
+static int branch_fmt(const faq_qconfig& c) {
+  switch (c.dtype) {
+    case FAQ_FLOAT: return FMT_BF16;
+    case FAQ_INT8: return FMT_INT8;
+    case FAQ_MXFP4: return FMT_MX4;
+    case FAQ_MXFP8: return FMT_MX8;
+    default: return FMT_FP8;
+  }
+}
+
 static int pv_mode(const faq_qconfig& c) {
   switch (c.dtype) {
     case FAQ_FLOAT: return PV_BF;
@@ -235,11 +245,13 @@ static int pv_mode(const faq_qconfig& c) {
 
 // Branch configurations for attention ("fa3_quant 配置说明" §2.3: each of
 // fa_q / fa_k / fa_v configured on its own, an unconfigured branch not
-// quantized - FAQ_FLOAT, bf16 values in `codes`).  Q and K share one
-// configuration (token blocks may differ in size) or are both unquantized;
-// V is either of their configuration or unquantized.
+// quantized - FAQ_FLOAT, bf16 values in `codes`).  Every combination runs:
+// Q and K of one (dtype, scope) (token blocks may differ in size) with V of
+// that configuration or unquantized take the specialised score kernels; any
+// other combination takes the general score mode, which widens Q and K of
+// any format exactly to bf16.
 static faq_status attn_check(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
-                             int* qk, int* pv, const char* fn) {
+                             int* qk, int* pv, int* qfmt, int* kfmt, const char* fn) {
   if (!q || !k || !v) return fail(FAQ_ERR_INVALID_ARG, fn, "NULL tensor");
   for (const faq_qtensor* t : {q, k, v}) {
     if (t->cfg.dtype != FAQ_FLOAT) {
@@ -249,12 +261,12 @@ static faq_status attn_check(const faq_qtensor* q, const faq_qtensor* k, const f
     if (!shape_ok(&t->shape)) return fail(FAQ_ERR_INVALID_ARG, fn, "shape");
     if (!d_supported(t->shape.D)) return fail(FAQ_ERR_UNSUPPORTED, fn, "head_dim must be 64 or 128");
   }
-  if (q->cfg.dtype != k->cfg.dtype || (q->cfg.dtype != FAQ_FLOAT && q->cfg.scope != k->cfg.scope))
-    return fail(FAQ_ERR_UNSUPPORTED, fn, "q and k must share one (dtype, scope)");
-  *qk = qk_mode(k->cfg);
+  const bool same = q->cfg.dtype == k->cfg.dtype && (q->cfg.dtype == FAQ_FLOAT || q->cfg.scope == k->cfg.scope);
+  *qk = same ? qk_mode(k->cfg) : QK_GEN;
   *pv = pv_mode(v->cfg);
-  if (!attn_pair_supported(*qk, *pv))
-    return fail(FAQ_ERR_UNSUPPORTED, fn, "v must share the (dtype, scope) of q and k, or be unquantized");
+  if (!attn_pair_supported(*qk, *pv)) *qk = QK_GEN;
+  *qfmt = branch_fmt(q->cfg);
+  *kfmt = branch_fmt(k->cfg);
   if (q->shape.B != k->shape.B || q->shape.B != v->shape.B || q->shape.H != k->shape.H ||
       q->shape.H != v->shape.H || q->shape.D != k->shape.D || q->shape.D != v->shape.D ||
       k->shape.S != v->shape.S)
@@ -264,8 +276,8 @@ static faq_status attn_check(const faq_qtensor* q, const faq_qtensor* k, const f
 
 size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtensor* k,
                                           const faq_qtensor* v) {
-  int qk, pv;
-  if (attn_check(q, k, v, &qk, &pv, "fa_quant_attention_workspace_bytes") != FAQ_OK) return 0;
+  int qk, pv, qf, kf;
+  if (attn_check(q, k, v, &qk, &pv, &qf, &kf, "fa_quant_attention_workspace_bytes") != FAQ_OK) return 0;
   // the non-causal size: it covers causal calls too (they never split keys)
   return attn_workspace_bytes(qk, pv, k->shape.B, k->shape.H, q->shape.S, k->shape.S, k->shape.D, 0);
 }
@@ -274,8 +286,8 @@ faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const 
                               float sm_scale, int32_t causal, void* out, int32_t out_dtype,
                               void* workspace, size_t workspace_bytes, void* stream) {
   static const char* fn = "fa_quant_attention";
-  int qk, pv;
-  const faq_status cs = attn_check(q, k, v, &qk, &pv, fn);
+  int qk, pv, qf, kf;
+  const faq_status cs = attn_check(q, k, v, &qk, &pv, &qf, &kf, fn);
   if (cs != FAQ_OK) return cs;
   if (out_dtype != FAQ_T_F32 && out_dtype != FAQ_T_BF16) return fail(FAQ_ERR_INVALID_ARG, fn, "out_dtype");
   if (causal != 0 && causal != 1) return fail(FAQ_ERR_INVALID_ARG, fn, "causal must be 0 or 1");
@@ -292,6 +304,7 @@ faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const 
   AttnArgs a{};
   a.qk = qk;
   a.pv = pv;
+  a.qfmt = qf; a.kfmt = kf;
   a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv; a.D = D;
   a.qmap = row_map(q->shape); a.kmap = row_map(k->shape); a.vmap = row_map(v->shape);
   a.q_codes = q->codes; a.q_scales = q->scales;

@@ -112,6 +112,51 @@ FAQ_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w, float sc = 1.0f) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, sc, HI));
 }
 
+// Eight E2M1 codes (the four bytes of `w`, element 2i in the low nibble of
+// byte i) -> eight bf16, times the power of two `sc`.
+FAQ_DEV uint4 e2m1x8_to_bf16x8(uint32_t w, float sc) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3)));
+}
+
+// Two INT8 codes (bytes B and B + 1 of `w`) -> two bf16, exactly.
+template <int B>
+FAQ_DEV uint32_t i8x2_to_bf16x2(uint32_t w) {
+  const float a = (float)(int8_t)(w >> (8 * B)), b = (float)(int8_t)(w >> (8 * B + 8));
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+// Eight elements of a row, from `row` (bytes) at element e0 (a multiple of
+// 8), widened exactly to bf16 relative to 2^-E_rel for the MX formats: the
+// general score mode's operand.  ex: the row's E8M0 bytes (MX only).
+FAQ_DEV uint4 widen8(int fmt, const uint8_t* row, int e0, const uint8_t* ex, int erow) {
+  switch (fmt) {
+    case FMT_BF16: return *reinterpret_cast<const uint4*>(row + 2 * e0);
+    case FMT_INT8: {
+      const uint2 a = *reinterpret_cast<const uint2*>(row + e0);
+      return make_uint4(i8x2_to_bf16x2<0>(a.x), i8x2_to_bf16x2<2>(a.x), i8x2_to_bf16x2<0>(a.y),
+                        i8x2_to_bf16x2<2>(a.y));
+    }
+    case FMT_MX4: {
+      const float sc = __builtin_amdgcn_ldexpf(1.0f, (int)ex[e0 >> 5] - erow);
+      return e2m1x8_to_bf16x8(*reinterpret_cast<const uint32_t*>(row + e0 / 2), sc);
+    }
+    default: {  // FP8, MX8 (E4M3 codes)
+      const float sc = fmt == FMT_MX8 ? __builtin_amdgcn_ldexpf(1.0f, (int)ex[e0 >> 5] - erow) : 1.0f;
+      const uint2 a = *reinterpret_cast<const uint2*>(row + e0);
+      return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)a.x, sc, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)a.x, sc, true)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)a.y, sc, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)a.y, sc, true)));
+    }
+  }
+}
+
+// Bytes of a row of D elements in a branch format.
+FAQ_DEV int fmt_row_bytes(int fmt, int D) { return fmt == FMT_BF16 ? 2 * D : (fmt == FMT_MX4 ? D / 2 : D); }
+
 // 2^e as a float for e in [-126, 127] (a normal number, built from its bits).
 FAQ_DEV float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
@@ -129,9 +174,11 @@ FAQ_DEV float halves_sum(float x) {
 template <int QK, int PV, int D>
 struct Cfg {
   static constexpr bool QI8 = QK == QK_I8H || QK == QK_I8T;                                 // int8 score MFMA
-  static constexpr bool QBF = QK == QK_F8T || QK == QK_F8C || QK == QK_MX8 || QK == QK_BF;  // bf16 score MFMA
-  static constexpr bool QIMG = QK == QK_F8T || QK == QK_F8C || QK == QK_MX8;  // K widened in the workspace
-  static constexpr bool KSC = QK == QK_I8T || QK == QK_F8T || QK == QK_F8C || QK == QK_MX8;  // per-key K floats
+  static constexpr bool QBF =
+      QK == QK_F8T || QK == QK_F8C || QK == QK_MX8 || QK == QK_BF || QK == QK_GEN;  // bf16 score MFMA
+  static constexpr bool QIMG = QK == QK_F8T || QK == QK_F8C || QK == QK_MX8 || QK == QK_GEN;  // K widened
+  static constexpr bool KSC =
+      QK == QK_I8T || QK == QK_F8T || QK == QK_F8C || QK == QK_MX8 || QK == QK_GEN;  // per-key K floats
   static constexpr bool PI8 = PV == PV_I8H || PV == PV_I8T;  // int8 value MFMA
   static constexpr bool PMX = PV == PV_MX4 || PV == PV_MX8;  // MX probability groups
   static constexpr bool PVW = PV == PV_I8T || PV == PV_F8W;  // per-key V scale folded into P
@@ -193,7 +240,7 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int6
   const int64_t nt = (Skv + BN - 1) / BN;
   const size_t tiles = (size_t)(B * H * nt);
   const bool pi8 = pv == PV_I8H || pv == PV_I8T;
-  const bool qimg = qk == QK_F8T || qk == QK_F8C || qk == QK_MX8;
+  const bool qimg = qk == QK_F8T || qk == QK_F8C || qk == QK_MX8 || qk == QK_GEN;
   const bool ksc = qk == QK_I8T || qimg;
   const bool pvw = pv == PV_I8T || pv == PV_F8W;
   const bool sig = pvw || pv == PV_F8C;
@@ -232,6 +279,7 @@ struct PrepArgs {
   RowMap kmap, vmap;  // rows of K and V codes (BNSD or BSND)
   int64_t H, Skv, nt, ksb, ksh, vsb, vsh;
   int kblk, vblk;
+  int kfmt;  // general score mode: K's BranchFmt
   uint8_t* vt;
   uint8_t* kb;
   uint8_t* aux;
@@ -270,7 +318,25 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
     }
   }
   // K image, 16 codes (two 16-byte image columns) per item
-  if (C::QIMG) {
+  if (QK == QK_GEN) {
+    const int rb = fmt_row_bytes(a.kfmt, D);
+    for (int c = threadIdx.x; c < BN * (D / 16); c += 256) {
+      const int kl = c / (D / 16), cc = c % (D / 16);
+      uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+      if (k0 + kl < a.Skv) {
+        const uint8_t* row = a.k + a.kmap.row(b_, h_, k0 + kl) * rb;
+        const uint8_t* ke = reinterpret_cast<const uint8_t*>(a.ks) + (bh * a.Skv + k0 + kl) * NB;
+        int emax = 0;
+        if (a.kfmt == FMT_MX4 || a.kfmt == FMT_MX8)
+          for (int b = 0; b < NB; ++b) emax = max(emax, (int)ke[b]);
+        lo = widen8(a.kfmt, row, 16 * cc, ke, emax);
+        hi = widen8(a.kfmt, row, 16 * cc + 8, ke, emax);
+      }
+      uint8_t* img = a.kb + tile_id * C::KBYTES + kslot(kl) * 16;
+      *reinterpret_cast<uint4*>(img + (2 * cc) * BN * 16) = lo;
+      *reinterpret_cast<uint4*>(img + (2 * cc + 1) * BN * 16) = hi;
+    }
+  } else if (C::QIMG) {
     for (int c = threadIdx.x; c < BN * (D / 16); c += 256) {
       const int kl = c / (D / 16), cc = c % (D / 16);
       uint4 kv = make_uint4(0, 0, 0, 0);
@@ -305,8 +371,11 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
   const int kl = threadIdx.x;
   if (C::KSC && kl < BN) {
     float sk = 0.0f;
+    const bool kmx = QK == QK_MX8 || (QK == QK_GEN && (a.kfmt == FMT_MX4 || a.kfmt == FMT_MX8));
     if (k0 + kl < a.Skv) {
-      if (QK == QK_MX8) {
+      if (QK == QK_GEN && a.kfmt == FMT_BF16) {
+        sk = 1.0f;
+      } else if (kmx) {
         const uint8_t* ke = reinterpret_cast<const uint8_t*>(a.ks) + (bh * a.Skv + k0 + kl) * NB;
         int emax = 0;
 #pragma unroll
@@ -405,6 +474,7 @@ struct KParams {
   const float* vs_head;  // INT8 per-head V: V scale
   int64_t q_sb, q_sh;    // float Q scale index b * q_sb + h * q_sh + i / q_block
   int q_block;
+  int qfmt;              // general score mode: Q's BranchFmt
   float c_log2;  // sm_scale * log2(e)
   void* out;
   int out_bf16;
@@ -469,7 +539,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   constexpr int KS = G::KS, DB = G::DB, NB = G::NB;
   // per-key K scales multiply the scores (per-token scopes, MXFP8 rows); a
   // K scale constant over the tile folds into the exponent factor
-  constexpr bool PERKEY = QK == QK_I8T || QK == QK_F8T || QK == QK_MX8;
+  constexpr bool PERKEY = QK == QK_I8T || QK == QK_F8T || QK == QK_MX8 || QK == QK_GEN;
   constexpr bool KCONST = QK == QK_F8C;
   static_assert(!(G::PMX && QK == QK_I8H), "MX probabilities need the float score path");
   // K (+ its per-key extras) and V^T tiles in separate LDS objects: V(t)
@@ -525,7 +595,27 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
     const int64_t qmem = p.qmap.row(bb, hd, ok ? qi : 0);  // memory row (codes)
     // per-token / token-block / per-head float Q scale of this query
     const int64_t qsi = (bh / p.H) * p.q_sb + hd * p.q_sh + (ok ? qi : 0) / p.q_block;
-    if (QK == QK_BF) {
+    if (QK == QK_GEN) {
+      // any format, widened exactly (MX relative to the row's largest block
+      // exponent, which scales the scores); once per workgroup, so the
+      // format is a runtime switch
+      const int fmt = p.qfmt;
+      const uint8_t* qrow = p.q + qmem * fmt_row_bytes(fmt, D);
+      const bool mx = fmt == FMT_MX4 || fmt == FMT_MX8;
+      const uint8_t* qe = reinterpret_cast<const uint8_t*>(p.qs) + qrow_i * NB;
+      int emax = 0;
+      if (mx && ok)
+        for (int b = 0; b < NB; ++b) emax = max(emax, (int)qe[b]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 a = make_uint4(0, 0, 0, 0);
+        if (ok) a = widen8(fmt, qrow, 16 * ks + 8 * h, qe, emax);
+        qbf[ks] = __builtin_bit_cast(bf16x8, a);
+      }
+      if (fmt == FMT_BF16) cq = p.c_log2;
+      else if (mx) cq = __builtin_amdgcn_ldexpf(1.0f, (ok ? emax : 127) - 127) * p.c_log2;
+      else cq = (ok ? reinterpret_cast<const float*>(p.qs)[qsi] : 1.0f) * p.c_log2;
+    } else if (QK == QK_BF) {
       const uint8_t* qrow = p.q + qmem * (2 * D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -1069,6 +1159,7 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   pa.H = a.H; pa.Skv = a.Skv; pa.nt = nt;
   pa.ksb = a.k_sb; pa.ksh = a.k_sh; pa.kblk = a.k_block;
   pa.vsb = a.v_sb; pa.vsh = a.v_sh; pa.vblk = a.v_block;
+  pa.kfmt = a.kfmt;
   pa.vt = ws + l.vt_off; pa.kb = ws + l.kb_off; pa.aux = ws + l.aux_off;
   pa.sig = reinterpret_cast<float*>(ws + l.sig_off);
   const KvSplit sp = kv_split(a.B, a.H, a.Sq, a.Skv, a.causal);
@@ -1093,6 +1184,7 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   p.sig = reinterpret_cast<const float*>(ws + l.sig_off);
   p.vs_head = (const float*)a.v_scales;
   p.q_sb = a.q_sb; p.q_sh = a.q_sh; p.q_block = a.q_block;
+  p.qfmt = a.qfmt;
   p.c_log2 = a.sm_scale * kLog2e;
   p.out = a.out; p.out_bf16 = a.out_bf16;
   p.nsplit = sp.nsplit; p.tps = sp.tps;
@@ -1133,7 +1225,7 @@ hipError_t launch_qk(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
 }  // namespace
 
 bool attn_pair_supported(int qk, int pv) {
-  if (pv == PV_BF || qk == QK_BF) return true;
+  if (pv == PV_BF || qk == QK_BF || qk == QK_GEN) return true;
   switch (qk) {
     case QK_I8H: return pv == PV_I8H;
     case QK_I8T: return pv == PV_I8T;
@@ -1158,6 +1250,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     case QK_F8C: return launch_qk<QK_F8C, PV_F8C>(a, l, st);
     case QK_MX4: return launch_qk<QK_MX4, PV_MX4>(a, l, st);
     case QK_MX8: return launch_qk<QK_MX8, PV_MX8>(a, l, st);
+    case QK_GEN:
+      // any Q/K formats with any value mode
+      switch (a.pv) {
+        case PV_I8H: return launch_pair<QK_GEN, PV_I8H>(a, l, st);
+        case PV_I8T: return launch_pair<QK_GEN, PV_I8T>(a, l, st);
+        case PV_F8W: return launch_pair<QK_GEN, PV_F8W>(a, l, st);
+        case PV_F8C: return launch_pair<QK_GEN, PV_F8C>(a, l, st);
+        case PV_MX4: return launch_pair<QK_GEN, PV_MX4>(a, l, st);
+        case PV_MX8: return launch_pair<QK_GEN, PV_MX8>(a, l, st);
+        default: return launch_pair<QK_GEN, PV_BF>(a, l, st);
+      }
     default:
       // unquantized Q and K with any value mode
       switch (a.pv) {

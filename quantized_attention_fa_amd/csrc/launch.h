@@ -49,8 +49,12 @@ hipError_t launch_rot_fp8_block(const uint16_t* x, const uint16_t* rot, const fa
 // ---- attention (attention.hip)
 // Score modes, from the configuration Q and K share: INT8 per-head, INT8
 // per-token, FP8 with per-token K scales, FP8 with one K scale per 128-key
-// tile (per-head, token blocks), MXFP4, MXFP8, unquantized bf16.
-enum QkMode { QK_I8H = 0, QK_I8T, QK_F8T, QK_F8C, QK_MX4, QK_MX8, QK_BF };
+// tile (per-head, token blocks), MXFP4, MXFP8, unquantized bf16; and the
+// general mode for any other Q/K/V combination (Q and K of any formats
+// widened exactly to bf16, per-query and per-key scale factors).
+enum QkMode { QK_I8H = 0, QK_I8T, QK_F8T, QK_F8C, QK_MX4, QK_MX8, QK_BF, QK_GEN };
+// Element formats of one branch for the general score mode.
+enum BranchFmt { FMT_BF16 = 0, FMT_INT8, FMT_FP8, FMT_MX4, FMT_MX8 };
 // Value modes, from V's configuration: INT8 per-head, INT8 per-token, FP8
 // with per-token V scales (folded into P), FP8 with one V scale per tile,
 // MXFP4, MXFP8, unquantized bf16.
@@ -58,6 +62,7 @@ enum PvMode { PV_I8H = 0, PV_I8T, PV_F8W, PV_F8C, PV_MX4, PV_MX8, PV_BF };
 
 struct AttnArgs {
   int qk, pv;
+  int qfmt, kfmt;  // BranchFmt of Q and K (general score mode)
   int64_t B, H, Sq, Skv, D;
   const void* q_codes;
   const void* q_scales;

@@ -22,9 +22,11 @@ MODE_CFG = {
     "fp8_head": lambda spec, br: faq.QConfig("fp8_e4m3", "per_head"),
     "int8_token": lambda spec, br: faq.QConfig("int8", "per_token"),
     "mxfp8": lambda spec, br: faq.QConfig("mxfp8", "per_block"),
+    "fp8_block128": lambda spec, br: faq.QConfig("fp8_e4m3", "per_token_block", block_tokens=128),
+    "fp8_block256": lambda spec, br: faq.QConfig("fp8_e4m3", "per_token_block", block_tokens=256),
 }
 P_RULE = {"int8_head": "int8", "fp8_token": "fp8", "mxfp4": "mxfp4", "rot_fp8_block": "fp8",
-          "fp8_head": "fp8", "int8_token": "int8", "mxfp8": "mxfp8"}
+          "fp8_head": "fp8", "int8_token": "int8", "mxfp8": "mxfp8", "fp8_block128": "fp8", "fp8_block256": "fp8"}
 STATIC_DTYPE = {"int8_head": "int8", "fp8_head": "fp8_e4m3"}
 
 
@@ -44,7 +46,8 @@ class GpuRun:
         for br in range(3):
             if self.modes[br] in STATIC_DTYPE:
                 amax = torch.zeros(w.shape[1], dtype=torch.float32, device=DEV)
-                for c in w.calib[br]:
+                # the workload's calibration batch, else the tensor itself
+                for c in (w.calib[br] if w.calib else [self.x[br]]):
                     faq.fa_quant_calibrate(c.to(DEV), amax)
                 self.amax[br] = amax
                 self.static[br] = faq.fa_quant_scales_from_amax(amax, STATIC_DTYPE[self.modes[br]])

@@ -138,25 +138,28 @@ def test_attention_validation():
     qs = _qt(tok, _abi.faq_shape(1, 2, 100, 128))
     assert _attn(qs, k, v, causal=1) == _abi.FAQ_ERR_SHAPE
     mx = _cfg(_abi.FAQ_MXFP4, _abi.FAQ_PER_BLOCK)
-    assert _attn(q, _qt(mx, s), v) == _abi.FAQ_ERR_UNSUPPORTED
     assert _attn(q, k, v, out_dtype=9) == _abi.FAQ_ERR_INVALID_ARG
     assert _attn(q, k, v, causal=2) == _abi.FAQ_ERR_INVALID_ARG
     assert _attn(q, k, v, sm=-1.0) == _abi.FAQ_ERR_INVALID_ARG
     assert _attn(q, k, v, sm=float("nan")) == _abi.FAQ_ERR_INVALID_ARG
-    # per-branch configurations: Q and K share one configuration (token
-    # blocks may differ in size) or are both unquantized; V has theirs or is
-    # unquantized
+    # per-branch configurations: every combination of the three branches
+    # runs (fa3_quant 配置说明 §2.3); pairs without a specialised score
+    # kernel widen Q and K to bf16, and K's bf16 image (2 bytes per element)
+    # is part of their workspace
     ws = lambda a, b, c: lib.fa_quant_attention_workspace_bytes(ctypes.byref(_qt(a, s)), ctypes.byref(_qt(b, s)),
                                                                 ctypes.byref(_qt(c, s)))
     b1 = _cfg(_abi.FAQ_FP8_E4M3, _abi.FAQ_PER_TOKEN_BLOCK, 128)
     b2 = _cfg(_abi.FAQ_FP8_E4M3, _abi.FAQ_PER_TOKEN_BLOCK, 256)
     fl = _cfg(_abi.FAQ_FLOAT, _abi.FAQ_PER_HEAD)
     i8t = _cfg(_abi.FAQ_INT8, _abi.FAQ_PER_TOKEN)
+    i8h = _cfg(_abi.FAQ_INT8, _abi.FAQ_PER_HEAD)
+    m8 = _cfg(_abi.FAQ_MXFP8, _abi.FAQ_PER_BLOCK)
     for ok in [(b1, b2, b2), (b1, b2, fl), (fl, fl, tok), (fl, fl, mx), (fl, fl, fl), (tok, tok, fl), (i8t, i8t, i8t)]:
         assert ws(*ok) > 0, ok
-    for bad in [(tok, tok, i8t), (fl, tok, tok), (tok, fl, fl), (i8t, tok, tok), (mx, mx, tok)]:
-        assert ws(*bad) == 0, bad
-        assert _attn(_qt(bad[0], s), _qt(bad[1], s), _qt(bad[2], s)) == _abi.FAQ_ERR_UNSUPPORTED
+    for mixed in [(tok, tok, i8t), (fl, tok, tok), (tok, fl, fl), (i8t, tok, tok), (mx, mx, tok), (mx, m8, i8h),
+                  (i8h, i8t, mx), (tok, b1, fl)]:
+        assert ws(*mixed) >= 2 * 2 * 256 * 128, mixed
+    assert _attn(_qt(mx, s), _qt(i8h, s), _qt(tok, s), ws_bytes=ws(mx, i8h, tok) - 1) == _abi.FAQ_ERR_WORKSPACE
     # unquantized branches need no scales; quantized ones do
     nos = _abi.faq_qtensor(tok, s, 0x2000, None)
     assert _attn(nos, k, v) == _abi.FAQ_ERR_INVALID_ARG

@@ -120,11 +120,42 @@ def test_full_size_per_branch_configs(cfg, modes, rows_per_bh):
     check_attention(got, oracle_attention(run, rows=rows), f"cfg{cfg} {modes} full size")
 
 
-def test_mixed_q_k_configurations_are_rejected():
-    w = small_workload(3, (1, 2, 128, 128))
-    run = GpuRun(w, modes=("fp8_token", "float", "float"))
-    with pytest.raises(faq.FaQuantError):
-        run.attention(torch.float32)
-    run = GpuRun(w, modes=("fp8_token", "fp8_token", "int8_token"))
-    with pytest.raises(faq.FaQuantError):
-        run.attention(torch.float32)
+# Q, K and V of different formats: the pairs without a specialised score
+# kernel (Q and K of different (dtype, scope), or V of a third configuration)
+# take the general score mode; ragged lengths, both head sizes, causal and not.
+GENERAL = [
+    (3, (1, 2, 300, 128), False, ("fp8_token", "float", "float")),
+    (3, (1, 2, 300, 64), True, ("float", "fp8_token", "fp8_token")),
+    (2, (1, 2, 300, 128), True, ("int8_head", "fp8_token", "mxfp4")),
+    (4, (1, 2, 300, 64), False, ("mxfp4", "mxfp8", "int8_token")),
+    (8, (1, 2, 257, 128), False, ("mxfp8", "mxfp4", "fp8_head")),
+    (7, (1, 2, 300, 128), True, ("int8_token", "int8_head", "fp8_block128")),
+    (6, (1, 2, 300, 64), False, ("fp8_block128", "fp8_token", "int8_head")),
+    (3, (1, 2, 300, 128), False, ("fp8_token", "fp8_token", "int8_token")),
+    (2, (1, 2, 300, 128), True, ("int8_head", "int8_head", "fp8_token")),
+    (4, (1, 2, 300, 128), False, ("mxfp4", "mxfp4", "mxfp8")),
+    (6, (1, 2, 384, 128), True, ("fp8_head", "fp8_block256", "float")),
+    (7, (1, 2, 257, 64), False, ("float", "int8_token", "mxfp8")),
+    (8, (2, 2, 300, 128), False, ("fp8_block256", "mxfp8", "mxfp4")),
+]
+
+
+@pytest.mark.parametrize("cfg,shape,causal,modes", GENERAL)
+def test_attention_general_score_mode(cfg, shape, causal, modes):
+    w = small_workload(cfg, shape)
+    run = GpuRun(w, modes=modes)
+    o32 = run.attention(torch.float32, causal=causal).cpu().numpy()
+    ref = oracle_attention(run, causal=causal)
+    check_attention(o32, ref, f"cfg{cfg} {shape} causal={causal} {modes}")
+    o16 = run.attention(torch.bfloat16, causal=causal)
+    assert np.array_equal(o16.view(torch.int16).cpu().numpy(), bf16_of(o32))
+
+
+def test_full_size_general_score_mode():
+    # the FP8-Q / bf16-V video workload with K per-token INT8 instead
+    w = make_inputs(9)
+    run = GpuRun(w, modes=("fp8_token", "int8_token", "float"))
+    o = run.attention(torch.float32)
+    rows = sample_rows(9, w.shape[2], 6, edge=4)
+    got = o[:, :, torch.from_numpy(rows).to(o.device)].cpu().numpy()
+    check_attention(got, oracle_attention(run, rows=rows), "cfg9 fp8/int8/float full size")

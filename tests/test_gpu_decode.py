@@ -27,6 +27,8 @@ DECODE = [
     (8, (1, 2, 1000, 128), 1, None),
     (3, (1, 2, 1000, 128), 16, ("fp8_token", "fp8_token", "float")),
     (2, (1, 2, 1000, 128), 7, ("float", "float", "float")),
+    (2, (2, 2, 1000, 128), 16, ("fp8_token", "int8_head", "int8_head")),
+    (4, (1, 2, 1000, 64), 4, ("float", "mxfp4", "fp8_token")),
     # a long sequence over few heads splits keys too (Sq = Skv, not causal)
     (3, (1, 2, 1024, 64), None, None),
 ]
