@@ -315,7 +315,13 @@ def main():
     w = make_inputs(args.config)
     modes = branch_modes(w)
     quantize, attention = make_step(w, dev, args.layout)
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = None
+    if not args.no_flush:
+        # read (not write) 512 MB between steps: evicts the inputs from L2
+        # and the Infinity Cache and leaves only clean lines, so no
+        # write-back of the flush's own data lands inside the timed step
+        flush = torch.zeros(64 << 20, dtype=torch.int64, device=dev)
+        flush_out = torch.empty((), dtype=torch.int64, device=dev)
 
     for _ in range(args.warmup):
         quantize()
@@ -328,7 +334,7 @@ def main():
     t_wall = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
-            flush.fill_(i & 0xff)  # evict the inputs from the caches (outside the step's events)
+            torch.sum(flush, dim=0, out=flush_out)  # evict the inputs from the caches (outside the step's events)
         ev[i][0].record(st)
         quantize()
         ev[i][1].record(st)
