@@ -67,6 +67,7 @@
 // tiles first.
 
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -188,10 +189,11 @@ struct Cfg {
   static constexpr int NB = D / 32;  // MX blocks per row
   // per-key extras: after the K tile the K scales (floats; MXFP8: 2^ of
   // the row exponent) or the MXFP4 K block exponents; after the V^T tile
-  // the multipliers qmax w_j (floats), which the probabilities read after
-  // the K buffer is refilled
+  // the multipliers qmax w_j (floats), then sigma_t (one float, padded to
+  // 16 bytes), which the value phase reads after the K buffer is refilled
   static constexpr int XKBYTES = QK == QK_MX4 ? BN * NB : (KSC ? BN * 4 : 0);
-  static constexpr int XVBYTES = PVW ? BN * 4 : 0;
+  static constexpr int XVW = PVW ? BN * 4 : 0;  // offset of sigma_t in the V extras
+  static constexpr int XVBYTES = XVW + (SIG ? 16 : 0);
   static constexpr int XBYTES = XKBYTES + XVBYTES;  // per tile in the workspace
   static constexpr int VROW = PI8 ? BN : 2 * BN;    // bytes of a V^T row
   static constexpr int VBYTES = D * VROW;
@@ -208,12 +210,12 @@ struct Cfg {
 //         the end are 0; MXFP8 relative to the row's largest block exponent)
 //   aux : K extras (K scales; MXFP8 row scales 2^(E_row); MXFP4 K block
 //         exponents, 128 rows x D/32 bytes, 127 past the end), then V
-//         extras (the multipliers qmax w_j)
-//   sig : sigma_t = max over the tile's keys of s_v,j (FP8 / INT8 per-token
-//         and FP8 with one V scale per tile)
+//         extras (the multipliers qmax w_j; sigma_t = max over the tile's
+//         keys of s_v,j for FP8 / INT8 per-token and FP8 with one V scale
+//         per tile)
 // ------------------------------------------------------------------------
 struct WsLayout {
-  size_t vt_off, kb_off, aux_off, sig_off, part_off, total;
+  size_t vt_off, kb_off, aux_off, part_off, total;
 };
 
 // Key splits: with few query tiles per head (decode: a handful of queries
@@ -245,14 +247,13 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int6
   const bool pvw = pv == PV_I8T || pv == PV_F8W;
   const bool sig = pvw || pv == PV_F8C;
   const size_t xk = qk == QK_MX4 ? BN * (D / 32) : (ksc ? BN * 4 : 0);
-  const size_t xv = pvw ? BN * 4 : 0;
+  const size_t xv = (pvw ? BN * 4 : 0) + (sig ? 16 : 0);
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WsLayout l{};
   l.vt_off = 0;
   l.kb_off = up(tiles * D * BN * (pi8 ? 1 : 2));
   l.aux_off = l.kb_off + up(qimg ? tiles * BN * D * 2 : 0);
-  l.sig_off = l.aux_off + up(tiles * (xk + xv));
-  l.part_off = l.sig_off + up(sig ? tiles * 4 : 0);
+  l.part_off = l.aux_off + up(tiles * (xk + xv));
   const KvSplit sp = kv_split(B, H, Sq, Skv, causal);
   l.total = l.part_off + up(sp.nsplit > 1 ? (size_t)sp.nsplit * B * H * Sq * (D + 2) * 4 : 0);
   return l;
@@ -283,7 +284,6 @@ struct PrepArgs {
   uint8_t* vt;
   uint8_t* kb;
   uint8_t* aux;
-  float* sig;
 };
 
 template <int QK, int PV, int D>
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
       constexpr float qmax = PV == PV_F8W ? 448.0f : 127.0f;
       reinterpret_cast<float*>(auxt + C::XKBYTES)[kl] = (sv > 0.0f) ? qmax * (sv / m) : 0.0f;
     }
-    if (threadIdx.x == 0) a.sig[tile_id] = m;
+    if (threadIdx.x == 0) reinterpret_cast<float*>(auxt + C::XKBYTES + C::XVW)[0] = m;
   }
 }
 
@@ -470,7 +470,6 @@ struct KParams {
   const void* ks;        // INT8 per-head: K scale
   const uint8_t* vt;     // V^T images in the workspace
   const uint8_t* aux;    // per-tile K extras, then V extras (see Cfg)
-  const float* sig;      // sigma_t per tile
   const float* vs_head;  // INT8 per-head V: V scale
   int64_t q_sb, q_sh;    // float Q scale index b * q_sb + h * q_sh + i / q_block
   int q_block;
@@ -501,30 +500,85 @@ FAQ_DEV float* part_ml(float* part, int nsplit, int c, int64_t BH, int64_t Sq, i
 using gptr = const __attribute__((address_space(1))) void*;
 using lptr = __attribute__((address_space(3))) void*;
 
-// Copy NCH 16-byte chunks global -> LDS.  The workgroup moves one round of
-// NTHR chunks per step (one global_load_lds_dwordx4 per wave, 1 KiB);
-// chunk p = NTHR i + 64 wave + lane lands at lds + 16 p and comes from
-// base + off(i), off being the lane's 32-bit byte offset in round i.
-template <int NCH, class Off>
+// One 16-byte global -> LDS copy per lane (lane i of the wave to
+// lds + 16 i).  ASM: the same instruction written out, so that the
+// compiler does not track the copy: its completion is then waited for only
+// where the kernel says so (vmcnt), never before reads of other LDS
+// buffers.  The instruction has no result registers; M0 holds the wave's
+// LDS base.
+template <bool ASM>
+FAQ_DEV void copy16(const uint8_t* g, uint8_t* lds) {
+  if (ASM) {
+    const uint32_t m = (uint32_t)(uintptr_t)(lptr)lds;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory", "m0");
+  } else {
+    __builtin_amdgcn_global_load_lds((gptr)g, (lptr)lds, 16, 0, 0);
+  }
+}
+
+// Copy NCH 16-byte chunks global -> LDS with NT threads.  The workgroup
+// moves one round of NT chunks per step (one global_load_lds_dwordx4 per
+// wave, 1 KiB); chunk p = NT i + 64 wave + lane lands at lds + 16 p and
+// comes from base + off(i), off being the lane's 32-bit byte offset in
+// round i.
+template <int NCH, int NT, bool ASM = false, class Off>
 FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, Off off) {
   // the tile base is a wave-uniform value held in SGPRs; hiding it from the
   // optimizer keeps it from turning every copy into a 64-bit per-lane
   // pointer carried across loop iterations
   asm volatile("" : "+s"(base));
-  constexpr int ROUNDS = NCH / NTHR;
+  constexpr int ROUNDS = NCH / NT;
 #pragma unroll
   for (int i = 0; i < ROUNDS; ++i) {
-    const int grp = i * NTHR + wave * 64;
-    __builtin_amdgcn_global_load_lds((gptr)(base + (uint32_t)off(i)), (lptr)(lds + grp * 16), 16, 0, 0);
+    const int grp = i * NT + wave * 64;
+    copy16<ASM>(base + (uint32_t)off(i), lds + grp * 16);
   }
-  constexpr int REM = NCH - ROUNDS * NTHR;  // < one round: the first waves take it
+  constexpr int REM = NCH - ROUNDS * NT;  // < one round: the first waves take it
   if (REM > 0) {
-    const int grp = ROUNDS * NTHR + wave * 64;
+    const int grp = ROUNDS * NT + wave * 64;
     if (grp < NCH) {
-      if (REM % 64 == 0 || grp + lane < NCH)
-        __builtin_amdgcn_global_load_lds((gptr)(base + (uint32_t)off(ROUNDS)), (lptr)(lds + grp * 16), 16, 0, 0);
+      if (REM % 64 == 0 || grp + lane < NCH) copy16<ASM>(base + (uint32_t)off(ROUNDS), lds + grp * 16);
     }
   }
+}
+
+// Copies (global_load_lds instructions) wave `wave` of NT threads issues
+// for NCH chunks: the full rounds, plus one if it takes part in the rest.
+template <int NCH, int NT>
+FAQ_DEV int stage_loads(int wave) {
+  return NCH / NT + ((NCH / NT) * NT + wave * 64 < NCH ? 1 : 0);
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n (the count must be an immediate)
+FAQ_DEV void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // (never above 12 here)
+  }
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// copy in flight): this wave's LDS reads and writes complete first
+// (lgkmcnt(0)); copies into LDS may stay in flight, their completion being
+// waited for with vmcnt before the barrier that publishes them.  The signal
+// fences keep the compiler from moving memory accesses across it.
+FAQ_DEV void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <class T>
@@ -532,9 +586,18 @@ FAQ_DEV T lds_ld(const uint8_t* p) {
   return *reinterpret_cast<const T*>(p);
 }
 
-template <int QK, int PV, int D, bool CAUSAL, bool VDIR = false>
-__global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
+// PP (ping-pong): eight waves in two groups of four, each group a 128-query
+// tile; the second group runs one phase behind the first, so each SIMD
+// holds one wave computing scores (MFMA) while the other computes
+// probabilities and their products (vector work), and the two overlap.  K
+// and V^T tiles are double-buffered.
+template <int QK, int PV, int D, bool CAUSAL, bool VDIR = false, bool PP = false>
+__global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const KParams p) {
   using G = Cfg<QK, PV, D>;
+  constexpr int NWK = PP ? 2 * NW : NW;  // waves per workgroup
+  constexpr int NTK = NWK * 64;          // threads per workgroup
+  constexpr int BMK = NWK * 32;          // queries per workgroup
+  static_assert(!(PP && VDIR), "ping-pong tiles come from the workspace");
   static_assert(!VDIR || (G::PI8 && D == 128), "direct V: int8 codes, D = 128");
   constexpr int KS = G::KS, DB = G::DB, NB = G::NB;
   // per-key K scales multiply the scores (per-token scopes, MXFP8 rows); a
@@ -547,12 +610,17 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   // from K(t), and K(t+1) while the products with V(t) run.  As distinct
   // objects the compiler knows an LDS read of one does not alias a copy in
   // flight into the other, so it never waits for the copy.
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[G::KBYTES + G::XKBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[G::VBYTES + G::XVBYTES];
+  constexpr int KSZ = G::KBYTES + G::XKBYTES, VSZ = G::VBYTES + G::XVBYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[KSZ];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[VSZ];
+  // ping-pong: the second K and V^T buffers (odd tiles of the work item)
+  __shared__ __attribute__((aligned(PP ? 1024 : 16))) uint8_t kbuf1[PP ? KSZ : 16];
+  __shared__ __attribute__((aligned(PP ? 1024 : 16))) uint8_t vbuf1[PP ? VSZ : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __builtin_assume(wave >= 0 && wave < NW);
+  __builtin_assume(wave >= 0 && wave < NWK);
+  const int grp = PP ? wave >> 2 : 0;  // ping-pong group
 
   // ---- work item: (b,h), query tile and key split
   int64_t bh;
@@ -572,7 +640,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
   }
   const int64_t hd = bh % p.H;
   const int Sq = (int)p.Sq, Skv = (int)p.Skv, nt = (int)p.nt;
-  const int q0 = qt * BM + wave * 32;  // this wave's first query
+  const int q0 = qt * BMK + wave * 32;  // this wave's first query
   const int qi = q0 + j;               // this lane's query
   const bool act = q0 < Sq;            // uniform per wave: any query to compute
   const int64_t bb = bh / p.H;
@@ -678,31 +746,34 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
     }
   }
 
-  // ---- operand addresses: per-lane bases, constant offsets per step
-  const uint8_t* kop_base = kbuf + h * (BN * 16) + kslot(qk_row(j)) * 16;  // + ks 2 BN 16 + kb 256
-  const uint8_t* vop_base = vbuf + h * (D * 16) + j * 16;                   // + kstep 2 D 16 + db 512
-  const float* xk = reinterpret_cast<const float*>(kbuf + G::KBYTES) + 64 * h;  // the lane's keys' K scales
-  const float* xv = reinterpret_cast<const float*>(vbuf + G::VBYTES) + 64 * h;  // their qmax w_j
-  const uint8_t* xmx = kbuf + G::KBYTES + qk_row(j) * NB + h;               // MXFP4: + 16 kb NB + 2 ks
+  // ---- operand addresses in a K / V^T buffer: per-lane offsets, constant
+  // offsets per step
+  const int kop_off = h * (BN * 16) + kslot(qk_row(j)) * 16;  // + ks 2 BN 16 + kb 256
+  const int vop_off = h * (D * 16) + j * 16;                  // + kstep 2 D 16 + db 512
+  const int xk_off = G::KBYTES + 256 * h;                     // the lane's keys' K scales (floats)
+  const int xv_off = G::VBYTES + 256 * h;                     // their qmax w_j (floats)
+  const int xmx_off = G::KBYTES + qk_row(j) * NB + h;         // MXFP4: + 16 kb NB + 2 ks
 
   // ---- tile copies.  K: FP8 / MXFP8 copy the bf16 image from the
   // workspace; the other modes gather K rows into the chunk-major layout
-  // (round i of a lane moves column 2 i + pw / 128 of slot pw % 128, i.e.
+  // (round i of a lane moves column (NTK / 128) i + pw / 128 of slot
+  // pw % 128, i.e.
   // of K row kslot(pw % 128); rows past the end re-read the last row,
   // masked).
   const int pw = wave * 64 + lane;
   const int krow = kslot(pw & (BN - 1));
-  auto issue_k = [&](int t) {
+  auto issue_k = [&](int t, uint8_t* kb) {
     if (G::QIMG) {
-      stage<G::KBYTES / 16>(kbuf, kbase + (int64_t)t * G::KBYTES, wave, lane,
-                            [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
+      stage<G::KBYTES / 16, NTK, PP>(kb, kbase + (int64_t)t * G::KBYTES, wave, lane,
+                                 [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
     } else {
       const uint32_t roff = (uint32_t)min(t * BN + krow, Skv - 1) * kstride + (uint32_t)((pw >> 7) * 16);
-      stage<G::KBYTES / 16>(kbuf, kbase, wave, lane, [&](int i) { return roff + (uint32_t)(2 * i * 16); });
+      stage<G::KBYTES / 16, NTK, PP>(kb, kbase, wave, lane,
+                                 [&](int i) { return roff + (uint32_t)((NTK / 128) * i * 16); });
     }
     if (G::XKBYTES > 0)
-      stage<G::XKBYTES / 16>(kbuf + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
-                             [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
+      stage<G::XKBYTES / 16, NTK, PP>(kb + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
+                                  [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
   };
   // direct V: thread (cc, g) = (tid / 32, tid % 32) moves the 16 keys of
   // V^T column cc (keys 64 (cc & 1) + 16 (cc >> 1) + r) times channels
@@ -735,13 +806,18 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
     for (int jj = 0; jj < 4; ++jj)
       *reinterpret_cast<uint4*>(vbuf + (vcc * D + 4 * vg + jj) * 16) = make_uint4(o[jj][0], o[jj][1], o[jj][2], o[jj][3]);
   };
-  auto issue_v = [&](int t) {
-    stage<G::VBYTES / 16>(vbuf, vtbase + (int64_t)t * G::VBYTES, wave, lane,
-                          [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
+  auto issue_v = [&](int t, uint8_t* vb) {
+    stage<G::VBYTES / 16, NTK, PP>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane,
+                               [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
     if (G::XVBYTES > 0)
-      stage<G::XVBYTES / 16>(vbuf + G::VBYTES, auxbase + (int64_t)t * G::XBYTES + G::XKBYTES, wave, lane,
-                             [&](int i) { return (uint32_t)((i * NTHR + pw) * 16); });
+      stage<G::XVBYTES / 16, NTK, PP>(vb + G::VBYTES, auxbase + (int64_t)t * G::XBYTES + G::XKBYTES, wave, lane,
+                                  [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
   };
+  // copies each tile costs this wave (the wait counts of the ping-pong loop)
+  const int kloads = stage_loads<G::KBYTES / 16, NTK>(wave) +
+                     (G::XKBYTES > 0 ? stage_loads<G::XKBYTES / 16, NTK>(wave) : 0);
+  const int vloads = stage_loads<G::VBYTES / 16, NTK>(wave) +
+                     (G::XVBYTES > 0 ? stage_loads<G::XVBYTES / 16, NTK>(wave) : 0);
 
   // Row state (each lane holds its query's; both halves agree).  O holds
   // the output relative to a reference factor fref: the true accumulator is
@@ -753,316 +829,409 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(const KParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) O[db] = f32x16{};
 
-  const int qlast = min(Sq, (qt + 1) * BM) - 1;
+  // per-group query range (ping-pong: group g holds queries
+  // [qt BMK + 128 g, qt BMK + 128 g + 128)) and its causal diagonal tile
+  const int gq0 = qt * BMK + 128 * grp;
+  const int qlast = min(Sq, (qt + 1) * BMK) - 1;           // the workgroup's
+  const int qlast_g = min(Sq, gq0 + 128) - 1;               // the group's
+  const int dtile = gq0 / BN;
   const int t_beg = split * p.tps;
   const int t_end = CAUSAL ? min(nt, qlast / BN + 1) : min(nt, t_beg + p.tps);
+  const int t_end_g = CAUSAL ? min(t_end, qlast_g / BN + 1) : t_end;
   const float vscale_i8 = (PV == PV_I8H) ? p.vs_head[hd] * (1.0f / 127.0f) : 1.0f;
   // valid keys of this lane's query: [0, lim)
   const int lim = CAUSAL ? min(Skv, qi + 1) : Skv;
 
-  issue_k(t_beg);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-#pragma clang loop unroll(disable)
-  for (int t = t_beg; t < t_end; ++t) {
-    if (VDIR) load_v(t);
-    else issue_v(t);
-    const int k0 = t * BN;
-    // the ragged last tile and the causal diagonal need a per-key validity
-    // test; the other tiles skip it (uniform branch)
-    const bool masked = (k0 + BN > Skv) || (CAUSAL && t == qt);
-    const int rel = lim - k0 - 64 * h;  // key 64 h + 16 kb + r is valid when 16 kb + r < rel
-
-    f32x16 S[4];
-    i32x16 SI[4];
-    float rscale = 1.f, ce = cq, ms = 0.f, bt = 0.f;
-    float gmax[2] = {-INFINITY, -INFINITY};
-    if (act) {
-      // ---- S^T = K Q^T: four 32-key blocks, two at a time (two
-      // independent accumulation chains keep the MFMA pipe full)
+  // ---- one tile in two phases.  Scores: S^T = K Q^T, per-key scales,
+  // masking, the tile maximum and the row's combination factors.  Values:
+  // probabilities, tile sum, the quantized P operand and O^T += V^T P^T.
+  // The score phase leaves its state here for the value phase.
+  f32x16 S[4];
+  i32x16 SI[4];
+  float rscale = 1.f, ce = cq, ms = 0.f, bt = 0.f;
+  float gmax[2] = {-INFINITY, -INFINITY};
+  auto phase_scores = [&](const int t, const uint8_t* kb) __attribute__((always_inline)) {
+      const int k0 = t * BN;
+      // the ragged last tile and the causal diagonal need a per-key validity
+      // test; the other tiles skip it (uniform branch)
+      const bool masked = (k0 + BN > Skv) || (CAUSAL && t == dtile);
+      const int rel = lim - k0 - 64 * h;  // key 64 h + 16 kb + r is valid when 16 kb + r < rel
+      const uint8_t* kop_base = kb + kop_off;
+      const float* xk = reinterpret_cast<const float*>(kb + xk_off);
+      const uint8_t* xmx = kb + xmx_off;
+      rscale = 1.f; ce = cq; ms = 0.f; bt = 0.f;
+      gmax[0] = -INFINITY; gmax[1] = -INFINITY;
+      if (act) {
+        // ---- S^T = K Q^T: four 32-key blocks, two at a time (two
+        // independent accumulation chains keep the MFMA pipe full)
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
+        for (int pr = 0; pr < 2; ++pr) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+          for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int kb = 2 * pr + kk;
-            const uint8_t* a = kop_base + ks * (2 * BN * 16) + kb * 256;
-            if (G::QBF) {
-              if (ks == 0) S[kb] = f32x16{};
-              S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld<bf16x8>(a), qbf[ks], S[kb], 0, 0, 0);
-            } else if (G::QI8) {
-              if (ks == 0) SI[kb] = i32x16{};
-              const uint4 v = lds_ld<uint4>(a);
-              SI[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, qi8[ks],
-                                                             SI[kb], 0, 0, 0);
-            } else {
-              if (ks == 0) S[kb] = f32x16{};
-              const uint4 v = lds_ld<uint4>(a);
-              const int sc = xmx[16 * kb * NB + 2 * ks];
-              S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}, qmx[ks], S[kb], 4, 4, 0, sc, 0, qsc[ks]);
+            for (int kk = 0; kk < 2; ++kk) {
+              const int kb = 2 * pr + kk;
+              const uint8_t* a = kop_base + ks * (2 * BN * 16) + kb * 256;
+              if (G::QBF) {
+                if (ks == 0) S[kb] = f32x16{};
+                S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld<bf16x8>(a), qbf[ks], S[kb], 0, 0, 0);
+              } else if (G::QI8) {
+                if (ks == 0) SI[kb] = i32x16{};
+                const uint4 v = lds_ld<uint4>(a);
+                SI[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, qi8[ks],
+                                                               SI[kb], 0, 0, 0);
+              } else {
+                if (ks == 0) S[kb] = f32x16{};
+                const uint4 v = lds_ld<uint4>(a);
+                const int sc = xmx[16 * kb * NB + 2 * ks];
+                S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}, qmx[ks], S[kb], 4, 4, 0, sc, 0, qsc[ks]);
+              }
             }
           }
         }
-      }
 
-      // ---- per-key K scale, masking, tile maximum
-      float m;
-      if (QK == QK_I8H) {
-        if (!masked) {
-          // exact int32 scores (|s| < 2^21): max in integers, converted once
-          int mi = INT_MIN;
+        // ---- per-key K scale, masking, tile maximum
+        float m;
+        if (QK == QK_I8H) {
+          if (!masked) {
+            // exact int32 scores (|s| < 2^21): max in integers, converted once
+            int mi = INT_MIN;
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mi = max(mi, max(SI[kb][r], SI[kb][r + 1]));
-          m = (float)mi;
+              for (int r = 0; r < 16; r += 2) mi = max(mi, max(SI[kb][r], SI[kb][r + 1]));
+            m = (float)mi;
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[kb][r] = (float)SI[kb][r];
+              for (int r = 0; r < 16; ++r) S[kb][r] = (float)SI[kb][r];
+          } else {
+            m = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                S[kb][r] = (16 * kb + r < rel) ? (float)SI[kb][r] : -INFINITY;
+                m = fmaxf(m, S[kb][r]);
+              }
+          }
         } else {
-          m = -INFINITY;
+          if (QK == QK_I8T) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              S[kb][r] = (16 * kb + r < rel) ? (float)SI[kb][r] : -INFINITY;
-              m = fmaxf(m, S[kb][r]);
-            }
+              for (int r = 0; r < 16; ++r) S[kb][r] = (float)SI[kb][r];
+          }
+          if (PERKEY) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 sk = *reinterpret_cast<const float4*>(xk + 16 * kb + 4 * q4);
+                S[kb][4 * q4 + 0] *= sk.x; S[kb][4 * q4 + 1] *= sk.y;
+                S[kb][4 * q4 + 2] *= sk.z; S[kb][4 * q4 + 3] *= sk.w;
+              }
+          }
+          if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) S[kb][r] = (16 * kb + r < rel) ? S[kb][r] : -INFINITY;
+          }
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            float x = -INFINITY;
+#pragma unroll
+            for (int kb = 2 * g2; kb < 2 * g2 + 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(S[kb][r], S[kb][r + 1]));
+            gmax[g2] = x;  // MX probabilities: the lane's 32-key group maxima
+          }
+          m = fmaxf(gmax[0], gmax[1]);
         }
-      } else {
-        if (QK == QK_I8T) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[kb][r] = (float)SI[kb][r];
-        }
-        if (PERKEY) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const float4 sk = *reinterpret_cast<const float4*>(xk + 16 * kb + 4 * q4);
-              S[kb][4 * q4 + 0] *= sk.x; S[kb][4 * q4 + 1] *= sk.y;
-              S[kb][4 * q4 + 2] *= sk.z; S[kb][4 * q4 + 3] *= sk.w;
-            }
-        }
-        if (masked) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[kb][r] = (16 * kb + r < rel) ? S[kb][r] : -INFINITY;
-        }
-#pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-          float x = -INFINITY;
-#pragma unroll
-          for (int kb = 2 * g2; kb < 2 * g2 + 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(S[kb][r], S[kb][r + 1]));
-          gmax[g2] = x;  // MX probabilities: the lane's 32-key group maxima
-        }
-        m = fmaxf(gmax[0], gmax[1]);
-      }
-      m = halves_max(m);
+        m = halves_max(m);
 
-      // ---- the row's combination factors: a rescales what was
-      // accumulated so far, bt weights this tile
-      if (KCONST) ce = cq * xk[-64 * h];  // the tile's K scale
-      const float ml = m * ce;  // tile max, log2 units (M is kept in these units)
-      float Mn, a;
-      if (G::PI8) {
-        // lazy reference: keep the running reference unless this tile's max
-        // exceeds it by more than 2^8 (tile weights stay <= 2^8, far from
-        // overflow), so O is rescaled only when the max jumps
-        const bool jump = ml > M + 8.0f;
-        Mn = jump ? ml : M;
-        a = jump ? __builtin_amdgcn_exp2f(M - ml) : 1.0f;
-      } else {
-        Mn = fmaxf(M, ml);
-        a = __builtin_amdgcn_exp2f(M - Mn);
-      }
-      bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml - Mn);
-      M = Mn;
-      bool live = true;
-      if (G::PI8) {
-        rscale = a;
-      } else {
-        // new reference factor f = bt (times sigma_t / 448 for FP8 values);
+        // ---- the row's combination factors: a rescales what was
+        // accumulated so far, bt weights this tile
+        if (KCONST) ce = cq * xk[-64 * h];  // the tile's K scale
+        const float ml = m * ce;  // tile max, log2 units (M is kept in these units)
+        float Mn, a;
+        if (G::PI8) {
+          // lazy reference: keep the running reference unless this tile's max
+          // exceeds it by more than 2^8 (tile weights stay <= 2^8, far from
+          // overflow), so O is rescaled only when the max jumps
+          const bool jump = ml > M + 8.0f;
+          Mn = jump ? ml : M;
+          a = jump ? __builtin_amdgcn_exp2f(M - ml) : 1.0f;
+        } else {
+          Mn = fmaxf(M, ml);
+          a = __builtin_amdgcn_exp2f(M - Mn);
+        }
+        bt = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml - Mn);
+        M = Mn;
         // a row whose tile is negligible (bt < 2^-64) keeps its reference
-        // and contributes nothing, which keeps O bounded
-        float ft = bt;
-        if (PV == PV_F8W || PV == PV_F8C) ft *= p.sig[bh * nt + t] * (1.0f / 448.0f);
-        live = bt >= 0x1p-64f;
-        rscale = live ? fref * a * __builtin_amdgcn_rcpf(ft) : a;
-        fref = live ? ft : fref;
+        // and contributes nothing, which keeps O bounded (bf16 value
+        // product; the value phase takes the new reference factor)
+        const bool live = G::PI8 || bt >= 0x1p-64f;
+        rscale = a;
+        L *= a;
+        // a row that is not live takes +inf as its reference, so all its p are 0
+        ms = (m == -INFINITY) ? 0.0f : (live ? m : INFINITY);
       }
-      L *= a;
-      // a row that is not live takes +inf as its reference, so all its p are 0
-      ms = (m == -INFINITY) ? 0.0f : (live ? m : INFINITY);
-    }
-
-    // V(t) has landed everywhere and every wave is done with K(t) (direct V:
-    // every wave finished P V of tile t - 1 at the last barrier, so V^T(t)
-    // goes into the LDS tile now)
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    if (VDIR) store_vt();
-    __syncthreads();
-    if (t + 1 < t_end) issue_k(t + 1);
-
-    if (act) {
-      // ---- probabilities, tile sum, the quantized P operand and
-      // O^T += V^T P^T
-      float ls0 = 0.f, ls1 = 0.f;
-      if (G::PI8) {
-        // the running max moves rarely once a row has seen its largest
-        // scores: rescale only when some row of the wave needs it (before
-        // the probabilities, so that they and their products share a block)
-        if (__builtin_amdgcn_ballot_w64(rscale != 1.0f) != 0) {
+  };
+  auto phase_values = [&](const int t, const uint8_t* vb) __attribute__((always_inline)) {
+      // the vector-heavy phase issues first when both waves of a SIMD are
+      // ready, so the other wave's products fill the matrix unit meanwhile
+      __builtin_amdgcn_s_setprio(1);
+      const uint8_t* vop_base = vb + vop_off;
+      const float* xv = reinterpret_cast<const float*>(vb + xv_off);
+      const float sig_t = G::SIG ? *reinterpret_cast<const float*>(vb + G::VBYTES + G::XVW) : 1.0f;
+      if (act) {
+        // ---- probabilities, tile sum, the quantized P operand and
+        // O^T += V^T P^T
+        float ls0 = 0.f, ls1 = 0.f;
+        if (G::PI8) {
+          // the running max moves rarely once a row has seen its largest
+          // scores: rescale only when some row of the wave needs it (before
+          // the probabilities, so that they and their products share a block)
+          if (__builtin_amdgcn_ballot_w64(rscale != 1.0f) != 0) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) O[db] *= rscale;
+          }
+          // per-head: 127 p = 2^((s - m) ce + log2 127), s - m exact (integer
+          // scores), so every p of the tile is relative to the tile maximum
+          // with no error growing with |m ce| (the unquantized p also feed
+          // the row sum L).  per-token: p = 1 exactly at the maximum, times
+          // 127 w_j.
+          i32x4 P[4];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              float4 vm4;
+              if (PV == PV_I8T) vm4 = *reinterpret_cast<const float4*>(xv + 16 * kb + 4 * w);
+              const float vm[4] = {vm4.x, vm4.y, vm4.z, vm4.w};
+              uint32_t word = 0;
+#pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                const float x = S[kb][4 * w + b];
+                float pv = PV == PV_I8H ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_127))
+                                        : __builtin_amdgcn_exp2f((x - ms) * ce);
+                if (b & 1) ls1 += pv; else ls0 += pv;
+                if (PV == PV_I8T) pv *= vm[b];
+                word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
+              }
+              P[kb][w] = (int)word;
+            }
+          }
+          L += halves_sum(ls0 + ls1) * (PV == PV_I8H ? bt * (1.0f / 127.0f) : bt);
+          const float bv = PV == PV_I8H ? bt * vscale_i8 : bt * sig_t * (1.0f / 127.0f);
+          // two output blocks at a time: two independent accumulation chains
+#pragma unroll
+          for (int d2 = 0; d2 < DB; d2 += 2) {
+            i32x16 C[2] = {i32x16{}, i32x16{}};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int dd = 0; dd < 2; ++dd) {
+                const uint4 v = lds_ld<uint4>(vop_base + kb * (2 * D * 16) + (d2 + dd) * 512);
+                C[dd] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, P[kb],
+                                                              C[dd], 0, 0, 0);
+              }
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) O[d2 + dd][r] = __builtin_fmaf((float)C[dd][r], bv, O[d2 + dd][r]);
+          }
+        } else {
+          // bf16 value product: the new reference factor f = bt (times
+          // sigma_t / 448 for FP8 values; a row that is not live keeps its
+          // own), rescale, then per 32-key block: probabilities, the bf16 P
+          // operand of its two k-steps, and their products
+          {
+            float ft = bt;
+            if (PV == PV_F8W || PV == PV_F8C) ft *= sig_t * (1.0f / 448.0f);
+            const bool live = bt >= 0x1p-64f;
+            rscale = live ? fref * rscale * __builtin_amdgcn_rcpf(ft) : rscale;
+            fref = live ? ft : fref;
+          }
 #pragma unroll
           for (int db = 0; db < DB; ++db) O[db] *= rscale;
-        }
-        // per-head: 127 p = 2^((s - m) ce + log2 127), s - m exact (integer
-        // scores), so every p of the tile is relative to the tile maximum
-        // with no error growing with |m ce| (the unquantized p also feed
-        // the row sum L).  per-token: p = 1 exactly at the maximum, times
-        // 127 w_j.
-        i32x4 P[4];
+          float sc = 1.0f, isc = 1.0f;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+          for (int kb = 0; kb < 4; ++kb) {
+            if (G::PMX && (kb & 1) == 0) {
+              // this lane's keys of blocks kb, kb + 1 are one MX group:
+              // group max -> shared exponent; p -> E2M1 / E4M3 of p / 2^E,
+              // times 2^E, exact in bf16.  The group's largest p is the same
+              // function of the group's largest score.
+              const float pmax = __builtin_amdgcn_exp2f((gmax[kb >> 1] - ms) * ce);
+              const int E = PV == PV_MX4 ? mx_exponent(pmax) : mx_exponent<8>(pmax);
+              sc = E > -127 ? pow2f(E) : 1.0f;
+              isc = E > -127 ? pow2f(-E) : 1.0f;
+            }
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            float4 vm4;
-            if (PV == PV_I8T) vm4 = *reinterpret_cast<const float4*>(xv + 16 * kb + 4 * w);
-            const float vm[4] = {vm4.x, vm4.y, vm4.z, vm4.w};
-            uint32_t word = 0;
+            for (int s2 = 0; s2 < 2; ++s2) {
+              float pv[8];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const float x = S[kb][4 * w + b];
-              float pv = PV == PV_I8H ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_127))
+              for (int t8 = 0; t8 < 8; ++t8) {
+                const float x = S[kb][8 * s2 + t8];
+                // one V scale per tile: 448 p = 2^((x - m) ce + log2 448), at
+                // the maximum within an ulp of 448, whose code both roundings
+                // give.  Otherwise p = 1 exactly at the tile maximum: there
+                // 448 w_j can sit on an E4M3 tie (bf16-derived scale ratios
+                // do), and the MX group of the maximum has its amax at a power
+                // of two.  Both are relative to the tile maximum with no error
+                // growing with |m ce| (the unquantized p also feed L).
+                pv[t8] = PV == PV_F8C ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_448))
                                       : __builtin_amdgcn_exp2f((x - ms) * ce);
-              if (b & 1) ls1 += pv; else ls0 += pv;
-              if (PV == PV_I8T) pv *= vm[b];
-              word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
-            }
-            P[kb][w] = (int)word;
-          }
-        }
-        L += halves_sum(ls0 + ls1) * (PV == PV_I8H ? bt * (1.0f / 127.0f) : bt);
-        const float bv = PV == PV_I8H ? bt * vscale_i8 : bt * p.sig[bh * nt + t] * (1.0f / 127.0f);
-        // two output blocks at a time: two independent accumulation chains
-#pragma unroll
-        for (int d2 = 0; d2 < DB; d2 += 2) {
-          i32x16 C[2] = {i32x16{}, i32x16{}};
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-              const uint4 v = lds_ld<uint4>(vop_base + kb * (2 * D * 16) + (d2 + dd) * 512);
-              C[dd] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, P[kb],
-                                                            C[dd], 0, 0, 0);
-            }
-#pragma unroll
-          for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) O[d2 + dd][r] = __builtin_fmaf((float)C[dd][r], bv, O[d2 + dd][r]);
-        }
-      } else {
-        // bf16 value product: rescale, then per 32-key block: probabilities,
-        // the bf16 P operand of its two k-steps, and their products
-#pragma unroll
-        for (int db = 0; db < DB; ++db) O[db] *= rscale;
-        float sc = 1.0f, isc = 1.0f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          if (G::PMX && (kb & 1) == 0) {
-            // this lane's keys of blocks kb, kb + 1 are one MX group:
-            // group max -> shared exponent; p -> E2M1 / E4M3 of p / 2^E,
-            // times 2^E, exact in bf16.  The group's largest p is the same
-            // function of the group's largest score.
-            const float pmax = __builtin_amdgcn_exp2f((gmax[kb >> 1] - ms) * ce);
-            const int E = PV == PV_MX4 ? mx_exponent(pmax) : mx_exponent<8>(pmax);
-            sc = E > -127 ? pow2f(E) : 1.0f;
-            isc = E > -127 ? pow2f(-E) : 1.0f;
-          }
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            float pv[8];
-#pragma unroll
-            for (int t8 = 0; t8 < 8; ++t8) {
-              const float x = S[kb][8 * s2 + t8];
-              // one V scale per tile: 448 p = 2^((x - m) ce + log2 448), at
-              // the maximum within an ulp of 448, whose code both roundings
-              // give.  Otherwise p = 1 exactly at the tile maximum: there
-              // 448 w_j can sit on an E4M3 tie (bf16-derived scale ratios
-              // do), and the MX group of the maximum has its amax at a power
-              // of two.  Both are relative to the tile maximum with no error
-              // growing with |m ce| (the unquantized p also feed L).
-              pv[t8] = PV == PV_F8C ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_448))
-                                    : __builtin_amdgcn_exp2f((x - ms) * ce);
-              if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
-            }
-            i32x4 pop;
-            if (PV == PV_F8W || PV == PV_F8C) {
-              // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
-              if (PV == PV_F8W) {
-                const float4 v0 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2);
-                const float4 v1 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2 + 4);
-                pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
-                pv[4] *= v1.x; pv[5] *= v1.y; pv[6] *= v1.z; pv[7] *= v1.w;
+                if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
               }
-              int e0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-              e0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], e0, true);
-              int e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4], pv[5], 0, false);
-              e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], e1, true);
-              pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0), (int)e4m3x2_to_bf16x2<true>((uint32_t)e0),
-                          (int)e4m3x2_to_bf16x2<false>((uint32_t)e1), (int)e4m3x2_to_bf16x2<true>((uint32_t)e1)};
-            } else if (PV == PV_MX8) {
-              // E4M3 of p / 2^E (exact scaling; the group maximum lies in
-              // [256, 512) and saturates above 448), then back times 2^E
-              float u[8];
+              i32x4 pop;
+              if (PV == PV_F8W || PV == PV_F8C) {
+                // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
+                if (PV == PV_F8W) {
+                  const float4 v0 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2);
+                  const float4 v1 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2 + 4);
+                  pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
+                  pv[4] *= v1.x; pv[5] *= v1.y; pv[6] *= v1.z; pv[7] *= v1.w;
+                }
+                int e0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+                e0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], e0, true);
+                int e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4], pv[5], 0, false);
+                e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], e1, true);
+                pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0), (int)e4m3x2_to_bf16x2<true>((uint32_t)e0),
+                            (int)e4m3x2_to_bf16x2<false>((uint32_t)e1), (int)e4m3x2_to_bf16x2<true>((uint32_t)e1)};
+              } else if (PV == PV_MX8) {
+                // E4M3 of p / 2^E (exact scaling; the group maximum lies in
+                // [256, 512) and saturates above 448), then back times 2^E
+                float u[8];
 #pragma unroll
-              for (int t8 = 0; t8 < 8; ++t8) u[t8] = fminf(pv[t8] * isc, 448.0f);
-              int e0 = __builtin_amdgcn_cvt_pk_fp8_f32(u[0], u[1], 0, false);
-              e0 = __builtin_amdgcn_cvt_pk_fp8_f32(u[2], u[3], e0, true);
-              int e1 = __builtin_amdgcn_cvt_pk_fp8_f32(u[4], u[5], 0, false);
-              e1 = __builtin_amdgcn_cvt_pk_fp8_f32(u[6], u[7], e1, true);
-              pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0, sc),
-                          (int)e4m3x2_to_bf16x2<true>((uint32_t)e0, sc),
-                          (int)e4m3x2_to_bf16x2<false>((uint32_t)e1, sc),
-                          (int)e4m3x2_to_bf16x2<true>((uint32_t)e1, sc)};
-            } else if (PV == PV_MX4) {
-              // each pair through byte 0: E2M1(p / 2^E), then back times 2^E
+                for (int t8 = 0; t8 < 8; ++t8) u[t8] = fminf(pv[t8] * isc, 448.0f);
+                int e0 = __builtin_amdgcn_cvt_pk_fp8_f32(u[0], u[1], 0, false);
+                e0 = __builtin_amdgcn_cvt_pk_fp8_f32(u[2], u[3], e0, true);
+                int e1 = __builtin_amdgcn_cvt_pk_fp8_f32(u[4], u[5], 0, false);
+                e1 = __builtin_amdgcn_cvt_pk_fp8_f32(u[6], u[7], e1, true);
+                pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0, sc),
+                            (int)e4m3x2_to_bf16x2<true>((uint32_t)e0, sc),
+                            (int)e4m3x2_to_bf16x2<false>((uint32_t)e1, sc),
+                            (int)e4m3x2_to_bf16x2<true>((uint32_t)e1, sc)};
+              } else if (PV == PV_MX4) {
+                // each pair through byte 0: E2M1(p / 2^E), then back times 2^E
 #pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                const uint32_t f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv[2 * b], pv[2 * b + 1], sc, 0);
-                pop[b] = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
+                for (int b = 0; b < 4; ++b) {
+                  const uint32_t f4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pv[2 * b], pv[2 * b + 1], sc, 0);
+                  pop[b] = (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f4, sc, 0));
+                }
+              } else {
+                // unquantized V: p rounded to bf16 (nearest even)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                  const bf16x2 pr2 = {(__bf16)pv[2 * b], (__bf16)pv[2 * b + 1]};
+                  pop[b] = (int)__builtin_bit_cast(uint32_t, pr2);
+                }
               }
-            } else {
-              // unquantized V: p rounded to bf16 (nearest even)
+              const bf16x8 pb = __builtin_bit_cast(bf16x8, pop);
+              const int kst = 2 * kb + s2;
 #pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                const bf16x2 pr2 = {(__bf16)pv[2 * b], (__bf16)pv[2 * b + 1]};
-                pop[b] = (int)__builtin_bit_cast(uint32_t, pr2);
-              }
+              for (int db = 0; db < DB; ++db)
+                O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    lds_ld<bf16x8>(vop_base + kst * (2 * D * 16) + db * 512), pb, O[db], 0, 0, 0);
             }
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pop);
-            const int kst = 2 * kb + s2;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-              O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  lds_ld<bf16x8>(vop_base + kst * (2 * D * 16) + db * 512), pb, O[db], 0, 0, 0);
           }
+          const float lsc = PV == PV_F8C ? (1.0f / 448.0f) : 1.0f;
+          L += halves_sum(ls0 + ls1) * (bt * lsc);
         }
-        const float lsc = PV == PV_F8C ? (1.0f / 448.0f) : 1.0f;
-        L += halves_sum(ls0 + ls1) * (bt * lsc);
       }
-    }
-    // K(t+1) has landed everywhere and every wave is done with V(t)
+      __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (!PP) {
+    issue_k(t_beg, kbuf);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+#pragma clang loop unroll(disable)
+    for (int t = t_beg; t < t_end; ++t) {
+      if (VDIR) load_v(t);
+      else issue_v(t, vbuf);
+      phase_scores(t, kbuf);
+      // V(t) has landed everywhere and every wave is done with K(t) (direct
+      // V: every wave finished P V of tile t - 1 at the last barrier, so
+      // V^T(t) goes into the LDS tile now)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      if (VDIR) store_vt();
+      __syncthreads();
+      if (t + 1 < t_end) issue_k(t + 1, kbuf);
+      phase_values(t, vbuf);
+      // K(t+1) has landed everywhere and every wave is done with V(t)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+    }
+  } else {
+    // Slots separated by workgroup barriers.  Slot 2r: group 0 scores tile
+    // r while group 1 takes the values of tile r - 1; slot 2r + 1: group 0
+    // the values of r, group 1 the scores of r.  Copies: slot 2r issues
+    // K(r + 1), slot 2r + 1 issues V(r + 1), each into the buffer of its
+    // tile's parity; the tile a slot needs next has landed at its end,
+    // while the copy it issued may stay in flight (vmcnt of that copy).
+    // r counts tiles from t_beg; even r use kbuf / vbuf, odd r kbuf1 / vbuf1
+    // (separate objects, so the compiler sees that reads of one buffer never
+    // alias copies into the other).
+    const int nr = t_end - t_beg, nr_g = t_end_g - t_beg;
+    auto slot_k = [&](int r, auto odd) __attribute__((always_inline)) {  // issue K(r) into its buffer
+      if (r < nr) issue_k(t_beg + r, decltype(odd)::value ? kbuf1 : kbuf);
+      return r < nr ? kloads : 0;
+    };
+    auto slot_v = [&](int r, auto odd) __attribute__((always_inline)) {
+      if (r < nr) issue_v(t_beg + r, decltype(odd)::value ? vbuf1 : vbuf);
+      return r < nr ? vloads : 0;
+    };
+    using Even = std::integral_constant<bool, false>;
+    using Odd = std::integral_constant<bool, true>;
+    // tile r (parity ODD) of this wave: its two slots
+    auto tile = [&](int r, auto odd) __attribute__((always_inline)) {
+      constexpr bool O1 = decltype(odd)::value;
+      using Next = std::integral_constant<bool, !O1>;
+      const uint8_t* kb = O1 ? kbuf1 : kbuf;
+      const uint8_t* vb = O1 ? vbuf1 : vbuf;
+      int n;
+      // scores of r: group 0 in slot 2r (issues K(r + 1)), group 1 in slot
+      // 2r + 1 (issues V(r + 1))
+      if (grp == 0) n = slot_k(r + 1, Next{});
+      else n = slot_v(r + 1, Next{});
+      if (r < nr_g) phase_scores(t_beg + r, kb);
+      wait_vm(n);
+      barrier_lds();
+      // values of r: group 0 in slot 2r + 1 (issues V(r + 1)), group 1 in
+      // slot 2r + 2 (issues K(r + 2))
+      if (grp == 0) n = slot_v(r + 1, Next{});
+      else n = slot_k(r + 2, odd);
+      if (r < nr_g) phase_values(t_beg + r, vb);
+      wait_vm(n);
+      barrier_lds();
+    };
+    // prologue: the Q operands are in registers (so that no wait for them
+    // lands inside the loop, where it would also wait for the copies);
+    // K(0) lands before slot 0, V(0) during it
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    issue_k(t_beg, kbuf);
+    issue_v(t_beg, vbuf);
+    wait_vm(vloads);
+    barrier_lds();
+    if (grp == 1) {  // slot 0 of group 1: no work, its share of K(1)
+      wait_vm(slot_k(1, Odd{}));
+      barrier_lds();
+    }
+#pragma clang loop unroll(disable)
+    for (int r = 0; r < nr; r += 2) {
+      tile(r, Even{});
+      if (r + 1 < nr) tile(r + 1, Odd{});
+    }
+    if (grp == 0) {  // the last slot: group 1 finishes, no copies left
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      barrier_lds();
+    }
   }
 
   // ---- a key split leaves its partial result: O times its reference
@@ -1161,7 +1330,6 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   pa.vsb = a.v_sb; pa.vsh = a.v_sh; pa.vblk = a.v_block;
   pa.kfmt = a.kfmt;
   pa.vt = ws + l.vt_off; pa.kb = ws + l.kb_off; pa.aux = ws + l.aux_off;
-  pa.sig = reinterpret_cast<float*>(ws + l.sig_off);
   const KvSplit sp = kv_split(a.B, a.H, a.Sq, a.Skv, a.causal);
   // decode with INT8 per-head V: the kernel transposes V itself
   constexpr bool VDIR_OK = QK == QK_I8H && PV == PV_I8H && D == 128;
@@ -1181,7 +1349,6 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   p.ks = a.k_scales;
   p.vt = ws + l.vt_off;
   p.aux = ws + l.aux_off;
-  p.sig = reinterpret_cast<const float*>(ws + l.sig_off);
   p.vs_head = (const float*)a.v_scales;
   p.q_sb = a.q_sb; p.q_sh = a.q_sh; p.q_block = a.q_block;
   p.qfmt = a.qfmt;
@@ -1201,8 +1368,20 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
       return hipGetLastError();
     }
   }
+  if constexpr (G::QBF) {
+    if (sp.nsplit == 1) {
+      // bf16 score products, no key split: the ping-pong kernel, 256
+      // queries per workgroup (INT8 / MXFP4 scores keep the four-wave
+      // kernel, which is faster for them)
+      p.nqt = (int)((a.Sq + 2 * BM - 1) / (2 * BM));
+      const dim3 g2((unsigned)(p.nqt * p.BH));
+      if (a.causal) k_attn<QK, PV, D, true, false, true><<<g2, 2 * NTHR, 0, st>>>(p);
+      else k_attn<QK, PV, D, false, false, true><<<g2, 2 * NTHR, 0, st>>>(p);
+      return hipGetLastError();
+    }
+  }
   if (a.causal) k_attn<QK, PV, D, true><<<grid, NTHR, 0, st>>>(p);
-  else k_attn<QK, PV, D, false><<<grid, NTHR, 0, st>>>(p);
+  else k_attn<QK, PV, D, false><<<grid, NTHR, 0, st>>>(p);  // key splits are never causal
   e = hipGetLastError();
   if (e != hipSuccess || sp.nsplit == 1) return e;
   k_combine<D><<<(unsigned)((p.BH * p.Sq + 3) / 4), 256, 0, st>>>(p.part, sp.nsplit, p.BH, a.H, a.Sq, a.qmap, a.out,
