@@ -220,8 +220,10 @@ struct WsLayout {
 
 // Key splits: with few query tiles per head (decode: a handful of queries
 // against a long cache) the (b,h, query tile) grid cannot fill 256 CUs, so
-// the key tiles are split across workgroups, tps tiles each, for about
-// 2048 workgroups.  Causal attention (Sq == Skv) never splits.
+// the key tiles are split across workgroups, tps tiles each, for about 512
+// workgroups: one full round at two per CU, each streaming a long run of
+// tiles (fewer, longer splits measure faster than more rounds of short
+// ones).  Causal attention (Sq == Skv) never splits.
 struct KvSplit {
   int nsplit, tps;
 };
@@ -230,7 +232,7 @@ inline KvSplit kv_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int causa
   const int64_t nt = (Skv + BN - 1) / BN;
   const int64_t base = B * H * ((Sq + BM - 1) / BM);
   if (causal || base >= 1024 || nt < 4) return KvSplit{1, (int)nt};
-  int64_t want = (2048 + base - 1) / base;
+  int64_t want = (512 + base - 1) / base;
   if (want > nt / 2) want = nt / 2;
   if (want > 64) want = 64;  // the merge keeps one split per lane
   const int64_t tps = (nt + want - 1) / want;
@@ -783,14 +785,20 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   const int vcc = tid >> 5, vg = tid & 31;
   const int vkey0 = 64 * (vcc & 1) + 16 * (vcc >> 1);
   const uint8_t* vrow = VDIR ? p.vcodes + p.vmap.row(bb, hd, 0) * D + 4 * vg : nullptr;
+  // (every thread issues exactly 16 loads - rows past the end re-read the
+  // last row and are zeroed when stored - so the wait for the K copy issued
+  // before them can count them)
   auto load_v = [&](int t) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = t * BN + vkey0 + r;
-      vreg[r] = key < Skv ? *reinterpret_cast<const uint32_t*>(vrow + (int64_t)key * p.vmap.ss * D) : 0u;
+      vreg[r] = *reinterpret_cast<const uint32_t*>(vrow + (int64_t)min(key, Skv - 1) * p.vmap.ss * D);
     }
   };
-  auto store_vt = [&]() {
+  auto store_vt = [&](int t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (t * BN + vkey0 + r >= Skv) vreg[r] = 0u;
     uint32_t o[4][4];  // [channel j][4-key group]
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
@@ -1148,24 +1156,36 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   };
 
   if (!PP) {
+    // direct V: the rows of V(t + 1) are loaded into registers while the
+    // products of tile t and the scores of t + 1 run (16 loads per thread,
+    // issued after the copy of K(t + 1))
     issue_k(t_beg, kbuf);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (VDIR) {
+      load_v(t_beg);
+      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): K(t_beg) has landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
     __syncthreads();
 #pragma clang loop unroll(disable)
     for (int t = t_beg; t < t_end; ++t) {
-      if (VDIR) load_v(t);
-      else issue_v(t, vbuf);
+      if (!VDIR) issue_v(t, vbuf);
       phase_scores(t, kbuf);
       // V(t) has landed everywhere and every wave is done with K(t) (direct
       // V: every wave finished P V of tile t - 1 at the last barrier, so
       // V^T(t) goes into the LDS tile now)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      if (VDIR) store_vt();
+      if (VDIR) store_vt(t);
       __syncthreads();
-      if (t + 1 < t_end) issue_k(t + 1, kbuf);
+      const bool more = t + 1 < t_end;
+      if (more) {
+        issue_k(t + 1, kbuf);
+        if (VDIR) load_v(t + 1);
+      }
       phase_values(t, vbuf);
       // K(t+1) has landed everywhere and every wave is done with V(t)
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      if (VDIR && more) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): V(t + 1) may stay in flight
+      else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
       __syncthreads();
     }
   } else {
