@@ -615,8 +615,9 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   constexpr int KSZ = G::KBYTES + G::XKBYTES, VSZ = G::VBYTES + G::XVBYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[KSZ];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[VSZ];
-  // ping-pong: the second K and V^T buffers (odd tiles of the work item)
-  __shared__ __attribute__((aligned(PP ? 1024 : 16))) uint8_t kbuf1[PP ? KSZ : 16];
+  // ping-pong: the second K and V^T buffers (odd tiles of the work item);
+  // direct V: the second K buffer
+  __shared__ __attribute__((aligned(PP || VDIR ? 1024 : 16))) uint8_t kbuf1[PP || VDIR ? KSZ : 16];
   __shared__ __attribute__((aligned(PP ? 1024 : 16))) uint8_t vbuf1[PP ? VSZ : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, j = lane & 31, h = lane >> 5;
@@ -766,15 +767,15 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   const int krow = kslot(pw & (BN - 1));
   auto issue_k = [&](int t, uint8_t* kb) {
     if (G::QIMG) {
-      stage<G::KBYTES / 16, NTK, PP>(kb, kbase + (int64_t)t * G::KBYTES, wave, lane,
+      stage<G::KBYTES / 16, NTK, PP || VDIR>(kb, kbase + (int64_t)t * G::KBYTES, wave, lane,
                                  [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
     } else {
       const uint32_t roff = (uint32_t)min(t * BN + krow, Skv - 1) * kstride + (uint32_t)((pw >> 7) * 16);
-      stage<G::KBYTES / 16, NTK, PP>(kb, kbase, wave, lane,
+      stage<G::KBYTES / 16, NTK, PP || VDIR>(kb, kbase, wave, lane,
                                  [&](int i) { return roff + (uint32_t)((NTK / 128) * i * 16); });
     }
     if (G::XKBYTES > 0)
-      stage<G::XKBYTES / 16, NTK, PP>(kb + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
+      stage<G::XKBYTES / 16, NTK, PP || VDIR>(kb + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
                                   [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
   };
   // direct V: thread (cc, g) = (tid / 32, tid % 32) moves the 16 keys of
@@ -1155,37 +1156,49 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
       __builtin_amdgcn_s_setprio(0);
   };
 
-  if (!PP) {
-    // direct V: the rows of V(t + 1) are loaded into registers while the
-    // products of tile t and the scores of t + 1 run (16 loads per thread,
-    // issued after the copy of K(t + 1))
-    issue_k(t_beg, kbuf);
-    if (VDIR) {
-      load_v(t_beg);
-      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): K(t_beg) has landed
-    } else {
+  if (VDIR) {
+    // direct V (decode): the rows of V(t + 1) are loaded into registers and
+    // K(t + 2) is copied into the other K buffer while the products of
+    // tile t and the scores of t + 1 run.  K copies are not tracked by the
+    // compiler; the wait for the V rows (vmcnt(0) before they are stored)
+    // also covers the K copy issued before them, and the barriers drain
+    // nothing else.
+    // (K(t) lives in the buffer of t's parity)
+    issue_k(t_beg, (t_beg & 1) ? kbuf1 : kbuf);
+    if (t_beg + 1 < t_end) issue_k(t_beg + 1, (t_beg & 1) ? kbuf : kbuf1);
+    load_v(t_beg);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    barrier_lds();
+#pragma clang loop unroll(disable)
+    for (int t = t_beg; t < t_end; ++t) {
+      uint8_t* kb = (t & 1) ? kbuf1 : kbuf;
+      phase_scores(t, kb);
+      // V(t) and K(t + 1) have landed; V^T(t) goes into the LDS tile (every
+      // wave finished the products of t - 1 at the last barrier)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      store_vt(t);
+      barrier_lds();
+      // every wave is done with K(t): its buffer takes K(t + 2)
+      if (t + 2 < t_end) issue_k(t + 2, kb);
+      if (t + 1 < t_end) load_v(t + 1);
+      phase_values(t, vbuf);
+      barrier_lds();
     }
+  } else if (!PP) {
+    issue_k(t_beg, kbuf);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 #pragma clang loop unroll(disable)
     for (int t = t_beg; t < t_end; ++t) {
-      if (!VDIR) issue_v(t, vbuf);
+      issue_v(t, vbuf);
       phase_scores(t, kbuf);
-      // V(t) has landed everywhere and every wave is done with K(t) (direct
-      // V: every wave finished P V of tile t - 1 at the last barrier, so
-      // V^T(t) goes into the LDS tile now)
+      // V(t) has landed everywhere and every wave is done with K(t)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      if (VDIR) store_vt(t);
       __syncthreads();
-      const bool more = t + 1 < t_end;
-      if (more) {
-        issue_k(t + 1, kbuf);
-        if (VDIR) load_v(t + 1);
-      }
+      if (t + 1 < t_end) issue_k(t + 1, kbuf);
       phase_values(t, vbuf);
       // K(t+1) has landed everywhere and every wave is done with V(t)
-      if (VDIR && more) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): V(t + 1) may stay in flight
-      else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
     }
   } else {
