@@ -197,6 +197,14 @@ struct Cfg {
   static constexpr int XBYTES = XKBYTES + XVBYTES;  // per tile in the workspace
   static constexpr int VROW = PI8 ? BN : 2 * BN;    // bytes of a V^T row
   static constexpr int VBYTES = D * VROW;
+  // INT8 per-head V: the tile is copied straight from the V rows
+  // (chunk-major, like K) and the value MFMA reads it through the
+  // transposing LDS reads, so no V^T image is made.  (For bf16 V the same
+  // scheme doubles the LDS read instructions of the value product and
+  // measured slower than the V^T image.)
+  static constexpr bool VROWS = PV == PV_I8H;
+  // nothing to prepare: no K image, no per-key extras, V read as rows
+  static constexpr bool NOPREP = VROWS && !QIMG && XKBYTES == 0 && XVBYTES == 0;
   static constexpr int KS = QI8 ? D / 32 : (QBF ? D / 16 : D / 64);  // score k-steps
   static constexpr int DB = D / 32;                                  // 32-channel output blocks
 };
@@ -252,8 +260,9 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int6
   const size_t xv = (pvw ? BN * 4 : 0) + (sig ? 16 : 0);
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WsLayout l{};
+  const bool vrows = pv == PV_I8H;  // V read as rows, no V^T image
   l.vt_off = 0;
-  l.kb_off = up(tiles * D * BN * (pi8 ? 1 : 2));
+  l.kb_off = up(vrows ? 0 : tiles * D * BN * (pi8 ? 1 : 2));
   l.aux_off = l.kb_off + up(qimg ? tiles * BN * D * 2 : 0);
   l.part_off = l.aux_off + up(tiles * (xk + xv));
   const KvSplit sp = kv_split(B, H, Sq, Skv, causal);
@@ -304,8 +313,8 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
   const int64_t tile_id = bh * a.nt + t;
   const int64_t b_ = bh / a.H, h_ = bh % a.H;
   uint8_t* auxt = a.aux + tile_id * C::XBYTES;
-  // V rows -> LDS
-  for (int c = threadIdx.x; c < BN * (VR / 16); c += 256) {
+  // V rows -> LDS (not for V read as rows by the attention kernel)
+  for (int c = threadIdx.x; c < (C::VROWS ? 0 : BN * (VR / 16)); c += 256) {
     const int kl = c / (VR / 16), cc = c % (VR / 16);
     uint4 val = make_uint4(0, 0, 0, 0);
     if (k0 + kl < a.Skv) val = *reinterpret_cast<const uint4*>(a.v + a.vmap.row(b_, h_, k0 + kl) * VR + cc * 16);
@@ -394,7 +403,7 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
   // threads write consecutive 16-byte slots of one column)
   uint8_t* img = a.vt + tile_id * C::VBYTES;
   constexpr int VCOLS = C::VROW / 16;
-  for (int i = threadIdx.x; i < VCOLS * D; i += 256) {
+  for (int i = threadIdx.x; i < (C::VROWS ? 0 : VCOLS * D); i += 256) {
     const int c = i / D, d = i % D;
     uint32_t w[4];
     if (C::PI8) {
@@ -583,6 +592,14 @@ FAQ_DEV void barrier_lds() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Transposing LDS read of bytes (gfx950): within each 16-lane group, lane l
+// receives as its byte k byte l % 8 of the 8 bytes source lane
+// 2 k + (l / 8) % 2 points at.
+using v2i = int __attribute__((ext_vector_type(2)));
+FAQ_DEV v2i lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+}
+
 template <class T>
 FAQ_DEV T lds_ld(const uint8_t* p) {
   return *reinterpret_cast<const T*>(p);
@@ -756,6 +773,25 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   const int xk_off = G::KBYTES + 256 * h;                     // the lane's keys' K scales (floats)
   const int xv_off = G::VBYTES + 256 * h;                     // their qmax w_j (floats)
   const int xmx_off = G::KBYTES + qk_row(j) * NB + h;         // MXFP4: + 16 kb NB + 2 ks
+  // V read as rows: the tile is chunk-major (16-byte column c of the key
+  // rows, key in slot key ^ VSWZ (c & 1), which keeps the two 16-lane
+  // groups of one read in distinct banks).  The A operand of the value MFMA
+  // (rows = channels, k = the keys in P's lane order: k-position 16 h + r
+  // is key 64 h + 16 kb + r) comes from two transposing reads rd: in
+  // 16-lane group g = lane / 16, source lane s points at bytes 8 (s % 2) ..
+  // + 7 of channel chunk g % 2 of key 64 (g / 2) + 16 kb + 8 rd + s / 2, so
+  // output lane l holds channel 16 (g % 2) + l % 16 of keys 8 rd .. + 7.
+  // Offsets at kb = db = 0; kb adds 256 bytes, db 4096.
+  constexpr int VSWZ = 8;
+  int vtr_off[2] = {0, 0};
+  if (G::VROWS && !VDIR) {
+    const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int c = g & 1, key = 64 * (g >> 1) + 8 * rd + (s >> 1);
+      vtr_off[rd] = c * (BN * 16) + (key ^ (VSWZ * (c & 1))) * 16 + 8 * (s & 1);
+    }
+  }
 
   // ---- tile copies.  K: FP8 / MXFP8 copy the bf16 image from the
   // workspace; the other modes gather K rows into the chunk-major layout
@@ -815,9 +851,22 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
     for (int jj = 0; jj < 4; ++jj)
       *reinterpret_cast<uint4*>(vbuf + (vcc * D + 4 * vg + jj) * 16) = make_uint4(o[jj][0], o[jj][1], o[jj][2], o[jj][3]);
   };
+  // V rows (read as rows): the rows of head (b, h) at vrows + r vrstride
+  constexpr int VRB = G::PI8 ? D : 2 * D;  // bytes of a V row
+  const uint8_t* vrows = (G::VROWS && !VDIR) ? p.vcodes + p.vmap.row(bb, hd, 0) * VRB : nullptr;
+  const uint32_t vrstride = (uint32_t)(p.vmap.ss * VRB);
   auto issue_v = [&](int t, uint8_t* vb) {
-    stage<G::VBYTES / 16, NTK, PP>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane,
-                               [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
+    if (G::VROWS && !VDIR) {
+      // chunk i NTK + pw: column c, slot pw % 128 holding key slot ^ VSWZ (c & 1)
+      stage<G::VBYTES / 16, NTK, PP>(vb, vrows, wave, lane, [&](int i) {
+        const int c = i * (NTK / 128) + (pw >> 7);
+        const int key = (pw & (BN - 1)) ^ (VSWZ * (c & 1));
+        return (uint32_t)min(t * BN + key, Skv - 1) * vrstride + (uint32_t)(c * 16);
+      });
+    } else {
+      stage<G::VBYTES / 16, NTK, PP>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane,
+                                 [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
+    }
     if (G::XVBYTES > 0)
       stage<G::XVBYTES / 16, NTK, PP>(vb + G::VBYTES, auxbase + (int64_t)t * G::XBYTES + G::XKBYTES, wave, lane,
                                   [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
@@ -1044,9 +1093,16 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
               for (int dd = 0; dd < 2; ++dd) {
-                const uint4 v = lds_ld<uint4>(vop_base + kb * (2 * D * 16) + (d2 + dd) * 512);
-                C[dd] = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, P[kb],
-                                                              C[dd], 0, 0, 0);
+                i32x4 va;
+                if (G::VROWS && !VDIR) {
+                  const v2i lo = lds_tr8(vb + vtr_off[0] + kb * 256 + (d2 + dd) * 4096);
+                  const v2i hi = lds_tr8(vb + vtr_off[1] + kb * 256 + (d2 + dd) * 4096);
+                  va = i32x4{lo.x, lo.y, hi.x, hi.y};
+                } else {
+                  const uint4 v = lds_ld<uint4>(vop_base + kb * (2 * D * 16) + (d2 + dd) * 512);
+                  va = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                }
+                C[dd] = __builtin_amdgcn_mfma_i32_32x32x32_i8(va, P[kb], C[dd], 0, 0, 0);
               }
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd)
@@ -1368,7 +1424,7 @@ hipError_t launch_d(const AttnArgs& a, const WsLayout& l, hipStream_t st) {
   constexpr bool VDIR_OK = QK == QK_I8H && PV == PV_I8H && D == 128;
   const bool vdir = VDIR_OK && sp.nsplit > 1;
   hipError_t e = hipSuccess;
-  if (!vdir) {
+  if (!vdir && !G::NOPREP) {
     k_prep<QK, PV, D><<<dim3((unsigned)nt, (unsigned)(a.B * a.H)), 256, 0, st>>>(pa);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

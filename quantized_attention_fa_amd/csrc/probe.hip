@@ -190,6 +190,28 @@ extern "C" int faq_probe_global_load_lds(const uint8_t* src, const int* perm, ui
 }
 
 namespace {
+// ds_read_b64_tr_b8: 1 KiB of src in LDS; lane l reads through the
+// transposing instruction at byte offset offs[l] (a multiple of 8, at most
+// 1016) and writes its 8 bytes to out[8 l ..].
+__global__ void k_probe_lds_tr8(const uint8_t* src, const int* offs, uint8_t* out) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[1024];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < 256; i += 64) reinterpret_cast<uint32_t*>(buf)[i] = reinterpret_cast<const uint32_t*>(src)[i];
+  __syncthreads();
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(buf + offs[lane]));
+  reinterpret_cast<uint32_t*>(out)[2 * lane] = (uint32_t)v.x;
+  reinterpret_cast<uint32_t*>(out)[2 * lane + 1] = (uint32_t)v.y;
+}
+}  // namespace
+
+// src: 1024 bytes; offs: 64 ints, multiples of 8 in [0, 1016]; out: 512 bytes.
+extern "C" int faq_probe_lds_tr8(const uint8_t* src, const int* offs, uint8_t* out) {
+  k_probe_lds_tr8<<<1, 64>>>(src, offs, out);
+  return (int)hipDeviceSynchronize();
+}
+
+namespace {
 // v_cvt_pk_u8_f32 on n floats, one byte each (byte 0 of a zero word).
 __global__ void k_probe_cvt_u8(const float* x, int n, uint8_t* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;

@@ -9,7 +9,9 @@ checked against a CPU reference built from the oracle's format tables:
   FP8 attention runs its products on the bf16 MFMA), the bf16 MFMA does not;
 * hardware conversions: f32 -> E4M3 (OCP, nearest even), f32 -> E2M1 with a
   power-of-two scale (x / scale, saturating), E4M3 -> bf16 and
-  E2M1 * scale -> bf16 (both exact).
+  E2M1 * scale -> bf16 (both exact);
+* the lane mapping of the LDS copy (global_load_lds) and of the
+  transposing LDS read of bytes (ds_read_b64_tr_b8).
 """
 
 import ctypes
@@ -215,3 +217,22 @@ def test_global_load_lds_layout(lib):
     assert not o[:1024].any()
     want = src.reshape(64, 16)[perm].reshape(-1)
     assert np.array_equal(o[1024:], want)
+
+
+def test_lds_transposing_read_layout(lib):
+    """ds_read_b64_tr_b8: in each 16-lane group, lane l receives as byte k
+    byte l % 8 of the 8 bytes source lane 2 k + (l / 8) % 2 points at (the
+    INT8 value product reads V rows this way)."""
+    g = np.random.default_rng(5)
+    src = g.integers(0, 256, 1024).astype(np.uint8)
+    offs = (8 * g.integers(0, 128, 64)).astype(np.int32)
+    s_d, o_d = _d(src), _d(offs)
+    out = torch.zeros(512, dtype=torch.uint8, device=DEV)
+    assert lib.faq_probe_lds_tr8(_p(s_d), _p(o_d), _p(out)) == 0
+    o = out.cpu().numpy().reshape(64, 8)
+    want = np.zeros((64, 8), dtype=np.uint8)
+    for lane in range(64):
+        for k in range(8):
+            srcl = 16 * (lane >> 4) + 2 * k + ((lane >> 3) & 1)
+            want[lane, k] = src[offs[srcl] + (lane & 7)]
+    assert np.array_equal(o, want)
