@@ -181,7 +181,9 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
                MXFP4 on the scaled f8f6f4 MFMA); any other mix widens Q and
                K exactly to bf16 (MX rows relative to their largest block
                exponent) and scores on bf16 MFMA.  B, H, D equal; k and v
-               share S.
+               share S.  The rows of one head of k and of v must span
+               less than 4 GiB (in BSND they lie H rows apart), else
+               FAQ_ERR_UNSUPPORTED.
    sm_scale    softmax scale; 0 means 1/sqrt(D).
    causal      1: key j is masked for query i when j > i (needs Sq == Skv).
    out         device [B,H,Sq,D] in q's layout, out_dtype F32 or BF16

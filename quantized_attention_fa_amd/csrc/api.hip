@@ -267,6 +267,16 @@ static faq_status attn_check(const faq_qtensor* q, const faq_qtensor* k, const f
   if (!attn_pair_supported(*qk, *pv)) *qk = QK_GEN;
   *qfmt = branch_fmt(q->cfg);
   *kfmt = branch_fmt(k->cfg);
+  // the kernels address the K / V rows of one head with 32-bit byte
+  // offsets: a head's rows must span less than 4 GiB (BSND rows are H rows
+  // apart)
+  for (const faq_qtensor* t : {k, v}) {
+    const int64_t rb = t->cfg.dtype == FAQ_FLOAT ? 2 * t->shape.D
+                       : (t->cfg.dtype == FAQ_MXFP4 ? t->shape.D / 2 : t->shape.D);
+    const int64_t ss = t->shape.layout == FAQ_LAYOUT_BSND ? t->shape.H : 1;
+    if (t->shape.S > 0 && ((t->shape.S - 1) * ss + 1) * rb >= ((int64_t)1 << 32))
+      return fail(FAQ_ERR_UNSUPPORTED, fn, "the K / V rows of one head span 4 GiB or more");
+  }
   if (q->shape.B != k->shape.B || q->shape.B != v->shape.B || q->shape.H != k->shape.H ||
       q->shape.H != v->shape.H || q->shape.D != k->shape.D || q->shape.D != v->shape.D ||
       k->shape.S != v->shape.S)

@@ -160,6 +160,14 @@ def test_attention_validation():
                   (i8h, i8t, mx), (tok, b1, fl)]:
         assert ws(*mixed) >= 2 * 2 * 256 * 128, mixed
     assert _attn(_qt(mx, s), _qt(i8h, s), _qt(tok, s), ws_bytes=ws(mx, i8h, tok) - 1) == _abi.FAQ_ERR_WORKSPACE
+    # a head's K / V rows must span less than 4 GiB (32-bit row offsets):
+    # BSND bf16 with S = 2^20, H = 20, D = 128 spans about 2^20 * 20 * 256
+    # bytes (5 GiB)
+    big = _abi.faq_shape(1, 20, 1 << 20, 128, _abi.FAQ_LAYOUT_BSND)
+    assert _attn(_qt(fl, big), _qt(fl, big), _qt(fl, big)) == _abi.FAQ_ERR_UNSUPPORTED
+    ok_big = _abi.faq_shape(1, 20, 1 << 20, 128, _abi.FAQ_LAYOUT_BNSD)  # 256 MiB per head
+    assert lib.fa_quant_attention_workspace_bytes(ctypes.byref(_qt(fl, ok_big)), ctypes.byref(_qt(fl, ok_big)),
+                                                  ctypes.byref(_qt(fl, ok_big))) > 0
     # unquantized branches need no scales; quantized ones do
     nos = _abi.faq_qtensor(tok, s, 0x2000, None)
     assert _attn(nos, k, v) == _abi.FAQ_ERR_INVALID_ARG
