@@ -86,7 +86,7 @@ __global__ void k_scales_from_amax(const float* amax, int64_t H, float qmax, flo
 template <bool FAST, bool FP8, typename T>
 FAQ_DEV void head_slice(const T* __restrict__ src, uint8_t* __restrict__ dst, int64_t row0, const RowMap& rm,
                         int dsh, int64_t per_bh, float s) {
-  constexpr int U = 2;
+  constexpr int U = 1;
   const float r = 1.0f / s;
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads * 16 * U; c0 < per_bh;
        c0 += (int64_t)gridDim.x * kThreads * 16 * U) {
@@ -147,7 +147,7 @@ template <typename T, int D, bool I8>
 __global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ x, int64_t rows, RowMap rm,
                                                           uint32_t H, uint32_t S, uint8_t* __restrict__ codes,
                                                           float* __restrict__ scales) {
-  constexpr int EPT = 16, TPR = D / EPT, RPB = kThreads / TPR, U = 2;
+  constexpr int EPT = 16, TPR = D / EPT, RPB = kThreads / TPR, U = 1;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
   for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
     float v[U][EPT];
@@ -193,7 +193,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ x, int64_t rows, RowMap rm,
                                                           uint32_t H, uint32_t S, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ e8m0) {
-  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 4, NB = D / 32;
+  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 2, NB = D / 32;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
   const int lane = threadIdx.x & 63;
   for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
@@ -259,7 +259,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ x, int64_t rows, RowMap rm,
                                                           uint32_t H, uint32_t S, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ e8m0) {
-  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 4, NB = D / 32;
+  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 2, NB = D / 32;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
   const int lane = threadIdx.x & 63;
   for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
@@ -504,7 +504,7 @@ static hipError_t head_q(const void* x, int x_dtype, const faq_shape& s, const f
   const int64_t per_bh = s.S * s.D;
   const RowMap rm = row_map(s);
   const int dsh = s.D == 128 ? 7 : 6;
-  dim3 grid(grid_chunks(per_bh, kThreads * 16 * 2, 65535), (unsigned)(s.B * s.H));
+  dim3 grid(grid_chunks(per_bh, kThreads * 16 * 1, 65535), (unsigned)(s.B * s.H));
   if (x_dtype == FAQ_T_BF16)
     k_quant_head<uint16_t, FP8><<<grid, kThreads, 0, st>>>((const uint16_t*)x, scale, rm, dsh, per_bh, (int)s.H,
                                                            codes);
@@ -529,7 +529,7 @@ static hipError_t token_d(const void* x, int x_dtype, const faq_shape& s, uint8_
   constexpr int RPB = kThreads / (D / 16);
   const int64_t rows = s.B * s.H * s.S;
   const RowMap rm = row_map(s);
-  const unsigned grid = grid_chunks(rows, RPB * 2, 1u << 20);
+  const unsigned grid = grid_chunks(rows, RPB * 1, 1u << 20);
   if (x_dtype == FAQ_T_BF16)
     k_quant_token<uint16_t, D, I8><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, rm, (uint32_t)s.H,
                                                               (uint32_t)s.S, codes, scales);
@@ -559,7 +559,7 @@ static hipError_t mx_d(const void* x, int x_dtype, const faq_shape& s, uint8_t* 
   const int64_t rows = s.B * s.H * s.S;
   const RowMap rm = row_map(s);
   const uint32_t H = (uint32_t)s.H, S = (uint32_t)s.S;
-  const unsigned grid = grid_chunks(rows, RPB * 4, 1u << 20);
+  const unsigned grid = grid_chunks(rows, RPB * 2, 1u << 20);
   if (FP4) {
     if (x_dtype == FAQ_T_BF16)
       k_quant_mxfp4<uint16_t, D><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rows, rm, H, S, codes, e8m0);
