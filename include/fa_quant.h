@@ -162,10 +162,12 @@ faq_status fa_quantize(const void* x, int32_t x_dtype, const faq_shape* shape,
                        faq_qtensor* out, void* debug_rotated, void* stream);
 
 /* Device workspace (bytes) fa_quant_attention needs for these operands
-   (V re-laid out tile by tile with its per-tile scale data, K widened to
-   bf16 where its format has no MFMA path of its own; with few
-   queries per head - decode - also the partial results of the key splits);
-   enough for causal and non-causal calls; 0 on invalid operands. */
+   (V re-laid out tile by tile with its per-tile scale data - not for INT8
+   per-head V, which the kernel reads as rows - and K widened to bf16 where
+   its format has no MFMA path of its own; with few queries per head -
+   decode - also the partial results of the key splits); enough for causal
+   and non-causal calls; at least 256 for valid operands, 0 on invalid
+   operands. */
 size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtensor* k,
                                           const faq_qtensor* v);
 

@@ -42,9 +42,14 @@
 // the tile sum L uses unquantized p, and tiles combine with the usual
 // running-max rescale, O = sum_t e^{m_t-M} C_t / sum_t e^{m_t-M} L_t.
 //
-// Kernel shape: a workgroup is 4 waves and 128 queries of one (b,h); two
-// workgroups share a CU, so the two waves on a SIMD come from independent
-// workgroups and one's softmax (VALU) overlaps the other's products (MFMA).
+// Kernel shape: each tile runs in a score phase (S^T = K Q^T, mostly MFMA)
+// and a value phase (probabilities, P quantization, O^T += V^T P^T, mostly
+// vector work).  Four-wave kernel (INT8 and MXFP4 scores, and every call
+// with key splits): a workgroup is 4 waves and 128 queries of one (b,h);
+// two workgroups share a CU.  Ping-pong kernel (bf16 score products without
+// key splits): 8 waves in two 128-query groups, the second one phase behind
+// the first, so the two waves of a SIMD are always in different phases; K
+// and V^T tiles are double-buffered.
 // Each wave owns 32 queries: one 32x32 MFMA column block for both products.
 // Scores are computed transposed (S^T = K Q^T): a lane holds one query and,
 // with the K rows fed to the MFMA permuted (qk_row), 64 consecutive keys of
@@ -52,14 +57,17 @@
 // cross-lane step, and the lane's probabilities are already the B operand of
 // O^T = V^T P^T.  V^T comes from a per-call workspace with its key columns in
 // the order the lanes hold their probabilities (FP8 / MXFP8 K widened there
-// to bf16 too).
+// to bf16 too).  INT8 per-head V needs no workspace: its tile is copied as
+// rows and read through the transposing LDS read (prefill), or loaded into
+// registers and transposed by the kernel (key splits).
 //
 // LDS tiles are chunk-major: 16-byte column c of every row, then column c+1.
 // The 16 lanes that share an LDS cycle read 16 distinct rows of one column,
 // which the row permutation kslot spreads over all 64 banks, and every
-// operand address is a per-lane base plus a constant.  The K tile of t+1 is
-// copied (global_load_lds) while P V of tile t runs, and V^T of tile t while
-// the scores and probabilities of t are computed: two barriers per tile.
+// operand address is a per-lane base plus a constant.  In the four-wave
+// kernel the K tile of t+1 is copied (global_load_lds) while P V of tile t
+// runs, and V^T of tile t while the scores of t are computed: two barriers
+// per tile.
 //
 // Workgroups are numbered so that all query tiles of one (b,h) land on the
 // same XCD (workgroups are dealt to the 8 XCDs round robin), which keeps a
@@ -267,6 +275,7 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int6
   l.part_off = l.aux_off + up(tiles * (xk + xv));
   const KvSplit sp = kv_split(B, H, Sq, Skv, causal);
   l.total = l.part_off + up(sp.nsplit > 1 ? (size_t)sp.nsplit * B * H * Sq * (D + 2) * 4 : 0);
+  if (l.total < 256) l.total = 256;  // valid operands never report 0 (that means invalid)
   return l;
 }
 
@@ -278,7 +287,9 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int6
 //              block exponents.
 //   V (by PV): the V^T image: INT8 codes, E4M3 codes widened to bf16, MX
 //              values exact in bf16, or the unquantized bf16 values; the
-//              per-key multipliers qmax w_j and sigma_t.
+//              per-key multipliers qmax w_j and sigma_t.  None for INT8
+//              per-head V (read as rows by the attention kernel); a pair of
+//              INT8 per-head Q/K with such V needs no re-layout at all.
 // Float scales of K and V are read at b * sb + h * sh + key / blk
 // (per-token: blk 1; token blocks: blk tokens; per-head: sb 0, sh 1, one
 // block).
