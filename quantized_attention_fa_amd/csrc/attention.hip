@@ -527,12 +527,15 @@ using lptr = __attribute__((address_space(3))) void*;
 // compiler does not track the copy: its completion is then waited for only
 // where the kernel says so (vmcnt), never before reads of other LDS
 // buffers.  The instruction has no result registers; M0 holds the wave's
-// LDS base.
+// LDS base.  M0 is a reserved register the compiler does not treat as
+// clobberable, so kernels that copy this way issue no other M0-using
+// instruction: all their LDS copies go through this form (their assembly
+// has no M0 access outside these blocks).
 template <bool ASM>
 FAQ_DEV void copy16(const uint8_t* g, uint8_t* lds) {
   if (ASM) {
     const uint32_t m = (uint32_t)(uintptr_t)(lptr)lds;
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory");
   } else {
     __builtin_amdgcn_global_load_lds((gptr)g, (lptr)lds, 16, 0, 0);
   }

@@ -27,6 +27,16 @@ FAQ_DEV int64_t mem_row(const RowMap& m, int64_t r, uint32_t H, uint32_t S) {
   return m.row(b, h, s);
 }
 
+// Logical (b, h, s) row of memory row r, the inverse of mem_row (BSND
+// memory rows run (b, s, h)).  The per-row quantizers walk memory rows in
+// order, so neighbouring threads read neighbouring rows in either layout,
+// and place each row's scales at its logical index.
+FAQ_DEV int64_t logical_row(const RowMap& m, int64_t r, uint32_t H, uint32_t S) {
+  if (m.ident) return r;
+  const uint32_t r32 = (uint32_t)r, bs = r32 / H, h = r32 - bs * H, b = bs / S, s = bs - b * S;
+  return ((int64_t)b * H + h) * S + s;
+}
+
 // Element offset of element i (0 <= i < S D) of the (b, h) slice: rows of D
 // = 2^dsh elements, consecutive tokens m.ss rows apart.
 FAQ_DEV int64_t slice_off(int64_t row0, int64_t i, const RowMap& m, int dsh) {
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ 
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       if (row < rows) {
-        const int64_t mr = mem_row(rm, row, H, S);
+        const int64_t mr = row;  // memory row
         float a[8], b[8];
         load8(x + mr * D + sub * EPT, a);
         load8(x + mr * D + sub * EPT + 8, b);
@@ -178,8 +188,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ 
       if (I8) int8_code_words<EPT>(v[u], s, w);
       else e4m3_code_words<EPT>(v[u], s, w);
       if (row < rows) {
-        *reinterpret_cast<uint4*>(codes + mem_row(rm, row, H, S) * D + sub * EPT) = make_uint4(w[0], w[1], w[2], w[3]);
-        if (sub == 0) scales[row] = s;
+        *reinterpret_cast<uint4*>(codes + row * D + sub * EPT) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (sub == 0) scales[logical_row(rm, row, H, S)] = s;
       }
     }
   }
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       if (row < rows) {
-        load8(x + mem_row(rm, row, H, S) * D + sub * 8, v[u]);
+        load8(x + row * D + sub * 8, v[u]);  // memory row
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
@@ -240,10 +250,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
 #pragma unroll
       for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
       if (row < rows) {
-        *reinterpret_cast<uint32_t*>(codes + mem_row(rm, row, H, S) * (D / 2) + sub * 4) = packed;
+        *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + sub * 4) = packed;
         if (sub == 0) {
-          if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + row * NB) = word;
-          else *reinterpret_cast<uint16_t*>(e8m0 + row * NB) = (uint16_t)word;
+          const int64_t lr = logical_row(rm, row, H, S);
+          if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + lr * NB) = word;
+          else *reinterpret_cast<uint16_t*>(e8m0 + lr * NB) = (uint16_t)word;
         }
       }
     }
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ 
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       if (row < rows) {
-        load8(x + mem_row(rm, row, H, S) * D + sub * 8, v[u]);
+        load8(x + row * D + sub * 8, v[u]);  // memory row
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
@@ -298,10 +309,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ 
 #pragma unroll
       for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
       if (row < rows) {
-        *reinterpret_cast<uint2*>(codes + mem_row(rm, row, H, S) * D + sub * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
+        *reinterpret_cast<uint2*>(codes + row * D + sub * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
         if (sub == 0) {
-          if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + row * NB) = word;
-          else *reinterpret_cast<uint16_t*>(e8m0 + row * NB) = (uint16_t)word;
+          const int64_t lr = logical_row(rm, row, H, S);
+          if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + lr * NB) = word;
+          else *reinterpret_cast<uint16_t*>(e8m0 + lr * NB) = (uint16_t)word;
         }
       }
     }
