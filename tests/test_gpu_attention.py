@@ -159,3 +159,23 @@ def test_full_size_general_score_mode():
     rows = sample_rows(9, w.shape[2], 6, edge=4)
     got = o[:, :, torch.from_numpy(rows).to(o.device)].cpu().numpy()
     check_attention(got, oracle_attention(run, rows=rows), "cfg9 fp8/int8/float full size")
+
+
+# The ping-pong kernel (bf16 score products, no key split) gives each
+# 256-query workgroup two 128-query groups, the second one phase behind:
+# lengths around the group and workgroup boundaries, causal (the second
+# group's diagonal tile is one later than the first's) and not, leave the
+# second group empty, partly filled or full, and the last key tile ragged
+# (non-causal lengths stay under four key tiles, which never split keys).
+PINGPONG = [(6, ("fp8_head",) * 3), (8, ("mxfp8",) * 3), (10, ("float",) * 3), (9, ("fp8_token", "fp8_token", "float")),
+            (3, ("fp8_token", "int8_token", "float"))]
+
+
+@pytest.mark.parametrize("cfg,modes", PINGPONG)
+@pytest.mark.parametrize("S,D,causal", [(129, 128, True), (255, 64, True), (256, 128, True), (257, 128, False),
+                                        (383, 64, False), (511, 64, True), (640, 128, True)])
+def test_ping_pong_group_boundaries(cfg, modes, S, D, causal):
+    w = small_workload(cfg, (1, 2, S, D))
+    run = GpuRun(w, modes=modes)
+    o32 = run.attention(torch.float32, causal=causal).cpu().numpy()
+    check_attention(o32, oracle_attention(run, causal=causal), f"cfg{cfg} {modes} S={S} D={D} causal={causal}")
