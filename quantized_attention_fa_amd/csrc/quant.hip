@@ -20,15 +20,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Memory row of logical row r = (b H + h) S + s (rows below 2^32).
-FAQ_DEV int64_t mem_row(const RowMap& m, int64_t r, uint32_t H, uint32_t S) {
-  if (m.ident) return r;
-  const uint32_t r32 = (uint32_t)r, bh = r32 / S, s = r32 - bh * S, b = bh / H, h = bh - b * H;
-  return m.row(b, h, s);
-}
-
-// Logical (b, h, s) row of memory row r, the inverse of mem_row (BSND
-// memory rows run (b, s, h)).  The per-row quantizers walk memory rows in
+// Logical row (b H + h) S + s of memory row r (BSND memory rows run
+// (b, s, h); rows below 2^32).  The per-row quantizers walk memory rows in
 // order, so neighbouring threads read neighbouring rows in either layout,
 // and place each row's scales at its logical index.
 FAQ_DEV int64_t logical_row(const RowMap& m, int64_t r, uint32_t H, uint32_t S) {
