@@ -32,14 +32,15 @@ STATIC_DTYPE = {"int8_head": "int8", "fp8_head": "fp8_e4m3"}
 
 class GpuRun:
     """Quantized Q/K/V of one workload produced by the HIP path.  `modes`
-    gives each branch's mode (default: the workload's mode for all three);
-    "float" leaves a branch unquantized (bf16)."""
+    gives each branch's mode (default: the workload's per-branch modes, else
+    its mode for all three); "float" leaves a branch unquantized (bf16)."""
 
     def __init__(self, w, keep_rotated=False, modes=None):
         self.w = w
         mode = w.spec["mode"]
         self.mode = mode
-        self.modes = list(modes) if modes is not None else [mode] * 3
+        # explicit modes, else the workload's own per-branch modes, else its mode for all three
+        self.modes = list(modes) if modes is not None else list(w.spec.get("modes", [mode] * 3))
         self.x = [t.to(DEV) for t in (w.q, w.k, w.v)]
         self.static = [None, None, None]
         self.amax = [None, None, None]

@@ -63,7 +63,7 @@ def test_attention_custom_scale_and_determinism():
 
 
 @pytest.mark.parametrize("cfg,rows_per_bh", [(1, None), (2, 24), (3, 8), (4, 24), (5, 8), (6, 24), (7, 8),
-                                             (8, 24)])
+                                             (8, 24), (9, 6), (10, 24)])
 def test_full_size_attention(cfg, rows_per_bh):
     w = make_inputs(cfg)
     run = GpuRun(w)
