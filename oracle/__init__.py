@@ -21,8 +21,9 @@ where the arithmetic is floating point:
 
 Parity pins: see the header of each module.  The probability-quantization
 rule inside ``attention`` is a reading (the pages are silent on how the
-softmax output enters the low-bit PV product); it is pinned only by
-self-consistency properties and is marked "parity unpinned" there.
+softmax output enters the low-bit PV product, so they print no value for
+it); the oracle's arithmetic for it is pinned by hand-worked two-key closed
+forms for every rule, invariants and special cases (see ``attention``).
 """
 
 from . import formats, quantize, attention  # noqa: F401

@@ -9,10 +9,12 @@ dequantized back to the original precision (MindIE SD "量化" page, FA量化 /
 技术特点, FP8 Attention).  The flash-attention structure (tiles, online
 softmax) is the one of the FlashAttention reference the "FA 量化" page cites.
 
-What the pages leave open, and the reading taken here (parity unpinned: the
-rule below is pinned only by self-consistency properties - tile-order
-invariance, the single-tile closed form, equal-score and dominant-key cases -
-not by any value on the pages):
+What the pages leave open, and the reading taken here.  The pages print no
+value for this rule; its arithmetic is pinned by closed forms worked by hand
+(two keys in one tile, for every rule, with and without per-key V scales),
+invariants (tile-order invariance, the tile-local maximum, sigma per tile)
+and special cases (exact p equals softmax attention; equal scores give the
+mean of V; a dominant key gives its V):
 
 * Keys are cut into P-tiles of 128 keys aligned to absolute key index.  For
   each query row i and tile t with at least one unmasked key:
