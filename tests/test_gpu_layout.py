@@ -86,3 +86,26 @@ def test_attention_bsnd_equals_bnsd(cfg, shape, causal, modes, layouts):
     assert torch.equal(o16, ref16)
     if layouts == ("bsnd", "bsnd", "bsnd") and cfg == 3 and modes is None:
         check_attention(o32.cpu().numpy(), oracle_attention(run, causal=causal), "bsnd vs oracle")
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_bsnd_equals_bnsd(cfg):
+    """At the bench's full sizes (INT8 per-head prefill: four-wave kernel;
+    FP8 per-token video: ping-pong kernel): quantizing the BSND inputs gives
+    the BSND codes and the same scales, and attention on BSND operands gives
+    the BNSD result bit for bit, in BSND."""
+    from synth import make_inputs
+    w = make_inputs(cfg)
+    run = GpuRun(w)
+    for br, x in enumerate(run.x):
+        qt = faq.fa_quantize(_bsnd(x), run.qt[br].cfg, static_scale=run.static[br], layout="bsnd")
+        torch.cuda.synchronize()
+        assert torch.equal(_bsnd(qt.codes), run.qt[br].codes), br
+        assert torch.equal(qt.scales, run.qt[br].scales), br
+        del qt
+    ref32 = run.attention(torch.float32)
+    q, k, v = (_to_layout(t, "bsnd") for t in run.qt)
+    o32 = faq.fa_quant_attention(q, k, v, causal=w.spec["causal"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o32.shape[1] == w.shape[2]
+    assert torch.equal(_bsnd(o32), ref32)
