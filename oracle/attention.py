@@ -24,10 +24,11 @@ mean of V; a dominant key gives its V):
   per-key V scale and w_j = s_v,j / sigma_t (the V scale folded into P; w = 1
   when V has one scale per tile - per-head and token-block scopes - or when
   no V scale is given):
-    - 'int8':  Pq = rne(127 p w_j) / (127 w_j), the code decided with the
-               multiplier fl32(127 fl32(w_j));
-    - 'fp8':   Pq = E4M3(448 p w_j) / (448 w_j), the code decided with the
-               multiplier fl32(448 fl32(w_j));
+    - 'int8':  Pq = rne(127 p w_j) / (127 w_j);
+    - 'fp8':   Pq = E4M3(448 p w_j) / (448 w_j);
+    the code is decided on the exact product (the multiplier qmax w_j is
+    formed as (qmax s_v,j) / sigma_t with one rounding of an fp64 quotient,
+    which lands on a rounding boundary exactly when the exact value does);
     - 'mxfp4': the MXFP4 quantizer applied along keys, 32-key groups aligned
                to absolute key index, masked keys counting as p = 0;
     - 'mxfp8': the same with the MXFP8 quantizer (E4M3 elements, emax 8);
@@ -53,12 +54,11 @@ MX_GROUP = 32
 TIE_REL = 2.0 ** -12
 
 
-def _quantize_p(p, rule, w=None, w_dec=None):
+def _quantize_p(p, rule, mult=None):
     """Dequantized quantized probabilities for one row-chunk, per tile.
 
-    p: [nr, nt, 128] fp64 (masked -> 0); w: [nt, 128] exact s_v,j / sigma_t
-    and w_dec: [nt, 128] the fp32 multiplier fl32(qmax fl32(s_v,j / sigma_t))
-    ('int8' / 'fp8'; None means w = 1).
+    p: [nr, nt, 128] fp64 (masked -> 0); mult: [nt, 128] the multiplier
+    qmax w_j = qmax s_v,j / sigma_t ('int8' / 'fp8'; None means w = 1).
     Returns (Pq, step, near) where `near` flags elements whose pre-rounding
     value lies within 2^-12 (relative) of a rounding boundary and `step` is
     the size of the code step such an element may flip by (in p units)."""
@@ -66,19 +66,17 @@ def _quantize_p(p, rule, w=None, w_dec=None):
         z = np.zeros_like(p)
         return p.copy(), z, z.astype(bool)
     if rule in _PQMAX:
-        # The code is decided on u = qmax p w_j.  The pages fix no precision
-        # for this decision, so it is taken in fp32 as the kernel takes it:
-        # the multiplier is fl32(qmax * fl32(s_v,j / sigma_t)) (for the
-        # tile's own maximum, p = 1, u is exactly that multiplier on both
-        # sides; bf16-derived scale ratios land on E4M3 ties there).  The
-        # dequantized value divides by the exact qmax w_j.
+        # The code is decided on u = qmax p w_j and the dequantized value
+        # divides by qmax w_j.  For the tile's own maximum (p = 1) u is the
+        # multiplier itself: qmax s_v,j / sigma_t, exact up to one fp64
+        # rounding, which keeps every exact tie on its tie and every
+        # non-tie (at least ~2^-29 away from a boundary for fp32 scales) on
+        # its own side.
         qmax = _PQMAX[rule]
-        if w is None:
-            mult = np.full(p.shape[1:], qmax)[None]
-            scale = mult
-        else:
-            mult = w_dec[None, :, :]
-            scale = qmax * w[None, :, :]
+        if mult is None:
+            mult = np.full(p.shape[1:], qmax)
+        mult = mult[None, :, :]
+        scale = mult
         u = p * mult
         if rule == "int8":
             pq = np.rint(u) / scale
@@ -163,18 +161,14 @@ def attention(qhat, khat, vhat, p_rule, *, v_scale=None, causal=False,
             k = khat[b, h]
             v = np.concatenate([vhat[b, h], np.zeros((pad, D))], axis=0)
             vt = v.reshape(nt, P_TILE, D)
-            w = w_dec = None
+            mult = None
             if p_rule in _PQMAX and v_scale is not None:
+                # sigma_t = the tile's largest V scale; qmax w_j = qmax s_v,j / sigma_t
                 qmax = _PQMAX[p_rule]
                 sv = np.asarray(v_scale[b, h], dtype=np.float64)
                 svp = np.concatenate([sv, np.zeros(pad)]).reshape(nt, P_TILE)
                 sigma = svp.max(axis=1, keepdims=True)
-                w = np.where(svp > 0, svp / np.where(sigma > 0, sigma, 1.0), 1.0)
-                sv32 = svp.astype(np.float32)
-                s32 = sv32.max(axis=1, keepdims=True)
-                ratio32 = (sv32 / np.where(s32 > 0, s32, np.float32(1.0))).astype(np.float32)
-                w_dec = np.where(svp > 0, (np.float32(qmax) * ratio32).astype(np.float32), qmax)
-                w_dec = w_dec.astype(np.float64)
+                mult = np.where(svp > 0, (qmax * svp) / np.where(sigma > 0, sigma, 1.0), qmax)
             for c0 in range(0, rows.size, chunk):
                 r = rows[c0:c0 + chunk]
                 s = (qhat[b, h, r] @ k.T) * sm_scale  # [nr, Skv]
@@ -191,7 +185,7 @@ def attention(qhat, khat, vhat, p_rule, *, v_scale=None, causal=False,
                 m_safe = np.where(live, m_t, 0.0)
                 p = np.where(vmask, np.exp(sp - m_safe[..., None]), 0.0)
                 L_t = p.sum(axis=2)
-                pq, step, near = _quantize_p(p, p_rule, w=w, w_dec=w_dec)
+                pq, step, near = _quantize_p(p, p_rule, mult=mult)
                 C_t = np.matmul(pq.transpose(1, 0, 2), vt).transpose(1, 0, 2)  # [nr, nt, D]
                 M = np.where(live, m_t, -np.inf).max(axis=1)
                 f = np.where(live, np.exp(m_safe - M[:, None]), 0.0)  # e^{m_t - M}

@@ -204,21 +204,56 @@ def test_allowance_flags_ties():
     assert T[0, 0, 0, 0] == pytest.approx((1 / 127) / (1 + t), rel=1e-9)
 
 
-def test_fp8_code_decided_in_fp32():
-    """The probability code of the tile's maximum (p = 1) is decided on the
-    fp32 multiplier fl32(448 fl32(s_v,j / sigma_t)).  With V amaxes 2.125 and
-    14 (bf16 values) the exact 448 w_j is 68.000001 (above the 64/72 tie,
-    code 72) while the fp32 multiplier is exactly 68.0 (tie -> even, 64)."""
+def _top_key_code(rule, sv0, sv1):
+    """Two keys: key 0 holds the tile maximum (p = 1), key 1's p underflows,
+    so O[1] = code(qmax w_0) / (qmax w_0) * vhat_0 with vhat_0 = s_v0 * 1.
+    Returns the code the oracle took for the maximum: O[1] * qmax w_0 / vhat_0."""
     D = 64
-    sv0 = np.float32(2.125) / np.float32(448)
-    sv1 = np.float32(14.0) / np.float32(448)
     q = np.zeros((1, 1, 1, D)); q[..., 0] = math.sqrt(D)
-    k = np.zeros((1, 1, 2, D)); k[0, 0, 1, 0] = -200.0  # p1 underflows
-    v = np.zeros((1, 1, 2, D)); v[0, 0, 0, 1] = float(sv0) * 448; v[0, 0, 1, 2] = float(sv1)
+    k = np.zeros((1, 1, 2, D)); k[0, 0, 1, 0] = -200.0  # p1 = e^-200 rounds to code 0
+    v = np.zeros((1, 1, 2, D)); v[0, 0, 0, 1] = sv0; v[0, 0, 1, 2] = sv1
     vs = np.array([[[sv0, sv1]]], dtype=np.float64)
-    o = A.attention(q, k, v, "fp8", v_scale=vs)[0, 0, 0]
-    w = float(sv0) / float(sv1)
-    assert o[1] == pytest.approx(64.0 / (448 * w) * float(sv0) * 448, rel=1e-12)
+    o = A.attention(q, k, v, rule, v_scale=vs)[0, 0, 0]
+    qmax = 448.0 if rule == "fp8" else 127.0
+    return o[1] * (qmax * sv0 / max(sv0, sv1)) / sv0
+
+
+def test_fp8_code_of_the_maximum_is_decided_exactly():
+    """The probability code of the tile's maximum (p = 1) is decided on the
+    exact 448 w_j (the reading of the P rule: V's scale folded into P, then
+    E4M3 round-to-nearest-even).  Hand-worked: V amaxes 2.125 and 14 give
+    fp32 scales s0 = fl32(2.125/448) and s1 = 14/448 = 2^-5 exactly, so
+    448 w_0 = 448 * 32 * fl32(2.125/448) = 68 (1 + e) with e the (positive)
+    rounding error of fl32(2.125/448): just above the 64 / 72 midpoint, code
+    72.  An fp32 multiplier fl32(448 fl32(w_0)) rounds to 68.0 exactly and
+    would give the even code 64."""
+    s0 = float(np.float32(2.125) / np.float32(448))
+    s1 = float(np.float32(14.0) / np.float32(448))
+    assert s1 == 2.0 ** -5 and 448 * 32 * s0 > 68.0  # the hand-worked premises
+    assert float(np.float32(448) * (np.float32(s0) / np.float32(s1))) == 68.0
+    assert _top_key_code("fp8", s0, s1) == pytest.approx(72.0, rel=1e-12)
+
+
+def test_fp8_code_of_the_maximum_at_an_exact_tie():
+    """448 w_j exactly on the 64 / 72 midpoint: s0 = 17/128, sigma = 7/8 give
+    448 * (17/128) / (7/8) = 68 exactly, so round-half-even takes 64."""
+    assert _top_key_code("fp8", 17.0 / 128.0, 7.0 / 8.0) == pytest.approx(64.0, rel=1e-12)
+    # and just above the tie (s0 one fp32 ulp larger): 72
+    s0_up = float(np.nextafter(np.float32(17.0 / 128.0), np.float32(1.0)))
+    assert _top_key_code("fp8", s0_up, 7.0 / 8.0) == pytest.approx(72.0, rel=1e-12)
+
+
+def test_int8_code_of_the_maximum_is_decided_exactly():
+    """INT8 per-token V: 127 w_j = 127 * (93/256) / (127/128) = 46.5 exactly
+    rounds half to even, to 46; one fp32 ulp more in s_v,j gives 47, one
+    less 46."""
+    s0, sig = 93.0 / 256.0, 127.0 / 128.0
+    assert 127 * s0 / sig == 46.5
+    assert _top_key_code("int8", s0, sig) == pytest.approx(46.0, rel=1e-12)
+    up = float(np.nextafter(np.float32(s0), np.float32(1.0)))
+    dn = float(np.nextafter(np.float32(s0), np.float32(0.0)))
+    assert _top_key_code("int8", up, sig) == pytest.approx(47.0, rel=1e-12)
+    assert _top_key_code("int8", dn, sig) == pytest.approx(46.0, rel=1e-12)
 
 
 def test_bf16_rule_is_one_rounding_of_p():
