@@ -179,6 +179,36 @@ FAQ_DEV float halves_sum(float x) {
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
+// The probability multiplier qmax w_j = qmax s_v,j / sigma_t of a key whose
+// V scale varies along the tile (per-token V), as an fp32 value in the same
+// rounding interval of the code grid (E4M3 for qmax 448, integers for 127)
+// as the exact quotient, so that the tile maximum (p = 1 exactly) takes the
+// code of the exact product.  u is the fp64 quotient (one rounding): an
+// exact tie stays on the tie, and every other quotient of fp32 scales lies
+// at least ~2^-29 (relative) from a boundary, far beyond that rounding.
+// Its fp32 rounding can land on or across the nearest boundary b; it is
+// then moved one ulp off b, to u's side.
+FAQ_DEV float p_multiplier(float sv, float sigma, bool e4m3) {
+  const double u = (e4m3 ? 448.0 : 127.0) * (double)sv / (double)sigma;
+  const float mu = (float)u;
+  float b;
+  if (e4m3) {
+    // E4M3 steps: 2^(e-3) in the binade [2^e, 2^(e+1)) for e >= -6, 2^-9
+    // below; mu / step is exact (a power-of-two scaling)
+    int e;
+    (void)__builtin_frexpf(mu, &e);  // mu = f 2^e, f in [0.5, 1)
+    const float step = __builtin_amdgcn_ldexpf(1.0f, max(e - 1, -6) - 3);
+    b = (__builtin_rintf(mu / step - 0.5f) + 0.5f) * step;
+  } else {
+    b = __builtin_rintf(mu - 0.5f) + 0.5f;
+  }
+  const double d = u - (double)b;
+  if (d == 0.0) return b;
+  if (d > 0.0 && mu <= b) return __uint_as_float(__float_as_uint(b) + 1u);
+  if (d < 0.0 && mu >= b) return __uint_as_float(__float_as_uint(b) - 1u);
+  return mu;
+}
+
 // Geometry of the LDS tiles, from the score mode QK and the value mode PV.
 template <int QK, int PV, int D>
 struct Cfg {
@@ -471,10 +501,8 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (C::PVW && kl < BN) {
-      constexpr float qmax = PV == PV_F8W ? 448.0f : 127.0f;
-      reinterpret_cast<float*>(auxt + C::XKBYTES)[kl] = (sv > 0.0f) ? qmax * (sv / m) : 0.0f;
-    }
+    if (C::PVW && kl < BN)
+      reinterpret_cast<float*>(auxt + C::XKBYTES)[kl] = (sv > 0.0f) ? p_multiplier(sv, m, PV == PV_F8W) : 0.0f;
     if (threadIdx.x == 0) reinterpret_cast<float*>(auxt + C::XKBYTES + C::XVW)[0] = m;
   }
 }
