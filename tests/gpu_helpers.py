@@ -2,6 +2,11 @@
 the HIP library (via the C ABI binding) and bring its codes back to the CPU,
 and the oracle-side dequantization / attention on those same codes."""
 
+import json
+import os
+import time
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -111,27 +116,76 @@ def dequant(run: GpuRun, br: int):
     return OQ.dequantize_per_token(c, st, F.e4m3_decode), st
 
 
+def _oracle_threads():
+    """Worker threads for the oracle (numpy releases the GIL in its array
+    operations): the host's cores, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def oracle_attention(run: GpuRun, rows=None, causal=None, sm_scale=None):
+    """The oracle on the GPU run's codes, one (b, h) head per task on a
+    thread pool; returns (O, T, n_tie) as oracle.attention does."""
     causal = run.w.spec["causal"] if causal is None else causal
     q, _ = dequant(run, 0)
     k, _ = dequant(run, 1)
     v, vs = dequant(run, 2)
     rule = "bf16" if run.modes[2] == "float" else P_RULE[run.modes[2]]
-    return OA.attention(q, k, v, rule, v_scale=vs, causal=causal, rows=rows, allowance=True,
-                        sm_scale=sm_scale)
+    B, H = q.shape[:2]
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        return OA.attention(q[sl], k[sl], v[sl], rule, v_scale=None if vs is None else vs[sl], causal=causal,
+                            rows=rows, allowance=True, sm_scale=sm_scale)
+
+    with ThreadPoolExecutor(_oracle_threads()) as ex:
+        parts = list(ex.map(one, range(B * H)))
+    R = parts[0][0].shape[2]
+    D = q.shape[3]
+    o = np.concatenate([p[0] for p in parts], axis=0).reshape(B, H, R, D)
+    T = np.concatenate([p[1] for p in parts], axis=0).reshape(B, H, R, D)
+    return o, T, sum(p[2] for p in parts)
+
+
+def _parity_log(rec):
+    """Append one parity record (JSON line) to gpurun_out/parity.jsonl."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    d = os.path.join(root, "gpurun_out")
+    try:
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "parity.jsonl"), "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    except OSError:
+        pass
 
 
 def check_attention(gpu_out: np.ndarray, ref, label=""):
     """Parity bar: relative Frobenius <= 1e-3 and |err| <= 2e-3 + T (tie
-    allowance) element by element."""
+    allowance) element by element.  Elements above 2e-3 may only be ones
+    the allowance covers: the query rows holding them number at most the
+    probability elements near a rounding boundary, and they are at most 1 %
+    of the output.  The counts go to the parity log."""
     o, T, n_tie = ref
-    err = np.abs(gpu_out.astype(np.float64) - o)
-    rel = np.linalg.norm(gpu_out.astype(np.float64) - o) / max(np.linalg.norm(o), 1e-300)
-    viol = err > 2e-3 + T
+    g64 = gpu_out.astype(np.float64)
+    err = np.abs(g64 - o)
+    rel = float(np.linalg.norm(g64 - o) / max(np.linalg.norm(o), 1e-300))
+    over = err > 2e-3
+    n_over = int(over.sum())
+    n_over_rows = int(over.any(axis=-1).sum()) if err.size else 0
+    excess = float((err - 2e-3).max()) if err.size else 0.0
+    rec = {"case": label, "t": round(time.time(), 1), "outputs": int(err.size), "rel_frobenius": rel,
+           "max_abs": float(err.max()) if err.size else 0.0, "tie_p_elements": int(n_tie),
+           "outputs_with_T": int((T > 0).sum()), "outputs_over_2e-3": n_over, "rows_over_2e-3": n_over_rows,
+           "max_excess_over_2e-3": max(excess, 0.0)}
+    _parity_log(rec)
     assert not np.isnan(gpu_out).any(), f"{label}: NaN in output"
     assert rel <= 1e-3, f"{label}: relative Frobenius {rel:.3e} > 1e-3"
+    viol = err > 2e-3 + T
     assert not viol.any(), (f"{label}: {int(viol.sum())} elements over 2e-3 + T; max err {err.max():.3e}, "
                             f"worst excess {(err - 2e-3 - T).max():.3e}; tie elements {n_tie}")
+    assert n_over_rows <= n_tie and n_over <= 0.01 * err.size, (
+        f"{label}: {n_over} elements in {n_over_rows} rows over 2e-3 (tie elements {n_tie}, "
+        f"outputs {err.size})")
     return rel, float(err.max()), n_tie
 
 

@@ -2,6 +2,9 @@
 the oracle, on small multi-tile shapes with ragged tails, on hand-built edge
 values, and at the full workload sizes (sampled rows / blocks there)."""
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -9,8 +12,8 @@ import torch
 import quantized_attention_fa_amd as faq
 from oracle import formats as F
 from oracle import quantize as OQ
-from synth import CONFIGS, make_inputs, sample_rows
-from gpu_helpers import DEV, GpuRun, small_workload
+from synth import CONFIGS, make_inputs
+from gpu_helpers import DEV, GpuRun, _parity_log, small_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -180,19 +183,28 @@ def test_fp8_block_small(bt, S):
     assert np.array_equal(qt.codes.cpu().numpy(), codes)
 
 
-def _check_rotated(y_gpu, x, R):
+def _check_rotated(y_gpu, x, R, label="rotate"):
     """The GPU rounds an fp32-accumulated product X.R to bf16, the oracle the
-    exact one: they agree except where the exact value lies within the fp32
-    accumulation error of a bf16 rounding boundary.  Bound: one bf16 ulp plus
-    D * 2^-22 * sum_i |x_i| |R_ij| (fp32 dot-product error of the MFMA);
-    at least 99.9% of the elements are identical."""
+    exact one (fp64).  Where the exact value lies within the fp32
+    accumulation error of a bf16 rounding boundary the two may round apart:
+    by one bf16 ulp, or by more where X.R cancels (|y| far below
+    sum_i |x_i| |R_ij|), which the fp32 bound D * 2^-22 * sum_i |x_i| |R_ij|
+    covers.  Elements whose bound is under a quarter ulp must agree within
+    one ulp; the equal fraction (measured, logged) must be >= 99.9 %."""
     y_ref = OQ.rotate(x, R)
     diff = np.abs(y_gpu.astype(np.float64) - y_ref)
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(y_ref), 1e-30))) - 7)
     D = R.shape[0]
     acc = D * 2.0 ** -22 * (np.abs(x.astype(np.float64)) @ np.abs(R.astype(np.float64)))
+    eq = float(np.mean(diff == 0))
+    over1 = diff > ulp * 1.0001
+    _parity_log({"case": label, "elements": int(diff.size), "equal_fraction": eq,
+                 "over_1ulp": int(over1.sum()), "max_ulps": float((diff / ulp).max()) if diff.size else 0.0,
+                 "over_1ulp_with_small_bound": int((over1 & (acc < 0.25 * ulp)).sum())})
     assert np.all(diff <= ulp * 1.0001 + acc)
-    assert np.mean(diff == 0) >= 0.999
+    assert not np.any(over1 & (acc < 0.25 * ulp))
+    assert eq >= 0.999
+    return eq
 
 
 @pytest.mark.parametrize("bt,S,D", [(128, 300, 128), (256, 300, 128), (128, 256, 64), (256, 70, 64)])
@@ -208,7 +220,7 @@ def test_rotate_block_small(bt, S, D):
     qt = faq.fa_quantize(xt.to(DEV), faq.QConfig("fp8_e4m3", "per_token_block", block_tokens=bt),
                          rot=R.to(DEV), debug_rotated=dbg)
     y = _np(dbg)
-    _check_rotated(y, _np(xt), _np(R))
+    _check_rotated(y, _np(xt), _np(R), f"rotate bt={bt} S={S} D={D}")
     codes, s = OQ.quantize_fp8_block(y, bt)
     assert np.array_equal(qt.scales.cpu().numpy().reshape(s.shape), s)
     assert np.array_equal(qt.codes.cpu().numpy(), codes)
@@ -331,38 +343,41 @@ def test_empty_tensor_is_a_no_op():
 # ---------------------------------------------------------------- full sizes
 
 
-def _rows_check(run, br, rows_per_bh=24, seed=0):
-    """Oracle recomputation of sampled token rows (every (b,h)) from the
-    GPU's inputs; per-token and MX quantization are row-local."""
+def _rows_check(run, br):
+    """Oracle recomputation of every token row from the GPU's inputs, head by
+    head on a thread pool; codes and scales compared bit for bit."""
     w = run.w
     B, H, S, D = w.shape
     x = (w.q, w.k, w.v)[br]
-    rows = sample_rows(w.cfg * 10 + br + seed, S, rows_per_bh, edge=4)
-    xs = x[:, :, rows].to(torch.float32).numpy()
-    if run.mode == "fp8_token":
-        codes, s = OQ.quantize_fp8_per_token(xs)
-        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
-        assert np.array_equal(run.qt[br].scales.view(B, H, S)[:, :, rows].cpu().numpy(), s)
-    elif run.mode == "mxfp4":
-        packed, e8 = OQ.quantize_mxfp4(xs)
-        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), packed)
-        assert np.array_equal(run.qt[br].scales[:, :, rows].cpu().numpy(), e8)
-    elif run.mode == "int8_head":
-        codes = OQ.quantize_int8_per_head(xs, run.static[br].cpu().numpy())
-        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
-    elif run.mode == "fp8_head":
-        codes = OQ.quantize_fp8_per_head(xs, run.static[br].cpu().numpy())
-        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
-    elif run.mode == "int8_token":
-        codes, s = OQ.quantize_int8_per_token(xs)
-        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
-        assert np.array_equal(run.qt[br].scales.view(B, H, S)[:, :, rows].cpu().numpy(), s)
-    elif run.mode == "mxfp8":
-        codes, e8 = OQ.quantize_mxfp8(xs)
-        assert np.array_equal(run.qt[br].codes[:, :, rows].cpu().numpy(), codes)
-        assert np.array_equal(run.qt[br].scales[:, :, rows].cpu().numpy(), e8)
-    else:
-        raise AssertionError(run.mode)
+    codes_gpu = run.qt[br].codes.cpu().numpy()
+    sc = run.qt[br].scales
+    scales_gpu = (sc.view(B, H, S) if run.mode in ("fp8_token", "int8_token") else sc).cpu().numpy()
+    static = run.static[br].cpu().numpy() if run.static[br] is not None else None
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        xs = x[b:b + 1, h:h + 1].to(torch.float32).numpy()
+        cg = codes_gpu[b:b + 1, h:h + 1]
+        if run.mode == "fp8_token":
+            codes, s = OQ.quantize_fp8_per_token(xs)
+        elif run.mode == "int8_token":
+            codes, s = OQ.quantize_int8_per_token(xs)
+        elif run.mode == "mxfp4":
+            codes, s = OQ.quantize_mxfp4(xs)
+        elif run.mode == "mxfp8":
+            codes, s = OQ.quantize_mxfp8(xs)
+        elif run.mode == "int8_head":
+            codes, s = OQ.quantize_int8_per_head(xs, static[h:h + 1]), None
+        elif run.mode == "fp8_head":
+            codes, s = OQ.quantize_fp8_per_head(xs, static[h:h + 1]), None
+        else:
+            raise AssertionError(run.mode)
+        assert np.array_equal(cg, codes), (run.mode, br, b, h)
+        if s is not None:
+            assert np.array_equal(scales_gpu[b:b + 1, h:h + 1], s), (run.mode, br, b, h)
+
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        list(ex.map(one, range(B * H)))
 
 
 def _calib_check(run):
@@ -376,28 +391,38 @@ def _calib_check(run):
         assert np.array_equal(run.static[br].cpu().numpy(), scales(ref))
 
 
-def _blocks_check(run, br, nblocks=6):
-    """Sampled token blocks of the rotate path: rotated values within a bf16
-    ulp of the oracle, codes/scales bit-exact against the oracle run on the
-    GPU's rotated values."""
+def _blocks_check(run, br):
+    """Every token block of the rotate path, head by head: rotated values
+    against the oracle's (_check_rotated), then codes and scales bit-exact
+    against the oracle's block quantizer run on the GPU's rotated values."""
     w = run.w
     B, H, S, D = w.shape
     bt = run.qt[br].cfg.block_tokens
     nb = -(-S // bt)
-    g = np.random.default_rng([w.cfg, br, 7])
     scales = run.qt[br].scales.view(B, H, nb).cpu().numpy()
-    for _ in range(nblocks):
-        b, h, k = int(g.integers(B)), int(g.integers(H)), int(g.integers(nb))
-        sl = slice(k * bt, min(S, (k + 1) * bt))
-        x = (w.q, w.k, w.v)[br][b:b + 1, h:h + 1, sl].to(torch.float32).numpy()
+    codes_gpu = run.qt[br].codes.cpu().numpy()
+    xs = (w.q, w.k, w.v)[br]
+    ys = run.rotated[br].cpu() if br < 2 else None
+    R = w.rot.to(torch.float32).numpy()
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        x = xs[b:b + 1, h:h + 1].to(torch.float32).numpy()
         if br < 2:
-            y = run.rotated[br][b:b + 1, h:h + 1, sl].to(torch.float32).cpu().numpy()
-            _check_rotated(y, x, w.rot.to(torch.float32).numpy())
+            y = ys[b:b + 1, h:h + 1].to(torch.float32).numpy()
+            eq = _check_rotated(y, x, R, f"cfg{w.cfg} branch {br} rotated (b={b}, h={h}) full size")
         else:
-            y = x
+            y, eq = x, 1.0
         codes, s = OQ.quantize_fp8_block(y, bt)
-        assert np.array_equal(run.qt[br].codes[b:b + 1, h:h + 1, sl].cpu().numpy(), codes)
-        assert scales[b, h, k] == s.ravel()[0]
+        assert np.array_equal(codes_gpu[b:b + 1, h:h + 1], codes), (b, h)
+        assert np.array_equal(scales[b:b + 1, h:h + 1], s), (b, h)
+        return eq
+
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        eqs = list(ex.map(one, range(B * H)))
+    if br < 2:
+        _parity_log({"case": f"cfg{w.cfg} branch {br} rotated, all heads", "equal_fraction_min": min(eqs),
+                     "equal_fraction_mean": float(np.mean(eqs))})
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7, 8])
