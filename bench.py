@@ -9,12 +9,16 @@ Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
 
-prints one JSON line.  The default workload is the INT8 per-head static
-LLM-prefill case (bf16 [2,32,4096,128], causal).  `value` is attention
-operations (4*D per unmasked query-key pair) per second of the whole step,
-in TOPS.  `roofline` reports the attention call (V re-layout + fused kernel)
-against the mode's dense MFMA peak; `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+prints one JSON line.  The default workload is the largest configuration
+that fits one GPU: FP8 E4M3 per-token dynamic on the video-DiT shape (bf16
+[1,40,32760,128], non-causal).  `value` is attention operations (4*D per
+unmasked query-key pair) per second of the whole step (mean over the timed
+steps), in TFLOPS (TOPS for INT8); the median and minimum step times are
+reported beside it.  `roofline` reports the attention call (K/V re-layout +
+fused kernel) against the mode's dense MFMA peak; `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload; `clocks` records the
+GPU's shader and memory clocks, read with amd-smi while attention calls
+run back to back after the timed steps.
 """
 
 import argparse
@@ -271,6 +275,42 @@ def recorded_traffic(workload):
     return rec.get("attention_bytes_per_launch")
 
 
+def _amd_smi_clocks(proc):
+    """Shader clocks of the 8 XCDs (gfx_0..gfx_7) and the memory clock, MHz,
+    from a finished `amd-smi metric -c --json` process."""
+    try:
+        out, _ = proc.communicate(timeout=30)
+        clk = json.loads(out)["gpu_data"][0]["clock"]
+        gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
+        return {"sclk_mhz_per_xcd": gfx, "sclk_mhz_mean": round(sum(gfx) / len(gfx), 1),
+                "mclk_mhz": clk["mem_0"]["clk"]["value"]}
+    except Exception as e:  # pragma: no cover - depends on the host's tools
+        return {"error": f"amd-smi: {type(e).__name__}: {e}"[:200]}
+
+
+def clocks_under_load(fn, ms_per_call, seconds=4.0):
+    """GPU clocks read while about `seconds` of `fn` calls are queued on the
+    GPU (an idle GPU drops its clocks, so they are sampled under the load
+    the timed steps put on it)."""
+    import subprocess
+    import torch
+    n = max(10, int(seconds * 1e3 / max(ms_per_call, 1e-3)))
+    n = min(n, 20000)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        fn()
+    try:
+        proc = subprocess.Popen(["amd-smi", "metric", "-g", "0", "-c", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except Exception as e:  # pragma: no cover
+        torch.cuda.synchronize()
+        return {"error": f"amd-smi: {type(e).__name__}"}
+    res = _amd_smi_clocks(proc)
+    torch.cuda.synchronize()
+    res["calls_queued"] = n
+    return res
+
+
 def copy_calibration(dev, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size, for scaling the
     profiler's FETCH_SIZE / WRITE_SIZE counters."""
@@ -286,11 +326,13 @@ def copy_calibration(dev, nbytes=1 << 30, reps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload 1..11 (default 2, the metric's workload; 6-8 are the sibling FA modes, "
-                         "9-10 per-branch configurations, 11 decode over a quantized cache)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 1..11 (default 3, FP8 per-token on the video-DiT shape: the largest of the "
+                         "metric's configurations; 1-5 are the metric's configurations, 6-8 the sibling FA "
+                         "modes, 9-10 per-branch configurations, 11 decode over a quantized cache)")
+    ap.add_argument("--no-clocks", action="store_true", help="do not read the GPU clocks with amd-smi")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--layout", choices=("bnsd", "bsnd"), default="bnsd",
                     help="memory layout of Q/K/V, their codes and the output")
@@ -346,6 +388,7 @@ def main():
     a_ms = [e[1].elapsed_time(e[2]) for e in ev]
     step_ms = [q + a for q, a in zip(q_ms, a_ms)]
     mean = lambda v: sum(v) / len(v)
+    median = lambda v: sorted(v)[len(v) // 2] if len(v) % 2 else 0.5 * sum(sorted(v)[len(v) // 2 - 1:len(v) // 2 + 1])
     ms_step = mean(step_ms)
     ops = attention_ops(w)
     qbytes = quantize_bytes(w)
@@ -397,9 +440,14 @@ def main():
         "quantize": ({"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(q_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": qbytes,
                       "ms_per_step": round(mean(q_ms), 4)} if qbytes else None),
-        "timing": {"method": "hip events on the compute stream, per step", "min_step_ms": round(min(step_ms), 4),
+        "timing": {"method": "hip events on the compute stream, per step", "mean_step_ms": round(ms_step, 4),
+                   "median_step_ms": round(median(step_ms), 4), "min_step_ms": round(min(step_ms), 4),
+                   "attention_median_ms": round(median(a_ms), 4), "attention_min_ms": round(min(a_ms), 4),
+                   "quantize_median_ms": round(median(q_ms), 4), "quantize_min_ms": round(min(q_ms), 4),
                    "wall_s_incl_flush": round(wall, 3), "cache_flush_between_steps": flush is not None},
     }
+    if not args.no_clocks:
+        line["clocks"] = {"attention_under_load": clocks_under_load(attention, att_ms)}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -59,7 +59,10 @@ typedef enum {
 
 /* Quantized data type ("fa3_quant 配置说明" §2.2 QConfig.dtype, the subset the
    FA modes use: "FA 量化" page, 该类下的模式清单).  FAQ_FLOAT means "not
-   quantized" and is rejected by this version of the library. */
+   quantized" ("fa3_quant 配置说明" §2.3: an unconfigured branch): attention
+   accepts it for any of Q, K and V (the branch's bf16 values stand in for
+   codes); fa_quantize and the size queries reject it (there is nothing to
+   quantize). */
 typedef enum { FAQ_FLOAT = 0, FAQ_INT8 = 1, FAQ_FP8_E4M3 = 2, FAQ_MXFP4 = 3, FAQ_MXFP8 = 4 } faq_dtype;
 
 /* Quantization granularity (QConfig.scope):
@@ -83,8 +86,11 @@ typedef struct {
   int32_t scope;        /* faq_scope                                         */
   int32_t symmetric;    /* must be 1: symmetric, no offset (组合 1)           */
   int32_t method;       /* 0 = minmax (QConfig.method)                       */
-  int32_t block_tokens; /* PER_TOKEN_BLOCK only: 128 (Q) or 256 (K/V), any
-                           positive multiple of 128 is accepted               */
+  int32_t block_tokens; /* PER_TOKEN_BLOCK only: 128 (the Q block of the
+                           rotate path) or 256 (its K/V block), for any
+                           branch; another positive value is
+                           FAQ_ERR_UNSUPPORTED, zero or negative
+                           FAQ_ERR_INVALID_ARG                                */
 } faq_qconfig;
 
 /* Memory layout of a tensor with logical shape (B, H, S, D). */
@@ -199,9 +205,11 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
    Probabilities enter the PV product quantized per 128-key tile relative
    to the tile's own row maximum: int8 round(127 p w_j) or E4M3 of
    448 p w_j, with w_j the key's V scale over the tile's largest (1 when V
-   has one scale per tile), decided on the fp32 multiplier
-   fl32(qmax fl32(w_j)); MXFP4 / MXFP8 over 32-key groups in the MX modes.
-   The softmax denominator uses unquantized p. */
+   has one scale per tile), round to nearest even; the key holding the
+   tile maximum (p = 1) takes the code of the exact 448 w_j / 127 w_j, the
+   others that of their fp32 p times it; MXFP4 / MXFP8 over 32-key groups
+   in the MX modes; bf16 of p for an unquantized V.  The softmax
+   denominator uses unquantized p. */
 faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
                               float sm_scale, int32_t causal, void* out, int32_t out_dtype,
                               void* workspace, size_t workspace_bytes, void* stream);

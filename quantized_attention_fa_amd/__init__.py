@@ -144,6 +144,31 @@ def _physical(shape: tuple, layout: str, last: int) -> tuple:
     return (B, H, S, last) if layout == "bnsd" else (B, S, H, last)
 
 
+def _check_buffer(t: torch.Tensor, nbytes: int, device, where: str):
+    """A caller-supplied device buffer: contiguous, on `device`, holding at
+    least `nbytes` bytes (the C ABI cannot check sizes)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG, f"{where}: need a contiguous CUDA tensor on {device}")
+    if t.numel() * t.element_size() < nbytes:
+        raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG,
+                           f"{where}: {t.numel() * t.element_size()} bytes, need {nbytes}")
+
+
+def _check_qtensor(t: QTensor, device, where: str):
+    """Codes and scales of a QTensor large enough for its config and shape."""
+    if t.cfg.dtype == "float":
+        B, H, S, D = t.shape
+        _check_buffer(t.codes, 2 * B * H * S * D, device, f"{where} (bf16 values)")
+        if t.codes.dtype != torch.bfloat16:
+            raise FaQuantError(_abi.FAQ_ERR_UNSUPPORTED, f"{where}: unquantized branches are bf16")
+        return
+    c, s = t.cfg.to_c(), _abi.faq_shape(*t.shape, _LAYOUTS[t.layout])
+    nc = int(_abi.lib().fa_quant_codes_bytes(ctypes.byref(c), ctypes.byref(s)))
+    ns = int(_abi.lib().fa_quant_scales_bytes(ctypes.byref(c), ctypes.byref(s)))
+    _check_buffer(t.codes, nc, device, f"{where} (codes)")
+    _check_buffer(t.scales, ns, device, f"{where} (scales)")
+
+
 def fa_quant_codes_bytes(cfg: QConfig, shape) -> int:
     c, s = cfg.to_c(), _abi.faq_shape(*shape)
     return int(_abi.lib().fa_quant_codes_bytes(ctypes.byref(c), ctypes.byref(s)))
@@ -166,7 +191,13 @@ def fa_quant_calibrate(x: torch.Tensor, amax: torch.Tensor, layout: str = "bnsd"
 
 
 def fa_quant_scales_from_amax(amax: torch.Tensor, dtype: str = "int8", out: torch.Tensor = None) -> torch.Tensor:
+    if amax.dtype != torch.float32 or not amax.is_cuda or not amax.is_contiguous():
+        raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG, "fa_quant_scales_from_amax: amax must be contiguous float32 "
+                                                     "on the GPU")
     out = torch.empty_like(amax) if out is None else out
+    if out.dtype != torch.float32:
+        raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG, "fa_quant_scales_from_amax: out must be float32")
+    _check_buffer(out, 4 * amax.numel(), amax.device, "fa_quant_scales_from_amax out")
     _check(_abi.lib().fa_quant_scales_from_amax(amax.data_ptr(), amax.numel(), _DTYPES[dtype], out.data_ptr(),
                                                 _stream(amax)), "fa_quant_scales_from_amax")
     return out
@@ -194,6 +225,17 @@ def fa_quantize(x: torch.Tensor, cfg: QConfig, static_scale: torch.Tensor = None
             codes = codes.view(*_physical(shape, layout, shape[3]))
             scales = torch.empty(max(ns // 4, 0), dtype=torch.float32, device=x.device)
         out = QTensor(cfg, shape, codes, scales, layout)
+    else:
+        if out.cfg != cfg or tuple(out.shape) != shape or out.layout != layout:
+            raise FaQuantError(_abi.FAQ_ERR_INVALID_ARG, "fa_quantize: out was made for another config, "
+                                                         "shape or layout")
+        _check_qtensor(out, x.device, "fa_quantize out")
+    if static_scale is not None:
+        _check_buffer(static_scale, 4 * shape[1], x.device, "fa_quantize static_scale")
+    if rot is not None:
+        _check_buffer(rot, 2 * shape[3] * shape[3], x.device, "fa_quantize rot")
+    if debug_rotated is not None:
+        _check_buffer(debug_rotated, 2 * x.numel(), x.device, "fa_quantize debug_rotated")
     qt = out.to_c()
     st = lib.fa_quantize(x.data_ptr(), _tdtype(x), ctypes.byref(s), ctypes.byref(c),
                          static_scale.data_ptr() if static_scale is not None else None,
@@ -214,12 +256,19 @@ def fa_quant_attention(q: QTensor, k: QTensor, v: QTensor, sm_scale: float = 0.0
     lib = _abi.lib()
     qc, kc, vc = q.to_c(), k.to_c(), v.to_c()
     dev = q.codes.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check_qtensor(t, dev, f"fa_quant_attention {name}")
     if out is None:
         out = torch.empty(_physical(q.shape, q.layout, q.shape[3]), dtype=out_dtype, device=dev)
     odt = FAQ_T_BF16 if out.dtype == torch.bfloat16 else FAQ_T_F32 if out.dtype == torch.float32 else -1
+    if odt >= 0:
+        B, H, Sq, D = q.shape
+        _check_buffer(out, B * H * Sq * D * out.element_size(), dev, "fa_quant_attention out")
+    need = int(lib.fa_quant_attention_workspace_bytes(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc)))
     if workspace is None:
-        need = lib.fa_quant_attention_workspace_bytes(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc))
-        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_buffer(workspace, need, dev, "fa_quant_attention workspace")
     st = lib.fa_quant_attention(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), float(sm_scale),
                                 int(bool(causal)), out.data_ptr(), odt, workspace.data_ptr(),
                                 workspace.numel(), _stream(out))
