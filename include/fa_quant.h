@@ -214,6 +214,26 @@ faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const 
                               float sm_scale, int32_t causal, void* out, int32_t out_dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the static workspace of fa_quant_attention_static_ws, per GPU. */
+#define FA_QUANT_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* fa_quant_attention for callers that cannot allocate device memory (code
+   under HIP graph capture, tight serving loops, harnesses that forbid
+   allocation): the same operation, arguments and results, without a
+   workspace argument.  The kernels' workspace is a static device array of
+   FA_QUANT_STATIC_WORKSPACE_BYTES (64 MiB) on each GPU the library runs on,
+   held until the process ends; the call allocates nothing (no hipMalloc,
+   hipFree or allocating library routine).  A call whose workspace need
+   (fa_quant_attention_workspace_bytes) exceeds the array returns
+   FAQ_ERR_WORKSPACE and enqueues nothing.  Every call on one GPU shares
+   that GPU's array: calls that overlap on one GPU (other streams, other
+   host threads) race, and the caller must serialize them; the stream must
+   belong to the current device.  The array's contents between calls are
+   never read (each call writes all it reads). */
+faq_status fa_quant_attention_static_ws(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
+                                        float sm_scale, int32_t causal, void* out, int32_t out_dtype,
+                                        void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_quant_status_string(int32_t status);
 

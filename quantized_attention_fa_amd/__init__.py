@@ -24,7 +24,7 @@ from ._abi import (FAQ_FP8_E4M3, FAQ_INT8, FAQ_MXFP4, FAQ_MXFP8, FAQ_FLOAT, FAQ_
 __all__ = [
     "QConfig", "QTensor", "FaQuantError", "resolve_fa3_config", "default_qconfig", "float_branch",
     "fa_quant_calibrate", "fa_quant_scales_from_amax", "fa_quantize",
-    "fa_quant_attention", "fa_quant_attention_workspace_bytes",
+    "fa_quant_attention", "fa_quant_attention_workspace_bytes", "fa_quant_attention_static_ws",
     "fa_quant_codes_bytes", "fa_quant_scales_bytes", "fa_quant_status_string",
 ]
 
@@ -273,4 +273,24 @@ def fa_quant_attention(q: QTensor, k: QTensor, v: QTensor, sm_scale: float = 0.0
                                 int(bool(causal)), out.data_ptr(), odt, workspace.data_ptr(),
                                 workspace.numel(), _stream(out))
     _check(st, "fa_quant_attention")
+    return out
+
+
+def fa_quant_attention_static_ws(q: QTensor, k: QTensor, v: QTensor, out: torch.Tensor, sm_scale: float = 0.0,
+                                 causal: bool = False) -> torch.Tensor:
+    """fa_quant_attention without a workspace and without any allocation:
+    the library's static per-GPU workspace (calls on one GPU must not
+    overlap).  `out` is required (bf16 or float32, q's shape and layout)."""
+    lib = _abi.lib()
+    qc, kc, vc = q.to_c(), k.to_c(), v.to_c()
+    dev = q.codes.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check_qtensor(t, dev, f"fa_quant_attention_static_ws {name}")
+    odt = FAQ_T_BF16 if out.dtype == torch.bfloat16 else FAQ_T_F32 if out.dtype == torch.float32 else -1
+    if odt >= 0:
+        B, H, Sq, D = q.shape
+        _check_buffer(out, B * H * Sq * D * out.element_size(), dev, "fa_quant_attention_static_ws out")
+    st = lib.fa_quant_attention_static_ws(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), float(sm_scale),
+                                          int(bool(causal)), out.data_ptr(), odt, _stream(out))
+    _check(st, "fa_quant_attention_static_ws")
     return out

@@ -33,8 +33,10 @@ EXPORTS = (
     "fa_quantize",
     "fa_quant_attention_workspace_bytes",
     "fa_quant_attention",
+    "fa_quant_attention_static_ws",
     "fa_quant_status_string",
 )
+FA_QUANT_STATIC_WORKSPACE_BYTES = 64 << 20
 
 
 class faq_qconfig(ctypes.Structure):
@@ -82,6 +84,9 @@ def _declare(lib):
     lib.fa_quant_attention.argtypes = [_P(faq_qtensor), _P(faq_qtensor), _P(faq_qtensor), ctypes.c_float,
                                        ctypes.c_int32, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
     lib.fa_quant_attention.restype = ctypes.c_int32
+    lib.fa_quant_attention_static_ws.argtypes = [_P(faq_qtensor), _P(faq_qtensor), _P(faq_qtensor), ctypes.c_float,
+                                                 ctypes.c_int32, _vp, ctypes.c_int32, _vp]
+    lib.fa_quant_attention_static_ws.restype = ctypes.c_int32
     lib.fa_quant_status_string.argtypes = [ctypes.c_int32]
     lib.fa_quant_status_string.restype = ctypes.c_char_p
     return lib

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 ARCH = os.environ.get("FAQ_OFFLOAD_ARCH", "gfx950")
 
-LIB_SOURCES = ["api.hip", "quant.hip", "attention.hip"]
+LIB_SOURCES = ["api.hip", "quant.hip", "attention.hip", "static_ws.hip"]
 PROBE_SOURCES = ["probe.hip"]
 LIB = os.path.join(PKG, "libfaquant.so")
 PROBE_LIB = os.path.join(PKG, "libfaquant_probe.so")

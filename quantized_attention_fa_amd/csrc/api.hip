@@ -292,10 +292,13 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
   return attn_workspace_bytes(qk, pv, k->shape.B, k->shape.H, q->shape.S, k->shape.S, k->shape.D, 0);
 }
 
-faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
-                              float sm_scale, int32_t causal, void* out, int32_t out_dtype,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  static const char* fn = "fa_quant_attention";
+}  // extern "C"
+
+// The body of the attention entry points: validation (before any HIP
+// call), the workspace check, dispatch.
+faq_status faq::attention_entry(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
+                                float sm_scale, int32_t causal, void* out, int32_t out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream, const char* fn) {
   int qk, pv, qf, kf;
   const faq_status cs = attn_check(q, k, v, &qk, &pv, &qf, &kf, fn);
   if (cs != FAQ_OK) return cs;
@@ -331,4 +334,9 @@ faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const 
   return hip_status(launch_attention(a, (hipStream_t)stream), fn);
 }
 
-}  // extern "C"
+extern "C" faq_status fa_quant_attention(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v,
+                                         float sm_scale, int32_t causal, void* out, int32_t out_dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_entry(q, k, v, sm_scale, causal, out, out_dtype, workspace, workspace_bytes, stream,
+                         "fa_quant_attention");
+}

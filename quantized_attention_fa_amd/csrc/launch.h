@@ -90,4 +90,11 @@ bool attn_pair_supported(int qk, int pv);
 size_t attn_workspace_bytes(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int causal);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
+// The common body of the attention entry points (api.hip): validation
+// before any HIP call, the workspace check, dispatch.  `fn` names the entry
+// point in log lines.
+faq_status attention_entry(const faq_qtensor* q, const faq_qtensor* k, const faq_qtensor* v, float sm_scale,
+                           int32_t causal, void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                           void* stream, const char* fn);
+
 }  // namespace faq
