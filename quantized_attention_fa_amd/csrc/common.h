@@ -269,3 +269,16 @@ FAQ_DEV void int8_code_words(const float* x, float s, uint32_t* w) {
 FAQ_DEV float scale_from_amax(float amax, float qmax) {
   return amax == 0.0f ? 1.0f : amax / qmax;  // IEEE division
 }
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// global access in flight): this wave's LDS reads and writes complete first
+// (lgkmcnt(0)); global loads - and copies into LDS - may stay in flight,
+// their completion being waited for with vmcnt where their data is used.
+// The signal fences keep the compiler from moving memory accesses across
+// it.
+FAQ_DEV void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}

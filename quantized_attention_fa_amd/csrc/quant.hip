@@ -38,34 +38,48 @@ FAQ_DEV int64_t slice_off(int64_t row0, int64_t i, const RowMap& m, int dsh) {
 
 // ------------------------------------------------------------------------
 // Min-max calibration: amax[h] = max(amax[h], max |x[b,h,:,:]|).
-// grid = (chunks per (b,h) slice, B*H); the float bits of a non-negative
-// value order like unsigned integers, so the running max is an atomicMax.
+// grid = (chunks per (b,h) slice, B*H).  A thread keeps U 16-byte loads in
+// flight and reduces their magnitudes as integers: for finite values |x|
+// orders like its magnitude bits (bf16: the low 15 bits of each half-word,
+// two at a time with packed 16-bit max; fp32: the low 31 bits), so the max
+// is exact.  The float bits of a non-negative value also order like
+// unsigned integers, so the running max across workgroups and calls is an
+// atomicMax (one per workgroup).
 // ------------------------------------------------------------------------
-template <typename T>
+template <typename T, int U>
 __global__ __launch_bounds__(kThreads) void k_calibrate(const T* __restrict__ x, RowMap rm, int dsh, int64_t per_bh,
                                                         int H, float* __restrict__ amax) {
-  constexpr int U = 4;
+  constexpr int EPL = 16 / sizeof(T);  // elements per 16-byte load
+  constexpr bool BF = sizeof(T) == 2;
   const int64_t bh = blockIdx.y;
   const int64_t row0 = rm.row(bh / H, bh % H, 0);
-  float m = 0.0f;
-  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * 8 * U; c0 < per_bh;
-       c0 += (int64_t)gridDim.x * kThreads * 8 * U) {
-    float v[U][8];
+  uint32_t mb = 0;  // bf16: two packed 15-bit magnitudes; fp32: one 31-bit magnitude
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * EPL * U; c0 < per_bh;
+       c0 += (int64_t)gridDim.x * kThreads * EPL * U) {
+    uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t i = c0 + ((int64_t)u * kThreads + threadIdx.x) * 8;
-      if (i < per_bh) {
-        load8(x + slice_off(row0, i, rm, dsh), v[u]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
-      }
+      const int64_t i = c0 + ((int64_t)u * kThreads + threadIdx.x) * EPL;
+      v[u] = i < per_bh ? *reinterpret_cast<const uint4*>(x + slice_off(row0, i, rm, dsh)) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
+      for (int k = 0; k < 4; ++k) {
+        if (BF) {
+          typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+          const u16x2 a = __builtin_bit_cast(u16x2, w[k] & 0x7fff7fffu);
+          const u16x2 b = __builtin_bit_cast(u16x2, mb);
+          mb = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+        } else {
+          mb = max(mb, w[k] & 0x7fffffffu);
+        }
+      }
+    }
   }
+  if (BF) mb = max(mb & 0xffffu, mb >> 16) << 16;  // the larger half, as fp32 bits
+  float m = __uint_as_float(mb);
   m = wave_max(m);
   __shared__ float red[kThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -314,57 +328,126 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ 
 }
 
 // ------------------------------------------------------------------------
+// Persistent walk over token blocks: workgroup g takes blocks g, g + grid,
+// g + 2 grid, ... of the (b, h, block) order.  A position advances by the
+// grid stride with carries (uniform scalar work): a division inside the
+// loop would take vector registers that may still be the targets of loads
+// in flight, which makes the compiler wait for all of them.
+// ------------------------------------------------------------------------
+struct BlockPos {
+  int b, h, blk;
+};
+
+struct BlockWalk {
+  int nblk, H, dblk, dh, db;  // blocks per head, heads, the grid stride split
+  __device__ __forceinline__ BlockWalk(int grid, int nblk_, int H_) : nblk(nblk_), H(H_) {
+    dblk = grid % nblk;
+    const int dbh = grid / nblk;
+    dh = dbh % H;
+    db = dbh / H;
+  }
+  __device__ __forceinline__ BlockPos at(int work) const { return BlockPos{work / nblk / H, (work / nblk) % H, work % nblk}; }
+  __device__ __forceinline__ BlockPos next(BlockPos p) const {
+    p.blk += dblk;
+    const int c = p.blk >= nblk ? 1 : 0;
+    p.blk -= c * nblk;
+    p.h += dh + c;  // < 2 H
+    const int c2 = p.h >= H ? 1 : 0;
+    p.h -= c2 * H;
+    p.b += db + c2;
+    return p;
+  }
+};
+
+// ------------------------------------------------------------------------
 // FP8 E4M3 token-block quantization without rotation (the V branch of the
 // rotate path): one scale per (b,h, BT tokens x D).  bf16 input.
-// One workgroup per block; the block stays in registers between the amax
-// reduction and the encode.
+// Persistent workgroups walk the blocks; a block stays in registers between
+// the amax reduction and the encode, and the next block's loads are issued
+// before it is reduced (two register buffers; every load unconditional -
+// rows past S re-read row S - 1 and are left out of the maximum and the
+// stores - so the compiler's wait for one block leaves the next in
+// flight).  The block maximum crosses the waves through LDS behind a
+// barrier without a memory fence; alternating slots make one barrier per
+// block enough.
 // ------------------------------------------------------------------------
 template <int D, int BT>
-__global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __restrict__ x, RowMap rm, int H,
-                                                              int64_t S, int nblk,
-                                                              uint8_t* __restrict__ codes,
-                                                              float* __restrict__ scales) {
-  constexpr int NV = BT * D / (kThreads * 8);
-  const int64_t bh = blockIdx.y;
-  const int blk = blockIdx.x;
-  const int64_t tok0 = (int64_t)blk * BT;
-  const int64_t ntok = (S - tok0) < BT ? (S - tok0) : BT;
+constexpr int fp8_block_threads() { return BT * D >= 256 * 128 ? 512 : kThreads; }
+
+template <int D, int BT>
+__global__ __launch_bounds__((fp8_block_threads<D, BT>()), 2) void k_quant_fp8_block(
+    const uint16_t* __restrict__ x, RowMap rm, int H, int64_t S, int nblk, int nwork, uint8_t* __restrict__ codes,
+    float* __restrict__ scales) {
+  constexpr int NT = fp8_block_threads<D, BT>(), NW = NT / 64;
+  constexpr int NV = BT * D / (NT * 8);  // 16-byte loads per thread and block
+  __shared__ float red[2][NW];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const BlockWalk walk((int)gridDim.x, nblk, H);
   // element e of the block: token tok0 + e / D, channel e % D
-  const int64_t row0 = rm.row(bh / H, bh % H, tok0);
-  auto off = [&](int e) { return (row0 + (int64_t)(e / D) * rm.ss) * D + e % D; };
-  uint4 raw[NV];
-  float m = 0.0f;
+  auto load = [&](BlockPos p, uint4(&raw)[NV]) __attribute__((always_inline)) {
+    const int64_t tok0 = (int64_t)p.blk * BT;
+    const int64_t row0 = rm.row(p.b, p.h, 0);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = (i * kThreads + threadIdx.x) * 8;
-    raw[i] = (e / D < ntok) ? *reinterpret_cast<const uint4*>(x + off(e)) : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
-  }
-  m = wave_max(m);
-  __shared__ float red[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = scale_from_amax(m, 448.0f);
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = (i * kThreads + threadIdx.x) * 8;
-    if (e / D < ntok) {
-      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-      float f[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { f[2 * j] = bf16_lo(w[j]); f[2 * j + 1] = bf16_hi(w[j]); }
-      uint32_t c[2];
-      e4m3_code_words<8>(f, s, c);
-      *reinterpret_cast<uint2*>(codes + off(e)) = make_uint2(c[0], c[1]);
+    for (int i = 0; i < NV; ++i) {
+      const int e = (i * NT + threadIdx.x) * 8;
+      const int64_t tok = min(tok0 + e / D, S - 1);
+      raw[i] = *reinterpret_cast<const uint4*>(x + (row0 + tok * rm.ss) * D + e % D);
     }
+  };
+  auto process = [&](BlockPos p, const uint4(&raw)[NV], int slot) __attribute__((always_inline)) {
+    const int64_t tok0 = (int64_t)p.blk * BT;
+    const int64_t ntok = (S - tok0) < BT ? (S - tok0) : BT;
+    const int64_t row0 = rm.row(p.b, p.h, 0);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = (i * NT + threadIdx.x) * 8;
+      const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      float mi = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mi = fmaxf(mi, fmaxf(fabsf(bf16_lo(wd[j])), fabsf(bf16_hi(wd[j]))));
+      if (e / D < ntok) m = fmaxf(m, mi);
+    }
+    m = wave_max(m);
+    if (lane == 0) red[slot][w] = m;
+    barrier_lds();
+    m = red[slot][0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) m = fmaxf(m, red[slot][i]);
+    const float s = scale_from_amax(m, 448.0f);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = (i * NT + threadIdx.x) * 8;
+      if (e / D < ntok) {
+        const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { f[2 * j] = bf16_lo(wd[j]); f[2 * j + 1] = bf16_hi(wd[j]); }
+        uint32_t c[2];
+        e4m3_code_words<8>(f, s, c);
+        *reinterpret_cast<uint2*>(codes + (row0 + (tok0 + e / D) * rm.ss) * D + e % D) = make_uint2(c[0], c[1]);
+      }
+    }
+    if (threadIdx.x == 0) scales[((int64_t)p.b * H + p.h) * nblk + p.blk] = s;
+  };
+  uint4 ra[NV], rc[NV];
+  int work = (int)blockIdx.x;
+  BlockPos pa = walk.at(work);
+  load(pa, ra);
+  for (;;) {
+    const BlockPos pc = walk.next(pa);
+    const bool more1 = work + (int)gridDim.x < nwork;
+    load(more1 ? pc : pa, rc);
+    process(pa, ra, 0);
+    if (!more1) break;
+    const BlockPos pn = walk.next(pc);
+    const bool more2 = work + 2 * (int)gridDim.x < nwork;
+    load(more2 ? pn : pc, ra);
+    process(pc, rc, 1);
+    if (!more2) break;
+    pa = pn;
+    work += 2 * (int)gridDim.x;
   }
-  if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
 }
 
 // ------------------------------------------------------------------------
@@ -372,44 +455,67 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_block(const uint16_t* __
 //   Y = bf16_rne(X . R),  then per (b,h, BT tokens): s = fl32(amax|Y| / 448),
 //   code = E4M3(fl32(Y / s)).
 // Y^T = R^T X^T on the bf16 MFMA (16x16x32, fp32 accumulate): the A operand
-// is R^T from LDS (staged once per workgroup; the workgroup then walks
-// blocks in a grid-stride loop), the B operand is X read straight from
-// global memory (each lane's 8 bf16 are contiguous in a token row).  The
-// accumulator holds, per lane, 4 consecutive output channels of one token.
-// One wave per 32 tokens: BT/32 waves per workgroup.
+// is R^T from LDS, the B operand X read straight from global memory (each
+// lane's 8 bf16 are contiguous in a token row).  The accumulator holds, per
+// lane, 4 consecutive output channels of one token.  One wave per 32
+// tokens: BT/32 waves per workgroup.
+// Persistent workgroups (as many as fit on the GPU at once) stage R^T once
+// and walk the blocks; the X rows of the next block are loaded while the
+// current one is rotated, reduced and encoded.  The block maximum crosses
+// the waves through LDS behind a barrier without a memory fence, so those
+// loads stay in flight across it (alternating reduction slots make one
+// barrier per block enough: a slot is rewritten two blocks later, after
+// every wave has passed the barrier that follows its last read).
 // ------------------------------------------------------------------------
 template <int D, int BT>
-__global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(BT * 2, BT == 128 ? 3 : 2) void k_rot_fp8_block(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ rot, RowMap rm, int H,
-                                                          int64_t S, int nblk, int64_t nwork,
+                                                          int64_t S, int nblk, int nwork,
                                                           uint8_t* __restrict__ codes,
                                                           float* __restrict__ scales,
                                                           uint16_t* __restrict__ dbg) {
   constexpr int NW = BT / 32, NT = BT * 2, KK = D / 32, DB = D / 16, RS = D + 8;
   __shared__ uint16_t rt[D * RS];  // R^T, one padded row per output channel
-  __shared__ float red[NW];
-  for (int i = threadIdx.x; i < D * D; i += NT) {
-    const int k = i / D, n = i % D;
-    rt[n * RS + k] = rot[i];
+  __shared__ float red[2][NW];
+  // R^T: 16-byte loads of R's rows k, each element to row n of rt
+  for (int i = threadIdx.x; i < D * D / 8; i += NT) {
+    const int k = i / (D / 8), n0 = (i % (D / 8)) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(rot + k * D + n0);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      rt[(n0 + 2 * q) * RS + k] = (uint16_t)(wv[q] & 0xffffu);
+      rt[(n0 + 2 * q + 1) * RS + k] = (uint16_t)(wv[q] >> 16);
+    }
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-  for (int64_t work = blockIdx.x; work < nwork; work += gridDim.x) {
-    const int64_t bh = work / nblk;
-    const int blk = (int)(work % nblk);
-    const int64_t tok0 = (int64_t)blk * BT + w * 32;
-    const int64_t row0 = rm.row(bh / H, bh % H, 0);  // token tok is row row0 + tok rm.ss
-    bf16x8 xb[2][KK];
+
+  const int G = (int)gridDim.x;
+  const BlockWalk walk(G, nblk, H);
+
+  // X rows of block p (this wave's 32 tokens).  Every load is issued
+  // unconditionally - rows past S re-read row S - 1 and are left out of the
+  // block maximum and the stores - so that no branch separates the loads and
+  // the compiler counts them exactly: the wait for the block being
+  // processed leaves the next block's loads in flight.
+  auto load = [&](BlockPos p, bf16x8(&xb)[2][KK]) __attribute__((always_inline)) {
+    const int64_t tok0 = (int64_t)p.blk * BT + w * 32;
+    const int64_t row0 = rm.row(p.b, p.h, 0);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int64_t tok = tok0 + tb * 16 + l16;
+      const int64_t tok = min(tok0 + tb * 16 + l16, S - 1);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        uint4 r = make_uint4(0, 0, 0, 0);
-        if (tok < S) r = *reinterpret_cast<const uint4*>(x + (row0 + tok * rm.ss) * D + kk * 32 + g * 8);
-        xb[tb][kk] = __builtin_bit_cast(bf16x8, r);
-      }
+      for (int kk = 0; kk < KK; ++kk)
+        xb[tb][kk] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(x + (row0 + tok * rm.ss) * D + kk * 32 + g * 8));
     }
+  };
+
+  // rotate, block maximum, encode and store block p from its X rows
+  auto process = [&](BlockPos p, const bf16x8(&xb)[2][KK], int slot) __attribute__((always_inline)) {
+    const int64_t tok0 = (int64_t)p.blk * BT + w * 32;
+    const int64_t row0 = rm.row(p.b, p.h, 0);  // token tok is row row0 + tok rm.ss
     f32x4 acc[2][DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -417,17 +523,17 @@ __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __rest
       acc[1][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&rt[(db * 16 + l16) * RS + kk * 32 + g * 8]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&rt[(db * 16 + l16) * RS + kk * 32 + g * 8]);
         acc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[0][kk], acc[0][db], 0, 0, 0);
         acc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[1][kk], acc[1][db], 0, 0, 0);
       }
     }
     // round to bf16 (the rotated tensor is bf16; the hardware conversion
-    // rounds to nearest even), block max
+    // rounds to nearest even), block max over the tokens below S
     float m = 0.0f;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < 2; ++tb) {
+      float mt = 0.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -436,15 +542,16 @@ __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __rest
           const uint32_t yw = __builtin_bit_cast(uint32_t, y);
           acc[tb][db][r] = bf16_lo(yw);
           acc[tb][db][r + 1] = bf16_hi(yw);
-          m = fmaxf(m, fmaxf(fabsf(acc[tb][db][r]), fabsf(acc[tb][db][r + 1])));
+          mt = fmaxf(mt, fmaxf(fabsf(acc[tb][db][r]), fabsf(acc[tb][db][r + 1])));
         }
+      if (tok0 + tb * 16 + l16 < S) m = fmaxf(m, mt);
+    }
     m = wave_max(m);
-    if (lane == 0) red[w] = m;
-    __syncthreads();
-    m = red[0];
+    if (lane == 0) red[slot][w] = m;
+    barrier_lds();
+    m = red[slot][0];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) m = fmaxf(m, red[i]);
-    __syncthreads();  // red is rewritten by the next block
+    for (int i = 1; i < NW; ++i) m = fmaxf(m, red[slot][i]);
     const float s = scale_from_amax(m, 448.0f);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -470,8 +577,48 @@ __global__ __launch_bounds__(BT * 2) void k_rot_fp8_block(const uint16_t* __rest
         }
       }
     }
-    if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
+    if (threadIdx.x == 0) scales[((int64_t)p.b * H + p.h) * nblk + p.blk] = s;
+  };
+
+  // two register buffers of X rows, alternating: block b + grid is loaded
+  // while block b is processed (past the last block the current one is
+  // re-read and not processed; the exits are uniform over the workgroup:
+  // they depend on the work index only).  The grid never exceeds nwork.
+  bf16x8 xa[2][KK], xc[2][KK];
+  int work = (int)blockIdx.x;
+  BlockPos pa = walk.at(work);
+  load(pa, xa);
+  for (;;) {
+    const BlockPos pc = walk.next(pa);
+    const bool more1 = work + G < nwork;
+    load(more1 ? pc : pa, xc);
+    process(pa, xa, 0);
+    if (!more1) break;
+    const BlockPos pn = walk.next(pc);
+    const bool more2 = work + 2 * G < nwork;
+    load(more2 ? pn : pc, xa);
+    process(pc, xc, 1);
+    if (!more2) break;
+    pa = pn;
+    work += 2 * G;
   }
+}
+
+// Workgroups of `kernel` the GPU holds at once (per CU from the occupancy
+// query, times the CUs), for persistent grids; queried once per kernel.
+template <class K>
+int resident_workgroups(K kernel, int threads) {
+  static int resident = 0;
+  if (resident == 0) {
+    int dev = 0, per_cu = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) == hipSuccess && per_cu > 0)
+      resident = per_cu * prop.multiProcessorCount;
+    else
+      resident = 256;
+  }
+  return resident;
 }
 
 inline unsigned grid_chunks(int64_t n, int64_t per_block, unsigned cap) {
@@ -489,11 +636,15 @@ hipError_t launch_calibrate(const void* x, int x_dtype, const faq_shape& s, floa
   const int64_t per_bh = s.S * s.D;
   const RowMap rm = row_map(s);
   const int dsh = s.D == 128 ? 7 : 6;
-  dim3 grid(grid_chunks(per_bh, kThreads * 8 * 4, 65535), (unsigned)(s.B * s.H));
-  if (x_dtype == FAQ_T_BF16)
-    k_calibrate<uint16_t><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rm, dsh, per_bh, (int)s.H, amax);
-  else
-    k_calibrate<float><<<grid, kThreads, 0, st>>>((const float*)x, rm, dsh, per_bh, (int)s.H, amax);
+  // 16 loads of 16 bytes in flight per thread: 64 KiB per workgroup round
+  constexpr int U = 16;
+  if (x_dtype == FAQ_T_BF16) {
+    dim3 grid(grid_chunks(per_bh, kThreads * 8 * U, 65535), (unsigned)(s.B * s.H));
+    k_calibrate<uint16_t, U><<<grid, kThreads, 0, st>>>((const uint16_t*)x, rm, dsh, per_bh, (int)s.H, amax);
+  } else {
+    dim3 grid(grid_chunks(per_bh, kThreads * 4 * U, 65535), (unsigned)(s.B * s.H));
+    k_calibrate<float, U><<<grid, kThreads, 0, st>>>((const float*)x, rm, dsh, per_bh, (int)s.H, amax);
+  }
   return hipGetLastError();
 }
 
@@ -595,8 +746,12 @@ template <int D, int BT>
 static hipError_t fp8_block_d(const uint16_t* x, const faq_shape& s, uint8_t* codes,
                               float* scales, hipStream_t st) {
   const int nblk = (int)((s.S + BT - 1) / BT);
-  dim3 grid((unsigned)nblk, (unsigned)(s.B * s.H));
-  k_quant_fp8_block<D, BT><<<grid, kThreads, 0, st>>>(x, row_map(s), (int)s.H, s.S, nblk, codes, scales);
+  const int64_t nwork = (int64_t)nblk * s.B * s.H;
+  constexpr int NT = fp8_block_threads<D, BT>();
+  const int res = resident_workgroups(k_quant_fp8_block<D, BT>, NT);
+  const unsigned grid = (unsigned)(nwork < res ? nwork : res);
+  k_quant_fp8_block<D, BT><<<grid, NT, 0, st>>>(x, row_map(s), (int)s.H, s.S, nblk, (int)nwork, codes,
+                                                       scales);
   return hipGetLastError();
 }
 
@@ -614,9 +769,10 @@ static hipError_t rot_block_d(const uint16_t* x, const uint16_t* rot, const faq_
                               uint8_t* codes, float* scales, uint16_t* dbg, hipStream_t st) {
   const int nblk = (int)((s.S + BT - 1) / BT);
   const int64_t nwork = (int64_t)nblk * s.B * s.H;
-  const unsigned grid = (unsigned)(nwork < 2048 ? nwork : 2048);
-  k_rot_fp8_block<D, BT><<<grid, BT * 2, 0, st>>>(x, rot, row_map(s), (int)s.H, s.S, nblk, nwork, codes, scales,
-                                                   dbg);
+  const int res = resident_workgroups(k_rot_fp8_block<D, BT>, BT * 2);
+  const unsigned grid = (unsigned)(nwork < res ? nwork : res);
+  k_rot_fp8_block<D, BT><<<grid, BT * 2, 0, st>>>(x, rot, row_map(s), (int)s.H, s.S, nblk, (int)nwork, codes,
+                                                   scales, dbg);
   return hipGetLastError();
 }
 
