@@ -110,6 +110,10 @@ FAQ_DEV int kslot(int row) { return row ^ ((row >> 3) & 8); }
 // column p = 32 kb + 16 s + 8 h + t <-> key 64 h + 16 kb + 8 s + t.
 // int8 P V (32x32x32): k-step kb takes registers 0..15 of block kb:
 // column p = 32 kb + 16 h + r <-> key 64 h + 16 kb + r.
+// E4M3 P V for per-token V (32x32x64 f8f6f4): k-step s takes, in lane half h, the 32 bytes
+// of blocks 2 s and 2 s + 1 (keys 64 h + 32 s + 0..31); A and B pair their
+// bytes position by position, so column p <-> key p (natural order): lane
+// (i, h) reads 16-byte columns 4 h + 2 s and 4 h + 2 s + 1 of row i.
 FAQ_DEV int vt_key_bf16(int p) { return 64 * ((p >> 3) & 1) + 16 * (p >> 5) + 8 * ((p >> 4) & 1) + (p & 7); }
 FAQ_DEV int vt_key_i8(int p) { return 64 * ((p >> 4) & 1) + 16 * (p >> 5) + (p & 15); }
 
@@ -219,6 +223,12 @@ struct Cfg {
   static constexpr bool KSC =
       QK == QK_I8T || QK == QK_F8T || QK == QK_F8C || QK == QK_MX8 || QK == QK_GEN;  // per-key K floats
   static constexpr bool PI8 = PV == PV_I8H || PV == PV_I8T;  // int8 value MFMA
+  // E4M3 value MFMA (f8f6f4) for per-token V.  The instruction sums its
+  // products to about 2^-12 of the largest, an error of ~2^-12 |O| per
+  // output: within the absolute bar for per-token V, whose codes are
+  // normalised row by row, but not for V with one scale per tile, whose
+  // outlier channels carry outputs of tens; those keep the bf16 product.
+  static constexpr bool PF8 = PV == PV_F8W;
   static constexpr bool PMX = PV == PV_MX4 || PV == PV_MX8;  // MX probability groups
   static constexpr bool PVW = PV == PV_I8T || PV == PV_F8W;  // per-key V scale folded into P
   static constexpr bool SIG = PVW || PV == PV_F8C;            // sigma_t per tile
@@ -233,7 +243,7 @@ struct Cfg {
   static constexpr int XVW = PVW ? BN * 4 : 0;  // offset of sigma_t in the V extras
   static constexpr int XVBYTES = XVW + (SIG ? 16 : 0);
   static constexpr int XBYTES = XKBYTES + XVBYTES;  // per tile in the workspace
-  static constexpr int VROW = PI8 ? BN : 2 * BN;    // bytes of a V^T row
+  static constexpr int VROW = (PI8 || PF8) ? BN : 2 * BN;  // bytes of a V^T row
   static constexpr int VBYTES = D * VROW;
   // INT8 per-head V: the tile is copied straight from the V rows
   // (chunk-major, like K) and the value MFMA reads it through the
@@ -250,8 +260,9 @@ struct Cfg {
 // ------------------------------------------------------------------------
 // Workspace layout (per (b,h), per 128-key tile t):
 //   vt  : V^T of the tile as its LDS image (chunk-major, columns in the lane
-//         key order): INT8 codes (1 byte) or bf16 values (2 bytes: E4M3
-//         codes, exact MX values, or the unquantized V)
+//         key order): INT8 or per-token E4M3 codes (1 byte) or bf16 values
+//         (2 bytes: E4M3 codes of V with one scale per tile, exact MX
+//         values, or the unquantized V)
 //   kb  : FP8 / MXFP8 scores: K widened to bf16 as its LDS image (rows past
 //         the end are 0; MXFP8 relative to the row's largest block exponent)
 //   aux : K extras (K scales; MXFP8 row scales 2^(E_row); MXFP4 K block
@@ -290,6 +301,7 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int6
   const int64_t nt = (Skv + BN - 1) / BN;
   const size_t tiles = (size_t)(B * H * nt);
   const bool pi8 = pv == PV_I8H || pv == PV_I8T;
+  const bool pf8 = pv == PV_F8W;
   const bool qimg = qk == QK_F8T || qk == QK_F8C || qk == QK_MX8 || qk == QK_GEN;
   const bool ksc = qk == QK_I8T || qimg;
   const bool pvw = pv == PV_I8T || pv == PV_F8W;
@@ -300,7 +312,7 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int6
   WsLayout l{};
   const bool vrows = pv == PV_I8H;  // V read as rows, no V^T image
   l.vt_off = 0;
-  l.kb_off = up(vrows ? 0 : tiles * D * BN * (pi8 ? 1 : 2));
+  l.kb_off = up(vrows ? 0 : tiles * D * BN * ((pi8 || pf8) ? 1 : 2));
   l.aux_off = l.kb_off + up(qimg ? tiles * BN * D * 2 : 0);
   l.part_off = l.aux_off + up(tiles * (xk + xv));
   const KvSplit sp = kv_split(B, H, Sq, Skv, causal);
@@ -447,12 +459,16 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
   for (int i = threadIdx.x; i < (C::VROWS ? 0 : VCOLS * D); i += 256) {
     const int c = i / D, d = i % D;
     uint32_t w[4];
-    if (C::PI8) {
+    if (C::PI8 || C::PF8) {
+      // one byte per code; E4M3 values: keys in their natural order
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t acc = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc |= (uint32_t)tile[vt_key_i8(16 * c + 4 * q + r)][d] << (8 * r);
+        for (int r = 0; r < 4; ++r) {
+          const int p = 16 * c + 4 * q + r;
+          acc |= (uint32_t)tile[C::PF8 ? p : vt_key_i8(p)][d] << (8 * r);
+        }
         w[q] = acc;
       }
     } else {
@@ -620,18 +636,6 @@ FAQ_DEV void wait_vm(int n) {
     case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
     default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // (never above 12 here)
   }
-}
-
-// Workgroup barrier without a memory fence (a fence would wait for every
-// copy in flight): this wave's LDS reads and writes complete first
-// (lgkmcnt(0)); copies into LDS may stay in flight, their completion being
-// waited for with vmcnt before the barrier that publishes them.  The signal
-// fences keep the compiler from moving memory accesses across it.
-FAQ_DEV void barrier_lds() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Transposing LDS read of bytes (gfx950): within each 16-lane group, lane l
@@ -812,6 +816,7 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   // offsets per step
   const int kop_off = h * (BN * 16) + kslot(qk_row(j)) * 16;  // + ks 2 BN 16 + kb 256
   const int vop_off = h * (D * 16) + j * 16;                  // + kstep 2 D 16 + db 512
+  const int vop8_off = (4 * h * D + j) * 16;                  // E4M3 V^T: + s 2 D 16 + db 512 (+ D 16)
   const int xk_off = G::KBYTES + 256 * h;                     // the lane's keys' K scales (floats)
   const int xv_off = G::VBYTES + 256 * h;                     // their qmax w_j (floats)
   const int xmx_off = G::KBYTES + qk_row(j) * NB + h;         // MXFP4: + 16 kb NB + 2 ks
@@ -1100,31 +1105,48 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
             for (int db = 0; db < DB; ++db) O[db] *= rscale;
           }
           // per-head: 127 p = 2^((s - m) ce + log2 127), s - m exact (integer
-          // scores), so every p of the tile is relative to the tile maximum
-          // with no error growing with |m ce| (the unquantized p also feed
-          // the row sum L).  per-token: p = 1 exactly at the maximum, times
-          // 127 w_j.
+          // scores).  When every row of the wave has |m ce| <= 64 (log2
+          // units: all but extreme score magnitudes) the subtraction folds
+          // into the fma, 2^(s ce + (log2 127 - m ce)): the argument then
+          // carries the roundings of m ce and of that constant, below
+          // 1.2e-5, a relative error of p ~30x under the 2^-12 of a code
+          // near its rounding boundary (and 127 p at the maximum stays
+          // within 1e-5 of 127, whose code it keeps).  Larger |m ce| would
+          // carry ~2^-24 |m ce|, so those waves keep the subtraction.
+          // per-token: p = 1 exactly at the maximum, times 127 w_j, whose
+          // code is decided at the multiplier itself.
           i32x4 P[4];
+          auto probs = [&](auto fused) __attribute__((always_inline)) {
+            const float c127 = kLog2_127 - ms * ce;
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              float4 vm4;
-              if (PV == PV_I8T) vm4 = *reinterpret_cast<const float4*>(xv + 16 * kb + 4 * w);
-              const float vm[4] = {vm4.x, vm4.y, vm4.z, vm4.w};
-              uint32_t word = 0;
+              for (int w = 0; w < 4; ++w) {
+                float4 vm4;
+                if (PV == PV_I8T) vm4 = *reinterpret_cast<const float4*>(xv + 16 * kb + 4 * w);
+                const float vm[4] = {vm4.x, vm4.y, vm4.z, vm4.w};
+                uint32_t word = 0;
 #pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                const float x = S[kb][4 * w + b];
-                float pv = PV == PV_I8H ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_127))
-                                        : __builtin_amdgcn_exp2f((x - ms) * ce);
-                if (b & 1) ls1 += pv; else ls0 += pv;
-                if (PV == PV_I8T) pv *= vm[b];
-                word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
+                for (int b = 0; b < 4; ++b) {
+                  const float x = S[kb][4 * w + b];
+                  float pv;
+                  if (PV == PV_I8H)
+                    pv = decltype(fused)::value ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, c127))
+                                                : __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_127));
+                  else
+                    pv = __builtin_amdgcn_exp2f((x - ms) * ce);
+                  if (b & 1) ls1 += pv; else ls0 += pv;
+                  if (PV == PV_I8T) pv *= vm[b];
+                  word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
+                }
+                P[kb][w] = (int)word;
               }
-              P[kb][w] = (int)word;
             }
-          }
+          };
+          if (PV == PV_I8H && __builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) == 0)
+            probs(std::true_type{});
+          else
+            probs(std::false_type{});
           L += halves_sum(ls0 + ls1) * (PV == PV_I8H ? bt * (1.0f / 127.0f) : bt);
           const float bv = PV == PV_I8H ? bt * vscale_i8 : bt * sig_t * (1.0f / 127.0f);
           // two output blocks at a time: two independent accumulation chains
@@ -1163,9 +1185,13 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
             rscale = live ? fref * rscale * __builtin_amdgcn_rcpf(ft) : rscale;
             fref = live ? ft : fref;
           }
+          // (E4M3 values fold the rescale into the sum of each tile's products)
+          if (!G::PF8) {
 #pragma unroll
-          for (int db = 0; db < DB; ++db) O[db] *= rscale;
+            for (int db = 0; db < DB; ++db) O[db] *= rscale;
+          }
           float sc = 1.0f, isc = 1.0f;
+          i32x8 p8[2];  // E4M3 values: the P codes of the two 64-key k-steps
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             if (G::PMX && (kb & 1) == 0) {
@@ -1187,17 +1213,18 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
                 // one V scale per tile: 448 p = 2^((x - m) ce + log2 448), at
                 // the maximum within an ulp of 448, whose code both roundings
                 // give.  Otherwise p = 1 exactly at the tile maximum: there
-                // 448 w_j can sit on an E4M3 tie (bf16-derived scale ratios
-                // do), and the MX group of the maximum has its amax at a power
-                // of two.  Both are relative to the tile maximum with no error
-                // growing with |m ce| (the unquantized p also feed L).
+                // 448 w_j can sit next to an E4M3 tie, and the MX group of the
+                // maximum has its amax at a power of two.  Both are relative
+                // to the tile maximum with no error growing with |m ce| (the
+                // unquantized p also feed L).
                 pv[t8] = PV == PV_F8C ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_448))
                                       : __builtin_amdgcn_exp2f((x - ms) * ce);
                 if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
               }
               i32x4 pop;
               if (PV == PV_F8W || PV == PV_F8C) {
-                // E4M3 of 448 p w_j (round to nearest even), then its exact bf16 image
+                // E4M3 of 448 p w_j (round to nearest even): the f8f6f4
+                // operand (per-token V), or its exact bf16 image
                 if (PV == PV_F8W) {
                   const float4 v0 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2);
                   const float4 v1 = *reinterpret_cast<const float4*>(xv + 16 * kb + 8 * s2 + 4);
@@ -1208,6 +1235,13 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
                 e0 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], e0, true);
                 int e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4], pv[5], 0, false);
                 e1 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[6], pv[7], e1, true);
+                if (G::PF8) {
+                  // the codes of keys 16 kb + 8 s2 .. + 7 of the lane's half:
+                  // bytes 16 (kb % 2) + 8 s2 .. of k-step kb / 2
+                  p8[kb >> 1][4 * (kb & 1) + 2 * s2] = e0;
+                  p8[kb >> 1][4 * (kb & 1) + 2 * s2 + 1] = e1;
+                  continue;
+                }
                 pop = i32x4{(int)e4m3x2_to_bf16x2<false>((uint32_t)e0), (int)e4m3x2_to_bf16x2<true>((uint32_t)e0),
                             (int)e4m3x2_to_bf16x2<false>((uint32_t)e1), (int)e4m3x2_to_bf16x2<true>((uint32_t)e1)};
               } else if (PV == PV_MX8) {
@@ -1245,6 +1279,32 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
               for (int db = 0; db < DB; ++db)
                 O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     lds_ld<bf16x8>(vop_base + kst * (2 * D * 16) + db * 512), pb, O[db], 0, 0, 0);
+            }
+          }
+          if (G::PF8) {
+            // O^T = rescale O^T + V^T P^T on the f8f6f4 MFMA (E4M3 x E4M3):
+            // each tile's sum starts from zero (the MFMA sums its products
+            // to about 2^-12 of the largest, which enters O linearly) and
+            // is folded into O by one fma per element; two output blocks at
+            // a time keep two independent chains
+            const uint8_t* vop8 = vb + vop8_off;
+#pragma unroll
+            for (int d2 = 0; d2 < DB; d2 += 2) {
+              f32x16 C[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+              for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int dd = 0; dd < 2; ++dd) {
+                  const uint8_t* a = vop8 + (2 * s * D + 32 * (d2 + dd)) * 16;
+                  const uint4 lo = lds_ld<uint4>(a), hi = lds_ld<uint4>(a + D * 16);
+                  const i32x8 va = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                  C[dd] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, p8[s], C[dd], 0, 0, 0, 0, 0, 0);
+                }
+#pragma unroll
+              for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) O[d2 + dd][r] = __builtin_fmaf(O[d2 + dd][r], rscale, C[dd][r]);
             }
           }
           const float lsc = PV == PV_F8C ? (1.0f / 448.0f) : 1.0f;

@@ -268,6 +268,29 @@ __global__ void k_probe_mfma32_fp4(const uint8_t* A, const uint8_t* Bt, const ui
 }
 }  // namespace
 
+namespace {
+// v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands (no block scales): A, Bt
+// [32][64] bytes; lane (i, h) holds bytes 32h .. 32h + 31 of row i of each.
+// The hardware's K numbering of those 32 bytes does not matter as long as
+// A and B use the same one, which this probe checks.
+__global__ void k_probe_mfma32_fp8(const uint8_t* A, const uint8_t* Bt, float* C) {
+  const int l = threadIdx.x, i = l & 31, h = l >> 5;
+  const uint4* pa = reinterpret_cast<const uint4*>(A + i * 64 + 32 * h);
+  const uint4* pb = reinterpret_cast<const uint4*>(Bt + i * 64 + 32 * h);
+  const uint4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+  const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  f32x16 c = {};
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+  for (int r = 0; r < 16; ++r) C[(8 * (r / 4) + 4 * h + r % 4) * 32 + i] = c[r];
+}
+}  // namespace
+
+extern "C" int faq_probe_mfma32_fp8(const uint8_t* A, const uint8_t* Bt, float* C) {
+  k_probe_mfma32_fp8<<<1, 64>>>(A, Bt, C);
+  return (int)hipDeviceSynchronize();
+}
+
 extern "C" int faq_probe_mfma32_bf16(const uint16_t* A, const uint16_t* Bt, float* C) {
   k_probe_mfma32_bf16<<<1, 64>>>(A, Bt, C);
   return (int)hipDeviceSynchronize();

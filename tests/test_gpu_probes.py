@@ -102,6 +102,22 @@ def test_mfma32_i8_layout(lib):
     assert np.array_equal(C.cpu().numpy(), A.astype(np.int64) @ B.astype(np.int64).T)
 
 
+def test_mfma32_fp8_layout(lib):
+    """v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands (the FP8 value product):
+    lane (i, h) holds bytes 32h..32h+31 of row i of A and of B^T, paired
+    byte for byte (whatever K order the hardware gives them), accumulator r
+    is row 8(r/4) + 4h + r%4 of column i.  Values of a narrow exponent range
+    keep every sum exact."""
+    g = np.random.default_rng(24)
+    vals = np.array([0.5, 0.75, 1.0, 1.25, 1.5, 2.0, 2.5, 3.0])
+    A = vals[g.integers(0, 8, (32, 64))] * np.where(g.random((32, 64)) < 0.5, -1.0, 1.0)
+    B = vals[g.integers(0, 8, (32, 64))] * np.where(g.random((32, 64)) < 0.5, -1.0, 1.0)
+    a, b = _d(F.e4m3_encode(A)), _d(F.e4m3_encode(B))
+    C = torch.zeros((32, 32), dtype=torch.float32, device=DEV)
+    assert lib.faq_probe_mfma32_fp8(_p(a), _p(b), _p(C)) == 0
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), A @ B.T)
+
+
 def test_mfma32_fp4_scaled_layout(lib):
     """v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands: lane (i, h) holds
     elements 32h..32h+31 of row i (16 bytes) and that block's E8M0 scale."""
