@@ -75,11 +75,11 @@ def test_static_workspace_matches_workspace_entry(cfg, big, small, mode, causal,
 
 
 def test_static_workspace_too_small_is_refused():
-    # FP8 per-token [1,16,8192,128]: K and V^T images need 64 MiB plus the
-    # per-tile data, more than the array holds
-    qts = _operands(3, (1, 16, 8192, 128), "fp8_token")
+    # FP8 per-token [1,24,8192,128]: the bf16 K image and the V^T codes of
+    # 1536 key tiles need 72 MiB, more than the array holds
+    qts = _operands(3, (1, 24, 8192, 128), "fp8_token")
     assert faq.fa_quant_attention_workspace_bytes(*qts) > _abi.FA_QUANT_STATIC_WORKSPACE_BYTES
-    out = torch.full((1, 16, 8192, 128), 7.0, dtype=torch.float32, device=DEV)
+    out = torch.full((1, 24, 8192, 128), 7.0, dtype=torch.float32, device=DEV)
     with pytest.raises(faq.FaQuantError) as e:
         faq.fa_quant_attention_static_ws(*qts, out=out)
     assert e.value.status == _abi.FAQ_ERR_WORKSPACE
