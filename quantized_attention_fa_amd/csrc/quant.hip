@@ -468,7 +468,7 @@ __global__ __launch_bounds__((fp8_block_threads<D, BT>()), 2) void k_quant_fp8_b
 // every wave has passed the barrier that follows its last read).
 // ------------------------------------------------------------------------
 template <int D, int BT>
-__global__ __launch_bounds__(BT * 2, BT == 128 ? 3 : 2) void k_rot_fp8_block(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(BT * 2, 2) void k_rot_fp8_block(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ rot, RowMap rm, int H,
                                                           int64_t S, int nblk, int nwork,
                                                           uint8_t* __restrict__ codes,
@@ -477,6 +477,11 @@ __global__ __launch_bounds__(BT * 2, BT == 128 ? 3 : 2) void k_rot_fp8_block(con
   constexpr int NW = BT / 32, NT = BT * 2, KK = D / 32, DB = D / 16, RS = D + 8;
   __shared__ uint16_t rt[D * RS];  // R^T, one padded row per output channel
   __shared__ float red[2][NW];
+  // each wave's 32 x D codes on their way to memory: the accumulator gives
+  // a lane 4 consecutive channels of one token, the stores want 16
+  // contiguous bytes per lane (a 128-byte row per 8 lanes)
+  constexpr int CR = D + 16;  // padded code row (bytes)
+  __shared__ __attribute__((aligned(16))) uint8_t cst[NW][32 * CR];
   // R^T: 16-byte loads of R's rows k, each element to row n of rt
   for (int i = threadIdx.x; i < D * D / 8; i += NT) {
     const int k = i / (D / 8), n0 = (i % (D / 8)) * 8;
@@ -553,10 +558,10 @@ __global__ __launch_bounds__(BT * 2, BT == 128 ? 3 : 2) void k_rot_fp8_block(con
 #pragma unroll
     for (int i = 1; i < NW; ++i) m = fmaxf(m, red[slot][i]);
     const float s = scale_from_amax(m, 448.0f);
+    uint8_t* cw = cst[w];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const int64_t tok = tok0 + tb * 16 + l16;
-      if (tok >= S) continue;
       float y[4 * DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -565,10 +570,13 @@ __global__ __launch_bounds__(BT * 2, BT == 128 ? 3 : 2) void k_rot_fp8_block(con
       uint32_t c[DB];
       e4m3_code_words<4 * DB>(y, s, c);
 #pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<uint32_t*>(cw + (tb * 16 + l16) * CR + db * 16 + g * 4) = c[db];
+      if (tok >= S || !dbg) continue;
+#pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int64_t off = (row0 + tok * rm.ss) * D + db * 16 + g * 4;
-        *reinterpret_cast<uint32_t*>(codes + off) = c[db];
-        if (dbg) {
+        {
           // y holds bf16 values: their top halves are the bf16 bits
           const float* yd = y + 4 * db;
           const uint32_t b0 = (__float_as_uint(yd[0]) >> 16) | (__float_as_uint(yd[1]) & 0xffff0000u);
@@ -576,6 +584,15 @@ __global__ __launch_bounds__(BT * 2, BT == 128 ? 3 : 2) void k_rot_fp8_block(con
           *reinterpret_cast<uint2*>(dbg + off) = make_uint2(b0, b1);
         }
       }
+    }
+    // the wave's codes, 16 bytes per lane and store: 32 rows of D / 16
+    // chunks (the LDS writes and reads of one wave are done in order)
+#pragma unroll
+    for (int i = 0; i < 32 * (D / 16) / 64; ++i) {
+      const int c = i * 64 + lane, row = c / (D / 16), ch = c % (D / 16);
+      const uint4 v = *reinterpret_cast<const uint4*>(cw + row * CR + ch * 16);
+      const int64_t tok = tok0 + row;
+      if (tok < S) *reinterpret_cast<uint4*>(codes + (row0 + tok * rm.ss) * D + ch * 16) = v;
     }
     if (threadIdx.x == 0) scales[((int64_t)p.b * H + p.h) * nblk + p.blk] = s;
   };
