@@ -567,31 +567,35 @@ using gptr = const __attribute__((address_space(1))) void*;
 using lptr = __attribute__((address_space(3))) void*;
 
 // One 16-byte global -> LDS copy per lane (lane i of the wave to
-// lds + 16 i).  ASM: the same instruction written out, so that the
-// compiler does not track the copy: its completion is then waited for only
-// where the kernel says so (vmcnt), never before reads of other LDS
-// buffers.  The instruction has no result registers; M0 holds the wave's
-// LDS base.  M0 is a reserved register the compiler does not treat as
-// clobberable, so kernels that copy this way issue no other M0-using
-// instruction: all their LDS copies go through this form (their assembly
-// has no M0 access outside these blocks).
+// lds + 16 i) from base + off, base wave-uniform, off the lane's 32-bit
+// byte offset.  ASM: the same instruction written out in its SGPR-base
+// form (the address is one VGPR), so that the compiler does not track
+// the copy: its completion is then waited for only where the kernel says
+// so (vmcnt), never before reads of other LDS buffers.  The instruction
+// has no result registers; M0 holds the wave's LDS base.  M0 is a
+// reserved register the compiler does not treat as clobberable, so
+// kernels that copy this way issue no other M0-using instruction: all
+// their LDS copies go through this form (their assembly has no M0 access
+// outside these blocks).
 template <bool ASM>
-FAQ_DEV void copy16(const uint8_t* g, uint8_t* lds) {
+FAQ_DEV void copy16(const uint8_t* base, uint32_t off, uint8_t* lds) {
   if (ASM) {
     const uint32_t m = (uint32_t)(uintptr_t)(lptr)lds;
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(m)
+                 : "memory");
   } else {
-    __builtin_amdgcn_global_load_lds((gptr)g, (lptr)lds, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr)(base + off), (lptr)lds, 16, 0, 0);
   }
 }
 
 // Copy NCH 16-byte chunks global -> LDS with NT threads.  The workgroup
 // moves one round of NT chunks per step (one global_load_lds_dwordx4 per
 // wave, 1 KiB); chunk p = NT i + 64 wave + lane lands at lds + 16 p and
-// comes from base + off(i), off being the lane's 32-bit byte offset in
-// round i.
-template <int NCH, int NT, bool ASM = false, class Off>
-FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, Off off) {
+// comes from base + i rstride + loff: loff is the lane's 32-bit byte
+// offset (the same register in every round), rstride a wave-uniform
+// stride added to the scalar base.
+template <int NCH, int NT, bool ASM = false>
+FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, uint32_t loff, uint32_t rstride) {
   // the tile base is a wave-uniform value held in SGPRs; hiding it from the
   // optimizer keeps it from turning every copy into a 64-bit per-lane
   // pointer carried across loop iterations
@@ -600,13 +604,13 @@ FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, Off of
 #pragma unroll
   for (int i = 0; i < ROUNDS; ++i) {
     const int grp = i * NT + wave * 64;
-    copy16<ASM>(base + (uint32_t)off(i), lds + grp * 16);
+    copy16<ASM>(base + (size_t)i * rstride, loff, lds + grp * 16);
   }
   constexpr int REM = NCH - ROUNDS * NT;  // < one round: the first waves take it
   if (REM > 0) {
     const int grp = ROUNDS * NT + wave * 64;
     if (grp < NCH) {
-      if (REM % 64 == 0 || grp + lane < NCH) copy16<ASM>(base + (uint32_t)off(ROUNDS), lds + grp * 16);
+      if (REM % 64 == 0 || grp + lane < NCH) copy16<ASM>(base + (size_t)ROUNDS * rstride, loff, lds + grp * 16);
     }
   }
 }
@@ -661,6 +665,7 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   using G = Cfg<QK, PV, D>;
   constexpr int NWK = PP ? 2 * NW : NW;  // waves per workgroup
   constexpr int NTK = NWK * 64;          // threads per workgroup
+  static_assert(NTK % 256 == 0, "tile copies: an even number of 128-lane columns per round");
   constexpr int BMK = NWK * 32;          // queries per workgroup
   static_assert(!(PP && VDIR), "ping-pong tiles come from the workspace");
   static_assert(!VDIR || (G::PI8 && D == 128), "direct V: int8 codes, D = 128");
@@ -847,19 +852,19 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   // of K row kslot(pw % 128); rows past the end re-read the last row,
   // masked).
   const int pw = wave * 64 + lane;
+  const uint32_t loff_lin = (uint32_t)pw * 16;  // chunk i NTK + pw of a contiguous image
   const int krow = kslot(pw & (BN - 1));
   auto issue_k = [&](int t, uint8_t* kb) {
     if (G::QIMG) {
-      stage<G::KBYTES / 16, NTK, PP || VDIR>(kb, kbase + (int64_t)t * G::KBYTES, wave, lane,
-                                 [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
+      stage<G::KBYTES / 16, NTK, PP || VDIR>(kb, kbase + (int64_t)t * G::KBYTES, wave, lane, loff_lin,
+                                             NTK * 16);
     } else {
       const uint32_t roff = (uint32_t)min(t * BN + krow, Skv - 1) * kstride + (uint32_t)((pw >> 7) * 16);
-      stage<G::KBYTES / 16, NTK, PP || VDIR>(kb, kbase, wave, lane,
-                                 [&](int i) { return roff + (uint32_t)((NTK / 128) * i * 16); });
+      stage<G::KBYTES / 16, NTK, PP || VDIR>(kb, kbase, wave, lane, roff, (NTK / 128) * 16);
     }
     if (G::XKBYTES > 0)
       stage<G::XKBYTES / 16, NTK, PP || VDIR>(kb + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
-                                  [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
+                                              loff_lin, NTK * 16);
   };
   // direct V: thread (cc, g) = (tid / 32, tid % 32) moves the 16 keys of
   // V^T column cc (keys 64 (cc & 1) + 16 (cc >> 1) + r) times channels
@@ -904,19 +909,20 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   const uint32_t vrstride = (uint32_t)(p.vmap.ss * VRB);
   auto issue_v = [&](int t, uint8_t* vb) {
     if (G::VROWS && !VDIR) {
-      // chunk i NTK + pw: column c, slot pw % 128 holding key slot ^ VSWZ (c & 1)
-      stage<G::VBYTES / 16, NTK, PP>(vb, vrows, wave, lane, [&](int i) {
-        const int c = i * (NTK / 128) + (pw >> 7);
-        const int key = (pw & (BN - 1)) ^ (VSWZ * (c & 1));
-        return (uint32_t)min(t * BN + key, Skv - 1) * vrstride + (uint32_t)(c * 16);
-      });
+      // chunk i NTK + pw: column c = i (NTK / 128) + pw / 128, slot pw % 128
+      // holding key slot ^ VSWZ (c & 1) (NTK / 128 is even: c & 1 is the
+      // same in every round)
+      const int c0 = pw >> 7;
+      const int key = (pw & (BN - 1)) ^ (VSWZ * (c0 & 1));
+      stage<G::VBYTES / 16, NTK, PP>(vb, vrows, wave, lane,
+                                     (uint32_t)min(t * BN + key, Skv - 1) * vrstride + (uint32_t)(c0 * 16),
+                                     (NTK / 128) * 16);
     } else {
-      stage<G::VBYTES / 16, NTK, PP>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane,
-                                 [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
+      stage<G::VBYTES / 16, NTK, PP>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane, loff_lin, NTK * 16);
     }
     if (G::XVBYTES > 0)
       stage<G::XVBYTES / 16, NTK, PP>(vb + G::VBYTES, auxbase + (int64_t)t * G::XBYTES + G::XKBYTES, wave, lane,
-                                  [&](int i) { return (uint32_t)((i * NTK + pw) * 16); });
+                                      loff_lin, NTK * 16);
   };
   // copies each tile costs this wave (the wait counts of the ping-pong loop)
   const int kloads = stage_loads<G::KBYTES / 16, NTK>(wave) +
