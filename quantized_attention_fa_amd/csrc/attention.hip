@@ -62,8 +62,8 @@
 // registers and transposed by the kernel (key splits).
 //
 // LDS tiles are chunk-major: 16-byte column c of every row, then column c+1.
-// The 16 lanes that share an LDS cycle read 16 distinct rows of one column,
-// which the row permutation kslot spreads over all 64 banks, and every
+// An operand read takes one column per lane half (distinct rows of it), which
+// runs without bank conflicts (measured on the fixed lane pattern), and every
 // operand address is a per-lane base plus a constant.  In the four-wave
 // kernel the K tile of t+1 is copied (global_load_lds) while P V of tile t
 // runs, and V^T of tile t while the scores of t are computed: two barriers
@@ -99,11 +99,14 @@ constexpr float kLog2_127 = 6.9886846867721655f, kLog2_448 = 8.807354922057604f;
 // key 64 h + 16 kb + r.
 FAQ_DEV int qk_row(int R) { return 64 * ((R >> 2) & 1) + 4 * (R >> 3) + (R & 3); }
 
-// LDS slot of K row `row` within a 16-byte column: rows 64.. swap their
-// 8-row halves, so the 16 rows one LDS cycle reads ({16kb + 0..7} and
-// {64 + 16kb + 0..7}, or the next eight of each) fill 16 distinct bank
-// groups.  An involution that commutes with adding 16 kb.
-FAQ_DEV int kslot(int row) { return row ^ ((row >> 3) & 8); }
+// LDS slot of K row `row` within a 16-byte column: the row itself.  The
+// score MFMA's K operand read (lane j of half h: row qk_row(j) of column h)
+// has no bank conflicts in this order (SQ_LDS_BANK_CONFLICT on the fixed
+// pattern is 0).  Swapping the 8-row halves of rows 64.., which a plain
+// 64 x 4-byte bank model predicts to spread the read over all banks,
+// measures 4 conflict cycles per read: gfx950 maps addresses to banks with
+// more than the low address bits.
+FAQ_DEV int kslot(int row) { return row; }
 
 // Key at column p of a V^T tile.  bf16 P V (32x32x16): k-step 2 kb + s of
 // the tile takes, in lane half h, registers 8 s .. 8 s + 7 of block kb:

@@ -306,3 +306,53 @@ extern "C" int faq_probe_mfma32_fp4(const uint8_t* A, const uint8_t* Bt, const u
   k_probe_mfma32_fp4<<<1, 64>>>(A, Bt, sa, sb, C);
   return (int)hipDeviceSynchronize();
 }
+
+namespace {
+// LDS read pattern: a 16 KiB LDS buffer holds word i = i * 2654435761 (mod
+// 2^32); each of the 64 lanes reads W bytes at byte offset offs[lane],
+// `reps` times (the address is made opaque per repetition, so every
+// repetition issues its own ds_read), and writes the wrapped sum of its
+// words.  Under SQ_INSTS_LDS / SQ_LDS_BANK_CONFLICT each launch gives the
+// bank-conflict cycles of one access pattern.
+struct LdsOffs {
+  int v[64];
+};
+template <int W>
+__global__ void k_probe_lds_read(const LdsOffs offs, int reps, uint32_t* out) {
+  __shared__ __attribute__((aligned(16))) uint32_t buf[4096];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < 4096; i += 64) buf[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  int off = offs.v[lane];
+  uint32_t acc[W / 4] = {};
+  for (int r = 0; r < reps; ++r) {
+    asm volatile("" : "+v"(off));
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(buf) + off;
+    if constexpr (W == 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+    } else if constexpr (W == 8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      acc[0] += v.x; acc[1] += v.y;
+    } else {
+      acc[0] += *reinterpret_cast<const uint32_t*>(p);
+    }
+  }
+  for (int k = 0; k < W / 4; ++k) out[lane * (W / 4) + k] = acc[k];
+}
+}  // namespace
+
+// offs: 64 host ints, multiples of width in [0, 16384 - width]; width 4, 8
+// or 16; reps >= 0; out: 64 * width / 4 device words.  -1 on bad arguments.
+extern "C" int faq_probe_lds_read(const int* offs, int width, int reps, uint32_t* out) {
+  if (!offs || !out || reps < 0 || !(width == 4 || width == 8 || width == 16)) return -1;
+  LdsOffs o;
+  for (int i = 0; i < 64; ++i) {
+    if (offs[i] < 0 || offs[i] > 16384 - width || offs[i] % width) return -1;
+    o.v[i] = offs[i];
+  }
+  if (width == 16) k_probe_lds_read<16><<<1, 64>>>(o, reps, out);
+  else if (width == 8) k_probe_lds_read<8><<<1, 64>>>(o, reps, out);
+  else k_probe_lds_read<4><<<1, 64>>>(o, reps, out);
+  return (int)hipDeviceSynchronize();
+}

@@ -6,12 +6,15 @@ checked against a CPU reference built from the oracle's format tables:
 * the K order of 8-bit f8f6f4 operands (lane group g: bytes 0-15 at K
   16g.., bytes 16-31 at K 64+16g..), which differs from the 4-bit one;
 * the f8f6f4 MFMA sums 8-bit products with limited precision (the reason the
-  FP8 attention runs its products on the bf16 MFMA), the bf16 MFMA does not;
+  FP8 attention runs its score products on the bf16 MFMA), the bf16 MFMA
+  does not;
 * hardware conversions: f32 -> E4M3 (OCP, nearest even), f32 -> E2M1 with a
   power-of-two scale (x / scale, saturating), E4M3 -> bf16 and
   E2M1 * scale -> bf16 (both exact);
 * the lane mapping of the LDS copy (global_load_lds) and of the
-  transposing LDS read of bytes (ds_read_b64_tr_b8).
+  transposing LDS read of bytes (ds_read_b64_tr_b8);
+* LDS reads of fixed lane patterns (the workload the LDS bank-conflict
+  counter is read on).
 """
 
 import ctypes
@@ -252,3 +255,49 @@ def test_lds_transposing_read_layout(lib):
             srcl = 16 * (lane >> 4) + 2 * k + ((lane >> 3) & 1)
             want[lane, k] = src[offs[srcl] + (lane & 7)]
     assert np.array_equal(o, want)
+
+
+def _qk_row(r):
+    return 64 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3)
+
+
+def _kslot(row):
+    return row ^ ((row >> 3) & 8)
+
+
+# Byte offsets per lane of the LDS read patterns (width, offsets).  The
+# K-operand pattern is the one the attention kernel's score MFMA reads: lane
+# half h takes 16-byte column h of a chunk-major tile, lane j of the half K
+# row qk_row(j) in slot kslot(row).
+LDS_PATTERNS = [
+    ("b128_contiguous", 16, [16 * l for l in range(64)]),
+    ("b128_k_operand", 16, [2048 * (l // 32) + 16 * _kslot(_qk_row(l % 32)) for l in range(64)]),
+    ("b128_k_operand_unswizzled", 16, [2048 * (l // 32) + 16 * _qk_row(l % 32) for l in range(64)]),
+    ("b128_stride32", 16, [32 * l for l in range(64)]),
+    ("b128_8lane_groups_1k_apart", 16, [16 * (l % 8) + 1024 * (l // 8) for l in range(64)]),
+    ("b128_broadcast", 16, [0] * 64),
+    ("b64_contiguous", 8, [8 * l for l in range(64)]),
+    ("b32_contiguous", 4, [4 * l for l in range(64)]),
+]
+
+
+def test_lds_read_patterns(lib):
+    """Each pattern's reads return the addressed words (the launches, in this
+    order, are the workload of the LDS bank-conflict counter calibration)."""
+    f = lib.faq_probe_lds_read
+    f.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    reps = 1024
+    words = (np.arange(4096, dtype=np.uint64) * 2654435761) % (1 << 32)
+    for name, width, offs in LDS_PATTERNS:
+        assert all(0 <= o <= 16384 - width and o % width == 0 for o in offs), name
+        out = torch.zeros(64 * width // 4, dtype=torch.int32, device=DEV)
+        arr = (ctypes.c_int * 64)(*offs)
+        assert f(arr, width, reps, _p(out)) == 0, name
+        got = out.cpu().numpy().view(np.uint32).reshape(64, width // 4).astype(np.uint64)
+        want = np.array([[(reps * int(words[o // 4 + k])) % (1 << 32) for k in range(width // 4)] for o in offs],
+                        dtype=np.uint64)
+        assert np.array_equal(got, want), name
+    bad = (ctypes.c_int * 64)(*([8] * 64))
+    out = torch.zeros(256, dtype=torch.int32, device=DEV)
+    assert f(bad, 16, 1, _p(out)) == -1  # misaligned for a 16-byte read
