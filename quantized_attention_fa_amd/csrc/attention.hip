@@ -186,33 +186,44 @@ FAQ_DEV float halves_sum(float x) {
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
+// Code of u under the hardware conversions the value phase uses (E4M3 or
+// unsigned 8-bit, round to nearest even).
+FAQ_DEV uint32_t p_code(float u, bool e4m3) {
+  return e4m3 ? ((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false) & 0xffu)
+              : (__builtin_amdgcn_cvt_pk_u8_f32(u, 0u, 0u) & 0xffu);
+}
+
 // The probability multiplier qmax w_j = qmax s_v,j / sigma_t of a key whose
-// V scale varies along the tile (per-token V), as an fp32 value in the same
-// rounding interval of the code grid (E4M3 for qmax 448, integers for 127)
-// as the exact quotient, so that the tile maximum (p = 1 exactly) takes the
-// code of the exact product.  u is the fp64 quotient (one rounding): an
-// exact tie stays on the tie, and every other quotient of fp32 scales lies
-// at least ~2^-29 (relative) from a boundary, far beyond that rounding.
-// Its fp32 rounding can land on or across the nearest boundary b; it is
-// then moved one ulp off b, to u's side.
+// V scale varies along the tile (per-token V), as an fp32 value that the
+// code grid (E4M3 for qmax 448, integers for 127) rounds like the exact
+// quotient, with room to spare: the tile maximum (p = 1 exactly) must take
+// the code of the exact product even when its p carries the few-ulp error
+// of the fused exponent argument.  u is the fp64 quotient (one rounding):
+// an exact tie stays on the tie, and every other quotient of fp32 scales
+// lies at least ~2^-29 (relative) from a boundary.  A quotient within
+// 2^-15 (relative) of the nearest code boundary b is moved to b (1 +- 2^-15)
+// on its own side; an exact tie to the side of the code round-to-nearest-
+// even gives b.  Other quotients keep their fp32 rounding, which cannot
+// cross b.  Away from the maximum the multiplier then differs from the
+// quotient by at most 2^-15, so a key's code can differ from the exact
+// rule's only if its product lies that close to a boundary.
 FAQ_DEV float p_multiplier(float sv, float sigma, bool e4m3) {
   const double u = (e4m3 ? 448.0 : 127.0) * (double)sv / (double)sigma;
   const float mu = (float)u;
-  float b;
+  float b;  // the code boundary nearest to mu
   if (e4m3) {
-    // E4M3 steps: 2^(e-3) in the binade [2^e, 2^(e+1)) for e >= -6, 2^-9
-    // below; mu / step is exact (a power-of-two scaling)
     int e;
-    (void)__builtin_frexpf(mu, &e);  // mu = f 2^e, f in [0.5, 1)
-    const float step = __builtin_amdgcn_ldexpf(1.0f, max(e - 1, -6) - 3);
+    (void)__builtin_frexpf(mu, &e);
+    const float step = __builtin_amdgcn_ldexpf(1.0f, max(e - 1, -6) - 3);  // E4M3 spacing at mu
     b = (__builtin_rintf(mu / step - 0.5f) + 0.5f) * step;
   } else {
     b = __builtin_rintf(mu - 0.5f) + 0.5f;
   }
   const double d = u - (double)b;
-  if (d == 0.0) return b;
-  if (d > 0.0 && mu <= b) return __uint_as_float(__float_as_uint(b) + 1u);
-  if (d < 0.0 && mu >= b) return __uint_as_float(__float_as_uint(b) - 1u);
+  const float gap = b * 0x1p-15f;
+  if (d == 0.0) return p_code(b - gap, e4m3) == p_code(b, e4m3) ? b - gap : b + gap;
+  if (d > 0.0 && d < (double)gap) return b + gap;
+  if (d < 0.0 && -d < (double)gap) return b - gap;
   return mu;
 }
 
@@ -1122,8 +1133,10 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
           // near its rounding boundary (and 127 p at the maximum stays
           // within 1e-5 of 127, whose code it keeps).  Larger |m ce| would
           // carry ~2^-24 |m ce|, so those waves keep the subtraction.
-          // per-token: p = 1 exactly at the maximum, times 127 w_j, whose
-          // code is decided at the multiplier itself.
+          // per-token: the same fold, 2^(s ce - m ce) times 127 w_j: p at
+          // the maximum within 3e-6 of 1, and the multiplier is kept 2^-15
+          // off every code boundary, so the maximum keeps the exact rule's
+          // code; other waves take p = 1 exactly at the maximum.
           i32x4 P[4];
           auto probs = [&](auto fused) __attribute__((always_inline)) {
             const float c127 = kLog2_127 - ms * ce;
@@ -1143,7 +1156,8 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
                     pv = decltype(fused)::value ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, c127))
                                                 : __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_127));
                   else
-                    pv = __builtin_amdgcn_exp2f((x - ms) * ce);
+                    pv = decltype(fused)::value ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, -ms * ce))
+                                                : __builtin_amdgcn_exp2f((x - ms) * ce);
                   if (b & 1) ls1 += pv; else ls0 += pv;
                   if (PV == PV_I8T) pv *= vm[b];
                   word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
@@ -1152,7 +1166,7 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
               }
             }
           };
-          if (PV == PV_I8H && __builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) == 0)
+          if (__builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) == 0)
             probs(std::true_type{});
           else
             probs(std::false_type{});
@@ -1194,13 +1208,24 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
             rscale = live ? fref * rscale * __builtin_amdgcn_rcpf(ft) : rscale;
             fref = live ? ft : fref;
           }
-          // (E4M3 values fold the rescale into the sum of each tile's products)
-          if (!G::PF8) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) O[db] *= rscale;
-          }
+          for (int db = 0; db < DB; ++db) O[db] *= rscale;
           float sc = 1.0f, isc = 1.0f;
           i32x8 p8[2];  // E4M3 values: the P codes of the two 64-key k-steps
+          // The exponent argument.  (s - m) ce: exactly 0 at the tile
+          // maximum, where p = 1 exactly (the MX group of the maximum then
+          // has its amax at a power of two).  E4M3 values with per-token
+          // scales fold the subtraction when every row of the wave has
+          // |m ce| <= 64 (log2 units): s ce + c0, c0 = -m ce, one
+          // instruction per score.  That argument carries the rounding of
+          // m ce, below 2^-18 absolute: p within 1e-5 (relative) of the
+          // exact value, inside the 2^-12 a code counts as tied near a
+          // boundary, and at the maximum within 2e-6 of 1, which keeps the
+          // code of the multiplier (kept 2^-15 off every boundary).  The
+          // two forms are two copies of the probability loop (E4M3 values
+          // issue their products after it).
+          auto values = [&](auto fused) __attribute__((always_inline)) {
+          const float c0 = -ms * ce;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             if (G::PMX && (kb & 1) == 0) {
@@ -1219,15 +1244,11 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
 #pragma unroll
               for (int t8 = 0; t8 < 8; ++t8) {
                 const float x = S[kb][8 * s2 + t8];
-                // one V scale per tile: 448 p = 2^((x - m) ce + log2 448), at
-                // the maximum within an ulp of 448, whose code both roundings
-                // give.  Otherwise p = 1 exactly at the tile maximum: there
-                // 448 w_j can sit next to an E4M3 tie, and the MX group of the
-                // maximum has its amax at a power of two.  Both are relative
-                // to the tile maximum with no error growing with |m ce| (the
-                // unquantized p also feed L).
-                pv[t8] = PV == PV_F8C ? __builtin_amdgcn_exp2f(__builtin_fmaf(x - ms, ce, kLog2_448))
-                                      : __builtin_amdgcn_exp2f((x - ms) * ce);
+                // 448 p (one V scale per tile) or p
+                float arg;
+                if constexpr (decltype(fused)::value) arg = __builtin_fmaf(x, ce, c0);
+                else arg = PV == PV_F8C ? __builtin_fmaf(x - ms, ce, kLog2_448) : (x - ms) * ce;
+                pv[t8] = __builtin_amdgcn_exp2f(arg);
                 if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
               }
               i32x4 pop;
@@ -1290,31 +1311,30 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
                     lds_ld<bf16x8>(vop_base + kst * (2 * D * 16) + db * 512), pb, O[db], 0, 0, 0);
             }
           }
+          };
+          if constexpr (G::PF8) {
+            if (__builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) == 0) values(std::true_type{});
+            else values(std::false_type{});
+          } else {
+            values(std::false_type{});
+          }
           if (G::PF8) {
-            // O^T = rescale O^T + V^T P^T on the f8f6f4 MFMA (E4M3 x E4M3):
-            // each tile's sum starts from zero (the MFMA sums its products
-            // to about 2^-12 of the largest, which enters O linearly) and
-            // is folded into O by one fma per element; two output blocks at
-            // a time keep two independent chains
+            // O^T += V^T P^T on the f8f6f4 MFMA (E4M3 x E4M3), straight into
+            // the rescaled O: the MFMA adds its accumulator input at fp32
+            // precision and sums its products to about 2^-12 of the largest,
+            // an error that enters O linearly (no code is decided after it).
+            // The DB output blocks are independent chains of two MFMAs each.
             const uint8_t* vop8 = vb + vop8_off;
 #pragma unroll
-            for (int d2 = 0; d2 < DB; d2 += 2) {
-              f32x16 C[2] = {f32x16{}, f32x16{}};
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-              for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int dd = 0; dd < 2; ++dd) {
-                  const uint8_t* a = vop8 + (2 * s * D + 32 * (d2 + dd)) * 16;
-                  const uint4 lo = lds_ld<uint4>(a), hi = lds_ld<uint4>(a + D * 16);
-                  const i32x8 va = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                  C[dd] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, p8[s], C[dd], 0, 0, 0, 0, 0, 0);
-                }
-#pragma unroll
-              for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) O[d2 + dd][r] = __builtin_fmaf(O[d2 + dd][r], rscale, C[dd][r]);
-            }
+              for (int db = 0; db < DB; ++db) {
+                const uint8_t* a = vop8 + (2 * s * D + 32 * db) * 16;
+                const uint4 lo = lds_ld<uint4>(a), hi = lds_ld<uint4>(a + D * 16);
+                const i32x8 va = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, p8[s], O[db], 0, 0, 0, 0, 0, 0);
+              }
           }
           const float lsc = PV == PV_F8C ? (1.0f / 448.0f) : 1.0f;
           L += halves_sum(ls0 + ls1) * (bt * lsc);

@@ -356,3 +356,25 @@ extern "C" int faq_probe_lds_read(const int* offs, int width, int reps, uint32_t
   else k_probe_lds_read<4><<<1, 64>>>(o, reps, out);
   return (int)hipDeviceSynchronize();
 }
+
+namespace {
+// The same MFMA with an accumulator input: C = Cin + A . Bt^T, Cin and C
+// [32][32] floats in the output layout above.
+__global__ void k_probe_mfma32_fp8_acc(const uint8_t* A, const uint8_t* Bt, const float* Cin, float* C) {
+  const int l = threadIdx.x, i = l & 31, h = l >> 5;
+  const uint4* pa = reinterpret_cast<const uint4*>(A + i * 64 + 32 * h);
+  const uint4* pb = reinterpret_cast<const uint4*>(Bt + i * 64 + 32 * h);
+  const uint4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+  const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  f32x16 c;
+  for (int r = 0; r < 16; ++r) c[r] = Cin[(8 * (r / 4) + 4 * h + r % 4) * 32 + i];
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+  for (int r = 0; r < 16; ++r) C[(8 * (r / 4) + 4 * h + r % 4) * 32 + i] = c[r];
+}
+}  // namespace
+
+extern "C" int faq_probe_mfma32_fp8_acc(const uint8_t* A, const uint8_t* Bt, const float* Cin, float* C) {
+  k_probe_mfma32_fp8_acc<<<1, 64>>>(A, Bt, Cin, C);
+  return (int)hipDeviceSynchronize();
+}

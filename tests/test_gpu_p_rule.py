@@ -8,7 +8,11 @@ derived from bf16 amaxes) must take the exact rule's code.
 
 The operands are built by hand: query i and key j share a one-hot channel
 when j = i (mod 128), which gives one dominant key per query and tile with a
-score margin of ~70 (every other p underflows to code 0), so each output is
+score margin of ~70 (every other p underflows to code 0).  In the centered
+variant the dominant score is 0 and the others -70 (query i is -big on
+every channel but its own, which is 0), so |m| is small and the kernel's
+fused exponent argument (p within a few ulps of 1 at the maximum) is the
+one exercised; otherwise m is ~70 nats.  Each output is
 sum_t code(qmax w_j) * sigma_t / qmax * vhat_j / (number of tiles) up to
 fp32 rounding, and any code decided on the wrong side of a midpoint moves it
 by at least 1/16 of a tile's term.  The bar is therefore far tighter than
@@ -106,13 +110,17 @@ def _qtensor(dtype, codes, scales, S):
     return faq.QTensor(cfg, (1, 1, S, D), codes.to(DEV), scales.to(DEV))
 
 
-def _build(qk, vrule, nt, skv, seed):
+def _build(qk, vrule, nt, skv, seed, centered=False):
     """Q [128 queries], K / V [skv keys] codes and scales of one head."""
     g = np.random.default_rng(seed)
     big = 0x7E if qk == "fp8" else 127  # the largest code of the Q / K format
     sq = 1.0 / 16.0 if qk == "fp8" else 1.0 / 4.0
     qc = np.zeros((1, 1, 128, D), np.uint8 if qk == "fp8" else np.int8)
-    qc[0, 0, np.arange(128), np.arange(128)] = big
+    if centered:
+        qc[...] = (0x80 | big) if qk == "fp8" else -big  # -big everywhere ...
+        qc[0, 0, np.arange(128), np.arange(128)] = 0  # ... but the own channel
+    else:
+        qc[0, 0, np.arange(128), np.arange(128)] = big
     kc = np.zeros((1, 1, skv, D), qc.dtype)
     kc[0, 0, np.arange(skv), np.arange(skv) % 128] = big
     sv = _v_scales(vrule, nt, g)[:skv]
@@ -140,14 +148,18 @@ def _build(qk, vrule, nt, skv, seed):
 # kernel for FP8 scores), 16 tiles split the keys (128 queries per head);
 # a ragged last tile leaves some queries without their one-hot key there,
 # so every key of that tile ties at the maximum (p = 1 for all of them).
-CASES = [("fp8", "fp8", 3, 384), ("fp8", "fp8", 16, 2048), ("fp8", "fp8", 4, 428),
-         ("int8", "int8", 3, 384), ("int8", "int8", 16, 2048), ("int8", "int8", 16, 2000),
-         ("fp8", "int8", 16, 2048), ("int8", "fp8", 3, 384)]
+CASES = [("fp8", "fp8", 3, 384, False), ("fp8", "fp8", 16, 2048, False), ("fp8", "fp8", 4, 428, False),
+         ("int8", "int8", 3, 384, False), ("int8", "int8", 16, 2048, False), ("int8", "int8", 16, 2000, False),
+         ("fp8", "int8", 16, 2048, False), ("int8", "fp8", 3, 384, False),
+         ("fp8", "fp8", 3, 384, True), ("fp8", "fp8", 16, 2048, True), ("fp8", "fp8", 4, 428, True),
+         ("int8", "int8", 3, 384, True), ("int8", "int8", 16, 2000, True), ("fp8", "int8", 16, 2048, True),
+         ("int8", "fp8", 3, 384, True)]
 
 
-@pytest.mark.parametrize("qk,vrule,nt,skv", CASES)
-def test_code_of_the_tile_maximum(qk, vrule, nt, skv):
-    tens, (dq, dk, vhat, sv) = _build(qk, vrule, nt, skv, seed=nt * 1000 + skv + (qk == "fp8") * 7 + (vrule == "fp8"))
+@pytest.mark.parametrize("qk,vrule,nt,skv,centered", CASES)
+def test_code_of_the_tile_maximum(qk, vrule, nt, skv, centered):
+    tens, (dq, dk, vhat, sv) = _build(qk, vrule, nt, skv, seed=nt * 1000 + skv + (qk == "fp8") * 7 + (vrule == "fp8"),
+                                      centered=centered)
     # the crafted scales must separate the exact rule from an fp32 multiplier
     m32, ex = _fp32_multiplier_codes(vrule, np.pad(sv[0, 0], (0, nt * 128 - skv)), nt)
     assert (m32 != ex).sum() >= 16

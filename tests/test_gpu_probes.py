@@ -7,7 +7,7 @@ checked against a CPU reference built from the oracle's format tables:
   16g.., bytes 16-31 at K 64+16g..), which differs from the 4-bit one;
 * the f8f6f4 MFMA sums 8-bit products with limited precision (the reason the
   FP8 attention runs its score products on the bf16 MFMA), the bf16 MFMA
-  does not;
+  does not; it adds its accumulator input exactly;
 * hardware conversions: f32 -> E4M3 (OCP, nearest even), f32 -> E2M1 with a
   power-of-two scale (x / scale, saturating), E4M3 -> bf16 and
   E2M1 * scale -> bf16 (both exact);
@@ -181,6 +181,39 @@ def test_mfma_fp8_accumulation_is_truncating(lib):
     C = _f8f6f4(lib, A, Bt, 0, 0)
     exact = 448 + 127 * 2.0 ** -7
     assert C[0, 0] < exact and exact - C[0, 0] < 2.0 ** -4
+
+
+def test_mfma32_fp8_accumulator_input_is_added_exactly(lib):
+    """The 32x32x64 f8f6f4 MFMA adds its accumulator input at fp32
+    precision, not aligned with the products: a large C plus small products
+    comes back as the correctly rounded sum (the FP8 value product
+    accumulates into the running output this way)."""
+    f = lib.faq_probe_mfma32_fp8_acc
+    one = int(F.e4m3_encode(1.0))
+    for cin, pv, n in [(2.0 ** 20, 1.0, 64), (2.0 ** 20, 1.0, 1), (1024.0, 2.0 ** -7, 64), (1024.0, 2.0 ** -7, 1),
+                       (-(2.0 ** 20), 1.0, 64), (2.0 ** 12, 2.0 ** -3, 64)]:
+        A = np.zeros((32, 64), np.uint8)
+        A[:, :n] = int(F.e4m3_encode(pv))
+        Bt = np.full((32, 64), one, np.uint8)
+        keep = [_d(A), _d(Bt), _d(np.full((32, 32), cin, np.float32))]
+        C = torch.zeros((32, 32), dtype=torch.float32, device=DEV)
+        assert f(*[_p(t) for t in keep], _p(C)) == 0
+        got = C.cpu().numpy().astype(np.float64)
+        assert np.all(got == float(np.float32(cin + n * pv))), (cin, pv, n, got[0, 0])
+
+
+def test_cvt_f32_to_u8_rounds_to_nearest_even(lib):
+    """v_cvt_pk_u8_f32 on [0, 128) (the INT8 probability codes): round to
+    nearest, ties to even (the value phase takes a tie's side from this
+    conversion)."""
+    x = np.concatenate([np.arange(0, 127) + 0.5, np.arange(0, 127) + 0.25, np.arange(0, 127) + 0.75,
+                        np.nextafter(np.arange(0, 127) + 0.5, 0), np.nextafter(np.arange(0, 127) + 0.5, 1e9),
+                        [0.0, 127.0]]).astype(np.float32)
+    xd = _d(x)
+    out = torch.zeros(x.size, dtype=torch.uint8, device=DEV)
+    assert lib.faq_probe_cvt_u8(_p(xd), x.size, _p(out)) == 0
+    want = np.rint(x.astype(np.float64)).astype(np.uint8)
+    assert np.array_equal(out.cpu().numpy(), want)
 
 
 def test_cvt_f32_to_e4m3_and_fp4(lib):
