@@ -1070,7 +1070,7 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
 #pragma unroll
             for (int kb = 2 * g2; kb < 2 * g2 + 2; ++kb)
 #pragma unroll
-              for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(S[kb][r], S[kb][r + 1]));
+              for (int r = 0; r < 16; r += 2) x = fmaxf(fmaxf(x, S[kb][r]), S[kb][r + 1]);  // v_max3
             gmax[g2] = x;  // MX probabilities: the lane's 32-key group maxima
           }
           m = fmaxf(gmax[0], gmax[1]);
