@@ -288,6 +288,31 @@ def _amd_smi_clocks(proc):
         return {"error": f"amd-smi: {type(e).__name__}: {e}"[:200]}
 
 
+def copy_reference(dev, nbytes, flush, flush_out, reps=10):
+    """HBM rate of a plain device-to-device copy moving `nbytes` in total
+    (nbytes / 2 read, nbytes / 2 written), timed like the quantize step
+    (cache flushed before each copy): the practical ceiling the quantize
+    fraction is read against on this machine."""
+    import torch
+    n = max(nbytes // 2, 1)
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    st = torch.cuda.current_stream()
+    ms = []
+    for _ in range(reps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=flush_out)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        dst.copy_(src)
+        b.record(st)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    return 2 * n / (ms[len(ms) // 2] * 1e-3) / 1e9
+
+
 def clocks_under_load(fn, ms_per_call, seconds=4.0):
     """GPU clocks read while about `seconds` of `fn` calls are queued on the
     GPU (an idle GPU drops its clocks, so they are sampled under the load
@@ -439,7 +464,9 @@ def main():
         "roofline": roofline,
         "quantize": ({"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(q_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": qbytes,
-                      "ms_per_step": round(mean(q_ms), 4)} if qbytes else None),
+                      "ms_per_step": round(mean(q_ms), 4),
+                      "copy_same_bytes_gbs": round(copy_reference(dev, qbytes, flush, flush_out if flush is not None
+                                                                  else None), 1)} if qbytes else None),
         "timing": {"method": "hip events on the compute stream, per step", "mean_step_ms": round(ms_step, 4),
                    "median_step_ms": round(median(step_ms), 4), "min_step_ms": round(min(step_ms), 4),
                    "attention_median_ms": round(median(a_ms), 4), "attention_min_ms": round(min(a_ms), 4),

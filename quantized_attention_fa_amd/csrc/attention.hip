@@ -1025,7 +1025,7 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-              for (int r = 0; r < 16; r += 2) mi = max(mi, max(SI[kb][r], SI[kb][r + 1]));
+              for (int r = 0; r < 16; r += 2) mi = max(max(mi, SI[kb][r]), SI[kb][r + 1]);  // v_max3_i32
             m = (float)mi;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)

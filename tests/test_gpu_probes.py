@@ -294,18 +294,20 @@ def _qk_row(r):
     return 64 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3)
 
 
-def _kslot(row):
+def _half_swap(row):
     return row ^ ((row >> 3) & 8)
 
 
 # Byte offsets per lane of the LDS read patterns (width, offsets).  The
 # K-operand pattern is the one the attention kernel's score MFMA reads: lane
 # half h takes 16-byte column h of a chunk-major tile, lane j of the half K
-# row qk_row(j) in slot kslot(row).
+# row qk_row(j) (plain row order); the half-swapped variant puts rows 64..
+# in the other 8-row half, which a plain 64 x 4-byte bank model predicts to
+# be the conflict-free one.
 LDS_PATTERNS = [
     ("b128_contiguous", 16, [16 * l for l in range(64)]),
-    ("b128_k_operand", 16, [2048 * (l // 32) + 16 * _kslot(_qk_row(l % 32)) for l in range(64)]),
-    ("b128_k_operand_unswizzled", 16, [2048 * (l // 32) + 16 * _qk_row(l % 32) for l in range(64)]),
+    ("b128_k_operand_half_swapped", 16, [2048 * (l // 32) + 16 * _half_swap(_qk_row(l % 32)) for l in range(64)]),
+    ("b128_k_operand", 16, [2048 * (l // 32) + 16 * _qk_row(l % 32) for l in range(64)]),
     ("b128_stride32", 16, [32 * l for l in range(64)]),
     ("b128_8lane_groups_1k_apart", 16, [16 * (l % 8) + 1024 * (l // 8) for l in range(64)]),
     ("b128_broadcast", 16, [0] * 64),
