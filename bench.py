@@ -252,12 +252,18 @@ def cpu_baseline(w, budget_s=20.0):
 
 
 def source_digest():
-    """sha256 of the attention kernel source: HBM traffic counted by the
-    profiler is only reported for the kernel it was counted on."""
+    """sha256 of the attention kernel source with its comments and
+    whitespace removed: HBM traffic counted by the profiler is only reported
+    for the kernel code it was counted on."""
     import hashlib
+    import re
     src = os.path.join(ROOT, "quantized_attention_fa_amd", "csrc", "attention.hip")
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(src, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+    text = re.sub(r"//[^\n]*", " ", text)                # line comments
+    code = " ".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def recorded_traffic(workload):

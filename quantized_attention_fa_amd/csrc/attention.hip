@@ -25,7 +25,12 @@
 //   values, by V's configuration, with the probabilities P quantized to
 //   V's type
 //     INT8            int8 P, v_mfma_i32_32x32x32_i8, exact int32 sums
-//     FP8 E4M3        E4M3 P on the bf16 MFMA (exact images)
+//     FP8 E4M3        per-token V: E4M3 P times the E4M3 V codes on
+//                     v_mfma_scale_f32_32x32x64_f8f6f4 (unscaled),
+//                     accumulating into O (the instruction adds its
+//                     accumulator input exactly; the alignment error of its
+//                     products enters O linearly); V with one scale per
+//                     tile: E4M3 P on the bf16 MFMA (exact images)
 //     MXFP4 / MXFP8   MX-quantized P on the bf16 MFMA, V exact in bf16 (V's
 //                     exponents run along D, not along the keys the MFMA
 //                     sums over)
