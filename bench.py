@@ -281,12 +281,11 @@ def recorded_traffic(workload):
     return rec.get("attention_bytes_per_launch")
 
 
-def _amd_smi_clocks(proc):
+def _amd_smi_clocks(text):
     """Shader clocks of the 8 XCDs (gfx_0..gfx_7) and the memory clock, MHz,
-    from a finished `amd-smi metric -c --json` process."""
+    from the output of `amd-smi metric -c --json`."""
     try:
-        out, _ = proc.communicate(timeout=30)
-        clk = json.loads(out)["gpu_data"][0]["clock"]
+        clk = json.loads(text)["gpu_data"][0]["clock"]
         gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
         return {"sclk_mhz_per_xcd": gfx, "sclk_mhz_mean": round(sum(gfx) / len(gfx), 1),
                 "mclk_mhz": clk["mem_0"]["clk"]["value"]}
@@ -319,26 +318,52 @@ def copy_reference(dev, nbytes, flush, flush_out, reps=10):
     return 2 * n / (ms[len(ms) // 2] * 1e-3) / 1e9
 
 
-def clocks_under_load(fn, ms_per_call, seconds=4.0):
-    """GPU clocks read while about `seconds` of `fn` calls are queued on the
-    GPU (an idle GPU drops its clocks, so they are sampled under the load
-    the timed steps put on it)."""
+def clocks_under_load(fn, ms_per_call, warm_s=1.0, limit_s=30.0):
+    """GPU clocks read while `fn` calls keep the GPU busy (an idle GPU drops
+    its clocks within milliseconds).  The calls are issued for `warm_s`
+    seconds first, then for as long as amd-smi runs, never more than about
+    40 ms of work ahead of the GPU: a deep queue would leave the host done
+    (and amd-smi reading an idle GPU) while the work still drains."""
+    import collections
     import subprocess
+    import tempfile
     import torch
-    n = max(10, int(seconds * 1e3 / max(ms_per_call, 1e-3)))
-    n = min(n, 20000)
+    depth = max(2, int(40.0 / max(ms_per_call, 1e-3)) + 1)
+    pending = collections.deque()
+    calls = 0
+
+    def pump(done):
+        nonlocal calls
+        while not done():
+            fn()
+            calls += 1
+            e = torch.cuda.Event()
+            e.record(torch.cuda.current_stream())
+            pending.append(e)
+            if len(pending) > depth:
+                pending.popleft().synchronize()
+
     torch.cuda.synchronize()
-    for _ in range(n):
-        fn()
-    try:
-        proc = subprocess.Popen(["amd-smi", "metric", "-g", "0", "-c", "--json"], stdout=subprocess.PIPE,
-                                stderr=subprocess.DEVNULL, text=True)
-    except Exception as e:  # pragma: no cover
+    t0 = time.perf_counter()
+    pump(lambda: time.perf_counter() - t0 > warm_s)
+    with tempfile.TemporaryFile(mode="w+") as out:
+        try:
+            proc = subprocess.Popen(["amd-smi", "metric", "-g", "0", "-c", "--json"], stdout=out,
+                                    stderr=subprocess.DEVNULL, text=True)
+        except Exception as e:  # pragma: no cover - depends on the host's tools
+            torch.cuda.synchronize()
+            return {"error": f"amd-smi: {type(e).__name__}"}
+        t1 = time.perf_counter()
+        pump(lambda: proc.poll() is not None or time.perf_counter() - t1 > limit_s)
         torch.cuda.synchronize()
-        return {"error": f"amd-smi: {type(e).__name__}"}
-    res = _amd_smi_clocks(proc)
-    torch.cuda.synchronize()
-    res["calls_queued"] = n
+        if proc.poll() is None:  # pragma: no cover
+            proc.kill()
+            proc.wait()
+            return {"error": "amd-smi did not finish", "calls_issued": calls}
+        out.seek(0)
+        res = _amd_smi_clocks(out.read())
+    res["calls_issued"] = calls
+    res["seconds_sampled_under"] = round(time.perf_counter() - t1, 2)
     return res
 
 

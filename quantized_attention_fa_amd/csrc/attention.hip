@@ -1219,16 +1219,21 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
           i32x8 p8[2];  // E4M3 values: the P codes of the two 64-key k-steps
           // The exponent argument.  (s - m) ce: exactly 0 at the tile
           // maximum, where p = 1 exactly (the MX group of the maximum then
-          // has its amax at a power of two).  E4M3 values with per-token
-          // scales fold the subtraction when every row of the wave has
-          // |m ce| <= 64 (log2 units): s ce + c0, c0 = -m ce, one
+          // has its amax at a power of two, which MX values need).  The
+          // other value modes fold the subtraction when every row of the
+          // wave has |m ce| <= 64 (log2 units): s ce + c0, c0 = -m ce, one
           // instruction per score.  That argument carries the rounding of
           // m ce, below 2^-18 absolute: p within 1e-5 (relative) of the
           // exact value, inside the 2^-12 a code counts as tied near a
           // boundary, and at the maximum within 2e-6 of 1, which keeps the
-          // code of the multiplier (kept 2^-15 off every boundary).  The
-          // two forms are two copies of the probability loop (E4M3 values
-          // issue their products after it).
+          // code there: the per-token multiplier is kept 2^-15 off every
+          // boundary, and 448 p (one V scale per tile) or bf16(p) stays
+          // 448 or 1.  Other waves take (s - m) ce: per-token E4M3 values
+          // through a second copy of the probability loop (their products
+          // come after it); one-scale and unquantized values by shifting S
+          // in place and folding with m = 0, the same roundings as the
+          // unfused form, since their products are interleaved with the
+          // probabilities and a second copy of that loop spills.
           auto values = [&](auto fused) __attribute__((always_inline)) {
           const float c0 = -ms * ce;
 #pragma unroll
@@ -1251,7 +1256,7 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
                 const float x = S[kb][8 * s2 + t8];
                 // 448 p (one V scale per tile) or p
                 float arg;
-                if constexpr (decltype(fused)::value) arg = __builtin_fmaf(x, ce, c0);
+                if constexpr (decltype(fused)::value) arg = __builtin_fmaf(x, ce, PV == PV_F8C ? c0 + kLog2_448 : c0);
                 else arg = PV == PV_F8C ? __builtin_fmaf(x - ms, ce, kLog2_448) : (x - ms) * ce;
                 pv[t8] = __builtin_amdgcn_exp2f(arg);
                 if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
@@ -1320,6 +1325,16 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
           if constexpr (G::PF8) {
             if (__builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) == 0) values(std::true_type{});
             else values(std::false_type{});
+          } else if constexpr (!G::PMX) {
+            // rare: a wave with a large |m ce| shifts its scores instead
+            if (__builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) != 0) {
+#pragma unroll
+              for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) S[kb][r] -= ms;
+              ms = 0.0f;
+            }
+            values(std::true_type{});
           } else {
             values(std::false_type{});
           }
