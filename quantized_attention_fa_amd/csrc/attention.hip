@@ -1218,22 +1218,21 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
           float sc = 1.0f, isc = 1.0f;
           i32x8 p8[2];  // E4M3 values: the P codes of the two 64-key k-steps
           // The exponent argument.  (s - m) ce: exactly 0 at the tile
-          // maximum, where p = 1 exactly (the MX group of the maximum then
-          // has its amax at a power of two, which MX values need).  The
-          // other value modes fold the subtraction when every row of the
-          // wave has |m ce| <= 64 (log2 units): s ce + c0, c0 = -m ce, one
-          // instruction per score.  That argument carries the rounding of
+          // maximum, where p = 1 exactly.  The value modes fold the
+          // subtraction when every row of the wave has |m ce| <= 64 (log2
+          // units): s ce + c0, c0 = -m ce, one instruction per score.  That argument carries the rounding of
           // m ce, below 2^-18 absolute: p within 1e-5 (relative) of the
           // exact value, inside the 2^-12 a code counts as tied near a
           // boundary, and at the maximum within 2e-6 of 1, which keeps the
           // code there: the per-token multiplier is kept 2^-15 off every
-          // boundary, and 448 p (one V scale per tile) or bf16(p) stays
-          // 448 or 1.  Other waves take (s - m) ce: per-token E4M3 values
-          // through a second copy of the probability loop (their products
-          // come after it); one-scale and unquantized values by shifting S
-          // in place and folding with m = 0, the same roundings as the
-          // unfused form, since their products are interleaved with the
-          // probabilities and a second copy of that loop spills.
+          // boundary, 448 p (one V scale per tile) and bf16(p) stay 448 and
+          // 1, and an MX group takes its exponent from the unfused form.
+          // Other waves take (s - m) ce: per-token E4M3 values through a
+          // second copy of the probability loop (their products come after
+          // it); the other modes by shifting S in place and folding with
+          // m = 0, the same roundings as the unfused form, since their
+          // products are interleaved with the probabilities and a second
+          // copy of that loop spills.
           auto values = [&](auto fused) __attribute__((always_inline)) {
           const float c0 = -ms * ce;
 #pragma unroll
@@ -1241,8 +1240,11 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
             if (G::PMX && (kb & 1) == 0) {
               // this lane's keys of blocks kb, kb + 1 are one MX group:
               // group max -> shared exponent; p -> E2M1 / E4M3 of p / 2^E,
-              // times 2^E, exact in bf16.  The group's largest p is the same
-              // function of the group's largest score.
+              // times 2^E, exact in bf16.  The exponent comes from the
+              // unfused p of the group's largest score (exactly 1 at the
+              // tile maximum); a fused p lies within 1e-5 of it, so the
+              // group maximum still lands at [4, 8) 2^E (E2M1, saturating
+              // to 6) or [256, 512) 2^E (E4M3, 448) and keeps its code.
               const float pmax = __builtin_amdgcn_exp2f((gmax[kb >> 1] - ms) * ce);
               const int E = PV == PV_MX4 ? mx_exponent(pmax) : mx_exponent<8>(pmax);
               sc = E > -127 ? pow2f(E) : 1.0f;
@@ -1325,18 +1327,21 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
           if constexpr (G::PF8) {
             if (__builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) == 0) values(std::true_type{});
             else values(std::false_type{});
-          } else if constexpr (!G::PMX) {
-            // rare: a wave with a large |m ce| shifts its scores instead
+          } else {
+            // rare: a wave with a large |m ce| shifts its scores (and MX
+            // group maxima) instead
             if (__builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) != 0) {
 #pragma unroll
               for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) S[kb][r] -= ms;
+              if (G::PMX) {
+                gmax[0] -= ms;
+                gmax[1] -= ms;
+              }
               ms = 0.0f;
             }
             values(std::true_type{});
-          } else {
-            values(std::false_type{});
           }
           if (G::PF8) {
             // O^T += V^T P^T on the f8f6f4 MFMA (E4M3 x E4M3), straight into
