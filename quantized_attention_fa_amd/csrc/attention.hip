@@ -1152,7 +1152,7 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
                 float4 vm4;
                 if (PV == PV_I8T) vm4 = *reinterpret_cast<const float4*>(xv + 16 * kb + 4 * w);
                 const float vm[4] = {vm4.x, vm4.y, vm4.z, vm4.w};
-                uint32_t word = 0;
+                uint32_t word = 0, u[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                   const float x = S[kb][4 * w + b];
@@ -1164,8 +1164,20 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
                     pv = decltype(fused)::value ? __builtin_amdgcn_exp2f(__builtin_fmaf(x, ce, -ms * ce))
                                                 : __builtin_amdgcn_exp2f((x - ms) * ce);
                   if (b & 1) ls1 += pv; else ls0 += pv;
-                  if (PV == PV_I8T) pv *= vm[b];
-                  word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p w_j)
+                  if (PV == PV_I8T) {
+                    // 2^23 + rne(127 p w_j) (ulp 1 in [2^23, 2^24), one
+                    // rounding of the exact product, ties to even): the
+                    // code is the low byte (0 <= 127 p w_j < 127.5)
+                    u[b] = __builtin_bit_cast(uint32_t, __builtin_fmaf(pv, vm[b], 0x1p23f));
+                  } else {
+                    word = __builtin_amdgcn_cvt_pk_u8_f32(pv, (uint32_t)b, word);  // rne(127 p)
+                  }
+                }
+                if (PV == PV_I8T) {
+                  // bytes 0 of u0..u3 -> bytes 0..3: two pairs, then the pairs
+                  const uint32_t lo = __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u);
+                  const uint32_t hi = __builtin_amdgcn_perm(u[3], u[2], 0x0c0c0400u);
+                  word = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                 }
                 P[kb][w] = (int)word;
               }
