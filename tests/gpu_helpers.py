@@ -9,6 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 import quantized_attention_fa_amd as faq
 from oracle import attention as OA
@@ -122,6 +123,14 @@ def _oracle_threads():
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
+def oracle_pool_map(fn, items):
+    """map over a thread pool of _oracle_threads() workers, with the BLAS
+    library held to one thread meanwhile: one multithreaded BLAS call per
+    worker would run workers x cores threads (measured 12x slower)."""
+    with threadpool_limits(1), ThreadPoolExecutor(_oracle_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
 def oracle_attention(run: GpuRun, rows=None, causal=None, sm_scale=None):
     """The oracle on the GPU run's codes, one (b, h) head per task on a
     thread pool; returns (O, T, n_tie) as oracle.attention does."""
@@ -138,8 +147,7 @@ def oracle_attention(run: GpuRun, rows=None, causal=None, sm_scale=None):
         return OA.attention(q[sl], k[sl], v[sl], rule, v_scale=None if vs is None else vs[sl], causal=causal,
                             rows=rows, allowance=True, sm_scale=sm_scale)
 
-    with ThreadPoolExecutor(_oracle_threads()) as ex:
-        parts = list(ex.map(one, range(B * H)))
+    parts = oracle_pool_map(one, range(B * H))
     R = parts[0][0].shape[2]
     D = q.shape[3]
     o = np.concatenate([p[0] for p in parts], axis=0).reshape(B, H, R, D)

@@ -2,9 +2,6 @@
 the oracle, on small multi-tile shapes with ragged tails, on hand-built edge
 values, and at the full workload sizes (sampled rows / blocks there)."""
 
-import os
-from concurrent.futures import ThreadPoolExecutor
-
 import numpy as np
 import pytest
 import torch
@@ -13,7 +10,7 @@ import quantized_attention_fa_amd as faq
 from oracle import formats as F
 from oracle import quantize as OQ
 from synth import CONFIGS, make_inputs
-from gpu_helpers import DEV, GpuRun, _parity_log, small_workload
+from gpu_helpers import DEV, GpuRun, _parity_log, oracle_pool_map, small_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -376,8 +373,7 @@ def _rows_check(run, br):
         if s is not None:
             assert np.array_equal(scales_gpu[b:b + 1, h:h + 1], s), (run.mode, br, b, h)
 
-    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
-        list(ex.map(one, range(B * H)))
+    oracle_pool_map(one, range(B * H))
 
 
 def _calib_check(run):
@@ -418,8 +414,7 @@ def _blocks_check(run, br):
         assert np.array_equal(scales[b:b + 1, h:h + 1], s), (b, h)
         return eq
 
-    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
-        eqs = list(ex.map(one, range(B * H)))
+    eqs = oracle_pool_map(one, range(B * H))
     if br < 2:
         _parity_log({"case": f"cfg{w.cfg} branch {br} rotated, all heads", "equal_fraction_min": min(eqs),
                      "equal_fraction_mean": float(np.mean(eqs))})
