@@ -188,7 +188,13 @@ size_t fa_quant_attention_workspace_bytes(const faq_qtensor* q, const faq_qtenso
                kernels specialised to that pair (INT8 scores on INT8 MFMA,
                MXFP4 on the scaled f8f6f4 MFMA); any other mix widens Q and
                K exactly to bf16 (MX rows relative to their largest block
-               exponent) and scores on bf16 MFMA.  B, H, D equal; k and v
+               exponent) and scores on bf16 MFMA.  With Q, K and V all
+               MXFP4 the value product also runs on the scaled f8f6f4 MFMA:
+               V is re-expressed per (32-key group, 32-channel block) as
+               E5M2 under one E8M0 scale, exact while a group's block
+               exponents span at most 57; an element more than 57 binades
+               below its group's largest exponent (so below 2^-55 of that
+               group's largest |V|) is left out.  B, H, D equal; k and v
                share S.  The rows of one head of k and of v must span
                less than 4 GiB (in BSND they lie H rows apart), else
                FAQ_ERR_UNSUPPORTED.

@@ -31,9 +31,16 @@
 //                     accumulator input exactly; the alignment error of its
 //                     products enters O linearly); V with one scale per
 //                     tile: E4M3 P on the bf16 MFMA (exact images)
-//     MXFP4 / MXFP8   MX-quantized P on the bf16 MFMA, V exact in bf16 (V's
-//                     exponents run along D, not along the keys the MFMA
-//                     sums over)
+//     MXFP4           with MXFP4 Q and K: E2M1 P with its 32-key group
+//                     exponents as the B scales of the block-scaled f8f6f4
+//                     MFMA, times V re-expressed per (32-key group, 32-channel
+//                     block) as E5M2 under one E8M0 A scale (V's own
+//                     exponents run along D, the MFMA's scales along keys);
+//                     exact for exponent spreads up to 57 within a group (a
+//                     second image and product past 28); the instruction
+//                     sums the products to about 2^-12 of the largest
+//     MXFP4 / MXFP8   otherwise: MX-quantized P on the bf16 MFMA, V exact in
+//                     bf16
 //     unquantized     bf16 P on the bf16 MFMA
 // The output is dequantized to bf16 (or fp32) ("量化" page, FA量化 / FP8
 // Attention).
@@ -249,6 +256,12 @@ struct Cfg {
   // outlier channels carry outputs of tens; those keep the bf16 product.
   static constexpr bool PF8 = PV == PV_F8W;
   static constexpr bool PMX = PV == PV_MX4 || PV == PV_MX8;  // MX probability groups
+  // MXFP4 Q, K and V: the value product on the block-scaled f8f6f4 MFMA,
+  // E2M1 P (its 32-key group exponents as B scales) times V re-expressed
+  // per (32-key group, 32-channel block) as E5M2 with one E8M0 A scale.
+  // A tile whose V exponents spread too far for one image takes a second
+  // one and a second product (a per-tile flag).
+  static constexpr bool PF4 = QK == QK_MX4 && PV == PV_MX4;
   static constexpr bool PVW = PV == PV_I8T || PV == PV_F8W;  // per-key V scale folded into P
   static constexpr bool SIG = PVW || PV == PV_F8C;            // sigma_t per tile
   static constexpr int KROW = QI8 ? D : (QBF ? 2 * D : D / 2);  // bytes of a K row in LDS
@@ -260,10 +273,14 @@ struct Cfg {
   // 16 bytes), which the value phase reads after the K buffer is refilled
   static constexpr int XKBYTES = QK == QK_MX4 ? BN * NB : (KSC ? BN * 4 : 0);
   static constexpr int XVW = PVW ? BN * 4 : 0;  // offset of sigma_t in the V extras
-  static constexpr int XVBYTES = XVW + (SIG ? 16 : 0);
+  // MXFP4 values: 16 bytes of scales of the first E5M2 image (byte 4 g + b:
+  // key group g, channel block b), 16 of the second, then the tile's flag
+  // word (nonzero: the second image is used)
+  static constexpr int XVBYTES = PF4 ? 48 : XVW + (SIG ? 16 : 0);
   static constexpr int XBYTES = XKBYTES + XVBYTES;  // per tile in the workspace
   static constexpr int VROW = (PI8 || PF8) ? BN : 2 * BN;  // bytes of a V^T row
   static constexpr int VBYTES = D * VROW;
+  static constexpr int VF4BYTES = D * BN;  // MXFP4 values: one E5M2 image (half of the slot)
   // INT8 per-head V: the tile is copied straight from the V rows
   // (chunk-major, like K) and the value MFMA reads it through the
   // transposing LDS reads, so no V^T image is made.  (For bf16 V the same
@@ -281,14 +298,17 @@ struct Cfg {
 //   vt  : V^T of the tile as its LDS image (chunk-major, columns in the lane
 //         key order): INT8 or per-token E4M3 codes (1 byte) or bf16 values
 //         (2 bytes: E4M3 codes of V with one scale per tile, exact MX
-//         values, or the unquantized V)
+//         values, or the unquantized V).  MXFP4 Q, K and V: the E5M2 image
+//         (1 byte, natural key order) in the first half of a 2-byte slot,
+//         a flagged tile's second E5M2 image in the other half
 //   kb  : FP8 / MXFP8 scores: K widened to bf16 as its LDS image (rows past
 //         the end are 0; MXFP8 relative to the row's largest block exponent)
 //   aux : K extras (K scales; MXFP8 row scales 2^(E_row); MXFP4 K block
 //         exponents, 128 rows x D/32 bytes, 127 past the end), then V
 //         extras (the multipliers qmax w_j; sigma_t = max over the tile's
 //         keys of s_v,j for FP8 / INT8 per-token and FP8 with one V scale
-//         per tile)
+//         per tile; MXFP4 values: the E5M2 images' E8M0 scales and the
+//         tile's flag)
 // ------------------------------------------------------------------------
 struct WsLayout {
   size_t vt_off, kb_off, aux_off, part_off, total;
@@ -325,8 +345,9 @@ inline WsLayout ws_layout(int qk, int pv, int64_t B, int64_t H, int64_t Sq, int6
   const bool ksc = qk == QK_I8T || qimg;
   const bool pvw = pv == PV_I8T || pv == PV_F8W;
   const bool sig = pvw || pv == PV_F8C;
+  const bool pf4 = qk == QK_MX4 && pv == PV_MX4;
   const size_t xk = qk == QK_MX4 ? BN * (D / 32) : (ksc ? BN * 4 : 0);
-  const size_t xv = (pvw ? BN * 4 : 0) + (sig ? 16 : 0);
+  const size_t xv = pf4 ? 48 : (pvw ? BN * 4 : 0) + (sig ? 16 : 0);
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WsLayout l{};
   const bool vrows = pv == PV_I8H;  // V read as rows, no V^T image
@@ -379,6 +400,12 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
   __shared__ uint8_t tile[BN][VR + 4];
   __shared__ uint8_t vex[VEX ? BN : 1][NB];
   __shared__ float red[4];
+  // MXFP4 values: per (row, channel block) the exponent byte where the
+  // block holds a nonzero code (else 0 / 255), the scales of the two E5M2
+  // images, and the tile's flag (second image used)
+  __shared__ uint8_t ehi[C::PF4 ? BN : 1][NB], elo[C::PF4 ? BN : 1][NB];
+  __shared__ uint8_t gsc[4][NB], gsc1[4][NB];
+  __shared__ int vwide;
   const int t = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t k0 = (int64_t)t * BN;
@@ -475,7 +502,82 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
   // threads write consecutive 16-byte slots of one column)
   uint8_t* img = a.vt + tile_id * C::VBYTES;
   constexpr int VCOLS = C::VROW / 16;
-  for (int i = threadIdx.x; i < (C::VROWS ? 0 : VCOLS * D); i += 256) {
+  if constexpr (C::PF4) {
+    // MXFP4 values, re-expressed per (32-key group g, channel block b):
+    // element e2m1 * 2^(E_j - 127) = (e2m1 * 2^(E_j - A)) * 2^(A - 127)
+    // with A = max(E_max - 13, 0) (E_max over the group's rows whose block
+    // holds a nonzero code): the largest element becomes at most
+    // 6 * 2^13 < 57344 and every element with E_j - A in [-15, 13] is an
+    // exact E5M2 value (e2m1 has at most two significant bits; E5M2 keeps
+    // three down to its subnormal step 2^-16).  A nonzero element with
+    // E_j < A - 15 flags the tile: such elements go to a second image
+    // under A1 = max(A - 29, 0), exact for E_j >= A1 - 15, i.e. exponent
+    // spreads up to 57 within a group; an element beyond that (below
+    // 2^-55 of its group's largest) is left out.
+    if (threadIdx.x == 0) vwide = 0;
+    for (int c = threadIdx.x; c < BN * NB; c += 256) {
+      const int kl = c / NB, b = c % NB;
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(&tile[kl][16 * b]);
+      const bool nz = ((w[0] | w[1] | w[2] | w[3]) & 0x77777777u) != 0u;  // magnitude bits; rows past the end are 0
+      ehi[kl][b] = nz ? vex[kl][b] : (uint8_t)0;
+      elo[kl][b] = nz ? vex[kl][b] : (uint8_t)255;
+    }
+    __syncthreads();
+    if (threadIdx.x < 4 * NB) {
+      const int g = threadIdx.x / NB, b = threadIdx.x % NB;
+      int mx = 0, mn = 255;
+      for (int r = 0; r < 32; ++r) {
+        mx = max(mx, (int)ehi[32 * g + r][b]);
+        mn = min(mn, (int)elo[32 * g + r][b]);
+      }
+      const int sa = max(mx - 13, 0), sa1 = max(sa - 29, 0);
+      gsc[g][b] = (uint8_t)sa;
+      gsc1[g][b] = (uint8_t)sa1;
+      auxt[C::XKBYTES + 4 * g + b] = (uint8_t)sa;
+      auxt[C::XKBYTES + 16 + 4 * g + b] = (uint8_t)sa1;
+      if (mn != 255 && mn < sa - 15) vwide = 1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(auxt + C::XKBYTES + 32) = (uint32_t)vwide;
+  }
+  if (C::PF4) {
+    // the E5M2 image(s), keys in natural order: column c holds keys
+    // 16 c .. 16 c + 15 of row d; a flagged tile's second image follows
+    // the first
+    const bool two = vwide != 0;
+    for (int i = threadIdx.x; i < (BN / 16) * D; i += 256) {
+      const int c = i / D, d = i % D, b = d >> 5;
+      const int sa = gsc[c >> 1][b], sa1 = gsc1[c >> 1][b];
+      uint32_t w[4], w1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[4], f1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * c + 4 * q + r;
+          const uint32_t nib = (tile[key][d >> 1] >> (4 * (d & 1))) & 0xfu;
+          const uint32_t mag = nib & 7u;
+          const float fm = mag < 2 ? 0.5f * (float)mag
+                                   : (float)(1u << ((mag >> 1) - 1)) * (1.0f + 0.5f * (float)(mag & 1u));
+          const int e = (int)vex[key][b];
+          const bool in0 = mag != 0 && e >= sa - 15, in1 = mag != 0 && !in0 && e >= sa1 - 15;
+          const float x0 = in0 ? __builtin_amdgcn_ldexpf(fm, e - sa) : 0.0f;
+          const float x1 = in1 ? __builtin_amdgcn_ldexpf(fm, e - sa1) : 0.0f;
+          f[r] = (nib & 8u) ? -x0 : x0;
+          f1[r] = (nib & 8u) ? -x1 : x1;
+        }
+        int pk = __builtin_amdgcn_cvt_pk_bf8_f32(f[0], f[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_bf8_f32(f[2], f[3], pk, true);
+        w[q] = (uint32_t)pk;
+        int pk1 = __builtin_amdgcn_cvt_pk_bf8_f32(f1[0], f1[1], 0, false);
+        pk1 = __builtin_amdgcn_cvt_pk_bf8_f32(f1[2], f1[3], pk1, true);
+        w1[q] = (uint32_t)pk1;
+      }
+      *reinterpret_cast<uint4*>(img + (c * D + d) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      if (two) *reinterpret_cast<uint4*>(img + C::VF4BYTES + (c * D + d) * 16) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+    }
+  }
+  for (int i = threadIdx.x; i < ((C::VROWS || C::PF4) ? 0 : VCOLS * D); i += 256) {
     const int c = i / D, d = i % D;
     uint32_t w[4];
     if (C::PI8 || C::PF8) {
@@ -687,6 +789,7 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   static_assert(NTK % 256 == 0, "tile copies: an even number of 128-lane columns per round");
   constexpr int BMK = NWK * 32;          // queries per workgroup
   static_assert(!(PP && VDIR), "ping-pong tiles come from the workspace");
+  static_assert(!(G::PF4 && (PP || VDIR)), "MXFP4 value tiles: four-wave kernel");
   static_assert(!VDIR || (G::PI8 && D == 128), "direct V: int8 codes, D = 128");
   constexpr int KS = G::KS, DB = G::DB, NB = G::NB;
   // per-key K scales multiply the scores (per-token scopes, MXFP8 rows); a
@@ -841,6 +944,13 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   const int kop_off = h * (BN * 16) + kslot(qk_row(j)) * 16;  // + ks 2 BN 16 + kb 256
   const int vop_off = h * (D * 16) + j * 16;                  // + kstep 2 D 16 + db 512
   const int vop8_off = (4 * h * D + j) * 16;                  // E4M3 V^T: + s 2 D 16 + db 512 (+ D 16)
+  // E5M2 V^T (MXFP4 values): the 8-bit A operand of the 32x32x64 f8f6f4
+  // MFMA holds, in lane half h, K 16 h .. 16 h + 15 in bytes 0-15 and K
+  // 32 + 16 h .. in bytes 16-31, while the E2M1 P operand holds K 32 h' ..
+  // 32 h' + 31 in order (keys 64 h' + 32 s + 0..31).  So byte b < 16 of
+  // lane half h is key 32 s + 16 h + b (image column 2 s + h) and byte
+  // 16 + b key 64 + 32 s + 16 h + b (column 4 + 2 s + h).
+  const int vop4_off = (h * D + j) * 16;                      // + s 2 D 16 + db 512 (+ 4 D 16)
   const int xk_off = G::KBYTES + 256 * h;                     // the lane's keys' K scales (floats)
   const int xv_off = G::VBYTES + 256 * h;                     // their qmax w_j (floats)
   const int xmx_off = G::KBYTES + qk_row(j) * NB + h;         // MXFP4: + 16 kb NB + 2 ks
@@ -926,8 +1036,11 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   constexpr int VRB = G::PI8 ? D : 2 * D;  // bytes of a V row
   const uint8_t* vrows = (G::VROWS && !VDIR) ? p.vcodes + p.vmap.row(bb, hd, 0) * VRB : nullptr;
   const uint32_t vrstride = (uint32_t)(p.vmap.ss * VRB);
-  auto issue_v = [&](int t, uint8_t* vb) {
-    if (G::VROWS && !VDIR) {
+  // f4: copy only the first E5M2 image of an MXFP4 value tile
+  auto issue_v = [&](int t, uint8_t* vb, bool f4 = false) {
+    if (G::PF4 && f4) {
+      stage<G::VF4BYTES / 16, NTK, PP>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane, loff_lin, NTK * 16);
+    } else if (G::VROWS && !VDIR) {
       // chunk i NTK + pw: column c = i (NTK / 128) + pw / 128, slot pw % 128
       // holding key slot ^ VSWZ (c & 1) (NTK / 128 is even: c & 1 is the
       // same in every round)
@@ -955,6 +1068,12 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   // with an fma; the bf16 value product rescales O once per tile and lets
   // the P V MFMA accumulate straight into it).
   float M = -INFINITY, L = 0.f, fref = 1.f;
+  // MXFP4 values: the current tile's flag (nonzero: a second E5M2 image)
+  uint32_t vwide = 1;
+  auto load_vwide = [&](int t) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(
+        *reinterpret_cast<const uint32_t*>(auxbase + (int64_t)t * G::XBYTES + G::XKBYTES + 32));
+  };
   f32x16 O[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) O[db] = f32x16{};
@@ -1336,6 +1455,71 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
             }
           }
           };
+          // MXFP4 Q, K and V, tile with an E5M2 V^T image: per 32-key group
+          // (k-step s: the lane's keys 64 h + 32 s + 0..31, one MX group)
+          // the group exponent E as in the bf16 path, the E2M1 codes of
+          // p / 2^E packed eight to a word (the B operand, E + 127 its
+          // scale), then O^T += V^T P^T on the block-scaled f8f6f4 MFMA
+          // with the E5M2 image as A (its scale per key group and channel
+          // block), accumulating into the rescaled O.  The products are
+          // those of the exact values; the instruction sums them to about
+          // 2^-12 of the largest, an error that enters O linearly.
+          auto values_f4 = [&]() __attribute__((always_inline)) {
+            const float c0 = -ms * ce;
+            const uint8_t* vop4 = vb + vop4_off;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              const float pmax = __builtin_amdgcn_exp2f((gmax[s] - ms) * ce);
+              const int E = mx_exponent(pmax);
+              const float psc = E > -127 ? pow2f(E) : 1.0f;
+              const int pe = E > -127 ? E + 127 : 127;
+              i32x8 pb = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                  float pv[8];
+#pragma unroll
+                  for (int t8 = 0; t8 < 8; ++t8) {
+                    pv[t8] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * s + kk][8 * s2 + t8], ce, c0));
+                    if (t8 & 1) ls1 += pv[t8]; else ls0 += pv[t8];
+                  }
+                  // keys 16 kk + 8 s2 + 0..7 of the group: nibbles of word 2 kk + s2
+                  uint32_t w = 0;
+                  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pv[0], pv[1], psc, 0);
+                  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pv[2], pv[3], psc, 1);
+                  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pv[4], pv[5], psc, 2);
+                  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, pv[6], pv[7], psc, 3);
+                  pb[2 * kk + s2] = (int)w;
+                }
+              // E5M2 scales of key group 2 h + s: byte b for channel block b
+              const uint32_t vsc = *reinterpret_cast<const uint32_t*>(vb + G::VBYTES + 4 * (2 * h + s));
+#pragma unroll
+              for (int db = 0; db < DB; ++db) {
+                const uint8_t* a = vop4 + (2 * s * D + 32 * db) * 16;
+                const uint4 lo = lds_ld<uint4>(a), hi = lds_ld<uint4>(a + 4 * D * 16);
+                const i32x8 va = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, O[db], 1, 4, 0,
+                                                                        (int)((vsc >> (8 * db)) & 0xffu), 0, pe);
+              }
+              if (vwide != 0) {
+                // flagged tile: the elements the first image leaves out are
+                // in the second one (upper half of the slot), its scales
+                // after the first image's
+                const uint32_t vsc1 = *reinterpret_cast<const uint32_t*>(vb + G::VBYTES + 16 + 4 * (2 * h + s));
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                  const uint8_t* a = vop4 + G::VF4BYTES + (2 * s * D + 32 * db) * 16;
+                  const uint4 lo = lds_ld<uint4>(a), hi = lds_ld<uint4>(a + 4 * D * 16);
+                  const i32x8 va = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                  O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, O[db], 1, 4, 0,
+                                                                          (int)((vsc1 >> (8 * db)) & 0xffu), 0, pe);
+                }
+              }
+            }
+          };
           if constexpr (G::PF8) {
             if (__builtin_amdgcn_ballot_w64(!(fabsf(ms * ce) <= 64.0f)) == 0) values(std::true_type{});
             else values(std::false_type{});
@@ -1353,7 +1537,8 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
               }
               ms = 0.0f;
             }
-            values(std::true_type{});
+            if constexpr (G::PF4) values_f4();
+            else values(std::true_type{});
           }
           if (G::PF8) {
             // O^T += V^T P^T on the f8f6f4 MFMA (E4M3 x E4M3), straight into
@@ -1410,11 +1595,17 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
     }
   } else if (!PP) {
     issue_k(t_beg, kbuf);
+    // MXFP4 values: each tile's flag is read one tile ahead
+    uint32_t vwide_next = G::PF4 && t_beg < t_end ? load_vwide(t_beg) : 1u;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 #pragma clang loop unroll(disable)
     for (int t = t_beg; t < t_end; ++t) {
-      issue_v(t, vbuf);
+      if (G::PF4) {
+        vwide = vwide_next;
+        if (t + 1 < t_end) vwide_next = load_vwide(t + 1);
+      }
+      issue_v(t, vbuf, vwide == 0);
       phase_scores(t, kbuf);
       // V(t) has landed everywhere and every wave is done with K(t)
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)

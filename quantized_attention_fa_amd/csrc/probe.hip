@@ -308,6 +308,32 @@ extern "C" int faq_probe_mfma32_fp4(const uint8_t* A, const uint8_t* Bt, const u
 }
 
 namespace {
+// v_mfma_scale_f32_32x32x64_f8f6f4 with E5M2 A and E2M1 B (the MXFP4 value
+// product): A [32][64] bytes, lane (i, h) holds bytes 32h .. 32h + 31 of
+// row i; Bt [32][32] bytes (64 elements per row, element 2k in the low
+// nibble of byte k), lane (i, h) holds elements 32h .. 32h + 31; E8M0
+// scales sa, sb [32][2] for row i and lane half h.
+__global__ void k_probe_mfma32_bf8_fp4(const uint8_t* A, const uint8_t* Bt, const uint8_t* sa, const uint8_t* sb,
+                                       float* C) {
+  const int l = threadIdx.x, i = l & 31, h = l >> 5;
+  const uint4* pa = reinterpret_cast<const uint4*>(A + i * 64 + 32 * h);
+  const uint4 a0 = pa[0], a1 = pa[1];
+  const uint4 b = *reinterpret_cast<const uint4*>(Bt + i * 32 + 16 * h);
+  const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  f32x16 c = {};
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 1, 4, 0, (int)sa[i * 2 + h], 0, (int)sb[i * 2 + h]);
+  for (int r = 0; r < 16; ++r) C[(8 * (r / 4) + 4 * h + r % 4) * 32 + i] = c[r];
+}
+}  // namespace
+
+extern "C" int faq_probe_mfma32_bf8_fp4(const uint8_t* A, const uint8_t* Bt, const uint8_t* sa, const uint8_t* sb,
+                                        float* C) {
+  k_probe_mfma32_bf8_fp4<<<1, 64>>>(A, Bt, sa, sb, C);
+  return (int)hipDeviceSynchronize();
+}
+
+namespace {
 // LDS read pattern: a 16 KiB LDS buffer holds word i = i * 2654435761 (mod
 // 2^32); each of the 64 lanes reads W bytes at byte offset offs[lane],
 // `reps` times (the address is made opaque per repetition, so every

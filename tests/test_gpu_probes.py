@@ -2,7 +2,8 @@
 checked against a CPU reference built from the oracle's format tables:
 
 * MFMA operand layouts (i8 16x16x64, bf16 16x16x32, f8f6f4 16x16x128 with
-  E2M1 operands and per-lane E8M0 scales);
+  E2M1 operands and per-lane E8M0 scales; 32x32 forms of each, and the
+  32x32x64 f8f6f4 with E5M2 A and E2M1 B, whose scales follow K blocks);
 * the K order of 8-bit f8f6f4 operands (lane group g: bytes 0-15 at K
   16g.., bytes 16-31 at K 64+16g..), which differs from the 4-bit one;
 * the f8f6f4 MFMA sums 8-bit products with limited precision (the reason the
@@ -135,6 +136,76 @@ def test_mfma32_fp4_scaled_layout(lib):
     C = torch.zeros((32, 32), dtype=torch.float32, device=DEV)
     assert lib.faq_probe_mfma32_fp4(*[_p(t) for t in keep], _p(C)) == 0
     assert np.array_equal(C.cpu().numpy().astype(np.float64), va @ vb.T)
+
+
+def _e5m2_decode(codes):
+    """E5M2 (OCP FP8, bias 15, subnormals at 2^-16 steps); no Inf/NaN codes
+    are used here."""
+    c = np.asarray(codes).astype(np.int64)
+    e, m = (c >> 2) & 0x1F, c & 3
+    mag = np.where(e == 0, m * 2.0 ** -16, (1 + m / 4) * 2.0 ** (e - 15))
+    return np.where(c & 0x80, -mag, mag)
+
+
+# K position of byte p (lane half p // 32, byte p % 32) of an 8-bit operand
+# of the 32x32x64 f8f6f4 MFMA, against the 4-bit operand's elements (lane
+# half h holds elements 32h .. 32h + 31 in order)
+MFMA32_8BIT_K = [16 * (p // 32) + p % 32 if p % 32 < 16 else 32 + 16 * (p // 32) + p % 32 - 16 for p in range(64)]
+
+
+def _mfma32_bf8_fp4(lib, A, Bp, sa, sb):
+    keep = [_d(A), _d(Bp), _d(sa), _d(sb)]
+    C = torch.zeros((32, 32), dtype=torch.float32, device=DEV)
+    assert lib.faq_probe_mfma32_bf8_fp4(*[_p(t) for t in keep], _p(C)) == 0
+    return C.cpu().numpy().astype(np.float64)
+
+
+def test_mfma32_bf8_fp4_k_order(lib):
+    """E5M2 A times E2M1 B on v_mfma_scale_f32_32x32x64_f8f6f4 (the MXFP4
+    value product), each A byte's K position read off bit-encoded B rows: in
+    lane half h, bytes 0-15 sit at K 16h.., bytes 16-31 at K 32 + 16h..,
+    while the E2M1 elements of B are in order."""
+    kappa = np.full(64, -1)
+    ones = np.full((32, 2), 127, np.uint8)
+    for m in range(2):
+        A = np.zeros((32, 64), np.uint8)
+        for i in range(32):
+            A[i, 32 * m + i] = 0x3C  # 1.0
+        Bc = np.zeros((32, 64), np.uint8)
+        for j in range(6):
+            Bc[j, [q for q in range(64) if (q >> j) & 1]] = 2  # 1.0
+        C = _mfma32_bf8_fp4(lib, A, _pack4(Bc), ones, ones)
+        for i in range(32):
+            kappa[32 * m + i] = int(sum(int(round(C[i, j])) << j for j in range(6)))
+    assert kappa.tolist() == MFMA32_8BIT_K
+
+
+def test_mfma32_bf8_fp4_values(lib):
+    """The same instruction on E5M2 values e2m1 * 2^-k (k = 0..15, down to
+    the E5M2 subnormals) with E8M0 scales per row and K block: each row's
+    products span < 2^6 within a block, so the sums are exact."""
+    g = np.random.default_rng(25)
+    e2m1_mag = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    k = g.integers(0, 16, (32, 1))  # one shift per row: its products span < 2^8
+    Aval = e2m1_mag[g.integers(0, 7, (32, 64))] * 2.0 ** -k.astype(np.float64)
+    Aval *= np.where(g.random((32, 64)) < 0.5, -1.0, 1.0)
+    grid = np.arange(256)
+    dec = _e5m2_decode(grid)
+    lut = {float(v): int(c) for c, v in zip(grid, dec) if (c & 0x7F) < 0x7C}
+    A = np.vectorize(lambda v: lut[float(v)])(Aval).astype(np.uint8)
+    assert np.array_equal(_e5m2_decode(A), Aval)
+    Bc = g.integers(0, 16, (32, 64)).astype(np.uint8)
+    # block scales within 2^5 of 1: the two block sums stay exact in fp32
+    sa = g.integers(125, 131, (32, 2)).astype(np.uint8)
+    sb = g.integers(125, 131, (32, 2)).astype(np.uint8)
+    C = _mfma32_bf8_fp4(lib, A, _pack4(Bc), sa, sb)
+    Ak = np.zeros_like(Aval)
+    Ak[:, MFMA32_8BIT_K] = Aval  # A in K order
+    # the scale of lane half h applies to K block h (K 32h .. 32h + 31), not
+    # to the bytes that lane holds
+    ref = (Ak * np.repeat(F.e8m0_decode(sa), 32, axis=1)) @ (
+        F.e2m1_decode(Bc) * np.repeat(F.e8m0_decode(sb), 32, axis=1)).T
+    assert np.array_equal(C, ref)
 
 
 def test_mfma_fp4_scaled_layout(lib):
