@@ -544,38 +544,48 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
     // the E5M2 image(s), keys in natural order: column c holds keys
     // 16 c .. 16 c + 15 of row d; a flagged tile's second image follows
     // the first
-    const bool two = vwide != 0;
-    for (int i = threadIdx.x; i < (BN / 16) * D; i += 256) {
-      const int c = i / D, d = i % D, b = d >> 5;
-      const int sa = gsc[c >> 1][b], sa1 = gsc1[c >> 1][b];
-      uint32_t w[4], w1[4];
+    auto image = [&](auto two) __attribute__((always_inline)) {
+      constexpr bool TWO = decltype(two)::value;
+      for (int i = threadIdx.x; i < (BN / 16) * D; i += 256) {
+        const int c = i / D, d = i % D, b = d >> 5;
+        const int sa = gsc[c >> 1][b], sa1 = gsc1[c >> 1][b];
+        uint32_t w[4], w1[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float f[4], f1[4];
+        for (int q = 0; q < 4; ++q) {
+          float f[4], f1[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * c + 4 * q + r;
-          const uint32_t nib = (tile[key][d >> 1] >> (4 * (d & 1))) & 0xfu;
-          const uint32_t mag = nib & 7u;
-          const float fm = mag < 2 ? 0.5f * (float)mag
-                                   : (float)(1u << ((mag >> 1) - 1)) * (1.0f + 0.5f * (float)(mag & 1u));
-          const int e = (int)vex[key][b];
-          const bool in0 = mag != 0 && e >= sa - 15, in1 = mag != 0 && !in0 && e >= sa1 - 15;
-          const float x0 = in0 ? __builtin_amdgcn_ldexpf(fm, e - sa) : 0.0f;
-          const float x1 = in1 ? __builtin_amdgcn_ldexpf(fm, e - sa1) : 0.0f;
-          f[r] = (nib & 8u) ? -x0 : x0;
-          f1[r] = (nib & 8u) ? -x1 : x1;
+          for (int r = 0; r < 4; ++r) {
+            const int key = 16 * c + 4 * q + r;
+            const uint32_t nib = (tile[key][d >> 1] >> (4 * (d & 1))) & 0xfu;
+            const uint32_t mag = nib & 7u;
+            const float fm = mag < 2 ? 0.5f * (float)mag
+                                     : (float)(1u << ((mag >> 1) - 1)) * (1.0f + 0.5f * (float)(mag & 1u));
+            const int e = (int)vex[key][b];
+            const bool in0 = mag != 0 && e >= sa - 15;
+            const float x0 = in0 ? __builtin_amdgcn_ldexpf(fm, e - sa) : 0.0f;
+            f[r] = (nib & 8u) ? -x0 : x0;
+            if (TWO) {
+              const bool in1 = mag != 0 && !in0 && e >= sa1 - 15;
+              const float x1 = in1 ? __builtin_amdgcn_ldexpf(fm, e - sa1) : 0.0f;
+              f1[r] = (nib & 8u) ? -x1 : x1;
+            }
+          }
+          int pk = __builtin_amdgcn_cvt_pk_bf8_f32(f[0], f[1], 0, false);
+          pk = __builtin_amdgcn_cvt_pk_bf8_f32(f[2], f[3], pk, true);
+          w[q] = (uint32_t)pk;
+          if (TWO) {
+            int pk1 = __builtin_amdgcn_cvt_pk_bf8_f32(f1[0], f1[1], 0, false);
+            pk1 = __builtin_amdgcn_cvt_pk_bf8_f32(f1[2], f1[3], pk1, true);
+            w1[q] = (uint32_t)pk1;
+          }
         }
-        int pk = __builtin_amdgcn_cvt_pk_bf8_f32(f[0], f[1], 0, false);
-        pk = __builtin_amdgcn_cvt_pk_bf8_f32(f[2], f[3], pk, true);
-        w[q] = (uint32_t)pk;
-        int pk1 = __builtin_amdgcn_cvt_pk_bf8_f32(f1[0], f1[1], 0, false);
-        pk1 = __builtin_amdgcn_cvt_pk_bf8_f32(f1[2], f1[3], pk1, true);
-        w1[q] = (uint32_t)pk1;
+        *reinterpret_cast<uint4*>(img + (c * D + d) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (TWO)
+          *reinterpret_cast<uint4*>(img + C::VF4BYTES + (c * D + d) * 16) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
       }
-      *reinterpret_cast<uint4*>(img + (c * D + d) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-      if (two) *reinterpret_cast<uint4*>(img + C::VF4BYTES + (c * D + d) * 16) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-    }
+    };
+    if (vwide != 0) image(std::true_type{});
+    else image(std::false_type{});
   }
   for (int i = threadIdx.x; i < ((C::VROWS || C::PF4) ? 0 : VCOLS * D); i += 256) {
     const int c = i / D, d = i % D;

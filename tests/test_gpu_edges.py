@@ -78,28 +78,39 @@ def test_nothing_to_compute():
         faq.fa_quant_attention(run.qt[0], k0, k0)
 
 
-@pytest.mark.parametrize("shift", [30, 50])
-def test_mxfp4_value_exponent_spread(shift):
+@pytest.mark.parametrize("shift,q_len,causal,S", [(30, None, False, 256), (50, None, False, 256),
+                                                  (30, 5, False, 640), (40, None, True, 384)])
+def test_mxfp4_value_exponent_spread(shift, q_len, causal, S):
     """MXFP4 values whose 32-key groups span more binades than one E5M2
     image holds: the odd keys' V rows are scaled by 2^-shift (a group's
     exponents then spread over shift + ~3 binades), and Q and K put the
     weight on those keys (scores ~11 above the even keys', whose
     probabilities quantize to 0), so every output comes from the small
     elements and the relative error sees them.  Spreads up to 57 are exact
-    through the second image."""
-    w = small_workload(4, (1, 2, 256, 128))
+    through the second image; also with key splits (a short query set: a
+    split starts past tile 0) and under the causal mask."""
+    w = small_workload(4, (1, 2, S, 128), q_len=q_len)
     g = torch.Generator().manual_seed(101 + shift)
-    B, H, S, D = w.q.shape
+    B, H, Sq, D = w.q.shape
     u = torch.randn((1, H, 1, D), generator=g)
     u = u / u.norm(dim=-1, keepdim=True)
     sign = torch.where(torch.arange(S) % 2 == 1, 1.0, -1.0).reshape(1, 1, S, 1)
-    q = 8.0 * u + 0.3 * torch.randn((B, H, S, D), generator=g)
+    q = 8.0 * u + 0.3 * torch.randn((B, H, Sq, D), generator=g)
     k = 8.0 * sign * u + 0.3 * torch.randn((B, H, S, D), generator=g)
     v = w.v.float() * torch.where(torch.arange(S) % 2 == 1, 2.0 ** -shift, 1.0).reshape(1, 1, S, 1)
     w.q.copy_(q.to(w.q.dtype)); w.k.copy_(k.to(w.k.dtype)); w.v.copy_(v.to(w.v.dtype))
     run = GpuRun(w)
-    o = run.attention(torch.float32, causal=False).cpu().numpy()
-    o_ref, T, n_tie = oracle_attention(run, causal=False)
-    assert np.abs(o_ref).max() < 2.0 ** (-shift + 6)  # the outputs are the small elements'
+    o = run.attention(torch.float32, causal=causal).cpu().numpy()
+    o_ref, T, n_tie = oracle_attention(run, causal=causal)
+    # the outputs are the small elements', except, under the causal mask,
+    # rows at a 32-key group start (row 0, 32, ...): the last group they see
+    # holds one even key alone, whose probability takes that group's
+    # exponent and a nonzero code; those rows are checked on their own
+    big = (np.arange(Sq) % 32 == 0) if causal else np.zeros(Sq, bool)
+    assert np.abs(o_ref[:, :, ~big]).max() < 2.0 ** (-shift + 6)
     for h in range(H):
-        check_attention(o[:, h:h + 1], (o_ref[:, h:h + 1], T[:, h:h + 1], n_tie), f"mxfp4 V spread 2^-{shift} head {h}")
+        sl = (slice(None), slice(h, h + 1), ~big)
+        check_attention(o[sl], (o_ref[sl], T[sl], n_tie), f"mxfp4 V spread 2^-{shift} q_len={q_len} causal={causal} head {h}")
+    if causal:
+        sl = (slice(None), slice(None), big)
+        check_attention(o[sl], (o_ref[sl], T[sl], n_tie), f"mxfp4 V spread 2^-{shift} causal group-start rows")
