@@ -694,29 +694,23 @@ FAQ_DEV float* part_ml(float* part, int nsplit, int c, int64_t BH, int64_t Sq, i
   return part + (int64_t)nsplit * BH * Sq * D + (((int64_t)c * BH + bh) * Sq + i) * 2;
 }
 
-using gptr = const __attribute__((address_space(1))) void*;
 using lptr = __attribute__((address_space(3))) void*;
 
 // One 16-byte global -> LDS copy per lane (lane i of the wave to
 // lds + 16 i) from base + off, base wave-uniform, off the lane's 32-bit
-// byte offset.  ASM: the same instruction written out in its SGPR-base
-// form (the address is one VGPR), so that the compiler does not track
-// the copy: its completion is then waited for only where the kernel says
-// so (vmcnt), never before reads of other LDS buffers.  The instruction
-// has no result registers; M0 holds the wave's LDS base.  M0 is a
-// reserved register the compiler does not treat as clobberable, so
-// kernels that copy this way issue no other M0-using instruction: all
-// their LDS copies go through this form (their assembly has no M0 access
-// outside these blocks).
-template <bool ASM>
+// byte offset: global_load_lds_dwordx4 written out in its SGPR-base form
+// (the address is one VGPR, no 64-bit per-lane address arithmetic), so
+// that the compiler does not track the copy: its completion is waited for
+// only where the kernel says so (vmcnt), never before reads of other LDS
+// buffers.  The instruction has no result registers; M0 holds the wave's
+// LDS base.  M0 is a reserved register the compiler does not treat as
+// clobberable, so the attention kernels issue no other M0-using
+// instruction: all their LDS copies go through this form (their assembly
+// has no M0 access outside these blocks).
 FAQ_DEV void copy16(const uint8_t* base, uint32_t off, uint8_t* lds) {
-  if (ASM) {
-    const uint32_t m = (uint32_t)(uintptr_t)(lptr)lds;
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(m)
-                 : "memory");
-  } else {
-    __builtin_amdgcn_global_load_lds((gptr)(base + off), (lptr)lds, 16, 0, 0);
-  }
+  const uint32_t m = (uint32_t)(uintptr_t)(lptr)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(m)
+               : "memory");
 }
 
 // Copy NCH 16-byte chunks global -> LDS with NT threads.  The workgroup
@@ -725,7 +719,7 @@ FAQ_DEV void copy16(const uint8_t* base, uint32_t off, uint8_t* lds) {
 // comes from base + i rstride + loff: loff is the lane's 32-bit byte
 // offset (the same register in every round), rstride a wave-uniform
 // stride added to the scalar base.
-template <int NCH, int NT, bool ASM = false>
+template <int NCH, int NT>
 FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, uint32_t loff, uint32_t rstride) {
   // the tile base is a wave-uniform value held in SGPRs; hiding it from the
   // optimizer keeps it from turning every copy into a 64-bit per-lane
@@ -735,13 +729,13 @@ FAQ_DEV void stage(uint8_t* lds, const uint8_t* base, int wave, int lane, uint32
 #pragma unroll
   for (int i = 0; i < ROUNDS; ++i) {
     const int grp = i * NT + wave * 64;
-    copy16<ASM>(base + (size_t)i * rstride, loff, lds + grp * 16);
+    copy16(base + (size_t)i * rstride, loff, lds + grp * 16);
   }
   constexpr int REM = NCH - ROUNDS * NT;  // < one round: the first waves take it
   if (REM > 0) {
     const int grp = ROUNDS * NT + wave * 64;
     if (grp < NCH) {
-      if (REM % 64 == 0 || grp + lane < NCH) copy16<ASM>(base + (size_t)ROUNDS * rstride, loff, lds + grp * 16);
+      if (REM % 64 == 0 || grp + lane < NCH) copy16(base + (size_t)ROUNDS * rstride, loff, lds + grp * 16);
     }
   }
 }
@@ -995,14 +989,14 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   const int krow = kslot(pw & (BN - 1));
   auto issue_k = [&](int t, uint8_t* kb) {
     if (G::QIMG) {
-      stage<G::KBYTES / 16, NTK, PP || VDIR>(kb, kbase + (int64_t)t * G::KBYTES, wave, lane, loff_lin,
+      stage<G::KBYTES / 16, NTK>(kb, kbase + (int64_t)t * G::KBYTES, wave, lane, loff_lin,
                                              NTK * 16);
     } else {
       const uint32_t roff = (uint32_t)min(t * BN + krow, Skv - 1) * kstride + (uint32_t)((pw >> 7) * 16);
-      stage<G::KBYTES / 16, NTK, PP || VDIR>(kb, kbase, wave, lane, roff, (NTK / 128) * 16);
+      stage<G::KBYTES / 16, NTK>(kb, kbase, wave, lane, roff, (NTK / 128) * 16);
     }
     if (G::XKBYTES > 0)
-      stage<G::XKBYTES / 16, NTK, PP || VDIR>(kb + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
+      stage<G::XKBYTES / 16, NTK>(kb + G::KBYTES, auxbase + (int64_t)t * G::XBYTES, wave, lane,
                                               loff_lin, NTK * 16);
   };
   // direct V: thread (cc, g) = (tid / 32, tid % 32) moves the 16 keys of
@@ -1049,21 +1043,21 @@ __global__ __launch_bounds__(PP ? 2 * NTHR : NTHR, PP ? 1 : 2) void k_attn(const
   // f4: copy only the first E5M2 image of an MXFP4 value tile
   auto issue_v = [&](int t, uint8_t* vb, bool f4 = false) {
     if (G::PF4 && f4) {
-      stage<G::VF4BYTES / 16, NTK, PP>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane, loff_lin, NTK * 16);
+      stage<G::VF4BYTES / 16, NTK>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane, loff_lin, NTK * 16);
     } else if (G::VROWS && !VDIR) {
       // chunk i NTK + pw: column c = i (NTK / 128) + pw / 128, slot pw % 128
       // holding key slot ^ VSWZ (c & 1) (NTK / 128 is even: c & 1 is the
       // same in every round)
       const int c0 = pw >> 7;
       const int key = (pw & (BN - 1)) ^ (VSWZ * (c0 & 1));
-      stage<G::VBYTES / 16, NTK, PP>(vb, vrows, wave, lane,
+      stage<G::VBYTES / 16, NTK>(vb, vrows, wave, lane,
                                      (uint32_t)min(t * BN + key, Skv - 1) * vrstride + (uint32_t)(c0 * 16),
                                      (NTK / 128) * 16);
     } else {
-      stage<G::VBYTES / 16, NTK, PP>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane, loff_lin, NTK * 16);
+      stage<G::VBYTES / 16, NTK>(vb, vtbase + (int64_t)t * G::VBYTES, wave, lane, loff_lin, NTK * 16);
     }
     if (G::XVBYTES > 0)
-      stage<G::XVBYTES / 16, NTK, PP>(vb + G::VBYTES, auxbase + (int64_t)t * G::XBYTES + G::XKBYTES, wave, lane,
+      stage<G::XVBYTES / 16, NTK>(vb + G::VBYTES, auxbase + (int64_t)t * G::XBYTES + G::XKBYTES, wave, lane,
                                       loff_lin, NTK * 16);
   };
   // copies each tile costs this wave (the wait counts of the ping-pong loop)
