@@ -204,25 +204,27 @@ __global__ __launch_bounds__(kThreads) void k_quant_token(const T* __restrict__ 
 
 // ------------------------------------------------------------------------
 // MXFP4 per-block: 32 consecutive elements along D share an E8M0 exponent.
-// D/8 threads per row; 4 threads per 32-element block.
+// D/16 threads per row; two neighbouring lanes per 32-element block, whose
+// maximum crosses them with one DPP swap (no LDS round trip); the lane
+// holding the first half writes the block's exponent byte.
 // ------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ x, int64_t rows, RowMap rm,
                                                           uint32_t H, uint32_t S, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ e8m0) {
-  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 2, NB = D / 32;
+  constexpr int TPR = D / 16, RPB = kThreads / TPR, U = 2, NB = D / 32;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
-  const int lane = threadIdx.x & 63;
   for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
-    float v[U][8];
+    float a[U][8], b[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       if (row < rows) {
-        load8(x + row * D + sub * 8, v[u]);  // memory row
+        load8(x + row * D + sub * 16, a[u]);  // memory row
+        load8(x + row * D + sub * 16 + 8, b[u]);
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
+        for (int k = 0; k < 8; ++k) a[u][k] = b[u][k] = 0.0f;
       }
     }
 #pragma unroll
@@ -230,39 +232,38 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
       const int64_t row = r0 + u * RPB + rin;
       float m = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
-      m = group_max<4>(m);
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fmaxf(fabsf(a[u][k]), fabsf(b[u][k])));
+      // the other half of the block: lane ^ 1 (quad_perm [1, 0, 3, 2])
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
       const int E = mx_exponent(m);
       // hardware E2M1 of x / 2^E (exact division by a power of two;
       // nearest, ties to even, saturating at 6, sign kept)
       const float sc = __uint_as_float((uint32_t)(E > -127 ? E + 127 : 127) << 23);
-      uint32_t packed = 0;
-      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[u][0], v[u][1], sc, 0);
-      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[u][2], v[u][3], sc, 1);
-      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[u][4], v[u][5], sc, 2);
-      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[u][6], v[u][7], sc, 3);
+      uint32_t p0 = 0, p1 = 0;
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, a[u][0], a[u][1], sc, 0);
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, a[u][2], a[u][3], sc, 1);
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, a[u][4], a[u][5], sc, 2);
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, a[u][6], a[u][7], sc, 3);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, b[u][0], b[u][1], sc, 0);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, b[u][2], b[u][3], sc, 1);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, b[u][4], b[u][5], sc, 2);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, b[u][6], b[u][7], sc, 3);
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(E == -127) != 0, 0)) {
         // 2^-127 is not a normal float: blocks with zero or subnormal amax
         // scale with ldexp and encode in software
         if (E == -127) {
-          packed = 0;
+          p0 = 0;
+          p1 = 0;
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            packed |= enc_e2m1(__builtin_amdgcn_ldexpf(v[u][k], 127)) << (4 * k);
+          for (int k = 0; k < 8; ++k) {
+            p0 |= enc_e2m1(__builtin_amdgcn_ldexpf(a[u][k], 127)) << (4 * k);
+            p1 |= enc_e2m1(__builtin_amdgcn_ldexpf(b[u][k], 127)) << (4 * k);
+          }
         }
       }
-      // gather the row's NB exponent bytes into the row's first lane
-      uint32_t eb = (uint32_t)(E + 127);
-      uint32_t word = eb;
-#pragma unroll
-      for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
       if (row < rows) {
-        *reinterpret_cast<uint32_t*>(codes + row * (D / 2) + sub * 4) = packed;
-        if (sub == 0) {
-          const int64_t lr = logical_row(rm, row, H, S);
-          if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + lr * NB) = word;
-          else *reinterpret_cast<uint16_t*>(e8m0 + lr * NB) = (uint16_t)word;
-        }
+        *reinterpret_cast<uint2*>(codes + row * (D / 2) + sub * 8) = make_uint2(p0, p1);
+        if ((sub & 1) == 0) e8m0[logical_row(rm, row, H, S) * NB + (sub >> 1)] = (uint8_t)(E + 127);
       }
     }
   }
@@ -271,57 +272,56 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp4(const T* __restrict__ 
 // ------------------------------------------------------------------------
 // MXFP8 per-block: 32 consecutive elements along D share an E8M0 exponent
 // E = floor(log2 amax) - 8; elements are E4M3 of x / 2^E (exact scaling),
-// saturating at 448 (FA PerBlock, MXFP8).  D/8 threads per row, 4 per block.
+// saturating at 448 (FA PerBlock, MXFP8).  D/16 threads per row, two neighbouring
+// lanes per block (one DPP swap for its maximum).
 // ------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const T* __restrict__ x, int64_t rows, RowMap rm,
                                                           uint32_t H, uint32_t S, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ e8m0) {
-  constexpr int TPR = D / 8, RPB = kThreads / TPR, U = 2, NB = D / 32;
+  constexpr int TPR = D / 16, RPB = kThreads / TPR, U = 2, NB = D / 32;
   const int sub = threadIdx.x % TPR, rin = threadIdx.x / TPR;
-  const int lane = threadIdx.x & 63;
   for (int64_t r0 = (int64_t)blockIdx.x * RPB * U; r0 < rows; r0 += (int64_t)gridDim.x * RPB * U) {
-    float v[U][8];
+    float v[U][16];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
+      float a[8], b[8];
       if (row < rows) {
-        load8(x + row * D + sub * 8, v[u]);  // memory row
+        load8(x + row * D + sub * 16, a);  // memory row
+        load8(x + row * D + sub * 16 + 8, b);
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[u][k] = 0.0f;
+        for (int k = 0; k < 8; ++k) a[k] = b[k] = 0.0f;
       }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { v[u][k] = a[k]; v[u][8 + k] = b[k]; }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t row = r0 + u * RPB + rin;
       float m = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[u][k]));
-      m = group_max<4>(m);
+      for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(v[u][k]));
+      // the other half of the block: lane ^ 1 (quad_perm [1, 0, 3, 2])
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
       const int E = mx_exponent<8>(m);
       // x / 2^E is exact wherever it can reach a nonzero code; the block
       // maximum lies in [256, 512) and saturates above 448
-      float q[8];
+      float q[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
+      for (int k = 0; k < 16; ++k)
         q[k] = with_sign_of(__builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(v[u][k], -E), -448.0f, 448.0f), v[u][k]);
-      int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
-      int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
-      // gather the row's NB exponent bytes into the row's first lane
-      uint32_t eb = (uint32_t)(E + 127);
-      uint32_t word = eb;
+      uint32_t w[4];
 #pragma unroll
-      for (int j = 1; j < NB; ++j) word |= (uint32_t)__shfl(eb, lane + 4 * j, 64) << (8 * j);
+      for (int k = 0; k < 4; ++k) {
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * k], q[4 * k + 1], 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * k + 2], q[4 * k + 3], c, true);
+        w[k] = (uint32_t)c;
+      }
       if (row < rows) {
-        *reinterpret_cast<uint2*>(codes + row * D + sub * 8) = make_uint2((uint32_t)w0, (uint32_t)w1);
-        if (sub == 0) {
-          const int64_t lr = logical_row(rm, row, H, S);
-          if (NB == 4) *reinterpret_cast<uint32_t*>(e8m0 + lr * NB) = word;
-          else *reinterpret_cast<uint16_t*>(e8m0 + lr * NB) = (uint16_t)word;
-        }
+        *reinterpret_cast<uint4*>(codes + row * D + sub * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        if ((sub & 1) == 0) e8m0[logical_row(rm, row, H, S) * NB + (sub >> 1)] = (uint8_t)(E + 127);
       }
     }
   }
@@ -728,7 +728,9 @@ hipError_t launch_quant_int8_token(const void* x, int x_dtype, const faq_shape& 
 template <int D, bool FP4>
 static hipError_t mx_d(const void* x, int x_dtype, const faq_shape& s, uint8_t* codes,
                        uint8_t* e8m0, hipStream_t st) {
-  constexpr int RPB = kThreads / (D / 8);
+  // rows per workgroup and step (16 elements per thread); two steps per
+  // workgroup round
+  constexpr int RPB = kThreads / (D / 16);
   const int64_t rows = s.B * s.H * s.S;
   const RowMap rm = row_map(s);
   const uint32_t H = (uint32_t)s.H, S = (uint32_t)s.S;
