@@ -116,15 +116,6 @@ FAQ_DEV int mx_exponent(float amax) {
 
 // ---------------------------------------------------------------- reductions
 
-template <int WIDTH>
-FAQ_DEV float group_max(float v) {
-#pragma unroll
-  for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
-FAQ_DEV float wave_max(float v) { return group_max<64>(v); }
-
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
 // l^48) with the in-register row swaps of gfx950 (no LDS round trip).
 FAQ_DEV float rows4_max(float x) {
@@ -133,6 +124,28 @@ FAQ_DEV float rows4_max(float x) {
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+
+// x of another lane by a DPP pattern (all lanes active, in-row sources)
+template <int CTRL>
+FAQ_DEV float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max over aligned groups of WIDTH lanes, all lanes active, in registers:
+// quad swaps (lane ^ 1, lane ^ 2), the half-row and row mirrors (lane
+// 7 - i within 8, 15 - i within 16), then the row swaps for a whole wave.
+template <int WIDTH>
+FAQ_DEV float group_max(float v) {
+  static_assert(WIDTH == 2 || WIDTH == 4 || WIDTH == 8 || WIDTH == 16 || WIDTH == 64, "group width");
+  if constexpr (WIDTH >= 2) v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  if constexpr (WIDTH >= 4) v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  if constexpr (WIDTH >= 8) v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  if constexpr (WIDTH >= 16) v = fmaxf(v, dpp_f<0x140>(v)); // row_mirror
+  if constexpr (WIDTH == 64) v = rows4_max(v);
+  return v;
+}
+
+FAQ_DEV float wave_max(float v) { return group_max<64>(v); }
 
 FAQ_DEV float rows4_sum(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
